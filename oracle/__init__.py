@@ -1,0 +1,144 @@
+"""fp64 CPU oracle for the fast-weight delta-rule layer with DPFP projection.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the package's smoke() check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the HIP library and never
+imports it.
+
+`dpfp`, `dpfp_mask`, `delta_forward` and `delta_step` wrap the plain-C fp64 implementation in
+fwa_oracle.c (built by oracle/build.py); `twin` holds an independent NumPy transcription used to
+cross-check it.  All arrays are float64, C-contiguous, in the [B, H, T, d] layout; W is
+[B, H, d_v, D] with D = 2 * d_k * nu.  Inputs given in fp32 or bf16 are taken exactly (bf16 and
+fp32 values are exactly representable in fp64).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """Bindings to one compiled copy of fwa_oracle.c (the real one, or a test's variant)."""
+
+    def __init__(self, path):
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int, ctypes.c_int64
+        L.oracle_dpfp.argtypes = [P, P, i64, i32, i32]
+        L.oracle_dpfp_mask.argtypes = [P, P, i64, i32, i32]
+        L.oracle_delta_forward.argtypes = [P, P, P, P, P, P, P] + [i32] * 6
+        L.oracle_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5
+        L.oracle_sigmoid.argtypes = [ctypes.c_double]
+        L.oracle_sigmoid.restype = ctypes.c_double
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        self.lib = L
+        self.path = path
+
+    def num_threads(self):
+        return self.lib.oracle_num_threads()
+
+    def set_num_threads(self, n):
+        self.lib.oracle_set_num_threads(int(n))
+
+    def sigmoid(self, x):
+        return self.lib.oracle_sigmoid(float(x))
+
+    def dpfp(self, x, nu):
+        """phi = DPFP(x) over the last axis; x [..., d_k] -> [..., 2*d_k*nu] (float64)."""
+        x = _f64(x)
+        d_k = x.shape[-1]
+        n = int(np.prod(x.shape[:-1], dtype=np.int64))
+        out = np.empty(x.shape[:-1] + (2 * d_k * nu,), dtype=np.float64)
+        self.lib.oracle_dpfp(_p(x), _p(out), n, d_k, nu)
+        return out
+
+    def dpfp_mask(self, x, nu):
+        """Boolean zero/nonzero pattern of DPFP(x), decided from signs alone."""
+        x = _f64(x)
+        d_k = x.shape[-1]
+        n = int(np.prod(x.shape[:-1], dtype=np.int64))
+        out = np.empty(x.shape[:-1] + (2 * d_k * nu,), dtype=np.uint8)
+        self.lib.oracle_dpfp_mask(_p(x), _p(out), n, d_k, nu)
+        return out.astype(bool)
+
+    def delta_forward(self, q, k, v, beta_logit, W0=None, nu=1):
+        """Literal per-step recurrence. Returns (y [B,H,T,d_v], W_final [B,H,d_v,D])."""
+        q, k, v, beta_logit = _f64(q), _f64(k), _f64(v), _f64(beta_logit)
+        B, H, T, d_k = q.shape
+        d_v = v.shape[-1]
+        D = 2 * d_k * nu
+        assert k.shape == q.shape and v.shape == (B, H, T, d_v)
+        assert beta_logit.shape == (B, H, T)
+        if W0 is not None:
+            W0 = _f64(W0)
+            assert W0.shape == (B, H, d_v, D)
+        y = np.zeros((B, H, T, d_v), dtype=np.float64)
+        Wf = np.empty((B, H, d_v, D), dtype=np.float64)
+        self.lib.oracle_delta_forward(_p(q), _p(k), _p(v), _p(beta_logit), _p(W0), _p(y),
+                                      _p(Wf), B, H, T, d_k, d_v, nu)
+        return y, Wf
+
+    def delta_step(self, q, k, v, beta_logit, W, nu=1):
+        """One decode step. q,k [B,H,d_k], v [B,H,d_v], beta_logit [B,H], W [B,H,d_v,D].
+        Returns (y [B,H,d_v], W_new); the W passed in is not modified."""
+        q, k, v, beta_logit = _f64(q), _f64(k), _f64(v), _f64(beta_logit)
+        B, H, d_k = q.shape
+        d_v = v.shape[-1]
+        W = np.array(W, dtype=np.float64, copy=True, order="C")
+        assert W.shape == (B, H, d_v, 2 * d_k * nu)
+        y = np.empty((B, H, d_v), dtype=np.float64)
+        self.lib.oracle_delta_step(_p(q), _p(k), _p(v), _p(beta_logit), _p(W), _p(y),
+                                   B, H, d_k, d_v, nu)
+        return y, W
+
+
+_DEFAULT = None
+
+
+def default():
+    """The oracle built from oracle/fwa_oracle.c (rebuilt when the source is newer)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        _DEFAULT = Oracle(_build.LIB)
+    return _DEFAULT
+
+
+def num_threads():
+    return default().num_threads()
+
+
+def set_num_threads(n):
+    default().set_num_threads(n)
+
+
+def sigmoid(x):
+    return default().sigmoid(x)
+
+
+def dpfp(x, nu):
+    return default().dpfp(x, nu)
+
+
+def dpfp_mask(x, nu):
+    return default().dpfp_mask(x, nu)
+
+
+def delta_forward(q, k, v, beta_logit, W0=None, nu=1):
+    return default().delta_forward(q, k, v, beta_logit, W0, nu)
+
+
+def delta_step(q, k, v, beta_logit, W, nu=1):
+    return default().delta_step(q, k, v, beta_logit, W, nu)

@@ -1,0 +1,373 @@
+"""Pins that tie the fp64 oracle to the pages and to mathematics, not to itself.
+
+Each pin_* function takes an oracle object (oracle.Oracle: the real build, or a build of a
+deliberately broken copy of fwa_oracle.c) and raises AssertionError when the oracle violates
+what the pages or the mathematics fix.  tests/test_oracle_pins.py runs every pin against the
+real oracle; tests/test_oracle_mutants.py checks that every planted mistake fails at least one.
+
+Sources: the Fast Weights Transformer guide (xdnf.cn/news/308600), sections "DPFP / projection
+formula and hyper-parameters", "DPFP / normalisation", "FastWeightsAttention / update formula",
+"FastWeightsAttention / module structure and source walkthrough", and "Background / fast
+computation form of linear self-attention" (the sum-update form used in pin_disjoint_keys).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+EPS = 1e-6
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- sign-pattern helpers
+
+def _positive_positions(bits, d_k):
+    """Cycle positions of relu([k, -k]) that are > 0 for the sign pattern `bits`
+    (bit j set <=> k_j > 0; no k_j is zero)."""
+    first = (bits[:, None] >> np.arange(d_k)[None, :]) & 1
+    return np.concatenate([first, 1 - first], axis=1).astype(bool)
+
+
+def _all_patterns(d_k):
+    return np.arange(1 << d_k, dtype=np.int64)
+
+
+def _keys_from_bits(bits, d_k, rng):
+    """Vectors with the given sign patterns and magnitudes in [0.5, 2)."""
+    mag = rng.uniform(0.5, 2.0, size=(len(bits), d_k))
+    sign = np.where(((bits[:, None] >> np.arange(d_k)[None, :]) & 1) == 1, 1.0, -1.0)
+    return sign * mag
+
+
+def onehot_patterns(d_k=16):
+    """All sign patterns whose shift-1 DPFP block has exactly one nonzero entry, grouped by
+    the index m of that entry.  Entry j of the shift-1 block is nonzero exactly when cycle
+    positions j and j-1 (mod 2*d_k) are both positive -- the roll by +1 of the pages' code."""
+    bits = _all_patterns(d_k)
+    pos = _positive_positions(bits, d_k)
+    prev = np.concatenate([pos[:, -1:], pos[:, :-1]], axis=1)  # position j-1, cyclic
+    both = pos & prev
+    one = both.sum(axis=1) == 1
+    m = np.argmax(both, axis=1)
+    out = {}
+    for b, mm in zip(bits[one], m[one]):
+        out.setdefault(int(mm), []).append(int(b))
+    return out
+
+
+# ---------------------------------------------------------------- DPFP pins
+
+def pin_dpfp_shape_nonneg_sum(O):
+    """phi has 2*d_k*nu entries, all >= 0, summing to just below 1 (sum-normalised with an
+    additive eps)."""
+    rng = np.random.default_rng(11)
+    for d_k, nu in [(16, 1), (16, 3), (64, 1), (64, 2), (64, 3), (8, 15), (32, 5)]:
+        k = rng.standard_normal((257, d_k))
+        phi = O.dpfp(k, nu)
+        assert phi.shape == (257, 2 * d_k * nu), (d_k, nu, phi.shape)
+        assert np.all(phi >= 0.0), (d_k, nu)
+        s = phi.sum(axis=1)
+        assert np.all(s < 1.0) and np.all(s > 1.0 - 1e-3), (d_k, nu, s.min(), s.max())
+
+
+def pin_dpfp_eps_is_additive(O):
+    """Scaling k by c scales every raw product by c^2, so with an additive eps
+    (1/sum(phi(c k)) - 1) / (1/sum(phi(k)) - 1) = 1/c^2 exactly in exact arithmetic."""
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((64, 16))
+    for c in (0.5, 0.1, 0.01):
+        r_k = 1.0 / O.dpfp(k, 2).sum(axis=1) - 1.0
+        r_ck = 1.0 / O.dpfp(c * k, 2).sum(axis=1) - 1.0
+        np.testing.assert_allclose(r_ck / r_k, 1.0 / c ** 2, rtol=1e-6)
+
+
+def pin_dpfp_onehot_roll_direction(O):
+    """Sign pattern (+,+,-,+,-,+,...,+) at d_k = 16 leaves exactly one adjacent pair of
+    positive cycle positions, (0, 1).  Under the roll by +i of the pages' code the surviving
+    product sits at index 1 (it would sit at index 0 under the formula's literal x_j * x_{j+i});
+    its value is p/(p+eps) with p = k_0 * k_1.  With nu = 2 the second block (offset 32) is
+    x[j] * x[j-2]: for this pattern the positive positions j with j-2 (mod 32) positive are
+    0 (paired with 30), 3, 5, ..., 15 and 20, 22, ..., 30."""
+    d_k = 16
+    signs = np.array([1, 1] + [(-1 if j % 2 == 0 else 1) for j in range(2, 16)], dtype=float)
+    mag = np.linspace(0.7, 1.9, 16)
+    k = signs * mag
+    phi = O.dpfp(k[None], 1)[0]
+    nz = np.flatnonzero(phi)
+    assert list(nz) == [1], nz
+    p = k[0] * k[1]
+    assert math.isclose(phi[1], p / (p + EPS), rel_tol=1e-14), (phi[1], p / (p + EPS))
+    eps_back = p * (1.0 / phi[1] - 1.0)
+    assert math.isclose(eps_back, EPS, rel_tol=1e-6), eps_back
+    phi2 = O.dpfp(k[None], 2)[0]
+    expect2 = {1} | {32 + j for j in [0] + list(range(3, 16, 2)) + list(range(20, 31, 2))}
+    assert set(np.flatnonzero(phi2)) == expect2, sorted(set(np.flatnonzero(phi2)) ^ expect2)
+
+
+def pin_dpfp_hand_examples(O):
+    """Worked examples derived by hand from the DPFP definition (tests/golden/dpfp_hand.txt)."""
+    with open(os.path.join(GOLDEN, "dpfp_hand.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            head, k_s, raw_s, s_s = [x.strip() for x in line.split("|")]
+            d_k, nu = (int(x) for x in head.split())
+            k = np.array([float(x) for x in k_s.split()])
+            raw = np.array([float(x) for x in raw_s.split()])
+            S = float(s_s)
+            assert len(k) == d_k and len(raw) == 2 * d_k * nu and raw.sum() == S
+            phi = O.dpfp(k[None], nu)[0]
+            np.testing.assert_allclose(phi, raw / (S + EPS), rtol=1e-14, atol=0)
+
+
+def pin_dpfp_mask_sign_predicate(O):
+    """For every sign pattern at d_k = 12 and nu = 1..3, the nonzero entries of phi are exactly
+    the (i, j) whose cycle positions j and j-i are both positive, and dpfp_mask agrees."""
+    d_k = 12
+    rng = np.random.default_rng(13)
+    bits = _all_patterns(d_k)
+    k = _keys_from_bits(bits, d_k, rng)
+    pos = _positive_positions(bits, d_k)
+    for nu in (1, 2, 3):
+        expect = np.concatenate(
+            [pos & np.concatenate([pos[:, 2 * d_k - i:], pos[:, :2 * d_k - i]], axis=1)
+             for i in range(1, nu + 1)], axis=1)
+        got = O.dpfp(k, nu) != 0.0
+        assert np.array_equal(got, expect), (nu, int((got != expect).sum()))
+        assert np.array_equal(O.dpfp_mask(k, nu), expect), nu
+
+
+def pin_dpfp_degenerate(O):
+    """Shift d_k pairs x[j] with x[j - d_k], i.e. relu(k) with relu(-k) of the same entry, so
+    its block is identically zero; d_k = 1 (only nu = 1 allowed) gives phi = 0; k = 0 and odd
+    d_k with strictly alternating signs also give all-zero products, and phi = 0 / eps = 0."""
+    rng = np.random.default_rng(14)
+    k = rng.standard_normal((50, 4))
+    phi = O.dpfp(k, 7)
+    assert np.all(phi[:, 3 * 8:4 * 8] == 0.0)        # block of shift i = 4 = d_k
+    assert np.all(O.dpfp(rng.standard_normal((10, 1)), 1) == 0.0)
+    assert np.all(O.dpfp(np.zeros((3, 16)), 2) == 0.0)
+    alt = np.array([[1.0, -2.0, 3.0]])                # cycle + - + | - + -: no adjacent pair
+    assert np.all(O.dpfp(alt, 1) == 0.0)
+    assert not np.any(np.isnan(O.dpfp(np.zeros((1, 5)), 4)))
+
+
+def pin_dpfp_negation_rotates_blocks(O):
+    """[-k, k] is [k, -k] rolled by d_k, so phi(-k) is phi(k) with every block rotated by d_k."""
+    rng = np.random.default_rng(15)
+    d_k, nu = 16, 3
+    k = rng.standard_normal((40, d_k))
+    a = O.dpfp(k, nu).reshape(40, nu, 2 * d_k)
+    b = O.dpfp(-k, nu).reshape(40, nu, 2 * d_k)
+    np.testing.assert_array_equal(b != 0.0, np.roll(a, d_k, axis=2) != 0.0)
+    np.testing.assert_allclose(b, np.roll(a, d_k, axis=2), rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------- sigmoid pins
+
+def pin_sigmoid_values(O):
+    assert O.sigmoid(0.0) == 0.5
+    assert O.sigmoid(-math.inf) == 0.0 and O.sigmoid(math.inf) == 1.0
+    assert math.isclose(O.sigmoid(math.log(3.0)), 0.75, rel_tol=1e-15)
+    assert math.isclose(O.sigmoid(-math.log(3.0)), 0.25, rel_tol=1e-15)
+    for x in (0.3, 2.0, 17.0, 700.0):
+        assert math.isclose(O.sigmoid(x) + O.sigmoid(-x), 1.0, rel_tol=1e-15)
+    assert O.sigmoid(-745.0) > 0.0 or O.sigmoid(-745.0) == 0.0  # no overflow / NaN
+    assert O.sigmoid(-800.0) == 0.0 and O.sigmoid(800.0) == 1.0
+
+
+# ---------------------------------------------------------------- recurrence pins
+
+def _rand_case(rng, B, H, T, d_k, d_v, nu, w0=True):
+    q = rng.standard_normal((B, H, T, d_k))
+    k = rng.standard_normal((B, H, T, d_k))
+    v = rng.standard_normal((B, H, T, d_v))
+    l = rng.standard_normal((B, H, T))
+    W0 = 0.1 * rng.standard_normal((B, H, d_v, 2 * d_k * nu)) if w0 else None
+    return q, k, v, l, W0
+
+
+def pin_beta_zero_freezes_state(O):
+    """beta = sigmoid(-inf) = 0 makes every write vanish: W_final = W0, y_t = W0 phi(q_t)."""
+    rng = np.random.default_rng(21)
+    q, k, v, l, W0 = _rand_case(rng, 2, 2, 9, 8, 5, 2)
+    l[:] = -math.inf
+    y, W = O.delta_forward(q, k, v, l, W0, nu=2)
+    np.testing.assert_array_equal(W, W0)
+    np.testing.assert_allclose(y, np.einsum("bhvd,bhtd->bhtv", W0, O.dpfp(q, 2)),
+                               rtol=1e-13, atol=1e-15)
+
+
+def pin_single_step_from_zero(O):
+    """One step from W = 0: v_bar = 0, so W = beta v phi(k)^T and y = beta v (phi(k).phi(q))."""
+    rng = np.random.default_rng(22)
+    q, k, v, l, _ = _rand_case(rng, 1, 3, 1, 16, 7, 1, w0=False)
+    y, W = O.delta_forward(q, k, v, l, None, nu=1)
+    beta = 1.0 / (1.0 + np.exp(-l))
+    fk, fq = O.dpfp(k, 1), O.dpfp(q, 1)
+    W_exp = beta[:, :, 0, None, None] * v[:, :, 0, :, None] * fk[:, :, 0, None, :]
+    np.testing.assert_allclose(W, W_exp, rtol=1e-13, atol=1e-16)
+    y_exp = beta[:, :, 0, None] * v[:, :, 0] * np.sum(fk[:, :, 0] * fq[:, :, 0], axis=-1)[..., None]
+    np.testing.assert_allclose(y[:, :, 0], y_exp, rtol=1e-12, atol=1e-16)
+
+
+def pin_transition_matrix_form(O):
+    """Tiny-T brute force through explicit D x D matrices:
+    W_t = W_{t-1} (I - beta_t f_t f_t^T) + beta_t v_t f_t^T, y_t = W_t phi(q_t)."""
+    rng = np.random.default_rng(23)
+    q, k, v, l, W0 = _rand_case(rng, 1, 2, 6, 4, 3, 2)
+    y, W = O.delta_forward(q, k, v, l, W0, nu=2)
+    fk, fq = O.dpfp(k, 2), O.dpfp(q, 2)
+    beta = 1.0 / (1.0 + np.exp(-l))
+    D = fk.shape[-1]
+    for h in range(2):
+        Wt = W0[0, h].copy()
+        for t in range(6):
+            f = fk[0, h, t]
+            Wt = Wt @ (np.eye(D) - beta[0, h, t] * np.outer(f, f)) + beta[0, h, t] * np.outer(v[0, h, t], f)
+            np.testing.assert_allclose(y[0, h, t], Wt @ fq[0, h, t], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(W[0, h], Wt, rtol=1e-12, atol=1e-14)
+
+
+def pin_disjoint_keys_reduce_to_linear_attention(O):
+    """Keys with pairwise disjoint DPFP supports and W = 0 at the start make every retrieval
+    v_bar = 0, so the rule reduces to the pages' sum-update linear attention without the z
+    normaliser: Y = tril_incl(phi(Q) phi(K)^T) diag(beta) V -- a masked matmul."""
+    rng = np.random.default_rng(24)
+    groups = onehot_patterns(16)
+    ms = sorted(groups)[:12]
+    T = len(ms)
+    bits = np.array([groups[m][rng.integers(len(groups[m]))] for m in ms])
+    k = _keys_from_bits(bits, 16, rng)[None, None]         # [1,1,T,16]
+    q = rng.standard_normal((1, 1, T, 16))
+    q[0, 0, 3] = k[0, 0, 1]                                 # a query that hits an earlier key
+    v = rng.standard_normal((1, 1, T, 5))
+    l = rng.standard_normal((1, 1, T))
+    y, W = O.delta_forward(q, k, v, l, None, nu=1)
+    fk, fq = O.dpfp(k, 1)[0, 0], O.dpfp(q, 1)[0, 0]
+    assert np.count_nonzero(fk @ fk.T - np.diag(np.diag(fk @ fk.T))) == 0
+    beta = 1.0 / (1.0 + np.exp(-l[0, 0]))
+    Y = np.tril(fq @ fk.T) @ (beta[:, None] * v[0, 0])
+    np.testing.assert_allclose(y[0, 0], Y, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(W[0, 0], (beta[:, None] * v[0, 0]).T @ fk, rtol=1e-12, atol=1e-15)
+
+
+def pin_repeated_key_is_ema(O):
+    """The same one-hot key f = c e_m at every step: column m of W follows
+    w_t = (1 - beta_t c^2) w_{t-1} + beta_t c v_t and every other column keeps its W0 value."""
+    rng = np.random.default_rng(25)
+    groups = onehot_patterns(16)
+    m = sorted(groups)[5]
+    bits = np.array([groups[m][0]] * 20)
+    k = _keys_from_bits(bits[:1], 16, rng).repeat(20, axis=0)[None, None]
+    T = 20
+    q = rng.standard_normal((1, 1, T, 16))
+    v = rng.standard_normal((1, 1, T, 4))
+    l = rng.standard_normal((1, 1, T)) + 1.0
+    W0 = rng.standard_normal((1, 1, 4, 32))
+    y, W = O.delta_forward(q, k, v, l, W0, nu=1)
+    c = O.dpfp(k[0, 0, :1], 1)[0, m]
+    beta = 1.0 / (1.0 + np.exp(-l[0, 0]))
+    w = W0[0, 0, :, m].copy()
+    for t in range(T):
+        w = (1.0 - beta[t] * c * c) * w + beta[t] * c * v[0, 0, t]
+    np.testing.assert_allclose(W[0, 0, :, m], w, rtol=1e-12, atol=1e-14)
+    others = [d for d in range(32) if d != m]
+    np.testing.assert_array_equal(W[0, 0][:, others], W0[0, 0][:, others])
+
+
+def pin_hand_recurrence(O):
+    """Two steps worked by hand (tests/golden/recurrence_hand.txt): d_k = 2, nu = 1, d_v = 1,
+    k = q = [1, -2] both steps (phi = c e_0 with c = 2/(2+eps)), beta_logit = 0 (beta = 1/2),
+    v = 1 then 3, W0 = 0.  Then y_1 = c^2/2, W_1 = c/2, y_2 = 2c^2 - c^4/4, W_2 = 2c - c^3/4."""
+    with open(os.path.join(GOLDEN, "recurrence_hand.txt")) as f:
+        rows = [ln.split("#", 1)[0].split(None, 1) for ln in f]
+    rows = [r for r in rows if r]
+    c = Fraction(2) / (Fraction(2) + Fraction(1, 10 ** 6))
+    env = {"c": c}
+    k = np.array([[[[1.0, -2.0], [1.0, -2.0]]]])
+    y, W = O.delta_forward(k, k, np.array([[[[1.0], [3.0]]]]), np.zeros((1, 1, 2)), None, nu=1)
+    got = {"y1": y[0, 0, 0, 0], "y2": y[0, 0, 1, 0], "W2_0": W[0, 0, 0, 0],
+           "W2_1": W[0, 0, 0, 1], "W2_2": W[0, 0, 0, 2], "W2_3": W[0, 0, 0, 3]}
+    for name, expr in rows:
+        want = float(eval(expr, {"__builtins__": {}}, env))
+        assert math.isclose(got[name], want, rel_tol=1e-14, abs_tol=0.0), (name, got[name], want)
+
+
+def pin_linearity(O):
+    """(y, W_final) is linear in (v, W0) jointly for fixed q, k, beta."""
+    rng = np.random.default_rng(26)
+    q, k, v1, l, A = _rand_case(rng, 2, 2, 17, 8, 6, 2)
+    v2 = rng.standard_normal(v1.shape)
+    Bm = 0.1 * rng.standard_normal(A.shape)
+    y1, W1 = O.delta_forward(q, k, v1, l, A, nu=2)
+    y2, W2 = O.delta_forward(q, k, v2, l, Bm, nu=2)
+    y3, W3 = O.delta_forward(q, k, v1 - 2.5 * v2, l, A - 2.5 * Bm, nu=2)
+    np.testing.assert_allclose(y3, y1 - 2.5 * y2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(W3, W1 - 2.5 * W2, rtol=1e-11, atol=1e-13)
+
+
+def pin_contraction(O):
+    """||phi||_2 <= ||phi||_1 < 1, so each step's transition I - beta f f^T has eigenvalues in
+    [0, 1]: a perturbation of W0 never grows in Frobenius norm, and it shrinks over many steps."""
+    rng = np.random.default_rng(27)
+    q, k, v, l, W0 = _rand_case(rng, 1, 3, 200, 4, 3, 1)
+    d = rng.standard_normal(W0.shape)
+    _, Wa = O.delta_forward(q, k, v, l, W0, nu=1)
+    _, Wb = O.delta_forward(q, k, v, l, W0 + d, nu=1)
+    for h in range(3):
+        n0 = np.linalg.norm(d[0, h])
+        n1 = np.linalg.norm(Wb[0, h] - Wa[0, h])
+        assert n1 <= n0 * (1 + 1e-12) and n1 < 0.9 * n0, (h, n0, n1)
+
+
+def pin_segmentation_and_steps(O):
+    """forward(T1) then forward(T2, W0 = W_final) equals forward(T1 + T2), and equals T
+    successive single-token steps carrying W."""
+    rng = np.random.default_rng(28)
+    q, k, v, l, W0 = _rand_case(rng, 2, 3, 23, 8, 4, 2)
+    y, W = O.delta_forward(q, k, v, l, W0, nu=2)
+    ya, Wa = O.delta_forward(q[:, :, :10], k[:, :, :10], v[:, :, :10], l[:, :, :10], W0, nu=2)
+    yb, Wb = O.delta_forward(q[:, :, 10:], k[:, :, 10:], v[:, :, 10:], l[:, :, 10:], Wa, nu=2)
+    np.testing.assert_allclose(np.concatenate([ya, yb], axis=2), y, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(Wb, W, rtol=1e-13, atol=1e-15)
+    Ws = W0.copy()
+    for t in range(23):
+        ys, Ws = O.delta_step(q[:, :, t], k[:, :, t], v[:, :, t], l[:, :, t], Ws, nu=2)
+        np.testing.assert_allclose(ys, y[:, :, t], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(Ws, W, rtol=1e-13, atol=1e-15)
+
+
+def pin_permutation_equivariance(O):
+    """Permuting v's components permutes the rows of W and the components of y; permuting
+    (batch, head) slices permutes the outputs (slices are independent)."""
+    rng = np.random.default_rng(29)
+    q, k, v, l, W0 = _rand_case(rng, 2, 3, 11, 8, 6, 1)
+    y, W = O.delta_forward(q, k, v, l, W0, nu=1)
+    pv = rng.permutation(6)
+    yp, Wp = O.delta_forward(q, k, v[..., pv], l, W0[:, :, pv], nu=1)
+    np.testing.assert_allclose(yp, y[..., pv], rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(Wp, W[:, :, pv], rtol=1e-14, atol=1e-16)
+    ph = rng.permutation(3)
+    yh, Wh = O.delta_forward(q[:, ph], k[:, ph], v[:, ph], l[:, ph], W0[:, ph], nu=1)
+    np.testing.assert_array_equal(yh, y[:, ph])
+    np.testing.assert_array_equal(Wh, W[:, ph])
+
+
+def pin_matches_numpy_twin(O):
+    """Two independent transcriptions (explicit C indices vs. the roll/concat NumPy form)."""
+    from oracle import twin
+    rng = np.random.default_rng(30)
+    for (B, H, T, d_k, d_v, nu) in [(1, 1, 64, 16, 16, 1), (1, 2, 40, 64, 64, 1),
+                                    (2, 1, 33, 8, 5, 3)]:
+        q, k, v, l, W0 = _rand_case(rng, B, H, T, d_k, d_v, nu)
+        y, W = O.delta_forward(q, k, v, l, W0, nu=nu)
+        y2, W2 = twin.delta_forward(q, k, v, l, W0, nu=nu)
+        np.testing.assert_allclose(y, y2, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(W, W2, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(O.dpfp(k, nu), twin.dpfp(k, nu), rtol=0, atol=1e-15)
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -1,0 +1,137 @@
+/*
+ * fwa.h -- C ABI of the MI355X (gfx950) fast-weight delta-rule layer with DPFP projection.
+ *
+ * The method (sources are web pages, cited by title and section):
+ *   [FWT] "Fast Weights Transformer" technical guide for the labml annotated implementation,
+ *         xdnf.cn/news/308600;
+ *   [FWA] "Deep dive into Fast Weight Attention (lucidrains)", gitcode.csdn.net;
+ *   [TRF] "Transformer", wineandchord.com/llm/architecture/transformer/.
+ *
+ *   DPFP    phi(k): x = relu([k, -k]) (length 2*d_k); for shift i = 1..nu the block at
+ *           offset (i-1)*2*d_k holds x[j] * x[(j - i) mod 2*d_k] (x times x rolled by +i);
+ *           then phi = raw / (sum(raw) + 1e-6).  D = d_dot = 2*d_k*nu.
+ *           [FWT] sections "DPFP / projection formula and hyper-parameters", "DPFP /
+ *           normalisation".
+ *   step    per (batch, head), with beta = sigmoid(beta_logit):
+ *             v_bar = W phi(k);  W <- W + beta (v - v_bar) phi(k)^T;  y = W phi(q)
+ *           (the read uses the W just written).  [FWT] sections "FastWeightsAttention /
+ *           update formula" and "FastWeightsAttention / module structure and source
+ *           walkthrough".  No 1/sqrt(d) scale and no z normaliser.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library allocates
+ *     nothing, keeps no state between calls and never synchronises `stream`.  Every launch
+ *     goes on `stream` (0 = the legacy default stream).  FWA_OK means "enqueued".
+ *   - Layouts are row-major and contiguous (the [B, H, T, d] convention of [TRF], section
+ *     "Scaled dot-product attention").  The fast-weight memory W is [B, H, d_v, D] fp32
+ *     (d_value x d_key orientation of [FWT], module walkthrough).
+ *   - `dtype` is the element type of q, k, v, beta_logit, y and phi (FWA_F32 or FWA_BF16);
+ *     W is always fp32.  Arithmetic is fp32 with fp32 state; bf16 results are rounded to
+ *     nearest-even.
+ *   - Arguments are checked on the host before anything is launched.  On any error nothing
+ *     is launched and no output is written:
+ *       FWA_ERR_INVALID_ARG   a required pointer is NULL, a size is negative, d_k < 1,
+ *                             d_v < 1, nu outside [1, 2*d_k - 1] (the range [FWT] gives for
+ *                             nu), chunk not in {16, 32, 64, 128}, an unknown dtype, or a
+ *                             pointer not aligned to 16 bytes;
+ *       FWA_ERR_UNSUPPORTED   valid arguments outside the shapes the kernels implement
+ *                             (listed per entry point), or sizes whose index arithmetic would
+ *                             overflow 64 bits;
+ *       FWA_ERR_HIP           the HIP runtime rejected a launch (the message is available
+ *                             from fwa_last_error()).
+ *   - Inputs holding NaN or Inf give unspecified values but never a fault.
+ */
+#ifndef FWA_H
+#define FWA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FWA_OK = 0,
+    FWA_ERR_INVALID_ARG = 1,
+    FWA_ERR_UNSUPPORTED = 2,
+    FWA_ERR_HIP = 3
+} fwa_status;
+
+typedef enum {
+    FWA_F32 = 0,
+    FWA_BF16 = 1
+} fwa_dtype;
+
+/*
+ * fwa_dpfp -- phi[n, :] = DPFP(x[n, :]) for n in [0, n_vec).
+ *   [FWT] sections "DPFP / projection formula and hyper-parameters" and "DPFP /
+ *   normalisation" (eps = 1e-6, added to the sum).
+ *   x    [n_vec, d_k]        input, `dtype`
+ *   phi  [n_vec, 2*d_k*nu]   output, `dtype`; entry (i-1)*2*d_k + j is the shift-i product
+ *                            at position j.  Exact zeros are written as +0.0.
+ *   n_vec == 0 is a no-op.
+ *   Implemented shapes: d_k in {16, 32, 64, 128}, any valid nu.
+ */
+fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
+                    fwa_dtype dtype, hipStream_t stream);
+
+/*
+ * fwa_delta_forward -- causal forward of the delta rule over T steps for every (b, h),
+ * starting from W0 and returning the final memory.
+ *   [FWT] section "FastWeightsAttention / module structure and source walkthrough" (the
+ *   per-step loop this reproduces), [FWA] section 4.2 (chunked processing that passes the
+ *   memory between chunks and returns it).
+ *   q, k        [B, H, T, d_k]  `dtype`
+ *   v           [B, H, T, d_v]  `dtype`
+ *   beta_logit  [B, H, T]       `dtype`  (pre-sigmoid; beta = sigmoid(beta_logit))
+ *   W0          [B, H, d_v, D]  fp32, or NULL for a zero initial memory ([FWT]'s default)
+ *   y           [B, H, T, d_v]  `dtype`, output: y_t = W_t phi(q_t) after the step-t write
+ *   W_final     [B, H, d_v, D]  fp32 output, or NULL to skip it; may equal W0 (in-place
+ *                               carry), must not overlap any other argument
+ *   chunk       rows per chunk of the chunk-parallel evaluation, one of {16, 32, 64, 128}.
+ *               It changes only the rounding order: results agree for every chunk within
+ *               the stated tolerances.
+ *   T == 0 leaves y untouched and writes W_final = W0 (or zeros).  B*H == 0 is a no-op.
+ *   T need not be a multiple of chunk.
+ *   Implemented shapes: d_k in {16, 32, 64}, d_v in {16, 32, 64}, D = 2*d_k*nu <= 512, and
+ *   the chunk's on-chip working set (3*chunk*D elements plus chunk-sized scratch) within the
+ *   160 KiB of LDS of one compute unit; other valid shapes give FWA_ERR_UNSUPPORTED.
+ */
+fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
+                             const void* beta_logit, const float* W0, void* y, float* W_final,
+                             int B, int H, int T, int d_k, int d_v, int nu, int chunk,
+                             fwa_dtype dtype, hipStream_t stream);
+
+/*
+ * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory
+ * carried in and out through W, updated in place.
+ *   [FWT] sections "token_wise variant" and "Inference and sampling" (each new token updates
+ *   the carried fast weights with no recomputation over the history); [TRF] section
+ *   "Complexity" (decode streams its state, so it is bandwidth-bound).
+ *   q, k        [B, H, d_k]     `dtype`
+ *   v           [B, H, d_v]     `dtype`
+ *   beta_logit  [B, H]          `dtype`
+ *   W           [B, H, d_v, D]  fp32, read and written in place (read once, written once)
+ *   y           [B, H, d_v]     `dtype`, output
+ *   B*H == 0 is a no-op.  y must not overlap W or the inputs.
+ *   Implemented shapes: d_k in {16, 32, 64, 128}, d_v >= 1, D = 2*d_k*nu <= 1024.
+ */
+fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,
+                          float* W, void* y, int B, int H, int d_k, int d_v, int nu,
+                          fwa_dtype dtype, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* fwa_status_string(fwa_status s);
+
+/* Detail of the most recent non-OK status returned on the calling thread ("" if none). */
+const char* fwa_last_error(void);
+
+/* Version of this ABI, as major * 10000 + minor * 100 + patch. */
+int fwa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FWA_H */

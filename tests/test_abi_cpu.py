@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: the library loads, exports every function include/fwa.h declares,
+and rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from weight_linear_attention_amd import fwa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fwa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fwa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_step", "fwa_status_string",
+              "fwa_last_error", "fwa_version"):
+        assert n in names
+    assert set(names) == set(fwa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = fwa.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fwa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (fwa_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings():
+    L = fwa.lib()
+    assert L.fwa_version() == 10000
+    assert L.fwa_status_string(0) == b"FWA_OK"
+    assert L.fwa_status_string(1) == b"FWA_ERR_INVALID_ARG"
+    assert L.fwa_status_string(2) == b"FWA_ERR_UNSUPPORTED"
+    assert L.fwa_status_string(3) == b"FWA_ERR_HIP"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)        # aligned, never dereferenced: every call below fails validation first
+MISALIGNED = P(0x10008)
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((None, None, 10, 16, 1, 0, None), 1, "NULL"),
+    ((FAKE, FAKE, -1, 16, 1, 0, None), 1, "n_vec"),
+    ((FAKE, FAKE, 10, 0, 1, 0, None), 1, "d_k"),
+    ((FAKE, FAKE, 10, 16, 32, 0, None), 1, "nu"),
+    ((FAKE, FAKE, 10, 16, 0, 0, None), 1, "nu"),
+    ((FAKE, FAKE, 10, 16, 1, 7, None), 1, "dtype"),
+    ((MISALIGNED, FAKE, 10, 16, 1, 0, None), 1, "aligned"),
+    ((FAKE, FAKE, 10, 24, 1, 0, None), 2, "d_k"),
+    ((FAKE, FAKE, 10, 16, 1, 0, None), 1, "overlap"),
+])
+def test_dpfp_rejects(args, status, msg):
+    L = fwa.lib()
+    assert L.fwa_dpfp(*args) == status
+    assert msg in L.fwa_last_error().decode()
+
+
+def test_dpfp_zero_vectors_is_noop():
+    assert fwa.lib().fwa_dpfp(None, None, 0, 16, 1, 0, None) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=P(0x20000), v=P(0x30000), bl=P(0x40000), W0=None, y=P(0x50000),
+             Wf=None, B=1, H=1, T=8, d_k=16, d_v=16, nu=1, chunk=64, dtype=0)
+    a.update(kw)
+    return fwa.lib().fwa_delta_forward(a["q"], a["k"], a["v"], a["bl"], a["W0"], a["y"], a["Wf"],
+                                       a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["nu"],
+                                       a["chunk"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "NULL"),
+    (dict(B=-1), 1, "negative"),
+    (dict(T=-3), 1, "negative"),
+    (dict(d_v=0), 1, "d_v"),
+    (dict(nu=40), 1, "nu"),
+    (dict(chunk=48), 1, "chunk"),
+    (dict(dtype=3), 1, "dtype"),
+    (dict(y=MISALIGNED), 1, "aligned"),
+    (dict(y=FAKE), 1, "overlap"),
+    (dict(Wf=P(0x20000)), 1, "overlap"),
+    (dict(d_k=128), 2, "d_k"),
+    (dict(d_v=48), 2, "d_v"),
+    (dict(d_k=64, nu=5), 2, "512"),
+    (dict(d_k=64, nu=3, chunk=128, dtype=1), 2, "on-chip"),
+])
+def test_forward_rejects(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+def test_forward_empty_batch_is_noop():
+    assert _fwd(B=0, q=None, k=None, v=None, bl=None, y=None) == 0
+    assert _fwd(H=0) == 0
+
+
+def _step(**kw):
+    a = dict(q=FAKE, k=P(0x20000), v=P(0x30000), bl=P(0x40000), W=P(0x100000), y=P(0x50000),
+             B=2, H=2, d_k=16, d_v=16, nu=1, dtype=0)
+    a.update(kw)
+    return fwa.lib().fwa_delta_step(a["q"], a["k"], a["v"], a["bl"], a["W"], a["y"], a["B"],
+                                    a["H"], a["d_k"], a["d_v"], a["nu"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(W=None), 1, "NULL"),
+    (dict(H=-1), 1, "negative"),
+    (dict(nu=0), 1, "nu"),
+    (dict(dtype=2), 1, "dtype"),
+    (dict(W=MISALIGNED), 1, "aligned"),
+    (dict(y=P(0x100000)), 1, "overlap"),
+    (dict(d_k=24), 2, "d_k"),
+    (dict(d_k=64, nu=5), 2, "row layout"),
+])
+def test_step_rejects(kw, status, msg):
+    assert _step(**kw) == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+def test_step_empty_batch_is_noop():
+    assert _step(B=0, q=None, W=None) == 0

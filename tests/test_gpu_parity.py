@@ -1,0 +1,226 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Bars: fp32 inputs 1e-4, bf16 inputs 2e-2 (fp32 state), normwise per (b, h) slice; the DPFP
+zero/nonzero pattern must match the oracle's sign predicate bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import TOL, log, normwise, oracle_forward
+from weight_linear_attention_amd import fwa
+from weight_linear_attention_amd.synthetic import (make_decode_inputs, make_inputs, to_f64,
+                                                   workload)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _dev(inp):
+    return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+
+
+def _forward(inp_d, nu, chunk, W0=True):
+    y, Wf = fwa.delta_forward(inp_d["q"], inp_d["k"], inp_d["v"], inp_d["beta_logit"],
+                              inp_d["W0"] if W0 else None, chunk=chunk, nu=nu)
+    torch.cuda.synchronize()
+    return y, Wf
+
+
+# ------------------------------------------------------------------------------ DPFP
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d_k,nu", [(16, 1), (16, 3), (32, 2), (64, 1), (64, 2), (64, 3),
+                                    (128, 1), (64, 7), (16, 31)])
+def test_dpfp_parity_and_mask(dtype, d_k, nu):
+    log(f"dpfp dtype={dtype} d_k={d_k} nu={nu}")
+    g = torch.Generator().manual_seed(d_k * 100 + nu)
+    n_vec = 1000 + 37                        # several workgroup rounds plus a ragged tail
+    x = torch.randn(n_vec, d_k, generator=g).to(dtype)
+    phi = fwa.dpfp(x.to(DEV), nu)
+    torch.cuda.synchronize()
+    got = to_f64(phi)
+    ref = oracle.dpfp(to_f64(x), nu)
+    assert got.shape == (n_vec, 2 * d_k * nu)
+    assert np.array_equal(got != 0.0, oracle.dpfp_mask(to_f64(x), nu))
+    assert np.array_equal(got != 0.0, ref != 0.0)
+    assert not np.signbit(got).any()             # zeros are +0.0
+    err = normwise(got, ref, 1)
+    log(f"  normwise err {err:.3e}")
+    assert err <= (1e-6 if dtype == torch.float32 else 4e-3)
+
+
+def test_dpfp_empty_and_full_size_sample():
+    x = torch.empty(0, 64, device=DEV)
+    assert fwa.dpfp(x, 3).shape == (0, 384)
+    # the q tensor of the 8 x 16 x 16384 workload (2M vectors), checked on a random sample
+    w = workload("b8_h16_t16384_d64_nu3_bf16")
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(w.B * w.H * w.T, w.d_k, generator=g).to(torch.bfloat16)
+    phi = fwa.dpfp(x.to(DEV), w.nu)
+    torch.cuda.synchronize()
+    idx = torch.randint(0, x.shape[0], (2000,), generator=g)
+    got = to_f64(phi[idx.to(DEV)])
+    ref = oracle.dpfp(to_f64(x[idx]), w.nu)
+    assert np.array_equal(got != 0.0, ref != 0.0)
+    assert normwise(got, ref, 1) <= 4e-3
+
+
+# ------------------------------------------------------------------------------ forward
+
+FWD_CASES = [
+    # name, overrides
+    ("tiny_t64_d16_nu1_f32", {}),
+    ("tiny_t64_d16_nu1_f32", {"chunk": 16}),
+    ("tiny_t64_d16_nu1_f32", {"chunk": 32, "T": 77}),
+    ("h8_t1024_d64_nu1_f32", {}),
+    ("h8_t1024_d64_nu1_f32", {"chunk": 32, "T": 1000}),
+    ("h8_t1024_d64_nu1_f32", {"T": 300, "w0_std": 0.05, "nu": 2, "chunk": 32}),
+    ("h8_t1024_d64_nu1_f32", {"T": 200, "d_k": 32, "nu": 3, "d_v": 32}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"T": 1000, "chunk": 32}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 333, "chunk": 16, "d_v": 16}),
+]
+
+
+@pytest.mark.parametrize("name,ov", FWD_CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(FWD_CASES)])
+def test_forward_parity(name, ov):
+    w = workload(name, **ov)
+    log(f"forward {w}")
+    inp = make_inputs(w)
+    y, Wf = _forward(_dev(inp), w.nu, w.chunk)
+    yr, Wr = oracle_forward(inp, w.nu)
+    ey, ew = normwise(to_f64(y), yr, 2), normwise(to_f64(Wf), Wr, 2)
+    log(f"  y err {ey:.3e}  W_final err {ew:.3e}")
+    tol = TOL[w.torch_dtype]
+    assert ey <= tol and ew <= tol
+
+
+def test_forward_full_size_long_sequence_sampled():
+    """The 8 x 16 x 16384 (D 384, bf16) workload at full size, chunk 64, in the launch
+    configuration the benchmark uses; the oracle checks 6 sampled (b, h) slices end to end."""
+    w = workload("b8_h16_t16384_d64_nu3_bf16")
+    log(f"forward full {w}")
+    inp = make_inputs(w)
+    y, Wf = _forward(_dev(inp), w.nu, 64)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(Wf).all()
+    picks = [(0, 0), (3, 7), (7, 15), (5, 2), (1, 11), (6, 9)]
+    yr, Wr = oracle_forward(inp, w.nu, bh_index=picks)
+    sel = tuple(torch.tensor(ix) for ix in zip(*picks))
+    ey = normwise(to_f64(y.cpu()[sel])[None], yr, 2)
+    ew = normwise(to_f64(Wf.cpu()[sel])[None], Wr, 2)
+    log(f"  sampled y err {ey:.3e}  W_final err {ew:.3e}")
+    assert ey <= 2e-2 and ew <= 2e-2
+
+
+def test_forward_T0_and_empty():
+    w = workload("h8_t1024_d64_nu1_f32", T=0, w0_std=0.1)
+    inp = _dev(make_inputs(w))
+    y, Wf = _forward(inp, w.nu, 64)
+    assert torch.equal(Wf, inp["W0"])
+    y, Wf = _forward(inp, w.nu, 64, W0=False)
+    assert torch.count_nonzero(Wf) == 0
+    w = workload("h8_t1024_d64_nu1_f32", B=0)
+    inp = _dev(make_inputs(w))
+    y, Wf = _forward(inp, w.nu, 64)
+    assert y.numel() == 0
+
+
+def test_forward_in_place_carry_and_segments():
+    """forward(T1) then forward(T2) with W0 = W_final (in place) equals forward(T1 + T2)."""
+    w = workload("b4_h8_t4096_d64_nu2_bf16_carried", T=700, B=2)
+    inp = _dev(make_inputs(w))
+    y, Wf = _forward(inp, w.nu, 64)
+    W = inp["W0"].clone()
+    ys = []
+    for lo, hi in [(0, 300), (300, 301), (301, 700)]:
+        sl = {k: inp[k][:, :, lo:hi].contiguous() for k in ("q", "k", "v", "beta_logit")}
+        yy, _ = fwa.delta_forward(sl["q"], sl["k"], sl["v"], sl["beta_logit"], W, chunk=64,
+                                  nu=w.nu, W_final=W)
+        ys.append(yy)
+    torch.cuda.synchronize()
+    e1 = normwise(to_f64(torch.cat(ys, 2)), to_f64(y), 2)
+    e2 = normwise(to_f64(W), to_f64(Wf), 2)
+    log(f"  segmented vs whole: y {e1:.3e} W {e2:.3e}")
+    assert e1 <= 2e-2 and e2 <= 2e-2
+
+
+def test_forward_chunk_independence_and_determinism():
+    w = workload("h8_t1024_d64_nu1_f32", T=500, w0_std=0.02)
+    inp = _dev(make_inputs(w))
+    outs = {c: _forward(inp, w.nu, c) for c in (16, 32, 64)}
+    for c in (16, 32):
+        assert normwise(to_f64(outs[c][0]), to_f64(outs[64][0]), 2) <= 1e-4
+        assert normwise(to_f64(outs[c][1]), to_f64(outs[64][1]), 2) <= 1e-4
+    y2, W2 = _forward(inp, w.nu, 64)
+    assert torch.equal(y2, outs[64][0]) and torch.equal(W2, outs[64][1])   # run to run
+
+
+def test_forward_unsupported_shapes_raise():
+    q = torch.zeros(1, 1, 4, 64, device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(fwa.FwaError) as e:          # D = 2*64*5 = 640 > 512
+        fwa.delta_forward(q, q, q, torch.zeros(1, 1, 4, device=DEV, dtype=torch.bfloat16),
+                          nu=5)
+    assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
+    with pytest.raises(fwa.FwaError) as e:
+        fwa.delta_forward(q, q, q, torch.zeros(1, 1, 4, device=DEV, dtype=torch.bfloat16),
+                          chunk=48)
+    assert e.value.status == fwa.FWA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("dtype,d_k,nu,d_v", [(torch.float32, 64, 1, 64),
+                                              (torch.bfloat16, 64, 3, 64),
+                                              (torch.float32, 16, 1, 16),
+                                              (torch.float32, 128, 2, 48),
+                                              (torch.bfloat16, 32, 4, 24)])
+def test_step_parity_many_steps(dtype, d_k, nu, d_v):
+    w = workload("decode_b256_h8_d64_nu1_f32", B=8, H=3, d_k=d_k, d_v=d_v, nu=nu,
+                 dtype="bf16" if dtype == torch.bfloat16 else "f32", w0_std=0.05)
+    steps = 40
+    log(f"step {w} steps={steps}")
+    inp = make_decode_inputs(w, steps=steps)
+    dev = _dev(inp)
+    W = dev["W0"].clone()
+    ys = []
+    for s in range(steps):
+        ys.append(fwa.delta_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["beta_logit"][s], W,
+                                 nu=nu))
+    torch.cuda.synchronize()
+    # the oracle runs the same tokens as one T = steps sequence
+    perm = lambda t: to_f64(t).transpose(1, 2, 0, *range(3, t.dim()))
+    yr, Wr = oracle.delta_forward(perm(inp["q"]), perm(inp["k"]), perm(inp["v"]),
+                                  to_f64(inp["beta_logit"]).transpose(1, 2, 0),
+                                  to_f64(inp["W0"]), nu=nu)
+    ey = normwise(to_f64(torch.stack(ys, 2)), yr, 2)
+    ew = normwise(to_f64(W), Wr, 2)
+    log(f"  y err {ey:.3e}  W err {ew:.3e}")
+    assert ey <= TOL[dtype] and ew <= TOL[dtype]
+
+
+def test_step_matches_forward_full_decode_shape():
+    """The 256 x 8 (D 128) decode state at full size: 16 steps through fwa_delta_step equal
+    fwa_delta_forward over the same 16 tokens, and a sample of slices matches the oracle."""
+    w = workload("decode_b256_h8_d64_nu1_f32")
+    inp = make_decode_inputs(w, steps=16)
+    dev = _dev(inp)
+    W = dev["W0"].clone()
+    ys = [fwa.delta_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["beta_logit"][s], W)
+          for s in range(16)]
+    perm = lambda t: t.permute(1, 2, 0, *range(3, t.dim())).contiguous()
+    yf, Wf = fwa.delta_forward(perm(dev["q"]), perm(dev["k"]), perm(dev["v"]),
+                               dev["beta_logit"].permute(1, 2, 0).contiguous(), dev["W0"],
+                               chunk=16)
+    torch.cuda.synchronize()
+    ys = torch.stack(ys, 2)
+    assert normwise(to_f64(ys), to_f64(yf), 2) <= 1e-4
+    assert normwise(to_f64(W), to_f64(Wf), 2) <= 1e-4
+    picks = [0, 77, 1000, 2047]
+    flat = lambda t: to_f64(perm(t)).reshape(1, 2048, *perm(t).shape[2:])[:, picks]
+    yr, Wr = oracle.delta_forward(flat(inp["q"]), flat(inp["k"]), flat(inp["v"]),
+                                  to_f64(inp["beta_logit"].permute(1, 2, 0)).reshape(1, 2048, 16)[:, picks],
+                                  to_f64(inp["W0"]).reshape(1, 2048, 64, 128)[:, picks])
+    assert normwise(to_f64(ys).reshape(1, 2048, 16, 64)[:, picks], yr, 2) <= 1e-4
+    assert normwise(to_f64(W).reshape(1, 2048, 64, 128)[:, picks], Wr, 2) <= 1e-4

@@ -1,0 +1,168 @@
+// Standalone DPFP kernel: phi[n, :] = DPFP(x[n, :]).
+//
+// DPFP ("Fast Weights Transformer" guide, xdnf.cn/news/308600, sections "DPFP / projection
+// formula and hyper-parameters" and "DPFP / normalisation"): x = relu([k, -k]); for shift
+// i = 1..nu the block at offset (i-1)*2*d_k holds x[j] * x[(j - i) mod 2*d_k]; the whole vector
+// is divided by (sum + 1e-6).
+//
+// The kernel is HBM-bound (it reads d_k and writes 2*d_k*nu elements per vector), so it is
+// organised around wide, coalesced global traffic:
+//   - a team of TL = d_k/4 lanes owns one vector; each lane loads 4 consecutive inputs
+//     (one 16-byte fp32 or 8-byte bf16 load) and stores 16 bytes per output group
+//     (8 bf16 or 4 fp32 outputs), so a team writes 256 contiguous bytes per store round;
+//   - the team stages relu([k, -k]) twice over (4*d_k floats) in LDS so that a rolled window
+//     x[j - i .. j - i + E) is a plain contiguous read with no modular index;
+//   - the sum is reduced across the team with lane shuffles; exact zeros come out as +0.0.
+#include "fwa_common.h"
+#include "fwa_internal.h"
+
+namespace fwa {
+
+template <bool BF16, int DK>
+__global__ __launch_bounds__(256) void dpfp_kernel(const void* __restrict__ x,
+                                                    void* __restrict__ phi, int64_t n_vec,
+                                                    int nu) {
+    constexpr int TL = DK / 4;                // lanes per vector
+    constexpr int TEAMS = 256 / TL;           // vectors per workgroup round
+    constexpr int E = BF16 ? 8 : 4;           // outputs per 16-byte store
+    constexpr int XE = 4 * DK + 4;            // staged floats per vector (+4 spreads banks)
+    constexpr int GMAX = 32 / E;              // output groups a lane keeps in registers
+    __shared__ __attribute__((aligned(16))) float xe_all[TEAMS * XE];
+
+    const int tid = threadIdx.x;
+    const int team = tid / TL, lt = tid % TL;
+    float* xe = xe_all + team * XE;
+    const int two_dk = 2 * DK;
+    const int D = two_dk * nu;
+    const int gpl = D / (E * TL);             // output groups per lane: nu (bf16), 2*nu (fp32)
+
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * TEAMS; base < n_vec;
+         base += static_cast<int64_t>(gridDim.x) * TEAMS) {
+        const int64_t n = base + team;
+        const bool valid = n < n_vec;
+        float kv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (valid) {
+            if constexpr (BF16) {
+                const uint2 raw = *reinterpret_cast<const uint2*>(
+                    static_cast<const u16*>(x) + n * DK + 4 * lt);
+                kv[0] = __uint_as_float(raw.x << 16);
+                kv[1] = __uint_as_float(raw.x & 0xffff0000u);
+                kv[2] = __uint_as_float(raw.y << 16);
+                kv[3] = __uint_as_float(raw.y & 0xffff0000u);
+            } else {
+                const float4 raw = *reinterpret_cast<const float4*>(
+                    static_cast<const float*>(x) + n * DK + 4 * lt);
+                kv[0] = raw.x; kv[1] = raw.y; kv[2] = raw.z; kv[3] = raw.w;
+            }
+        }
+        // xe[m] = relu([k, -k])[m mod 2*d_k] for m in [0, 4*d_k)
+        float4 pos = make_float4(relu(kv[0]), relu(kv[1]), relu(kv[2]), relu(kv[3]));
+        float4 neg = make_float4(relu(-kv[0]), relu(-kv[1]), relu(-kv[2]), relu(-kv[3]));
+        *reinterpret_cast<float4*>(xe + 4 * lt) = pos;
+        *reinterpret_cast<float4*>(xe + DK + 4 * lt) = neg;
+        *reinterpret_cast<float4*>(xe + two_dk + 4 * lt) = pos;
+        *reinterpret_cast<float4*>(xe + two_dk + DK + 4 * lt) = neg;
+        __syncthreads();
+
+        // Output group g = lt + TL*m covers positions p0 = E*g .. E*g + E-1, all inside the
+        // block of shift i = p0 / (2*d_k) + 1 (E divides 2*d_k).
+        if (gpl <= GMAX) {
+            float prod[GMAX * E];
+            float S = 0.0f;
+#pragma unroll
+            for (int m = 0; m < GMAX; ++m) {
+                if (m < gpl) {
+                    const int p0 = E * (lt + TL * m);
+                    const int i = p0 / two_dk + 1;
+                    const int j0 = p0 - (i - 1) * two_dk;
+                    const float* a = xe + j0;
+                    const float* b = xe + j0 - i + two_dk;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        prod[m * E + e] = a[e] * b[e];
+                        S += prod[m * E + e];
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = TL / 2; off >= 1; off >>= 1) S += __shfl_xor(S, off, TL);
+            const float rs = 1.0f / (S + kDpfpEps);
+            if (valid) {
+#pragma unroll
+                for (int m = 0; m < GMAX; ++m) {
+                    if (m < gpl) {
+                        const int64_t p0 = static_cast<int64_t>(E) * (lt + TL * m);
+                        if constexpr (BF16) {
+                            uint4 o;
+                            o.x = pack_bf16x2(prod[m * E + 0] * rs, prod[m * E + 1] * rs);
+                            o.y = pack_bf16x2(prod[m * E + 2] * rs, prod[m * E + 3] * rs);
+                            o.z = pack_bf16x2(prod[m * E + 4] * rs, prod[m * E + 5] * rs);
+                            o.w = pack_bf16x2(prod[m * E + 6] * rs, prod[m * E + 7] * rs);
+                            *reinterpret_cast<uint4*>(static_cast<u16*>(phi) + n * D + p0) = o;
+                        } else {
+                            *reinterpret_cast<float4*>(static_cast<float*>(phi) + n * D + p0) =
+                                make_float4(prod[m * E + 0] * rs, prod[m * E + 1] * rs,
+                                            prod[m * E + 2] * rs, prod[m * E + 3] * rs);
+                        }
+                    }
+                }
+            }
+        } else {
+            // Large nu: first pass for the sum, second pass recomputes, scales and stores.
+            float S = 0.0f;
+            for (int m = 0; m < gpl; ++m) {
+                const int p0 = E * (lt + TL * m);
+                const int i = p0 / two_dk + 1;
+                const int j0 = p0 - (i - 1) * two_dk;
+#pragma unroll
+                for (int e = 0; e < E; ++e) S += xe[j0 + e] * xe[j0 + e - i + two_dk];
+            }
+#pragma unroll
+            for (int off = TL / 2; off >= 1; off >>= 1) S += __shfl_xor(S, off, TL);
+            const float rs = 1.0f / (S + kDpfpEps);
+            if (valid) {
+                for (int m = 0; m < gpl; ++m) {
+                    const int p0 = E * (lt + TL * m);
+                    const int i = p0 / two_dk + 1;
+                    const int j0 = p0 - (i - 1) * two_dk;
+                    float v[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) v[e] = xe[j0 + e] * xe[j0 + e - i + two_dk] * rs;
+                    if constexpr (BF16) {
+                        uint4 o;
+                        o.x = pack_bf16x2(v[0], v[1]);
+                        o.y = pack_bf16x2(v[2], v[3]);
+                        o.z = pack_bf16x2(v[4], v[5]);
+                        o.w = pack_bf16x2(v[6], v[7]);
+                        *reinterpret_cast<uint4*>(static_cast<u16*>(phi) + n * D + p0) = o;
+                    } else {
+                        *reinterpret_cast<float4*>(static_cast<float*>(phi) + n * D + p0) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // xe is rewritten by the next round
+    }
+}
+
+// Launch on `stream`; the caller has validated the arguments (d_k in {16,32,64,128}).
+hipError_t launch_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, bool bf16,
+                       hipStream_t stream) {
+    const int teams = 256 / (d_k / 4);
+    int64_t blocks = (n_vec + teams - 1) / teams;
+    if (blocks > 4096) blocks = 4096;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+#define FWA_DPFP_CASE(BF, DKV)                                                             \
+    if (bf16 == BF && d_k == DKV) {                                                        \
+        hipLaunchKernelGGL((dpfp_kernel<BF, DKV>), grid, block, 0, stream, x, phi, n_vec, nu); \
+        return hipGetLastError();                                                          \
+    }
+    FWA_DPFP_CASE(false, 16) FWA_DPFP_CASE(false, 32) FWA_DPFP_CASE(false, 64)
+    FWA_DPFP_CASE(false, 128) FWA_DPFP_CASE(true, 16) FWA_DPFP_CASE(true, 32)
+    FWA_DPFP_CASE(true, 64) FWA_DPFP_CASE(true, 128)
+#undef FWA_DPFP_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fwa

@@ -1,0 +1,201 @@
+// C ABI of the fast-weight delta-rule library: argument checks on the host, then one launch
+// on the caller's stream.  Every check runs before any HIP call, so an invalid call touches
+// neither the device nor the outputs.
+#include "fwa.h"
+#include "fwa_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fwa_status fail(fwa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fwa_status fail(fwa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+fwa_status ok() {
+    g_last_error.clear();
+    return FWA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [lo, lo + bytes) as an address range.
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool valid_dtype(fwa_dtype d) { return d == FWA_F32 || d == FWA_BF16; }
+int elem_bytes(fwa_dtype d) { return d == FWA_BF16 ? 2 : 4; }
+
+// a * b * c ... <= limit without overflow (all factors >= 0)
+bool mul_le(int64_t limit, std::initializer_list<int64_t> fs) {
+    int64_t acc = 1;
+    for (int64_t f : fs) {
+        if (f == 0) return true;
+        if (acc > limit / f) return false;
+        acc *= f;
+    }
+    return acc <= limit;
+}
+constexpr int64_t kIndexLimit = int64_t(1) << 61;
+
+fwa_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(FWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fwa_status_string(fwa_status s) {
+    switch (s) {
+        case FWA_OK: return "FWA_OK";
+        case FWA_ERR_INVALID_ARG: return "FWA_ERR_INVALID_ARG";
+        case FWA_ERR_UNSUPPORTED: return "FWA_ERR_UNSUPPORTED";
+        case FWA_ERR_HIP: return "FWA_ERR_HIP";
+    }
+    return "FWA_UNKNOWN_STATUS";
+}
+
+const char* fwa_last_error(void) { return g_last_error.c_str(); }
+
+int fwa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, fwa_dtype dtype,
+                    hipStream_t stream) {
+    if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: unknown dtype %d", dtype);
+    if (n_vec < 0) return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: n_vec < 0");
+    if (d_k < 1) return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: d_k < 1");
+    if (nu < 1 || nu > 2 * d_k - 1)
+        return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: nu=%d outside [1, 2*d_k-1]", nu);
+    if (n_vec == 0) return ok();
+    if (!x || !phi) return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: NULL pointer");
+    if (!aligned16(x) || !aligned16(phi))
+        return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: pointers must be 16-byte aligned");
+    if (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128)
+        return fail(FWA_ERR_UNSUPPORTED, "fwa_dpfp: d_k=%d not in {16,32,64,128}", d_k);
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
+    if (!mul_le(kIndexLimit, {n_vec, D}))
+        return fail(FWA_ERR_UNSUPPORTED, "fwa_dpfp: n_vec * D overflows the index range");
+    const int es = elem_bytes(dtype);
+    if (overlap(span(x, n_vec * d_k * es), span(phi, n_vec * D * es)))
+        return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: x and phi overlap");
+    return hip_status(fwa::launch_dpfp(x, phi, n_vec, d_k, nu, dtype == FWA_BF16, stream),
+                      "fwa_dpfp launch");
+}
+
+fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const void* beta_logit,
+                             const float* W0, void* y, float* W_final, int B, int H, int T,
+                             int d_k, int d_v, int nu, int chunk, fwa_dtype dtype,
+                             hipStream_t stream) {
+    const char* fn = "fwa_delta_forward";
+    if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (B < 0 || H < 0 || T < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H/T", fn);
+    if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
+    if (nu < 1 || nu > 2 * d_k - 1)
+        return fail(FWA_ERR_INVALID_ARG, "%s: nu=%d outside [1, 2*d_k-1]", fn, nu);
+    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
+        return fail(FWA_ERR_INVALID_ARG, "%s: chunk=%d not in {16,32,64,128}", fn, chunk);
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    if (BH == 0) return ok();
+    if (T > 0 && (!q || !k || !v || !beta_logit || !y))
+        return fail(FWA_ERR_INVALID_ARG, "%s: NULL input or output pointer", fn);
+    const void* ptrs[] = {q, k, v, beta_logit, W0, y, W_final};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p))
+            return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (d_k != 16 && d_k != 32 && d_k != 64)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: d_k=%d not in {16,32,64}", fn, d_k);
+    if (d_v != 16 && d_v != 32 && d_v != 64)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: d_v=%d not in {16,32,64}", fn, d_v);
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
+    if (D > 512) return fail(FWA_ERR_UNSUPPORTED, "%s: D=2*d_k*nu=%lld > 512", fn, (long long)D);
+    if (!mul_le(kIndexLimit, {BH, T, d_k > d_v ? d_k : d_v}) || !mul_le(kIndexLimit, {BH, d_v, D}))
+        return fail(FWA_ERR_UNSUPPORTED, "%s: sizes overflow the index range", fn);
+    if (BH > (int64_t(1) << 26) || static_cast<int64_t>(T) * d_v > (int64_t(1) << 31))
+        return fail(FWA_ERR_UNSUPPORTED, "%s: too many (b, h) slices for one launch", fn);
+    fwa::FwdPlan plan;
+    if (!fwa::plan_forward(static_cast<int>(BH), d_k, d_v, nu, chunk, dtype == FWA_BF16, &plan))
+        return fail(FWA_ERR_UNSUPPORTED,
+                    "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn,
+                    d_k, d_v, nu, chunk);
+    const int es = elem_bytes(dtype);
+    const int64_t nqk = BH * T * d_k * es, nv = BH * T * d_v * es, nb = BH * T * es;
+    const int64_t nW = BH * d_v * D * 4;
+    const Span in[] = {span(q, T ? nqk : 0), span(k, T ? nqk : 0), span(v, T ? nv : 0),
+                       span(beta_logit, T ? nb : 0), span(W0, W0 ? nW : 0)};
+    const Span sy = span(y, T && y ? nv : 0), sw = span(W_final, W_final ? nW : 0);
+    for (const Span& s : in)
+        if (overlap(s, sy)) return fail(FWA_ERR_INVALID_ARG, "%s: y overlaps an input", fn);
+    for (int i = 0; i < 4; ++i)
+        if (overlap(in[i], sw)) return fail(FWA_ERR_INVALID_ARG, "%s: W_final overlaps an input", fn);
+    if (W0 && W_final && W0 != W_final && overlap(in[4], sw))
+        return fail(FWA_ERR_INVALID_ARG, "%s: W0 and W_final partially overlap", fn);
+    if (overlap(sy, sw)) return fail(FWA_ERR_INVALID_ARG, "%s: y overlaps W_final", fn);
+    return hip_status(fwa::launch_delta_forward(plan, q, k, v, beta_logit, W0, y, W_final,
+                                                static_cast<int>(BH), H, T, d_k, d_v, nu, chunk,
+                                                dtype == FWA_BF16, stream),
+                      "fwa_delta_forward launch");
+}
+
+fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,
+                          float* W, void* y, int B, int H, int d_k, int d_v, int nu,
+                          fwa_dtype dtype, hipStream_t stream) {
+    const char* fn = "fwa_delta_step";
+    if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (B < 0 || H < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H", fn);
+    if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
+    if (nu < 1 || nu > 2 * d_k - 1)
+        return fail(FWA_ERR_INVALID_ARG, "%s: nu=%d outside [1, 2*d_k-1]", fn, nu);
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    if (BH == 0) return ok();
+    if (!q || !k || !v || !beta_logit || !W || !y)
+        return fail(FWA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    const void* ptrs[] = {q, k, v, beta_logit, W, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p))
+            return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: d_k=%d not in {16,32,64,128}", fn, d_k);
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
+    int LR = 0;
+    if (D > 1024 || fwa::step_cpl_for(static_cast<int>(D), &LR) == 0)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: D=%lld has no row layout (D <= 1024, D/4 = 8..64 x 1..4)",
+                    fn, (long long)D);
+    if (!mul_le(kIndexLimit, {BH, d_v, D}) || BH > (int64_t(1) << 31) - 1)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: sizes overflow the index range", fn);
+    const int es = elem_bytes(dtype);
+    const Span sW = span(W, BH * d_v * D * 4), sy = span(y, BH * d_v * es);
+    const Span in[] = {span(q, BH * d_k * es), span(k, BH * d_k * es), span(v, BH * d_v * es),
+                       span(beta_logit, BH * es)};
+    for (const Span& s : in)
+        if (overlap(s, sW) || overlap(s, sy))
+            return fail(FWA_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    if (overlap(sW, sy)) return fail(FWA_ERR_INVALID_ARG, "%s: y overlaps W", fn);
+    return hip_status(fwa::launch_delta_step(q, k, v, beta_logit, W, y, BH, d_k, d_v, nu,
+                                             dtype == FWA_BF16, stream),
+                      "fwa_delta_step launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels of the fast-weight delta-rule layer.
+// Types, bf16 <-> fp32 conversion, element loads/stores for the two I/O element types, and
+// thin wrappers over the two MFMA shapes the kernels use.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fwa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16;
+
+constexpr float kDpfpEps = 1e-6f;  // [FWT] "DPFP / normalisation": added to the sum
+
+__device__ __forceinline__ float bf16_bits_to_f32(u16 h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
+    __bf16 b = static_cast<__bf16>(f);
+    return __builtin_bit_cast(u16, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = static_cast<__bf16>(lo);
+    v[1] = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Element I/O for the caller's dtype (fp32 or bf16 storage).
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+    if constexpr (BF16) return bf16_bits_to_f32(static_cast<const u16*>(p)[i]);
+    else return static_cast<const float*>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
+    if constexpr (BF16) static_cast<u16*>(p)[i] = f32_to_bf16_bits(v);
+    else static_cast<float*>(p)[i] = v;
+}
+
+__device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
+
+// sigmoid evaluated so that neither branch overflows; sigmoid(-inf) = 0, sigmoid(+inf) = 1.
+__device__ __forceinline__ float sigmoid_stable(float x) {
+    if (x >= 0.0f) return 1.0f / (1.0f + expf(-x));
+    float e = expf(x);
+    return e / (1.0f + e);
+}
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).
+// Lane l holds A[l%16][8*(l/16) + s] and B[8*(l/16) + s][l%16] in slot s; the result holds
+// D[4*(l/16) + r][l%16] in slot r.
+__device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16 fp32) += A(16x4 fp32) * B(4x16 fp32).
+// Lane l holds A[l%16][l/16] and B[l/16][l%16]; the result layout is as above.
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+}  // namespace fwa

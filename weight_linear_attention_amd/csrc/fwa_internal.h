@@ -1,0 +1,45 @@
+// Host-side interface between the C ABI (fwa_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fwa {
+
+// Kernel arguments of the chunked forward, including its LDS layout (byte offsets and row
+// strides in elements of each region's type).
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* bl;
+    const float* W0;
+    void* y;
+    float* Wf;
+    int BH, H, T, d_k, d_v, nu;
+    int R, NVT, DP, NDP;
+    int off_kc, off_kr, off_qr, off_ls, off_ps, off_li, off_red, off_small;
+    int kcs, krs, lss, pss;
+};
+
+struct FwdPlan {
+    int R, NVT, DP, NDP, NDPM;
+    FwdArgs args;
+    int lds_bytes;
+};
+
+hipError_t launch_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, bool bf16,
+                       hipStream_t stream);
+
+int step_cpl_for(int D, int* LR_out);
+hipError_t launch_delta_step(const void* q, const void* k, const void* v, const void* bl,
+                             float* W, void* y, int64_t BH, int d_k, int d_v, int nu, bool bf16,
+                             hipStream_t stream);
+
+bool plan_forward(int BH, int d_k, int d_v, int nu, int C, bool bf16, FwdPlan* plan);
+hipError_t launch_delta_forward(const FwdPlan& plan, const void* q, const void* k,
+                                const void* v, const void* bl, const float* W0, void* y,
+                                float* Wf, int BH, int H, int T, int d_k, int d_v, int nu, int C,
+                                bool bf16, hipStream_t stream);
+
+}  // namespace fwa

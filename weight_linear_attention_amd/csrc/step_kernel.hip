@@ -1,0 +1,178 @@
+// Single-token decode step of the fast-weight delta rule, W updated in place.
+//
+// Per (b, h), with f = phi(k), g = phi(q), beta = sigmoid(beta_logit) ("Fast Weights
+// Transformer" guide, xdnf.cn/news/308600, sections "FastWeightsAttention / update formula"
+// and "token_wise variant"):
+//     v_bar = W f;  W <- W + beta (v - v_bar) f^T;  y = W g  (read after the write).
+// Row r of W evolves independently: with u_r = beta (v_r - W_r.f),
+//     y_r = (W_r + u_r f).g = W_r.g + u_r (f.g),
+// so one pass over the rows reads W once (two dot products per row against the old row) and
+// writes it once (W_r + u_r f).  The step is bound by HBM traffic on W (8 * d_v * D bytes per
+// (b, h)), the decode regime the "Transformer" page (wineandchord.com), section "Complexity",
+// describes.
+//
+// Mapping: one workgroup (4 waves) per (b, h).  A row of D floats is spread over LR lanes of
+// one wave, CPL float4 columns per lane (D = 4 * LR * CPL), so every row dot product is a
+// lane-shuffle reduction inside a wave and each lane issues 16-byte loads and stores.  Each
+// lane computes the f and g entries of its own columns straight from k and q (cached global
+// reads) and the group reduces the DPFP sums, so the kernel needs no LDS and no barrier and
+// every W load is in flight from the first instruction.
+#include "fwa_common.h"
+#include "fwa_internal.h"
+
+namespace fwa {
+
+template <bool BF16, int CPL>
+__global__ __launch_bounds__(256) void delta_step_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ bl, float* __restrict__ W, void* __restrict__ y, int d_k, int d_v,
+    int nu, int LR) {
+    constexpr int RB = (CPL == 1) ? 8 : (CPL == 2 ? 4 : 2);  // row rounds per batch
+    const int64_t s = blockIdx.x;
+    const int two_dk = 2 * d_k;
+    const int D = two_dk * nu;
+    float* Ws = W + s * static_cast<int64_t>(d_v) * D;
+    const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+    const int rpw = 64 / LR;           // rows per wave per round
+    const int RPR = 4 * rpw;           // rows per workgroup round
+    const int rr = wv * rpw + l / LR;  // this lane's row inside a round
+    const int c = l % LR;
+    const int rounds = (d_v + RPR - 1) / RPR;
+
+    // First batch of W rows: issued before anything else.
+    float4 wrow[RB][CPL];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+        const int row = rr + RPR * b;
+#pragma unroll
+        for (int m = 0; m < CPL; ++m)
+            wrow[b][m] = (b < rounds && row < d_v)
+                             ? *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(row) * D +
+                                                                4 * (c + LR * m))
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // f and g on this lane's 4*CPL columns.  Position d lies in the block of shift
+    // i = d / (2 d_k) + 1 at j = d mod 2 d_k; its factors are relu([k,-k]) at j and at
+    // (j - i) mod 2 d_k.
+    const int64_t kb = s * d_k;
+    float f[CPL * 4], g[CPL * 4];
+    float Sf = 0.0f, Sg = 0.0f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = 4 * (c + LR * m) + e;
+            const int i = d / two_dk + 1;
+            const int j = d - (i - 1) * two_dk;
+            const int jr = ((j - i) % two_dk + two_dk) % two_dk;
+            const int ja = j < d_k ? j : j - d_k, jb = jr < d_k ? jr : jr - d_k;
+            const float sa = j < d_k ? 1.0f : -1.0f, sb = jr < d_k ? 1.0f : -1.0f;
+            const float fk = relu(sa * load_elem<BF16>(k, kb + ja)) *
+                             relu(sb * load_elem<BF16>(k, kb + jb));
+            const float fq = relu(sa * load_elem<BF16>(q, kb + ja)) *
+                             relu(sb * load_elem<BF16>(q, kb + jb));
+            f[m * 4 + e] = fk;
+            g[m * 4 + e] = fq;
+            Sf += fk;
+            Sg += fq;
+        }
+    }
+    for (int off = LR / 2; off >= 1; off >>= 1) {
+        Sf += __shfl_xor(Sf, off, LR);
+        Sg += __shfl_xor(Sg, off, LR);
+    }
+    const float rf = 1.0f / (Sf + kDpfpEps), rg = 1.0f / (Sg + kDpfpEps);
+    float fg = 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPL * 4; ++e) {
+        f[e] *= rf;
+        g[e] *= rg;
+        fg += f[e] * g[e];
+    }
+    for (int off = LR / 2; off >= 1; off >>= 1) fg += __shfl_xor(fg, off, LR);
+    const float beta = sigmoid_stable(load_elem<BF16>(bl, s));
+    const int64_t vb = s * d_v;
+
+    for (int r0 = 0; r0 < rounds; r0 += RB) {
+        if (r0 > 0) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int row = rr + RPR * (r0 + b);
+#pragma unroll
+                for (int m = 0; m < CPL; ++m)
+                    wrow[b][m] = (r0 + b < rounds && row < d_v)
+                                     ? *reinterpret_cast<const float4*>(
+                                           Ws + static_cast<int64_t>(row) * D + 4 * (c + LR * m))
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int row = rr + RPR * (r0 + b);
+            float dk = 0.0f, dq = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) {
+                const float4 w4 = wrow[b][m];
+                dk += w4.x * f[m * 4 + 0] + w4.y * f[m * 4 + 1] + w4.z * f[m * 4 + 2] +
+                      w4.w * f[m * 4 + 3];
+                dq += w4.x * g[m * 4 + 0] + w4.y * g[m * 4 + 1] + w4.z * g[m * 4 + 2] +
+                      w4.w * g[m * 4 + 3];
+            }
+            for (int off = LR / 2; off >= 1; off >>= 1) {
+                dk += __shfl_xor(dk, off, LR);
+                dq += __shfl_xor(dq, off, LR);
+            }
+            if (r0 + b < rounds && row < d_v) {
+                const float u = beta * (load_elem<BF16>(v, vb + row) - dk);
+                if (c == 0) store_elem<BF16>(y, vb + row, dq + u * fg);
+#pragma unroll
+                for (int m = 0; m < CPL; ++m) {
+                    float4 w4 = wrow[b][m];
+                    w4.x += u * f[m * 4 + 0];
+                    w4.y += u * f[m * 4 + 1];
+                    w4.z += u * f[m * 4 + 2];
+                    w4.w += u * f[m * 4 + 3];
+                    *reinterpret_cast<float4*>(Ws + static_cast<int64_t>(row) * D +
+                                               4 * (c + LR * m)) = w4;
+                }
+            }
+        }
+    }
+}
+
+// Columns per lane for a row of D floats: the smallest CPL in 1..4 with D / (4 CPL) a power of
+// two in [8, 64].  Returns 0 when none exists (shape not implemented).
+int step_cpl_for(int D, int* LR_out) {
+    for (int cpl = 1; cpl <= 4; ++cpl) {
+        if (D % (4 * cpl)) continue;
+        const int lr = D / (4 * cpl);
+        if (lr == 8 || lr == 16 || lr == 32 || lr == 64) {
+            *LR_out = lr;
+            return cpl;
+        }
+    }
+    return 0;
+}
+
+hipError_t launch_delta_step(const void* q, const void* k, const void* v, const void* bl,
+                             float* W, void* y, int64_t BH, int d_k, int d_v, int nu, bool bf16,
+                             hipStream_t stream) {
+    const int D = 2 * d_k * nu;
+    int LR = 0;
+    const int cpl = step_cpl_for(D, &LR);
+    const dim3 grid(static_cast<unsigned>(BH)), block(256);
+#define FWA_STEP_CASE(BF, C)                                                                 \
+    if (bf16 == BF && cpl == C) {                                                            \
+        hipLaunchKernelGGL((delta_step_kernel<BF, C>), grid, block, 0, stream, q, k, v, bl, W, \
+                           y, d_k, d_v, nu, LR);                                             \
+        return hipGetLastError();                                                            \
+    }
+    FWA_STEP_CASE(false, 1) FWA_STEP_CASE(false, 2) FWA_STEP_CASE(false, 3)
+    FWA_STEP_CASE(false, 4) FWA_STEP_CASE(true, 1) FWA_STEP_CASE(true, 2)
+    FWA_STEP_CASE(true, 3) FWA_STEP_CASE(true, 4)
+#undef FWA_STEP_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fwa

@@ -1,0 +1,283 @@
+"""Benchmark of the fast-weight delta-rule layer (DPFP + chunked forward + decode step) on one
+MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step of the default workload is one pass of the whole hot path over one batch: the chunked
+causal forward over B x T tokens (DPFP, beta, intra-chunk work, state work, y and the final
+memory) followed by one decode step per sequence that continues from that memory.  Tokens per
+step = B * (T + 1).  Inputs are seeded synthetic tensors (weight_linear_attention_amd/synthetic.py)
+already resident in HBM when timing starts.  Other workloads (--workload):
+    b4_h8_t4096_d64_nu2_bf16_carried, b8_h16_t16384_d64_nu3_bf16   forward only
+    decode_b256_h8_d64_nu1_f32                                      one fwa_delta_step per step
+    dpfp_b8_h16_t16384_d64_nu3_bf16                                 fwa_dpfp on q and k
+
+Prints ONE JSON line.  `roofline` describes the dominant kernel: algorithmic bytes or flops of
+one launch divided by its mean duration, measured with HIP events on the launch stream over the
+timed region.  `cpu_baseline` times the fp64 oracle on the host (rank 0 only).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+DEFAULT_WORKLOAD = "h8_t1024_d64_nu1_f32"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--chunk", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash(name):
+    path = os.path.join(HERE, "weight_linear_attention_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source for this workload; otherwise None."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    ent = table.get(f"{kernel_file}:{workload}")
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash(kernel_file):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from weight_linear_attention_amd import fwa
+    from weight_linear_attention_amd.synthetic import (WORKLOADS, make_decode_inputs,
+                                                       make_inputs, workload)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    kind = "prefill+decode"
+    if name.startswith("dpfp_"):
+        kind, w = "dpfp", workload(name[len("dpfp_"):])
+    elif name.startswith("decode_"):
+        kind, w = "decode", workload(name)
+    elif name == DEFAULT_WORKLOAD:
+        w = workload(name)
+    else:
+        kind, w = "prefill", workload(name)
+    if args.chunk is not None:
+        w = workload(w.name, chunk=args.chunk)
+    steps = args.steps if args.steps is not None else (1024 if kind == "decode" else 20)
+    warmup = args.warmup if args.warmup is not None else 3
+    es = 2 if w.dtype == "bf16" else 4
+    D, BH = w.D, w.B * w.H
+
+    # ------------------------------------------------------------------ inputs in HBM
+    if kind == "decode":
+        inp = make_decode_inputs(w, steps=steps + warmup)
+        d = {k: v.to(dev) for k, v in inp.items()}
+        W = d["W0"].clone()
+    else:
+        inp = make_inputs(w)
+        d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    if kind == "prefill+decode":
+        g = torch.Generator().manual_seed(w.seed + 7)
+        nxt = {n: torch.randn(w.B, w.H, dd, generator=g).to(w.torch_dtype).to(dev)
+               for n, dd in (("q", w.d_k), ("k", w.d_k), ("v", w.d_v))}
+        nxt["beta_logit"] = torch.randn(w.B, w.H, generator=g).to(w.torch_dtype).to(dev)
+    y = Wf = phi_q = phi_k = None
+    if kind in ("prefill", "prefill+decode"):
+        y = torch.empty(w.B, w.H, w.T, w.d_v, dtype=w.torch_dtype, device=dev)
+        Wf = torch.empty(w.B, w.H, w.d_v, D, dtype=torch.float32, device=dev)
+    if kind == "dpfp":
+        phi_q = torch.empty(w.B, w.H, w.T, D, dtype=w.torch_dtype, device=dev)
+        phi_k = torch.empty_like(phi_q)
+    ystep = torch.empty(w.B, w.H, w.d_v, dtype=w.torch_dtype, device=dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one_step(i, marks):
+        if kind in ("prefill", "prefill+decode"):
+            marks[0].record()
+            fwa.delta_forward(d["q"], d["k"], d["v"], d["beta_logit"], d["W0"], chunk=w.chunk,
+                              nu=w.nu, out=y, W_final=Wf)
+            marks[1].record()
+            if kind == "prefill+decode":
+                fwa.delta_step(nxt["q"], nxt["k"], nxt["v"], nxt["beta_logit"], Wf, nu=w.nu,
+                               out=ystep)
+                marks[2].record()
+        elif kind == "decode":
+            marks[0].record()
+            fwa.delta_step(d["q"][i], d["k"][i], d["v"][i], d["beta_logit"][i], W, nu=w.nu,
+                           out=ystep)
+            marks[1].record()
+        else:
+            marks[0].record()
+            fwa.dpfp(d["q"], w.nu, out=phi_q)
+            fwa.dpfp(d["k"], w.nu, out=phi_k)
+            marks[1].record()
+
+    for i in range(warmup):
+        one_step(i, [ev(), ev(), ev()])
+    torch.cuda.synchronize()
+    marks = [[ev(), ev(), ev()] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(warmup + i if kind == "decode" else i, marks[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    main_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    step_ms = (sum(m[1].elapsed_time(m[2]) for m in marks) / steps
+               if kind == "prefill+decode" else None)
+
+    # ------------------------------------------------------------------ metric + roofline
+    if kind == "prefill+decode":
+        tokens = w.B * (w.T + 1)
+    elif kind == "prefill":
+        tokens = w.B * w.T
+    elif kind == "decode":
+        tokens = w.B
+    else:
+        tokens = 2 * BH * w.T          # DPFP vectors (q and k) per step
+    value = tokens * steps / elapsed
+
+    if kind in ("prefill", "prefill+decode"):
+        kernel_file = "forward_kernel.hip"
+        flops = BH * w.T * (6 * D * w.d_v + 6 * D)
+        nbytes = (BH * w.T * ((3 * w.d_k + 1) * es + w.d_v * es)
+                  + BH * w.d_v * D * 4 * (1 + (d["W0"] is not None)))
+        t_mfma = flops / (PEAK_TFLOPS[w.dtype] * 1e12)
+        t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+        if t_mfma >= t_hbm:
+            ach = flops / (main_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_TFLOPS[w.dtype],
+                    "unit": "TFLOP/s", "frac": ach / PEAK_TFLOPS[w.dtype]}
+        else:
+            ach = nbytes / (main_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": ach / PEAK_HBM_GBPS}
+        roof.update(kernel="delta_forward_kernel", algorithmic_flops=flops,
+                    algorithmic_bytes=nbytes, mean_launch_ms=main_ms)
+    else:
+        if kind == "decode":
+            kernel_file = "step_kernel.hip"
+            nbytes = BH * (2 * w.d_v * D * 4 + (2 * w.d_k + 1 + 2 * w.d_v) * es)
+            kname = "delta_step_kernel"
+        else:
+            kernel_file = "dpfp_kernel.hip"
+            nbytes = 2 * BH * w.T * (w.d_k + D) * es
+            kname = "dpfp_kernel (q and k launches)"
+        ach = nbytes / (main_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBPS, "kernel": kname, "algorithmic_bytes": nbytes,
+                "mean_launch_ms": main_ms}
+    roof["traffic"] = measured_traffic(kernel_file, w.name if kind != "dpfp" else name)
+
+    out = {
+        "metric": "tokens/sec through fast-weight layer (fwd + decode step) & % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name if kind != "prefill+decode" else
+                   f"{w.name}: chunked forward over B*T tokens + 1 decode step per sequence",
+                   "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "nu": w.nu,
+                   "D": D, "chunk": w.chunk, "tokens_per_step": tokens,
+                   "initial_memory": "zeros" if w.w0_std is None else f"N(0,{w.w0_std}^2)"},
+        "roofline": roof,
+        "kernels_ms": {"main": main_ms, "decode_step": step_ms},
+    }
+
+    # ------------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, kind, inp, nxt if kind == "prefill+decode" else None)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, kind, inp, nxt):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload, timed on the
+    host; the sample is scaled to tokens/s exactly like the GPU value."""
+    import numpy as np
+    import oracle
+    from weight_linear_attention_amd.synthetic import to_f64
+
+    threads = oracle.num_threads()
+    if kind == "decode":
+        # 16 successive steps over all 2048 (b, h) slices (the oracle's step function)
+        S = 16
+        Wd = to_f64(inp["W0"])
+        t0 = time.perf_counter()
+        for s in range(S):
+            _, Wd = oracle.delta_step(to_f64(inp["q"][s]), to_f64(inp["k"][s]), to_f64(inp["v"][s]),
+                                      to_f64(inp["beta_logit"][s]), Wd, nu=w.nu)
+        dt = time.perf_counter() - t0
+        return {"value": w.B * S / dt, "unit": "tokens/s", "cores": min(threads, w.B * w.H),
+                "kind": "oracle", "sample": f"{S} decode steps x {w.B}x{w.H} slices (full state)"}
+    if kind == "dpfp":
+        n = 65536
+        x = to_f64(inp["q"].reshape(-1, w.d_k)[:n])
+        t0 = time.perf_counter()
+        oracle.dpfp(x, w.nu)
+        dt = time.perf_counter() - t0
+        return {"value": n / dt, "unit": "vectors/s", "cores": threads, "kind": "oracle",
+                "sample": f"{n} q vectors"}
+    # forward (+ decode): whole (b, h) slices, as many as needed for a bounded sample
+    BH = w.B * w.H
+    nsl = min(BH, max(1, threads))
+    if w.T * w.D * w.d_v * 6 * nsl > 4e10:      # cap the sample at roughly 1e10..4e10 flops
+        nsl = max(1, int(4e10 // (w.T * w.D * w.d_v * 6)))
+    q = to_f64(inp["q"]).reshape(1, BH, w.T, w.d_k)[:, :nsl]
+    k = to_f64(inp["k"]).reshape(1, BH, w.T, w.d_k)[:, :nsl]
+    v = to_f64(inp["v"]).reshape(1, BH, w.T, w.d_v)[:, :nsl]
+    l = to_f64(inp["beta_logit"]).reshape(1, BH, w.T)[:, :nsl]
+    W0 = None if inp["W0"] is None else to_f64(inp["W0"]).reshape(1, BH, w.d_v, w.D)[:, :nsl]
+    reps, dt = 0, 0.0
+    t0 = time.perf_counter()
+    while dt < 2.0 or reps == 0:
+        _, Wf = oracle.delta_forward(q, k, v, l, W0, nu=w.nu)
+        if nxt is not None:
+            sel = lambda t: to_f64(t).reshape(1, BH, -1)[:, :nsl]
+            oracle.delta_step(sel(nxt["q"]), sel(nxt["k"]), sel(nxt["v"]),
+                              to_f64(nxt["beta_logit"]).reshape(1, BH)[:, :nsl], Wf, nu=w.nu)
+        reps += 1
+        dt = time.perf_counter() - t0
+    # tokens of the sample, scaled like the GPU metric: a (b, h) slice is 1/H of a sequence
+    tok = (w.T + (1 if nxt is not None else 0)) * nsl / w.H * reps
+    return {"value": tok / dt, "unit": "tokens/s", "cores": min(threads, nsl), "kind": "oracle",
+            "sample": f"{nsl} of {BH} (b,h) slices x T={w.T}"
+                      + (" + 1 decode step" if nxt is not None else "") + f", {reps} rep(s)"}
+
+
+if __name__ == "__main__":
+    main()

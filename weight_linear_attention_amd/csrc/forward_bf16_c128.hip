@@ -1,0 +1,8 @@
+// Instantiates the chunked forward kernel for bf16 inputs and chunks of 128 rows.
+#include "forward_kernel.h"
+
+namespace fwa {
+hipError_t launch_fwd_bf16_c128(const FwdPlan& p, int BH, hipStream_t s) {
+    return launch_fwd_dispatch<true, 128>(p, BH, s);
+}
+}  // namespace fwa

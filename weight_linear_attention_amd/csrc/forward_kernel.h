@@ -31,6 +31,8 @@
 // a valid B operand (and the transpose of an A operand) for a product whose contraction runs
 // over those 16 rows, as long as the other operand takes its k-slots in the same order; so W,
 // U and the intermediate blocks feed the next MFMA with no data movement.
+#pragma once
+
 #include "fwa_common.h"
 #include "fwa_internal.h"
 
@@ -40,7 +42,71 @@ namespace fwa {
 
 
 constexpr int kLiStride = 20;   // floats per row of the diagonal-inverse buffer
-constexpr int kRedStride = 17;  // floats per row of the cross-wave reduction buffer
+
+// Sum of v over the d_k-lane group of lane l (d_k in {16, 32, 64}), in every lane of the group:
+// rotations inside each 16-lane row (DPP), then the row sums combined with readlane.
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
+    return v;
+}
+
+__device__ __forceinline__ float group_sum(float v, int d_k, int l) {
+    const float r = row_sum16(v);
+    if (d_k == 16) return r;
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
+    if (d_k == 32) return l < 32 ? r0 + r1 : r2 + r3;
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Raw DPFP products of one row (lane jl of a d_k-lane group holds k_jl and q_jl) for every
+// shift, written to the row-major K and Q tiles; returns the row sums through sk, sq.  With a
+// compile-time NU all rolled operands are fetched (ds_bpermute) before any LDS write, so the
+// writes never sit in front of a permute the lane is waiting for.
+template <typename LT, int NU>
+__device__ __forceinline__ void dpfp_row(float kv, float qv, int nu, int jl, int gbase, int d_k,
+                                         LT* krow, LT* qrow, float& sk, float& sq) {
+    const int two_dk = 2 * d_k;
+    const float ka = relu(kv), kb = relu(-kv), qa = relu(qv), qb = relu(-qv);
+    auto emit = [&](int i, float xk, float xq) {
+        const float pk1 = ka * relu(xk), pk2 = kb * relu(-xk);
+        const float pq1 = qa * relu(xq), pq2 = qb * relu(-xq);
+        sk += pk1 + pk2;
+        sq += pq1 + pq2;
+        const int o1 = (i - 1) * two_dk;
+        krow[o1] = from_f32<LT>(pk1);
+        krow[o1 + d_k] = from_f32<LT>(pk2);
+        qrow[o1] = from_f32<LT>(pq1);
+        qrow[o1 + d_k] = from_f32<LT>(pq2);
+    };
+    // rolled source position m = (j - i) mod 2 d_k (d_k is a power of two): lane (m mod d_k)
+    // of the row's group, negated when m falls in the -k half.
+    auto fetch = [&](int i, float& xk, float& xq) {
+        const int m = (jl - i) & (two_dk - 1);
+        const int src4 = (gbase + (m & (d_k - 1))) << 2;
+        const float sgn = (m & d_k) ? -1.0f : 1.0f;
+        xk = sgn * __int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(kv)));
+        xq = sgn * __int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(qv)));
+    };
+    if constexpr (NU > 0) {
+        float xk[NU], xq[NU];
+#pragma unroll
+        for (int i = 1; i <= NU; ++i) fetch(i, xk[i - 1], xq[i - 1]);
+#pragma unroll
+        for (int i = 1; i <= NU; ++i) emit(i, xk[i - 1], xq[i - 1]);
+    } else {
+        for (int i = 1; i <= nu; ++i) {
+            float xk, xq;
+            fetch(i, xk, xq);
+            emit(i, xk, xq);
+        }
+    }
+}
 
 template <bool BF16, int C, int NDPM>
 __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
@@ -48,15 +114,18 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     constexpr int NT = C / 16;
     constexpr int NGP = NT * (NT + 1);                 // G and P lower-triangle tiles
     constexpr int MAXTW = (NGP + 3) / 4;               // of those, per wave
+    constexpr int RS = C + 4;                          // row stride of the partials buffer
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    LT* Kc = reinterpret_cast<LT*>(smem + a.off_kc);   // [D][kcs]  K transposed
-    LT* Kr = reinterpret_cast<LT*>(smem + a.off_kr);   // [C][krs]  K
-    LT* Qr = reinterpret_cast<LT*>(smem + a.off_qr);   // [C][krs]  Q
+    LT* Kr = reinterpret_cast<LT*>(smem + a.off_kr);   // [C][krs]  K (lives through D)
+    LT* Qr = reinterpret_cast<LT*>(smem + a.off_qr);   // [C][krs]  Q (dead after B)
+    using ITs = std::conditional_t<BF16, u16, float>;
+    ITs* Xk = reinterpret_cast<ITs*>(smem + a.off_xs);              // [C][d_k] raw k rows
+    ITs* Xq = Xk + C * a.d_k;                                       // [C][d_k] raw q rows
     float* Ls = reinterpret_cast<float*>(smem + a.off_ls);   // [C][lss] beta*strict_lower(G)
     LT* Ps = reinterpret_cast<LT*>(smem + a.off_ps);          // [C][pss] lower_incl(Q K^T)
     float* Li = reinterpret_cast<float*>(smem + a.off_li);    // [C][20]  diagonal inverses
-    float* Red = reinterpret_cast<float*>(smem + a.off_red);  // [4][2][C][17] partials
+    float* Red = reinterpret_cast<float*>(smem + a.off_red);  // [4][2][16][C+4] partials
     float* rhok = reinterpret_cast<float*>(smem + a.off_small);
     float* rhoq = rhok + C;
     float* betas = rhoq + C;
@@ -65,7 +134,6 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     const int l16 = l & 15, g4 = l >> 4;
     const int d_k = a.d_k, two_dk = 2 * d_k, nu = a.nu;
     const int D = two_dk * nu;
-    const int ND = D / 16;
     const int d_v = a.d_v, T = a.T;
 
     // Workgroup -> (b*H + h, d_v slice r).  When the grid splits evenly over the 8 XCDs,
@@ -96,112 +164,156 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     }
 
     const int64_t row0 = static_cast<int64_t>(bh) * T;  // first (b, h, t=0) row
+    // Per-(b, h) base pointers; offsets inside one (b, h) fit in 32 bits (checked on the host).
+    using IT = std::conditional_t<BF16, u16, float>;  // storage type of q, k, v, beta_logit, y
+    const IT* kB = static_cast<const IT*>(a.k) + row0 * d_k;
+    const IT* qB = static_cast<const IT*>(a.q) + row0 * d_k;
+    const IT* vB = static_cast<const IT*>(a.v) + row0 * d_v;
+    const IT* bB = static_cast<const IT*>(a.bl) + row0;
+    IT* yB = static_cast<IT*>(a.y) + row0 * d_v;
     const int nchunks = (T + C - 1) / C;
     const int rpw = 64 / d_k;                             // DPFP rows per wave pass
     const int jl = l % d_k, grp = l / d_k;
     const int gbase = grp * d_k;
 
+    // The next chunk's raw inputs are fetched into registers while the current chunk is
+    // being computed, so no global-memory latency sits on the serial chain over chunks.
+    const int npass = C / (4 * rpw);
+    // The next chunk's k and q rows form two contiguous blocks of C*d_k elements; each thread
+    // fetches its share as 16-byte units into registers while the current chunk computes.
+    // Loads are branch-free: a unit past the sequence end reads unit 0 of the chunk (always in
+    // range) and is zeroed when it is staged, so no wait sits next to the loads.
+    constexpr int NRM = C / 16;                      // units per thread at d_k = 64, fp32
+    const int ubytes = d_k * static_cast<int>(sizeof(IT));  // bytes per row
+    const int nunits = C * ubytes / 16;              // 16-byte units per chunk block
+    const int nr = (nunits + 255) / 256;
+    uint4 kraw[NRM], qraw[NRM];
+    IT blpre = IT(0);
+    auto prefetch = [&](int chn) {
+        const int tn0 = chn * C;
+        const int Cn = min(C, T - tn0);
+        const char* kc = reinterpret_cast<const char*>(kB + static_cast<int64_t>(tn0) * d_k);
+        const char* qc = reinterpret_cast<const char*>(qB + static_cast<int64_t>(tn0) * d_k);
+#pragma unroll
+        for (int i = 0; i < NRM; ++i) {
+            if (i < nr) {
+                const int u = tid + 256 * i;
+                const bool ok = u < nunits && (u * 16) / ubytes < Cn;
+                const int off = ok ? u * 16 : 0;
+                kraw[i] = *reinterpret_cast<const uint4*>(kc + off);
+                qraw[i] = *reinterpret_cast<const uint4*>(qc + off);
+            }
+        }
+        blpre = bB[tn0 + min(tid, Cn - 1)];
+    };
+    if (nchunks > 0) prefetch(0);
+
     for (int ch = 0; ch < nchunks; ++ch) {
         const int t0 = ch * C;
         const int Cc = min(C, T - t0);
 
-        // ---------------- A: DPFP rows, beta, and this wave's V tile
-        for (int p = 0; p < C / (4 * rpw); ++p) {
-            const int t = p * 4 * rpw + w * rpw + grp;
-            const bool tv = t < Cc;
-            const int64_t gi = (row0 + t0 + t) * d_k + jl;
-            const float kv = tv ? load_elem<BF16>(a.k, gi) : 0.0f;
-            const float qv = tv ? load_elem<BF16>(a.q, gi) : 0.0f;
-            const float ka = relu(kv), kb = relu(-kv), qa = relu(qv), qb = relu(-qv);
-            float sk = 0.0f, sq = 0.0f;
-            for (int i = 1; i <= nu; ++i) {
-                // rolled source position m = (j - i) mod 2 d_k: lane (m mod d_k), negated
-                // when m falls in the -k half.
-                const int m = ((jl - i) % two_dk + two_dk) % two_dk;
-                const int srcl = gbase + (m % d_k);
-                const bool neg = m >= d_k;
-                const float rk = __int_as_float(
-                    __builtin_amdgcn_ds_bpermute(srcl * 4, __float_as_int(kv)));
-                const float rq = __int_as_float(
-                    __builtin_amdgcn_ds_bpermute(srcl * 4, __float_as_int(qv)));
-                const float xk = neg ? -rk : rk, xq = neg ? -rq : rq;
-                const float pk1 = ka * relu(xk), pk2 = kb * relu(-xk);
-                const float pq1 = qa * relu(xq), pq2 = qb * relu(-xq);
-                sk += pk1 + pk2;
-                sq += pq1 + pq2;
-                const int d1 = (i - 1) * two_dk + jl, d2 = d1 + d_k;
-                if constexpr (BF16) {
-                    Kr[t * a.krs + d1] = f32_to_bf16_bits(pk1);
-                    Kr[t * a.krs + d2] = f32_to_bf16_bits(pk2);
-                    Kc[d1 * a.kcs + t] = f32_to_bf16_bits(pk1);
-                    Kc[d2 * a.kcs + t] = f32_to_bf16_bits(pk2);
-                    Qr[t * a.krs + d1] = f32_to_bf16_bits(pq1);
-                    Qr[t * a.krs + d2] = f32_to_bf16_bits(pq2);
-                } else {
-                    Kr[t * a.krs + d1] = pk1;
-                    Kr[t * a.krs + d2] = pk2;
-                    Kc[d1 * a.kcs + t] = pk1;
-                    Kc[d2 * a.kcs + t] = pk2;
-                    Qr[t * a.krs + d1] = pq1;
-                    Qr[t * a.krs + d2] = pq2;
-                }
-            }
-            for (int off = d_k / 2; off >= 1; off >>= 1) {
-                sk += __shfl_xor(sk, off, d_k);
-                sq += __shfl_xor(sq, off, d_k);
-            }
-            if (jl == 0) {
-                rhok[t] = 1.0f / (sk + kDpfpEps);
-                rhoq[t] = 1.0f / (sq + kDpfpEps);
-            }
-        }
-        if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(load_elem<BF16>(a.bl, row0 + t0 + tid))
-                                           : 0.0f;
+        // ---------------- A: DPFP rows, beta, and this wave's V tile (consumed in C)
         f32x4 Xv[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tt + 4 * g4 + e;
-                Xv[tt][e] = (has_state && t < Cc)
-                                ? load_elem<BF16>(a.v, (row0 + t0 + t) * d_v + vcol)
-                                : 0.0f;
+                const bool ok = has_state && t < Cc;
+                const float vv = to_f32(vB[(t0 + (ok ? t : 0)) * d_v + vcol]);
+                Xv[tt][e] = ok ? vv : 0.0f;
             }
+        }
+        // Stage this chunk's raw rows (zeros past the sequence end) for the DPFP passes.
+#pragma unroll
+        for (int i = 0; i < NRM; ++i) {
+            if (i < nr) {
+                const int u = tid + 256 * i;
+                if (u < nunits) {
+                    const uint32_t m = (u * 16) / ubytes < Cc ? 0xffffffffu : 0u;
+                    const uint4 kr4 = kraw[i], qr4 = qraw[i];
+                    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Xk) + u * 16) =
+                        make_uint4(kr4.x & m, kr4.y & m, kr4.z & m, kr4.w & m);
+                    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Xq) + u * 16) =
+                        make_uint4(qr4.x & m, qr4.y & m, qr4.z & m, qr4.w & m);
+                }
+            }
+        }
+        if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(to_f32(blpre)) : 0.0f;
+        if (ch + 1 < nchunks) prefetch(ch + 1);
+        __syncthreads();
+
+        // One row per d_k-lane group and pass; the shift count is a compile-time constant for
+        // nu <= 4 so each row's permutes are all issued before its writes.
+        auto dpfp_passes = [&](auto nu_tag) {
+            constexpr int NU = decltype(nu_tag)::value;
+#pragma unroll 4
+            for (int p = 0; p < npass; ++p) {
+                const int t = p * 4 * rpw + w * rpw + grp;
+                const float kv = to_f32(Xk[t * d_k + jl]), qv = to_f32(Xq[t * d_k + jl]);
+                float sk = 0.0f, sq = 0.0f;
+                dpfp_row<LT, NU>(kv, qv, nu, jl, gbase, d_k, Kr + t * a.krs + jl,
+                                 Qr + t * a.krs + jl, sk, sq);
+                sk = group_sum(sk, d_k, l);
+                sq = group_sum(sq, d_k, l);
+                if (jl == 0) {
+                    rhok[t] = __builtin_amdgcn_rcpf(sk + kDpfpEps);
+                    rhoq[t] = __builtin_amdgcn_rcpf(sq + kDpfpEps);
+                }
+            }
+        };
+        switch (nu) {
+            case 1: dpfp_passes(std::integral_constant<int, 1>{}); break;
+            case 2: dpfp_passes(std::integral_constant<int, 2>{}); break;
+            case 3: dpfp_passes(std::integral_constant<int, 3>{}); break;
+            case 4: dpfp_passes(std::integral_constant<int, 4>{}); break;
+            default: dpfp_passes(std::integral_constant<int, 0>{}); break;
         }
         __syncthreads();
 
         // ---------------- B: G, P tiles; K W^T and Q W^T against the memory
+        // Tiles w, w+4, ... of the list [G tiles (ta >= tb)..., P tiles (ta >= tb)...]; the
+        // k-step loop is outside so the wave's independent tiles interleave on the MFMA pipe.
         f32x4 gp[MAXTW];
+        const LT* Ap[MAXTW];
+        const LT* Bp[MAXTW];
 #pragma unroll
         for (int j = 0; j < MAXTW; ++j) {
             gp[j] = zero4();
-            const int tix = w + 4 * j;
-            if (tix < NGP) {
-                const bool isP = tix >= NGP / 2;
-                int idx = isP ? tix - NGP / 2 : tix;
-                int ta = 0;
-                while ((ta + 1) * (ta + 2) / 2 <= idx) ++ta;
-                const int tb = idx - ta * (ta + 1) / 2;
-                const LT* Arow = (isP ? Qr : Kr) + (16 * ta + l16) * a.krs;
-                const LT* Brow = Kr + (16 * tb + l16) * a.krs;
-                f32x4 acc = zero4();
-                if constexpr (BF16) {
-                    for (int kk = 0; kk < D / 32; ++kk) {
-                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Arow + 32 * kk + 8 * g4);
-                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Brow + 32 * kk + 8 * g4);
-                        acc = mfma_bf16_k32(av, bv, acc);
-                    }
-                } else {
-                    for (int kk = 0; kk < D / 16; ++kk) {
-                        const float4 av = *reinterpret_cast<const float4*>(Arow + 16 * kk + 4 * g4);
-                        const float4 bv = *reinterpret_cast<const float4*>(Brow + 16 * kk + 4 * g4);
-                        acc = mfma_f32_k4(av.x, bv.x, acc);
-                        acc = mfma_f32_k4(av.y, bv.y, acc);
-                        acc = mfma_f32_k4(av.z, bv.z, acc);
-                        acc = mfma_f32_k4(av.w, bv.w, acc);
+            const int tix = min(w + 4 * j, NGP - 1);
+            const bool isP = tix >= NGP / 2;
+            const int idx = isP ? tix - NGP / 2 : tix;
+            int ta = 0;
+            while ((ta + 1) * (ta + 2) / 2 <= idx) ++ta;
+            const int tb = idx - ta * (ta + 1) / 2;
+            Ap[j] = (isP ? Qr : Kr) + (16 * ta + l16) * a.krs;
+            Bp[j] = Kr + (16 * tb + l16) * a.krs;
+        }
+        if constexpr (BF16) {
+#pragma unroll 2
+            for (int kk = 0; kk < D / 32; ++kk) {
+#pragma unroll
+                for (int j = 0; j < MAXTW; ++j) {
+                    if (w + 4 * j < NGP) {
+                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Ap[j] + 32 * kk + 8 * g4);
+                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Bp[j] + 32 * kk + 8 * g4);
+                        gp[j] = mfma_bf16_k32(av, bv, gp[j]);
                     }
                 }
-                gp[j] = acc;
+            }
+        } else {
+            for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+                for (int j = 0; j < MAXTW; ++j) {
+                    if (w + 4 * j < NGP) {
+                        const float4 av = *reinterpret_cast<const float4*>(Ap[j] + 16 * kk + 4 * g4);
+                        const float4 bv = *reinterpret_cast<const float4*>(Bp[j] + 16 * kk + 4 * g4);
+                        gp[j] = mfma_f32_k4(av.x, bv.x, gp[j]);
+                        gp[j] = mfma_f32_k4(av.y, bv.y, gp[j]);
+                        gp[j] = mfma_f32_k4(av.z, bv.z, gp[j]);
+                        gp[j] = mfma_f32_k4(av.w, bv.w, gp[j]);
+                    }
+                }
             }
         }
         f32x4 S1[NT], QW[NT];
@@ -258,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 }
             }
         }
-        __syncthreads();  // K (row-major) and Q are dead from here; their space is reused
+        __syncthreads();  // Q is dead from here; its space is reused
 
         // ---------------- B': scaled G and P to LDS, state partials to the reduction buffer
 #pragma unroll
@@ -266,48 +378,56 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             const int tix = w + 4 * j;
             if (tix < NGP) {
                 const bool isP = tix >= NGP / 2;
-                int idx = isP ? tix - NGP / 2 : tix;
+                const int idx = isP ? tix - NGP / 2 : tix;
                 int ta = 0;
                 while ((ta + 1) * (ta + 2) / 2 <= idx) ++ta;
                 const int tb = idx - ta * (ta + 1) / 2;
-                const int s = 16 * tb + l16;
+                const int s = 16 * tb + l16, tr = 16 * ta + 4 * g4;
+                const float rks = rhok[s];
+                if (isP) {
+                    const f32x4 rq = *reinterpret_cast<const f32x4*>(rhoq + tr);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * ta + 4 * g4 + e;
-                    if (isP) {
-                        const float val = s <= t ? rhoq[t] * rhok[s] * gp[j][e] : 0.0f;
-                        if constexpr (BF16) Ps[t * a.pss + s] = f32_to_bf16_bits(val);
-                        else Ps[t * a.pss + s] = val;
-                    } else {
-                        Ls[t * a.lss + s] = s < t ? betas[t] * rhok[t] * rhok[s] * gp[j][e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) {
+                        const float val = s <= tr + e ? rq[e] * rks * gp[j][e] : 0.0f;
+                        Ps[(tr + e) * a.pss + s] = from_f32<LT>(val);
                     }
+                } else {
+                    const f32x4 rk = *reinterpret_cast<const f32x4*>(rhok + tr);
+                    const f32x4 bt = *reinterpret_cast<const f32x4*>(betas + tr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        Ls[(tr + e) * a.lss + s] = s < tr + e ? bt[e] * rk[e] * rks * gp[j][e] : 0.0f;
                 }
             }
         }
         if (has_state && a.DP > 1) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * tt + 4 * g4 + e;
-                    Red[((w * 2 + 0) * C + t) * kRedStride + l16] = S1[tt][e];
-                    Red[((w * 2 + 1) * C + t) * kRedStride + l16] = QW[tt][e];
-                }
+                *reinterpret_cast<f32x4*>(Red + ((w * 2 + 0) * 16 + l16) * RS + 16 * tt + 4 * g4) = S1[tt];
+                *reinterpret_cast<f32x4*>(Red + ((w * 2 + 1) * 16 + l16) * RS + 16 * tt + 4 * g4) = QW[tt];
             }
         }
         __syncthreads();
 
         // ---------------- C: diagonal-block inverses; reduce the state partials
         if (tid < C) {
+            // Column sc of the inverse of the unit lower 16x16 block ab; each row's dot product
+            // is split over four partial sums to keep the dependency chains short.
             const int ab = tid >> 4, sc = tid & 15;
             const float* Lb = Ls + (16 * ab) * a.lss + 16 * ab;
             float xcol[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                float acc = 0.0f;
+                f32x4 rw[4];
 #pragma unroll
-                for (int w2 = 0; w2 < u; ++w2) acc += Lb[u * a.lss + w2] * xcol[w2];
-                xcol[u] = (u == sc) ? 1.0f : (u < sc ? 0.0f : -acc);
+                for (int q4 = 0; q4 < 4; ++q4)
+                    rw[q4] = (4 * q4 < u) ? *reinterpret_cast<const f32x4*>(Lb + u * a.lss + 4 * q4)
+                                          : zero4();
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int w2 = 0; w2 < u; ++w2) acc[w2 & 3] += rw[w2 >> 2][w2 & 3] * xcol[w2];
+                const float tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                xcol[u] = (u == sc) ? 1.0f : (u < sc ? 0.0f : -tot);
             }
 #pragma unroll
             for (int u = 0; u < 16; ++u) Li[(16 * ab + u) * kLiStride + sc] = xcol[u];
@@ -320,12 +440,8 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                     f32x4 s1 = zero4(), qw = zero4();
                     for (int pp = 0; pp < a.DP; ++pp) {
                         const int ww = vt + a.NVT * pp;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int t = 16 * tt + 4 * g4 + e;
-                            s1[e] += Red[((ww * 2 + 0) * C + t) * kRedStride + l16];
-                            qw[e] += Red[((ww * 2 + 1) * C + t) * kRedStride + l16];
-                        }
+                        s1 += *reinterpret_cast<const f32x4*>(Red + ((ww * 2 + 0) * 16 + l16) * RS + 16 * tt + 4 * g4);
+                        qw += *reinterpret_cast<const f32x4*>(Red + ((ww * 2 + 1) * 16 + l16) * RS + 16 * tt + 4 * g4);
                     }
                     S1[tt] = s1;
                     QW[tt] = qw;
@@ -408,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * ta + 4 * g4 + e;
-                    if (t < Cc) store_elem<BF16>(a.y, (row0 + t0 + t) * d_v + vcol, acc[e]);
+                    if (t < Cc) yB[(t0 + t) * d_v + vcol] = from_f32<IT>(acc[e]);
                 }
             }
             // W^T += K^T (rho_k U): rows of U scaled by the key normalisers
@@ -417,6 +533,10 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) U[tb][e] *= rhok[16 * tb + 4 * g4 + e];
             }
+            // A operand K^T[d][t]: lane l16 of group g4 needs K[t][16 dt + l16] for the four
+            // rows t = 16 tb + 4 g4 + 0..3 (and the same for tile tb + 1).  For bf16 one
+            // ds_read_b64_tr_b16 delivers exactly that from the row-major tile when lane j of
+            // the group addresses K[16 tb + 4 g4 + j/4][16 dt + 4 (j%4)].
             if constexpr (BF16) {
 #pragma unroll
                 for (int tb = 0; tb < NT; tb += 2) {
@@ -426,14 +546,15 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                         bu[e] = static_cast<__bf16>(U[tb][e]);
                         bu[4 + e] = static_cast<__bf16>(tb + 1 < NT ? U[tb + 1 < NT ? tb + 1 : tb][e] : 0.0f);
                     }
+                    const LT* kt = Kr + (16 * tb + 4 * g4 + (l16 >> 2)) * a.krs + 4 * (l16 & 3);
 #pragma unroll
                     for (int i = 0; i < NDPM; ++i) {
                         if (i < ndp) {
-                            const LT* kc = Kc + (16 * (dt0 + i) + l16) * a.kcs + 16 * tb + 4 * g4;
-                            const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(kc);
+                            const LT* kc = kt + 16 * (dt0 + i);
+                            const bf16x4 c0 = lds_read_tr_b16x4(kc);
                             bf16x4 c1;
                             if (tb + 1 < NT) {
-                                c1 = *reinterpret_cast<const bf16x4*>(kc + 16);
+                                c1 = lds_read_tr_b16x4(kc + 16 * a.krs);
                             } else {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) c1[e] = static_cast<__bf16>(0.0f);
@@ -446,15 +567,15 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             } else {
 #pragma unroll
                 for (int tb = 0; tb < NT; ++tb) {
+                    const LT* kt = Kr + (16 * tb + 4 * g4) * a.krs + l16;
 #pragma unroll
                     for (int i = 0; i < NDPM; ++i) {
                         if (i < ndp) {
-                            const float4 c4 = *reinterpret_cast<const float4*>(
-                                Kc + (16 * (dt0 + i) + l16) * a.kcs + 16 * tb + 4 * g4);
-                            Wst[i] = mfma_f32_k4(c4.x, U[tb][0], Wst[i]);
-                            Wst[i] = mfma_f32_k4(c4.y, U[tb][1], Wst[i]);
-                            Wst[i] = mfma_f32_k4(c4.z, U[tb][2], Wst[i]);
-                            Wst[i] = mfma_f32_k4(c4.w, U[tb][3], Wst[i]);
+                            const LT* kc = kt + 16 * (dt0 + i);
+                            Wst[i] = mfma_f32_k4(kc[0], U[tb][0], Wst[i]);
+                            Wst[i] = mfma_f32_k4(kc[a.krs], U[tb][1], Wst[i]);
+                            Wst[i] = mfma_f32_k4(kc[2 * a.krs], U[tb][2], Wst[i]);
+                            Wst[i] = mfma_f32_k4(kc[3 * a.krs], U[tb][3], Wst[i]);
                         }
                     }
                 }
@@ -475,73 +596,18 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ host-side planning
-
-static int align16(int x) { return (x + 15) & ~15; }
-
-
-constexpr int kMaxLds = 160 * 1024;
-
-// Chooses the d_v split and the LDS layout; returns false when the shape does not fit.
-bool plan_forward(int BH, int d_k, int d_v, int nu, int C, bool bf16, FwdPlan* plan) {
-    const int D = 2 * d_k * nu;
-    if (D % 32 != 0 || d_v % 16 != 0 || D > 512) return false;
-    const int ND = D / 16, NVT_total = d_v / 16;
-    const int pair = bf16 ? 2 : 1;
-    const int es = bf16 ? 2 : 4;
-    // Candidate splits: fewest workgroups per (b, h) that still give >= 256 workgroups.
-    int R0 = NVT_total > 4 ? NVT_total / 4 : 1;
-    if (NVT_total % R0) return false;
-    for (int R = R0; R <= NVT_total; R *= 2) {
-        if (NVT_total % R) continue;
-        const int NVT = NVT_total / R;
-        if (NVT > 4) continue;
-        const bool enough = static_cast<int64_t>(BH) * R >= 256 || R == NVT_total;
-        if (!enough) continue;
-        for (int DP = 4 / NVT; DP >= 1; DP /= 2) {
-            if (ND % (DP * pair)) continue;
-            const int NDP = ND / DP;
-            if (NDP > 32) continue;
-            FwdArgs fa = {};
-            fa.kcs = C + 4;
-            fa.krs = bf16 ? D + 8 : D + 4;
-            fa.lss = C + 4;
-            fa.pss = C + 4;
-            int off = 0;
-            fa.off_kc = off;
-            off = align16(off + D * fa.kcs * es);
-            const int ustart = off;
-            fa.off_kr = ustart;
-            fa.off_qr = align16(fa.off_kr + C * fa.krs * es);
-            const int uend1 = align16(fa.off_qr + C * fa.krs * es);
-            fa.off_ls = ustart;
-            fa.off_ps = align16(fa.off_ls + C * fa.lss * 4);
-            fa.off_li = align16(fa.off_ps + C * fa.pss * es);
-            fa.off_red = align16(fa.off_li + C * kLiStride * 4);
-            const int uend2 = align16(fa.off_red + (DP > 1 ? 4 * 2 * C * kRedStride * 4 : 0));
-            off = uend1 > uend2 ? uend1 : uend2;
-            fa.off_small = off;
-            off = align16(off + 3 * C * 4);
-            if (off > kMaxLds) continue;
-            fa.R = R;
-            fa.NVT = NVT;
-            fa.DP = DP;
-            fa.NDP = NDP;
-            plan->R = R;
-            plan->NVT = NVT;
-            plan->DP = DP;
-            plan->NDP = NDP;
-            plan->NDPM = NDP <= 8 ? 8 : 32;
-            plan->args = fa;
-            plan->lds_bytes = off;
-            return true;
-        }
-    }
-    return false;
+// Memory-tile capacities (16-row d-tiles of W^T per wave) a kernel is instantiated with; the
+// plan picks the smallest capacity that holds a wave's share of D.  Chunks of 128 rows only fit
+// the LDS for small D, so they get the small capacities only.
+inline int fwd_ndpm_bucket(int ndp, int C) {
+    const int caps[] = {2, 4, 8, 12, 16, 24, 32};
+    for (int c : caps)
+        if (ndp <= c && (C < 128 || c <= 8)) return c;
+    return 0;
 }
 
 template <bool BF16, int C, int NDPM>
-static hipError_t launch_fwd_t(const FwdPlan& p, int BH, hipStream_t stream) {
+hipError_t launch_fwd_t(const FwdPlan& p, int BH, hipStream_t stream) {
     auto kern = delta_forward_kernel<BF16, C, NDPM>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
@@ -551,26 +617,34 @@ static hipError_t launch_fwd_t(const FwdPlan& p, int BH, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_delta_forward(const FwdPlan& plan_in, const void* q, const void* k,
-                                const void* v, const void* bl, const float* W0, void* y,
-                                float* Wf, int BH, int H, int T, int d_k, int d_v, int nu, int C,
-                                bool bf16, hipStream_t stream) {
-    FwdPlan p = plan_in;
-    FwdArgs& a = p.args;
-    a.q = q; a.k = k; a.v = v; a.bl = bl; a.W0 = W0; a.y = y; a.Wf = Wf;
-    a.BH = BH; a.H = H; a.T = T; a.d_k = d_k; a.d_v = d_v; a.nu = nu;
-#define FWA_FWD_CASE(BF, CC, NM)                                                     \
-    if (bf16 == BF && C == CC && p.NDPM == NM) return launch_fwd_t<BF, CC, NM>(p, BH, stream);
-    FWA_FWD_CASE(false, 16, 8) FWA_FWD_CASE(false, 16, 32)
-    FWA_FWD_CASE(false, 32, 8) FWA_FWD_CASE(false, 32, 32)
-    FWA_FWD_CASE(false, 64, 8) FWA_FWD_CASE(false, 64, 32)
-    FWA_FWD_CASE(false, 128, 8) FWA_FWD_CASE(false, 128, 32)
-    FWA_FWD_CASE(true, 16, 8) FWA_FWD_CASE(true, 16, 32)
-    FWA_FWD_CASE(true, 32, 8) FWA_FWD_CASE(true, 32, 32)
-    FWA_FWD_CASE(true, 64, 8) FWA_FWD_CASE(true, 64, 32)
-    FWA_FWD_CASE(true, 128, 8) FWA_FWD_CASE(true, 128, 32)
-#undef FWA_FWD_CASE
+template <bool BF16, int C>
+hipError_t launch_fwd_dispatch(const FwdPlan& p, int BH, hipStream_t stream) {
+    switch (p.NDPM) {
+        case 2: return launch_fwd_t<BF16, C, 2>(p, BH, stream);
+        case 4: return launch_fwd_t<BF16, C, 4>(p, BH, stream);
+        case 8: return launch_fwd_t<BF16, C, 8>(p, BH, stream);
+        default: break;
+    }
+    if constexpr (C < 128) {
+        switch (p.NDPM) {
+            case 12: return launch_fwd_t<BF16, C, 12>(p, BH, stream);
+            case 16: return launch_fwd_t<BF16, C, 16>(p, BH, stream);
+            case 24: return launch_fwd_t<BF16, C, 24>(p, BH, stream);
+            case 32: return launch_fwd_t<BF16, C, 32>(p, BH, stream);
+            default: break;
+        }
+    }
     return hipErrorInvalidValue;
 }
+
+// One translation unit per (dtype, chunk) instantiates the capacities above.
+hipError_t launch_fwd_f32_c16(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_f32_c32(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_f32_c64(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_f32_c128(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_bf16_c16(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_bf16_c32(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_bf16_c64(const FwdPlan& p, int BH, hipStream_t s);
+hipError_t launch_fwd_bf16_c128(const FwdPlan& p, int BH, hipStream_t s);
 
 }  // namespace fwa

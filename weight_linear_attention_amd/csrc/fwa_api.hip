@@ -133,7 +133,8 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     if (D > 512) return fail(FWA_ERR_UNSUPPORTED, "%s: D=2*d_k*nu=%lld > 512", fn, (long long)D);
     if (!mul_le(kIndexLimit, {BH, T, d_k > d_v ? d_k : d_v}) || !mul_le(kIndexLimit, {BH, d_v, D}))
         return fail(FWA_ERR_UNSUPPORTED, "%s: sizes overflow the index range", fn);
-    if (BH > (int64_t(1) << 26) || static_cast<int64_t>(T) * d_v > (int64_t(1) << 31))
+    if (BH > (int64_t(1) << 26) || static_cast<int64_t>(T) * d_v >= (int64_t(1) << 31) ||
+        static_cast<int64_t>(T) * d_k >= (int64_t(1) << 31))
         return fail(FWA_ERR_UNSUPPORTED, "%s: too many (b, h) slices for one launch", fn);
     fwa::FwdPlan plan;
     if (!fwa::plan_forward(static_cast<int>(BH), d_k, d_v, nu, chunk, dtype == FWA_BF16, &plan))

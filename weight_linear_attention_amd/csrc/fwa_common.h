@@ -46,6 +46,12 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
     else static_cast<float*>(p)[i] = v;
 }
 
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(u16 h) { return bf16_bits_to_f32(h); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ u16 from_f32<u16>(float x) { return f32_to_bf16_bits(x); }
+
 __device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
 
 // sigmoid evaluated so that neither branch overflows; sigmoid(-inf) = 0, sigmoid(+inf) = 1.
@@ -66,6 +72,16 @@ __device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
 // Lane l holds A[l%16][l/16] and B[l/16][l%16]; the result layout is as above.
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// receives in slot e the (i % 4)-th 16-bit element of the 8 bytes addressed by lane
+// 4 e + i / 4 of the group.  `p` must point into LDS and be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr_b16x4(const void* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(p)));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }

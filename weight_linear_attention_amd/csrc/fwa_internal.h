@@ -18,8 +18,8 @@ struct FwdArgs {
     float* Wf;
     int BH, H, T, d_k, d_v, nu;
     int R, NVT, DP, NDP;
-    int off_kc, off_kr, off_qr, off_ls, off_ps, off_li, off_red, off_small;
-    int kcs, krs, lss, pss;
+    int off_kr, off_qr, off_ls, off_ps, off_li, off_red, off_xs, off_small;
+    int krs, lss, pss;
 };
 
 struct FwdPlan {

@@ -64,47 +64,91 @@ __device__ __forceinline__ float group_sum(float v, int d_k, int l) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Raw DPFP products of one row (lane jl of a d_k-lane group holds k_jl and q_jl) for every
-// shift, written to the row-major K and Q tiles; returns the row sums through sk, sq.  With a
-// compile-time NU all rolled operands are fetched (ds_bpermute) before any LDS write, so the
-// writes never sit in front of a permute the lane is waiting for.
-template <typename LT, int NU>
-__device__ __forceinline__ void dpfp_row(float kv, float qv, int nu, int jl, int gbase, int d_k,
-                                         LT* krow, LT* qrow, float& sk, float& sq) {
+// Roll constants of one lane for shifts 1..4: the ds_bpermute byte address of the source lane
+// and the sign mask.  For shift i the rolled operand of position j is relu([k,-k]) at
+// m = (j - i) mod 2 d_k, i.e. lane (m mod d_k) of the row's group, negated when m >= d_k.
+struct RollConst {
+    int src4[4];
+    uint32_t smask[4];
+};
+
+__device__ __forceinline__ RollConst roll_consts(int jl, int gbase, int d_k) {
+    RollConst rc;
+#pragma unroll
+    for (int i = 1; i <= 4; ++i) {
+        const int m = (jl - i) & (2 * d_k - 1);
+        rc.src4[i - 1] = (gbase + (m & (d_k - 1))) << 2;
+        rc.smask[i - 1] = (m & d_k) ? 0x80000000u : 0u;
+    }
+    return rc;
+}
+
+__device__ __forceinline__ float flip(float x, uint32_t mask) {
+    return __uint_as_float(__float_as_uint(x) ^ mask);
+}
+
+// K and Q tiles store their D columns in an internal order that puts the two halves of a
+// shift block next to each other: internal column 2 ((i-1) d_k + j) + h holds DPFP position
+// (i-1) 2 d_k + h d_k + j (h = 0: relu(k_j) * ..., h = 1: relu(-k_j) * ...).  Inner products
+// over D do not depend on the order; the memory W^T uses the same order internally and is
+// mapped back at load/store.  So a lane writes both halves of its position with one store.
+__device__ __forceinline__ int orig_col(int c, int d_k) {
+    const int m = c >> 1;
+    return (m / d_k) * 2 * d_k + (c & 1) * d_k + (m % d_k);
+}
+
+__device__ __forceinline__ float relu_f(float x) { return fmaxf(x, 0.0f); }
+
+template <typename LT>
+__device__ __forceinline__ void store_pair(LT* p, float lo, float hi) {
+    if constexpr (sizeof(LT) == 2) *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(lo, hi);
+    else *reinterpret_cast<float2*>(p) = make_float2(lo, hi);
+}
+
+// Raw DPFP products of R rows for NU shifts (lane jl of a DK-lane group holds k_jl and q_jl
+// of its row), written as (h = 0, h = 1) pairs to the row-major K and Q tiles.  All loads and
+// permutes of the R rows are issued before the first LDS write.
+template <typename LT, int NU, int R>
+__device__ __forceinline__ void dpfp_rows(const float (&kv)[R], const float (&qv)[R],
+                                          const RollConst& rc, int d_k, LT* const (&krow)[R],
+                                          LT* const (&qrow)[R]) {
+    float xk[R][NU], xq[R][NU];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            xk[r][i] = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(rc.src4[i], __float_as_int(kv[r]))),
+                            rc.smask[i]);
+            xq[r][i] = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(rc.src4[i], __float_as_int(qv[r]))),
+                            rc.smask[i]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float ka = relu_f(kv[r]), kb = relu_f(-kv[r]), qa = relu_f(qv[r]), qb = relu_f(-qv[r]);
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            // ka, kb >= 0, so ka * relu(x) = relu(ka * x) and kb * relu(-x) = relu(-(kb * x))
+            store_pair(krow[r] + 2 * i * d_k, relu_f(ka * xk[r][i]), relu_f(-(kb * xk[r][i])));
+            store_pair(qrow[r] + 2 * i * d_k, relu_f(qa * xq[r][i]), relu_f(-(qb * xq[r][i])));
+        }
+    }
+}
+
+// Any nu (slow path, one row): the permute address and sign are computed per shift.
+template <typename LT>
+__device__ __forceinline__ void dpfp_row_any(float kv, float qv, int nu, int jl, int gbase,
+                                             int d_k, LT* krow, LT* qrow) {
     const int two_dk = 2 * d_k;
-    const float ka = relu(kv), kb = relu(-kv), qa = relu(qv), qb = relu(-qv);
-    auto emit = [&](int i, float xk, float xq) {
-        const float pk1 = ka * relu(xk), pk2 = kb * relu(-xk);
-        const float pq1 = qa * relu(xq), pq2 = qb * relu(-xq);
-        sk += pk1 + pk2;
-        sq += pq1 + pq2;
-        const int o1 = (i - 1) * two_dk;
-        krow[o1] = from_f32<LT>(pk1);
-        krow[o1 + d_k] = from_f32<LT>(pk2);
-        qrow[o1] = from_f32<LT>(pq1);
-        qrow[o1 + d_k] = from_f32<LT>(pq2);
-    };
-    // rolled source position m = (j - i) mod 2 d_k (d_k is a power of two): lane (m mod d_k)
-    // of the row's group, negated when m falls in the -k half.
-    auto fetch = [&](int i, float& xk, float& xq) {
+    const float ka = relu_f(kv), kb = relu_f(-kv), qa = relu_f(qv), qb = relu_f(-qv);
+    for (int i = 1; i <= nu; ++i) {
         const int m = (jl - i) & (two_dk - 1);
         const int src4 = (gbase + (m & (d_k - 1))) << 2;
-        const float sgn = (m & d_k) ? -1.0f : 1.0f;
-        xk = sgn * __int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(kv)));
-        xq = sgn * __int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(qv)));
-    };
-    if constexpr (NU > 0) {
-        float xk[NU], xq[NU];
-#pragma unroll
-        for (int i = 1; i <= NU; ++i) fetch(i, xk[i - 1], xq[i - 1]);
-#pragma unroll
-        for (int i = 1; i <= NU; ++i) emit(i, xk[i - 1], xq[i - 1]);
-    } else {
-        for (int i = 1; i <= nu; ++i) {
-            float xk, xq;
-            fetch(i, xk, xq);
-            emit(i, xk, xq);
-        }
+        const uint32_t sm = (m & d_k) ? 0x80000000u : 0u;
+        const float xk = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(kv))), sm);
+        const float xq = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(qv))), sm);
+        store_pair(krow + 2 * (i - 1) * d_k, relu_f(ka * xk), relu_f(-(kb * xk)));
+        store_pair(qrow + 2 * (i - 1) * d_k, relu_f(qa * xq), relu_f(-(qb * xq)));
     }
 }
 
@@ -112,8 +156,8 @@ template <bool BF16, int C, int NDPM>
 __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     using LT = std::conditional_t<BF16, u16, float>;  // LDS element type of K, Q and P
     constexpr int NT = C / 16;
-    constexpr int NGP = NT * (NT + 1);                 // G and P lower-triangle tiles
-    constexpr int MAXTW = (NGP + 3) / 4;               // of those, per wave
+    constexpr int NQ = (NT + 1) / 2;                   // tile-row pairs {q, NT-1-q}
+    constexpr int UPW = (2 * NQ + 3) / 4;              // G/P units per wave
     constexpr int RS = C + 4;                          // row stride of the partials buffer
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -122,6 +166,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     using ITs = std::conditional_t<BF16, u16, float>;
     ITs* Xk = reinterpret_cast<ITs*>(smem + a.off_xs);              // [C][d_k] raw k rows
     ITs* Xq = Xk + C * a.d_k;                                       // [C][d_k] raw q rows
+    ITs* Xv = Xq + C * a.d_k;                                       // [C][16 NVT] v slice
     float* Ls = reinterpret_cast<float*>(smem + a.off_ls);   // [C][lss] beta*strict_lower(G)
     LT* Ps = reinterpret_cast<LT*>(smem + a.off_ps);          // [C][pss] lower_incl(Q K^T)
     float* Li = reinterpret_cast<float*>(smem + a.off_li);    // [C][20]  diagonal inverses
@@ -156,10 +201,12 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     for (int i = 0; i < NDPM; ++i) {
         Wst[i] = zero4();
         if (has_state && i < ndp && a.W0) {
+            // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
             const float* src = a.W0 + (static_cast<int64_t>(bh) * d_v + vcol) * D +
-                               16 * (dt0 + i) + 4 * g4;
-            const float4 t4 = *reinterpret_cast<const float4*>(src);
-            Wst[i] = f32x4{t4.x, t4.y, t4.z, t4.w};
+                               orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            const float2 lo = *reinterpret_cast<const float2*>(src);
+            const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
+            Wst[i] = f32x4{lo.x, hi.x, lo.y, hi.y};
         }
     }
 
@@ -187,8 +234,13 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     const int ubytes = d_k * static_cast<int>(sizeof(IT));  // bytes per row
     const int nunits = C * ubytes / 16;              // 16-byte units per chunk block
     const int nr = (nunits + 255) / 256;
-    uint4 kraw[NRM], qraw[NRM];
+    uint4 kraw[NRM], qraw[NRM], vraw[NRM];
     IT blpre = IT(0);
+    // V rows of this workgroup's d_v slice: VB = 16 * NVT columns, 16-byte units per row.
+    const int vbw = r * a.NVT * 16;                  // first column of the slice
+    const int vupr = a.NVT * 16 * static_cast<int>(sizeof(IT)) / 16;
+    const int nvunits = C * vupr;
+    const int nvr = (nvunits + 255) / 256;
     auto prefetch = [&](int chn) {
         const int tn0 = chn * C;
         const int Cn = min(C, T - tn0);
@@ -203,6 +255,14 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 kraw[i] = *reinterpret_cast<const uint4*>(kc + off);
                 qraw[i] = *reinterpret_cast<const uint4*>(qc + off);
             }
+            if (i < nvr) {
+                const int u = tid + 256 * i;
+                const int row = u / vupr;
+                const bool ok = u < nvunits && row < Cn;
+                const IT* src = vB + static_cast<int64_t>(tn0 + (ok ? row : 0)) * d_v + vbw +
+                                (ok ? (u % vupr) : 0) * (16 / static_cast<int>(sizeof(IT)));
+                vraw[i] = *reinterpret_cast<const uint4*>(src);
+            }
         }
         blpre = bB[tn0 + min(tid, Cn - 1)];
     };
@@ -213,17 +273,6 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
         const int Cc = min(C, T - t0);
 
         // ---------------- A: DPFP rows, beta, and this wave's V tile (consumed in C)
-        f32x4 Xv[NT];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * g4 + e;
-                const bool ok = has_state && t < Cc;
-                const float vv = to_f32(vB[(t0 + (ok ? t : 0)) * d_v + vcol]);
-                Xv[tt][e] = ok ? vv : 0.0f;
-            }
-        }
         // Stage this chunk's raw rows (zeros past the sequence end) for the DPFP passes.
 #pragma unroll
         for (int i = 0; i < NRM; ++i) {
@@ -238,28 +287,42 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                         make_uint4(qr4.x & m, qr4.y & m, qr4.z & m, qr4.w & m);
                 }
             }
+            if (i < nvr) {
+                const int u = tid + 256 * i;
+                if (u < nvunits) {
+                    const uint32_t m = u / vupr < Cc ? 0xffffffffu : 0u;
+                    const uint4 v4 = vraw[i];
+                    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Xv) + u * 16) =
+                        make_uint4(v4.x & m, v4.y & m, v4.z & m, v4.w & m);
+                }
+            }
         }
         if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(to_f32(blpre)) : 0.0f;
-        if (ch + 1 < nchunks) prefetch(ch + 1);
         __syncthreads();
 
-        // One row per d_k-lane group and pass; the shift count is a compile-time constant for
-        // nu <= 4 so each row's permutes are all issued before its writes.
+        // One row per d_k-lane group and pass, two passes per iteration; the shift count is
+        // a compile-time constant on the fast path (nu <= 4).  Row sums come from the MFMA
+        // pipe in phase B.
         auto dpfp_passes = [&](auto nu_tag) {
             constexpr int NU = decltype(nu_tag)::value;
-#pragma unroll 4
+            const RollConst rc = roll_consts(jl, gbase, d_k);
+            for (int p = 0; p < npass; p += 2) {
+                const bool two = p + 1 < npass;
+                const int t0r = p * 4 * rpw + w * rpw + grp;
+                const int t1r = two ? t0r + 4 * rpw : t0r;
+                const float kv[2] = {to_f32(Xk[t0r * d_k + jl]), to_f32(Xk[t1r * d_k + jl])};
+                const float qv[2] = {to_f32(Xq[t0r * d_k + jl]), to_f32(Xq[t1r * d_k + jl])};
+                LT* const krow[2] = {Kr + t0r * a.krs + 2 * jl, Kr + t1r * a.krs + 2 * jl};
+                LT* const qrow[2] = {Qr + t0r * a.krs + 2 * jl, Qr + t1r * a.krs + 2 * jl};
+                dpfp_rows<LT, NU, 2>(kv, qv, rc, d_k, krow, qrow);
+            }
+        };
+        auto dpfp_passes_any = [&]() {
             for (int p = 0; p < npass; ++p) {
                 const int t = p * 4 * rpw + w * rpw + grp;
                 const float kv = to_f32(Xk[t * d_k + jl]), qv = to_f32(Xq[t * d_k + jl]);
-                float sk = 0.0f, sq = 0.0f;
-                dpfp_row<LT, NU>(kv, qv, nu, jl, gbase, d_k, Kr + t * a.krs + jl,
-                                 Qr + t * a.krs + jl, sk, sq);
-                sk = group_sum(sk, d_k, l);
-                sq = group_sum(sq, d_k, l);
-                if (jl == 0) {
-                    rhok[t] = __builtin_amdgcn_rcpf(sk + kDpfpEps);
-                    rhoq[t] = __builtin_amdgcn_rcpf(sq + kDpfpEps);
-                }
+                dpfp_row_any<LT>(kv, qv, nu, jl, gbase, d_k, Kr + t * a.krs + 2 * jl,
+                                 Qr + t * a.krs + 2 * jl);
             }
         };
         switch (nu) {
@@ -267,51 +330,90 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             case 2: dpfp_passes(std::integral_constant<int, 2>{}); break;
             case 3: dpfp_passes(std::integral_constant<int, 3>{}); break;
             case 4: dpfp_passes(std::integral_constant<int, 4>{}); break;
-            default: dpfp_passes(std::integral_constant<int, 0>{}); break;
+            default: dpfp_passes_any(); break;
         }
         __syncthreads();
 
         // ---------------- B: G, P tiles; K W^T and Q W^T against the memory
-        // Tiles w, w+4, ... of the list [G tiles (ta >= tb)..., P tiles (ta >= tb)...]; the
-        // k-step loop is outside so the wave's independent tiles interleave on the MFMA pipe.
-        f32x4 gp[MAXTW];
-        const LT* Ap[MAXTW];
-        const LT* Bp[MAXTW];
+        // G = K K^T and P = Q K^T lower triangles in 16x16 tiles.  Work is split in units: one
+        // of G or P for the tile rows {q, NT-1-q}; unit u goes to wave u % 4.  Inside a unit the
+        // row operands are loaded once per k-step and reused by every tile of the two rows,
+        // and the tiles are independent accumulators that interleave on the MFMA pipe.
+        // gpa[ui][tb]: tile (ra, tb); gpb[ui][tb]: tile (rb, tb) (static register indices)
+        // sa/sb: row sums of the unit's rows (the same operands times a ones matrix).
+        f32x4 gpa[UPW][NT], gpb[UPW][NT], sa[UPW], sb[UPW];
 #pragma unroll
-        for (int j = 0; j < MAXTW; ++j) {
-            gp[j] = zero4();
-            const int tix = min(w + 4 * j, NGP - 1);
-            const bool isP = tix >= NGP / 2;
-            const int idx = isP ? tix - NGP / 2 : tix;
-            int ta = 0;
-            while ((ta + 1) * (ta + 2) / 2 <= idx) ++ta;
-            const int tb = idx - ta * (ta + 1) / 2;
-            Ap[j] = (isP ? Qr : Kr) + (16 * ta + l16) * a.krs;
-            Bp[j] = Kr + (16 * tb + l16) * a.krs;
+        for (int ui = 0; ui < UPW; ++ui) {
+            sa[ui] = sb[ui] = zero4();
+#pragma unroll
+            for (int tb = 0; tb < NT; ++tb) gpa[ui][tb] = gpb[ui][tb] = zero4();
         }
-        if constexpr (BF16) {
+#pragma unroll
+        for (int ui = 0; ui < UPW; ++ui) {
+            const int u = w + 4 * ui;
+            if (u < 2 * NQ) {
+                const bool isP = u >= NQ;
+                const int q = isP ? u - NQ : u;
+                const int ra = q, rb = NT - 1 - q;       // rb >= ra
+                const LT* Xa = (isP ? Qr : Kr) + (16 * ra + l16) * a.krs;
+                const LT* Xb = (isP ? Qr : Kr) + (16 * rb + l16) * a.krs;
+                const LT* Kb = Kr + l16 * a.krs;
+                if constexpr (BF16) {
+                    bf16x8 ones;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
 #pragma unroll 2
-            for (int kk = 0; kk < D / 32; ++kk) {
+                    for (int kk = 0; kk < D / 32; ++kk) {
+                        const int c0 = 32 * kk + 8 * g4;
+                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Xa + c0);
+                        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Xb + c0);
+                        sa[ui] = mfma_bf16_k32(va, ones, sa[ui]);
+                        if (rb != ra) sb[ui] = mfma_bf16_k32(vb, ones, sb[ui]);
 #pragma unroll
-                for (int j = 0; j < MAXTW; ++j) {
-                    if (w + 4 * j < NGP) {
-                        const bf16x8 av = *reinterpret_cast<const bf16x8*>(Ap[j] + 32 * kk + 8 * g4);
-                        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(Bp[j] + 32 * kk + 8 * g4);
-                        gp[j] = mfma_bf16_k32(av, bv, gp[j]);
+                        for (int tb = 0; tb < NT; ++tb) {
+                            if (tb <= rb) {
+                                const bf16x8 kv8 = *reinterpret_cast<const bf16x8*>(Kb + 16 * tb * a.krs + c0);
+                                if (tb <= ra) gpa[ui][tb] = mfma_bf16_k32(va, kv8, gpa[ui][tb]);
+                                if (rb != ra) gpb[ui][tb] = mfma_bf16_k32(vb, kv8, gpb[ui][tb]);
+                            }
+                        }
                     }
-                }
-            }
-        } else {
-            for (int kk = 0; kk < D / 16; ++kk) {
+                } else {
+#pragma unroll 2
+                    for (int kk = 0; kk < D / 16; ++kk) {
+                        const int c0 = 16 * kk + 4 * g4;
+                        const float4 va = *reinterpret_cast<const float4*>(Xa + c0);
+                        const float4 vb = *reinterpret_cast<const float4*>(Xb + c0);
+                        sa[ui] = mfma_f32_k4(va.x, 1.0f, sa[ui]);
+                        sa[ui] = mfma_f32_k4(va.y, 1.0f, sa[ui]);
+                        sa[ui] = mfma_f32_k4(va.z, 1.0f, sa[ui]);
+                        sa[ui] = mfma_f32_k4(va.w, 1.0f, sa[ui]);
+                        if (rb != ra) {
+                            sb[ui] = mfma_f32_k4(vb.x, 1.0f, sb[ui]);
+                            sb[ui] = mfma_f32_k4(vb.y, 1.0f, sb[ui]);
+                            sb[ui] = mfma_f32_k4(vb.z, 1.0f, sb[ui]);
+                            sb[ui] = mfma_f32_k4(vb.w, 1.0f, sb[ui]);
+                        }
 #pragma unroll
-                for (int j = 0; j < MAXTW; ++j) {
-                    if (w + 4 * j < NGP) {
-                        const float4 av = *reinterpret_cast<const float4*>(Ap[j] + 16 * kk + 4 * g4);
-                        const float4 bv = *reinterpret_cast<const float4*>(Bp[j] + 16 * kk + 4 * g4);
-                        gp[j] = mfma_f32_k4(av.x, bv.x, gp[j]);
-                        gp[j] = mfma_f32_k4(av.y, bv.y, gp[j]);
-                        gp[j] = mfma_f32_k4(av.z, bv.z, gp[j]);
-                        gp[j] = mfma_f32_k4(av.w, bv.w, gp[j]);
+                        for (int tb = 0; tb < NT; ++tb) {
+                            if (tb <= rb) {
+                                const float4 k4 = *reinterpret_cast<const float4*>(Kb + 16 * tb * a.krs + c0);
+                                if (tb <= ra) {
+                                    f32x4& g = gpa[ui][tb];
+                                    g = mfma_f32_k4(va.x, k4.x, g);
+                                    g = mfma_f32_k4(va.y, k4.y, g);
+                                    g = mfma_f32_k4(va.z, k4.z, g);
+                                    g = mfma_f32_k4(va.w, k4.w, g);
+                                }
+                                if (rb != ra) {
+                                    f32x4& g = gpb[ui][tb];
+                                    g = mfma_f32_k4(vb.x, k4.x, g);
+                                    g = mfma_f32_k4(vb.y, k4.y, g);
+                                    g = mfma_f32_k4(vb.z, k4.z, g);
+                                    g = mfma_f32_k4(vb.w, k4.w, g);
+                                }
+                            }
+                        }
                     }
                 }
             }
@@ -370,33 +472,59 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 }
             }
         }
+        // normalisers 1/(S + eps) of the unit's rows (G units: K rows, P units: Q rows)
+#pragma unroll
+        for (int ui = 0; ui < UPW; ++ui) {
+            const int u = w + 4 * ui;
+            if (u < 2 * NQ && l16 == 0) {
+                const bool isP = u >= NQ;
+                const int q = isP ? u - NQ : u;
+                const int ra = q, rb = NT - 1 - q;
+                float* rho = isP ? rhoq : rhok;
+                f32x4 r0, r1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    r0[e] = __builtin_amdgcn_rcpf(sa[ui][e] + kDpfpEps);
+                    r1[e] = __builtin_amdgcn_rcpf(sb[ui][e] + kDpfpEps);
+                }
+                *reinterpret_cast<f32x4*>(rho + 16 * ra + 4 * g4) = r0;
+                if (rb != ra) *reinterpret_cast<f32x4*>(rho + 16 * rb + 4 * g4) = r1;
+            }
+        }
         __syncthreads();  // Q is dead from here; its space is reused
 
         // ---------------- B': scaled G and P to LDS, state partials to the reduction buffer
 #pragma unroll
-        for (int j = 0; j < MAXTW; ++j) {
-            const int tix = w + 4 * j;
-            if (tix < NGP) {
-                const bool isP = tix >= NGP / 2;
-                const int idx = isP ? tix - NGP / 2 : tix;
-                int ta = 0;
-                while ((ta + 1) * (ta + 2) / 2 <= idx) ++ta;
-                const int tb = idx - ta * (ta + 1) / 2;
-                const int s = 16 * tb + l16, tr = 16 * ta + 4 * g4;
-                const float rks = rhok[s];
-                if (isP) {
-                    const f32x4 rq = *reinterpret_cast<const f32x4*>(rhoq + tr);
+        for (int ui = 0; ui < UPW; ++ui) {
+            const int u = w + 4 * ui;
+            if (u < 2 * NQ) {
+                const bool isP = u >= NQ;
+                const int q = isP ? u - NQ : u;
+                const int ra = q, rb = NT - 1 - q;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float val = s <= tr + e ? rq[e] * rks * gp[j][e] : 0.0f;
-                        Ps[(tr + e) * a.pss + s] = from_f32<LT>(val);
+                for (int k2 = 0; k2 < 2 * NT; ++k2) {
+                    // k2 < NT: tile (ra, k2) from gpa; k2 >= NT: tile (rb, k2 - NT) from gpb
+                    const bool rowa = k2 < NT;
+                    const int ta = rowa ? ra : rb;
+                    const int tb = rowa ? k2 : k2 - NT;
+                    if (tb > ta || (!rowa && rb == ra)) continue;
+                    const f32x4 acc = rowa ? gpa[ui][k2 % NT] : gpb[ui][k2 % NT];
+                    const int s = 16 * tb + l16, tr = 16 * ta + 4 * g4;
+                    const float rks = rhok[s];
+                    if (isP) {
+                        const f32x4 rq = *reinterpret_cast<const f32x4*>(rhoq + tr);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float val = s <= tr + e ? rq[e] * rks * acc[e] : 0.0f;
+                            Ps[(tr + e) * a.pss + s] = from_f32<LT>(val);
+                        }
+                    } else {
+                        const f32x4 rk = *reinterpret_cast<const f32x4*>(rhok + tr);
+                        const f32x4 bt = *reinterpret_cast<const f32x4*>(betas + tr);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            Ls[(tr + e) * a.lss + s] = s < tr + e ? bt[e] * rk[e] * rks * acc[e] : 0.0f;
                     }
-                } else {
-                    const f32x4 rk = *reinterpret_cast<const f32x4*>(rhok + tr);
-                    const f32x4 bt = *reinterpret_cast<const f32x4*>(betas + tr);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Ls[(tr + e) * a.lss + s] = s < tr + e ? bt[e] * rk[e] * rks * gp[j][e] : 0.0f;
                 }
             }
         }
@@ -410,6 +538,8 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
         __syncthreads();
 
         // ---------------- C: diagonal-block inverses; reduce the state partials
+        // (the next chunk's inputs are requested here: their registers are not live in B)
+        if (ch + 1 < nchunks) prefetch(ch + 1);
         if (tid < C) {
             // Column sc of the inverse of the unit lower 16x16 block ab; each row's dot product
             // is split over four partial sums to keep the dependency chains short.
@@ -449,7 +579,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 16 * tt + 4 * g4 + e;
-                    X[tt][e] = Xv[tt][e] - rhok[t] * S1[tt][e];
+                    X[tt][e] = to_f32(Xv[t * (16 * a.NVT) + 16 * vt + l16]) - rhok[t] * S1[tt][e];
                     QW[tt][e] *= rhoq[t];
                 }
             }
@@ -588,9 +718,10 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < NDPM; ++i) {
             if (i < ndp) {
-                float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + vcol) * D + 16 * (dt0 + i) +
-                             4 * g4;
-                *reinterpret_cast<float4*>(dst) = make_float4(Wst[i][0], Wst[i][1], Wst[i][2], Wst[i][3]);
+                float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + vcol) * D +
+                             orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+                *reinterpret_cast<float2*>(dst) = make_float2(Wst[i][0], Wst[i][2]);
+                *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[i][1], Wst[i][3]);
             }
         }
     }

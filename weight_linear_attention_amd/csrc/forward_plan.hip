@@ -46,7 +46,7 @@ bool plan_forward(int BH, int d_k, int d_v, int nu, int C, bool bf16, FwdPlan* p
             const int uend2 = align16(fa.off_red + (DP > 1 ? 4 * 2 * 16 * (C + 4) * 4 : 0));
             off = uend1 > uend2 ? uend1 : uend2;
             fa.off_xs = off;                      // raw k and q rows of the chunk
-            off = align16(off + 2 * C * d_k * es);
+            off = align16(off + (2 * C * d_k + C * 16 * NVT) * es);
             fa.off_small = off;
             off = align16(off + 3 * C * 4);
             if (off > kMaxLds) continue;

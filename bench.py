@@ -11,6 +11,8 @@ already resident in HBM when timing starts.  Other workloads (--workload):
     b4_h8_t4096_d64_nu2_bf16_carried, b8_h16_t16384_d64_nu3_bf16   forward only
     decode_b256_h8_d64_nu1_f32                                      one fwa_delta_step per step
     dpfp_b8_h16_t16384_d64_nu3_bf16                                 fwa_dpfp on q and k
+    copy_calibration                                                a 1 GiB device copy (the
+                                                                    reference for HBM counters)
 
 Prints ONE JSON line.  `roofline` describes the dominant kernel: algorithmic bytes or flops of
 one launch divided by its mean duration, measured with HIP events on the launch stream over the
@@ -78,6 +80,22 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = args.workload
+    if name == "copy_calibration":
+        # A plain device-to-device copy of a known size (1 GiB read + 1 GiB written): the
+        # reference that HBM byte counters (FETCH_SIZE, WRITE_SIZE) are scaled against.
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        print(json.dumps({"workload": "copy_calibration", "bytes_read": 4 * n,
+                          "bytes_written": 4 * n, "seconds": dt}), flush=True)
+        return
     kind = "prefill+decode"
     if name.startswith("dpfp_"):
         kind, w = "dpfp", workload(name[len("dpfp_"):])
@@ -166,7 +184,7 @@ def main():
     value = tokens * steps / elapsed
 
     if kind in ("prefill", "prefill+decode"):
-        kernel_file = "forward_kernel.hip"
+        kernel_file = "forward_kernel.h"
         flops = BH * w.T * (6 * D * w.d_v + 6 * D)
         nbytes = (BH * w.T * ((3 * w.d_k + 1) * es + w.d_v * es)
                   + BH * w.d_v * D * 4 * (1 + (d["W0"] is not None)))

@@ -21,6 +21,21 @@ def _dev(inp):
     return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
 
 
+FORWARD_PATHS = ["chunked", "fused"]
+
+
+@pytest.fixture(params=FORWARD_PATHS)
+def path(request, monkeypatch):
+    """Runs a forward test once per implementation (FWA_FORWARD_PATH)."""
+    monkeypatch.setenv("FWA_FORWARD_PATH", request.param)
+    return request.param
+
+
+def _skip_unless(path, chunk):
+    if path == "chunked" and chunk not in (32, 64):
+        pytest.skip("the chunked path takes chunks of 32 and 64 rows")
+
+
 def _forward(inp_d, nu, chunk, W0=True):
     y, Wf = fwa.delta_forward(inp_d["q"], inp_d["k"], inp_d["v"], inp_d["beta_logit"],
                               inp_d["W0"] if W0 else None, chunk=chunk, nu=nu)
@@ -85,9 +100,10 @@ FWD_CASES = [
 
 
 @pytest.mark.parametrize("name,ov", FWD_CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(FWD_CASES)])
-def test_forward_parity(name, ov):
+def test_forward_parity(name, ov, path):
     w = workload(name, **ov)
-    log(f"forward {w}")
+    _skip_unless(path, w.chunk)
+    log(f"forward[{path}] {w}")
     inp = make_inputs(w)
     y, Wf = _forward(_dev(inp), w.nu, w.chunk)
     yr, Wr = oracle_forward(inp, w.nu)
@@ -97,16 +113,25 @@ def test_forward_parity(name, ov):
     assert ey <= tol and ew <= tol
 
 
-def test_forward_full_size_long_sequence_sampled():
+_FULL_PICKS = [(0, 0), (3, 7), (7, 15), (5, 2), (1, 11), (6, 9)]
+
+
+@pytest.fixture(scope="module")
+def full_size_case():
+    """Inputs of the 8 x 16 x 16384 workload and the oracle on 6 sampled (b, h) slices."""
+    w = workload("b8_h16_t16384_d64_nu3_bf16")
+    inp = make_inputs(w)
+    return w, inp, oracle_forward(inp, w.nu, bh_index=_FULL_PICKS)
+
+
+def test_forward_full_size_long_sequence_sampled(path, full_size_case):
     """The 8 x 16 x 16384 (D 384, bf16) workload at full size, chunk 64, in the launch
     configuration the benchmark uses; the oracle checks 6 sampled (b, h) slices end to end."""
-    w = workload("b8_h16_t16384_d64_nu3_bf16")
-    log(f"forward full {w}")
-    inp = make_inputs(w)
+    w, inp, (yr, Wr) = full_size_case
+    log(f"forward[{path}] full {w}")
     y, Wf = _forward(_dev(inp), w.nu, 64)
     assert torch.isfinite(y.float()).all() and torch.isfinite(Wf).all()
-    picks = [(0, 0), (3, 7), (7, 15), (5, 2), (1, 11), (6, 9)]
-    yr, Wr = oracle_forward(inp, w.nu, bh_index=picks)
+    picks = _FULL_PICKS
     sel = tuple(torch.tensor(ix) for ix in zip(*picks))
     ey = normwise(to_f64(y.cpu()[sel])[None], yr, 2)
     ew = normwise(to_f64(Wf.cpu()[sel])[None], Wr, 2)
@@ -114,7 +139,7 @@ def test_forward_full_size_long_sequence_sampled():
     assert ey <= 2e-2 and ew <= 2e-2
 
 
-def test_forward_T0_and_empty():
+def test_forward_T0_and_empty(path):
     w = workload("h8_t1024_d64_nu1_f32", T=0, w0_std=0.1)
     inp = _dev(make_inputs(w))
     y, Wf = _forward(inp, w.nu, 64)
@@ -127,7 +152,7 @@ def test_forward_T0_and_empty():
     assert y.numel() == 0
 
 
-def test_forward_in_place_carry_and_segments():
+def test_forward_in_place_carry_and_segments(path):
     """forward(T1) then forward(T2) with W0 = W_final (in place) equals forward(T1 + T2)."""
     w = workload("b4_h8_t4096_d64_nu2_bf16_carried", T=700, B=2)
     inp = _dev(make_inputs(w))
@@ -146,15 +171,23 @@ def test_forward_in_place_carry_and_segments():
     assert e1 <= 2e-2 and e2 <= 2e-2
 
 
-def test_forward_chunk_independence_and_determinism():
+def test_forward_chunk_independence_and_determinism(monkeypatch):
+    """Every (implementation, chunk) pair agrees with the others; each is deterministic."""
     w = workload("h8_t1024_d64_nu1_f32", T=500, w0_std=0.02)
     inp = _dev(make_inputs(w))
-    outs = {c: _forward(inp, w.nu, c) for c in (16, 32, 64)}
-    for c in (16, 32):
-        assert normwise(to_f64(outs[c][0]), to_f64(outs[64][0]), 2) <= 1e-4
-        assert normwise(to_f64(outs[c][1]), to_f64(outs[64][1]), 2) <= 1e-4
-    y2, W2 = _forward(inp, w.nu, 64)
-    assert torch.equal(y2, outs[64][0]) and torch.equal(W2, outs[64][1])   # run to run
+    outs = {}
+    for p in FORWARD_PATHS:
+        monkeypatch.setenv("FWA_FORWARD_PATH", p)
+        for c in ((32, 64) if p == "chunked" else (16, 32, 64)):
+            outs[(p, c)] = _forward(inp, w.nu, c)
+    ref = outs[("fused", 64)]
+    for key, (y, Wf) in outs.items():
+        assert normwise(to_f64(y), to_f64(ref[0]), 2) <= 1e-4, key
+        assert normwise(to_f64(Wf), to_f64(ref[1]), 2) <= 1e-4, key
+    for p in FORWARD_PATHS:
+        monkeypatch.setenv("FWA_FORWARD_PATH", p)
+        y2, W2 = _forward(inp, w.nu, 64)
+        assert torch.equal(y2, outs[(p, 64)][0]) and torch.equal(W2, outs[(p, 64)][1])
 
 
 def test_forward_unsupported_shapes_raise():

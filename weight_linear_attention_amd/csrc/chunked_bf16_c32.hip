@@ -1,0 +1,8 @@
+// Instantiates the three-launch chunked forward for bf16 inputs and chunks of 32 rows.
+#include "chunked_kernels.h"
+
+namespace fwa {
+hipError_t launch_chunked_bf16_c32(const ChunkPlan& p, hipStream_t s) {
+    return launch_chunked_t<true, 32>(p, s);
+}
+}  // namespace fwa

@@ -1,0 +1,584 @@
+// Chunked forward of the fast-weight delta rule in three launches: chunk-parallel preparation,
+// the serial pass of the memory over the chunks, and chunk-parallel outputs.
+//
+// The recurrence ("Fast Weights Transformer" guide, xdnf.cn/news/308600, sections
+// "FastWeightsAttention / update formula" and "... / module structure and source walkthrough"):
+//     v_bar_t = W_{t-1} f_t,  W_t = W_{t-1} + beta_t (v_t - v_bar_t) f_t^T,  y_t = W_t g_t,
+// f = phi(k), g = phi(q) (DPFP), beta_t = sigmoid(l_t).  The lucidrains page ("Deep dive into
+// Fast Weight Attention", section 4.2) runs such layers chunk by chunk, parallel inside a chunk,
+// passing the memory from chunk to chunk; the algebra below is derived from the recurrence.
+// For a chunk of C rows starting from memory W (d_v x D), with raw DPFP product tiles K, Q,
+// normalisers rho_k, rho_q (phi = rho * raw), K~ = diag(rho_k) K, Q~ = diag(rho_q) Q and
+// L = diag(beta) strict_lower(K~ K~^T):
+//     (I + L) U = diag(beta) (V - K~ W^T)
+//  => U = U_y - W_y W^T  with  W_y = (I + L)^-1 diag(beta) K~,  U_y = (I + L)^-1 diag(beta) V
+//     Y = Q~ W^T + P~ U  with  P~ = lower_incl(Q~ K~^T),        W^T <- W^T + K~^T U.
+// W_y, U_y, P~ do not depend on the memory, so every chunk prepares them at once (prep);
+// only U = U_y - W_y W^T and the update K~^T U stay on the serial chain (chain), and Y for all
+// chunks follows from the chunk-start memories (output).
+//
+// Workspace blocks.  Every operand the chain and output kernels read is stored as 1 KiB blocks
+// in the exact register layout of one MFMA operand (64 lanes x 16 bytes), so each wave loads a
+// block with one fully coalesced 16-byte load per lane.  With pair = 2 for bf16 (16x16x32 MFMA,
+// the two halves of a lane's 8 slots cover two 16-wide k-tiles) and 1 for fp32 (16x16x4, a
+// lane's 4 slots feed four MFMAs):
+//   A operand (rows m, k-tiles):   lane l, half h, slot e = X[16 m + l % 16][16 (pair j + h) + 4 (l / 16) + e]
+//   B operand (k-tiles, cols n):   lane l, half h, slot e = X[16 (pair j + h) + 4 (l / 16) + e][16 n + l % 16]
+// An fp32 accumulator tile (lane l, slot e = D[4 (l / 16) + e][l % 16]) is a B block with
+// pair = 1 as it stands.
+#pragma once
+
+#include "chunk_tile.h"
+#include "fwa_internal.h"
+
+#include <type_traits>
+
+namespace fwa {
+
+template <bool BF16>
+struct ChunkTypes {
+    using LT = std::conditional_t<BF16, u16, float>;   // operand storage (and input) type
+    static constexpr int pair = BF16 ? 2 : 1;
+    static constexpr int es = BF16 ? 2 : 4;
+};
+
+__device__ __forceinline__ f32x4 as_f32x4(uint4 v) { return __builtin_bit_cast(f32x4, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint4 pack_bf16x8(const f32x4& lo, const f32x4& hi) {
+    return make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                      pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
+}
+
+// Workgroup placement.  Workgroups are dispatched to the 8 XCDs round robin by index; when
+// B*H is a multiple of 8, all workgroups of (b, h) go to XCD (b*H + h) mod 8 in all three
+// kernels, so the chain and output kernels find the prep kernel's results in that XCD's L2.
+// Maps a workgroup index to (bh, i), i = index among the workgroups of bh (per_bh of them).
+struct BhIndex {
+    int bh;
+    int64_t i;
+};
+__device__ __forceinline__ BhIndex xcd_local(int64_t b, int BH, int64_t per_bh) {
+    if ((BH & 7) == 0) {
+        const int64_t x = b & 7, j = b >> 3;      // XCD and index inside it
+        return BhIndex{static_cast<int>((j / per_bh) * 8 + x), j % per_bh};
+    }
+    return BhIndex{static_cast<int>(b / per_bh), b % per_bh};
+}
+
+// Byte address of lane l's 16 bytes in block `blk` of the region at `base`.
+__device__ __forceinline__ char* blk_ptr(char* base, int64_t blk, int l) {
+    return base + (blk * 64 + l) * 16;
+}
+__device__ __forceinline__ const char* blk_ptr(const char* base, int64_t blk, int l) {
+    return base + (blk * 64 + l) * 16;
+}
+
+// ------------------------------------------------------------------------------------------
+// prep: one workgroup per chunk (b, h, n).  DPFP, G and P with the normalisers, L and its
+// diagonal-block inverses, then the solves for W_y and U_y; writes
+//   WyA (A blocks of W_y, C x D), KtA (A blocks of K^T, D x C, raw products),
+//   QA (A blocks of Q, raw), PA (A blocks of P~, zero above the diagonal),
+//   Uy (fp32 accumulator tiles of U_y), RK, RQ (rho_k, rho_q).
+template <bool BF16, int C>
+__global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
+    using LT = typename ChunkTypes<BF16>::LT;
+    constexpr int pair = ChunkTypes<BF16>::pair;
+    constexpr int NT = C / 16, NTB = NT / pair;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    LT* Kr = reinterpret_cast<LT*>(smem + a.l_kr);        // [C][krs] K raw products
+    LT* Qr = reinterpret_cast<LT*>(smem + a.l_qr);        // [C][krs] Q, then W_y staging
+    LT* Xk = reinterpret_cast<LT*>(smem + a.l_x);         // [C][d_k] raw k rows (staging)
+    LT* Xq = Xk + C * a.d_k;                              // [C][d_k] raw q rows (staging)
+    float* Ls = reinterpret_cast<float*>(smem + a.l_ls);  // [C][lss] L (over the staging)
+    LT* Ps = reinterpret_cast<LT*>(smem + a.l_ps);        // [C][pss] P~
+    float* Li = reinterpret_cast<float*>(smem + a.l_li);  // [C][20] diagonal-block inverses
+    LT* Xv = reinterpret_cast<LT*>(smem + a.l_xv);        // [C][d_v] raw v rows
+    float* rhok = reinterpret_cast<float*>(smem + a.l_small);
+    float* rhoq = rhok + C;
+    float* betas = rhoq + C;
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_k = a.d_k, d_v = a.d_v, D = a.D, T = a.T, krs = a.krs;
+    const int ND = D / 16, NDB = ND / pair, NVT = d_v / 16;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, a.NC);
+    const int bh = bi.bh, n = static_cast<int>(bi.i);
+    const int64_t u = static_cast<int64_t>(bh) * a.NC + n;    // unit (b, h, chunk n)
+    const int t0 = n * C, Cc = min(C, T - t0);
+    const int64_t row0 = static_cast<int64_t>(bh) * T + t0;
+
+    // ---- stage the chunk's raw k, q, v rows (zeros past the sequence end) and beta
+    {
+        const char* kc = reinterpret_cast<const char*>(static_cast<const LT*>(a.k) + row0 * d_k);
+        const char* qc = reinterpret_cast<const char*>(static_cast<const LT*>(a.q) + row0 * d_k);
+        const char* vc = reinterpret_cast<const char*>(static_cast<const LT*>(a.v) + row0 * d_v);
+        const int kb = d_k * static_cast<int>(sizeof(LT)), vb = d_v * static_cast<int>(sizeof(LT));
+        // A unit past the sequence end reads the chunk's first unit (always in range) and is
+        // zeroed by the mask.
+        auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
+        for (int e = tid; e < C * kb / 16; e += 256) {
+            const bool ok = (e * 16) / kb < Cc;
+            const int off = ok ? e * 16 : 0;
+            const uint32_t m = ok ? 0xffffffffu : 0u;
+            reinterpret_cast<uint4*>(Xk)[e] = masked(*reinterpret_cast<const uint4*>(kc + off), m);
+            reinterpret_cast<uint4*>(Xq)[e] = masked(*reinterpret_cast<const uint4*>(qc + off), m);
+        }
+        for (int e = tid; e < C * vb / 16; e += 256) {
+            const bool ok = (e * 16) / vb < Cc;
+            const int off = ok ? e * 16 : 0;
+            const uint32_t m = ok ? 0xffffffffu : 0u;
+            reinterpret_cast<uint4*>(Xv)[e] = masked(*reinterpret_cast<const uint4*>(vc + off), m);
+        }
+        if (tid < C)
+            betas[tid] = tid < Cc ? sigmoid_stable(to_f32(static_cast<const LT*>(a.bl)[row0 + tid]))
+                                  : 0.0f;
+    }
+    __syncthreads();
+
+    dpfp_chunk<LT, LT, C>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l);
+    __syncthreads();
+
+    {
+        GPTiles<C> gp;
+        gp_compute<BF16, C>(gp, Kr, Qr, krs, D, w, l16, g4);
+        gp_write_rho<C>(gp, rhok, rhoq, w, l16, g4);
+        __syncthreads();   // rho complete; the staging rows are dead (L and P~ go over them)
+        gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
+    }
+    __syncthreads();
+
+    // ---- diagonal-block inverses; write-out of the Q, K^T and P~ blocks and the normalisers
+    if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
+    char* ws = a.ws;
+    {
+        // QA: blocks (tt, j), j < NDB
+        char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+        for (int e = tid; e < NT * NDB * 64; e += 256) {
+            const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
+            const LT* src = Qr + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
+            uint4 val;
+            if constexpr (BF16) {
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
+                val = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                val = *reinterpret_cast<const uint4*>(src);
+            }
+            *reinterpret_cast<uint4*>(qa + static_cast<int64_t>(e) * 16) = val;
+        }
+        // KtA: blocks (dt, j), j < NTB: slot (h, e) = K[16 (pair j + h) + 4 (lam / 16) + e][16 dt + lam % 16]
+        char* kt = ws + a.o_kt + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+        for (int e = tid; e < ND * NTB * 64; e += 256) {
+            const int blk = e >> 6, lam = e & 63, dt = blk / NTB, j = blk % NTB;
+            const LT* src = Kr + (16 * pair * j + 4 * (lam >> 4)) * krs + 16 * dt + (lam & 15);
+            uint4 val;
+            if constexpr (BF16) {
+                uint32_t wd[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const LT* s = src + 16 * h * krs;
+                    wd[2 * h] = static_cast<uint32_t>(s[0]) | (static_cast<uint32_t>(s[krs]) << 16);
+                    wd[2 * h + 1] = static_cast<uint32_t>(s[2 * krs]) | (static_cast<uint32_t>(s[3 * krs]) << 16);
+                }
+                val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            } else {
+                val = make_uint4(__float_as_uint(src[0]), __float_as_uint(src[krs]),
+                                 __float_as_uint(src[2 * krs]), __float_as_uint(src[3 * krs]));
+            }
+            *reinterpret_cast<uint4*>(kt + static_cast<int64_t>(e) * 16) = val;
+        }
+        // PA: blocks (ta, j), j < NTB; tiles above the diagonal are zero
+        char* pa = ws + a.o_pa + u * (static_cast<int64_t>(C) * C * sizeof(LT));
+        for (int e = tid; e < NT * NTB * 64; e += 256) {
+            const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
+            const LT* src = Ps + (16 * ta + (lam & 15)) * a.pss + 16 * pair * j + 4 * (lam >> 4);
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (BF16) {
+                if (2 * j <= ta) {
+                    const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                    val.x = lo.x;
+                    val.y = lo.y;
+                }
+                if (2 * j + 1 <= ta) {
+                    const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
+                    val.z = hi.x;
+                    val.w = hi.y;
+                }
+            } else {
+                if (j <= ta) val = *reinterpret_cast<const uint4*>(src);
+            }
+            *reinterpret_cast<uint4*>(pa + static_cast<int64_t>(e) * 16) = val;
+        }
+        if (tid < C) {
+            reinterpret_cast<float*>(ws + a.o_rk)[u * C + tid] = rhok[tid];
+            reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
+        }
+    }
+    __syncthreads();   // Li complete; Q is dead (its space stages W_y)
+
+    // ---- solves: column tiles ct < ND give W_y (staged in LDS), the rest give U_y
+    LT* Wys = Qr;
+    char* uy = ws + a.o_uy + u * (static_cast<int64_t>(C) * d_v * 4);
+    for (int ct = w; ct < ND + NVT; ct += 4) {
+        f32x4 X[NT];
+        const bool isK = ct < ND;
+        if (isK) {
+#pragma unroll
+            for (int ta = 0; ta < NT; ++ta)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * ta + 4 * g4 + e;
+                    X[ta][e] = betas[t] * rhok[t] * to_f32(Kr[t * krs + 16 * ct + l16]);
+                }
+        } else {
+#pragma unroll
+            for (int ta = 0; ta < NT; ++ta)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * ta + 4 * g4 + e;
+                    X[ta][e] = betas[t] * to_f32(Xv[t * d_v + 16 * (ct - ND) + l16]);
+                }
+        }
+        block_solve<NT>(X, Ls, a.lss, Li, l16, g4);
+        if (isK) {
+#pragma unroll
+            for (int ta = 0; ta < NT; ++ta) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Wys[(16 * ta + 4 * g4 + e) * krs + 16 * ct + l16] = from_f32<LT>(X[ta][e]);
+            }
+        } else {
+            const int vt = ct - ND;
+#pragma unroll
+            for (int ta = 0; ta < NT; ++ta)
+                *reinterpret_cast<f32x4*>(blk_ptr(uy, ta * NVT + vt, l)) = X[ta];
+        }
+    }
+    __syncthreads();
+
+    // ---- WyA: blocks (tt, j), j < NDB
+    {
+        char* wy = ws + a.o_wy + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+        for (int e = tid; e < NT * NDB * 64; e += 256) {
+            const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
+            const LT* src = Wys + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
+            uint4 val;
+            if constexpr (BF16) {
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
+                val = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                val = *reinterpret_cast<const uint4*>(src);
+            }
+            *reinterpret_cast<uint4*>(wy + static_cast<int64_t>(e) * 16) = val;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// chain: one workgroup of DP waves per (b, h, 16-column v-tile r); wave w holds the fp32 memory
+// tiles W^T[16 (dt0 + i) .. +16][v-tile r], i < NDP (dt0 = w NDP), in MFMA accumulators.  Per
+// chunk: store the chunk-start memory (Wn, B blocks); S = W_y W^T, partial over the wave's
+// d-tiles, summed over the waves through LDS; U = U_y - S (stored as Un, B blocks);
+// W^T += K^T (rho_k o U).
+// The next chunk's operand blocks are loaded into registers right after each set's last use.
+// The loop body has no data-dependent branches around memory operations (the last chunk's
+// prefetch re-reads that chunk; every wave stores the full U tile it computed, identical
+// across waves), so the compiler's wait counters stay exact and every wait covers just the
+// loads it needs, never the prefetch in flight.
+template <bool BF16, int C, int NDP, int DP>
+__global__ __launch_bounds__(64 * DP, 1) void delta_chain_kernel(ChunkArgs a) {
+    using LT = typename ChunkTypes<BF16>::LT;
+    constexpr int pair = ChunkTypes<BF16>::pair;
+    constexpr int NT = C / 16, NTB = NT / pair, NDPB = NDP / pair;
+    static_assert(NDP % pair == 0, "bf16 waves hold whole d-tile pairs");
+    // partial S of each wave, double-buffered: [2][DP][NT] tiles of 64 lanes
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    f32x4* Red = reinterpret_cast<f32x4*>(smem);
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_k = a.d_k, D = a.D, NC = a.NC;
+    const int ND = D / 16, NDB = ND / pair, NVT = a.d_v / 16;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, NVT);      // workgroup -> (b, h, v-tile r)
+    const int bh = bi.bh, r = static_cast<int>(bi.i);
+    const int dt0 = w * NDP;
+    const int vcol = 16 * r + l16;
+
+    f32x4 Wst[NDP];
+#pragma unroll
+    for (int i = 0; i < NDP; ++i) {
+        Wst[i] = zero4();
+        if (a.W0) {
+            // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+            const float* src = a.W0 + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                               orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            const float2 lo = *reinterpret_cast<const float2*>(src);
+            const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
+            Wst[i] = f32x4{lo.x, hi.x, lo.y, hi.y};
+        }
+    }
+
+    const int64_t szCD = static_cast<int64_t>(C) * D * sizeof(LT);
+    const int64_t szUy = static_cast<int64_t>(C) * a.d_v * 4;
+    const int64_t szWn = static_cast<int64_t>(D) * a.d_v * sizeof(LT);
+    const int64_t szUn = static_cast<int64_t>(C) * a.d_v * sizeof(LT);
+    // Per-lane base addresses of this workgroup's blocks; chunk uu adds uu * region size.
+    const char* wyB = a.ws + a.o_wy + (static_cast<int64_t>(dt0 / pair) * 64 + l) * 16;
+    const char* ktB = a.ws + a.o_kt + (static_cast<int64_t>(dt0) * NTB * 64 + l) * 16;
+    const char* uyB = a.ws + a.o_uy + (static_cast<int64_t>(r) * 64 + l) * 16;
+    const float* rkB = reinterpret_cast<const float*>(a.ws + a.o_rk) + 4 * g4;
+    char* wnB = a.ws + a.o_wn + ((static_cast<int64_t>(dt0 / pair) * NVT + r) * 64 + l) * 16;
+    char* unB = a.ws + a.o_un + (static_cast<int64_t>(r) * 64 + l) * 16;
+
+    uint4 wy[NT][NDPB];     // WyA blocks (tt, dt0 / pair + i)
+    uint4 kt[NDP][NTB];     // KtA blocks (dt0 + i, j)
+    f32x4 uy[NT];           // U_y tiles (tt, r)
+    f32x4 rk[NT];           // rho_k of rows 16 tt + 4 g4 + e
+    auto load_wy = [&](int64_t uu) {
+        const char* p = wyB + uu * szCD;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int i = 0; i < NDPB; ++i)
+                wy[tt][i] = *reinterpret_cast<const uint4*>(p + (static_cast<int64_t>(tt) * NDB + i) * 1024);
+    };
+    auto load_uy = [&](int64_t uu) {
+        const char* p = uyB + uu * szUy;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            uy[tt] = *reinterpret_cast<const f32x4*>(p + static_cast<int64_t>(tt) * NVT * 1024);
+            rk[tt] = *reinterpret_cast<const f32x4*>(rkB + uu * C + 16 * tt);
+        }
+    };
+    auto load_kt = [&](int64_t uu) {
+        const char* p = ktB + uu * szCD;
+#pragma unroll
+        for (int i = 0; i < NDP; ++i)
+#pragma unroll
+            for (int j = 0; j < NTB; ++j)
+                kt[i][j] = *reinterpret_cast<const uint4*>(p + (static_cast<int64_t>(i) * NTB + j) * 1024);
+    };
+    const int64_t u0 = static_cast<int64_t>(bh) * NC;
+    const int64_t ulast = u0 + NC - 1;
+    if (NC > 0) {
+        load_wy(u0);
+        load_uy(u0);
+        load_kt(u0);
+    }
+
+    for (int n = 0; n < NC; ++n) {
+        const int64_t uu = u0 + n;
+        const int64_t un = uu + 1 <= ulast ? uu + 1 : ulast;  // next chunk (clamped)
+        const int buf = n & 1;
+        // chunk-start memory for the output kernel
+#pragma unroll
+        for (int i = 0; i < NDPB; ++i) {
+            uint4 val;
+            if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
+            else val = __builtin_bit_cast(uint4, Wst[i]);
+            *reinterpret_cast<uint4*>(wnB + uu * szWn + static_cast<int64_t>(i) * NVT * 1024) = val;
+        }
+        // S = W_y W^T over this wave's d-tiles
+        f32x4 S[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) S[tt] = zero4();
+#pragma unroll
+        for (int i = 0; i < NDPB; ++i) {
+            if constexpr (BF16) {
+                const uint4 bw = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    S[tt] = mfma_bf16_k32(as_bf16x8(wy[tt][i]), as_bf16x8(bw), S[tt]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt)
+                        S[tt] = mfma_f32_k4(as_f32x4(wy[tt][i])[e], Wst[i][e], S[tt]);
+            }
+        }
+        load_wy(un);
+        if constexpr (DP > 1) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) Red[((buf * DP + w) * NT + tt) * 64 + l] = S[tt];
+            __syncthreads();
+            f32x4 part[DP][NT];
+#pragma unroll
+            for (int pp = 0; pp < DP; ++pp)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) part[pp][tt] = Red[((buf * DP + pp) * NT + tt) * 64 + l];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                f32x4 s2 = part[0][tt];
+#pragma unroll
+                for (int pp = 1; pp < DP; ++pp) s2 += part[pp][tt];
+                S[tt] = s2;
+            }
+        }
+        f32x4 U[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) U[tt] = uy[tt] - S[tt];
+        // U for the output kernel (B blocks (j, r)); every wave holds the same U
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            uint4 val;
+            if constexpr (BF16) val = pack_bf16x8(U[2 * j], U[2 * j + 1]);
+            else val = __builtin_bit_cast(uint4, U[j]);
+            *reinterpret_cast<uint4*>(unB + uu * szUn + static_cast<int64_t>(j) * NVT * 1024) = val;
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) U[tt] *= rk[tt];
+        load_uy(un);
+        // W^T += K^T (rho_k o U)
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            if constexpr (BF16) {
+                const uint4 bu = pack_bf16x8(U[2 * j], U[2 * j + 1]);
+#pragma unroll
+                for (int i = 0; i < NDP; ++i) Wst[i] = mfma_bf16_k32(as_bf16x8(kt[i][j]), as_bf16x8(bu), Wst[i]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < NDP; ++i)
+                        Wst[i] = mfma_f32_k4(as_f32x4(kt[i][j])[e], U[j][e], Wst[i]);
+            }
+        }
+        load_kt(un);
+    }
+
+    if (a.Wf) {
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) {
+            float* dst = a.Wf + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                         orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            *reinterpret_cast<float2*>(dst) = make_float2(Wst[i][0], Wst[i][2]);
+            *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[i][1], Wst[i][3]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// output: one wave per output tile (chunk u, row tile tt, v-tile vt), four tiles per workgroup:
+//   Y = rho_q o (Q W_n^T) + P~ U_n.
+template <bool BF16, int C>
+__global__ __launch_bounds__(256) void delta_output_kernel(ChunkArgs a) {
+    using LT = typename ChunkTypes<BF16>::LT;
+    constexpr int pair = ChunkTypes<BF16>::pair;
+    constexpr int NT = C / 16;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int D = a.D, d_v = a.d_v, T = a.T;
+    const int ND = D / 16, NDB = ND / pair, NVT = d_v / 16, NTB = NT / pair;
+    const int ntile = NT * NVT;
+    const int wgs = (ntile + 3) / 4;                      // workgroups per chunk
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, static_cast<int64_t>(a.NC) * wgs);
+    const int bh = bi.bh, n = static_cast<int>(bi.i / wgs);
+    const int64_t u = static_cast<int64_t>(bh) * a.NC + n;
+    const int tile = static_cast<int>(bi.i % wgs) * 4 + w;
+    if (tile >= ntile) return;                            // no barrier in this kernel
+    const int tt = tile / NVT, vt = tile % NVT;
+    const int t0 = n * C, Cc = min(C, T - t0);
+
+    const char* ws = a.ws;
+    const char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+    const char* wn = ws + a.o_wn + u * (static_cast<int64_t>(D) * d_v * sizeof(LT));
+    f32x4 acc = zero4();
+#pragma unroll 4
+    for (int j = 0; j < NDB; ++j) {
+        const uint4 av = *reinterpret_cast<const uint4*>(blk_ptr(qa, tt * NDB + j, l));
+        const uint4 bv = *reinterpret_cast<const uint4*>(blk_ptr(wn, j * NVT + vt, l));
+        if constexpr (BF16) {
+            acc = mfma_bf16_k32(as_bf16x8(av), as_bf16x8(bv), acc);
+        } else {
+            const f32x4 af = as_f32x4(av), bf = as_f32x4(bv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
+        }
+    }
+    const f32x4 rq = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(ws + a.o_rq) +
+                                                     u * C + 16 * tt + 4 * g4);
+    acc *= rq;
+    const char* pa = ws + a.o_pa + u * (static_cast<int64_t>(C) * C * sizeof(LT));
+    const char* un = ws + a.o_un + u * (static_cast<int64_t>(C) * d_v * sizeof(LT));
+    for (int j = 0; j < NTB && pair * j <= tt; ++j) {
+        const uint4 av = *reinterpret_cast<const uint4*>(blk_ptr(pa, tt * NTB + j, l));
+        const uint4 bv = *reinterpret_cast<const uint4*>(blk_ptr(un, j * NVT + vt, l));
+        if constexpr (BF16) {
+            acc = mfma_bf16_k32(as_bf16x8(av), as_bf16x8(bv), acc);
+        } else {
+            const f32x4 af = as_f32x4(av), bf = as_f32x4(bv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
+        }
+    }
+    LT* yB = static_cast<LT*>(a.y) + (static_cast<int64_t>(bh) * T + t0) * d_v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tt + 4 * g4 + e;
+        if (t < Cc) yB[static_cast<int64_t>(t) * d_v + 16 * vt + l16] = from_f32<LT>(acc[e]);
+    }
+}
+
+// (d-tiles per wave, waves) pairs of the chain kernel that plans use: fp32 waves hold 1 or 2
+// d-tiles, bf16 waves 2 or 4.
+inline bool chain_config_ok(bool bf16, int ndp, int dp) {
+    const bool waves = dp == 1 || dp == 2 || dp == 3 || dp == 4 || dp == 6 || dp == 8;
+    return waves && (bf16 ? (ndp == 2 || ndp == 4) : (ndp == 1 || ndp == 2));
+}
+
+template <bool BF16, int C, int NDP>
+hipError_t launch_chain_ndp(const ChunkArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.BH) * (a.d_v / 16)));
+    const unsigned red = a.DP > 1 ? 2u * a.DP * (C / 16) * 1024u : 0u;
+    switch (a.DP) {
+        case 1: hipLaunchKernelGGL((delta_chain_kernel<BF16, C, NDP, 1>), grid, dim3(64), red, stream, a); break;
+        case 2: hipLaunchKernelGGL((delta_chain_kernel<BF16, C, NDP, 2>), grid, dim3(128), red, stream, a); break;
+        case 3: hipLaunchKernelGGL((delta_chain_kernel<BF16, C, NDP, 3>), grid, dim3(192), red, stream, a); break;
+        case 4: hipLaunchKernelGGL((delta_chain_kernel<BF16, C, NDP, 4>), grid, dim3(256), red, stream, a); break;
+        case 6: hipLaunchKernelGGL((delta_chain_kernel<BF16, C, NDP, 6>), grid, dim3(384), red, stream, a); break;
+        case 8: hipLaunchKernelGGL((delta_chain_kernel<BF16, C, NDP, 8>), grid, dim3(512), red, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16, int C>
+hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
+    const ChunkArgs& a = p.args;
+    const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
+    if (NU > 0) {
+        auto prep = delta_prep_kernel<BF16, C>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_prep);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(256), p.lds_prep, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipError_t e;
+    if constexpr (BF16) e = a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream)
+                                       : (a.NDP == 4 ? launch_chain_ndp<BF16, C, 4>(a, stream) : hipErrorInvalidValue);
+    else e = a.NDP == 1 ? launch_chain_ndp<BF16, C, 1>(a, stream)
+                        : (a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream) : hipErrorInvalidValue);
+    if (e != hipSuccess) return e;
+    if (NU > 0) {
+        const int ntile = (C / 16) * (a.d_v / 16);
+        const int64_t grid = NU * ((ntile + 3) / 4);
+        hipLaunchKernelGGL((delta_output_kernel<BF16, C>), dim3(static_cast<unsigned>(grid)),
+                           dim3(256), 0, stream, a);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+hipError_t launch_chunked_f32_c32(const ChunkPlan& p, hipStream_t s);
+hipError_t launch_chunked_f32_c64(const ChunkPlan& p, hipStream_t s);
+hipError_t launch_chunked_bf16_c32(const ChunkPlan& p, hipStream_t s);
+hipError_t launch_chunked_bf16_c64(const ChunkPlan& p, hipStream_t s);
+
+}  // namespace fwa

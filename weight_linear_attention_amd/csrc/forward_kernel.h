@@ -33,131 +33,17 @@
 // U and the intermediate blocks feed the next MFMA with no data movement.
 #pragma once
 
-#include "fwa_common.h"
+#include "chunk_tile.h"
 #include "fwa_internal.h"
 
 #include <type_traits>
 
 namespace fwa {
 
-
-constexpr int kLiStride = 20;   // floats per row of the diagonal-inverse buffer
-
-// Sum of v over the d_k-lane group of lane l (d_k in {16, 32, 64}), in every lane of the group:
-// rotations inside each 16-lane row (DPP), then the row sums combined with readlane.
-__device__ __forceinline__ float row_sum16(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
-    return v;
-}
-
-__device__ __forceinline__ float group_sum(float v, int d_k, int l) {
-    const float r = row_sum16(v);
-    if (d_k == 16) return r;
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
-    if (d_k == 32) return l < 32 ? r0 + r1 : r2 + r3;
-    return (r0 + r1) + (r2 + r3);
-}
-
-// Roll constants of one lane for shifts 1..4: the ds_bpermute byte address of the source lane
-// and the sign mask.  For shift i the rolled operand of position j is relu([k,-k]) at
-// m = (j - i) mod 2 d_k, i.e. lane (m mod d_k) of the row's group, negated when m >= d_k.
-struct RollConst {
-    int src4[4];
-    uint32_t smask[4];
-};
-
-__device__ __forceinline__ RollConst roll_consts(int jl, int gbase, int d_k) {
-    RollConst rc;
-#pragma unroll
-    for (int i = 1; i <= 4; ++i) {
-        const int m = (jl - i) & (2 * d_k - 1);
-        rc.src4[i - 1] = (gbase + (m & (d_k - 1))) << 2;
-        rc.smask[i - 1] = (m & d_k) ? 0x80000000u : 0u;
-    }
-    return rc;
-}
-
-__device__ __forceinline__ float flip(float x, uint32_t mask) {
-    return __uint_as_float(__float_as_uint(x) ^ mask);
-}
-
-// K and Q tiles store their D columns in an internal order that puts the two halves of a
-// shift block next to each other: internal column 2 ((i-1) d_k + j) + h holds DPFP position
-// (i-1) 2 d_k + h d_k + j (h = 0: relu(k_j) * ..., h = 1: relu(-k_j) * ...).  Inner products
-// over D do not depend on the order; the memory W^T uses the same order internally and is
-// mapped back at load/store.  So a lane writes both halves of its position with one store.
-__device__ __forceinline__ int orig_col(int c, int d_k) {
-    const int m = c >> 1;
-    return (m / d_k) * 2 * d_k + (c & 1) * d_k + (m % d_k);
-}
-
-__device__ __forceinline__ float relu_f(float x) { return fmaxf(x, 0.0f); }
-
-template <typename LT>
-__device__ __forceinline__ void store_pair(LT* p, float lo, float hi) {
-    if constexpr (sizeof(LT) == 2) *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(lo, hi);
-    else *reinterpret_cast<float2*>(p) = make_float2(lo, hi);
-}
-
-// Raw DPFP products of R rows for NU shifts (lane jl of a DK-lane group holds k_jl and q_jl
-// of its row), written as (h = 0, h = 1) pairs to the row-major K and Q tiles.  All loads and
-// permutes of the R rows are issued before the first LDS write.
-template <typename LT, int NU, int R>
-__device__ __forceinline__ void dpfp_rows(const float (&kv)[R], const float (&qv)[R],
-                                          const RollConst& rc, int d_k, LT* const (&krow)[R],
-                                          LT* const (&qrow)[R]) {
-    float xk[R][NU], xq[R][NU];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            xk[r][i] = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(rc.src4[i], __float_as_int(kv[r]))),
-                            rc.smask[i]);
-            xq[r][i] = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(rc.src4[i], __float_as_int(qv[r]))),
-                            rc.smask[i]);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const float ka = relu_f(kv[r]), kb = relu_f(-kv[r]), qa = relu_f(qv[r]), qb = relu_f(-qv[r]);
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            // ka, kb >= 0, so ka * relu(x) = relu(ka * x) and kb * relu(-x) = relu(-(kb * x))
-            store_pair(krow[r] + 2 * i * d_k, relu_f(ka * xk[r][i]), relu_f(-(kb * xk[r][i])));
-            store_pair(qrow[r] + 2 * i * d_k, relu_f(qa * xq[r][i]), relu_f(-(qb * xq[r][i])));
-        }
-    }
-}
-
-// Any nu (slow path, one row): the permute address and sign are computed per shift.
-template <typename LT>
-__device__ __forceinline__ void dpfp_row_any(float kv, float qv, int nu, int jl, int gbase,
-                                             int d_k, LT* krow, LT* qrow) {
-    const int two_dk = 2 * d_k;
-    const float ka = relu_f(kv), kb = relu_f(-kv), qa = relu_f(qv), qb = relu_f(-qv);
-    for (int i = 1; i <= nu; ++i) {
-        const int m = (jl - i) & (two_dk - 1);
-        const int src4 = (gbase + (m & (d_k - 1))) << 2;
-        const uint32_t sm = (m & d_k) ? 0x80000000u : 0u;
-        const float xk = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(kv))), sm);
-        const float xq = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(qv))), sm);
-        store_pair(krow + 2 * (i - 1) * d_k, relu_f(ka * xk), relu_f(-(kb * xk)));
-        store_pair(qrow + 2 * (i - 1) * d_k, relu_f(qa * xq), relu_f(-(qb * xq)));
-    }
-}
-
 template <bool BF16, int C, int NDPM>
 __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     using LT = std::conditional_t<BF16, u16, float>;  // LDS element type of K, Q and P
     constexpr int NT = C / 16;
-    constexpr int NQ = (NT + 1) / 2;                   // tile-row pairs {q, NT-1-q}
-    constexpr int UPW = (2 * NQ + 3) / 4;              // G/P units per wave
     constexpr int RS = C + 4;                          // row stride of the partials buffer
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -219,13 +105,9 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     const IT* bB = static_cast<const IT*>(a.bl) + row0;
     IT* yB = static_cast<IT*>(a.y) + row0 * d_v;
     const int nchunks = (T + C - 1) / C;
-    const int rpw = 64 / d_k;                             // DPFP rows per wave pass
-    const int jl = l % d_k, grp = l / d_k;
-    const int gbase = grp * d_k;
 
     // The next chunk's raw inputs are fetched into registers while the current chunk is
     // being computed, so no global-memory latency sits on the serial chain over chunks.
-    const int npass = C / (4 * rpw);
     // The next chunk's k and q rows form two contiguous blocks of C*d_k elements; each thread
     // fetches its share as 16-byte units into registers while the current chunk computes.
     // Loads are branch-free: a unit past the sequence end reads unit 0 of the chunk (always in
@@ -300,124 +182,12 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
         if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(to_f32(blpre)) : 0.0f;
         __syncthreads();
 
-        // One row per d_k-lane group and pass, two passes per iteration; the shift count is
-        // a compile-time constant on the fast path (nu <= 4).  Row sums come from the MFMA
-        // pipe in phase B.
-        auto dpfp_passes = [&](auto nu_tag) {
-            constexpr int NU = decltype(nu_tag)::value;
-            const RollConst rc = roll_consts(jl, gbase, d_k);
-            for (int p = 0; p < npass; p += 2) {
-                const bool two = p + 1 < npass;
-                const int t0r = p * 4 * rpw + w * rpw + grp;
-                const int t1r = two ? t0r + 4 * rpw : t0r;
-                const float kv[2] = {to_f32(Xk[t0r * d_k + jl]), to_f32(Xk[t1r * d_k + jl])};
-                const float qv[2] = {to_f32(Xq[t0r * d_k + jl]), to_f32(Xq[t1r * d_k + jl])};
-                LT* const krow[2] = {Kr + t0r * a.krs + 2 * jl, Kr + t1r * a.krs + 2 * jl};
-                LT* const qrow[2] = {Qr + t0r * a.krs + 2 * jl, Qr + t1r * a.krs + 2 * jl};
-                dpfp_rows<LT, NU, 2>(kv, qv, rc, d_k, krow, qrow);
-            }
-        };
-        auto dpfp_passes_any = [&]() {
-            for (int p = 0; p < npass; ++p) {
-                const int t = p * 4 * rpw + w * rpw + grp;
-                const float kv = to_f32(Xk[t * d_k + jl]), qv = to_f32(Xq[t * d_k + jl]);
-                dpfp_row_any<LT>(kv, qv, nu, jl, gbase, d_k, Kr + t * a.krs + 2 * jl,
-                                 Qr + t * a.krs + 2 * jl);
-            }
-        };
-        switch (nu) {
-            case 1: dpfp_passes(std::integral_constant<int, 1>{}); break;
-            case 2: dpfp_passes(std::integral_constant<int, 2>{}); break;
-            case 3: dpfp_passes(std::integral_constant<int, 3>{}); break;
-            case 4: dpfp_passes(std::integral_constant<int, 4>{}); break;
-            default: dpfp_passes_any(); break;
-        }
+        dpfp_chunk<LT, ITs, C>(Xk, Xq, Kr, Qr, a.krs, d_k, nu, w, l);
         __syncthreads();
 
         // ---------------- B: G, P tiles; K W^T and Q W^T against the memory
-        // G = K K^T and P = Q K^T lower triangles in 16x16 tiles.  Work is split in units: one
-        // of G or P for the tile rows {q, NT-1-q}; unit u goes to wave u % 4.  Inside a unit the
-        // row operands are loaded once per k-step and reused by every tile of the two rows,
-        // and the tiles are independent accumulators that interleave on the MFMA pipe.
-        // gpa[ui][tb]: tile (ra, tb); gpb[ui][tb]: tile (rb, tb) (static register indices)
-        // sa/sb: row sums of the unit's rows (the same operands times a ones matrix).
-        f32x4 gpa[UPW][NT], gpb[UPW][NT], sa[UPW], sb[UPW];
-#pragma unroll
-        for (int ui = 0; ui < UPW; ++ui) {
-            sa[ui] = sb[ui] = zero4();
-#pragma unroll
-            for (int tb = 0; tb < NT; ++tb) gpa[ui][tb] = gpb[ui][tb] = zero4();
-        }
-#pragma unroll
-        for (int ui = 0; ui < UPW; ++ui) {
-            const int u = w + 4 * ui;
-            if (u < 2 * NQ) {
-                const bool isP = u >= NQ;
-                const int q = isP ? u - NQ : u;
-                const int ra = q, rb = NT - 1 - q;       // rb >= ra
-                const LT* Xa = (isP ? Qr : Kr) + (16 * ra + l16) * a.krs;
-                const LT* Xb = (isP ? Qr : Kr) + (16 * rb + l16) * a.krs;
-                const LT* Kb = Kr + l16 * a.krs;
-                if constexpr (BF16) {
-                    bf16x8 ones;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
-#pragma unroll 2
-                    for (int kk = 0; kk < D / 32; ++kk) {
-                        const int c0 = 32 * kk + 8 * g4;
-                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Xa + c0);
-                        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Xb + c0);
-                        sa[ui] = mfma_bf16_k32(va, ones, sa[ui]);
-                        if (rb != ra) sb[ui] = mfma_bf16_k32(vb, ones, sb[ui]);
-#pragma unroll
-                        for (int tb = 0; tb < NT; ++tb) {
-                            if (tb <= rb) {
-                                const bf16x8 kv8 = *reinterpret_cast<const bf16x8*>(Kb + 16 * tb * a.krs + c0);
-                                if (tb <= ra) gpa[ui][tb] = mfma_bf16_k32(va, kv8, gpa[ui][tb]);
-                                if (rb != ra) gpb[ui][tb] = mfma_bf16_k32(vb, kv8, gpb[ui][tb]);
-                            }
-                        }
-                    }
-                } else {
-#pragma unroll 2
-                    for (int kk = 0; kk < D / 16; ++kk) {
-                        const int c0 = 16 * kk + 4 * g4;
-                        const float4 va = *reinterpret_cast<const float4*>(Xa + c0);
-                        const float4 vb = *reinterpret_cast<const float4*>(Xb + c0);
-                        sa[ui] = mfma_f32_k4(va.x, 1.0f, sa[ui]);
-                        sa[ui] = mfma_f32_k4(va.y, 1.0f, sa[ui]);
-                        sa[ui] = mfma_f32_k4(va.z, 1.0f, sa[ui]);
-                        sa[ui] = mfma_f32_k4(va.w, 1.0f, sa[ui]);
-                        if (rb != ra) {
-                            sb[ui] = mfma_f32_k4(vb.x, 1.0f, sb[ui]);
-                            sb[ui] = mfma_f32_k4(vb.y, 1.0f, sb[ui]);
-                            sb[ui] = mfma_f32_k4(vb.z, 1.0f, sb[ui]);
-                            sb[ui] = mfma_f32_k4(vb.w, 1.0f, sb[ui]);
-                        }
-#pragma unroll
-                        for (int tb = 0; tb < NT; ++tb) {
-                            if (tb <= rb) {
-                                const float4 k4 = *reinterpret_cast<const float4*>(Kb + 16 * tb * a.krs + c0);
-                                if (tb <= ra) {
-                                    f32x4& g = gpa[ui][tb];
-                                    g = mfma_f32_k4(va.x, k4.x, g);
-                                    g = mfma_f32_k4(va.y, k4.y, g);
-                                    g = mfma_f32_k4(va.z, k4.z, g);
-                                    g = mfma_f32_k4(va.w, k4.w, g);
-                                }
-                                if (rb != ra) {
-                                    f32x4& g = gpb[ui][tb];
-                                    g = mfma_f32_k4(vb.x, k4.x, g);
-                                    g = mfma_f32_k4(vb.y, k4.y, g);
-                                    g = mfma_f32_k4(vb.z, k4.z, g);
-                                    g = mfma_f32_k4(vb.w, k4.w, g);
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-        }
+        GPTiles<C> gp;
+        gp_compute<BF16, C>(gp, Kr, Qr, a.krs, D, w, l16, g4);
         f32x4 S1[NT], QW[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) { S1[tt] = zero4(); QW[tt] = zero4(); }
@@ -472,62 +242,11 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 }
             }
         }
-        // normalisers 1/(S + eps) of the unit's rows (G units: K rows, P units: Q rows)
-#pragma unroll
-        for (int ui = 0; ui < UPW; ++ui) {
-            const int u = w + 4 * ui;
-            if (u < 2 * NQ && l16 == 0) {
-                const bool isP = u >= NQ;
-                const int q = isP ? u - NQ : u;
-                const int ra = q, rb = NT - 1 - q;
-                float* rho = isP ? rhoq : rhok;
-                f32x4 r0, r1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    r0[e] = __builtin_amdgcn_rcpf(sa[ui][e] + kDpfpEps);
-                    r1[e] = __builtin_amdgcn_rcpf(sb[ui][e] + kDpfpEps);
-                }
-                *reinterpret_cast<f32x4*>(rho + 16 * ra + 4 * g4) = r0;
-                if (rb != ra) *reinterpret_cast<f32x4*>(rho + 16 * rb + 4 * g4) = r1;
-            }
-        }
+        gp_write_rho<C>(gp, rhok, rhoq, w, l16, g4);
         __syncthreads();  // Q is dead from here; its space is reused
 
         // ---------------- B': scaled G and P to LDS, state partials to the reduction buffer
-#pragma unroll
-        for (int ui = 0; ui < UPW; ++ui) {
-            const int u = w + 4 * ui;
-            if (u < 2 * NQ) {
-                const bool isP = u >= NQ;
-                const int q = isP ? u - NQ : u;
-                const int ra = q, rb = NT - 1 - q;
-#pragma unroll
-                for (int k2 = 0; k2 < 2 * NT; ++k2) {
-                    // k2 < NT: tile (ra, k2) from gpa; k2 >= NT: tile (rb, k2 - NT) from gpb
-                    const bool rowa = k2 < NT;
-                    const int ta = rowa ? ra : rb;
-                    const int tb = rowa ? k2 : k2 - NT;
-                    if (tb > ta || (!rowa && rb == ra)) continue;
-                    const f32x4 acc = rowa ? gpa[ui][k2 % NT] : gpb[ui][k2 % NT];
-                    const int s = 16 * tb + l16, tr = 16 * ta + 4 * g4;
-                    const float rks = rhok[s];
-                    if (isP) {
-                        const f32x4 rq = *reinterpret_cast<const f32x4*>(rhoq + tr);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float val = s <= tr + e ? rq[e] * rks * acc[e] : 0.0f;
-                            Ps[(tr + e) * a.pss + s] = from_f32<LT>(val);
-                        }
-                    } else {
-                        const f32x4 rk = *reinterpret_cast<const f32x4*>(rhok + tr);
-                        const f32x4 bt = *reinterpret_cast<const f32x4*>(betas + tr);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            Ls[(tr + e) * a.lss + s] = s < tr + e ? bt[e] * rk[e] * rks * acc[e] : 0.0f;
-                    }
-                }
-            }
-        }
+        gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
         if (has_state && a.DP > 1) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -540,28 +259,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
         // ---------------- C: diagonal-block inverses; reduce the state partials
         // (the next chunk's inputs are requested here: their registers are not live in B)
         if (ch + 1 < nchunks) prefetch(ch + 1);
-        if (tid < C) {
-            // Column sc of the inverse of the unit lower 16x16 block ab; each row's dot product
-            // is split over four partial sums to keep the dependency chains short.
-            const int ab = tid >> 4, sc = tid & 15;
-            const float* Lb = Ls + (16 * ab) * a.lss + 16 * ab;
-            float xcol[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                f32x4 rw[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    rw[q4] = (4 * q4 < u) ? *reinterpret_cast<const f32x4*>(Lb + u * a.lss + 4 * q4)
-                                          : zero4();
-                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int w2 = 0; w2 < u; ++w2) acc[w2 & 3] += rw[w2 >> 2][w2 & 3] * xcol[w2];
-                const float tot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                xcol[u] = (u == sc) ? 1.0f : (u < sc ? 0.0f : -tot);
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) Li[(16 * ab + u) * kLiStride + sc] = xcol[u];
-        }
+        if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
         f32x4 X[NT];
         if (has_state) {
 #pragma unroll
@@ -588,32 +286,14 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
 
         // ---------------- D: U by block substitution, Y, and the memory update
         if (has_state) {
-            f32x4 U[NT];
+            // U = (I + L)^-1 beta X, solved in place
+            f32x4 (&U)[NT] = X;
 #pragma unroll
             for (int ta = 0; ta < NT; ++ta) {
-                f32x4 z;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z[e] = betas[16 * ta + 4 * g4 + e] * X[ta][e];
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int tb = 0; tb < ta; ++tb) {
-                    const float4 l4 = *reinterpret_cast<const float4*>(
-                        Ls + (16 * ta + l16) * a.lss + 16 * tb + 4 * g4);
-                    acc = mfma_f32_k4(l4.x, U[tb][0], acc);
-                    acc = mfma_f32_k4(l4.y, U[tb][1], acc);
-                    acc = mfma_f32_k4(l4.z, U[tb][2], acc);
-                    acc = mfma_f32_k4(l4.w, U[tb][3], acc);
-                }
-                z -= acc;
-                const float4 i4 = *reinterpret_cast<const float4*>(
-                    Li + (16 * ta + l16) * kLiStride + 4 * g4);
-                f32x4 u = zero4();
-                u = mfma_f32_k4(i4.x, z[0], u);
-                u = mfma_f32_k4(i4.y, z[1], u);
-                u = mfma_f32_k4(i4.z, z[2], u);
-                u = mfma_f32_k4(i4.w, z[3], u);
-                U[ta] = u;
+                for (int e = 0; e < 4; ++e) U[ta][e] *= betas[16 * ta + 4 * g4 + e];
             }
+            block_solve<NT>(U, Ls, a.lss, Li, l16, g4);
             // Y rows of chunk tiles ta = dp, dp + DP, ...
 #pragma unroll
             for (int ta = 0; ta < NT; ++ta) {

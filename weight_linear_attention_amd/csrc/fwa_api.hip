@@ -7,6 +7,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -62,6 +65,42 @@ constexpr int64_t kIndexLimit = int64_t(1) << 61;
 fwa_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
     return fail(FWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Forward implementation: FWA_FORWARD_PATH = "chunked" (three launches with a workspace),
+// "fused" (one launch, no workspace), or unset / "auto".  Auto takes the chunked path where it
+// applies and its workspace stays within kAutoWorkspaceLimit: beyond that the workspace
+// traffic (about 7 D-wide rows per token) outweighs the parallelism it buys, and the fused
+// kernel, which keeps everything on chip, is faster.
+enum class ForwardPath { kAuto, kChunked, kFused, kInvalid };
+constexpr int64_t kAutoWorkspaceLimit = int64_t(2) << 30;
+ForwardPath forward_path() {
+    const char* s = std::getenv("FWA_FORWARD_PATH");
+    if (!s || !*s || std::strcmp(s, "auto") == 0) return ForwardPath::kAuto;
+    if (std::strcmp(s, "chunked") == 0) return ForwardPath::kChunked;
+    if (std::strcmp(s, "fused") == 0) return ForwardPath::kFused;
+    return ForwardPath::kInvalid;
+}
+
+// Stream-ordered workspace from the device's default memory pool.  The pool keeps freed
+// memory for reuse (release threshold raised once per device), so repeated calls do not go
+// back to the driver.
+hipError_t workspace_alloc(char** ptr, int64_t bytes, hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static std::once_flag flags[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) {
+        std::call_once(flags[dev], [dev]() {
+            hipMemPool_t pool;
+            if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+                uint64_t threshold = UINT64_MAX;
+                (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+            }
+        });
+    }
+    return hipMallocAsync(reinterpret_cast<void**>(ptr), static_cast<size_t>(bytes), stream);
 }
 
 }  // namespace
@@ -136,11 +175,6 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     if (BH > (int64_t(1) << 26) || static_cast<int64_t>(T) * d_v >= (int64_t(1) << 31) ||
         static_cast<int64_t>(T) * d_k >= (int64_t(1) << 31))
         return fail(FWA_ERR_UNSUPPORTED, "%s: too many (b, h) slices for one launch", fn);
-    fwa::FwdPlan plan;
-    if (!fwa::plan_forward(static_cast<int>(BH), d_k, d_v, nu, chunk, dtype == FWA_BF16, &plan))
-        return fail(FWA_ERR_UNSUPPORTED,
-                    "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn,
-                    d_k, d_v, nu, chunk);
     const int es = elem_bytes(dtype);
     const int64_t nqk = BH * T * d_k * es, nv = BH * T * d_v * es, nb = BH * T * es;
     const int64_t nW = BH * d_v * D * 4;
@@ -154,9 +188,43 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     if (W0 && W_final && W0 != W_final && overlap(in[4], sw))
         return fail(FWA_ERR_INVALID_ARG, "%s: W0 and W_final partially overlap", fn);
     if (overlap(sy, sw)) return fail(FWA_ERR_INVALID_ARG, "%s: y overlaps W_final", fn);
+
+    const bool bf16 = dtype == FWA_BF16;
+    const ForwardPath want = forward_path();
+    if (want == ForwardPath::kInvalid)
+        return fail(FWA_ERR_INVALID_ARG, "%s: FWA_FORWARD_PATH must be auto, chunked or fused", fn);
+    fwa::ChunkPlan cplan;
+    bool can_chunk = want != ForwardPath::kFused &&
+                     fwa::plan_chunked(static_cast<int>(BH), T, d_k, d_v, nu, chunk, bf16, &cplan);
+    fwa::FwdPlan plan;
+    const bool can_fuse = fwa::plan_forward(static_cast<int>(BH), d_k, d_v, nu, chunk, bf16, &plan);
+    if (want == ForwardPath::kAuto && can_chunk && can_fuse && cplan.ws_bytes > kAutoWorkspaceLimit)
+        can_chunk = false;
+    if (can_chunk) {
+        char* ws = nullptr;
+        if (cplan.ws_bytes > 0) {
+            const hipError_t e = workspace_alloc(&ws, cplan.ws_bytes, stream);
+            if (e != hipSuccess)
+                return fail(FWA_ERR_HIP, "%s: workspace of %lld bytes: %s", fn,
+                            (long long)cplan.ws_bytes, hipGetErrorString(e));
+        }
+        const hipError_t le = fwa::launch_chunked(cplan, q, k, v, beta_logit, W0, y, W_final, ws,
+                                                  bf16, stream);
+        const hipError_t fe = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+        if (le != hipSuccess) return hip_status(le, "fwa_delta_forward launch");
+        return hip_status(fe, "fwa_delta_forward workspace release");
+    }
+    if (want == ForwardPath::kChunked)
+        return fail(FWA_ERR_UNSUPPORTED,
+                    "%s: the chunked path does not support d_k=%d d_v=%d nu=%d chunk=%d", fn, d_k,
+                    d_v, nu, chunk);
+    if (!can_fuse)
+        return fail(FWA_ERR_UNSUPPORTED,
+                    "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn,
+                    d_k, d_v, nu, chunk);
     return hip_status(fwa::launch_delta_forward(plan, q, k, v, beta_logit, W0, y, W_final,
                                                 static_cast<int>(BH), H, T, d_k, d_v, nu, chunk,
-                                                dtype == FWA_BF16, stream),
+                                                bf16, stream),
                       "fwa_delta_forward launch");
 }
 

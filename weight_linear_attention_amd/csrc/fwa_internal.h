@@ -42,4 +42,35 @@ hipError_t launch_delta_forward(const FwdPlan& plan, const void* q, const void* 
                                 float* Wf, int BH, int H, int T, int d_k, int d_v, int nu, int C,
                                 bool bf16, hipStream_t stream);
 
+// Arguments of the three-launch chunked forward (prep, chain, output kernels): inputs and
+// outputs, the workspace and the byte offsets of its regions, the chain split, and the prep
+// kernel's LDS layout (byte offsets; row strides in elements).
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* bl;
+    const float* W0;
+    void* y;
+    float* Wf;
+    char* ws;
+    int64_t o_wy, o_kt, o_qa, o_pa, o_uy, o_rk, o_rq, o_wn, o_un;
+    int BH, T, NC, d_k, d_v, nu, D;
+    int DP, NDP;
+    int krs, lss, pss;
+    int l_kr, l_qr, l_x, l_ls, l_ps, l_li, l_xv, l_small;
+};
+
+struct ChunkPlan {
+    ChunkArgs args;
+    int C;
+    int lds_prep;
+    int64_t ws_bytes;
+};
+
+bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, ChunkPlan* plan);
+hipError_t launch_chunked(const ChunkPlan& plan, const void* q, const void* k, const void* v,
+                          const void* bl, const float* W0, void* y, float* Wf, char* ws,
+                          bool bf16, hipStream_t stream);
+
 }  // namespace fwa

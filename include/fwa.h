@@ -19,9 +19,10 @@
  *           walkthrough".  No 1/sqrt(d) scale and no z normaliser.
  *
  * Conventions for every entry point:
- *   - All tensor pointers are DEVICE pointers owned by the caller; the library allocates
- *     nothing, keeps no state between calls and never synchronises `stream`.  Every launch
- *     goes on `stream` (0 = the legacy default stream).  FWA_OK means "enqueued".
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library keeps no
+ *     state between calls and never synchronises `stream`; every launch goes on `stream`
+ *     (0 = the legacy default stream) and FWA_OK means "enqueued".  Only fwa_delta_forward
+ *     may allocate: a stream-ordered workspace (see there).
  *   - Layouts are row-major and contiguous (the [B, H, T, d] convention of [TRF], section
  *     "Scaled dot-product attention").  The fast-weight memory W is [B, H, d_v, D] fp32
  *     (d_value x d_key orientation of [FWT], module walkthrough).
@@ -94,9 +95,25 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *               the stated tolerances.
  *   T == 0 leaves y untouched and writes W_final = W0 (or zeros).  B*H == 0 is a no-op.
  *   T need not be a multiple of chunk.
+ *   Two implementations compute the same result (within the tolerances above):
+ *     chunked  three launches: every chunk's memory-independent part in parallel, then the
+ *              memory carried through the chunks, then the outputs.  It needs a workspace of
+ *              B*H*ceil(T/chunk) * (3*chunk*D + chunk*chunk + D*d_v + chunk*d_v) elements of
+ *              `dtype` plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values, taken with
+ *              hipMallocAsync on `stream` and returned with hipFreeAsync on `stream` before
+ *              the call returns (the device's default memory pool is set, once, to keep freed
+ *              memory for reuse).  Chunks of
+ *              32 or 64 rows; D in {32, 64, 96, 128, 192, 256}, and for bf16 also 384, 512.
+ *     fused    one launch that keeps the chunk and the memory on chip; allocates nothing.
+ *              Needs the chunk's working set (3*chunk*D elements plus chunk-sized scratch)
+ *              within the 160 KiB of LDS of one compute unit.
+ *   The environment variable FWA_FORWARD_PATH = chunked | fused | auto (default) selects one;
+ *   auto takes the chunked path where it applies and its workspace is at most 2 GiB, else
+ *   the fused one.  A forced path that does not apply gives FWA_ERR_UNSUPPORTED, an unknown
+ *   value FWA_ERR_INVALID_ARG, a failed workspace allocation FWA_ERR_HIP.
  *   Implemented shapes: d_k in {16, 32, 64}, d_v in {16, 32, 64}, D = 2*d_k*nu <= 512, and
- *   the chunk's on-chip working set (3*chunk*D elements plus chunk-sized scratch) within the
- *   160 KiB of LDS of one compute unit; other valid shapes give FWA_ERR_UNSUPPORTED.
+ *   the conditions of at least one implementation above; other valid shapes give
+ *   FWA_ERR_UNSUPPORTED.
  */
 fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
                              const void* beta_logit, const float* W0, void* y, float* W_final,

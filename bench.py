@@ -14,9 +14,12 @@ already resident in HBM when timing starts.  Other workloads (--workload):
     copy_calibration                                                a 1 GiB device copy (the
                                                                     reference for HBM counters)
 
-Prints ONE JSON line.  `roofline` describes the dominant kernel: algorithmic bytes or flops of
-one launch divided by its mean duration, measured with HIP events on the launch stream over the
-timed region.  `cpu_baseline` times the fp64 oracle on the host (rank 0 only).
+Prints ONE JSON line.  `roofline` describes the dominant call: the forward (one launch on the
+fused path, three on the chunked path) or, for the decode and DPFP workloads, that kernel.
+`achieved` is its algorithmic bytes or flops divided by its mean duration, measured with HIP
+events on the launch stream over the timed region; `traffic` is the HBM bytes per call that
+rocprofv3 counted on the same sources (profiles/traffic.json), or null.  `cpu_baseline` times
+the fp64 oracle on the host (rank 0 only).
 """
 import argparse
 import hashlib
@@ -44,22 +47,33 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash(name):
-    path = os.path.join(HERE, "weight_linear_attention_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# Kernel sources behind each measured unit (their hash keys the committed counter data).
+SOURCES = {
+    "chunked": ("chunked_kernels.h", "chunk_tile.h"),
+    "fused": ("forward_kernel.h", "chunk_tile.h"),
+    "decode": ("step_kernel.hip",),
+    "dpfp": ("dpfp_kernel.hip",),
+}
 
 
-def measured_traffic(kernel_file, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source for this workload; otherwise None."""
+def kernel_source_hash(unit):
+    h = hashlib.sha256()
+    for name in SOURCES[unit]:
+        with open(os.path.join(HERE, "weight_linear_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(unit, workload):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources for this workload; otherwise None."""
     path = os.path.join(HERE, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         table = json.load(f)
-    ent = table.get(f"{kernel_file}:{workload}")
-    if not ent or ent.get("source_sha256_16") != kernel_source_hash(kernel_file):
+    ent = table.get(f"{unit}:{workload}")
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash(unit):
         return None
     return ent.get("bytes_per_launch")
 
@@ -184,7 +198,7 @@ def main():
     value = tokens * steps / elapsed
 
     if kind in ("prefill", "prefill+decode"):
-        kernel_file = "forward_kernel.h"
+        unit, _ = fwa.delta_forward_info(w.B, w.H, w.T, w.d_k, w.d_v, w.nu, w.chunk, w.torch_dtype)
         flops = BH * w.T * (6 * D * w.d_v + 6 * D)
         nbytes = (BH * w.T * ((3 * w.d_k + 1) * es + w.d_v * es)
                   + BH * w.d_v * D * 4 * (1 + (d["W0"] is not None)))
@@ -198,22 +212,25 @@ def main():
             ach = nbytes / (main_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": ach / PEAK_HBM_GBPS}
-        roof.update(kernel="delta_forward_kernel", algorithmic_flops=flops,
-                    algorithmic_bytes=nbytes, mean_launch_ms=main_ms)
+        kname = ("fwa_delta_forward, chunked: delta_prep_kernel + delta_chain_kernel + "
+                 "delta_output_kernel" if unit == "chunked" else
+                 "fwa_delta_forward, fused: delta_forward_kernel")
+        roof.update(kernel=kname, algorithmic_flops=flops, algorithmic_bytes=nbytes,
+                    mean_launch_ms=main_ms)
     else:
         if kind == "decode":
-            kernel_file = "step_kernel.hip"
+            unit = "decode"
             nbytes = BH * (2 * w.d_v * D * 4 + (2 * w.d_k + 1 + 2 * w.d_v) * es)
             kname = "delta_step_kernel"
         else:
-            kernel_file = "dpfp_kernel.hip"
+            unit = "dpfp"
             nbytes = 2 * BH * w.T * (w.d_k + D) * es
             kname = "dpfp_kernel (q and k launches)"
         ach = nbytes / (main_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBPS, "kernel": kname, "algorithmic_bytes": nbytes,
                 "mean_launch_ms": main_ms}
-    roof["traffic"] = measured_traffic(kernel_file, w.name if kind != "dpfp" else name)
+    roof["traffic"] = measured_traffic(unit, w.name if kind != "dpfp" else name)
 
     out = {
         "metric": "tokens/sec through fast-weight layer (fwd + decode step) & % of MFMA/HBM roofline",
@@ -282,7 +299,7 @@ def cpu_baseline(w, kind, inp, nxt):
     W0 = None if inp["W0"] is None else to_f64(inp["W0"]).reshape(1, BH, w.d_v, w.D)[:, :nsl]
     reps, dt = 0, 0.0
     t0 = time.perf_counter()
-    while dt < 2.0 or reps == 0:
+    while dt < 10.0 or reps == 0:
         _, Wf = oracle.delta_forward(q, k, v, l, W0, nu=w.nu)
         if nxt is not None:
             sel = lambda t: to_f64(t).reshape(1, BH, -1)[:, :nsl]

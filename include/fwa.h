@@ -64,6 +64,13 @@ typedef enum {
     FWA_BF16 = 1
 } fwa_dtype;
 
+/* Implementation of fwa_delta_forward (see there). */
+typedef enum {
+    FWA_PATH_NONE = 0,      /* nothing to launch (B*H == 0) */
+    FWA_PATH_CHUNKED = 1,
+    FWA_PATH_FUSED = 2
+} fwa_forward_path;
+
 /*
  * fwa_dpfp -- phi[n, :] = DPFP(x[n, :]) for n in [0, n_vec).
  *   [FWT] sections "DPFP / projection formula and hyper-parameters" and "DPFP /
@@ -119,6 +126,17 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
                              const void* beta_logit, const float* W0, void* y, float* W_final,
                              int B, int H, int T, int d_k, int d_v, int nu, int chunk,
                              fwa_dtype dtype, hipStream_t stream);
+
+/*
+ * fwa_delta_forward_info -- which implementation fwa_delta_forward takes for these sizes
+ * (under the current FWA_FORWARD_PATH) and the workspace it would allocate, without
+ * launching or allocating anything.
+ *   path             out (may be NULL): an fwa_forward_path value
+ *   workspace_bytes  out (may be NULL): bytes of the stream-ordered workspace, 0 for fused
+ *   Size errors are those fwa_delta_forward gives for the same sizes.
+ */
+fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
+                                  fwa_dtype dtype, int* path, int64_t* workspace_bytes);
 
 /*
  * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory

@@ -21,8 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_step", "fwa_status_string",
-              "fwa_last_error", "fwa_version"):
+    for n in ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_info", "fwa_delta_step",
+              "fwa_status_string", "fwa_last_error", "fwa_version"):
         assert n in names
     assert set(names) == set(fwa.EXPORTED)
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fwa.lib()
-    assert L.fwa_version() == 10000
+    assert L.fwa_version() == 10100
     assert L.fwa_status_string(0) == b"FWA_OK"
     assert L.fwa_status_string(1) == b"FWA_ERR_INVALID_ARG"
     assert L.fwa_status_string(2) == b"FWA_ERR_UNSUPPORTED"
@@ -132,3 +132,75 @@ def test_step_rejects(kw, status, msg):
 
 def test_step_empty_batch_is_noop():
     assert _step(B=0, q=None, W=None) == 0
+
+
+# ------------------------------------------------------------------ forward implementation choice
+
+def _workspace_formula(B, H, T, d_k, d_v, nu, chunk, es):
+    """The chunked path's workspace as fwa.h states it."""
+    D = 2 * d_k * nu
+    nc = -(-T // chunk)
+    per_chunk = 3 * chunk * D + chunk * chunk + D * d_v + chunk * d_v
+    return B * H * nc * per_chunk * es + B * H * nc * chunk * (d_v + 2) * 4
+
+
+@pytest.mark.parametrize("shape,dtype,path", [
+    ((1, 8, 1024, 64, 64, 1, 64), "f32", "chunked"),      # 8 heads x 1024, D 128
+    ((4, 8, 4096, 64, 64, 2, 64), "bf16", "chunked"),     # 32 heads x 4096, D 256
+    ((8, 16, 16384, 64, 64, 3, 64), "bf16", "fused"),     # 128 heads x 16384: 7.6 GB workspace
+    ((8, 16, 16384, 64, 64, 3, 128), "bf16", "none"),     # neither fits (LDS): unsupported
+    ((1, 1, 64, 16, 16, 1, 16), "f32", "fused"),          # chunk 16: fused only
+    ((1, 1, 77, 16, 16, 1, 32), "f32", "chunked"),
+    ((2, 2, 300, 64, 64, 6, 64), "f32", "fused"),         # fp32 D 768 > 512: unsupported
+    ((0, 8, 1024, 64, 64, 1, 64), "f32", "empty"),
+])
+def test_forward_info_auto_choice(shape, dtype, path, monkeypatch):
+    import torch
+    monkeypatch.delenv("FWA_FORWARD_PATH", raising=False)
+    B, H, T, d_k, d_v, nu, chunk = shape
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    if path == "none" or 2 * d_k * nu > 512:
+        with pytest.raises(fwa.FwaError) as e:
+            fwa.delta_forward_info(B, H, T, d_k, d_v, nu, chunk, td)
+        assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
+        return
+    got, ws = fwa.delta_forward_info(B, H, T, d_k, d_v, nu, chunk, td)
+    if path == "empty":
+        assert (got, ws) == ("none", 0)
+        return
+    assert got == path
+    if path == "chunked":
+        assert ws == _workspace_formula(B, H, T, d_k, d_v, nu, chunk, 2 if dtype == "bf16" else 4)
+    else:
+        assert ws == 0
+
+
+def test_forward_info_env_override(monkeypatch):
+    import torch
+    big = (8, 16, 16384, 64, 64, 3, 64, torch.bfloat16)
+    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
+    path, ws = fwa.delta_forward_info(*big)
+    assert path == "chunked" and ws == _workspace_formula(*big[:7], 2)
+    monkeypatch.setenv("FWA_FORWARD_PATH", "fused")
+    assert fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64) == ("fused", 0)
+    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
+    with pytest.raises(fwa.FwaError) as e:                # chunk 16 has no chunked plan
+        fwa.delta_forward_info(1, 1, 64, 16, 16, 1, 16)
+    assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
+    monkeypatch.setenv("FWA_FORWARD_PATH", "fast")
+    with pytest.raises(fwa.FwaError) as e:
+        fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64)
+    assert e.value.status == fwa.FWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args", [
+    (1, 1, 64, 16, 16, 1, 48, 0),     # chunk
+    (1, 1, 64, 16, 16, 0, 64, 0),     # nu
+    (1, -1, 64, 16, 16, 1, 64, 0),    # H
+    (1, 1, 64, 16, 16, 1, 64, 9),     # dtype
+])
+def test_forward_info_invalid(args):
+    L = fwa.lib()
+    path, ws = ctypes.c_int(7), ctypes.c_int64(7)
+    assert L.fwa_delta_forward_info(*args, ctypes.byref(path), ctypes.byref(ws)) == fwa.FWA_ERR_INVALID_ARG
+    assert (path.value, ws.value) == (7, 7)      # outputs untouched on error

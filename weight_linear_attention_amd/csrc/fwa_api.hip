@@ -119,7 +119,7 @@ const char* fwa_status_string(fwa_status s) {
 
 const char* fwa_last_error(void) { return g_last_error.c_str(); }
 
-int fwa_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int fwa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, fwa_dtype dtype,
                     hipStream_t stream) {
@@ -144,11 +144,13 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, fw
                       "fwa_dpfp launch");
 }
 
-fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const void* beta_logit,
-                             const float* W0, void* y, float* W_final, int B, int H, int T,
-                             int d_k, int d_v, int nu, int chunk, fwa_dtype dtype,
-                             hipStream_t stream) {
-    const char* fn = "fwa_delta_forward";
+}  // extern "C"
+
+namespace {
+
+// Checks of the sizes shared by fwa_delta_forward and fwa_delta_forward_info.
+fwa_status check_forward_sizes(const char* fn, int B, int H, int T, int d_k, int d_v, int nu,
+                               int chunk, fwa_dtype dtype) {
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || H < 0 || T < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H/T", fn);
     if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
@@ -156,14 +158,10 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
         return fail(FWA_ERR_INVALID_ARG, "%s: nu=%d outside [1, 2*d_k-1]", fn, nu);
     if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
         return fail(FWA_ERR_INVALID_ARG, "%s: chunk=%d not in {16,32,64,128}", fn, chunk);
-    const int64_t BH = static_cast<int64_t>(B) * H;
-    if (BH == 0) return ok();
-    if (T > 0 && (!q || !k || !v || !beta_logit || !y))
-        return fail(FWA_ERR_INVALID_ARG, "%s: NULL input or output pointer", fn);
-    const void* ptrs[] = {q, k, v, beta_logit, W0, y, W_final};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p))
-            return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    return ok();
+}
+
+fwa_status check_forward_shape(const char* fn, int64_t BH, int T, int d_k, int d_v, int nu) {
     if (d_k != 16 && d_k != 32 && d_k != 64)
         return fail(FWA_ERR_UNSUPPORTED, "%s: d_k=%d not in {16,32,64}", fn, d_k);
     if (d_v != 16 && d_v != 32 && d_v != 64)
@@ -175,6 +173,82 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     if (BH > (int64_t(1) << 26) || static_cast<int64_t>(T) * d_v >= (int64_t(1) << 31) ||
         static_cast<int64_t>(T) * d_k >= (int64_t(1) << 31))
         return fail(FWA_ERR_UNSUPPORTED, "%s: too many (b, h) slices for one launch", fn);
+    return ok();
+}
+
+// The implementation a forward call takes (FWA_FORWARD_PATH and the shape), with its plan.
+struct ForwardChoice {
+    bool chunked;
+    fwa::ChunkPlan cplan;
+    fwa::FwdPlan fplan;
+};
+
+fwa_status choose_forward(const char* fn, int BH, int T, int d_k, int d_v, int nu, int chunk,
+                          bool bf16, ForwardChoice* c) {
+    const ForwardPath want = forward_path();
+    if (want == ForwardPath::kInvalid)
+        return fail(FWA_ERR_INVALID_ARG, "%s: FWA_FORWARD_PATH must be auto, chunked or fused", fn);
+    bool can_chunk = want != ForwardPath::kFused &&
+                     fwa::plan_chunked(BH, T, d_k, d_v, nu, chunk, bf16, &c->cplan);
+    const bool can_fuse = fwa::plan_forward(BH, d_k, d_v, nu, chunk, bf16, &c->fplan);
+    if (want == ForwardPath::kAuto && can_chunk && can_fuse && c->cplan.ws_bytes > kAutoWorkspaceLimit)
+        can_chunk = false;
+    c->chunked = can_chunk;
+    if (can_chunk) return ok();
+    if (want == ForwardPath::kChunked)
+        return fail(FWA_ERR_UNSUPPORTED,
+                    "%s: the chunked path does not support d_k=%d d_v=%d nu=%d chunk=%d", fn, d_k,
+                    d_v, nu, chunk);
+    if (!can_fuse)
+        return fail(FWA_ERR_UNSUPPORTED,
+                    "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn,
+                    d_k, d_v, nu, chunk);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
+                                  fwa_dtype dtype, int* path, int64_t* workspace_bytes) {
+    const char* fn = "fwa_delta_forward_info";
+    fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
+    if (st != FWA_OK) return st;
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    int p = FWA_PATH_NONE;
+    int64_t ws = 0;
+    if (BH > 0) {
+        if ((st = check_forward_shape(fn, BH, T, d_k, d_v, nu)) != FWA_OK) return st;
+        ForwardChoice c;
+        if ((st = choose_forward(fn, static_cast<int>(BH), T, d_k, d_v, nu, chunk,
+                                 dtype == FWA_BF16, &c)) != FWA_OK)
+            return st;
+        p = c.chunked ? FWA_PATH_CHUNKED : FWA_PATH_FUSED;
+        ws = c.chunked ? c.cplan.ws_bytes : 0;
+    }
+    if (path) *path = p;
+    if (workspace_bytes) *workspace_bytes = ws;
+    return ok();
+}
+
+fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const void* beta_logit,
+                             const float* W0, void* y, float* W_final, int B, int H, int T,
+                             int d_k, int d_v, int nu, int chunk, fwa_dtype dtype,
+                             hipStream_t stream) {
+    const char* fn = "fwa_delta_forward";
+    fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
+    if (st != FWA_OK) return st;
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    if (BH == 0) return ok();
+    if (T > 0 && (!q || !k || !v || !beta_logit || !y))
+        return fail(FWA_ERR_INVALID_ARG, "%s: NULL input or output pointer", fn);
+    const void* ptrs[] = {q, k, v, beta_logit, W0, y, W_final};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p))
+            return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if ((st = check_forward_shape(fn, BH, T, d_k, d_v, nu)) != FWA_OK) return st;
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
     const int es = elem_bytes(dtype);
     const int64_t nqk = BH * T * d_k * es, nv = BH * T * d_v * es, nb = BH * T * es;
     const int64_t nW = BH * d_v * D * 4;
@@ -190,39 +264,24 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     if (overlap(sy, sw)) return fail(FWA_ERR_INVALID_ARG, "%s: y overlaps W_final", fn);
 
     const bool bf16 = dtype == FWA_BF16;
-    const ForwardPath want = forward_path();
-    if (want == ForwardPath::kInvalid)
-        return fail(FWA_ERR_INVALID_ARG, "%s: FWA_FORWARD_PATH must be auto, chunked or fused", fn);
-    fwa::ChunkPlan cplan;
-    bool can_chunk = want != ForwardPath::kFused &&
-                     fwa::plan_chunked(static_cast<int>(BH), T, d_k, d_v, nu, chunk, bf16, &cplan);
-    fwa::FwdPlan plan;
-    const bool can_fuse = fwa::plan_forward(static_cast<int>(BH), d_k, d_v, nu, chunk, bf16, &plan);
-    if (want == ForwardPath::kAuto && can_chunk && can_fuse && cplan.ws_bytes > kAutoWorkspaceLimit)
-        can_chunk = false;
-    if (can_chunk) {
+    ForwardChoice c;
+    if ((st = choose_forward(fn, static_cast<int>(BH), T, d_k, d_v, nu, chunk, bf16, &c)) != FWA_OK)
+        return st;
+    if (c.chunked) {
         char* ws = nullptr;
-        if (cplan.ws_bytes > 0) {
-            const hipError_t e = workspace_alloc(&ws, cplan.ws_bytes, stream);
+        if (c.cplan.ws_bytes > 0) {
+            const hipError_t e = workspace_alloc(&ws, c.cplan.ws_bytes, stream);
             if (e != hipSuccess)
                 return fail(FWA_ERR_HIP, "%s: workspace of %lld bytes: %s", fn,
-                            (long long)cplan.ws_bytes, hipGetErrorString(e));
+                            (long long)c.cplan.ws_bytes, hipGetErrorString(e));
         }
-        const hipError_t le = fwa::launch_chunked(cplan, q, k, v, beta_logit, W0, y, W_final, ws,
-                                                  bf16, stream);
+        const hipError_t le = fwa::launch_chunked(c.cplan, q, k, v, beta_logit, W0, y, W_final,
+                                                  ws, bf16, stream);
         const hipError_t fe = ws ? hipFreeAsync(ws, stream) : hipSuccess;
         if (le != hipSuccess) return hip_status(le, "fwa_delta_forward launch");
         return hip_status(fe, "fwa_delta_forward workspace release");
     }
-    if (want == ForwardPath::kChunked)
-        return fail(FWA_ERR_UNSUPPORTED,
-                    "%s: the chunked path does not support d_k=%d d_v=%d nu=%d chunk=%d", fn, d_k,
-                    d_v, nu, chunk);
-    if (!can_fuse)
-        return fail(FWA_ERR_UNSUPPORTED,
-                    "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn,
-                    d_k, d_v, nu, chunk);
-    return hip_status(fwa::launch_delta_forward(plan, q, k, v, beta_logit, W0, y, W_final,
+    return hip_status(fwa::launch_delta_forward(c.fplan, q, k, v, beta_logit, W0, y, W_final,
                                                 static_cast<int>(BH), H, T, d_k, d_v, nu, chunk,
                                                 bf16, stream),
                       "fwa_delta_forward launch");

@@ -10,6 +10,8 @@ Functions (same names as the C entry points, minus the prefix):
     delta_forward(q, k, v, beta_logit, W0=None, chunk=64, out=None, W_final=None)
                                                   -> (y, W_final)
     delta_step(q, k, v, beta_logit, W, out=None)  -> y      (W is updated in place)
+    delta_forward_info(B, H, T, d_k, d_v, nu, chunk, dtype)
+                                                  -> ("chunked" | "fused" | "none", workspace bytes)
 """
 import ctypes
 import os
@@ -21,9 +23,10 @@ LIB_PATH = os.path.join(_PKG, "libfwa.so")
 
 FWA_OK, FWA_ERR_INVALID_ARG, FWA_ERR_UNSUPPORTED, FWA_ERR_HIP = 0, 1, 2, 3
 FWA_F32, FWA_BF16 = 0, 1
+FWA_PATH_NONE, FWA_PATH_CHUNKED, FWA_PATH_FUSED = 0, 1, 2
 
-EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_step", "fwa_status_string",
-            "fwa_last_error", "fwa_version")
+EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_info", "fwa_delta_step",
+            "fwa_status_string", "fwa_last_error", "fwa_version")
 
 
 class FwaError(RuntimeError):
@@ -49,6 +52,8 @@ def lib():
     L.fwa_dpfp.restype = i32
     L.fwa_delta_forward.argtypes = [P, P, P, P, P, P, P] + [i32] * 7 + [i32, P]
     L.fwa_delta_forward.restype = i32
+    L.fwa_delta_forward_info.argtypes = [i32] * 8 + [ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.fwa_delta_forward_info.restype = i32
     L.fwa_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5 + [i32, P]
     L.fwa_delta_step.restype = i32
     L.fwa_status_string.argtypes = [i32]
@@ -131,6 +136,19 @@ def delta_forward(q, k, v, beta_logit, W0=None, chunk=64, nu=1, out=None, W_fina
                                    _ptr(out), _ptr(W_final), B, H, T, d_k, d_v, nu, chunk,
                                    _dtype_code(q), _stream(dev)))
     return out, W_final
+
+
+def delta_forward_info(B, H, T, d_k, d_v, nu=1, chunk=64, dtype=torch.float32):
+    """Implementation ("chunked", "fused" or "none") that delta_forward takes for these sizes
+    under the current FWA_FORWARD_PATH, and the bytes of workspace it allocates."""
+    code = {torch.float32: FWA_F32, torch.bfloat16: FWA_BF16}.get(dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {dtype}; expected float32 or bfloat16")
+    path, ws = ctypes.c_int(0), ctypes.c_int64(0)
+    _check(lib().fwa_delta_forward_info(B, H, T, d_k, d_v, nu, chunk, code, ctypes.byref(path),
+                                        ctypes.byref(ws)))
+    names = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED: "fused"}
+    return names[path.value], ws.value
 
 
 def delta_step(q, k, v, beta_logit, W, nu=1, out=None):

@@ -162,14 +162,68 @@ struct GPTiles {
     f32x4 a[UPW][NT], b[UPW][NT], sa[UPW], sb[UPW];
 };
 
+// One unit: tile rows RA = Q and RB = NT-1-Q of X (K or Q) against the K rows, with the row
+// sums of the two rows.  The rows are compile-time constants, so every tile condition folds away.
+template <bool BF16, int C, int Q>
+__device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16], f32x4& sa,
+                                        f32x4& sb, const void* Xv, const void* Kv, int krs,
+                                        int D, int l16, int g4) {
+    using LT = std::conditional_t<BF16, u16, float>;
+    constexpr int NT = C / 16, RA = Q, RB = NT - 1 - Q;   // RB >= RA
+    const LT* X = static_cast<const LT*>(Xv);
+    const LT* Kr = static_cast<const LT*>(Kv);
+    const LT* Xa = X + (16 * RA + l16) * krs;
+    const LT* Xb = X + (16 * RB + l16) * krs;
+    const LT* Kb = Kr + l16 * krs;
+    if constexpr (BF16) {
+        bf16x8 ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
+#pragma unroll 2
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const int c0 = 32 * kk + 8 * g4;
+            const bf16x8 va = *reinterpret_cast<const bf16x8*>(Xa + c0);
+            const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Xb + c0);
+            bf16x8 kv8[RB + 1];
+#pragma unroll
+            for (int tb = 0; tb <= RB; ++tb) kv8[tb] = *reinterpret_cast<const bf16x8*>(Kb + 16 * tb * krs + c0);
+            sa = mfma_bf16_k32(va, ones, sa);
+            if (RB != RA) sb = mfma_bf16_k32(vb, ones, sb);
+#pragma unroll
+            for (int tb = 0; tb <= RB; ++tb) {
+                if (tb <= RA) ta[tb] = mfma_bf16_k32(va, kv8[tb], ta[tb]);
+                if (RB != RA) tb_[tb] = mfma_bf16_k32(vb, kv8[tb], tb_[tb]);
+            }
+        }
+    } else {
+#pragma unroll 2
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const int c0 = 16 * kk + 4 * g4;
+            const f32x4 va = *reinterpret_cast<const f32x4*>(Xa + c0);
+            const f32x4 vb = *reinterpret_cast<const f32x4*>(Xb + c0);
+            f32x4 k4[RB + 1];
+#pragma unroll
+            for (int tb = 0; tb <= RB; ++tb) k4[tb] = *reinterpret_cast<const f32x4*>(Kb + 16 * tb * krs + c0);
+            // consecutive MFMAs write different accumulators
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sa = mfma_f32_k4(va[e], 1.0f, sa);
+                if (RB != RA) sb = mfma_f32_k4(vb[e], 1.0f, sb);
+#pragma unroll
+                for (int tb = 0; tb <= RB; ++tb) {
+                    if (tb <= RA) ta[tb] = mfma_f32_k4(va[e], k4[tb][e], ta[tb]);
+                    if (RB != RA) tb_[tb] = mfma_f32_k4(vb[e], k4[tb][e], tb_[tb]);
+                }
+            }
+        }
+    }
+}
+
 template <bool BF16, int C>
 __device__ __forceinline__ void gp_compute(GPTiles<C>& gp, const void* Kv, const void* Qv,
                                            int krs, int D, int w, int l16, int g4) {
-    using LT = std::conditional_t<BF16, u16, float>;
     using GP = GPTiles<C>;
     constexpr int NT = GP::NT, NQ = GP::NQ, UPW = GP::UPW;
-    const LT* Kr = static_cast<const LT*>(Kv);
-    const LT* Qr = static_cast<const LT*>(Qv);
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
         gp.sa[ui] = gp.sb[ui] = zero4();
@@ -182,67 +236,14 @@ __device__ __forceinline__ void gp_compute(GPTiles<C>& gp, const void* Kv, const
         if (u < 2 * NQ) {
             const bool isP = u >= NQ;
             const int q = isP ? u - NQ : u;
-            const int ra = q, rb = NT - 1 - q;       // rb >= ra
-            const LT* Xa = (isP ? Qr : Kr) + (16 * ra + l16) * krs;
-            const LT* Xb = (isP ? Qr : Kr) + (16 * rb + l16) * krs;
-            const LT* Kb = Kr + l16 * krs;
-            if constexpr (BF16) {
-                bf16x8 ones;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
-#pragma unroll 2
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const int c0 = 32 * kk + 8 * g4;
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(Xa + c0);
-                    const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Xb + c0);
-                    gp.sa[ui] = mfma_bf16_k32(va, ones, gp.sa[ui]);
-                    if (rb != ra) gp.sb[ui] = mfma_bf16_k32(vb, ones, gp.sb[ui]);
-#pragma unroll
-                    for (int tb = 0; tb < NT; ++tb) {
-                        if (tb <= rb) {
-                            const bf16x8 kv8 = *reinterpret_cast<const bf16x8*>(Kb + 16 * tb * krs + c0);
-                            if (tb <= ra) gp.a[ui][tb] = mfma_bf16_k32(va, kv8, gp.a[ui][tb]);
-                            if (rb != ra) gp.b[ui][tb] = mfma_bf16_k32(vb, kv8, gp.b[ui][tb]);
-                        }
-                    }
-                }
-            } else {
-#pragma unroll 2
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const int c0 = 16 * kk + 4 * g4;
-                    const float4 va = *reinterpret_cast<const float4*>(Xa + c0);
-                    const float4 vb = *reinterpret_cast<const float4*>(Xb + c0);
-                    gp.sa[ui] = mfma_f32_k4(va.x, 1.0f, gp.sa[ui]);
-                    gp.sa[ui] = mfma_f32_k4(va.y, 1.0f, gp.sa[ui]);
-                    gp.sa[ui] = mfma_f32_k4(va.z, 1.0f, gp.sa[ui]);
-                    gp.sa[ui] = mfma_f32_k4(va.w, 1.0f, gp.sa[ui]);
-                    if (rb != ra) {
-                        gp.sb[ui] = mfma_f32_k4(vb.x, 1.0f, gp.sb[ui]);
-                        gp.sb[ui] = mfma_f32_k4(vb.y, 1.0f, gp.sb[ui]);
-                        gp.sb[ui] = mfma_f32_k4(vb.z, 1.0f, gp.sb[ui]);
-                        gp.sb[ui] = mfma_f32_k4(vb.w, 1.0f, gp.sb[ui]);
-                    }
-#pragma unroll
-                    for (int tb = 0; tb < NT; ++tb) {
-                        if (tb <= rb) {
-                            const float4 k4 = *reinterpret_cast<const float4*>(Kb + 16 * tb * krs + c0);
-                            if (tb <= ra) {
-                                f32x4& g = gp.a[ui][tb];
-                                g = mfma_f32_k4(va.x, k4.x, g);
-                                g = mfma_f32_k4(va.y, k4.y, g);
-                                g = mfma_f32_k4(va.z, k4.z, g);
-                                g = mfma_f32_k4(va.w, k4.w, g);
-                            }
-                            if (rb != ra) {
-                                f32x4& g = gp.b[ui][tb];
-                                g = mfma_f32_k4(vb.x, k4.x, g);
-                                g = mfma_f32_k4(vb.y, k4.y, g);
-                                g = mfma_f32_k4(vb.z, k4.z, g);
-                                g = mfma_f32_k4(vb.w, k4.w, g);
-                            }
-                        }
-                    }
-                }
+            const void* X = isP ? Qv : Kv;
+            // q is uniform over the wave: one branch selects the unit's instantiation
+            switch (q) {
+                case 0: gp_unit<BF16, C, 0>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 1: if constexpr (NQ > 1) gp_unit<BF16, C, (NQ > 1 ? 1 : 0)>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 2: if constexpr (NQ > 2) gp_unit<BF16, C, (NQ > 2 ? 2 : 0)>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 3: if constexpr (NQ > 3) gp_unit<BF16, C, (NQ > 3 ? 3 : 0)>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                default: break;
             }
         }
     }
@@ -274,6 +275,42 @@ __device__ __forceinline__ void gp_write_rho(const GPTiles<C>& gp, float* rhok, 
     }
 }
 
+// Scaling of one unit's tiles (rows RA = Q and RB = NT-1-Q), see gp_scale.
+template <bool BF16, int C, int Q>
+__device__ __forceinline__ void gp_scale_unit(const f32x4 (&ta_)[C / 16], const f32x4 (&tb_)[C / 16],
+                                              bool isP, const float* rhok, const float* rhoq,
+                                              const float* betas, float* Ls, int lss, void* Pv,
+                                              int pss, int l16, int g4) {
+    using LT = std::conditional_t<BF16, u16, float>;
+    constexpr int NT = C / 16, RA = Q, RB = NT - 1 - Q;
+    LT* Ps = static_cast<LT*>(Pv);
+#pragma unroll
+    for (int k2 = 0; k2 < 2 * NT; ++k2) {
+        // k2 < NT: tile (RA, k2); k2 >= NT: tile (RB, k2 - NT)
+        const bool rowa = k2 < NT;
+        const int ta = rowa ? RA : RB;
+        const int tb = rowa ? k2 : k2 - NT;
+        if (tb > ta || (!rowa && RB == RA)) continue;
+        const f32x4 acc = rowa ? ta_[k2 % NT] : tb_[k2 % NT];
+        const int s = 16 * tb + l16, tr = 16 * ta + 4 * g4;
+        const float rks = rhok[s];
+        if (isP) {
+            const f32x4 rq = *reinterpret_cast<const f32x4*>(rhoq + tr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float val = s <= tr + e ? rq[e] * rks * acc[e] : 0.0f;
+                Ps[(tr + e) * pss + s] = from_f32<LT>(val);
+            }
+        } else {
+            const f32x4 rk = *reinterpret_cast<const f32x4*>(rhok + tr);
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(betas + tr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Ls[(tr + e) * lss + s] = s < tr + e ? bt[e] * rk[e] * rks * acc[e] : 0.0f;
+        }
+    }
+}
+
 // Writes Ls = beta_t rho_t rho_s G[t][s] (s < t, fp32) and Ps = rho_q,t rho_k,s P[t][s]
 // (s <= t, operand type) for the tiles of this wave's units; tiles above the diagonal are not
 // written.
@@ -281,41 +318,20 @@ template <bool BF16, int C>
 __device__ __forceinline__ void gp_scale(const GPTiles<C>& gp, const float* rhok,
                                          const float* rhoq, const float* betas, float* Ls,
                                          int lss, void* Pv, int pss, int w, int l16, int g4) {
-    using LT = std::conditional_t<BF16, u16, float>;
     using GP = GPTiles<C>;
-    constexpr int NT = GP::NT, NQ = GP::NQ, UPW = GP::UPW;
-    LT* Ps = static_cast<LT*>(Pv);
+    constexpr int NQ = GP::NQ, UPW = GP::UPW;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
         const int u = w + 4 * ui;
         if (u < 2 * NQ) {
             const bool isP = u >= NQ;
             const int q = isP ? u - NQ : u;
-            const int ra = q, rb = NT - 1 - q;
-#pragma unroll
-            for (int k2 = 0; k2 < 2 * NT; ++k2) {
-                // k2 < NT: tile (ra, k2) from a; k2 >= NT: tile (rb, k2 - NT) from b
-                const bool rowa = k2 < NT;
-                const int ta = rowa ? ra : rb;
-                const int tb = rowa ? k2 : k2 - NT;
-                if (tb > ta || (!rowa && rb == ra)) continue;
-                const f32x4 acc = rowa ? gp.a[ui][k2 % NT] : gp.b[ui][k2 % NT];
-                const int s = 16 * tb + l16, tr = 16 * ta + 4 * g4;
-                const float rks = rhok[s];
-                if (isP) {
-                    const f32x4 rq = *reinterpret_cast<const f32x4*>(rhoq + tr);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float val = s <= tr + e ? rq[e] * rks * acc[e] : 0.0f;
-                        Ps[(tr + e) * pss + s] = from_f32<LT>(val);
-                    }
-                } else {
-                    const f32x4 rk = *reinterpret_cast<const f32x4*>(rhok + tr);
-                    const f32x4 bt = *reinterpret_cast<const f32x4*>(betas + tr);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Ls[(tr + e) * lss + s] = s < tr + e ? bt[e] * rk[e] * rks * acc[e] : 0.0f;
-                }
+            switch (q) {
+                case 0: gp_scale_unit<BF16, C, 0>(gp.a[ui], gp.b[ui], isP, rhok, rhoq, betas, Ls, lss, Pv, pss, l16, g4); break;
+                case 1: if constexpr (NQ > 1) gp_scale_unit<BF16, C, (NQ > 1 ? 1 : 0)>(gp.a[ui], gp.b[ui], isP, rhok, rhoq, betas, Ls, lss, Pv, pss, l16, g4); break;
+                case 2: if constexpr (NQ > 2) gp_scale_unit<BF16, C, (NQ > 2 ? 2 : 0)>(gp.a[ui], gp.b[ui], isP, rhok, rhoq, betas, Ls, lss, Pv, pss, l16, g4); break;
+                case 3: if constexpr (NQ > 3) gp_scale_unit<BF16, C, (NQ > 3 ? 3 : 0)>(gp.a[ui], gp.b[ui], isP, rhok, rhoq, betas, Ls, lss, Pv, pss, l16, g4); break;
+                default: break;
             }
         }
     }

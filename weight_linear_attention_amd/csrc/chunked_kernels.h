@@ -76,7 +76,8 @@ __device__ __forceinline__ const char* blk_ptr(const char* base, int64_t blk, in
 
 // ------------------------------------------------------------------------------------------
 // prep: one workgroup per chunk (b, h, n).  DPFP, G and P with the normalisers, L and its
-// diagonal-block inverses, then the solves for W_y and U_y; writes
+// diagonal-block inverses, the block inverse A = (I + L)^-1, U_y by block substitution and
+// W_y^T = K^T (A diag(beta rho_k))^T on the MFMA; writes
 //   WyA (A blocks of W_y, C x D), KtA (A blocks of K^T, D x C, raw products),
 //   QA (A blocks of Q, raw), PA (A blocks of P~, zero above the diagonal),
 //   Uy (fp32 accumulator tiles of U_y), RK, RQ (rho_k, rho_q).
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     constexpr int NT = C / 16, NTB = NT / pair;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     LT* Kr = reinterpret_cast<LT*>(smem + a.l_kr);        // [C][krs] K raw products
-    LT* Qr = reinterpret_cast<LT*>(smem + a.l_qr);        // [C][krs] Q, then W_y staging
+    LT* Qr = reinterpret_cast<LT*>(smem + a.l_qr);        // [C][krs] Q, then A' (below)
     LT* Xk = reinterpret_cast<LT*>(smem + a.l_x);         // [C][d_k] raw k rows (staging)
     LT* Xq = Xk + C * a.d_k;                              // [C][d_k] raw q rows (staging)
     float* Ls = reinterpret_cast<float*>(smem + a.l_ls);  // [C][lss] L (over the staging)
@@ -175,14 +176,14 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
             const LT* src = Kr + (16 * pair * j + 4 * (lam >> 4)) * krs + 16 * dt + (lam & 15);
             uint4 val;
             if constexpr (BF16) {
-                uint32_t wd[4];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const LT* s = src + 16 * h * krs;
-                    wd[2 * h] = static_cast<uint32_t>(s[0]) | (static_cast<uint32_t>(s[krs]) << 16);
-                    wd[2 * h + 1] = static_cast<uint32_t>(s[2 * krs]) | (static_cast<uint32_t>(s[3 * krs]) << 16);
-                }
-                val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                // the wave holds one block (lam = lane): two LDS transpose reads give the 8
+                // slots; lane i of a 16-lane group addresses row 4 (lam / 16) + i / 4, column
+                // 16 dt + 4 (i % 4) of each 16-row half
+                const LT* kp = Kr + (16 * pair * j + 4 * (lam >> 4) + ((lam & 15) >> 2)) * krs +
+                               16 * dt + 4 * (lam & 3);
+                const bf16x4 c0 = lds_read_tr_b16x4(kp);
+                const bf16x4 c1 = lds_read_tr_b16x4(kp + 16 * krs);
+                val = __builtin_bit_cast(uint4, __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7));
             } else {
                 val = make_uint4(__float_as_uint(src[0]), __float_as_uint(src[krs]),
                                  __float_as_uint(src[2 * krs]), __float_as_uint(src[3 * krs]));
@@ -216,63 +217,194 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
             reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
         }
     }
-    __syncthreads();   // Li complete; Q is dead (its space stages W_y)
+    __syncthreads();   // Li complete; Q is dead (its space holds A')
 
-    // ---- solves: column tiles ct < ND give W_y (staged in LDS), the rest give U_y
-    LT* Wys = Qr;
-    char* uy = ws + a.o_uy + u * (static_cast<int64_t>(C) * d_v * 4);
-    for (int ct = w; ct < ND + NVT; ct += 4) {
-        f32x4 X[NT];
-        const bool isK = ct < ND;
-        if (isK) {
+    // ---- A = (I + L)^-1 by block columns (column block tb = w per wave), stored twice with
+    //      its columns scaled: A' = A diag(beta rho_k) and A'' = A diag(beta), each as fp32 or
+    //      as a bf16 hi + lo pair whose sum carries the fp32 value to about 2^-17.
+    float* Af = reinterpret_cast<float*>(smem + a.l_qr);           // fp32: A' [C][aps]
+    float* Bf = Af + C * a.aps;                                      //       A''
+    u16* Ah = reinterpret_cast<u16*>(smem + a.l_qr);                // bf16: A' hi, lo
+    u16* Al = Ah + C * a.aps;
+    u16* Bh = Al + C * a.aps;                                        //       A'' hi, lo
+    u16* Bl = Bh + C * a.aps;
+    const int aps = a.aps;
+    if (w < NT) {
+        const int tb = w;
+        const float bsc = betas[16 * tb + l16];
+        const float csc = bsc * rhok[16 * tb + l16];
+        f32x4 Ab[NT];
 #pragma unroll
-            for (int ta = 0; ta < NT; ++ta)
+        for (int ta = 0; ta < NT; ++ta) {
+            f32x4 val = zero4();
+            if (ta == tb) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * ta + 4 * g4 + e;
-                    X[ta][e] = betas[t] * rhok[t] * to_f32(Kr[t * krs + 16 * ct + l16]);
+                for (int e = 0; e < 4; ++e) val[e] = Li[(16 * ta + 4 * g4 + e) * kLiStride + l16];
+            } else if (ta > tb) {
+                // A[ta][tb] = -Li[ta] sum_{tc = tb}^{ta-1} L[ta][tc] A[tc][tb]
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int tc = 0; tc < NT; ++tc) {
+                    if (tc >= tb && tc < ta) {
+                        const float4 l4 = *reinterpret_cast<const float4*>(
+                            Ls + (16 * ta + l16) * a.lss + 16 * tc + 4 * g4);
+                        acc = mfma_f32_k4(l4.x, Ab[tc][0], acc);
+                        acc = mfma_f32_k4(l4.y, Ab[tc][1], acc);
+                        acc = mfma_f32_k4(l4.z, Ab[tc][2], acc);
+                        acc = mfma_f32_k4(l4.w, Ab[tc][3], acc);
+                    }
                 }
-        } else {
-#pragma unroll
-            for (int ta = 0; ta < NT; ++ta)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * ta + 4 * g4 + e;
-                    X[ta][e] = betas[t] * to_f32(Xv[t * d_v + 16 * (ct - ND) + l16]);
-                }
-        }
-        block_solve<NT>(X, Ls, a.lss, Li, l16, g4);
-        if (isK) {
-#pragma unroll
-            for (int ta = 0; ta < NT; ++ta) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Wys[(16 * ta + 4 * g4 + e) * krs + 16 * ct + l16] = from_f32<LT>(X[ta][e]);
+                const float4 i4 = *reinterpret_cast<const float4*>(Li + (16 * ta + l16) * kLiStride + 4 * g4);
+                val = mfma_f32_k4(i4.x, acc[0], val);
+                val = mfma_f32_k4(i4.y, acc[1], val);
+                val = mfma_f32_k4(i4.z, acc[2], val);
+                val = mfma_f32_k4(i4.w, acc[3], val);
+                val = -val;
             }
-        } else {
-            const int vt = ct - ND;
+            Ab[ta] = val;
 #pragma unroll
-            for (int ta = 0; ta < NT; ++ta)
-                *reinterpret_cast<f32x4*>(blk_ptr(uy, ta * NVT + vt, l)) = X[ta];
+            for (int e = 0; e < 4; ++e) {
+                const int at = (16 * ta + 4 * g4 + e) * aps + 16 * tb + l16;
+                const float x = val[e] * csc, y = val[e] * bsc;
+                if constexpr (BF16) {
+                    const u16 xh = f32_to_bf16_bits(x), yh = f32_to_bf16_bits(y);
+                    Ah[at] = xh;
+                    Al[at] = f32_to_bf16_bits(x - bf16_bits_to_f32(xh));
+                    Bh[at] = yh;
+                    Bl[at] = f32_to_bf16_bits(y - bf16_bits_to_f32(yh));
+                } else {
+                    Af[at] = x;
+                    Bf[at] = y;
+                }
+            }
         }
     }
     __syncthreads();
 
-    // ---- WyA: blocks (tt, j), j < NDB
-    {
-        char* wy = ws + a.o_wy + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < NT * NDB * 64; e += 256) {
-            const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
-            const LT* src = Wys + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
-            uint4 val;
-            if constexpr (BF16) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(src);
-                const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
-                val = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else {
-                val = *reinterpret_cast<const uint4*>(src);
+    // ---- U_y = A'' V as accumulator tiles (t-tile, v-tile), one v-tile per wave and pass
+    char* uy = ws + a.o_uy + u * (static_cast<int64_t>(C) * d_v * 4);
+    for (int vt = w; vt < NVT; vt += 4) {
+        f32x4 acc[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[tt] = zero4();
+        if constexpr (BF16) {
+            // k-slot (h, e) of lane group g is row s = 32 kb + 16 h + 4 g + e; V by transpose reads
+#pragma unroll
+            for (int kb = 0; kb < C / 32; ++kb) {
+                const LT* vp = Xv + (32 * kb + 4 * g4 + (l16 >> 2)) * d_v + 16 * vt + 4 * (l16 & 3);
+                const bf16x4 c0 = lds_read_tr_b16x4(vp);
+                const bf16x4 c1 = lds_read_tr_b16x4(vp + 16 * d_v);
+                const bf16x8 bv = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (32 * kb <= 16 * tt + 15) {
+                        const u16* hp = Bh + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const u16* lp = Bl + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const bf16x8 ah = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(hp),
+                                                                  *reinterpret_cast<const bf16x4*>(hp + 16),
+                                                                  0, 1, 2, 3, 4, 5, 6, 7);
+                        const bf16x8 al = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(lp),
+                                                                  *reinterpret_cast<const bf16x4*>(lp + 16),
+                                                                  0, 1, 2, 3, 4, 5, 6, 7);
+                        acc[tt] = mfma_bf16_k32(ah, bv, acc[tt]);
+                        acc[tt] = mfma_bf16_k32(al, bv, acc[tt]);
+                    }
+                }
             }
-            *reinterpret_cast<uint4*>(wy + static_cast<int64_t>(e) * 16) = val;
+        } else {
+            // k-slot of lane group g in the r-th of four MFMAs is row s = 16 m + 4 g + r
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                float vb[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vb[r] = to_f32(Xv[(16 * m + 4 * g4 + r) * d_v + 16 * vt + l16]);
+                f32x4 a4[NT];
+#pragma unroll
+                for (int tt = m; tt < NT; ++tt)
+                    a4[tt] = *reinterpret_cast<const f32x4*>(Bf + (16 * tt + l16) * aps + 16 * m + 4 * g4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(a4[tt][r], vb[r], acc[tt]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+            *reinterpret_cast<f32x4*>(blk_ptr(uy, tt * NVT + vt, l)) = acc[tt];
+    }
+
+    // ---- W_y^T = K^T A'^T as accumulator tiles (d-tile, t-tile), which are the WyA blocks:
+    //      lane l, slot e of tile (dt, tt) holds W_y[16 tt + l % 16][16 dt + 4 (l / 16) + e].
+    char* wy = ws + a.o_wy + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+    if constexpr (BF16) {
+        // k-slot (h, e) of lane group g is row s = 32 kb + 16 h + 4 g + e of the chunk; the K^T
+        // operand comes from the row-major K tile by two LDS transpose reads.
+        for (int j = w; j < NDB; j += 4) {
+            f32x4 acc[2][NT];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) acc[h][tt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < C / 32; ++kb) {
+                bf16x8 ka[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const LT* kp = Kr + (32 * kb + 4 * g4 + (l16 >> 2)) * krs + 16 * (2 * j + h) + 4 * (l16 & 3);
+                    const bf16x4 c0 = lds_read_tr_b16x4(kp);
+                    const bf16x4 c1 = lds_read_tr_b16x4(kp + 16 * krs);
+                    ka[h] = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (32 * kb <= 16 * tt + 15) {
+                        const u16* hp = Ah + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const u16* lp = Al + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(hp);
+                        const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(hp + 16);
+                        const bf16x4 o0 = *reinterpret_cast<const bf16x4*>(lp);
+                        const bf16x4 o1 = *reinterpret_cast<const bf16x4*>(lp + 16);
+                        const bf16x8 bh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const bf16x8 bl = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            acc[h][tt] = mfma_bf16_k32(ka[h], bh, acc[h][tt]);
+                            acc[h][tt] = mfma_bf16_k32(ka[h], bl, acc[h][tt]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                *reinterpret_cast<uint4*>(blk_ptr(wy, tt * NDB + j, l)) = pack_bf16x8(acc[0][tt], acc[1][tt]);
+        }
+    } else {
+        // k-slot of lane group g in the r-th of four MFMAs is row s = 16 m + 4 g + r.
+        for (int dt = w; dt < ND; dt += 4) {
+            f32x4 acc[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) acc[tt] = zero4();
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                float ka[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ka[r] = to_f32(Kr[(16 * m + 4 * g4 + r) * krs + 16 * dt + l16]);
+                float4 b4[NT];
+#pragma unroll
+                for (int tt = m; tt < NT; ++tt)
+                    b4[tt] = *reinterpret_cast<const float4*>(Af + (16 * tt + l16) * aps + 16 * m + 4 * g4);
+#pragma unroll
+                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[0], b4[tt].x, acc[tt]);
+#pragma unroll
+                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[1], b4[tt].y, acc[tt]);
+#pragma unroll
+                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[2], b4[tt].z, acc[tt]);
+#pragma unroll
+                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[3], b4[tt].w, acc[tt]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                *reinterpret_cast<f32x4*>(blk_ptr(wy, tt * NDB + dt, l)) = acc[tt];
         }
     }
 }

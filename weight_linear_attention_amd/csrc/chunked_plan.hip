@@ -35,8 +35,10 @@ bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Chu
     int off = 0;
     a.l_kr = off;
     off = align16(off + C * a.krs * es);
-    a.l_qr = off;
-    off = align16(off + C * a.krs * es);
+    a.l_qr = off;                                  // Q, then A' and A'' (fp32 or bf16 hi + lo)
+    a.aps = bf16 ? C + 8 : C + 4;
+    const int qbytes = C * a.krs * es, abytes = 8 * C * a.aps;   // two fp32-sized copies
+    off = align16(off + (qbytes > abytes ? qbytes : abytes));
     a.l_x = off;                                   // raw k, q rows; then L, P~ and Li
     const int xend = align16(off + 2 * C * d_k * es);
     a.l_ls = off;

@@ -57,7 +57,7 @@ struct ChunkArgs {
     int64_t o_wy, o_kt, o_qa, o_pa, o_uy, o_rk, o_rq, o_wn, o_un;
     int BH, T, NC, d_k, d_v, nu, D;
     int DP, NDP;
-    int krs, lss, pss;
+    int krs, lss, pss, aps;
     int l_kr, l_qr, l_x, l_ls, l_ps, l_li, l_xv, l_small;
 };
 

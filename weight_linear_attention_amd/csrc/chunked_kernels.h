@@ -543,6 +543,8 @@ __global__ __launch_bounds__(64 * DP, 1) void delta_chain_kernel(ChunkArgs a) {
             for (int pp = 0; pp < DP; ++pp)
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) part[pp][tt] = Red[((buf * DP + pp) * NT + tt) * 64 + l];
+            // all partial reads go out together, ahead of their uses (one LDS round trip)
+            __builtin_amdgcn_sched_group_barrier(0x100, DP * NT, 0);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 f32x4 s2 = part[0][tt];
@@ -565,20 +567,30 @@ __global__ __launch_bounds__(64 * DP, 1) void delta_chain_kernel(ChunkArgs a) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) U[tt] *= rk[tt];
         load_uy(un);
-        // W^T += K^T (rho_k o U)
+        // W^T += K^T (rho_k o U); fp32 sums even and odd t-tiles in separate accumulators so
+        // that consecutive MFMAs are independent
+        if constexpr (BF16) {
 #pragma unroll
-        for (int j = 0; j < NTB; ++j) {
-            if constexpr (BF16) {
+            for (int j = 0; j < NTB; ++j) {
                 const uint4 bu = pack_bf16x8(U[2 * j], U[2 * j + 1]);
 #pragma unroll
                 for (int i = 0; i < NDP; ++i) Wst[i] = mfma_bf16_k32(as_bf16x8(kt[i][j]), as_bf16x8(bu), Wst[i]);
-            } else {
+            }
+        } else {
+            f32x4 odd[NDP];
+#pragma unroll
+            for (int i = 0; i < NDP; ++i) odd[i] = zero4();
+#pragma unroll
+            for (int j = 0; j < NTB; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int i = 0; i < NDP; ++i)
-                        Wst[i] = mfma_f32_k4(as_f32x4(kt[i][j])[e], U[j][e], Wst[i]);
-            }
+                    for (int i = 0; i < NDP; ++i) {
+                        f32x4& dst = (j & 1) ? odd[i] : Wst[i];
+                        dst = mfma_f32_k4(as_f32x4(kt[i][j])[e], U[j][e], dst);
+                    }
+#pragma unroll
+            for (int i = 0; i < NDP; ++i) Wst[i] += odd[i];
         }
         load_kt(un);
     }

@@ -15,12 +15,30 @@
 // one wave, CPL float4 columns per lane (D = 4 * LR * CPL), so every row dot product is a
 // lane-shuffle reduction inside a wave and each lane issues 16-byte loads and stores.  Each
 // lane computes the f and g entries of its own columns straight from k and q (cached global
-// reads) and the group reduces the DPFP sums, so the kernel needs no LDS and no barrier and
-// every W load is in flight from the first instruction.
+// reads) and the group reduces the DPFP sums, so the kernel needs no LDS and no barrier; every
+// load (W rows, v, beta, k, q) is in flight before the first arithmetic.
 #include "fwa_common.h"
 #include "fwa_internal.h"
 
 namespace fwa {
+
+// Sum of x over each aligned group of LR lanes (LR in {8, 16, 32, 64}), in every lane of the
+// group: DPP inside 16-lane rows (quad permutes, then row rotations), one cross-row permute per
+// doubling beyond 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_group_sum(float x, int LR) {
+    x = dpp_add<0xB1>(x);                    // quad_perm [1,0,3,2]: lane ^ 1
+    x = dpp_add<0x4E>(x);                    // quad_perm [2,3,0,1]: lane ^ 2
+    if (LR == 8) return x + __shfl_xor(x, 4, 8);
+    x = dpp_add<0x124>(x);                   // row_ror:4
+    x = dpp_add<0x128>(x);                   // row_ror:8
+    if (LR >= 32) x += __shfl_xor(x, 16);
+    if (LR == 64) x += __shfl_xor(x, 32);
+    return x;
+}
 
 template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void delta_step_kernel(
@@ -29,7 +47,8 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
     int nu, int LR) {
     constexpr int RB = (CPL == 1) ? 8 : (CPL == 2 ? 4 : 2);  // row rounds per batch
     const int64_t s = blockIdx.x;
-    const int two_dk = 2 * d_k;
+    const int two_dk = 2 * d_k;                // a power of two (d_k in {16, 32, 64, 128})
+    const int sh = __builtin_ctz(two_dk);
     const int D = two_dk * nu;
     float* Ws = W + s * static_cast<int64_t>(d_v) * D;
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
@@ -38,19 +57,25 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
     const int rr = wv * rpw + l / LR;  // this lane's row inside a round
     const int c = l % LR;
     const int rounds = (d_v + RPR - 1) / RPR;
+    const int64_t vb = s * d_v;
 
-    // First batch of W rows: issued before anything else.
+    // Every load is issued up front: the first batch of W rows, then this lane's v entries,
+    // beta's logit and the k and q entries its columns need.
     float4 wrow[RB][CPL];
+    float vrow[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
         const int row = rr + RPR * b;
+        const bool ok = b < rounds && row < d_v;
+        const int rs = ok ? row : 0;                     // a row that exists; zeroed below
 #pragma unroll
-        for (int m = 0; m < CPL; ++m)
-            wrow[b][m] = (b < rounds && row < d_v)
-                             ? *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(row) * D +
-                                                                4 * (c + LR * m))
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int m = 0; m < CPL; ++m) {
+            const float4 w4 = *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(rs) * D + 4 * (c + LR * m));
+            wrow[b][m] = ok ? w4 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        vrow[b] = load_elem<BF16>(v, vb + rs);
     }
+    const float blog = load_elem<BF16>(bl, s);
 
     // f and g on this lane's 4*CPL columns.  Position d lies in the block of shift
     // i = d / (2 d_k) + 1 at j = d mod 2 d_k; its factors are relu([k,-k]) at j and at
@@ -63,10 +88,10 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int d = 4 * (c + LR * m) + e;
-            const int i = d / two_dk + 1;
-            const int j = d - (i - 1) * two_dk;
-            const int jr = ((j - i) % two_dk + two_dk) % two_dk;
-            const int ja = j < d_k ? j : j - d_k, jb = jr < d_k ? jr : jr - d_k;
+            const int i = (d >> sh) + 1;
+            const int j = d & (two_dk - 1);
+            const int jr = (j - i) & (two_dk - 1);
+            const int ja = j & (d_k - 1), jb = jr & (d_k - 1);
             const float sa = j < d_k ? 1.0f : -1.0f, sb = jr < d_k ? 1.0f : -1.0f;
             const float fk = relu(sa * load_elem<BF16>(k, kb + ja)) *
                              relu(sb * load_elem<BF16>(k, kb + jb));
@@ -78,10 +103,8 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
             Sg += fq;
         }
     }
-    for (int off = LR / 2; off >= 1; off >>= 1) {
-        Sf += __shfl_xor(Sf, off, LR);
-        Sg += __shfl_xor(Sg, off, LR);
-    }
+    Sf = lane_group_sum(Sf, LR);
+    Sg = lane_group_sum(Sg, LR);
     const float rf = 1.0f / (Sf + kDpfpEps), rg = 1.0f / (Sg + kDpfpEps);
     float fg = 0.0f;
 #pragma unroll
@@ -90,42 +113,48 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
         g[e] *= rg;
         fg += f[e] * g[e];
     }
-    for (int off = LR / 2; off >= 1; off >>= 1) fg += __shfl_xor(fg, off, LR);
-    const float beta = sigmoid_stable(load_elem<BF16>(bl, s));
-    const int64_t vb = s * d_v;
+    fg = lane_group_sum(fg, LR);
+    const float beta = sigmoid_stable(blog);
 
     for (int r0 = 0; r0 < rounds; r0 += RB) {
         if (r0 > 0) {
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int row = rr + RPR * (r0 + b);
+                const bool ok = r0 + b < rounds && row < d_v;
+                const int rs = ok ? row : 0;
 #pragma unroll
-                for (int m = 0; m < CPL; ++m)
-                    wrow[b][m] = (r0 + b < rounds && row < d_v)
-                                     ? *reinterpret_cast<const float4*>(
-                                           Ws + static_cast<int64_t>(row) * D + 4 * (c + LR * m))
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int m = 0; m < CPL; ++m) {
+                    const float4 w4 = *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(rs) * D + 4 * (c + LR * m));
+                    wrow[b][m] = ok ? w4 : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                vrow[b] = load_elem<BF16>(v, vb + rs);
+            }
+        }
+        float dk[RB], dq[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            dk[b] = dq[b] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) {
+                const float4 w4 = wrow[b][m];
+                dk[b] += w4.x * f[m * 4 + 0] + w4.y * f[m * 4 + 1] + w4.z * f[m * 4 + 2] +
+                         w4.w * f[m * 4 + 3];
+                dq[b] += w4.x * g[m * 4 + 0] + w4.y * g[m * 4 + 1] + w4.z * g[m * 4 + 2] +
+                         w4.w * g[m * 4 + 3];
             }
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            const int row = rr + RPR * (r0 + b);
-            float dk = 0.0f, dq = 0.0f;
+            dk[b] = lane_group_sum(dk[b], LR);
+            dq[b] = lane_group_sum(dq[b], LR);
+        }
 #pragma unroll
-            for (int m = 0; m < CPL; ++m) {
-                const float4 w4 = wrow[b][m];
-                dk += w4.x * f[m * 4 + 0] + w4.y * f[m * 4 + 1] + w4.z * f[m * 4 + 2] +
-                      w4.w * f[m * 4 + 3];
-                dq += w4.x * g[m * 4 + 0] + w4.y * g[m * 4 + 1] + w4.z * g[m * 4 + 2] +
-                      w4.w * g[m * 4 + 3];
-            }
-            for (int off = LR / 2; off >= 1; off >>= 1) {
-                dk += __shfl_xor(dk, off, LR);
-                dq += __shfl_xor(dq, off, LR);
-            }
+        for (int b = 0; b < RB; ++b) {
+            const int row = rr + RPR * (r0 + b);
             if (r0 + b < rounds && row < d_v) {
-                const float u = beta * (load_elem<BF16>(v, vb + row) - dk);
-                if (c == 0) store_elem<BF16>(y, vb + row, dq + u * fg);
+                const float u = beta * (vrow[b] - dk[b]);
+                if (c == 0) store_elem<BF16>(y, vb + row, dq[b] + u * fg);
 #pragma unroll
                 for (int m = 0; m < CPL; ++m) {
                     float4 w4 = wrow[b][m];

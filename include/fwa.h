@@ -110,7 +110,10 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *              hipMallocAsync on `stream` and returned with hipFreeAsync on `stream` before
  *              the call returns (the device's default memory pool is set, once, to keep freed
  *              memory for reuse).  Chunks of
- *              32 or 64 rows; D in {32, 64, 96, 128, 192, 256}, and for bf16 also 384, 512.
+ *              32 or 64 rows; D in {32, 64, 96, 128, 192, 256}, and for bf16 also 384, 512;
+ *              the prep kernel's working set (2*chunk*(D + 8) elements plus chunk-sized
+ *              scratch) must fit the 160 KiB of LDS, which leaves out chunk 64 for fp32 D = 256
+ *              and bf16 D = 512.
  *     fused    one launch that keeps the chunk and the memory on chip; allocates nothing.
  *              Needs the chunk's working set (3*chunk*D elements plus chunk-sized scratch)
  *              within the 160 KiB of LDS of one compute unit.

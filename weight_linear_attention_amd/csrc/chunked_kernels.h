@@ -43,6 +43,14 @@ struct ChunkTypes {
 };
 
 __device__ __forceinline__ f32x4 as_f32x4(uint4 v) { return __builtin_bit_cast(f32x4, v); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
+// global loads and stores in flight (those are ordered explicitly where needed).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint4 pack_bf16x8(const f32x4& lo, const f32x4& hi) {
@@ -607,6 +615,217 @@ __global__ __launch_bounds__(64 * DP, 1) void delta_chain_kernel(ChunkArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// chain, staged: the same recurrence with the operand fetch taken off the waves that run the
+// MFMAs.  One workgroup of 8 waves per (b, h, v-tile r): compute waves 0..3 and loader waves
+// 4..7 (loader 4 + w shares a SIMD with compute wave w and fetches its blocks).  Loaders copy the
+// next chunk's blocks straight into LDS with global_load_lds (lane i's 16 bytes land at the
+// block base + 16 i, the operand layout) into a two-slot ring.  Compute wave w:
+//   * owns row tile t = w of S = W_y W^T (GEMM1) over all of D, reading W^T from an LDS copy
+//     that every wave refreshes with its d-tiles at the top of the chunk;
+//   * forms U = U_y - S for its rows and publishes rho_k o U in LDS;
+//   * owns d-tiles dt0 = w NDP .. +NDP of the memory for the update W^T += K^T (rho_k o U).
+// Two barriers per chunk: B1 after the W^T copy is written (and, for the loaders, after the
+// slot they refill has been read), B2 after rho_k o U is written.  Each LDS buffer is written
+// only after the barrier that follows its last read, so the W^T copy and U need one buffer
+// each and the operand ring two slots.
+constexpr int kChainWaves = 4;
+
+template <bool BF16, int C, int NDP>
+struct StagedLayout {
+    static constexpr int pair = BF16 ? 2 : 1;
+    static constexpr int NT = C / 16, NTB = NT / pair;
+    static constexpr int ND = kChainWaves * NDP, NDB = ND / pair;
+    static constexpr int PW = NDB + NDP * NTB + 1;             // blocks per compute wave and slot
+    static constexpr int SLOT = (kChainWaves * PW + 1) * 1024;  // + rho_k (C floats)
+    static constexpr int XOFF = 2 * SLOT;                       // W^T copy: NDB blocks
+    static constexpr int UOFF = XOFF + NDB * 1024;              // rho_k o U: NT fp32 tiles
+    static constexpr int BYTES = UOFF + NT * 1024;
+};
+
+template <bool BF16, int C, int NDP>
+__global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a) {
+    using LT = typename ChunkTypes<BF16>::LT;
+    using SL = StagedLayout<BF16, C, NDP>;
+    constexpr int pair = SL::pair, NT = SL::NT, NTB = SL::NTB, ND = SL::ND, NDB = SL::NDB;
+    constexpr int NDPB = NDP / pair;
+    static_assert(NDP % pair == 0, "bf16 waves hold whole d-tile pairs");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= kChainWaves;
+    const int w = loader ? wave - kChainWaves : wave;    // the compute wave served or run
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_k = a.d_k, D = a.D, NC = a.NC, NVT = a.d_v / 16;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, NVT);
+    const int bh = bi.bh, r = static_cast<int>(bi.i);
+    const int dt0 = w * NDP;
+    const int vcol = 16 * r + l16;
+    const int64_t u0 = static_cast<int64_t>(bh) * NC;
+    const int64_t szCD = static_cast<int64_t>(C) * D * sizeof(LT);
+    char* X = smem + SL::XOFF;
+    char* Ub = smem + SL::UOFF;
+    auto lane16 = [&](char* base, int blk) { return base + blk * 1024 + l * 16; };
+
+    // ---- loader: chunk uu's blocks for compute wave w into ring slot `slot`
+    auto issue_loads = [&](int64_t uu, int slot) {
+        char* sw = smem + slot * SL::SLOT + w * SL::PW * 1024;
+        const char* wy = a.ws + a.o_wy + uu * szCD + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
+        const char* kt = a.ws + a.o_kt + uu * szCD + (static_cast<int64_t>(dt0) * NTB * 64 + l) * 16;
+        typedef __attribute__((address_space(1))) const void* gptr;
+        typedef __attribute__((address_space(3))) void* lptr;
+        if (w < NT) {
+#pragma unroll
+            for (int j = 0; j < NDB; ++j)
+                __builtin_amdgcn_global_load_lds((gptr)(wy + j * 1024), (lptr)(sw + j * 1024), 16, 0, 0);
+            const char* uy = a.ws + a.o_uy + uu * (static_cast<int64_t>(C) * a.d_v * 4) +
+                             ((static_cast<int64_t>(w) * NVT + r) * 64 + l) * 16;
+            __builtin_amdgcn_global_load_lds((gptr)uy, (lptr)(sw + (SL::PW - 1) * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < NDP * NTB; ++b)
+            __builtin_amdgcn_global_load_lds((gptr)(kt + b * 1024), (lptr)(sw + (NDB + b) * 1024), 16, 0, 0);
+        if (w == 0 && l < C) {
+            const float* rk = reinterpret_cast<const float*>(a.ws + a.o_rk) + uu * C + l;
+            __builtin_amdgcn_global_load_lds((gptr)rk, (lptr)(smem + slot * SL::SLOT + kChainWaves * SL::PW * 1024), 4, 0, 0);
+        }
+    };
+    constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
+
+    if (loader) {
+        // Loader loop: the same barrier sequence as the compute loop (one before it, B1 and B2 per
+        // chunk).  After B1(n) the slot of chunk n - 1 is free; chunk n + 1 goes there and is
+        // complete before this wave arrives at B1(n + 1).
+        // A loader publishes LDS only through its LDS-DMA loads, which it waits for explicitly
+        // (vmcnt) before B1; its barriers are bare so that B2 does not wait for the loads just
+        // issued.
+        auto bare_barrier = []() {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        if (NC > 0) {
+            issue_loads(u0, 0);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        }
+        bare_barrier();
+        for (int n = 0; n < NC; ++n) {
+            bare_barrier();                                          // B1
+            if (n + 1 < NC) issue_loads(u0 + n + 1, (n & 1) ^ 1);
+            bare_barrier();                                          // B2
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        }
+        return;
+    }
+
+    f32x4 Wst[NDP];
+#pragma unroll
+    for (int i = 0; i < NDP; ++i) {
+        Wst[i] = zero4();
+        if (a.W0) {
+            // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+            const float* src = a.W0 + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                               orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            const float2 lo = *reinterpret_cast<const float2*>(src);
+            const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
+            Wst[i] = f32x4{lo.x, hi.x, lo.y, hi.y};
+        }
+    }
+    lds_barrier();
+
+    const int64_t szWn = static_cast<int64_t>(D) * a.d_v * sizeof(LT);
+    const int64_t szUn = static_cast<int64_t>(C) * a.d_v * sizeof(LT);
+    for (int n = 0; n < NC; ++n) {
+        const int64_t uu = u0 + n;
+        const int slot = n & 1;
+        char* sw = smem + slot * SL::SLOT + w * SL::PW * 1024;
+        // chunk-start memory: the LDS copy for GEMM1 and the Wn blocks for the output kernel
+        char* wn = a.ws + a.o_wn + uu * szWn;
+#pragma unroll
+        for (int i = 0; i < NDPB; ++i) {
+            uint4 val;
+            if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
+            else val = __builtin_bit_cast(uint4, Wst[i]);
+            const int jb = dt0 / pair + i;
+            *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+            *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
+        }
+        lds_barrier();                                               // B1
+        if (w < NT) {
+            // S = W_y W^T for row tile w, two accumulators over alternating k-blocks
+            f32x4 s0 = zero4(), s1 = zero4();
+#pragma unroll
+            for (int j = 0; j < NDB; ++j) {
+                const uint4 av = *reinterpret_cast<const uint4*>(lane16(sw, j));
+                const uint4 bv = *reinterpret_cast<const uint4*>(lane16(X, j));
+                f32x4& acc = (j & 1) ? s1 : s0;
+                if constexpr (BF16) {
+                    acc = mfma_bf16_k32(as_bf16x8(av), as_bf16x8(bv), acc);
+                } else {
+                    const f32x4 af = as_f32x4(av), bf = as_f32x4(bv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
+                }
+            }
+            const f32x4 uyv = *reinterpret_cast<const f32x4*>(lane16(sw, SL::PW - 1));
+            const f32x4 U = uyv - (s0 + s1);
+            // U for the output kernel: B blocks (j, r); for bf16 tile w is half h = w & 1 of
+            // pair block w / 2 (slots 4 h .. 4 h + 3 of every lane)
+            char* un = a.ws + a.o_un + uu * szUn;
+            if constexpr (BF16) {
+                *reinterpret_cast<uint2*>(blk_ptr(un, static_cast<int64_t>(w >> 1) * NVT + r, l) + 8 * (w & 1)) =
+                    make_uint2(pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
+            } else {
+                *reinterpret_cast<f32x4*>(blk_ptr(un, static_cast<int64_t>(w) * NVT + r, l)) = U;
+            }
+            const float* rk = reinterpret_cast<const float*>(smem + slot * SL::SLOT + kChainWaves * SL::PW * 1024);
+            const f32x4 rkv = *reinterpret_cast<const f32x4*>(rk + 16 * w + 4 * g4);
+            *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rkv;
+        }
+        lds_barrier();                                               // B2
+        // W^T += K^T (rho_k o U) for this wave's d-tiles
+        f32x4 odd[NDP];
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) odd[i] = zero4();
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            if constexpr (BF16) {
+                const f32x4 u0v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j));
+                const f32x4 u1v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j + 1));
+                const uint4 bu = pack_bf16x8(u0v, u1v);
+#pragma unroll
+                for (int i = 0; i < NDP; ++i) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(lane16(sw, NDB + i * NTB + j));
+                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
+                    dst = mfma_bf16_k32(as_bf16x8(av), as_bf16x8(bu), dst);
+                }
+            } else {
+                const f32x4 uv = *reinterpret_cast<const f32x4*>(lane16(Ub, j));
+#pragma unroll
+                for (int i = 0; i < NDP; ++i) {
+                    const f32x4 af = as_f32x4(*reinterpret_cast<const uint4*>(lane16(sw, NDB + i * NTB + j)));
+                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst = mfma_f32_k4(af[e], uv[e], dst);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) Wst[i] += odd[i];
+    }
+
+    if (a.Wf) {
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) {
+            float* dst = a.Wf + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                         orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            *reinterpret_cast<float2*>(dst) = make_float2(Wst[i][0], Wst[i][2]);
+            *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[i][1], Wst[i][3]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // output: one wave per output tile (chunk u, row tile tt, v-tile vt), four tiles per workgroup:
 //   Y = rho_q o (Q W_n^T) + P~ U_n.
 template <bool BF16, int C>
@@ -692,6 +911,28 @@ hipError_t launch_chain_ndp(const ChunkArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Staged chain kernel: (d-tiles per compute wave) instantiated per dtype, and its LDS bytes
+// (0 when the shape has no staged instantiation).
+inline int staged_chain_lds(bool bf16, int C, int ndp) {
+    const int ok = bf16 ? (ndp == 2 || ndp == 4) : (ndp == 1 || ndp == 2);
+    if (!ok || (C != 32 && C != 64)) return 0;
+    const int pair = bf16 ? 2 : 1, NT = C / 16, NTB = NT / pair, ND = kChainWaves * ndp;
+    const int NDB = ND / pair, PW = NDB + ndp * NTB + 1;
+    return 2 * (kChainWaves * PW + 1) * 1024 + NDB * 1024 + NT * 1024;
+}
+
+template <bool BF16, int C, int NDP>
+hipError_t launch_chain_staged(const ChunkPlan& p, hipStream_t stream) {
+    auto kern = delta_chain_staged_kernel<BF16, C, NDP>;
+    static_assert(StagedLayout<BF16, C, NDP>::BYTES > 0, "layout");
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_chain);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / 16)));
+    hipLaunchKernelGGL(kern, grid, dim3(64 * 2 * kChainWaves), p.lds_chain, stream, p.args);
+    return hipGetLastError();
+}
+
 template <bool BF16, int C>
 hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     const ChunkArgs& a = p.args;
@@ -705,7 +946,12 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipError_t e;
-    if constexpr (BF16) e = a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream)
+    if (p.staged_ndp > 0) {
+        if constexpr (BF16) e = p.staged_ndp == 2 ? launch_chain_staged<BF16, C, 2>(p, stream)
+                                                  : launch_chain_staged<BF16, C, 4>(p, stream);
+        else e = p.staged_ndp == 1 ? launch_chain_staged<BF16, C, 1>(p, stream)
+                                   : launch_chain_staged<BF16, C, 2>(p, stream);
+    } else if constexpr (BF16) e = a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream)
                                        : (a.NDP == 4 ? launch_chain_ndp<BF16, C, 4>(a, stream) : hipErrorInvalidValue);
     else e = a.NDP == 1 ? launch_chain_ndp<BF16, C, 1>(a, stream)
                         : (a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream) : hipErrorInvalidValue);

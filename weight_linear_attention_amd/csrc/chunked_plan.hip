@@ -80,6 +80,18 @@ bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Chu
     plan->C = C;
     plan->lds_prep = off;
     plan->ws_bytes = a.o_un + NU * szUn;
+    // The staged chain kernel (loader waves, LDS operand ring) where its LDS fits: 4 compute
+    // waves, ND / 4 d-tiles each.
+    plan->staged_ndp = 0;
+    plan->lds_chain = 0;
+    if (ND % kChainWaves == 0) {
+        const int sndp = ND / kChainWaves;
+        const int lds = staged_chain_lds(bf16, C, sndp);
+        if (lds > 0 && lds <= kMaxLdsPrep) {
+            plan->staged_ndp = sndp;
+            plan->lds_chain = lds;
+        }
+    }
     return true;
 }
 

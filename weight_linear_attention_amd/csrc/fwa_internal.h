@@ -66,6 +66,8 @@ struct ChunkPlan {
     int C;
     int lds_prep;
     int64_t ws_bytes;
+    int staged_ndp;      // > 0: the staged chain kernel with this many d-tiles per compute wave
+    int lds_chain;       // its LDS bytes
 };
 
 bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, ChunkPlan* plan);

@@ -19,10 +19,10 @@
  *           walkthrough".  No 1/sqrt(d) scale and no z normaliser.
  *
  * Conventions for every entry point:
- *   - All tensor pointers are DEVICE pointers owned by the caller.  The library keeps no
- *     state between calls and never synchronises `stream`; every launch goes on `stream`
- *     (0 = the legacy default stream) and FWA_OK means "enqueued".  Only fwa_delta_forward
- *     may allocate: a stream-ordered workspace (see there).
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  Every launch goes on
+ *     `stream` (0 = the legacy default stream) and FWA_OK means "enqueued".  The only state
+ *     the library keeps between calls is the chunked forward's workspace (see
+ *     fwa_delta_forward) and which kernels already carry their LDS-size attribute.
  *   - Layouts are row-major and contiguous (the [B, H, T, d] convention of [TRF], section
  *     "Scaled dot-product attention").  The fast-weight memory W is [B, H, d_v, D] fp32
  *     (d_value x d_key orientation of [FWT], module walkthrough).
@@ -106,10 +106,13 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *     chunked  three launches: every chunk's memory-independent part in parallel, then the
  *              memory carried through the chunks, then the outputs.  It needs a workspace of
  *              B*H*ceil(T/chunk) * (3*chunk*D + chunk*chunk + D*d_v + chunk*d_v) elements of
- *              `dtype` plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values, taken with
- *              hipMallocAsync on `stream` and returned with hipFreeAsync on `stream` before
- *              the call returns (the device's default memory pool is set, once, to keep freed
- *              memory for reuse).  Chunks of
+ *              `dtype` plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values.  The library
+ *              keeps one workspace per (device, stream) for reuse by later calls on that
+ *              stream (they run in stream order, so reuse needs no synchronisation).  A call
+ *              that needs more than the stream's workspace holds synchronises `stream`, frees
+ *              it and allocates a larger one (hipMalloc); workspaces live until the process
+ *              ends.  A stream handle must not be destroyed and recreated while work that
+ *              used its workspace is still pending.  Chunks of
  *              32 or 64 rows; D in {32, 64, 96, 128, 192, 256}, and for bf16 also 384, 512;
  *              the prep kernel's working set (2*chunk*(D + 8) elements plus chunk-sized
  *              scratch) must fit the 160 KiB of LDS, which leaves out chunk 64 for fp32 D = 256

@@ -925,8 +925,7 @@ template <bool BF16, int C, int NDP>
 hipError_t launch_chain_staged(const ChunkPlan& p, hipStream_t stream) {
     auto kern = delta_chain_staged_kernel<BF16, C, NDP>;
     static_assert(StagedLayout<BF16, C, NDP>::BYTES > 0, "layout");
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_chain);
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_chain);
     if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / 16)));
     hipLaunchKernelGGL(kern, grid, dim3(64 * 2 * kChainWaves), p.lds_chain, stream, p.args);
@@ -939,8 +938,7 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
     if (NU > 0) {
         auto prep = delta_prep_kernel<BF16, C>;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_prep);
+        hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prep), p.lds_prep);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(256), p.lds_prep, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;

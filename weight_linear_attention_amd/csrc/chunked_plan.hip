@@ -3,9 +3,27 @@
 // (dtype, chunk) instantiation.
 #include "chunked_kernels.h"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace fwa {
 
 static int align16(int x) { return (x + 15) & ~15; }
+
+hipError_t ensure_lds_attr(const void* kernel, int bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> done;   // (kernel, device) -> bytes set
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    int& cur = done[{kernel, dev}];
+    if (cur >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) cur = bytes;
+    return e;
+}
 
 constexpr int kMaxLdsPrep = 160 * 1024;
 

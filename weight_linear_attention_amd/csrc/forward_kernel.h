@@ -420,8 +420,7 @@ inline int fwd_ndpm_bucket(int ndp, int C) {
 template <bool BF16, int C, int NDPM>
 hipError_t launch_fwd_t(const FwdPlan& p, int BH, hipStream_t stream) {
     auto kern = delta_forward_kernel<BF16, C, NDPM>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, p.lds_bytes);
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_bytes);
     if (e != hipSuccess) return e;
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(BH) * p.R)), block(256);
     hipLaunchKernelGGL(kern, grid, block, p.lds_bytes, stream, p.args);

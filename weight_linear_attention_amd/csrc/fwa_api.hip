@@ -9,7 +9,9 @@
 #include <cstdarg>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -82,27 +84,31 @@ ForwardPath forward_path() {
     return ForwardPath::kInvalid;
 }
 
-// Stream-ordered workspace from the device's default memory pool.  The pool keeps freed
-// memory for reuse (release threshold raised once per device), so repeated calls do not go
-// back to the driver.
-hipError_t workspace_alloc(char** ptr, int64_t bytes, hipStream_t stream) {
-    constexpr int kMaxDevices = 64;
-    static std::once_flag flags[kMaxDevices];
+// Workspace of the chunked forward: one buffer per (device, stream), reused by every call on
+// that stream (calls on one stream run in order, so reuse needs no synchronisation) and grown
+// when a call needs more: the stream is synchronised, the old buffer freed and a larger one
+// allocated.  Buffers are held until the process ends.
+hipError_t workspace_get(char** ptr, int64_t bytes, hipStream_t stream) {
+    static std::mutex mu;
+    static std::map<std::pair<int, uintptr_t>, std::pair<char*, int64_t>> cache;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) {
-        std::call_once(flags[dev], [dev]() {
-            hipMemPool_t pool;
-            if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
-                uint64_t threshold = UINT64_MAX;
-                (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
-            }
-        });
+    std::lock_guard<std::mutex> lock(mu);
+    auto& ent = cache[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    if (ent.second < bytes) {
+        if (ent.first) {
+            if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+            if ((e = hipFree(ent.first)) != hipSuccess) return e;
+            ent = {nullptr, 0};
+        }
+        void* p = nullptr;
+        if ((e = hipMalloc(&p, static_cast<size_t>(bytes))) != hipSuccess) return e;
+        ent = {static_cast<char*>(p), bytes};
     }
-    return hipMallocAsync(reinterpret_cast<void**>(ptr), static_cast<size_t>(bytes), stream);
+    *ptr = ent.first;
+    return hipSuccess;
 }
-
 }  // namespace
 
 extern "C" {
@@ -270,16 +276,14 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     if (c.chunked) {
         char* ws = nullptr;
         if (c.cplan.ws_bytes > 0) {
-            const hipError_t e = workspace_alloc(&ws, c.cplan.ws_bytes, stream);
+            const hipError_t e = workspace_get(&ws, c.cplan.ws_bytes, stream);
             if (e != hipSuccess)
                 return fail(FWA_ERR_HIP, "%s: workspace of %lld bytes: %s", fn,
                             (long long)c.cplan.ws_bytes, hipGetErrorString(e));
         }
-        const hipError_t le = fwa::launch_chunked(c.cplan, q, k, v, beta_logit, W0, y, W_final,
-                                                  ws, bf16, stream);
-        const hipError_t fe = ws ? hipFreeAsync(ws, stream) : hipSuccess;
-        if (le != hipSuccess) return hip_status(le, "fwa_delta_forward launch");
-        return hip_status(fe, "fwa_delta_forward workspace release");
+        return hip_status(fwa::launch_chunked(c.cplan, q, k, v, beta_logit, W0, y, W_final, ws,
+                                              bf16, stream),
+                          "fwa_delta_forward launch");
     }
     return hip_status(fwa::launch_delta_forward(c.fplan, q, k, v, beta_logit, W0, y, W_final,
                                                 static_cast<int>(BH), H, T, d_k, d_v, nu, chunk,

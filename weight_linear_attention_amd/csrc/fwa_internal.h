@@ -70,6 +70,10 @@ struct ChunkPlan {
     int lds_chain;       // its LDS bytes
 };
 
+// hipFuncSetAttribute(kernel, MaxDynamicSharedMemorySize, bytes) once per (kernel, device,
+// size): the attribute persists, so later launches skip the runtime call.
+hipError_t ensure_lds_attr(const void* kernel, int bytes);
+
 bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, ChunkPlan* plan);
 hipError_t launch_chunked(const ChunkPlan& plan, const void* q, const void* k, const void* v,
                           const void* bl, const float* W0, void* y, float* Wf, char* ws,

@@ -17,7 +17,9 @@ already resident in HBM when timing starts.  Other workloads (--workload):
 Prints ONE JSON line.  `roofline` describes the dominant call: the forward (one launch on the
 fused path, three on the chunked path) or, for the decode and DPFP workloads, that kernel.
 `achieved` is its algorithmic bytes or flops divided by its mean duration, measured with HIP
-events on the launch stream over the timed region; `traffic` is the HBM bytes per call that
+events on the launch stream over the timed region (forward workloads: an event pair around each
+call; decode and DPFP: one pair around the back-to-back calls, divided by their number);
+`traffic` is the HBM bytes per call that
 rocprofv3 counted on the same sources (profiles/traffic.json), or null.  `cpu_baseline` times
 the fp64 oracle on the host (rank 0 only).
 """
@@ -161,28 +163,35 @@ def main():
                                out=ystep)
                 marks[2].record()
         elif kind == "decode":
-            marks[0].record()
             fwa.delta_step(d["q"][i], d["k"][i], d["v"][i], d["beta_logit"][i], W, nu=w.nu,
                            out=ystep)
-            marks[1].record()
         else:
-            marks[0].record()
             fwa.dpfp(d["q"], w.nu, out=phi_q)
             fwa.dpfp(d["k"], w.nu, out=phi_k)
-            marks[1].record()
 
+    # The forward workloads bracket each call with events to split forward from decode step.
+    # The decode and DPFP workloads run back to back, as a serving loop would, with one event
+    # pair around the timed region: their mean launch duration is region time / calls, which
+    # includes the gaps between launches (events between launches would stall the queue).
+    per_call = kind in ("prefill", "prefill+decode")
     for i in range(warmup):
         one_step(i, [ev(), ev(), ev()])
     torch.cuda.synchronize()
-    marks = [[ev(), ev(), ev()] for _ in range(steps)]
+    marks = [[ev(), ev(), ev()] for _ in range(steps)] if per_call else None
+    region = (ev(), ev())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record()
     for i in range(steps):
-        one_step(warmup + i if kind == "decode" else i, marks[i])
+        one_step(warmup + i if kind == "decode" else i, marks[i] if per_call else None)
+    region[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    main_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    if per_call:
+        main_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    else:
+        main_ms = region[0].elapsed_time(region[1]) / steps
     step_ms = (sum(m[1].elapsed_time(m[2]) for m in marks) / steps
                if kind == "prefill+decode" else None)
 

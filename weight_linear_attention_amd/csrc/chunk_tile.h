@@ -19,34 +19,12 @@ namespace fwa {
 
 constexpr int kLiStride = 20;   // floats per row of the diagonal-inverse buffer
 
-// Roll constants of one lane for shifts 1..4: the ds_bpermute byte address of the source lane
-// and the sign mask.  For shift i the rolled operand of position j is relu([k,-k]) at
-// m = (j - i) mod 2 d_k, i.e. lane (m mod d_k) of the row's group, negated when m >= d_k.
-struct RollConst {
-    int src4[4];
-    uint32_t smask[4];
-};
-
-__device__ __forceinline__ RollConst roll_consts(int jl, int gbase, int d_k) {
-    RollConst rc;
-#pragma unroll
-    for (int i = 1; i <= 4; ++i) {
-        const int m = (jl - i) & (2 * d_k - 1);
-        rc.src4[i - 1] = (gbase + (m & (d_k - 1))) << 2;
-        rc.smask[i - 1] = (m & d_k) ? 0x80000000u : 0u;
-    }
-    return rc;
-}
-
-__device__ __forceinline__ float flip(float x, uint32_t mask) {
-    return __uint_as_float(__float_as_uint(x) ^ mask);
-}
-
 // K and Q tiles store their D columns in an internal order that puts the two halves of a
 // shift block next to each other: internal column 2 ((i-1) d_k + j) + h holds DPFP position
 // (i-1) 2 d_k + h d_k + j (h = 0: relu(k_j) * ..., h = 1: relu(-k_j) * ...).  Inner products
 // over D do not depend on the order; the memory W^T uses the same order internally and is
-// mapped back at load/store.  So a lane writes both halves of its position with one store.
+// mapped back at load/store.  The two halves of a position are adjacent, so a run of 8 positions
+// is 16 consecutive columns (two 16-byte stores for bf16).
 __device__ __forceinline__ int orig_col(int c, int d_k) {
     const int m = c >> 1;
     return (m / d_k) * 2 * d_k + (c & 1) * d_k + (m % d_k);
@@ -54,97 +32,174 @@ __device__ __forceinline__ int orig_col(int c, int d_k) {
 
 __device__ __forceinline__ float relu_f(float x) { return fmaxf(x, 0.0f); }
 
-template <typename LT>
-__device__ __forceinline__ void store_pair(LT* p, float lo, float hi) {
-    if constexpr (sizeof(LT) == 2) *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(lo, hi);
-    else *reinterpret_cast<float2*>(p) = make_float2(lo, hi);
+// x from another lane of the same 16-lane row, selected by a DPP control (compile-time).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Raw DPFP products of R rows for NU shifts (lane jl of a DK-lane group holds k_jl and q_jl
-// of its row), written as (h = 0, h = 1) pairs to the row-major K and Q tiles.  All loads and
-// permutes of the R rows are issued before the first LDS write.
-template <typename LT, int NU, int R>
-__device__ __forceinline__ void dpfp_rows(const float (&kv)[R], const float (&qv)[R],
-                                          const RollConst& rc, int d_k, LT* const (&krow)[R],
-                                          LT* const (&qrow)[R]) {
-    float xk[R][NU], xq[R][NU];
+// Eight consecutive staged inputs (bf16 or fp32) as fp32.  `p` is 16-byte aligned.
+__device__ __forceinline__ void load8_f32(const u16* p, float (&v)[8]) {
+    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            xk[r][i] = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(rc.src4[i], __float_as_int(kv[r]))),
-                            rc.smask[i]);
-            xq[r][i] = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(rc.src4[i], __float_as_int(qv[r]))),
-                            rc.smask[i]);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const float ka = relu_f(kv[r]), kb = relu_f(-kv[r]), qa = relu_f(qv[r]), qb = relu_f(-qv[r]);
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            // ka, kb >= 0, so ka * relu(x) = relu(ka * x) and kb * relu(-x) = relu(-(kb * x))
-            store_pair(krow[r] + 2 * i * d_k, relu_f(ka * xk[r][i]), relu_f(-(kb * xk[r][i])));
-            store_pair(qrow[r] + 2 * i * d_k, relu_f(qa * xq[r][i]), relu_f(-(qb * xq[r][i])));
-        }
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
 }
+__device__ __forceinline__ void load8_f32(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
-// Any nu (slow path, one row): the permute address and sign are computed per shift.
-template <typename LT>
-__device__ __forceinline__ void dpfp_row_any(float kv, float qv, int nu, int jl, int gbase,
-                                             int d_k, LT* krow, LT* qrow) {
-    const int two_dk = 2 * d_k;
-    const float ka = relu_f(kv), kb = relu_f(-kv), qa = relu_f(qv), qb = relu_f(-qv);
+// Sixteen consecutive tile columns from fp32 values (16-byte stores; `p` 32-byte aligned).
+__device__ __forceinline__ void store16(u16* p, const float (&f)[16]) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+    q[0] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    q[1] = make_uint4(pack_bf16x2(f[8], f[9]), pack_bf16x2(f[10], f[11]),
+                      pack_bf16x2(f[12], f[13]), pack_bf16x2(f[14], f[15]));
+}
+__device__ __forceinline__ void store16(float* p, const float (&f)[16]) {
+    float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = make_float4(f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]);
+}
+
+// One DPFP task: the 8 positions j0 .. j0+7 of one staged row (a = k[j0 .. j0+7]) for every
+// shift, written as 16 consecutive internal columns per shift.  The rolled operand of position
+// j for shift i is relu([k,-k]) at (j - i) mod 2 d_k, which is +-k[(j - i) mod d_k], negated
+// when j < i (the index wraps into the [-k] half).  pv = k over the 8 positions before j0
+// (cyclically), so window index 8 + e - i (mod 16) of [pv, a] is k[(j0 + e - i) mod d_k] for
+// every shift D <= 512 allows (d_k = 16: the window is the whole row, so the index is cyclic).
+// With ka = relu(k_j), kb = relu(-k_j) >= 0: ka relu(x) = relu(ka x), kb relu(-x) = relu(-(kb x)).
+template <typename LT, int NU>
+__device__ __forceinline__ float dpfp_task(const float (&a)[8], const float (&pv)[8], int j0,
+                                           int d_k, LT* out) {
+    float ka[8], kb[8], sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        ka[e] = relu_f(a[e]);
+        kb[e] = relu_f(-a[e]);
+    }
+#pragma unroll
+    for (int i = 1; i <= NU; ++i) {
+        float f[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            constexpr int kW = 16;
+            const int m = (8 + e - i + 4 * kW) % kW;         // compile-time window index
+            const float r = m >= 8 ? a[m - 8] : pv[m];
+            const float x = (j0 + e < i) ? -r : r;
+            f[2 * e] = relu_f(ka[e] * x);
+            f[2 * e + 1] = relu_f(-(kb[e] * x));
+            sum += f[2 * e] + f[2 * e + 1];
+        }
+        store16(out + 2 * ((i - 1) * d_k + j0), f);
+    }
+    return sum;
+}
+
+// Any nu (runtime shift count): the rolled operands are read from the staged row per shift.
+template <typename LT, typename IT>
+__device__ __forceinline__ float dpfp_task_any(const float (&a)[8], const IT* row, int j0,
+                                               int d_k, int nu, LT* out) {
+    float sum = 0.0f;
     for (int i = 1; i <= nu; ++i) {
-        const int m = (jl - i) & (two_dk - 1);
-        const int src4 = (gbase + (m & (d_k - 1))) << 2;
-        const uint32_t sm = (m & d_k) ? 0x80000000u : 0u;
-        const float xk = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(kv))), sm);
-        const float xq = flip(__int_as_float(__builtin_amdgcn_ds_bpermute(src4, __float_as_int(qv))), sm);
-        store_pair(krow + 2 * (i - 1) * d_k, relu_f(ka * xk), relu_f(-(kb * xk)));
-        store_pair(qrow + 2 * (i - 1) * d_k, relu_f(qa * xq), relu_f(-(qb * xq)));
+        float f[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = to_f32(row[(j0 + e - i + 2 * d_k) & (d_k - 1)]);
+            const float x = (j0 + e < i) ? -r : r;
+            f[2 * e] = relu_f(relu_f(a[e]) * x);
+            f[2 * e + 1] = relu_f(-(relu_f(-a[e]) * x));
+            sum += f[2 * e] + f[2 * e + 1];
+        }
+        store16(out + 2 * ((i - 1) * d_k + j0), f);
     }
+    return sum;
 }
 
 // DPFP of the C staged raw rows Xk, Xq ([C][d_k], input storage type) into the tiles Kr, Qr
-// ([C][krs], internal column order).  One row per d_k-lane group and pass, two passes per
-// iteration; the shift count is a compile-time constant on the fast path (nu <= 4).
+// ([C][krs], internal column order).  A task is (tile, row, group of 8 positions); the 256
+// threads take 2 C d_k / 8 tasks, two per pass with both tasks' loads issued first.  Each
+// task reads its row through two 16-byte LDS loads and writes 16-byte LDS stores; no lane
+// exchanges.  The shift count is a compile-time constant for nu <= 4.
+// With rhok / rhoq given, the row normalisers rho = 1 / (row sum + eps) are formed as well: a
+// row's d_k / 8 tasks sit in adjacent lanes of one pass, so their fp32 sums reduce by lane
+// shuffles and the row's first task writes rho[t].
 template <typename LT, typename IT, int C>
 __device__ __forceinline__ void dpfp_chunk(const IT* Xk, const IT* Xq, LT* Kr, LT* Qr, int krs,
-                                           int d_k, int nu, int w, int l) {
-    const int rpw = 64 / d_k;                 // rows per wave pass
-    const int jl = l % d_k, grp = l / d_k;
-    const int gbase = grp * d_k;
-    const int npass = C / (4 * rpw);
-    auto passes = [&](auto nu_tag) {
-        constexpr int NU = decltype(nu_tag)::value;
-        const RollConst rc = roll_consts(jl, gbase, d_k);
-        for (int p = 0; p < npass; p += 2) {
-            const bool two = p + 1 < npass;
-            const int t0r = p * 4 * rpw + w * rpw + grp;
-            const int t1r = two ? t0r + 4 * rpw : t0r;
-            const float kv[2] = {to_f32(Xk[t0r * d_k + jl]), to_f32(Xk[t1r * d_k + jl])};
-            const float qv[2] = {to_f32(Xq[t0r * d_k + jl]), to_f32(Xq[t1r * d_k + jl])};
-            LT* const krow[2] = {Kr + t0r * krs + 2 * jl, Kr + t1r * krs + 2 * jl};
-            LT* const qrow[2] = {Qr + t0r * krs + 2 * jl, Qr + t1r * krs + 2 * jl};
-            dpfp_rows<LT, NU, 2>(kv, qv, rc, d_k, krow, qrow);
-        }
+                                           int d_k, int nu, int w, int l,
+                                           float* rhok = nullptr, float* rhoq = nullptr) {
+    const int tid = 64 * w + l;
+    const int lg = __builtin_ctz(d_k >> 3);           // log2(groups per row)
+    const int gm = (d_k >> 3) - 1;
+    const int ntask = 2 * C * (d_k >> 3);
+    auto locate = [&](int tau, const IT*& row, LT*& out, int& j0, int& jp) {
+        const int jg = tau & gm;
+        const int rt = tau >> lg;                      // 0 .. 2C-1: K rows, then Q rows
+        const bool isq = rt >= C;
+        const int t = isq ? rt - C : rt;
+        row = (isq ? Xq : Xk) + t * d_k;
+        out = (isq ? Qr : Kr) + t * krs;
+        j0 = 8 * jg;
+        jp = 8 * ((jg + gm) & gm);
     };
-    auto passes_any = [&]() {
-        for (int p = 0; p < npass; ++p) {
-            const int t = p * 4 * rpw + w * rpw + grp;
-            const float kv = to_f32(Xk[t * d_k + jl]), qv = to_f32(Xq[t * d_k + jl]);
-            dpfp_row_any<LT>(kv, qv, nu, jl, gbase, d_k, Kr + t * krs + 2 * jl,
-                             Qr + t * krs + 2 * jl);
+    auto run = [&](auto nu_tag) {
+        constexpr int NU = decltype(nu_tag)::value;
+        for (int tau = tid; tau < ntask; tau += 512) {
+            // two tasks per pass (the second clamps to the first when past the end: it then
+            // rewrites identical values)
+            const int tau2 = tau + 256 < ntask ? tau + 256 : tau;
+            const IT *r1, *r2;
+            LT *o1, *o2;
+            int j1, p1, j2, p2;
+            locate(tau, r1, o1, j1, p1);
+            locate(tau2, r2, o2, j2, p2);
+            float a1[8], v1[8], a2[8], v2[8];
+            load8_f32(r1 + j1, a1);
+            load8_f32(r2 + j2, a2);
+            float s1, s2;
+            if constexpr (NU > 0) {
+                load8_f32(r1 + p1, v1);
+                load8_f32(r2 + p2, v2);
+                s1 = dpfp_task<LT, NU>(a1, v1, j1, d_k, o1);
+                s2 = dpfp_task<LT, NU>(a2, v2, j2, d_k, o2);
+            } else {
+                s1 = dpfp_task_any<LT, IT>(a1, r1, j1, d_k, nu, o1);
+                s2 = dpfp_task_any<LT, IT>(a2, r2, j2, d_k, nu, o2);
+            }
+            if (rhok != nullptr) {
+                // sums over aligned groups of 2, 4 or 8 lanes by DPP (no LDS traffic, so no
+                // wait on the task stores): lane ^ 1, lane ^ 2, then the mirror inside 8 lanes
+                s1 += dpp_f32<0xB1>(s1);
+                s2 += dpp_f32<0xB1>(s2);
+                if (gm >= 3) {
+                    s1 += dpp_f32<0x4E>(s1);
+                    s2 += dpp_f32<0x4E>(s2);
+                }
+                if (gm >= 7) {
+                    s1 += dpp_f32<0x141>(s1);
+                    s2 += dpp_f32<0x141>(s2);
+                }
+                if ((tau & gm) == 0) {
+                    const int rt1 = tau >> lg, rt2 = tau2 >> lg;
+                    (rt1 >= C ? rhoq + (rt1 - C) : rhok + rt1)[0] = __builtin_amdgcn_rcpf(s1 + kDpfpEps);
+                    (rt2 >= C ? rhoq + (rt2 - C) : rhok + rt2)[0] = __builtin_amdgcn_rcpf(s2 + kDpfpEps);
+                }
+            }
         }
     };
     switch (nu) {
-        case 1: passes(std::integral_constant<int, 1>{}); break;
-        case 2: passes(std::integral_constant<int, 2>{}); break;
-        case 3: passes(std::integral_constant<int, 3>{}); break;
-        case 4: passes(std::integral_constant<int, 4>{}); break;
-        default: passes_any(); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        default: run(std::integral_constant<int, 0>{}); break;
     }
 }
 
@@ -164,7 +219,7 @@ struct GPTiles {
 
 // One unit: tile rows RA = Q and RB = NT-1-Q of X (K or Q) against the K rows, with the row
 // sums of the two rows.  The rows are compile-time constants, so every tile condition folds away.
-template <bool BF16, int C, int Q>
+template <bool BF16, int C, int Q, bool ROWSUMS>
 __device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16], f32x4& sa,
                                         f32x4& sb, const void* Xv, const void* Kv, int krs,
                                         int D, int l16, int g4) {
@@ -187,8 +242,10 @@ __device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16
             bf16x8 kv8[RB + 1];
 #pragma unroll
             for (int tb = 0; tb <= RB; ++tb) kv8[tb] = *reinterpret_cast<const bf16x8*>(Kb + 16 * tb * krs + c0);
-            sa = mfma_bf16_k32(va, ones, sa);
-            if (RB != RA) sb = mfma_bf16_k32(vb, ones, sb);
+            if constexpr (ROWSUMS) {
+                sa = mfma_bf16_k32(va, ones, sa);
+                if (RB != RA) sb = mfma_bf16_k32(vb, ones, sb);
+            }
 #pragma unroll
             for (int tb = 0; tb <= RB; ++tb) {
                 if (tb <= RA) ta[tb] = mfma_bf16_k32(va, kv8[tb], ta[tb]);
@@ -207,8 +264,10 @@ __device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16
             // consecutive MFMAs write different accumulators
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sa = mfma_f32_k4(va[e], 1.0f, sa);
-                if (RB != RA) sb = mfma_f32_k4(vb[e], 1.0f, sb);
+                if constexpr (ROWSUMS) {
+                    sa = mfma_f32_k4(va[e], 1.0f, sa);
+                    if (RB != RA) sb = mfma_f32_k4(vb[e], 1.0f, sb);
+                }
 #pragma unroll
                 for (int tb = 0; tb <= RB; ++tb) {
                     if (tb <= RA) ta[tb] = mfma_f32_k4(va[e], k4[tb][e], ta[tb]);
@@ -219,7 +278,9 @@ __device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16
     }
 }
 
-template <bool BF16, int C>
+// ROWSUMS: the row sums (sa, sb) as the operands times a ones matrix; without it the caller
+// has formed the normalisers elsewhere (dpfp_chunk with rho outputs).
+template <bool BF16, int C, bool ROWSUMS = true>
 __device__ __forceinline__ void gp_compute(GPTiles<C>& gp, const void* Kv, const void* Qv,
                                            int krs, int D, int w, int l16, int g4) {
     using GP = GPTiles<C>;
@@ -239,10 +300,10 @@ __device__ __forceinline__ void gp_compute(GPTiles<C>& gp, const void* Kv, const
             const void* X = isP ? Qv : Kv;
             // q is uniform over the wave: one branch selects the unit's instantiation
             switch (q) {
-                case 0: gp_unit<BF16, C, 0>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
-                case 1: if constexpr (NQ > 1) gp_unit<BF16, C, (NQ > 1 ? 1 : 0)>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
-                case 2: if constexpr (NQ > 2) gp_unit<BF16, C, (NQ > 2 ? 2 : 0)>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
-                case 3: if constexpr (NQ > 3) gp_unit<BF16, C, (NQ > 3 ? 3 : 0)>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 0: gp_unit<BF16, C, 0, ROWSUMS>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 1: if constexpr (NQ > 1) gp_unit<BF16, C, (NQ > 1 ? 1 : 0), ROWSUMS>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 2: if constexpr (NQ > 2) gp_unit<BF16, C, (NQ > 2 ? 2 : 0), ROWSUMS>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
+                case 3: if constexpr (NQ > 3) gp_unit<BF16, C, (NQ > 3 ? 3 : 0), ROWSUMS>(gp.a[ui], gp.b[ui], gp.sa[ui], gp.sb[ui], X, Kv, krs, D, l16, g4); break;
                 default: break;
             }
         }

@@ -146,14 +146,13 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     }
     __syncthreads();
 
-    dpfp_chunk<LT, LT, C>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l);
+    dpfp_chunk<LT, LT, C>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l, rhok, rhoq);
     __syncthreads();
 
     {
         GPTiles<C> gp;
-        gp_compute<BF16, C>(gp, Kr, Qr, krs, D, w, l16, g4);
-        gp_write_rho<C>(gp, rhok, rhoq, w, l16, g4);
-        __syncthreads();   // rho complete; the staging rows are dead (L and P~ go over them)
+        gp_compute<BF16, C, false>(gp, Kr, Qr, krs, D, w, l16, g4);
+        __syncthreads();   // the staging rows are dead (L and P~ go over them)
         gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
     }
     __syncthreads();

@@ -44,13 +44,6 @@ struct ChunkTypes {
 
 __device__ __forceinline__ f32x4 as_f32x4(uint4 v) { return __builtin_bit_cast(f32x4, v); }
 
-// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
-// global loads and stores in flight (those are ordered explicitly where needed).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint4 pack_bf16x8(const f32x4& lo, const f32x4& hi) {
@@ -144,18 +137,18 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
             betas[tid] = tid < Cc ? sigmoid_stable(to_f32(static_cast<const LT*>(a.bl)[row0 + tid]))
                                   : 0.0f;
     }
-    __syncthreads();
+    lds_barrier();
 
     dpfp_chunk<LT, LT, C>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l, rhok, rhoq);
-    __syncthreads();
+    lds_barrier();
 
     {
         GPTiles<C> gp;
         gp_compute<BF16, C, false>(gp, Kr, Qr, krs, D, w, l16, g4);
-        __syncthreads();   // the staging rows are dead (L and P~ go over them)
+        lds_barrier();   // the staging rows are dead (L and P~ go over them)
         gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- diagonal-block inverses; write-out of the Q, K^T and P~ blocks and the normalisers
     if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
@@ -224,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
             reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
         }
     }
-    __syncthreads();   // Li complete; Q is dead (its space holds A')
+    lds_barrier();   // Li complete; Q is dead (its space holds A')
 
     // ---- A = (I + L)^-1 by block columns (column block tb = w per wave), stored twice with
     //      its columns scaled: A' = A diag(beta rho_k) and A'' = A diag(beta), each as fp32 or
@@ -286,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- U_y = A'' V as accumulator tiles (t-tile, v-tile), one v-tile per wave and pass
     char* uy = ws + a.o_uy + u * (static_cast<int64_t>(C) * d_v * 4);
@@ -544,7 +537,7 @@ __global__ __launch_bounds__(64 * DP, 1) void delta_chain_kernel(ChunkArgs a) {
         if constexpr (DP > 1) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) Red[((buf * DP + w) * NT + tt) * 64 + l] = S[tt];
-            __syncthreads();
+            lds_barrier();
             f32x4 part[DP][NT];
 #pragma unroll
             for (int pp = 0; pp < DP; ++pp)

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void dpfp_kernel(const void* __restrict__ x,
         *reinterpret_cast<float4*>(xe + DK + 4 * lt) = neg;
         *reinterpret_cast<float4*>(xe + two_dk + 4 * lt) = pos;
         *reinterpret_cast<float4*>(xe + two_dk + DK + 4 * lt) = neg;
-        __syncthreads();
+        lds_barrier();
 
         // Output group g = lt + TL*m covers positions p0 = E*g .. E*g + E-1, all inside the
         // block of shift i = p0 / (2*d_k) + 1 (E divides 2*d_k).
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void dpfp_kernel(const void* __restrict__ x,
                 }
             }
         }
-        __syncthreads();  // xe is rewritten by the next round
+        lds_barrier();  // xe is rewritten by the next round
       }
     }
 }

@@ -123,6 +123,9 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
     const int vupr = a.NVT * 16 * static_cast<int>(sizeof(IT)) / 16;
     const int nvunits = C * vupr;
     const int nvr = (nvunits + 255) / 256;
+    // bytes per row and units per v row are powers of two: row indices by shifts
+    const int ush = __builtin_ctz(ubytes) - 4;       // unit u of a k/q block is in row u >> ush
+    const int vsh = __builtin_ctz(vupr);             // unit u of the v block: row u >> vsh
     auto prefetch = [&](int chn) {
         const int tn0 = chn * C;
         const int Cn = min(C, T - tn0);
@@ -132,17 +135,17 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
         for (int i = 0; i < NRM; ++i) {
             if (i < nr) {
                 const int u = tid + 256 * i;
-                const bool ok = u < nunits && (u * 16) / ubytes < Cn;
+                const bool ok = u < nunits && (u >> ush) < Cn;
                 const int off = ok ? u * 16 : 0;
                 kraw[i] = *reinterpret_cast<const uint4*>(kc + off);
                 qraw[i] = *reinterpret_cast<const uint4*>(qc + off);
             }
             if (i < nvr) {
                 const int u = tid + 256 * i;
-                const int row = u / vupr;
+                const int row = u >> vsh;
                 const bool ok = u < nvunits && row < Cn;
                 const IT* src = vB + static_cast<int64_t>(tn0 + (ok ? row : 0)) * d_v + vbw +
-                                (ok ? (u % vupr) : 0) * (16 / static_cast<int>(sizeof(IT)));
+                                (ok ? (u & (vupr - 1)) : 0) * (16 / static_cast<int>(sizeof(IT)));
                 vraw[i] = *reinterpret_cast<const uint4*>(src);
             }
         }
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             if (i < nr) {
                 const int u = tid + 256 * i;
                 if (u < nunits) {
-                    const uint32_t m = (u * 16) / ubytes < Cc ? 0xffffffffu : 0u;
+                    const uint32_t m = (u >> ush) < Cc ? 0xffffffffu : 0u;
                     const uint4 kr4 = kraw[i], qr4 = qraw[i];
                     *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Xk) + u * 16) =
                         make_uint4(kr4.x & m, kr4.y & m, kr4.z & m, kr4.w & m);
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             if (i < nvr) {
                 const int u = tid + 256 * i;
                 if (u < nvunits) {
-                    const uint32_t m = u / vupr < Cc ? 0xffffffffu : 0u;
+                    const uint32_t m = (u >> vsh) < Cc ? 0xffffffffu : 0u;
                     const uint4 v4 = vraw[i];
                     *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Xv) + u * 16) =
                         make_uint4(v4.x & m, v4.y & m, v4.z & m, v4.w & m);
@@ -180,10 +183,10 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             }
         }
         if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(to_f32(blpre)) : 0.0f;
-        __syncthreads();
+        lds_barrier();
 
         dpfp_chunk<LT, ITs, C>(Xk, Xq, Kr, Qr, a.krs, d_k, nu, w, l);
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- B: G, P tiles; K W^T and Q W^T against the memory
         GPTiles<C> gp;
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
             }
         }
         gp_write_rho<C>(gp, rhok, rhoq, w, l16, g4);
-        __syncthreads();  // Q is dead from here; its space is reused
+        lds_barrier();  // Q is dead from here; its space is reused
 
         // ---------------- B': scaled G and P to LDS, state partials to the reduction buffer
         gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 *reinterpret_cast<f32x4*>(Red + ((w * 2 + 1) * 16 + l16) * RS + 16 * tt + 4 * g4) = QW[tt];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- C: diagonal-block inverses; reduce the state partials
         // (the next chunk's inputs are requested here: their registers are not live in B)
@@ -265,11 +268,16 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 if (a.DP > 1) {
+                    // all (up to 4) partials are read at once; a partial index past DP re-reads
+                    // the last wave's and is dropped by the select
                     f32x4 s1 = zero4(), qw = zero4();
-                    for (int pp = 0; pp < a.DP; ++pp) {
-                        const int ww = vt + a.NVT * pp;
-                        s1 += *reinterpret_cast<const f32x4*>(Red + ((ww * 2 + 0) * 16 + l16) * RS + 16 * tt + 4 * g4);
-                        qw += *reinterpret_cast<const f32x4*>(Red + ((ww * 2 + 1) * 16 + l16) * RS + 16 * tt + 4 * g4);
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) {
+                        const int ww = min(vt + a.NVT * pp, a.NVT * a.DP - 1);
+                        const f32x4 ps = *reinterpret_cast<const f32x4*>(Red + ((ww * 2 + 0) * 16 + l16) * RS + 16 * tt + 4 * g4);
+                        const f32x4 pq = *reinterpret_cast<const f32x4*>(Red + ((ww * 2 + 1) * 16 + l16) * RS + 16 * tt + 4 * g4);
+                        s1 += pp < a.DP ? ps : zero4();
+                        qw += pp < a.DP ? pq : zero4();
                     }
                     S1[tt] = s1;
                     QW[tt] = qw;
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- D: U by block substitution, Y, and the memory update
         if (has_state) {
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void delta_forward_kernel(FwdArgs a) {
                 }
             }
         }
-        __syncthreads();  // every LDS buffer is rewritten by the next chunk
+        lds_barrier();  // every LDS buffer is rewritten by the next chunk
     }
 
     if (has_state && a.Wf) {

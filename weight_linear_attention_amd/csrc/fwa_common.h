@@ -86,4 +86,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr_b16x4(const void* p) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
+// global loads and stores in flight.  The kernels here share data inside a workgroup through
+// LDS alone, so a barrier never has to drain prefetched loads or the stores of results that
+// only later kernels read.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace fwa

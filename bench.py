@@ -52,6 +52,7 @@ def parse():
 # Kernel sources behind each measured unit (their hash keys the committed counter data).
 SOURCES = {
     "chunked": ("chunked_kernels.h", "chunk_tile.h"),
+    "stream": ("stream_kernel.h", "stream_bf16_c64.hip", "chunked_kernels.h", "chunk_tile.h"),
     "fused": ("forward_kernel.h", "chunk_tile.h"),
     "decode": ("step_kernel.hip",),
     "dpfp": ("dpfp_kernel.hip",),
@@ -221,9 +222,11 @@ def main():
             ach = nbytes / (main_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": ach / PEAK_HBM_GBPS}
-        kname = ("fwa_delta_forward, chunked: delta_prep_kernel + delta_chain_kernel + "
-                 "delta_output_kernel" if unit == "chunked" else
-                 "fwa_delta_forward, fused: delta_forward_kernel")
+        kname = {"chunked": "fwa_delta_forward, chunked: delta_prep_kernel + delta_chain_kernel + "
+                            "delta_output_kernel",
+                 "stream": "fwa_delta_forward, stream: delta_prep_kernel (compact) + "
+                           "delta_stream_kernel",
+                 "fused": "fwa_delta_forward, fused: delta_forward_kernel"}[unit]
         roof.update(kernel=kname, algorithmic_flops=flops, algorithmic_bytes=nbytes,
                     mean_launch_ms=main_ms)
     else:

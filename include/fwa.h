@@ -68,7 +68,8 @@ typedef enum {
 typedef enum {
     FWA_PATH_NONE = 0,      /* nothing to launch (B*H == 0) */
     FWA_PATH_CHUNKED = 1,
-    FWA_PATH_FUSED = 2
+    FWA_PATH_FUSED = 2,
+    FWA_PATH_STREAM = 3
 } fwa_forward_path;
 
 /*
@@ -102,7 +103,7 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *               the stated tolerances.
  *   T == 0 leaves y untouched and writes W_final = W0 (or zeros).  B*H == 0 is a no-op.
  *   T need not be a multiple of chunk.
- *   Two implementations compute the same result (within the tolerances above):
+ *   Three implementations compute the same result (within the tolerances above):
  *     chunked  three launches: every chunk's memory-independent part in parallel, then the
  *              memory carried through the chunks, then the outputs.  It needs a workspace of
  *              B*H*ceil(T/chunk) * (3*chunk*D + chunk*chunk + D*d_v + chunk*d_v) elements of
@@ -117,13 +118,20 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *              the prep kernel's working set (2*chunk*(D + 8) elements plus chunk-sized
  *              scratch) must fit the 160 KiB of LDS, which leaves out chunk 64 for fp32 D = 256
  *              and bf16 D = 512.
+ *     stream   bf16 only, two launches: every chunk's (I + L)^-1 diag(beta), P~ and DPFP
+ *              normalisers in parallel, then one serial pass per (b, h, 32 columns of d_v)
+ *              that rebuilds the DPFP features from the raw rows and keeps the memory on chip.
+ *              Workspace of B*H*ceil(T/chunk) * (3*chunk*chunk*2 + 2*chunk*4) bytes (24.5 KiB
+ *              per chunk of 64), kept per (device, stream) as above.  Chunk 64; d_v in {32,
+ *              64}; D in {128, 256, 384} (the prep kernel's working set bounds D); nu <= 8.
  *     fused    one launch that keeps the chunk and the memory on chip; allocates nothing.
  *              Needs the chunk's working set (3*chunk*D elements plus chunk-sized scratch)
  *              within the 160 KiB of LDS of one compute unit.
- *   The environment variable FWA_FORWARD_PATH = chunked | fused | auto (default) selects one;
- *   auto takes the chunked path where it applies and its workspace is at most 2 GiB, else
- *   the fused one.  A forced path that does not apply gives FWA_ERR_UNSUPPORTED, an unknown
- *   value FWA_ERR_INVALID_ARG, a failed workspace allocation FWA_ERR_HIP.
+ *   The environment variable FWA_FORWARD_PATH = chunked | stream | fused | auto (default)
+ *   selects one; auto takes the chunked path where it applies and its workspace is at most
+ *   2 GiB, else the streaming one where it applies, else the fused one.  A forced path that
+ *   does not apply gives FWA_ERR_UNSUPPORTED, an unknown value FWA_ERR_INVALID_ARG, a failed
+ *   workspace allocation FWA_ERR_HIP.
  *   Implemented shapes: d_k in {16, 32, 64}, d_v in {16, 32, 64}, D = 2*d_k*nu <= 512, and
  *   the conditions of at least one implementation above; other valid shapes give
  *   FWA_ERR_UNSUPPORTED.
@@ -138,7 +146,8 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
  * (under the current FWA_FORWARD_PATH) and the workspace it would allocate, without
  * launching or allocating anything.
  *   path             out (may be NULL): an fwa_forward_path value
- *   workspace_bytes  out (may be NULL): bytes of the stream-ordered workspace, 0 for fused
+ *   workspace_bytes  out (may be NULL): bytes of the stream-ordered workspace (chunked and
+ *                    stream paths), 0 for fused
  *   Size errors are those fwa_delta_forward gives for the same sizes.
  */
 fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,

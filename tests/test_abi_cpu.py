@@ -144,10 +144,17 @@ def _workspace_formula(B, H, T, d_k, d_v, nu, chunk, es):
     return B * H * nc * per_chunk * es + B * H * nc * chunk * (d_v + 2) * 4
 
 
+def _stream_workspace_formula(B, H, T, chunk):
+    """The streaming path's workspace as fwa.h states it."""
+    nc = -(-T // chunk)
+    return B * H * nc * (3 * chunk * chunk * 2 + 2 * chunk * 4)
+
+
 @pytest.mark.parametrize("shape,dtype,path", [
     ((1, 8, 1024, 64, 64, 1, 64), "f32", "chunked"),      # 8 heads x 1024, D 128
     ((4, 8, 4096, 64, 64, 2, 64), "bf16", "chunked"),     # 32 heads x 4096, D 256
-    ((8, 16, 16384, 64, 64, 3, 64), "bf16", "fused"),     # 128 heads x 16384: 7.6 GB workspace
+    ((8, 16, 16384, 64, 64, 3, 64), "bf16", "stream"),    # 128 heads x 16384: 7.6 GB chunked workspace
+    ((8, 16, 16384, 64, 16, 3, 64), "bf16", "fused"),     # d_v 16: no streaming plan
     ((8, 16, 16384, 64, 64, 3, 128), "bf16", "none"),     # neither fits (LDS): unsupported
     ((1, 1, 64, 16, 16, 1, 16), "f32", "fused"),          # chunk 16: fused only
     ((1, 1, 77, 16, 16, 1, 32), "f32", "chunked"),
@@ -171,6 +178,8 @@ def test_forward_info_auto_choice(shape, dtype, path, monkeypatch):
     assert got == path
     if path == "chunked":
         assert ws == _workspace_formula(B, H, T, d_k, d_v, nu, chunk, 2 if dtype == "bf16" else 4)
+    elif path == "stream":
+        assert ws == _stream_workspace_formula(B, H, T, chunk)
     else:
         assert ws == 0
 
@@ -187,6 +196,16 @@ def test_forward_info_env_override(monkeypatch):
     with pytest.raises(fwa.FwaError) as e:                # chunk 16 has no chunked plan
         fwa.delta_forward_info(1, 1, 64, 16, 16, 1, 16)
     assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
+    monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
+    assert fwa.delta_forward_info(4, 8, 4096, 64, 64, 2, 64, torch.bfloat16) == (
+        "stream", _stream_workspace_formula(4, 8, 4096, 64))
+    for args in ((1, 8, 1024, 64, 64, 1, 64),                       # fp32
+                 (1, 8, 1024, 64, 64, 1, 32, torch.bfloat16),       # chunk 32
+                 (1, 8, 1024, 64, 16, 1, 64, torch.bfloat16),       # d_v 16
+                 (1, 8, 1024, 32, 64, 3, 64, torch.bfloat16)):      # D 192
+        with pytest.raises(fwa.FwaError) as e:
+            fwa.delta_forward_info(*args)
+        assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
     monkeypatch.setenv("FWA_FORWARD_PATH", "fast")
     with pytest.raises(fwa.FwaError) as e:
         fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64)

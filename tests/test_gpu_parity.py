@@ -21,7 +21,7 @@ def _dev(inp):
     return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
 
 
-FORWARD_PATHS = ["chunked", "fused"]
+FORWARD_PATHS = ["chunked", "stream", "fused"]
 
 
 @pytest.fixture(params=FORWARD_PATHS)
@@ -31,9 +31,14 @@ def path(request, monkeypatch):
     return request.param
 
 
-def _skip_unless(path, chunk):
-    if path == "chunked" and chunk not in (32, 64):
-        pytest.skip("the chunked path takes chunks of 32 and 64 rows")
+def _skip_unless(path, w):
+    """Skips when the implementation forced by FWA_FORWARD_PATH does not take this shape."""
+    try:
+        got, _ = fwa.delta_forward_info(w.B, w.H, w.T, w.d_k, w.d_v, w.nu, w.chunk, w.torch_dtype)
+    except fwa.FwaError as e:
+        assert e.status == fwa.FWA_ERR_UNSUPPORTED
+        pytest.skip(f"the {path} path does not take this shape: {e}")
+    assert got in (path, "none")
 
 
 def _forward(inp_d, nu, chunk, W0=True):
@@ -102,7 +107,7 @@ FWD_CASES = [
 @pytest.mark.parametrize("name,ov", FWD_CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(FWD_CASES)])
 def test_forward_parity(name, ov, path):
     w = workload(name, **ov)
-    _skip_unless(path, w.chunk)
+    _skip_unless(path, w)
     log(f"forward[{path}] {w}")
     inp = make_inputs(w)
     y, Wf = _forward(_dev(inp), w.nu, w.chunk)
@@ -128,6 +133,7 @@ def test_forward_full_size_long_sequence_sampled(path, full_size_case):
     """The 8 x 16 x 16384 (D 384, bf16) workload at full size, chunk 64, in the launch
     configuration the benchmark uses; the oracle checks 6 sampled (b, h) slices end to end."""
     w, inp, (yr, Wr) = full_size_case
+    _skip_unless(path, w)
     log(f"forward[{path}] full {w}")
     y, Wf = _forward(_dev(inp), w.nu, 64)
     assert torch.isfinite(y.float()).all() and torch.isfinite(Wf).all()
@@ -140,13 +146,15 @@ def test_forward_full_size_long_sequence_sampled(path, full_size_case):
 
 
 def test_forward_T0_and_empty(path):
-    w = workload("h8_t1024_d64_nu1_f32", T=0, w0_std=0.1)
+    w = workload("b4_h8_t4096_d64_nu2_bf16_carried" if path == "stream" else "h8_t1024_d64_nu1_f32",
+                 T=0, w0_std=0.1)
+    _skip_unless(path, workload(w.name, T=1))
     inp = _dev(make_inputs(w))
     y, Wf = _forward(inp, w.nu, 64)
     assert torch.equal(Wf, inp["W0"])
     y, Wf = _forward(inp, w.nu, 64, W0=False)
     assert torch.count_nonzero(Wf) == 0
-    w = workload("h8_t1024_d64_nu1_f32", B=0)
+    w = workload(w.name, B=0)
     inp = _dev(make_inputs(w))
     y, Wf = _forward(inp, w.nu, 64)
     assert y.numel() == 0
@@ -155,6 +163,7 @@ def test_forward_T0_and_empty(path):
 def test_forward_in_place_carry_and_segments(path):
     """forward(T1) then forward(T2) with W0 = W_final (in place) equals forward(T1 + T2)."""
     w = workload("b4_h8_t4096_d64_nu2_bf16_carried", T=700, B=2)
+    _skip_unless(path, w)
     inp = _dev(make_inputs(w))
     y, Wf = _forward(inp, w.nu, 64)
     W = inp["W0"].clone()
@@ -176,7 +185,8 @@ def test_forward_chunk_independence_and_determinism(monkeypatch):
     w = workload("h8_t1024_d64_nu1_f32", T=500, w0_std=0.02)
     inp = _dev(make_inputs(w))
     outs = {}
-    for p in FORWARD_PATHS:
+    paths = ("chunked", "fused")           # fp32 inputs: the streaming path takes bf16 only
+    for p in paths:
         monkeypatch.setenv("FWA_FORWARD_PATH", p)
         for c in ((32, 64) if p == "chunked" else (16, 32, 64)):
             outs[(p, c)] = _forward(inp, w.nu, c)
@@ -184,7 +194,7 @@ def test_forward_chunk_independence_and_determinism(monkeypatch):
     for key, (y, Wf) in outs.items():
         assert normwise(to_f64(y), to_f64(ref[0]), 2) <= 1e-4, key
         assert normwise(to_f64(Wf), to_f64(ref[1]), 2) <= 1e-4, key
-    for p in FORWARD_PATHS:
+    for p in paths:
         monkeypatch.setenv("FWA_FORWARD_PATH", p)
         y2, W2 = _forward(inp, w.nu, 64)
         assert torch.equal(y2, outs[(p, 64)][0]) and torch.equal(W2, outs[(p, 64)][1])

@@ -1,6 +1,6 @@
 """Parity of the forward over every chain-kernel configuration the chunked path's planner can
-pick (each D it accepts, both dtypes, chunks of 32 and 64), and over seeded random shapes on
-both implementations.  Same bars as test_gpu_parity: fp32 1e-4, bf16 2e-2 normwise per
+pick (each D it accepts, both dtypes, chunks of 32 and 64), over every memory split and roll
+length of the streaming path, and over seeded random shapes on all implementations.  Same bars as test_gpu_parity: fp32 1e-4, bf16 2e-2 normwise per
 (b, h) slice against the fp64 oracle."""
 import random
 
@@ -60,6 +60,34 @@ def test_chunked_every_chain_config(dt, D, C, monkeypatch):
     _run(w, "chunked", monkeypatch)
 
 
+# Streaming path (bf16, chunk 64, d_v in {32, 64}, D in {128, 256, 384}): each D gives a
+# different number of memory d-tiles per wave (1-3), each d_k a different roll window, nu up
+# to 8 the longest roll the extended q rows hold; T covers a lone partial chunk, an exact
+# chunk and ragged tails.  D = 512 (the prep kernel's working set exceeds LDS at chunk 64) and
+# nu > 8 are refused.
+STREAM_CASES = [
+    # (d_k, nu, d_v, B, H, T)
+    (64, 1, 64, 1, 2, 203), (64, 2, 64, 2, 2, 64), (64, 3, 32, 1, 3, 17), (64, 4, 64, 1, 2, 140),
+    (32, 2, 64, 1, 2, 129), (32, 4, 32, 2, 1, 200), (32, 6, 64, 1, 1, 75), (16, 4, 64, 1, 2, 100),
+    (16, 8, 32, 1, 2, 190), (16, 12, 64, 1, 1, 70),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES,
+                         ids=[f"dk{c[0]}-nu{c[1]}-dv{c[2]}-T{c[5]}" for c in STREAM_CASES])
+def test_stream_every_split(case, monkeypatch):
+    d_k, nu, d_v, B, H, T = case
+    w = workload("b4_h8_t4096_d64_nu2_bf16_carried", B=B, H=H, T=T, d_k=d_k, nu=nu, d_v=d_v,
+                 chunk=64, w0_std=0.05, seed=9000 + d_k * 10 + nu)
+    monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
+    if nu > 8 or 2 * d_k * nu > 384:
+        with pytest.raises(fwa.FwaError) as e:
+            fwa.delta_forward_info(B, H, T, d_k, d_v, nu, 64, w.torch_dtype)
+        assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
+        return
+    _run(w, "stream", monkeypatch)
+
+
 def _random_cases(n, seed):
     rng = random.Random(seed)
     out = []
@@ -82,12 +110,12 @@ RANDOM = _random_cases(24, 20261202)
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=[f"r{c[0]}" for c in RANDOM])
-def test_random_shapes_both_paths(case, monkeypatch):
+def test_random_shapes_every_path(case, monkeypatch):
     i, B, H, T, d_k, d_v, nu, dt, C, w0 = case
     w = workload("h8_t1024_d64_nu1_f32", B=B, H=H, T=T, d_k=d_k, d_v=d_v, nu=nu, dtype=dt,
                  chunk=C, w0_std=w0, seed=8000 + i)
     ran = 0
-    for path in ("chunked", "fused"):
+    for path in ("chunked", "stream", "fused"):
         monkeypatch.setenv("FWA_FORWARD_PATH", path)
         try:
             fwa.delta_forward_info(B, H, T, d_k, d_v, nu, C, w.torch_dtype)

@@ -124,21 +124,22 @@ __device__ __forceinline__ float dpfp_task_any(const float (&a)[8], const IT* ro
 }
 
 // DPFP of the C staged raw rows Xk, Xq ([C][d_k], input storage type) into the tiles Kr, Qr
-// ([C][krs], internal column order).  A task is (tile, row, group of 8 positions); the 256
+// ([C][krs], internal column order).  A task is (tile, row, group of 8 positions); the NTH
 // threads take 2 C d_k / 8 tasks, two per pass with both tasks' loads issued first.  Each
 // task reads its row through two 16-byte LDS loads and writes 16-byte LDS stores; no lane
 // exchanges.  The shift count is a compile-time constant for nu <= 4.
 // With rhok / rhoq given, the row normalisers rho = 1 / (row sum + eps) are formed as well: a
 // row's d_k / 8 tasks sit in adjacent lanes of one pass, so their fp32 sums reduce by lane
 // shuffles and the row's first task writes rho[t].
-template <typename LT, typename IT, int C>
+// NTH threads take part (64 w + l < NTH); WITH_Q = false forms the K tile only (Xq, Qr unused).
+template <typename LT, typename IT, int C, int NTH = 256, bool WITH_Q = true>
 __device__ __forceinline__ void dpfp_chunk(const IT* Xk, const IT* Xq, LT* Kr, LT* Qr, int krs,
                                            int d_k, int nu, int w, int l,
                                            float* rhok = nullptr, float* rhoq = nullptr) {
     const int tid = 64 * w + l;
     const int lg = __builtin_ctz(d_k >> 3);           // log2(groups per row)
     const int gm = (d_k >> 3) - 1;
-    const int ntask = 2 * C * (d_k >> 3);
+    const int ntask = (WITH_Q ? 2 : 1) * C * (d_k >> 3);
     auto locate = [&](int tau, const IT*& row, LT*& out, int& j0, int& jp) {
         const int jg = tau & gm;
         const int rt = tau >> lg;                      // 0 .. 2C-1: K rows, then Q rows
@@ -151,10 +152,10 @@ __device__ __forceinline__ void dpfp_chunk(const IT* Xk, const IT* Xq, LT* Kr, L
     };
     auto run = [&](auto nu_tag) {
         constexpr int NU = decltype(nu_tag)::value;
-        for (int tau = tid; tau < ntask; tau += 512) {
+        for (int tau = tid; tau < ntask; tau += 2 * NTH) {
             // two tasks per pass (the second clamps to the first when past the end: it then
             // rewrites identical values)
-            const int tau2 = tau + 256 < ntask ? tau + 256 : tau;
+            const int tau2 = tau + NTH < ntask ? tau + NTH : tau;
             const IT *r1, *r2;
             LT *o1, *o2;
             int j1, p1, j2, p2;
@@ -163,15 +164,17 @@ __device__ __forceinline__ void dpfp_chunk(const IT* Xk, const IT* Xq, LT* Kr, L
             float a1[8], v1[8], a2[8], v2[8];
             load8_f32(r1 + j1, a1);
             load8_f32(r2 + j2, a2);
-            float s1, s2;
+            float s1, s2 = 0.0f;
+            // ntask and NTH are multiples of 64, so `two` is uniform over each wave
+            const bool two = tau2 != tau;
             if constexpr (NU > 0) {
                 load8_f32(r1 + p1, v1);
                 load8_f32(r2 + p2, v2);
                 s1 = dpfp_task<LT, NU>(a1, v1, j1, d_k, o1);
-                s2 = dpfp_task<LT, NU>(a2, v2, j2, d_k, o2);
+                if (two) s2 = dpfp_task<LT, NU>(a2, v2, j2, d_k, o2);
             } else {
                 s1 = dpfp_task_any<LT, IT>(a1, r1, j1, d_k, nu, o1);
-                s2 = dpfp_task_any<LT, IT>(a2, r2, j2, d_k, nu, o2);
+                if (two) s2 = dpfp_task_any<LT, IT>(a2, r2, j2, d_k, nu, o2);
             }
             if (rhok != nullptr) {
                 // sums over aligned groups of 2, 4 or 8 lanes by DPP (no LDS traffic, so no
@@ -189,7 +192,7 @@ __device__ __forceinline__ void dpfp_chunk(const IT* Xk, const IT* Xq, LT* Kr, L
                 if ((tau & gm) == 0) {
                     const int rt1 = tau >> lg, rt2 = tau2 >> lg;
                     (rt1 >= C ? rhoq + (rt1 - C) : rhok + rt1)[0] = __builtin_amdgcn_rcpf(s1 + kDpfpEps);
-                    (rt2 >= C ? rhoq + (rt2 - C) : rhok + rt2)[0] = __builtin_amdgcn_rcpf(s2 + kDpfpEps);
+                    if (two) (rt2 >= C ? rhoq + (rt2 - C) : rhok + rt2)[0] = __builtin_amdgcn_rcpf(s2 + kDpfpEps);
                 }
             }
         }

@@ -82,7 +82,9 @@ __device__ __forceinline__ const char* blk_ptr(const char* base, int64_t blk, in
 //   WyA (A blocks of W_y, C x D), KtA (A blocks of K^T, D x C, raw products),
 //   QA (A blocks of Q, raw), PA (A blocks of P~, zero above the diagonal),
 //   Uy (fp32 accumulator tiles of U_y), RK, RQ (rho_k, rho_q).
-template <bool BF16, int C>
+// LITE (bf16 only, for the streaming forward): stage k, q and beta only; write PA, RK, RQ and
+// A'' = A diag(beta) as hi and lo A-operand blocks (AH, AL); no K^T, Q, W_y or U_y.
+template <bool BF16, int C, bool LITE = false>
 __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     using LT = typename ChunkTypes<BF16>::LT;
     constexpr int pair = ChunkTypes<BF16>::pair;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
             reinterpret_cast<uint4*>(Xk)[e] = masked(*reinterpret_cast<const uint4*>(kc + off), m);
             reinterpret_cast<uint4*>(Xq)[e] = masked(*reinterpret_cast<const uint4*>(qc + off), m);
         }
-        for (int e = tid; e < C * vb / 16; e += 256) {
+        for (int e = tid; e < (LITE ? 0 : C * vb / 16); e += 256) {
             const bool ok = (e * 16) / vb < Cc;
             const int off = ok ? e * 16 : 0;
             const uint32_t m = ok ? 0xffffffffu : 0u;
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     {
         // QA: blocks (tt, j), j < NDB
         char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < NT * NDB * 64; e += 256) {
+        for (int e = tid; e < (LITE ? 0 : NT * NDB * 64); e += 256) {
             const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
             const LT* src = Qr + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
             uint4 val;
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         }
         // KtA: blocks (dt, j), j < NTB: slot (h, e) = K[16 (pair j + h) + 4 (lam / 16) + e][16 dt + lam % 16]
         char* kt = ws + a.o_kt + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < ND * NTB * 64; e += 256) {
+        for (int e = tid; e < (LITE ? 0 : ND * NTB * 64); e += 256) {
             const int blk = e >> 6, lam = e & 63, dt = blk / NTB, j = blk % NTB;
             const LT* src = Kr + (16 * pair * j + 4 * (lam >> 4)) * krs + 16 * dt + (lam & 15);
             uint4 val;
@@ -280,6 +282,25 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         }
     }
     lds_barrier();
+
+    if constexpr (LITE) {
+        static_assert(BF16, "the compact mode serves the bf16 streaming forward");
+        // AH, AL: A-operand blocks (ta, j), j < NTB, of A'' hi and lo (slot (h, e) of lane l =
+        // A''[16 ta + l % 16][16 (2 j + h) + 4 (l / 16) + e]); blocks above the diagonal are zero
+        char* ah = ws + a.o_ah + u * (static_cast<int64_t>(C) * C * 2);
+        char* al = ws + a.o_al + u * (static_cast<int64_t>(C) * C * 2);
+        for (int e = tid; e < NT * NTB * 64; e += 256) {
+            const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
+            const int at = (16 * ta + (lam & 15)) * aps + 32 * j + 4 * (lam >> 4);
+            const uint2 h0 = *reinterpret_cast<const uint2*>(Bh + at);
+            const uint2 h1 = *reinterpret_cast<const uint2*>(Bh + at + 16);
+            const uint2 l0 = *reinterpret_cast<const uint2*>(Bl + at);
+            const uint2 l1 = *reinterpret_cast<const uint2*>(Bl + at + 16);
+            *reinterpret_cast<uint4*>(ah + static_cast<int64_t>(e) * 16) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            *reinterpret_cast<uint4*>(al + static_cast<int64_t>(e) * 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+        }
+        return;
+    }
 
     // ---- U_y = A'' V as accumulator tiles (t-tile, v-tile), one v-tile per wave and pass
     char* uy = ws + a.o_uy + u * (static_cast<int64_t>(C) * d_v * 4);

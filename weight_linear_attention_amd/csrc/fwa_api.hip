@@ -69,17 +69,19 @@ fwa_status hip_status(hipError_t e, const char* what) {
     return fail(FWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Forward implementation: FWA_FORWARD_PATH = "chunked" (three launches with a workspace),
-// "fused" (one launch, no workspace), or unset / "auto".  Auto takes the chunked path where it
-// applies and its workspace stays within kAutoWorkspaceLimit: beyond that the workspace
-// traffic (about 7 D-wide rows per token) outweighs the parallelism it buys, and the fused
-// kernel, which keeps everything on chip, is faster.
-enum class ForwardPath { kAuto, kChunked, kFused, kInvalid };
+// Forward implementation: FWA_FORWARD_PATH = "chunked" (three launches with a D-wide
+// workspace), "stream" (bf16: compact prep plus one serial kernel, a 24.5 KB-per-chunk
+// workspace), "fused" (one launch, no workspace), or unset / "auto".  Auto takes the chunked
+// path where it applies and its workspace stays within kAutoWorkspaceLimit: beyond that the
+// workspace traffic (about 7 D-wide rows per token) outweighs the parallelism it buys.  Larger
+// bf16 problems take the streaming path where it applies, else the fused kernel.
+enum class ForwardPath { kAuto, kChunked, kStream, kFused, kInvalid };
 constexpr int64_t kAutoWorkspaceLimit = int64_t(2) << 30;
 ForwardPath forward_path() {
     const char* s = std::getenv("FWA_FORWARD_PATH");
     if (!s || !*s || std::strcmp(s, "auto") == 0) return ForwardPath::kAuto;
     if (std::strcmp(s, "chunked") == 0) return ForwardPath::kChunked;
+    if (std::strcmp(s, "stream") == 0) return ForwardPath::kStream;
     if (std::strcmp(s, "fused") == 0) return ForwardPath::kFused;
     return ForwardPath::kInvalid;
 }
@@ -184,32 +186,49 @@ fwa_status check_forward_shape(const char* fn, int64_t BH, int T, int d_k, int d
 
 // The implementation a forward call takes (FWA_FORWARD_PATH and the shape), with its plan.
 struct ForwardChoice {
-    bool chunked;
+    int path;                       // FWA_PATH_CHUNKED, FWA_PATH_STREAM or FWA_PATH_FUSED
     fwa::ChunkPlan cplan;
+    fwa::StreamPlan splan;
     fwa::FwdPlan fplan;
+    int64_t ws_bytes;
 };
 
 fwa_status choose_forward(const char* fn, int BH, int T, int d_k, int d_v, int nu, int chunk,
                           bool bf16, ForwardChoice* c) {
     const ForwardPath want = forward_path();
     if (want == ForwardPath::kInvalid)
-        return fail(FWA_ERR_INVALID_ARG, "%s: FWA_FORWARD_PATH must be auto, chunked or fused", fn);
-    bool can_chunk = want != ForwardPath::kFused &&
-                     fwa::plan_chunked(BH, T, d_k, d_v, nu, chunk, bf16, &c->cplan);
-    const bool can_fuse = fwa::plan_forward(BH, d_k, d_v, nu, chunk, bf16, &c->fplan);
-    if (want == ForwardPath::kAuto && can_chunk && can_fuse && c->cplan.ws_bytes > kAutoWorkspaceLimit)
-        can_chunk = false;
-    c->chunked = can_chunk;
-    if (can_chunk) return ok();
-    if (want == ForwardPath::kChunked)
+        return fail(FWA_ERR_INVALID_ARG,
+                    "%s: FWA_FORWARD_PATH must be auto, chunked, stream or fused", fn);
+    const bool auto_ = want == ForwardPath::kAuto;
+    const bool can_chunk = (auto_ || want == ForwardPath::kChunked) &&
+                           fwa::plan_chunked(BH, T, d_k, d_v, nu, chunk, bf16, &c->cplan);
+    const bool can_stream = (auto_ || want == ForwardPath::kStream) &&
+                            fwa::plan_stream(BH, T, d_k, d_v, nu, chunk, bf16, &c->splan);
+    const bool can_fuse = (auto_ || want == ForwardPath::kFused) &&
+                          fwa::plan_forward(BH, d_k, d_v, nu, chunk, bf16, &c->fplan);
+    c->ws_bytes = 0;
+    if (can_chunk && (!auto_ || c->cplan.ws_bytes <= kAutoWorkspaceLimit || (!can_stream && !can_fuse))) {
+        c->path = FWA_PATH_CHUNKED;
+        c->ws_bytes = c->cplan.ws_bytes;
+        return ok();
+    }
+    if (can_stream) {
+        c->path = FWA_PATH_STREAM;
+        c->ws_bytes = c->splan.ws_bytes;
+        return ok();
+    }
+    if (can_fuse) {
+        c->path = FWA_PATH_FUSED;
+        return ok();
+    }
+    if (want == ForwardPath::kChunked || want == ForwardPath::kStream)
         return fail(FWA_ERR_UNSUPPORTED,
-                    "%s: the chunked path does not support d_k=%d d_v=%d nu=%d chunk=%d", fn, d_k,
-                    d_v, nu, chunk);
-    if (!can_fuse)
-        return fail(FWA_ERR_UNSUPPORTED,
-                    "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn,
-                    d_k, d_v, nu, chunk);
-    return ok();
+                    "%s: the %s path does not support d_k=%d d_v=%d nu=%d chunk=%d%s", fn,
+                    want == ForwardPath::kChunked ? "chunked" : "stream", d_k, d_v, nu, chunk,
+                    want == ForwardPath::kStream && !bf16 ? " (it takes bf16 inputs)" : "");
+    return fail(FWA_ERR_UNSUPPORTED,
+                "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn, d_k,
+                d_v, nu, chunk);
 }
 
 }  // namespace
@@ -230,8 +249,8 @@ fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu,
         if ((st = choose_forward(fn, static_cast<int>(BH), T, d_k, d_v, nu, chunk,
                                  dtype == FWA_BF16, &c)) != FWA_OK)
             return st;
-        p = c.chunked ? FWA_PATH_CHUNKED : FWA_PATH_FUSED;
-        ws = c.chunked ? c.cplan.ws_bytes : 0;
+        p = c.path;
+        ws = c.ws_bytes;
     }
     if (path) *path = p;
     if (workspace_bytes) *workspace_bytes = ws;
@@ -273,14 +292,18 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
     ForwardChoice c;
     if ((st = choose_forward(fn, static_cast<int>(BH), T, d_k, d_v, nu, chunk, bf16, &c)) != FWA_OK)
         return st;
-    if (c.chunked) {
+    if (c.path != FWA_PATH_FUSED) {
         char* ws = nullptr;
-        if (c.cplan.ws_bytes > 0) {
-            const hipError_t e = workspace_get(&ws, c.cplan.ws_bytes, stream);
+        if (c.ws_bytes > 0) {
+            const hipError_t e = workspace_get(&ws, c.ws_bytes, stream);
             if (e != hipSuccess)
                 return fail(FWA_ERR_HIP, "%s: workspace of %lld bytes: %s", fn,
-                            (long long)c.cplan.ws_bytes, hipGetErrorString(e));
+                            (long long)c.ws_bytes, hipGetErrorString(e));
         }
+        if (c.path == FWA_PATH_STREAM)
+            return hip_status(fwa::launch_stream(c.splan, q, k, v, beta_logit, W0, y, W_final, ws,
+                                                 stream),
+                              "fwa_delta_forward launch");
         return hip_status(fwa::launch_chunked(c.cplan, q, k, v, beta_logit, W0, y, W_final, ws,
                                               bf16, stream),
                           "fwa_delta_forward launch");

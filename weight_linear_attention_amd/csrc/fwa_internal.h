@@ -55,10 +55,14 @@ struct ChunkArgs {
     float* Wf;
     char* ws;
     int64_t o_wy, o_kt, o_qa, o_pa, o_uy, o_rk, o_rq, o_wn, o_un;
+    int64_t o_ah, o_al;          // streaming forward: (I + L)^-1 diag(beta) as bf16 hi, lo blocks
     int BH, T, NC, d_k, d_v, nu, D;
     int DP, NDP;
     int krs, lss, pss, aps;
     int l_kr, l_qr, l_x, l_ls, l_ps, l_li, l_xv, l_small;
+    // streaming kernel LDS layout (byte offsets): K and Q tiles, the raw-input slot (k rows,
+    // then q rows at s_qoff and v columns at s_voff inside it), W^T copy, Z (then y) and U tiles
+    int s_k, s_q, s_raw, s_qoff, s_voff, s_wt, s_z, s_u;
 };
 
 struct ChunkPlan {
@@ -78,5 +82,20 @@ bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Chu
 hipError_t launch_chunked(const ChunkPlan& plan, const void* q, const void* k, const void* v,
                           const void* bl, const float* W0, void* y, float* Wf, char* ws,
                           bool bf16, hipStream_t stream);
+
+// Streaming forward (bf16): the prep kernel in its compact mode, then one serial kernel per
+// (b, h, 32 columns of d_v).  plan_stream returns false for shapes it does not implement.
+struct StreamPlan {
+    ChunkArgs args;
+    int C;
+    int lds_prep;
+    int lds_stream;
+    int ndw;             // d-tiles of W^T per wave (of 8)
+    int64_t ws_bytes;
+};
+bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan);
+hipError_t launch_stream(const StreamPlan& plan, const void* q, const void* k, const void* v,
+                         const void* bl, const float* W0, void* y, float* Wf, char* ws,
+                         hipStream_t stream);
 
 }  // namespace fwa

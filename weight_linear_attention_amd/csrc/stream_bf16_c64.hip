@@ -1,0 +1,102 @@
+// Streaming forward (bf16, chunk 64): host planning, the LDS and workspace layouts, and the two
+// launches (prep kernel in compact mode, then the stream kernel).
+#include "stream_kernel.h"
+
+namespace fwa {
+
+static int align16s(int x) { return (x + 15) & ~15; }
+
+constexpr int kMaxLdsStream = 160 * 1024;
+
+bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan) {
+    const int D = 2 * d_k * nu;
+    // bf16, chunk 64, 32-column pairs of d_v, D in whole 8-wave shares of 16-row tiles, and
+    // rolls of at most 8 positions (the extended q rows hold 8 positions before 0)
+    if (!bf16 || C != 64 || d_v % 32 != 0 || D % 128 != 0 || nu > 8) return false;
+    if (d_k != 16 && d_k != 32 && d_k != 64) return false;
+    ChunkPlan cp;
+    if (!plan_chunked(BH, T, d_k, d_v, nu, C, bf16, &cp)) return false;   // prep LDS layout
+    ChunkArgs a = cp.args;
+    const int64_t NU = static_cast<int64_t>(BH) * a.NC;
+    const int64_t szCC = static_cast<int64_t>(C) * C * 2, szR = C * 4;
+    a.o_wy = a.o_kt = a.o_qa = a.o_uy = a.o_wn = a.o_un = 0;
+    a.o_pa = 0;
+    a.o_ah = a.o_pa + NU * szCC;
+    a.o_al = a.o_ah + NU * szCC;
+    a.o_rk = a.o_al + NU * szCC;
+    a.o_rq = a.o_rk + NU * szR;
+    // the y buffer's byte offsets (up to the last chunk's padded rows) fit 32 bits
+    if ((static_cast<int64_t>(T) + C) * d_v * 2 >= (int64_t(1) << 32)) return false;
+    // stream kernel LDS: K and Q tiles, the raw slot, W^T copy, Z (then y) and U tiles
+    int off = 0;
+    a.s_k = off;
+    off = align16s(off + C * a.krs * 2);
+    a.s_q = off;
+    off = align16s(off + C * a.krs * 2);
+    const int kbytes = C * d_k * 2;
+    a.s_raw = off;
+    a.s_qoff = kbytes;
+    a.s_voff = align16s(a.s_qoff + kbytes);
+    off = align16s(off + a.s_voff + C * 32 * 2);
+    a.s_wt = off;
+    off += (D / 32) * 2 * 1024;
+    a.s_z = off;
+    off += 8 * 1024;
+    a.s_u = off;
+    off += 8 * 1024;
+    if (off > kMaxLdsStream) return false;
+    plan->args = a;
+    plan->C = C;
+    plan->lds_prep = cp.lds_prep;
+    plan->lds_stream = off;
+    plan->ndw = D / 128;
+    plan->ws_bytes = a.o_rq + NU * szR;
+    return true;
+}
+
+template <int NDW>
+static hipError_t launch_stream_ndw(const StreamPlan& p, hipStream_t stream) {
+    auto kern = delta_stream_kernel<64, NDW>;
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_stream);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / 32)));
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kStreamWaves), p.lds_stream, stream, p.args);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_c64(const StreamPlan& p, hipStream_t stream) {
+    const ChunkArgs& a = p.args;
+    const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
+    if (NU > 0) {
+        auto prep = delta_prep_kernel<true, 64, true>;
+        hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prep), p.lds_prep);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(256), p.lds_prep, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    switch (p.ndw) {
+        case 1: return launch_stream_ndw<1>(p, stream);
+        case 2: return launch_stream_ndw<2>(p, stream);
+        case 3: return launch_stream_ndw<3>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_stream(const StreamPlan& plan_in, const void* q, const void* k, const void* v,
+                         const void* bl, const float* W0, void* y, float* Wf, char* ws,
+                         hipStream_t stream) {
+    StreamPlan p = plan_in;
+    ChunkArgs& a = p.args;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.bl = bl;
+    a.W0 = W0;
+    a.y = y;
+    a.Wf = Wf;
+    a.ws = ws;
+    if (p.C != 64) return hipErrorInvalidValue;
+    return launch_stream_c64(p, stream);
+}
+
+}  // namespace fwa

@@ -1,0 +1,296 @@
+// Streaming forward of the fast-weight delta rule for bf16 inputs: the serial pass over the
+// chunks without the D-wide workspace of the three-launch path.
+//
+// The recurrence ("Fast Weights Transformer" guide, xdnf.cn/news/308600, sections
+// "FastWeightsAttention / update formula" and "... / module structure and source walkthrough")
+// is evaluated chunk by chunk with the chunked algebra derived from it: for a chunk of C rows
+// starting from memory W (d_v x D), with raw DPFP tiles K, Q, normalisers rho_k, rho_q and
+// A'' = (I + L)^-1 diag(beta) (L = diag(beta) strict_lower(K~ K~^T)):
+//     X = K W^T,   U = A'' (V - rho_k o X),   Y = rho_q o (Q W^T) + P~ U,   W^T += K^T (rho_k o U).
+// A'', P~ and the normalisers do not depend on the memory; the prep kernel (compact mode) forms
+// them for all chunks at once, about 24.5 KB per chunk.  This kernel runs the memory-dependent
+// part: one workgroup of 8 waves per (b, h, 32 columns of d_v), the fp32 memory W^T (D x 32)
+// in MFMA accumulators, ND / 8 d-tiles per wave x 2 column tiles.  Per chunk:
+//   A  K and Q tiles from the raw rows (DPFP tasks over all 512 threads); each wave writes its
+//      memory tiles as bf16 halves of the B-operand blocks of W^T (the LDS copy the products
+//      read).
+//   Wave w owns tile (row tile w % 4, column tile w / 4) of X, Q W^T, U and Y:
+//   B  X = K W^T and Q W^T over all of D (one W^T block per k-step feeds both products); Z =
+//      V - rho_k o X to LDS (fp32 tiles), rho_q o Q W^T kept in registers.
+//   C  U = A'' Z (A'' and Z as bf16 hi + lo pairs, 3 MFMAs per k-step).
+//   D  Y = rho_q o (Q W^T) + P~ U, as bf16 rows in LDS (over Z); the wave's memory tiles +=
+//      K^T (rho_k o U), K^T read from the K tile by LDS
+//      transpose reads; the next chunk's raw k, q, v (loaded at the top of the chunk, after
+//      this chunk's A'', P~ and normalisers) go to the raw slot, dead since phase B.
+//   After the last barrier every thread stores 8 bytes of the chunk's y with a buffer store
+//   whose range check drops rows past the sequence end.
+// Four LDS-only barriers per chunk.  Every wave issues the same global loads and stores in
+// every chunk with no branch around them, so the compiler's in-order wait counts stay exact:
+// a wait for data loaded earlier never waits for the y stores issued after it.
+#pragma once
+
+#include "chunk_tile.h"
+#include "chunked_kernels.h"
+
+namespace fwa {
+
+constexpr int kStreamWaves = 8;
+// Word 3 of a raw buffer resource on gfx9-family GPUs: 32-bit data format (a zero format
+// disables the access); the hardware drops accesses at or past the range in word 2.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ uint4 bf16_lo_part(const f32x4& x0, const f32x4& x1) {
+    f32x4 r0, r1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r0[e] = x0[e] - static_cast<float>(static_cast<__bf16>(x0[e]));
+        r1[e] = x1[e] - static_cast<float>(static_cast<__bf16>(x1[e]));
+    }
+    return pack_bf16x8(r0, r1);
+}
+
+template <int C, int NDW>
+__global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
+    static_assert(C == 64, "row tiles map one-to-one onto waves 0-3 and 4-7");
+    constexpr int NT = C / 16, NTB = NT / 2;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_k = a.d_k, d_v = a.d_v, D = a.D, T = a.T, NC = a.NC, krs = a.krs;
+    const int NP = d_v / 32;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, NP);
+    const int bh = bi.bh, cp = static_cast<int>(bi.i);
+    const int col0 = 32 * cp;
+    const int rt = w & 3, ct = w >> 2;         // the wave's (row tile, column tile) of X, Q W^T,
+                                               // U and Y
+
+    u16* Kt = reinterpret_cast<u16*>(smem + a.s_k);
+    u16* Qt = reinterpret_cast<u16*>(smem + a.s_q);
+    char* WT = smem + a.s_wt;                  // B blocks (jb, ct) of W^T, bf16
+    float* Zb = reinterpret_cast<float*>(smem + a.s_z);
+    float* Ub = reinterpret_cast<float*>(smem + a.s_u);
+    char* sb = smem + a.s_raw;                 // raw k rows, q rows, v columns of one chunk
+    auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
+
+    // ---- memory tiles: d-tile w + 8 s, column tile ct
+    f32x4 Wst[NDW][2];
+#pragma unroll
+    for (int s = 0; s < NDW; ++s)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            Wst[s][ct] = zero4();
+            if (a.W0) {
+                // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+                const float* src = a.W0 + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
+                                   orig_col(16 * (w + 8 * s) + 4 * g4, d_k);
+                const float2 lo = *reinterpret_cast<const float2*>(src);
+                const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
+                Wst[s][ct] = f32x4{lo.x, hi.x, lo.y, hi.y};
+            }
+        }
+
+    // ---- raw inputs of a chunk: k and q rows (bf16 [C][d_k]) and the workgroup's 32 v columns
+    //      ([C][32]); registers at the top of the previous chunk, the LDS slot in its phase D
+    const int64_t row0 = static_cast<int64_t>(bh) * T;
+    const u16* kB = static_cast<const u16*>(a.k) + row0 * d_k;
+    const u16* qB = static_cast<const u16*>(a.q) + row0 * d_k;
+    const u16* vB = static_cast<const u16*>(a.v) + row0 * d_v + col0;
+    const int kunits = C * d_k / 8;            // 16-byte units of the k (and q) block: <= 512
+    const int ush = __builtin_ctz(d_k) - 3;    // unit u lies in row u >> ush
+    // Loads are branch-free: a unit past the sequence end reads unit 0 of the chunk (always in
+    // range) and is zeroed by its mask when it is written to LDS, so no wait follows the loads.
+    uint4 rk, rq, rv;
+    uint32_t mk = 0u, mv = 0u;
+    auto load_raw = [&](int n) {
+        const int t0 = n * C, Cn = min(C, T - t0);
+        const bool okk = tid < kunits && (tid >> ush) < Cn;
+        const int64_t ko = static_cast<int64_t>(t0) * d_k + (okk ? tid * 8 : 0);
+        rk = *reinterpret_cast<const uint4*>(kB + ko);
+        rq = *reinterpret_cast<const uint4*>(qB + ko);
+        const bool okv = tid < 4 * C && (tid >> 2) < Cn;
+        rv = *reinterpret_cast<const uint4*>(vB + static_cast<int64_t>(t0 + (okv ? tid >> 2 : 0)) * d_v +
+                                             (okv ? 8 * (tid & 3) : 0));
+        mk = okk ? 0xffffffffu : 0u;
+        mv = okv ? 0xffffffffu : 0u;
+    };
+    auto store_raw = [&]() {
+        rk = make_uint4(rk.x & mk, rk.y & mk, rk.z & mk, rk.w & mk);
+        rq = make_uint4(rq.x & mk, rq.y & mk, rq.z & mk, rq.w & mk);
+        rv = make_uint4(rv.x & mv, rv.y & mv, rv.z & mv, rv.w & mv);
+        if (tid < kunits) {
+            reinterpret_cast<uint4*>(sb)[tid] = rk;
+            reinterpret_cast<uint4*>(sb + a.s_qoff)[tid] = rq;
+        }
+        if (tid < 4 * C) reinterpret_cast<uint4*>(sb + a.s_voff)[tid] = rv;
+    };
+
+    // ---- per-chunk results of the prep kernel: A'' blocks (rt, j) hi and lo, P~ blocks
+    //      (rt, j) (Y waves), rho_k of every row tile and rho_q of row tile rt (accumulator row
+    //      order)
+    uint4 ah[NTB], al[NTB], pa[NTB];
+    f32x4 rka[NT], rqv;
+    auto load_ws = [&](int n) {
+        const int64_t u = static_cast<int64_t>(bh) * NC + n;
+        const char* ahp = a.ws + a.o_ah + u * (C * C * 2);
+        const char* alp = a.ws + a.o_al + u * (C * C * 2);
+        const char* pap = a.ws + a.o_pa + u * (C * C * 2);
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, rt * NTB + j, l));
+            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, rt * NTB + j, l));
+            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, rt * NTB + j, l));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+            rka[tt] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rk) + u * C + 16 * tt + 4 * g4);
+        rqv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rq) + u * C + 16 * rt + 4 * g4);
+    };
+
+    if (NC > 0) {
+        load_raw(0);
+        store_raw();
+    }
+    lds_barrier();
+
+    // y of this workgroup's columns as a buffer: offsets from (b, h, t = 0, col0); the range ends
+    // where row T would begin, so rows past the sequence end are dropped by the hardware
+    u16* Yb = reinterpret_cast<u16*>(smem + a.s_z);          // [C][32] bf16, over Z
+    const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0), (T * d_v - col0) * 2,
+        kBufferWord3);
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * C;
+        const int nn = n + 1 < NC ? n + 1 : n;          // the last chunk re-reads itself
+        // this chunk's prep results (first used in phase B), then the next chunk's raw rows
+        load_ws(n);
+        load_raw(nn);
+        const f32x4 rkc = rka[rt];
+
+        // ---- A: K and Q tiles, W^T copy
+        dpfp_chunk<u16, u16, C, 512, true>(reinterpret_cast<const u16*>(sb),
+                                           reinterpret_cast<const u16*>(sb + a.s_qoff), Kt, Qt,
+                                           krs, d_k, a.nu, w, l);
+#pragma unroll
+        for (int s = 0; s < NDW; ++s) {
+            const int dt = w + 8 * s;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                *reinterpret_cast<uint2*>(WT + (((dt >> 1) * 2 + ct) * 64 + l) * 16 + 8 * (dt & 1)) =
+                    make_uint2(pack_bf16x2(Wst[s][ct][0], Wst[s][ct][1]), pack_bf16x2(Wst[s][ct][2], Wst[s][ct][3]));
+        }
+        lds_barrier();                                           // B1
+
+        // ---- B: X = K W^T and Q W^T for tile (rt, ct)
+        f32x4 xacc = zero4(), qacc = zero4();
+        {
+            constexpr int NDB = 4 * NDW;                           // D / 32 k-steps
+            const u16* kr = Kt + (16 * rt + l16) * krs + 4 * g4;
+            const u16* qr = Qt + (16 * rt + l16) * krs + 4 * g4;
+            auto opnd = [&](const u16* r, int jb) {
+                const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(r + 32 * jb);
+                const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(r + 32 * jb + 16);
+                return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            auto wblk = [&](int jb) {
+                return as_bf16x8(*reinterpret_cast<const uint4*>(WT + ((jb * 2 + ct) * 64 + l) * 16));
+            };
+            // fully unrolled: the scheduler issues the LDS reads several k-steps ahead; two
+            // accumulators per product keep consecutive MFMAs independent
+            f32x4 xacc1 = zero4(), qacc1 = zero4();
+#pragma unroll
+            for (int jb = 0; jb < NDB; jb += 2) {
+                const bf16x8 w0 = wblk(jb), w1 = wblk(jb + 1);
+                xacc = mfma_bf16_k32(opnd(kr, jb), w0, xacc);
+                qacc = mfma_bf16_k32(opnd(qr, jb), w0, qacc);
+                xacc1 = mfma_bf16_k32(opnd(kr, jb + 1), w1, xacc1);
+                qacc1 = mfma_bf16_k32(opnd(qr, jb + 1), w1, qacc1);
+            }
+            xacc += xacc1;
+            qacc += qacc1;
+        }
+        {
+            // Z = V - rho_k o X (rows 16 rt + 4 g4 + e, columns 16 ct + l16)
+            const u16* vs = reinterpret_cast<const u16*>(sb + a.s_voff);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                xacc[e] = bf16_bits_to_f32(vs[(16 * rt + 4 * g4 + e) * 32 + 16 * ct + l16]) - rkc[e] * xacc[e];
+            *tile(Zb, rt, ct) = xacc;
+            qacc *= rqv;
+        }
+        lds_barrier();                                           // B2
+
+        // ---- C: U tile (rt, ct) = A'' Z
+        {
+            f32x4 u = zero4();
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > rt) break;                            // A'' is zero above the diagonal
+                const f32x4 z0 = *tile(Zb, 2 * j, ct), z1 = *tile(Zb, 2 * j + 1, ct);
+                const bf16x8 zh = as_bf16x8(pack_bf16x8(z0, z1));
+                const bf16x8 zl = as_bf16x8(bf16_lo_part(z0, z1));
+                u = mfma_bf16_k32(as_bf16x8(ah[j]), zh, u);
+                u = mfma_bf16_k32(as_bf16x8(ah[j]), zl, u);
+                u = mfma_bf16_k32(as_bf16x8(al[j]), zh, u);
+            }
+            *tile(Ub, rt, ct) = u;
+        }
+        lds_barrier();                                           // B3
+
+        // ---- D: Y tile (rt, ct), memory update, next chunk's raw inputs
+        {
+            f32x4 y = qacc;
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > rt) break;
+                const bf16x8 ub = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, ct), *tile(Ub, 2 * j + 1, ct)));
+                y = mfma_bf16_k32(as_bf16x8(pa[j]), ub, y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Yb[(16 * rt + 4 * g4 + e) * 32 + 16 * ct + l16] = f32_to_bf16_bits(y[e]);
+        }
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            // B operand rho_k o U of rows 32 j .. 32 j + 31 (tiles 2 j, 2 j + 1)
+            const bf16x8 ub0 = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, 0) * rka[2 * j], *tile(Ub, 2 * j + 1, 0) * rka[2 * j + 1]));
+            const bf16x8 ub1 = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, 1) * rka[2 * j], *tile(Ub, 2 * j + 1, 1) * rka[2 * j + 1]));
+            const u16* kt = Kt + (32 * j + 4 * g4 + (l16 >> 2)) * krs + 4 * (l16 & 3);
+#pragma unroll
+            for (int s = 0; s < NDW; ++s) {
+                const u16* kc = kt + 16 * (w + 8 * s);
+                const bf16x4 c0 = lds_read_tr_b16x4(kc);
+                const bf16x4 c1 = lds_read_tr_b16x4(kc + 16 * krs);
+                const bf16x8 kta = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                Wst[s][0] = mfma_bf16_k32(kta, ub0, Wst[s][0]);
+                Wst[s][1] = mfma_bf16_k32(kta, ub1, Wst[s][1]);
+            }
+        }
+        store_raw();
+        lds_barrier();                                           // B4
+        // y rows of the chunk: 8 bytes per thread; rows past the sequence end fall outside the
+        // buffer's range and are dropped
+        {
+            const int t = tid >> 3, c4 = 4 * (tid & 7);
+            const uint2 v2 = *reinterpret_cast<const uint2*>(Yb + t * 32 + c4);
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{v2.x, v2.y}, yrsrc,
+                                                  ((t0 + t) * d_v + c4) * 2, 0, 0);
+        }
+    }
+
+    if (a.Wf) {
+#pragma unroll
+        for (int s = 0; s < NDW; ++s)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
+                             orig_col(16 * (w + 8 * s) + 4 * g4, d_k);
+                *reinterpret_cast<float2*>(dst) = make_float2(Wst[s][ct][0], Wst[s][ct][2]);
+                *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[s][ct][1], Wst[s][ct][3]);
+            }
+    }
+}
+
+hipError_t launch_stream_c64(const StreamPlan& p, hipStream_t s);
+
+}  // namespace fwa

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libfwa.so")
 
 FWA_OK, FWA_ERR_INVALID_ARG, FWA_ERR_UNSUPPORTED, FWA_ERR_HIP = 0, 1, 2, 3
 FWA_F32, FWA_BF16 = 0, 1
-FWA_PATH_NONE, FWA_PATH_CHUNKED, FWA_PATH_FUSED = 0, 1, 2
+FWA_PATH_NONE, FWA_PATH_CHUNKED, FWA_PATH_FUSED, FWA_PATH_STREAM = 0, 1, 2, 3
 
 EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_info", "fwa_delta_step",
             "fwa_status_string", "fwa_last_error", "fwa_version")
@@ -147,7 +147,8 @@ def delta_forward_info(B, H, T, d_k, d_v, nu=1, chunk=64, dtype=torch.float32):
     path, ws = ctypes.c_int(0), ctypes.c_int64(0)
     _check(lib().fwa_delta_forward_info(B, H, T, d_k, d_v, nu, chunk, code, ctypes.byref(path),
                                         ctypes.byref(ws)))
-    names = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED: "fused"}
+    names = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED: "fused",
+             FWA_PATH_STREAM: "stream"}
     return names[path.value], ws.value
 
 

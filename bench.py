@@ -15,7 +15,8 @@ already resident in HBM when timing starts.  Other workloads (--workload):
                                                                     reference for HBM counters)
 
 Prints ONE JSON line.  `roofline` describes the dominant call: the forward (one launch on the
-fused path, three on the chunked path) or, for the decode and DPFP workloads, that kernel.
+fused path, two on the streaming path, three on the chunked path) or, for the decode and DPFP
+workloads, that kernel.
 `achieved` is its algorithmic bytes or flops divided by its mean duration, measured with HIP
 events on the launch stream over the timed region (forward workloads: an event pair around each
 call; decode and DPFP: one pair around the back-to-back calls, divided by their number);

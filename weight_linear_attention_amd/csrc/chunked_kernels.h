@@ -82,10 +82,15 @@ __device__ __forceinline__ const char* blk_ptr(const char* base, int64_t blk, in
 //   WyA (A blocks of W_y, C x D), KtA (A blocks of K^T, D x C, raw products),
 //   QA (A blocks of Q, raw), PA (A blocks of P~, zero above the diagonal),
 //   Uy (fp32 accumulator tiles of U_y), RK, RQ (rho_k, rho_q).
+// Eight waves (two per SIMD), so one wave's LDS and MFMA latencies overlap the other's work.
+// G/P, its scaling and the block inverse keep one unit or block column per wave (waves 0-3);
+// DPFP, the write-outs and the U_y / W_y GEMMs spread over all eight.
+constexpr int kPrepThreads = 512, kPrepWaves = kPrepThreads / 64;
+
 // LITE (bf16 only, for the streaming forward): stage k, q and beta only; write PA, RK, RQ and
 // A'' = A diag(beta) as hi and lo A-operand blocks (AH, AL); no K^T, Q, W_y or U_y.
 template <bool BF16, int C, bool LITE = false>
-__global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a) {
     using LT = typename ChunkTypes<BF16>::LT;
     constexpr int pair = ChunkTypes<BF16>::pair;
     constexpr int NT = C / 16, NTB = NT / pair;
@@ -122,14 +127,14 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         // A unit past the sequence end reads the chunk's first unit (always in range) and is
         // zeroed by the mask.
         auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
-        for (int e = tid; e < C * kb / 16; e += 256) {
+        for (int e = tid; e < C * kb / 16; e += kPrepThreads) {
             const bool ok = (e * 16) / kb < Cc;
             const int off = ok ? e * 16 : 0;
             const uint32_t m = ok ? 0xffffffffu : 0u;
             reinterpret_cast<uint4*>(Xk)[e] = masked(*reinterpret_cast<const uint4*>(kc + off), m);
             reinterpret_cast<uint4*>(Xq)[e] = masked(*reinterpret_cast<const uint4*>(qc + off), m);
         }
-        for (int e = tid; e < (LITE ? 0 : C * vb / 16); e += 256) {
+        for (int e = tid; e < (LITE ? 0 : C * vb / 16); e += kPrepThreads) {
             const bool ok = (e * 16) / vb < Cc;
             const int off = ok ? e * 16 : 0;
             const uint32_t m = ok ? 0xffffffffu : 0u;
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     }
     lds_barrier();
 
-    dpfp_chunk<LT, LT, C>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l, rhok, rhoq);
+    dpfp_chunk<LT, LT, C, kPrepThreads>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l, rhok, rhoq);
     lds_barrier();
 
     {
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     {
         // QA: blocks (tt, j), j < NDB
         char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < (LITE ? 0 : NT * NDB * 64); e += 256) {
+        for (int e = tid; e < (LITE ? 0 : NT * NDB * 64); e += kPrepThreads) {
             const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
             const LT* src = Qr + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
             uint4 val;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         }
         // KtA: blocks (dt, j), j < NTB: slot (h, e) = K[16 (pair j + h) + 4 (lam / 16) + e][16 dt + lam % 16]
         char* kt = ws + a.o_kt + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < (LITE ? 0 : ND * NTB * 64); e += 256) {
+        for (int e = tid; e < (LITE ? 0 : ND * NTB * 64); e += kPrepThreads) {
             const int blk = e >> 6, lam = e & 63, dt = blk / NTB, j = blk % NTB;
             const LT* src = Kr + (16 * pair * j + 4 * (lam >> 4)) * krs + 16 * dt + (lam & 15);
             uint4 val;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         }
         // PA: blocks (ta, j), j < NTB; tiles above the diagonal are zero
         char* pa = ws + a.o_pa + u * (static_cast<int64_t>(C) * C * sizeof(LT));
-        for (int e = tid; e < NT * NTB * 64; e += 256) {
+        for (int e = tid; e < NT * NTB * 64; e += kPrepThreads) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
             const LT* src = Ps + (16 * ta + (lam & 15)) * a.pss + 16 * pair * j + 4 * (lam >> 4);
             uint4 val = make_uint4(0u, 0u, 0u, 0u);
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         // A''[16 ta + l % 16][16 (2 j + h) + 4 (l / 16) + e]); blocks above the diagonal are zero
         char* ah = ws + a.o_ah + u * (static_cast<int64_t>(C) * C * 2);
         char* al = ws + a.o_al + u * (static_cast<int64_t>(C) * C * 2);
-        for (int e = tid; e < NT * NTB * 64; e += 256) {
+        for (int e = tid; e < NT * NTB * 64; e += kPrepThreads) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
             const int at = (16 * ta + (lam & 15)) * aps + 32 * j + 4 * (lam >> 4);
             const uint2 h0 = *reinterpret_cast<const uint2*>(Bh + at);
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
 
     // ---- U_y = A'' V as accumulator tiles (t-tile, v-tile), one v-tile per wave and pass
     char* uy = ws + a.o_uy + u * (static_cast<int64_t>(C) * d_v * 4);
-    for (int vt = w; vt < NVT; vt += 4) {
+    for (int vt = w; vt < NVT; vt += kPrepWaves) {
         f32x4 acc[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) acc[tt] = zero4();
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
     if constexpr (BF16) {
         // k-slot (h, e) of lane group g is row s = 32 kb + 16 h + 4 g + e of the chunk; the K^T
         // operand comes from the row-major K tile by two LDS transpose reads.
-        for (int j = w; j < NDB; j += 4) {
+        for (int j = w; j < NDB; j += kPrepWaves) {
             f32x4 acc[2][NT];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -401,7 +406,7 @@ __global__ __launch_bounds__(256, 1) void delta_prep_kernel(ChunkArgs a) {
         }
     } else {
         // k-slot of lane group g in the r-th of four MFMAs is row s = 16 m + 4 g + r.
-        for (int dt = w; dt < ND; dt += 4) {
+        for (int dt = w; dt < ND; dt += kPrepWaves) {
             f32x4 acc[NT];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) acc[tt] = zero4();
@@ -953,7 +958,7 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
         auto prep = delta_prep_kernel<BF16, C>;
         hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prep), p.lds_prep);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(256), p.lds_prep, stream, a);
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipError_t e;

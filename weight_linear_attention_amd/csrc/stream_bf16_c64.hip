@@ -71,7 +71,7 @@ hipError_t launch_stream_c64(const StreamPlan& p, hipStream_t stream) {
         auto prep = delta_prep_kernel<true, 64, true>;
         hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prep), p.lds_prep);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(256), p.lds_prep, stream, a);
+        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     switch (p.ndw) {

@@ -214,13 +214,18 @@ def test_forward_unsupported_shapes_raise():
 
 # ------------------------------------------------------------------------------ decode
 
-@pytest.mark.parametrize("dtype,d_k,nu,d_v", [(torch.float32, 64, 1, 64),
-                                              (torch.bfloat16, 64, 3, 64),
-                                              (torch.float32, 16, 1, 16),
-                                              (torch.float32, 128, 2, 48),
-                                              (torch.bfloat16, 32, 4, 24)])
-def test_step_parity_many_steps(dtype, d_k, nu, d_v):
-    w = workload("decode_b256_h8_d64_nu1_f32", B=8, H=3, d_k=d_k, d_v=d_v, nu=nu,
+# Few (b, h) slices make the step split each slice's rows over several workgroups: B*H = 24
+# gives one row round per workgroup; B*H = 64 with d_v = 40 (5 rounds of 8 rows) gives two
+# rounds per workgroup, a one-round part and an empty one.
+@pytest.mark.parametrize("dtype,d_k,nu,d_v,B,H", [(torch.float32, 64, 1, 64, 8, 3),
+                                                  (torch.bfloat16, 64, 3, 64, 8, 3),
+                                                  (torch.float32, 16, 1, 16, 8, 3),
+                                                  (torch.float32, 128, 2, 48, 8, 3),
+                                                  (torch.bfloat16, 32, 4, 24, 8, 3),
+                                                  (torch.float32, 64, 1, 40, 16, 4),
+                                                  (torch.float32, 64, 1, 64, 1, 1)])
+def test_step_parity_many_steps(dtype, d_k, nu, d_v, B, H):
+    w = workload("decode_b256_h8_d64_nu1_f32", B=B, H=H, d_k=d_k, d_v=d_v, nu=nu,
                  dtype="bf16" if dtype == torch.bfloat16 else "f32", w0_std=0.05)
     steps = 40
     log(f"step {w} steps={steps}")
@@ -229,8 +234,10 @@ def test_step_parity_many_steps(dtype, d_k, nu, d_v):
     W = dev["W0"].clone()
     ys = []
     for s in range(steps):
-        ys.append(fwa.delta_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["beta_logit"][s], W,
-                                 nu=nu))
+        # fresh copies: the entry point takes 16-byte aligned pointers, and a step's slice of a
+        # small batch (beta at B*H = 1) is not
+        ys.append(fwa.delta_step(dev["q"][s].clone(), dev["k"][s].clone(), dev["v"][s].clone(),
+                                 dev["beta_logit"][s].clone(), W, nu=nu))
     torch.cuda.synchronize()
     # the oracle runs the same tokens as one T = steps sequence
     perm = lambda t: to_f64(t).transpose(1, 2, 0, *range(3, t.dim()))

@@ -11,7 +11,8 @@
 // (b, h)), the decode regime the "Transformer" page (wineandchord.com), section "Complexity",
 // describes.
 //
-// Mapping: one workgroup (4 waves) per (b, h).  A row of D floats is spread over LR lanes of
+// Mapping: one workgroup (4 waves) per (b, h), or, when there are few (b, h) slices, a power
+// of two of workgroups per (b, h) that split its rows (each recomputes f and g).  A row of D floats is spread over LR lanes of
 // one wave, CPL float4 columns per lane (D = 4 * LR * CPL), so every row dot product is a
 // lane-shuffle reduction inside a wave and each lane issues 16-byte loads and stores.  Each
 // lane computes the f and g entries of its own columns straight from k and q (cached global
@@ -44,9 +45,10 @@ template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void delta_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ bl, float* __restrict__ W, void* __restrict__ y, int d_k, int d_v,
-    int nu, int LR) {
+    int nu, int LR, int rsplit) {
     constexpr int RB = (CPL == 1) ? 8 : (CPL == 2 ? 4 : 2);  // row rounds per batch
-    const int64_t s = blockIdx.x;
+    const int64_t s = blockIdx.x / rsplit;                    // (b, h)
+    const int part = blockIdx.x % rsplit;                     // its share of the row rounds
     const int two_dk = 2 * d_k;                // a power of two (d_k in {16, 32, 64, 128})
     const int sh = __builtin_ctz(two_dk);
     const int D = two_dk * nu;
@@ -56,7 +58,10 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
     const int RPR = 4 * rpw;           // rows per workgroup round
     const int rr = wv * rpw + l / LR;  // this lane's row inside a round
     const int c = l % LR;
-    const int rounds = (d_v + RPR - 1) / RPR;
+    const int all_rounds = (d_v + RPR - 1) / RPR;
+    const int rpp = (all_rounds + rsplit - 1) / rsplit;       // rounds per workgroup
+    const int rbase = part * rpp;                             // first round of this workgroup
+    const int rounds = max(0, min(all_rounds - rbase, rpp));
     const int64_t vb = s * d_v;
 
     // Every load is issued up front: the first batch of W rows, then this lane's v entries,
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
     float vrow[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-        const int row = rr + RPR * b;
+        const int row = rr + RPR * (rbase + b);
         const bool ok = b < rounds && row < d_v;
         const int rs = ok ? row : 0;                     // a row that exists; zeroed below
 #pragma unroll
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
         if (r0 > 0) {
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
-                const int row = rr + RPR * (r0 + b);
+                const int row = rr + RPR * (rbase + r0 + b);
                 const bool ok = r0 + b < rounds && row < d_v;
                 const int rs = ok ? row : 0;
 #pragma unroll
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            const int row = rr + RPR * (r0 + b);
+            const int row = rr + RPR * (rbase + r0 + b);
             if (r0 + b < rounds && row < d_v) {
                 const float u = beta * (vrow[b] - dk[b]);
                 if (c == 0) store_elem<BF16>(y, vb + row, dq[b] + u * fg);
@@ -190,11 +195,18 @@ hipError_t launch_delta_step(const void* q, const void* k, const void* v, const 
     const int D = 2 * d_k * nu;
     int LR = 0;
     const int cpl = step_cpl_for(D, &LR);
-    const dim3 grid(static_cast<unsigned>(BH)), block(256);
+    if (cpl == 0) return hipErrorInvalidValue;
+    // Few (b, h) slices: split each slice's rows over several workgroups (up to one row round
+    // each) so that at least ~256 workgroups share the latency-bound step.
+    const int RPR = 4 * (64 / LR), all_rounds = (d_v + RPR - 1) / RPR;
+    int rsplit = 1;
+    while (rsplit < all_rounds && BH * rsplit < 256) rsplit *= 2;
+    if (rsplit > all_rounds) rsplit = all_rounds;
+    const dim3 grid(static_cast<unsigned>(BH * rsplit)), block(256);
 #define FWA_STEP_CASE(BF, C)                                                                 \
     if (bf16 == BF && cpl == C) {                                                            \
         hipLaunchKernelGGL((delta_step_kernel<BF, C>), grid, block, 0, stream, q, k, v, bl, W, \
-                           y, d_k, d_v, nu, LR);                                             \
+                           y, d_k, d_v, nu, LR, rsplit);                                     \
         return hipGetLastError();                                                            \
     }
     FWA_STEP_CASE(false, 1) FWA_STEP_CASE(false, 2) FWA_STEP_CASE(false, 3)

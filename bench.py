@@ -18,8 +18,9 @@ Prints ONE JSON line.  `roofline` describes the dominant call: the forward (one 
 fused path, two on the streaming path, three on the chunked path) or, for the decode and DPFP
 workloads, that kernel.
 `achieved` is its algorithmic bytes or flops divided by its mean duration, measured with HIP
-events on the launch stream over the timed region (forward workloads: an event pair around each
-call; decode and DPFP: one pair around the back-to-back calls, divided by their number);
+events on the launch stream over the timed region (forward workloads: event pairs around the
+calls of every 8th step; decode and DPFP: one pair around the back-to-back calls, divided by
+their number);
 `traffic` is the HBM bytes per call that
 rocprofv3 counted on the same sources (profiles/traffic.json), or null.  `cpu_baseline` times
 the fp64 oracle on the host (rank 0 only).
@@ -37,6 +38,9 @@ sys.path.insert(0, HERE)
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 DEFAULT_WORKLOAD = "h8_t1024_d64_nu1_f32"
+WARMUP_SECONDS = 0.3       # default warm-up length
+EVENT_EVERY = 8            # forward workloads: event-bracketed step every EVENT_EVERY steps
+DECODE_WARM_SLICES = 64    # decode: input slices the warm-up cycles through
 
 
 def parse():
@@ -125,14 +129,18 @@ def main():
         kind, w = "prefill", workload(name)
     if args.chunk is not None:
         w = workload(w.name, chunk=args.chunk)
-    steps = args.steps if args.steps is not None else (1024 if kind == "decode" else 20)
-    warmup = args.warmup if args.warmup is not None else 3
+    steps = args.steps if args.steps is not None else {
+        "prefill+decode": 2000, "prefill": 50, "decode": 1024, "dpfp": 50}[kind]
+    # Warm-up: --warmup steps, else as many as fill WARMUP_SECONDS (at least 3): the GPU's
+    # clocks reach their steady state only after some tens of milliseconds of work.
+    warmup = args.warmup
     es = 2 if w.dtype == "bf16" else 4
     D, BH = w.D, w.B * w.H
 
     # ------------------------------------------------------------------ inputs in HBM
     if kind == "decode":
-        inp = make_decode_inputs(w, steps=steps + warmup)
+        # DECODE_WARM_SLICES slices for the warm-up (cycled), then one fresh slice per timed step
+        inp = make_decode_inputs(w, steps=DECODE_WARM_SLICES + steps)
         d = {k: v.to(dev) for k, v in inp.items()}
         W = d["W0"].clone()
     else:
@@ -156,14 +164,17 @@ def main():
 
     def one_step(i, marks):
         if kind in ("prefill", "prefill+decode"):
-            marks[0].record()
+            if marks:
+                marks[0].record()
             fwa.delta_forward(d["q"], d["k"], d["v"], d["beta_logit"], d["W0"], chunk=w.chunk,
                               nu=w.nu, out=y, W_final=Wf)
-            marks[1].record()
+            if marks:
+                marks[1].record()
             if kind == "prefill+decode":
                 fwa.delta_step(nxt["q"], nxt["k"], nxt["v"], nxt["beta_logit"], Wf, nu=w.nu,
                                out=ystep)
-                marks[2].record()
+                if marks:
+                    marks[2].record()
         elif kind == "decode":
             fwa.delta_step(d["q"][i], d["k"][i], d["v"][i], d["beta_logit"][i], W, nu=w.nu,
                            out=ystep)
@@ -171,30 +182,43 @@ def main():
             fwa.dpfp(d["q"], w.nu, out=phi_q)
             fwa.dpfp(d["k"], w.nu, out=phi_k)
 
-    # The forward workloads bracket each call with events to split forward from decode step.
-    # The decode and DPFP workloads run back to back, as a serving loop would, with one event
-    # pair around the timed region: their mean launch duration is region time / calls, which
-    # includes the gaps between launches (events between launches would stall the queue).
+    # Every step runs back to back, as a serving loop would, inside one event pair around the
+    # timed region.  The forward workloads also bracket the calls of every EVENT_EVERY-th step
+    # with events (forward, then decode step), which split forward from decode time: an event
+    # recorded between two launches stalls the queue for a few microseconds, so bracketing
+    # every call would slow the whole loop by about 15% on the default workload.  The decode and
+    # DPFP workloads' mean launch duration is region time / calls, gaps between launches
+    # included.
     per_call = kind in ("prefill", "prefill+decode")
-    for i in range(warmup):
-        one_step(i, [ev(), ev(), ev()])
+    sampled = list(range(0, steps, EVENT_EVERY)) if per_call else []
+    warm_idx = lambda i: i % DECODE_WARM_SLICES if kind == "decode" else i
+    if warmup is None:
+        warmup, t_w = 0, time.perf_counter()
+        while warmup < 3 or time.perf_counter() - t_w < WARMUP_SECONDS:
+            one_step(warm_idx(warmup), None)
+            warmup += 1
+            if warmup % 64 == 0:
+                torch.cuda.synchronize()
+    else:
+        for i in range(warmup):
+            one_step(warm_idx(i), None)
     torch.cuda.synchronize()
-    marks = [[ev(), ev(), ev()] for _ in range(steps)] if per_call else None
+    marks = {i: [ev(), ev(), ev()] for i in sampled}
     region = (ev(), ev())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record()
     for i in range(steps):
-        one_step(warmup + i if kind == "decode" else i, marks[i] if per_call else None)
+        one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, marks.get(i))
     region[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     if per_call:
-        main_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+        main_ms = sum(marks[i][0].elapsed_time(marks[i][1]) for i in sampled) / len(sampled)
     else:
         main_ms = region[0].elapsed_time(region[1]) / steps
-    step_ms = (sum(m[1].elapsed_time(m[2]) for m in marks) / steps
+    step_ms = (sum(marks[i][1].elapsed_time(marks[i][2]) for i in sampled) / len(sampled)
                if kind == "prefill+decode" else None)
 
     # ------------------------------------------------------------------ metric + roofline

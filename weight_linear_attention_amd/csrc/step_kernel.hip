@@ -12,12 +12,14 @@
 // describes.
 //
 // Mapping: one workgroup (4 waves) per (b, h), or, when there are few (b, h) slices, a power
-// of two of workgroups per (b, h) that split its rows (each recomputes f and g).  A row of D floats is spread over LR lanes of
-// one wave, CPL float4 columns per lane (D = 4 * LR * CPL), so every row dot product is a
+// of two of workgroups per (b, h) that split its rows (each recomputes f and g).  A row of D
+// floats is spread over LR lanes of one wave, CPL float4 columns per lane (D = 4 * LR * CPL,
+// both compile-time), so every row dot product is a
 // lane-shuffle reduction inside a wave and each lane issues 16-byte loads and stores.  Each
-// lane computes the f and g entries of its own columns straight from k and q (cached global
-// reads) and the group reduces the DPFP sums, so the kernel needs no LDS and no barrier; every
-// load (W rows, v, beta, k, q) is in flight before the first arithmetic.
+// lane computes the f and g entries of its own columns from 4-wide loads of k and q and a
+// per-wave LDS copy of relu([k,-k]) and relu([q,-q]), and the group reduces the DPFP sums, so
+// the kernel needs no barrier; every load (W rows, v, beta, k, q) is in flight before the
+// first arithmetic.
 #include "fwa_common.h"
 #include "fwa_internal.h"
 
@@ -30,22 +32,38 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float lane_group_sum(float x, int LR) {
+template <int LR>
+__device__ __forceinline__ float lane_group_sum(float x) {
     x = dpp_add<0xB1>(x);                    // quad_perm [1,0,3,2]: lane ^ 1
     x = dpp_add<0x4E>(x);                    // quad_perm [2,3,0,1]: lane ^ 2
-    if (LR == 8) return x + __shfl_xor(x, 4, 8);
+    if constexpr (LR == 8) return x + __shfl_xor(x, 4, 8);
     x = dpp_add<0x124>(x);                   // row_ror:4
     x = dpp_add<0x128>(x);                   // row_ror:8
-    if (LR >= 32) x += __shfl_xor(x, 16);
-    if (LR == 64) x += __shfl_xor(x, 32);
+    if constexpr (LR >= 32) x += __shfl_xor(x, 16);
+    if constexpr (LR == 64) x += __shfl_xor(x, 32);
     return x;
 }
 
-template <bool BF16, int CPL>
+// Elements i .. i+3 of an fp32 or bf16 vector (i a multiple of 4, the base 16-byte aligned).
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* p, int64_t i, float (&x)[4]) {
+    if constexpr (BF16) {
+        const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const u16*>(p) + i);
+        x[0] = __uint_as_float(r.x << 16);
+        x[1] = __uint_as_float(r.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.y << 16);
+        x[3] = __uint_as_float(r.y & 0xffff0000u);
+    } else {
+        const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+        x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+    }
+}
+
+template <bool BF16, int CPL, int LR>
 __global__ __launch_bounds__(256) void delta_step_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ bl, float* __restrict__ W, void* __restrict__ y, int d_k, int d_v,
-    int nu, int LR, int rsplit) {
+    int nu, int rsplit) {
     constexpr int RB = (CPL == 1) ? 8 : (CPL == 2 ? 4 : 2);  // row rounds per batch
     const int64_t s = blockIdx.x / rsplit;                    // (b, h)
     const int part = blockIdx.x % rsplit;                     // its share of the row rounds
@@ -54,8 +72,8 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
     const int D = two_dk * nu;
     float* Ws = W + s * static_cast<int64_t>(d_v) * D;
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
-    const int rpw = 64 / LR;           // rows per wave per round
-    const int RPR = 4 * rpw;           // rows per workgroup round
+    constexpr int rpw = 64 / LR;       // rows per wave per round
+    constexpr int RPR = 4 * rpw;       // rows per workgroup round
     const int rr = wv * rpw + l / LR;  // this lane's row inside a round
     const int c = l % LR;
     const int all_rounds = (d_v + RPR - 1) / RPR;
@@ -71,45 +89,64 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
         const int row = rr + RPR * (rbase + b);
-        const bool ok = b < rounds && row < d_v;
-        const int rs = ok ? row : 0;                     // a row that exists; zeroed below
+        const int rs = b < rounds && row < d_v ? row : 0;   // a row that exists; not stored
 #pragma unroll
-        for (int m = 0; m < CPL; ++m) {
-            const float4 w4 = *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(rs) * D + 4 * (c + LR * m));
-            wrow[b][m] = ok ? w4 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int m = 0; m < CPL; ++m)
+            wrow[b][m] = *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(rs) * D + 4 * (c + LR * m));
         vrow[b] = load_elem<BF16>(v, vb + rs);
     }
     const float blog = load_elem<BF16>(bl, s);
 
     // f and g on this lane's 4*CPL columns.  Position d lies in the block of shift
-    // i = d / (2 d_k) + 1 at j = d mod 2 d_k; its factors are relu([k,-k]) at j and at
-    // (j - i) mod 2 d_k.
+    // i = d / (2 d_k) + 1 at j = d mod 2 d_k; its factors are x[j] and x[(j - i) mod 2 d_k] with
+    // x = relu([k, -k]).  A lane's four columns d0 .. d0+3 share i and one half of x, so their
+    // first factors come from one 4-wide load of k.  The rolled factors come from a copy of x
+    // in LDS, one per wave: the first 2 d_k / 4 lanes of the wave hold x's blocks in their
+    // first column group (2 d_k / 4 <= LR always, since CPL <= nu), and write them there.
+    // Two vector loads per column group for k and q instead of sixteen scalar ones.
+    __shared__ __attribute__((aligned(16))) float xs_all[4][2][256];   // 2 d_k <= 256
+    float* xk = xs_all[wv][0];
+    float* xq = xs_all[wv][1];
     const int64_t kb = s * d_k;
+    float xa_k[CPL][4], xa_q[CPL][4];
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int j0 = (4 * (c + LR * m)) & (two_dk - 1);
+        const float sa = j0 < d_k ? 1.0f : -1.0f;
+        float kv[4], qv[4];
+        load4<BF16>(k, kb + (j0 & (d_k - 1)), kv);
+        load4<BF16>(q, kb + (j0 & (d_k - 1)), qv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xa_k[m][e] = relu(sa * kv[e]);
+            xa_q[m][e] = relu(sa * qv[e]);
+        }
+    }
+    if (l < two_dk / 4) {
+        *reinterpret_cast<float4*>(xk + 4 * l) = make_float4(xa_k[0][0], xa_k[0][1], xa_k[0][2], xa_k[0][3]);
+        *reinterpret_cast<float4*>(xq + 4 * l) = make_float4(xa_q[0][0], xa_q[0][1], xa_q[0][2], xa_q[0][3]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own LDS writes are done
     float f[CPL * 4], g[CPL * 4];
     float Sf = 0.0f, Sg = 0.0f;
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
+        const int d0 = 4 * (c + LR * m);
+        const int i = (d0 >> sh) + 1;
+        const int ws = ((d0 & (two_dk - 1)) - i) & (two_dk - 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int d = 4 * (c + LR * m) + e;
-            const int i = (d >> sh) + 1;
-            const int j = d & (two_dk - 1);
-            const int jr = (j - i) & (two_dk - 1);
-            const int ja = j & (d_k - 1), jb = jr & (d_k - 1);
-            const float sa = j < d_k ? 1.0f : -1.0f, sb = jr < d_k ? 1.0f : -1.0f;
-            const float fk = relu(sa * load_elem<BF16>(k, kb + ja)) *
-                             relu(sb * load_elem<BF16>(k, kb + jb));
-            const float fq = relu(sa * load_elem<BF16>(q, kb + ja)) *
-                             relu(sb * load_elem<BF16>(q, kb + jb));
+            const int jr = (ws + e) & (two_dk - 1);
+            const float fk = xa_k[m][e] * xk[jr];
+            const float fq = xa_q[m][e] * xq[jr];
             f[m * 4 + e] = fk;
             g[m * 4 + e] = fq;
             Sf += fk;
             Sg += fq;
         }
     }
-    Sf = lane_group_sum(Sf, LR);
-    Sg = lane_group_sum(Sg, LR);
+    Sf = lane_group_sum<LR>(Sf);
+    Sg = lane_group_sum<LR>(Sg);
     const float rf = 1.0f / (Sf + kDpfpEps), rg = 1.0f / (Sg + kDpfpEps);
     float fg = 0.0f;
 #pragma unroll
@@ -118,7 +155,7 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
         g[e] *= rg;
         fg += f[e] * g[e];
     }
-    fg = lane_group_sum(fg, LR);
+    fg = lane_group_sum<LR>(fg);
     const float beta = sigmoid_stable(blog);
 
     for (int r0 = 0; r0 < rounds; r0 += RB) {
@@ -126,13 +163,10 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int row = rr + RPR * (rbase + r0 + b);
-                const bool ok = r0 + b < rounds && row < d_v;
-                const int rs = ok ? row : 0;
+                const int rs = r0 + b < rounds && row < d_v ? row : 0;
 #pragma unroll
-                for (int m = 0; m < CPL; ++m) {
-                    const float4 w4 = *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(rs) * D + 4 * (c + LR * m));
-                    wrow[b][m] = ok ? w4 : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+                for (int m = 0; m < CPL; ++m)
+                    wrow[b][m] = *reinterpret_cast<const float4*>(Ws + static_cast<int64_t>(rs) * D + 4 * (c + LR * m));
                 vrow[b] = load_elem<BF16>(v, vb + rs);
             }
         }
@@ -151,8 +185,8 @@ __global__ __launch_bounds__(256) void delta_step_kernel(
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            dk[b] = lane_group_sum(dk[b], LR);
-            dq[b] = lane_group_sum(dq[b], LR);
+            dk[b] = lane_group_sum<LR>(dk[b]);
+            dq[b] = lane_group_sum<LR>(dq[b]);
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
@@ -203,15 +237,17 @@ hipError_t launch_delta_step(const void* q, const void* k, const void* v, const 
     while (rsplit < all_rounds && BH * rsplit < 256) rsplit *= 2;
     if (rsplit > all_rounds) rsplit = all_rounds;
     const dim3 grid(static_cast<unsigned>(BH * rsplit)), block(256);
-#define FWA_STEP_CASE(BF, C)                                                                 \
-    if (bf16 == BF && cpl == C) {                                                            \
-        hipLaunchKernelGGL((delta_step_kernel<BF, C>), grid, block, 0, stream, q, k, v, bl, W, \
-                           y, d_k, d_v, nu, LR, rsplit);                                     \
+#define FWA_STEP_CASE(BF, C, L)                                                              \
+    if (bf16 == BF && cpl == C && LR == L) {                                                 \
+        hipLaunchKernelGGL((delta_step_kernel<BF, C, L>), grid, block, 0, stream, q, k, v, bl, \
+                           W, y, d_k, d_v, nu, rsplit);                                      \
         return hipGetLastError();                                                            \
     }
-    FWA_STEP_CASE(false, 1) FWA_STEP_CASE(false, 2) FWA_STEP_CASE(false, 3)
-    FWA_STEP_CASE(false, 4) FWA_STEP_CASE(true, 1) FWA_STEP_CASE(true, 2)
-    FWA_STEP_CASE(true, 3) FWA_STEP_CASE(true, 4)
+#define FWA_STEP_LR(BF, C) \
+    FWA_STEP_CASE(BF, C, 8) FWA_STEP_CASE(BF, C, 16) FWA_STEP_CASE(BF, C, 32) FWA_STEP_CASE(BF, C, 64)
+    FWA_STEP_LR(false, 1) FWA_STEP_LR(false, 2) FWA_STEP_LR(false, 3) FWA_STEP_LR(false, 4)
+    FWA_STEP_LR(true, 1) FWA_STEP_LR(true, 2) FWA_STEP_LR(true, 3) FWA_STEP_LR(true, 4)
+#undef FWA_STEP_LR
 #undef FWA_STEP_CASE
     return hipErrorInvalidValue;
 }

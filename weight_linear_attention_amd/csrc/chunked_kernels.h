@@ -844,6 +844,178 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
 }
 
 // ------------------------------------------------------------------------------------------
+// chain, direct: the staged kernel's decomposition (compute wave w owns row tile w of
+// S = W_y W^T over all of D and d-tiles w NDP .. +NDP of the memory) with no loader waves: each
+// wave loads its own operand blocks (W_y row tile, K^T d-tiles, U_y tile, rho_k) into registers
+// two chunks ahead, into one of two register sets, right after their last use.  LDS carries only
+// what the waves share: the W^T copy (GEMM1's B operand) and rho_k o U (the update's B
+// operand), about a third of the staged kernel's LDS traffic.  Chunks go in pairs, one per
+// register set, so every register index is static; the loop body has no branches around memory
+// operations (prefetches past the last chunk re-read it), so every wait covers only the loads
+// it needs.
+template <bool BF16, int C, int NDP>
+__global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel(ChunkArgs a) {
+    using LT = typename ChunkTypes<BF16>::LT;
+    constexpr int pair = BF16 ? 2 : 1, NT = C / 16, NTB = NT / pair;
+    constexpr int ND = kChainWaves * NDP, NDB = ND / pair, NDPB = NDP / pair;
+    static_assert(NT == kChainWaves, "one row tile of S per wave");
+    static_assert(NDP % pair == 0, "bf16 waves hold whole d-tile pairs");
+    __shared__ __attribute__((aligned(1024))) char X[NDB * 1024];   // W^T copy
+    __shared__ __attribute__((aligned(1024))) char Ub[NT * 1024];   // rho_k o U, fp32 tiles
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_k = a.d_k, D = a.D, NC = a.NC, NVT = a.d_v / 16;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, NVT);
+    const int bh = bi.bh, r = static_cast<int>(bi.i);
+    const int dt0 = w * NDP;
+    const int vcol = 16 * r + l16;
+    const int64_t u0 = static_cast<int64_t>(bh) * NC;
+    const int64_t ulast = u0 + NC - 1;
+    const int64_t szCD = static_cast<int64_t>(C) * D * sizeof(LT);
+    const int64_t szUy = static_cast<int64_t>(C) * a.d_v * 4;
+    const int64_t szWn = static_cast<int64_t>(D) * a.d_v * sizeof(LT);
+    const int64_t szUn = static_cast<int64_t>(C) * a.d_v * sizeof(LT);
+    auto lane16 = [&](char* base, int blk) { return base + blk * 1024 + l * 16; };
+    const char* wyB = a.ws + a.o_wy + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
+    const char* ktB = a.ws + a.o_kt + (static_cast<int64_t>(dt0) * NTB * 64 + l) * 16;
+    const char* uyB = a.ws + a.o_uy + ((static_cast<int64_t>(w) * NVT + r) * 64 + l) * 16;
+    const float* rkB = reinterpret_cast<const float*>(a.ws + a.o_rk) + 16 * w + 4 * g4;
+
+    uint4 wy[2][NDB];          // W_y blocks of row tile w, per register set
+    uint4 kt[2][NDP * NTB];    // K^T blocks of d-tiles dt0 ..
+    f32x4 uy[2], rk[2];        // U_y tile (w, r) and rho_k of its rows
+    auto clampu = [&](int64_t uu) { return uu <= ulast ? uu : ulast; };
+    auto load_wy = [&](int set, int64_t uu) {
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) wy[set][j] = *reinterpret_cast<const uint4*>(wyB + uu * szCD + j * 1024);
+    };
+    auto load_kt = [&](int set, int64_t uu) {
+#pragma unroll
+        for (int b = 0; b < NDP * NTB; ++b) kt[set][b] = *reinterpret_cast<const uint4*>(ktB + uu * szCD + b * 1024);
+    };
+    auto load_uy = [&](int set, int64_t uu) {
+        uy[set] = *reinterpret_cast<const f32x4*>(uyB + uu * szUy);
+        rk[set] = *reinterpret_cast<const f32x4*>(rkB + uu * C);
+    };
+
+    f32x4 Wst[NDP];
+#pragma unroll
+    for (int i = 0; i < NDP; ++i) {
+        Wst[i] = zero4();
+        if (a.W0) {
+            // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+            const float* src = a.W0 + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                               orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            const float2 lo = *reinterpret_cast<const float2*>(src);
+            const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
+            Wst[i] = f32x4{lo.x, hi.x, lo.y, hi.y};
+        }
+    }
+
+    // One chunk with register set SET; its operands are replaced by those of chunk uu + 2.
+    auto chunk = [&](int64_t uu, auto set_tag) {
+        constexpr int SET = decltype(set_tag)::value;
+        const int64_t ua = clampu(uu + 2);
+        // chunk-start memory: the LDS copy for GEMM1 and the Wn blocks for the output kernel
+        char* wn = a.ws + a.o_wn + uu * szWn;
+#pragma unroll
+        for (int i = 0; i < NDPB; ++i) {
+            uint4 val;
+            if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
+            else val = __builtin_bit_cast(uint4, Wst[i]);
+            const int jb = dt0 / pair + i;
+            *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+            *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
+        }
+        lds_barrier();                                               // B1: W^T copy complete
+        // S = W_y W^T for row tile w, two accumulators over alternating k-blocks
+        f32x4 s0 = zero4(), s1 = zero4();
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) {
+            const uint4 bv = *reinterpret_cast<const uint4*>(lane16(X, j));
+            f32x4& acc = (j & 1) ? s1 : s0;
+            if constexpr (BF16) {
+                acc = mfma_bf16_k32(as_bf16x8(wy[SET][j]), as_bf16x8(bv), acc);
+            } else {
+                const f32x4 af = as_f32x4(wy[SET][j]), bf = as_f32x4(bv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
+            }
+        }
+        load_wy(SET, ua);
+        const f32x4 U = uy[SET] - (s0 + s1);
+        // U for the output kernel: B blocks (j, r); for bf16 tile w is half h = w & 1 of
+        // pair block w / 2 (slots 4 h .. 4 h + 3 of every lane)
+        char* unp = a.ws + a.o_un + uu * szUn;
+        if constexpr (BF16) {
+            *reinterpret_cast<uint2*>(blk_ptr(unp, static_cast<int64_t>(w >> 1) * NVT + r, l) + 8 * (w & 1)) =
+                make_uint2(pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
+        } else {
+            *reinterpret_cast<f32x4*>(blk_ptr(unp, static_cast<int64_t>(w) * NVT + r, l)) = U;
+        }
+        *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rk[SET];
+        load_uy(SET, ua);
+        lds_barrier();                                               // B2: rho_k o U complete
+        // W^T += K^T (rho_k o U) for this wave's d-tiles
+        f32x4 odd[NDP];
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) odd[i] = zero4();
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            if constexpr (BF16) {
+                const f32x4 u0v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j));
+                const f32x4 u1v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j + 1));
+                const uint4 bu = pack_bf16x8(u0v, u1v);
+#pragma unroll
+                for (int i = 0; i < NDP; ++i) {
+                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
+                    dst = mfma_bf16_k32(as_bf16x8(kt[SET][i * NTB + j]), as_bf16x8(bu), dst);
+                }
+            } else {
+                const f32x4 uv = *reinterpret_cast<const f32x4*>(lane16(Ub, j));
+#pragma unroll
+                for (int i = 0; i < NDP; ++i) {
+                    const f32x4 af = as_f32x4(kt[SET][i * NTB + j]);
+                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst = mfma_f32_k4(af[e], uv[e], dst);
+                }
+            }
+        }
+        load_kt(SET, ua);
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) Wst[i] += odd[i];
+    };
+
+    if (NC > 0) {
+        load_wy(0, u0);
+        load_uy(0, u0);
+        load_kt(0, u0);
+        load_wy(1, clampu(u0 + 1));
+        load_uy(1, clampu(u0 + 1));
+        load_kt(1, clampu(u0 + 1));
+    }
+    int n = 0;
+    for (; n + 1 < NC; n += 2) {
+        chunk(u0 + n, std::integral_constant<int, 0>());
+        chunk(u0 + n + 1, std::integral_constant<int, 1>());
+    }
+    if (n < NC) chunk(u0 + n, std::integral_constant<int, 0>());
+
+    if (a.Wf) {
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) {
+            float* dst = a.Wf + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                         orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+            *reinterpret_cast<float2*>(dst) = make_float2(Wst[i][0], Wst[i][2]);
+            *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[i][1], Wst[i][3]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // output: one wave per output tile (chunk u, row tile tt, v-tile vt), four tiles per workgroup:
 //   Y = rho_q o (Q W_n^T) + P~ U_n.
 template <bool BF16, int C>
@@ -962,7 +1134,21 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipError_t e;
-    if (p.staged_ndp > 0) {
+    bool direct = false;
+    if constexpr (BF16 && C == 64) {
+        // bf16: the direct chain (two chunks of register lookahead) over the staged one
+        if (p.staged_ndp > 0) {
+            const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.BH) * (a.d_v / 16)));
+            if (p.staged_ndp == 2)
+                hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 2>), grid, dim3(64 * kChainWaves), 0, stream, a);
+            else
+                hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 4>), grid, dim3(64 * kChainWaves), 0, stream, a);
+            direct = true;
+        }
+    }
+    if (direct) {
+        e = hipGetLastError();
+    } else if (p.staged_ndp > 0) {
         if constexpr (BF16) e = p.staged_ndp == 2 ? launch_chain_staged<BF16, C, 2>(p, stream)
                                                   : launch_chain_staged<BF16, C, 4>(p, stream);
         else e = p.staged_ndp == 1 ? launch_chain_staged<BF16, C, 1>(p, stream)

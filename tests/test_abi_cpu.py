@@ -155,7 +155,8 @@ def _stream_workspace_formula(B, H, T, chunk):
     ((4, 8, 4096, 64, 64, 2, 64), "bf16", "chunked"),     # 32 heads x 4096, D 256
     ((8, 16, 16384, 64, 64, 3, 64), "bf16", "stream"),    # 128 heads x 16384: 7.6 GB chunked workspace
     ((8, 16, 16384, 64, 16, 3, 64), "bf16", "fused"),     # d_v 16: no streaming plan
-    ((8, 16, 16384, 64, 64, 3, 128), "bf16", "none"),     # neither fits (LDS): unsupported
+    ((8, 16, 16384, 64, 64, 3, 128), "bf16", "stream"),   # chunk 128: shift-sliced streaming
+    ((8, 16, 16384, 64, 16, 3, 128), "bf16", "none"),     # d_v 16, chunk 128: nothing fits
     ((1, 1, 64, 16, 16, 1, 16), "f32", "fused"),          # chunk 16: fused only
     ((1, 1, 77, 16, 16, 1, 32), "f32", "chunked"),
     ((2, 2, 300, 64, 64, 6, 64), "f32", "fused"),         # fp32 D 768 > 512: unsupported

@@ -101,6 +101,13 @@ FWD_CASES = [
     ("b4_h8_t4096_d64_nu2_bf16_carried", {}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"T": 1000, "chunk": 32}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 333, "chunk": 16, "d_v": 16}),
+    # chunk 128 (shift-sliced streaming path): full size, a ragged tail, d_v 32 with nu 1,
+    # nu 4 (D 512) on 3 heads, and a single partial chunk
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"chunk": 128}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 1000, "chunk": 128, "nu": 3}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "H": 2, "T": 300, "chunk": 128, "nu": 1, "d_v": 32}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "H": 3, "T": 257, "chunk": 128, "nu": 4}),
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 2, "H": 1, "T": 45, "chunk": 128}),
 ]
 
 
@@ -129,13 +136,15 @@ def full_size_case():
     return w, inp, oracle_forward(inp, w.nu, bh_index=_FULL_PICKS)
 
 
-def test_forward_full_size_long_sequence_sampled(path, full_size_case):
-    """The 8 x 16 x 16384 (D 384, bf16) workload at full size, chunk 64, in the launch
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_forward_full_size_long_sequence_sampled(path, full_size_case, chunk):
+    """The 8 x 16 x 16384 (D 384, bf16) workload at full size, chunk 64 and 128, in the launch
     configuration the benchmark uses; the oracle checks 6 sampled (b, h) slices end to end."""
     w, inp, (yr, Wr) = full_size_case
+    w = workload(w.name, chunk=chunk)
     _skip_unless(path, w)
     log(f"forward[{path}] full {w}")
-    y, Wf = _forward(_dev(inp), w.nu, 64)
+    y, Wf = _forward(_dev(inp), w.nu, chunk)
     assert torch.isfinite(y.float()).all() and torch.isfinite(Wf).all()
     picks = _FULL_PICKS
     sel = tuple(torch.tensor(ix) for ix in zip(*picks))
@@ -198,6 +207,29 @@ def test_forward_chunk_independence_and_determinism(monkeypatch):
         monkeypatch.setenv("FWA_FORWARD_PATH", p)
         y2, W2 = _forward(inp, w.nu, 64)
         assert torch.equal(y2, outs[(p, 64)][0]) and torch.equal(W2, outs[(p, 64)][1])
+
+
+@pytest.mark.parametrize("prep", ["full", "sliced"])
+def test_stream_prep_variants_and_chunks(monkeypatch, prep):
+    """The streaming path with either prep kernel at chunk 64, and at chunk 128, against the
+    oracle and against each other; each is deterministic."""
+    monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
+    monkeypatch.setenv("FWA_STREAM_PREP", prep)
+    w = workload("b4_h8_t4096_d64_nu2_bf16_carried", B=1, H=4, T=777, nu=3)
+    inp = make_inputs(w)
+    d = _dev(inp)
+    yr, Wr = oracle_forward(inp, w.nu)
+    outs = {}
+    for c in (64, 128):
+        y, Wf = _forward(d, w.nu, c)
+        ey, ew = normwise(to_f64(y), yr, 2), normwise(to_f64(Wf), Wr, 2)
+        log(f"  stream prep={prep} chunk={c}: y err {ey:.3e}  W_final err {ew:.3e}")
+        assert ey <= 2e-2 and ew <= 2e-2
+        y2, W2 = _forward(d, w.nu, c)
+        assert torch.equal(y, y2) and torch.equal(Wf, W2)
+        outs[c] = (y, Wf)
+    assert normwise(to_f64(outs[64][0]), to_f64(outs[128][0]), 2) <= 2e-2
+    assert normwise(to_f64(outs[64][1]), to_f64(outs[128][1]), 2) <= 2e-2
 
 
 def test_forward_unsupported_shapes_raise():

@@ -212,11 +212,12 @@ __device__ __forceinline__ void dpfp_chunk(const IT* Xk, const IT* Xq, LT* Kr, L
 // independent accumulators that interleave on the MFMA pipe.  a[ui][tb] holds tile (ra, tb),
 // b[ui][tb] tile (rb, tb) (static register indices); sa / sb are the row sums of the unit's
 // rows, computed as the same operands times a ones matrix.
-template <int C>
+// NW waves share the units: unit u goes to wave u % NW.
+template <int C, int NW = 4>
 struct GPTiles {
     static constexpr int NT = C / 16;
     static constexpr int NQ = (NT + 1) / 2;            // tile-row pairs {q, NT-1-q}
-    static constexpr int UPW = (2 * NQ + 3) / 4;       // units per wave
+    static constexpr int UPW = (2 * NQ + NW - 1) / NW; // units per wave
     f32x4 a[UPW][NT], b[UPW][NT], sa[UPW], sb[UPW];
 };
 
@@ -281,22 +282,29 @@ __device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16
     }
 }
 
-// ROWSUMS: the row sums (sa, sb) as the operands times a ones matrix; without it the caller
-// has formed the normalisers elsewhere (dpfp_chunk with rho outputs).
-template <bool BF16, int C, bool ROWSUMS = true>
-__device__ __forceinline__ void gp_compute(GPTiles<C>& gp, const void* Kv, const void* Qv,
-                                           int krs, int D, int w, int l16, int g4) {
-    using GP = GPTiles<C>;
-    constexpr int NT = GP::NT, NQ = GP::NQ, UPW = GP::UPW;
+template <int C, int NW>
+__device__ __forceinline__ void gp_zero(GPTiles<C, NW>& gp) {
+    using GP = GPTiles<C, NW>;
 #pragma unroll
-    for (int ui = 0; ui < UPW; ++ui) {
+    for (int ui = 0; ui < GP::UPW; ++ui) {
         gp.sa[ui] = gp.sb[ui] = zero4();
 #pragma unroll
-        for (int tb = 0; tb < NT; ++tb) gp.a[ui][tb] = gp.b[ui][tb] = zero4();
+        for (int tb = 0; tb < GP::NT; ++tb) gp.a[ui][tb] = gp.b[ui][tb] = zero4();
     }
+}
+
+// Adds the products over D columns of the K and Q tiles (row stride krs) to the wave's units;
+// the tiles may be a slice of the columns, so several calls accumulate the full inner product.
+// ROWSUMS: the row sums (sa, sb) as the operands times a ones matrix; without it the caller
+// has formed the normalisers elsewhere (dpfp_chunk with rho outputs).
+template <bool BF16, int C, bool ROWSUMS = true, int NW = 4>
+__device__ __forceinline__ void gp_accumulate(GPTiles<C, NW>& gp, const void* Kv, const void* Qv,
+                                              int krs, int D, int w, int l16, int g4) {
+    using GP = GPTiles<C, NW>;
+    constexpr int NQ = GP::NQ, UPW = GP::UPW;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-        const int u = w + 4 * ui;
+        const int u = w + NW * ui;
         if (u < 2 * NQ) {
             const bool isP = u >= NQ;
             const int q = isP ? u - NQ : u;
@@ -313,15 +321,22 @@ __device__ __forceinline__ void gp_compute(GPTiles<C>& gp, const void* Kv, const
     }
 }
 
+template <bool BF16, int C, bool ROWSUMS = true, int NW = 4>
+__device__ __forceinline__ void gp_compute(GPTiles<C, NW>& gp, const void* Kv, const void* Qv,
+                                           int krs, int D, int w, int l16, int g4) {
+    gp_zero(gp);
+    gp_accumulate<BF16, C, ROWSUMS, NW>(gp, Kv, Qv, krs, D, w, l16, g4);
+}
+
 // Normalisers 1 / (row sum + eps) of the unit's rows (G units: K rows, P units: Q rows).
-template <int C>
-__device__ __forceinline__ void gp_write_rho(const GPTiles<C>& gp, float* rhok, float* rhoq,
+template <int C, int NW>
+__device__ __forceinline__ void gp_write_rho(const GPTiles<C, NW>& gp, float* rhok, float* rhoq,
                                              int w, int l16, int g4) {
-    using GP = GPTiles<C>;
+    using GP = GPTiles<C, NW>;
     constexpr int NT = GP::NT, NQ = GP::NQ, UPW = GP::UPW;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-        const int u = w + 4 * ui;
+        const int u = w + NW * ui;
         if (u < 2 * NQ && l16 == 0) {
             const bool isP = u >= NQ;
             const int q = isP ? u - NQ : u;
@@ -378,15 +393,15 @@ __device__ __forceinline__ void gp_scale_unit(const f32x4 (&ta_)[C / 16], const 
 // Writes Ls = beta_t rho_t rho_s G[t][s] (s < t, fp32) and Ps = rho_q,t rho_k,s P[t][s]
 // (s <= t, operand type) for the tiles of this wave's units; tiles above the diagonal are not
 // written.
-template <bool BF16, int C>
-__device__ __forceinline__ void gp_scale(const GPTiles<C>& gp, const float* rhok,
+template <bool BF16, int C, int NW>
+__device__ __forceinline__ void gp_scale(const GPTiles<C, NW>& gp, const float* rhok,
                                          const float* rhoq, const float* betas, float* Ls,
                                          int lss, void* Pv, int pss, int w, int l16, int g4) {
-    using GP = GPTiles<C>;
+    using GP = GPTiles<C, NW>;
     constexpr int NQ = GP::NQ, UPW = GP::UPW;
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
-        const int u = w + 4 * ui;
+        const int u = w + NW * ui;
         if (u < 2 * NQ) {
             const bool isP = u >= NQ;
             const int q = isP ? u - NQ : u;

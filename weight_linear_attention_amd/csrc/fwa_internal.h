@@ -59,10 +59,12 @@ struct ChunkArgs {
     int BH, T, NC, d_k, d_v, nu, D;
     int DP, NDP;
     int krs, lss, pss, aps;
+    int ss;                      // row stride (elements) of the shift-sliced K and Q tiles
     int l_kr, l_qr, l_x, l_ls, l_ps, l_li, l_xv, l_small;
     // streaming kernel LDS layout (byte offsets): K and Q tiles, the raw-input slot (k rows,
     // then q rows at s_qoff and v columns at s_voff inside it), W^T copy, Z (then y) and U tiles
     int s_k, s_q, s_raw, s_qoff, s_voff, s_wt, s_z, s_u;
+    int s_y;                     // sliced streaming kernel: the chunk's y rows (bf16 [C][32])
 };
 
 struct ChunkPlan {
@@ -91,9 +93,16 @@ struct StreamPlan {
     int lds_prep;
     int lds_stream;
     int ndw;             // d-tiles of W^T per wave (of 8)
+    bool sliced_prep;    // prep with shift-sliced K and Q tiles (d_k = 64, nu <= 4)
     int64_t ws_bytes;
 };
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan);
+// Shift-sliced pieces (bf16, d_k = 64, nu <= 4): the prep kernel's LDS layout for chunk C (its
+// bytes, 0 if it does not fit), the chunk-128 plan, and the launches.
+int plan_prep_sliced(int C, ChunkArgs* a);
+bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
+hipError_t launch_prep_sliced(const StreamPlan& plan, hipStream_t stream);
+hipError_t launch_stream_c128(const StreamPlan& plan, hipStream_t stream);
 hipError_t launch_stream(const StreamPlan& plan, const void* q, const void* k, const void* v,
                          const void* bl, const float* W0, void* y, float* Wf, char* ws,
                          hipStream_t stream);

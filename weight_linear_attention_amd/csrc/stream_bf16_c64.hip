@@ -2,14 +2,26 @@
 // launches (prep kernel in compact mode, then the stream kernel).
 #include "stream_kernel.h"
 
+#include <cstdlib>
+#include <cstring>
+
 namespace fwa {
 
 static int align16s(int x) { return (x + 15) & ~15; }
 
 constexpr int kMaxLdsStream = 160 * 1024;
 
+// Chunk 64 runs the prep kernel with full K and Q tiles (compact mode) or, for d_k = 64 and
+// nu <= 4, its shift-sliced form (FWA_STREAM_PREP=full|sliced; default sliced), whose 52 KB of
+// LDS let three workgroups share a CU.  Chunk 128 is the shift-sliced path throughout.
+static bool want_sliced_prep() {
+    const char* s = std::getenv("FWA_STREAM_PREP");
+    return s == nullptr || std::strcmp(s, "full") != 0;
+}
+
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan) {
     const int D = 2 * d_k * nu;
+    if (bf16 && C == 128) return plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
     // bf16, chunk 64, 32-column pairs of d_v, D in whole 8-wave shares of 16-row tiles, and
     // rolls of at most 8 positions (the extended q rows hold 8 positions before 0)
     if (!bf16 || C != 64 || d_v % 32 != 0 || D % 128 != 0 || nu > 8) return false;
@@ -45,9 +57,17 @@ bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Stre
     a.s_u = off;
     off += 8 * 1024;
     if (off > kMaxLdsStream) return false;
-    plan->args = a;
     plan->C = C;
     plan->lds_prep = cp.lds_prep;
+    plan->sliced_prep = false;
+    if (d_k == 64 && nu <= 4 && want_sliced_prep()) {
+        const int lds = plan_prep_sliced(C, &a);
+        if (lds > 0) {
+            plan->lds_prep = lds;
+            plan->sliced_prep = true;
+        }
+    }
+    plan->args = a;
     plan->lds_stream = off;
     plan->ndw = D / 128;
     plan->ws_bytes = a.o_rq + NU * szR;
@@ -67,7 +87,10 @@ static hipError_t launch_stream_ndw(const StreamPlan& p, hipStream_t stream) {
 hipError_t launch_stream_c64(const StreamPlan& p, hipStream_t stream) {
     const ChunkArgs& a = p.args;
     const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
-    if (NU > 0) {
+    if (p.sliced_prep) {
+        hipError_t e = launch_prep_sliced(p, stream);
+        if (e != hipSuccess) return e;
+    } else if (NU > 0) {
         auto prep = delta_prep_kernel<true, 64, true>;
         hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prep), p.lds_prep);
         if (e != hipSuccess) return e;
@@ -95,6 +118,7 @@ hipError_t launch_stream(const StreamPlan& plan_in, const void* q, const void* k
     a.y = y;
     a.Wf = Wf;
     a.ws = ws;
+    if (p.C == 128) return launch_stream_c128(p, stream);
     if (p.C != 64) return hipErrorInvalidValue;
     return launch_stream_c64(p, stream);
 }

@@ -1,0 +1,536 @@
+// Shift-sliced streaming forward (bf16, d_k = 64): the compact preparation and the serial pass
+// over chunks with the K and Q tiles built one DPFP shift block at a time, so the on-chip
+// working set no longer grows with D.  This is what lets a chunk of 128 rows run at D = 384.
+//
+// The recurrence ("Fast Weights Transformer" guide, xdnf.cn/news/308600, sections
+// "FastWeightsAttention / update formula" and "... / module structure and source walkthrough")
+// is evaluated chunk by chunk with the chunked algebra derived from it.  For a chunk of C rows
+// starting from memory W (d_v x D), with raw DPFP tiles K, Q, normalisers rho_k, rho_q, beta =
+// sigmoid(beta_logit) and L = diag(beta) strict_lower(K~ K~^T) (K~ = diag(rho_k) K):
+//     A'' = (I + L)^-1 diag(beta),   P~ = lower_incl(Q~ K~^T)                (prep, all chunks)
+//     X = K W^T,  U = A'' (V - rho_k o X),  Y = rho_q o (Q W^T) + P~ U,
+//     W^T += K^T (rho_k o U)                                                 (stream, serial)
+//
+// Shift slices.  The DPFP columns of shift i (1..nu) are one block of 2 d_k = 128 internal
+// columns (the two halves of a position side by side, as in the full tiles), built from the
+// staged raw rows by per-lane tasks: (row, 8 positions) -> 16 columns, with the rolled partner
+// taken from a 16-entry window [8 positions before, the 8 positions] of the row, so no lane
+// exchange is needed.  Every contraction over D is a sum of per-slice contractions:
+//   prep:   G += K_i K_i^T and P += Q_i K_i^T, accumulated in MFMA registers over the slices;
+//   stream: X += K_i W_i^T and Q W^T += Q_i W_i^T over the slices, then the memory update
+//           W_i^T += K_i^T (rho_k o U) with each K_i built again (the update needs U, which
+//           needs all of X first).  DPFP is cheap VALU work next to keeping C x D tiles.
+// LDS holds one K and one Q slice (C x 136 bf16 each), never the full C x D tiles.
+#pragma once
+
+#include "chunk_tile.h"
+#include "chunked_kernels.h"
+#include "stream_kernel.h"
+
+namespace fwa {
+
+constexpr int kSliceDk = 64;                 // d_k of the sliced kernels: one shift = 128 columns
+constexpr int kSliceCols = 2 * kSliceDk;
+constexpr int kSliceThreads = 512;
+
+// One DPFP task restricted to shift I: positions j0 .. j0+7 of a staged row (a = k[j0..j0+7],
+// pv = the 8 positions before j0, cyclically), written as 16 consecutive slice columns at
+// out + 2 j0.  Position j's partner is relu([k, -k]) at (j - I) mod 2 d_k = +-k[(j - I) mod d_k],
+// negated when j < I (the index wraps into the [-k] half); window index 8 + e - I of [pv, a]
+// holds k[(j0 + e - I) mod d_k] for 1 <= I <= 8.  Returns the task's sum of products.
+template <int I>
+__device__ __forceinline__ float dpfp_task_shift(const float (&a)[8], const float (&pv)[8], int j0,
+                                                 u16* out) {
+    static_assert(I >= 1 && I <= 8, "the window holds rolls of at most 8 positions");
+    float f[16], sum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        constexpr int kOff = 8 - I;
+        const int m = kOff + e;                                  // compile-time window index
+        const float r = m >= 8 ? a[m - 8] : pv[m];
+        const float x = (j0 + e < I) ? -r : r;
+        f[2 * e] = relu_f(relu_f(a[e]) * x);
+        f[2 * e + 1] = relu_f(-(relu_f(-a[e]) * x));
+        sum += f[2 * e] + f[2 * e + 1];
+    }
+    store16(out + 2 * j0, f);
+    return sum;
+}
+
+// The shift-I slices of the C staged rows Xk (and Xq) ([C][64] bf16) into Ks (and Qs)
+// ([C][ss] bf16).  Task tau = tid + NTH p (p < NP) is (row tau / 8, group tau % 8); K rows come
+// first, then Q rows.  A row's eight tasks sit in eight adjacent lanes, and each thread keeps
+// the same tasks for every shift, so sums[p] accumulates the row partial sums over the slices.
+template <int C, bool WITH_Q, int I, int NP>
+__device__ __forceinline__ void dpfp_slice(const u16* Xk, const u16* Xq, u16* Ks, u16* Qs, int ss,
+                                           int tid, float (&sums)[NP]) {
+    static_assert(NP * kSliceThreads == (WITH_Q ? 2 : 1) * C * (kSliceDk / 8), "task split");
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int tau = tid + kSliceThreads * p;
+        const int jg = tau & 7, rt = tau >> 3;
+        const bool isq = WITH_Q && rt >= C;                      // uniform per wave
+        const int t = isq ? rt - C : rt;
+        const u16* row = (isq ? Xq : Xk) + t * kSliceDk;
+        u16* out = (isq ? Qs : Ks) + t * ss;
+        float a[8], pv[8];
+        load8_f32(row + 8 * jg, a);
+        load8_f32(row + 8 * ((jg + 7) & 7), pv);
+        sums[p] += dpfp_task_shift<I>(a, pv, 8 * jg, out);
+    }
+}
+
+template <int C, bool WITH_Q, int NP>
+__device__ __forceinline__ void dpfp_slice_any(int i, const u16* Xk, const u16* Xq, u16* Ks,
+                                               u16* Qs, int ss, int tid, float (&sums)[NP]) {
+    switch (i) {
+        case 1: dpfp_slice<C, WITH_Q, 1>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        case 2: dpfp_slice<C, WITH_Q, 2>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        case 3: dpfp_slice<C, WITH_Q, 3>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        default: dpfp_slice<C, WITH_Q, 4>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// prep (compact, sliced): one workgroup of 8 waves per chunk (b, h, n).  Writes, per chunk, the
+// A-operand blocks of A'' = (I + L)^-1 diag(beta) as a bf16 hi + lo pair (AH, AL; the pair's sum
+// carries the fp32 value to about 2^-17), the A-operand blocks of P~ (PA, zero above the
+// diagonal) and the normalisers rho_k, rho_q (RK, RQ).
+// LDS: phase 1 holds the raw k, q rows and one K and one Q slice; phase 2 (over it) L (fp32),
+// the diagonal-block inverses, and P~ followed by A'' hi / lo over it.
+template <int C, int NU>
+__global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(ChunkArgs a) {
+    constexpr int NT = C / 16, NTB = NT / 2, NW = kSliceThreads / 64;
+    constexpr int NP = 2 * C * (kSliceDk / 8) / kSliceThreads;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    u16* Xk = reinterpret_cast<u16*>(smem + a.l_x);          // [C][64] raw k rows
+    u16* Xq = Xk + C * kSliceDk;                              // [C][64] raw q rows
+    u16* Ks = reinterpret_cast<u16*>(smem + a.l_kr);          // [C][ss] K slice
+    u16* Qs = reinterpret_cast<u16*>(smem + a.l_qr);          // [C][ss] Q slice
+    float* Ls = reinterpret_cast<float*>(smem + a.l_ls);      // [C][lss] L      (phase 2)
+    float* Li = reinterpret_cast<float*>(smem + a.l_li);      // [C][20] inverses (phase 2)
+    u16* Ps = reinterpret_cast<u16*>(smem + a.l_ps);          // [C][pss] P~     (phase 2)
+    u16* Bh = reinterpret_cast<u16*>(smem + a.l_ps);          // [C][aps] A'' hi, lo (over P~)
+    u16* Bl = Bh + C * a.aps;
+    float* rhok = reinterpret_cast<float*>(smem + a.l_small);
+    float* rhoq = rhok + C;
+    float* betas = rhoq + C;
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int T = a.T, ss = a.ss, aps = a.aps;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, a.NC);
+    const int bh = bi.bh, n = static_cast<int>(bi.i);
+    const int64_t u = static_cast<int64_t>(bh) * a.NC + n;
+    const int t0 = n * C, Cc = min(C, T - t0);
+    const int64_t row0 = static_cast<int64_t>(bh) * T + t0;
+
+    // ---- stage the chunk's raw k and q rows (zeros past the sequence end) and beta
+    {
+        const uint4* kc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.k) + row0 * kSliceDk);
+        const uint4* qc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.q) + row0 * kSliceDk);
+#pragma unroll
+        for (int p = 0; p < C * 8 / kSliceThreads; ++p) {
+            const int e = tid + kSliceThreads * p;               // 16-byte unit, row e / 8
+            const bool ok = (e >> 3) < Cc;
+            const uint32_t m = ok ? 0xffffffffu : 0u;
+            const uint4 rk = kc[ok ? e : 0], rq = qc[ok ? e : 0];
+            reinterpret_cast<uint4*>(Xk)[e] = make_uint4(rk.x & m, rk.y & m, rk.z & m, rk.w & m);
+            reinterpret_cast<uint4*>(Xq)[e] = make_uint4(rq.x & m, rq.y & m, rq.z & m, rq.w & m);
+        }
+        if (tid < C)
+            betas[tid] = tid < Cc ? sigmoid_stable(bf16_bits_to_f32(static_cast<const u16*>(a.bl)[row0 + tid]))
+                                  : 0.0f;
+    }
+    lds_barrier();
+
+    // ---- G = K K^T and P = Q K^T over the shift slices; row sums from the DPFP tasks
+    GPTiles<C, NW> gp;
+    gp_zero(gp);
+    float sums[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) sums[p] = 0.0f;
+    // a rolled loop: unrolled, the compiler keeps every slice's task inputs in registers
+#pragma unroll 1
+    for (int s = 0; s < NU; ++s) {
+        dpfp_slice_any<C, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
+        lds_barrier();
+        gp_accumulate<true, C, false, NW>(gp, Ks, Qs, ss, kSliceCols, w, l16, g4);
+        lds_barrier();
+    }
+    // row sums over the row's eight adjacent lanes (lane ^ 1, lane ^ 2, then the mirror inside
+    // 8 lanes); the row's first lane writes rho = 1 / (sum + eps)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        float s = sums[p];
+        s += dpp_f32<0xB1>(s);
+        s += dpp_f32<0x4E>(s);
+        s += dpp_f32<0x141>(s);
+        const int tau = tid + kSliceThreads * p, rt = tau >> 3;
+        if ((tau & 7) == 0) (rt >= C ? rhoq + (rt - C) : rhok + rt)[0] = __builtin_amdgcn_rcpf(s + kDpfpEps);
+    }
+    lds_barrier();
+
+    gp_scale<true, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
+    lds_barrier();
+
+    // ---- diagonal-block inverses; write-out of the P~ blocks and the normalisers
+    if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
+    {
+        char* pa = a.ws + a.o_pa + u * (static_cast<int64_t>(C) * C * 2);
+        for (int e = tid; e < NT * NTB * 64; e += kSliceThreads) {
+            const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
+            const u16* src = Ps + (16 * ta + (lam & 15)) * a.pss + 32 * j + 4 * (lam >> 4);
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if (2 * j <= ta) {
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                val.x = lo.x;
+                val.y = lo.y;
+            }
+            if (2 * j + 1 <= ta) {
+                const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
+                val.z = hi.x;
+                val.w = hi.y;
+            }
+            *reinterpret_cast<uint4*>(pa + static_cast<int64_t>(e) * 16) = val;
+        }
+        if (tid < C) {
+            reinterpret_cast<float*>(a.ws + a.o_rk)[u * C + tid] = rhok[tid];
+            reinterpret_cast<float*>(a.ws + a.o_rq)[u * C + tid] = rhoq[tid];
+        }
+    }
+    lds_barrier();   // Li complete; P~ is dead (its space holds A'')
+
+    // ---- A = (I + L)^-1 by block columns (column block tb = w), stored as A'' = A diag(beta)
+    //      in bf16 hi + lo:  A[ta][tb] = -Li[ta] sum_{tb <= tc < ta} L[ta][tc] A[tc][tb]
+    if (w < NT) {
+        const int tb = w;
+        const float bsc = betas[16 * tb + l16];
+        f32x4 Ab[NT];
+#pragma unroll
+        for (int ta = 0; ta < NT; ++ta) {
+            f32x4 val = zero4();
+            if (ta == tb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = Li[(16 * ta + 4 * g4 + e) * kLiStride + l16];
+            } else if (ta > tb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int tc = 0; tc < NT; ++tc) {
+                    if (tc >= tb && tc < ta) {
+                        const float4 l4 = *reinterpret_cast<const float4*>(
+                            Ls + (16 * ta + l16) * a.lss + 16 * tc + 4 * g4);
+                        acc = mfma_f32_k4(l4.x, Ab[tc][0], acc);
+                        acc = mfma_f32_k4(l4.y, Ab[tc][1], acc);
+                        acc = mfma_f32_k4(l4.z, Ab[tc][2], acc);
+                        acc = mfma_f32_k4(l4.w, Ab[tc][3], acc);
+                    }
+                }
+                const float4 i4 = *reinterpret_cast<const float4*>(Li + (16 * ta + l16) * kLiStride + 4 * g4);
+                val = mfma_f32_k4(i4.x, acc[0], val);
+                val = mfma_f32_k4(i4.y, acc[1], val);
+                val = mfma_f32_k4(i4.z, acc[2], val);
+                val = mfma_f32_k4(i4.w, acc[3], val);
+                val = -val;
+            }
+            Ab[ta] = val;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int at = (16 * ta + 4 * g4 + e) * aps + 16 * tb + l16;
+                const float y = val[e] * bsc;
+                const u16 yh = f32_to_bf16_bits(y);
+                Bh[at] = yh;
+                Bl[at] = f32_to_bf16_bits(y - bf16_bits_to_f32(yh));
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- AH, AL: A-operand blocks (ta, j) of A'' hi and lo (slot (h, e) of lane l =
+    //      A''[16 ta + l % 16][16 (2 j + h) + 4 (l / 16) + e]); blocks above the diagonal are zero
+    {
+        char* ah = a.ws + a.o_ah + u * (static_cast<int64_t>(C) * C * 2);
+        char* al = a.ws + a.o_al + u * (static_cast<int64_t>(C) * C * 2);
+        for (int e = tid; e < NT * NTB * 64; e += kSliceThreads) {
+            const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
+            const int at = (16 * ta + (lam & 15)) * aps + 32 * j + 4 * (lam >> 4);
+            const uint2 h0 = *reinterpret_cast<const uint2*>(Bh + at);
+            const uint2 h1 = *reinterpret_cast<const uint2*>(Bh + at + 16);
+            const uint2 l0 = *reinterpret_cast<const uint2*>(Bl + at);
+            const uint2 l1 = *reinterpret_cast<const uint2*>(Bl + at + 16);
+            *reinterpret_cast<uint4*>(ah + static_cast<int64_t>(e) * 16) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            *reinterpret_cast<uint4*>(al + static_cast<int64_t>(e) * 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// stream (sliced, chunk 128): one workgroup of 8 waves per (b, h, 32 columns of d_v), serial over
+// the chunks.  The fp32 memory W^T (D x 32) lives in MFMA accumulators: wave w holds d-tile
+// 8 s + w of every shift slice s, both 16-column tiles.  Wave w owns row tile w of X, Q W^T, U
+// and Y (both column tiles).  Per chunk:
+//   B  for each slice s: build K_s, Q_s; X += K_s W_s^T, Q W^T += Q_s W_s^T (bf16 W^T copy in
+//      LDS, refreshed at the top of the chunk); then Z = V - rho_k o X (fp32, over the Q slice)
+//   C  U = A'' Z (A'' and Z as bf16 hi + lo pairs, 3 MFMAs per k-step), over the Q slice
+//   D  Y = rho_q o (Q W^T) + P~ U (bf16 rows to LDS); for each slice s: build K_s again and
+//      W_s^T += K_s^T (rho_k o U), K_s^T read by LDS transpose reads; then the next chunk's raw
+//      rows, loaded into registers at the top of the chunk, go to the raw slot.
+//   After the last barrier every thread stores 16 bytes of the chunk's y with a buffer store
+//   whose range check drops rows past the sequence end.
+// Every wave issues the same global loads and stores in every chunk with no branch around
+// them, so the compiler's in-order wait counts stay exact.
+template <int C, int NU>
+__global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(ChunkArgs a) {
+    static_assert(C == 128, "row tile w of 8 per wave");
+    constexpr int NT = C / 16, NTB = NT / 2;
+    constexpr int NPK = C * (kSliceDk / 8) / kSliceThreads;   // K-only DPFP tasks per thread
+    constexpr int NPQ = 2 * NPK;                              // K and Q
+    constexpr int RU = C * kSliceDk / 8 / kSliceThreads;     // 16-byte raw k units per thread
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_v = a.d_v, D = a.D, T = a.T, NC = a.NC, ss = a.ss;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, d_v / 32);
+    const int bh = bi.bh, cp = static_cast<int>(bi.i);
+    const int col0 = 32 * cp;
+
+    u16* Ks = reinterpret_cast<u16*>(smem + a.s_k);
+    u16* Qs = reinterpret_cast<u16*>(smem + a.s_q);
+    char* WT = smem + a.s_wt;                       // B blocks (jb, ct) of W^T, bf16
+    float* Zb = reinterpret_cast<float*>(smem + a.s_z);   // over the Q slice
+    float* Ub = reinterpret_cast<float*>(smem + a.s_u);   // over the Q slice
+    u16* Yb = reinterpret_cast<u16*>(smem + a.s_y);       // [C][32] bf16
+    char* sb = smem + a.s_raw;
+    const u16* Xk = reinterpret_cast<const u16*>(sb);
+    const u16* Xq = reinterpret_cast<const u16*>(sb + a.s_qoff);
+    const u16* Xv = reinterpret_cast<const u16*>(sb + a.s_voff);   // [C][32]
+    auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
+
+    // ---- memory tiles: d-tile 8 s + w, column tile ct
+    f32x4 Wst[NU][2];
+#pragma unroll
+    for (int s = 0; s < NU; ++s)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            Wst[s][ct] = zero4();
+            if (a.W0) {
+                // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+                const float* src = a.W0 + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
+                                   orig_col(16 * (8 * s + w) + 4 * g4, kSliceDk);
+                const float2 lo = *reinterpret_cast<const float2*>(src);
+                const float2 hi = *reinterpret_cast<const float2*>(src + kSliceDk);
+                Wst[s][ct] = f32x4{lo.x, hi.x, lo.y, hi.y};
+            }
+        }
+
+    // ---- raw inputs of a chunk: k and q rows ([C][64] bf16, RU 16-byte units per thread) and
+    //      the workgroup's 32 v columns ([C][32], one unit per thread).  A unit past the
+    //      sequence end reads unit 0 of the chunk (in range) and is zeroed by its mask.
+    const int64_t row0 = static_cast<int64_t>(bh) * T;
+    const uint4* kB = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.k) + row0 * kSliceDk);
+    const uint4* qB = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.q) + row0 * kSliceDk);
+    const u16* vB = static_cast<const u16*>(a.v) + row0 * d_v + col0;
+    uint4 rk[RU], rq[RU], rv;
+    uint32_t mk[RU], mv = 0u;
+    auto load_raw = [&](int n) {
+        const int t0 = n * C, Cn = min(C, T - t0);
+#pragma unroll
+        for (int p = 0; p < RU; ++p) {
+            const int e = tid + kSliceThreads * p;
+            const bool ok = (e >> 3) < Cn;
+            const int64_t o = static_cast<int64_t>(t0) * 8 + (ok ? e : 0);
+            rk[p] = kB[o];
+            rq[p] = qB[o];
+            mk[p] = ok ? 0xffffffffu : 0u;
+        }
+        const bool okv = (tid >> 2) < Cn;
+        rv = *reinterpret_cast<const uint4*>(vB + static_cast<int64_t>(t0 + (okv ? tid >> 2 : 0)) * d_v +
+                                             (okv ? 8 * (tid & 3) : 0));
+        mv = okv ? 0xffffffffu : 0u;
+    };
+    auto store_raw = [&]() {
+#pragma unroll
+        for (int p = 0; p < RU; ++p) {
+            const int e = tid + kSliceThreads * p;
+            const uint32_t m = mk[p];
+            reinterpret_cast<uint4*>(sb)[e] = make_uint4(rk[p].x & m, rk[p].y & m, rk[p].z & m, rk[p].w & m);
+            reinterpret_cast<uint4*>(sb + a.s_qoff)[e] = make_uint4(rq[p].x & m, rq[p].y & m, rq[p].z & m, rq[p].w & m);
+        }
+        reinterpret_cast<uint4*>(sb + a.s_voff)[tid] = make_uint4(rv.x & mv, rv.y & mv, rv.z & mv, rv.w & mv);
+    };
+
+    // ---- per-chunk results of the prep kernel: A'' blocks (w, j) hi and lo, P~ blocks (w, j),
+    //      rho_k of every row tile and rho_q of row tile w (accumulator row order)
+    uint4 ah[NTB], al[NTB], pa[NTB];
+    f32x4 rka[NT], rqv;
+    auto load_ws = [&](int n) {
+        const int64_t u = static_cast<int64_t>(bh) * NC + n;
+        const char* ahp = a.ws + a.o_ah + u * (C * C * 2);
+        const char* alp = a.ws + a.o_al + u * (C * C * 2);
+        const char* pap = a.ws + a.o_pa + u * (C * C * 2);
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, w * NTB + j, l));
+            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, w * NTB + j, l));
+            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, w * NTB + j, l));
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+            rka[tt] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rk) + u * C + 16 * tt + 4 * g4);
+        rqv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rq) + u * C + 16 * w + 4 * g4);
+    };
+
+    if (NC > 0) {
+        load_raw(0);
+        store_raw();
+    }
+    lds_barrier();
+
+    // y of this workgroup's columns as a buffer: offsets from (b, h, t = 0, col0); the range ends
+    // where row T would begin, so rows past the sequence end are dropped by the hardware
+    const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0), (T * d_v - col0) * 2,
+        kBufferWord3);
+    float unused_q[NPQ], unused_k[NPK];   // the serial pass takes rho from the prep; the task
+                                          // sums written here are dead and compiled away
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * C;
+        const int nn = n + 1 < NC ? n + 1 : n;          // the last chunk re-reads itself
+        load_ws(n);
+        load_raw(nn);
+
+        // ---- W^T copy (bf16 B blocks): wave w writes its d-tiles
+#pragma unroll
+        for (int s = 0; s < NU; ++s) {
+            const int dt = 8 * s + w;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                *reinterpret_cast<uint2*>(WT + (((dt >> 1) * 2 + ct) * 64 + l) * 16 + 8 * (dt & 1)) =
+                    make_uint2(pack_bf16x2(Wst[s][ct][0], Wst[s][ct][1]), pack_bf16x2(Wst[s][ct][2], Wst[s][ct][3]));
+        }
+
+        // ---- B: X = K W^T and Q W^T for row tile w, slice by slice
+        f32x4 xacc[2] = {zero4(), zero4()}, qacc[2] = {zero4(), zero4()};
+        const u16* kr = Ks + (16 * w + l16) * ss + 4 * g4;
+        const u16* qr = Qs + (16 * w + l16) * ss + 4 * g4;
+        auto opnd = [&](const u16* r, int kk) {
+            const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(r + 32 * kk);
+            const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(r + 32 * kk + 16);
+            return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+#pragma unroll
+        for (int s = 0; s < NU; ++s) {
+            dpfp_slice_any<C, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, unused_q);
+            lds_barrier();
+#pragma unroll
+            for (int kk = 0; kk < kSliceCols / 32; ++kk) {
+                const int jb = (kSliceCols / 32) * s + kk;
+                const bf16x8 ak = opnd(kr, kk), aq = opnd(qr, kk);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const bf16x8 wb = as_bf16x8(*reinterpret_cast<const uint4*>(WT + ((jb * 2 + ct) * 64 + l) * 16));
+                    xacc[ct] = mfma_bf16_k32(ak, wb, xacc[ct]);
+                    qacc[ct] = mfma_bf16_k32(aq, wb, qacc[ct]);
+                }
+            }
+            lds_barrier();
+        }
+        {
+            // Z = V - rho_k o X (rows 16 w + 4 g4 + e, columns 16 ct + l16), over the Q slice
+            const f32x4 rkc = rka[w];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xacc[ct][e] = bf16_bits_to_f32(Xv[(16 * w + 4 * g4 + e) * 32 + 16 * ct + l16]) - rkc[e] * xacc[ct][e];
+                *tile(Zb, w, ct) = xacc[ct];
+                qacc[ct] *= rqv;
+            }
+        }
+        lds_barrier();
+
+        // ---- C: U tiles (w, ct) = A'' Z
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 uacc = zero4();
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > w) break;                            // A'' is zero above the diagonal
+                const f32x4 z0 = *tile(Zb, 2 * j, ct), z1 = *tile(Zb, 2 * j + 1, ct);
+                const bf16x8 zh = as_bf16x8(pack_bf16x8(z0, z1));
+                const bf16x8 zl = as_bf16x8(bf16_lo_part(z0, z1));
+                uacc = mfma_bf16_k32(as_bf16x8(ah[j]), zh, uacc);
+                uacc = mfma_bf16_k32(as_bf16x8(ah[j]), zl, uacc);
+                uacc = mfma_bf16_k32(as_bf16x8(al[j]), zh, uacc);
+            }
+            *tile(Ub, w, ct) = uacc;
+        }
+        lds_barrier();
+
+        // ---- D: Y tiles (w, ct), then the memory update slice by slice
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 y = qacc[ct];
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > w) break;
+                const bf16x8 ub = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, ct), *tile(Ub, 2 * j + 1, ct)));
+                y = mfma_bf16_k32(as_bf16x8(pa[j]), ub, y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Yb[(16 * w + 4 * g4 + e) * 32 + 16 * ct + l16] = f32_to_bf16_bits(y[e]);
+        }
+        // B operands rho_k o U of rows 32 j .. 32 j + 31 (tiles 2 j, 2 j + 1)
+        bf16x8 ubk[NTB][2];
+#pragma unroll
+        for (int j = 0; j < NTB; ++j)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                ubk[j][ct] = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, ct) * rka[2 * j], *tile(Ub, 2 * j + 1, ct) * rka[2 * j + 1]));
+#pragma unroll
+        for (int s = 0; s < NU; ++s) {
+            // K_s again (the previous K slice is dead: its last reads were in phase B)
+            dpfp_slice_any<C, false>(s + 1, Xk, nullptr, Ks, nullptr, ss, tid, unused_k);
+            lds_barrier();
+            const u16* kt = Ks + (4 * g4 + (l16 >> 2)) * ss + 16 * w + 4 * (l16 & 3);
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                const u16* kc = kt + 32 * j * ss;
+                const bf16x4 c0 = lds_read_tr_b16x4(kc);
+                const bf16x4 c1 = lds_read_tr_b16x4(kc + 16 * ss);
+                const bf16x8 kta = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                Wst[s][0] = mfma_bf16_k32(kta, ubk[j][0], Wst[s][0]);
+                Wst[s][1] = mfma_bf16_k32(kta, ubk[j][1], Wst[s][1]);
+            }
+            if (s + 1 < NU) lds_barrier();                       // compile-time condition
+        }
+        // the raw slot's last reads were the K builds above, each followed by a barrier
+        store_raw();
+        lds_barrier();
+        // y rows of the chunk: 16 bytes per thread; rows past the sequence end fall outside the
+        // buffer's range and are dropped
+        {
+            const int t = tid >> 2, c8 = 8 * (tid & 3);
+            const uint4 v4 = *reinterpret_cast<const uint4*>(Yb + t * 32 + c8);
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{v4.x, v4.y, v4.z, v4.w}, yrsrc,
+                                                   ((t0 + t) * d_v + c8) * 2, 0, 0);
+        }
+    }
+
+    if (a.Wf) {
+#pragma unroll
+        for (int s = 0; s < NU; ++s)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
+                             orig_col(16 * (8 * s + w) + 4 * g4, kSliceDk);
+                *reinterpret_cast<float2*>(dst) = make_float2(Wst[s][ct][0], Wst[s][ct][2]);
+                *reinterpret_cast<float2*>(dst + kSliceDk) = make_float2(Wst[s][ct][1], Wst[s][ct][3]);
+            }
+    }
+}
+
+}  // namespace fwa

@@ -154,7 +154,8 @@ def _stream_workspace_formula(B, H, T, chunk):
     ((1, 8, 1024, 64, 64, 1, 64), "f32", "chunked"),      # 8 heads x 1024, D 128
     ((4, 8, 4096, 64, 64, 2, 64), "bf16", "chunked"),     # 32 heads x 4096, D 256
     ((8, 16, 16384, 64, 64, 3, 64), "bf16", "stream"),    # 128 heads x 16384: 7.6 GB chunked workspace
-    ((8, 16, 16384, 64, 16, 3, 64), "bf16", "fused"),     # d_v 16: no streaming plan
+    ((8, 16, 16384, 64, 16, 3, 64), "bf16", "stream"),    # d_v 16: 16-column sliced serial kernel
+    ((8, 16, 16384, 32, 16, 4, 64), "bf16", "fused"),     # d_k 32, d_v 16: no streaming plan
     ((8, 16, 16384, 64, 64, 3, 128), "bf16", "stream"),   # chunk 128: shift-sliced streaming
     ((8, 16, 16384, 64, 16, 3, 128), "bf16", "none"),     # d_v 16, chunk 128: nothing fits
     ((1, 1, 64, 16, 16, 1, 16), "f32", "fused"),          # chunk 16: fused only
@@ -202,7 +203,7 @@ def test_forward_info_env_override(monkeypatch):
         "stream", _stream_workspace_formula(4, 8, 4096, 64))
     for args in ((1, 8, 1024, 64, 64, 1, 64),                       # fp32
                  (1, 8, 1024, 64, 64, 1, 32, torch.bfloat16),       # chunk 32
-                 (1, 8, 1024, 64, 16, 1, 64, torch.bfloat16),       # d_v 16
+                 (1, 8, 1024, 32, 16, 2, 64, torch.bfloat16),       # d_k 32 with d_v 16
                  (1, 8, 1024, 32, 64, 3, 64, torch.bfloat16)):      # D 192
         with pytest.raises(fwa.FwaError) as e:
             fwa.delta_forward_info(*args)

@@ -108,6 +108,8 @@ FWD_CASES = [
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "H": 2, "T": 300, "chunk": 128, "nu": 1, "d_v": 32}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "H": 3, "T": 257, "chunk": 128, "nu": 4}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 2, "H": 1, "T": 45, "chunk": 128}),
+    # d_v 16 at chunk 64 (16-column sliced serial kernel)
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "H": 2, "T": 200, "d_v": 16}),
 ]
 
 
@@ -209,11 +211,12 @@ def test_forward_chunk_independence_and_determinism(monkeypatch):
         assert torch.equal(y2, outs[(p, 64)][0]) and torch.equal(W2, outs[(p, 64)][1])
 
 
-@pytest.mark.parametrize("prep", ["full", "sliced"])
-def test_stream_prep_variants_and_chunks(monkeypatch, prep):
-    """The streaming path with either prep kernel at chunk 64, and at chunk 128, against the
-    oracle and against each other; each is deterministic."""
+@pytest.mark.parametrize("kernel,prep", [("default", "full"), ("default", "sliced"), ("sliced", "sliced")])
+def test_stream_prep_variants_and_chunks(monkeypatch, kernel, prep):
+    """The streaming path with each serial kernel and prep kernel at chunk 64, and at chunk
+    128, against the oracle and against each other; each is deterministic."""
     monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
+    monkeypatch.setenv("FWA_STREAM_KERNEL", kernel)
     monkeypatch.setenv("FWA_STREAM_PREP", prep)
     w = workload("b4_h8_t4096_d64_nu2_bf16_carried", B=1, H=4, T=777, nu=3)
     inp = make_inputs(w)
@@ -223,7 +226,7 @@ def test_stream_prep_variants_and_chunks(monkeypatch, prep):
     for c in (64, 128):
         y, Wf = _forward(d, w.nu, c)
         ey, ew = normwise(to_f64(y), yr, 2), normwise(to_f64(Wf), Wr, 2)
-        log(f"  stream prep={prep} chunk={c}: y err {ey:.3e}  W_final err {ew:.3e}")
+        log(f"  stream kernel={kernel} prep={prep} chunk={c}: y err {ey:.3e}  W_final err {ew:.3e}")
         assert ey <= 2e-2 and ew <= 2e-2
         y2, W2 = _forward(d, w.nu, c)
         assert torch.equal(y, y2) and torch.equal(Wf, W2)

@@ -1,6 +1,6 @@
 """Parity of the forward over every chain-kernel configuration the chunked path's planner can
 pick (each D it accepts, both dtypes, chunks of 32 and 64), over every memory split and roll
-length of the streaming path, and over seeded random shapes on all implementations.  Same bars as test_gpu_parity: fp32 1e-4, bf16 2e-2 normwise per
+length of the streaming path, and over seeded random shapes (chunks 32, 64, 128) on all implementations.  Same bars as test_gpu_parity: fp32 1e-4, bf16 2e-2 normwise per
 (b, h) slice against the fp64 oracle."""
 import random
 
@@ -60,27 +60,35 @@ def test_chunked_every_chain_config(dt, D, C, monkeypatch):
     _run(w, "chunked", monkeypatch)
 
 
-# Streaming path (bf16, chunk 64, d_v in {32, 64}, D in {128, 256, 384}): each D gives a
-# different number of memory d-tiles per wave (1-3), each d_k a different roll window, nu up
-# to 8 the longest roll the extended q rows hold; T covers a lone partial chunk, an exact
-# chunk and ragged tails.  D = 512 (the prep kernel's working set exceeds LDS at chunk 64) and
-# nu > 8 are refused.
+# Streaming path at chunk 64 (bf16), with each serial kernel.  The full-tile kernel takes d_v
+# in {32, 64} and D in {128, 256, 384}: each D gives a different number of memory d-tiles per
+# wave (1-3), each d_k a different roll window, nu up to 8 the longest roll the extended q rows
+# hold.  The shift-sliced kernel (16-column workgroups) takes d_k = 64 with nu <= 4, so D up to
+# 512, and any d_v here; it is the fallback for d_k = 64 shapes the full-tile kernel does not
+# take, and FWA_STREAM_KERNEL=sliced forces it.  T covers a lone
+# partial chunk, an exact chunk and ragged tails.  Shapes neither kernel takes are refused.
 STREAM_CASES = [
     # (d_k, nu, d_v, B, H, T)
     (64, 1, 64, 1, 2, 203), (64, 2, 64, 2, 2, 64), (64, 3, 32, 1, 3, 17), (64, 4, 64, 1, 2, 140),
+    (64, 3, 16, 2, 1, 150), (64, 1, 16, 1, 1, 64),
     (32, 2, 64, 1, 2, 129), (32, 4, 32, 2, 1, 200), (32, 6, 64, 1, 1, 75), (16, 4, 64, 1, 2, 100),
     (16, 8, 32, 1, 2, 190), (16, 12, 64, 1, 1, 70),
 ]
 
 
+@pytest.mark.parametrize("kernel", ["default", "sliced"])
 @pytest.mark.parametrize("case", STREAM_CASES,
                          ids=[f"dk{c[0]}-nu{c[1]}-dv{c[2]}-T{c[5]}" for c in STREAM_CASES])
-def test_stream_every_split(case, monkeypatch):
+def test_stream_every_split(case, kernel, monkeypatch):
     d_k, nu, d_v, B, H, T = case
     w = workload("b4_h8_t4096_d64_nu2_bf16_carried", B=B, H=H, T=T, d_k=d_k, nu=nu, d_v=d_v,
                  chunk=64, w0_std=0.05, seed=9000 + d_k * 10 + nu)
     monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
-    if nu > 8 or 2 * d_k * nu > 384:
+    monkeypatch.setenv("FWA_STREAM_KERNEL", kernel)
+    sliced_ok = d_k == 64 and nu <= 4
+    full_ok = nu <= 8 and 2 * d_k * nu <= 384 and d_v % 32 == 0
+    # the default takes the full-tile kernel and falls back to the sliced one; "sliced" forces it
+    if not (sliced_ok if kernel == "sliced" else (full_ok or sliced_ok)):
         with pytest.raises(fwa.FwaError) as e:
             fwa.delta_forward_info(B, H, T, d_k, d_v, nu, 64, w.torch_dtype)
         assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
@@ -98,7 +106,7 @@ def _random_cases(n, seed):
         if 2 * d_k * nu > 512:
             continue
         dt = rng.choice(("f32", "bf16"))
-        C = rng.choice((32, 64))
+        C = rng.choice((32, 64, 128))
         B, H = rng.choice(((1, 1), (1, 3), (2, 4), (3, 8)))
         T = rng.randint(1, 300)
         w0 = rng.choice((None, 0.02))

@@ -94,15 +94,16 @@ struct StreamPlan {
     int lds_stream;
     int ndw;             // d-tiles of W^T per wave (of 8)
     bool sliced_prep;    // prep with shift-sliced K and Q tiles (d_k = 64, nu <= 4)
+    bool sliced_stream;  // serial kernel with shift-sliced K and Q tiles (chunk 64 or 128)
     int64_t ws_bytes;
 };
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan);
 // Shift-sliced pieces (bf16, d_k = 64, nu <= 4): the prep kernel's LDS layout for chunk C (its
-// bytes, 0 if it does not fit), the chunk-128 plan, and the launches.
+// bytes, 0 if it does not fit), the sliced plan (chunk 64 or 128), and the launches.
 int plan_prep_sliced(int C, ChunkArgs* a);
 bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
 hipError_t launch_prep_sliced(const StreamPlan& plan, hipStream_t stream);
-hipError_t launch_stream_c128(const StreamPlan& plan, hipStream_t stream);
+hipError_t launch_stream_sliced(const StreamPlan& plan, hipStream_t stream);
 hipError_t launch_stream(const StreamPlan& plan, const void* q, const void* k, const void* v,
                          const void* bl, const float* W0, void* y, float* Wf, char* ws,
                          hipStream_t stream);

@@ -11,23 +11,37 @@ static int align16s(int x) { return (x + 15) & ~15; }
 
 constexpr int kMaxLdsStream = 160 * 1024;
 
-// Chunk 64 runs the prep kernel with full K and Q tiles (compact mode) or, for d_k = 64 and
-// nu <= 4, its shift-sliced form (FWA_STREAM_PREP=full|sliced; default sliced), whose 52 KB of
-// LDS let three workgroups share a CU.  Chunk 128 is the shift-sliced path throughout.
-static bool want_sliced_prep() {
-    const char* s = std::getenv("FWA_STREAM_PREP");
-    return s == nullptr || std::strcmp(s, "full") != 0;
+// Which kernels the streaming path runs.  Chunk 128 takes the shift-sliced kernels (d_k = 64,
+// nu <= 4).  Chunk 64 takes the 32-column full-tile serial kernel, with the sliced prep for
+// d_k = 64 and nu <= 4 (unless FWA_STREAM_PREP=full); shapes that kernel does not take (d_v 16,
+// D 512) fall back to the sliced serial kernel with 16-column workgroups, which
+// FWA_STREAM_KERNEL=sliced also forces.  On the 8 x 16 x 16384 (D 384) forward the full-tile
+// kernel takes 1.45 ms and the sliced one 2.5 ms: the sliced one builds the DPFP tiles three
+// times per chunk and column group (K and Q, then K again) and is bound by that VALU work.
+static bool env_is(const char* name, const char* value) {
+    const char* s = std::getenv(name);
+    return s != nullptr && std::strcmp(s, value) == 0;
 }
 
+static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
+
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan) {
+    if (!bf16) return false;
+    if (C == 128 || (C == 64 && env_is("FWA_STREAM_KERNEL", "sliced")))
+        return plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
+    if (!plan_stream_full(BH, T, d_k, d_v, nu, C, plan))
+        return C == 64 && plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
+    return true;
+}
+
+static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan) {
     const int D = 2 * d_k * nu;
-    if (bf16 && C == 128) return plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
-    // bf16, chunk 64, 32-column pairs of d_v, D in whole 8-wave shares of 16-row tiles, and
-    // rolls of at most 8 positions (the extended q rows hold 8 positions before 0)
-    if (!bf16 || C != 64 || d_v % 32 != 0 || D % 128 != 0 || nu > 8) return false;
+    // chunk 64, 32-column pairs of d_v, D in whole 8-wave shares of 16-row tiles, and rolls of
+    // at most 8 positions (the extended q rows hold 8 positions before 0)
+    if (C != 64 || d_v % 32 != 0 || D % 128 != 0 || nu > 8) return false;
     if (d_k != 16 && d_k != 32 && d_k != 64) return false;
     ChunkPlan cp;
-    if (!plan_chunked(BH, T, d_k, d_v, nu, C, bf16, &cp)) return false;   // prep LDS layout
+    if (!plan_chunked(BH, T, d_k, d_v, nu, C, true, &cp)) return false;   // prep LDS layout
     ChunkArgs a = cp.args;
     const int64_t NU = static_cast<int64_t>(BH) * a.NC;
     const int64_t szCC = static_cast<int64_t>(C) * C * 2, szR = C * 4;
@@ -60,7 +74,8 @@ bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Stre
     plan->C = C;
     plan->lds_prep = cp.lds_prep;
     plan->sliced_prep = false;
-    if (d_k == 64 && nu <= 4 && want_sliced_prep()) {
+    plan->sliced_stream = false;
+    if (d_k == 64 && nu <= 4 && !env_is("FWA_STREAM_PREP", "full")) {
         const int lds = plan_prep_sliced(C, &a);
         if (lds > 0) {
             plan->lds_prep = lds;
@@ -118,7 +133,7 @@ hipError_t launch_stream(const StreamPlan& plan_in, const void* q, const void* k
     a.y = y;
     a.Wf = Wf;
     a.ws = ws;
-    if (p.C == 128) return launch_stream_c128(p, stream);
+    if (p.sliced_stream) return launch_stream_sliced(p, stream);
     if (p.C != 64) return hipErrorInvalidValue;
     return launch_stream_c64(p, stream);
 }

@@ -58,16 +58,16 @@ __device__ __forceinline__ float dpfp_task_shift(const float (&a)[8], const floa
 }
 
 // The shift-I slices of the C staged rows Xk (and Xq) ([C][64] bf16) into Ks (and Qs)
-// ([C][ss] bf16).  Task tau = tid + NTH p (p < NP) is (row tau / 8, group tau % 8); K rows come
+// ([C][ss] bf16), by NTH threads.  Task tau = tid + NTH p (p < NP) is (row tau / 8, group tau % 8); K rows come
 // first, then Q rows.  A row's eight tasks sit in eight adjacent lanes, and each thread keeps
 // the same tasks for every shift, so sums[p] accumulates the row partial sums over the slices.
-template <int C, bool WITH_Q, int I, int NP>
+template <int C, int NTH, bool WITH_Q, int I, int NP>
 __device__ __forceinline__ void dpfp_slice(const u16* Xk, const u16* Xq, u16* Ks, u16* Qs, int ss,
                                            int tid, float (&sums)[NP]) {
-    static_assert(NP * kSliceThreads == (WITH_Q ? 2 : 1) * C * (kSliceDk / 8), "task split");
+    static_assert(NP * NTH == (WITH_Q ? 2 : 1) * C * (kSliceDk / 8), "task split");
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const int tau = tid + kSliceThreads * p;
+        const int tau = tid + NTH * p;
         const int jg = tau & 7, rt = tau >> 3;
         const bool isq = WITH_Q && rt >= C;                      // uniform per wave
         const int t = isq ? rt - C : rt;
@@ -80,14 +80,14 @@ __device__ __forceinline__ void dpfp_slice(const u16* Xk, const u16* Xq, u16* Ks
     }
 }
 
-template <int C, bool WITH_Q, int NP>
+template <int C, int NTH, bool WITH_Q, int NP>
 __device__ __forceinline__ void dpfp_slice_any(int i, const u16* Xk, const u16* Xq, u16* Ks,
                                                u16* Qs, int ss, int tid, float (&sums)[NP]) {
     switch (i) {
-        case 1: dpfp_slice<C, WITH_Q, 1>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
-        case 2: dpfp_slice<C, WITH_Q, 2>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
-        case 3: dpfp_slice<C, WITH_Q, 3>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
-        default: dpfp_slice<C, WITH_Q, 4>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        case 1: dpfp_slice<C, NTH, WITH_Q, 1>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        case 2: dpfp_slice<C, NTH, WITH_Q, 2>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        case 3: dpfp_slice<C, NTH, WITH_Q, 3>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
+        default: dpfp_slice<C, NTH, WITH_Q, 4>(Xk, Xq, Ks, Qs, ss, tid, sums); break;
     }
 }
 
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
     // a rolled loop: unrolled, the compiler keeps every slice's task inputs in registers
 #pragma unroll 1
     for (int s = 0; s < NU; ++s) {
-        dpfp_slice_any<C, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
+        dpfp_slice_any<C, kSliceThreads, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
         lds_barrier();
         gp_accumulate<true, C, false, NW>(gp, Ks, Qs, ss, kSliceCols, w, l16, g4);
         lds_barrier();
@@ -266,99 +266,116 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
 }
 
 // ------------------------------------------------------------------------------------------
-// stream (sliced, chunk 128): one workgroup of 8 waves per (b, h, 32 columns of d_v), serial over
-// the chunks.  The fp32 memory W^T (D x 32) lives in MFMA accumulators: wave w holds d-tile
-// 8 s + w of every shift slice s, both 16-column tiles.  Wave w owns row tile w of X, Q W^T, U
-// and Y (both column tiles).  Per chunk:
+// stream (sliced): one workgroup of NW = C / 16 waves per (b, h, 16 NCT columns of d_v), serial
+// over the chunks: chunk 128 with 8 waves and 32 columns, or chunk 64 with 4 waves and 16
+// columns (67.5 KB of LDS at D = 384, so two workgroups share a CU and overlap their phases).
+// The fp32 memory W^T (D x 16 NCT) lives in MFMA accumulators: wave w holds d-tiles
+// w + NW r (r < 8 / NW) of every shift slice s (global d-tile 8 s + w + NW r), all column
+// tiles.  Wave w owns row tile w of X, Q W^T, U and Y.  Per chunk:
 //   B  for each slice s: build K_s, Q_s; X += K_s W_s^T, Q W^T += Q_s W_s^T (bf16 W^T copy in
 //      LDS, refreshed at the top of the chunk); then Z = V - rho_k o X (fp32, over the Q slice)
 //   C  U = A'' Z (A'' and Z as bf16 hi + lo pairs, 3 MFMAs per k-step), over the Q slice
 //   D  Y = rho_q o (Q W^T) + P~ U (bf16 rows to LDS); for each slice s: build K_s again and
 //      W_s^T += K_s^T (rho_k o U), K_s^T read by LDS transpose reads; then the next chunk's raw
 //      rows, loaded into registers at the top of the chunk, go to the raw slot.
-//   After the last barrier every thread stores 16 bytes of the chunk's y with a buffer store
-//   whose range check drops rows past the sequence end.
+//   After the last barrier every thread stores 8 NCT bytes of the chunk's y with a buffer
+//   store whose range check drops rows past the sequence end.
 // Every wave issues the same global loads and stores in every chunk with no branch around
-// them, so the compiler's in-order wait counts stay exact.
-template <int C, int NU>
-__global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(ChunkArgs a) {
-    static_assert(C == 128, "row tile w of 8 per wave");
-    constexpr int NT = C / 16, NTB = NT / 2;
-    constexpr int NPK = C * (kSliceDk / 8) / kSliceThreads;   // K-only DPFP tasks per thread
-    constexpr int NPQ = 2 * NPK;                              // K and Q
-    constexpr int RU = C * kSliceDk / 8 / kSliceThreads;     // 16-byte raw k units per thread
+// them, so the compiler's in-order wait counts stay exact.  Per thread, every chunk moves 32
+// bytes of raw k and q rows, 8 NCT bytes of v and 8 NCT bytes of y for either shape.
+template <int C, int NU, int NCT>
+__global__ __launch_bounds__(4 * C, 512 / (4 * C)) void delta_stream_sliced_kernel(ChunkArgs a) {
+    constexpr int NW = C / 16, NTH = 64 * NW, NT = C / 16, NTB = NT / 2;
+    constexpr int NR = 8 / NW;                               // d-tiles per wave and slice
+    constexpr int NPK = C * (kSliceDk / 8) / NTH;            // K-only DPFP tasks per thread
+    constexpr int NPQ = 2 * NPK;                             // K and Q
+    constexpr int RU = C * kSliceDk / 8 / NTH;               // 16-byte raw k units per thread
+    constexpr int CW = 16 * NCT;                             // columns of the workgroup
+    static_assert(NW == 4 || NW == 8, "chunk 64 or 128");
+    static_assert(C * CW * 2 == NTH * 8 * NCT, "8 NCT bytes of v and y per thread");
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    using VU = std::conditional_t<NCT == 1, uint2, uint4>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = l & 15, g4 = l >> 4;
     const int d_v = a.d_v, D = a.D, T = a.T, NC = a.NC, ss = a.ss;
-    const BhIndex bi = xcd_local(blockIdx.x, a.BH, d_v / 32);
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, d_v / CW);
     const int bh = bi.bh, cp = static_cast<int>(bi.i);
-    const int col0 = 32 * cp;
+    const int col0 = CW * cp;
 
     u16* Ks = reinterpret_cast<u16*>(smem + a.s_k);
     u16* Qs = reinterpret_cast<u16*>(smem + a.s_q);
     char* WT = smem + a.s_wt;                       // B blocks (jb, ct) of W^T, bf16
     float* Zb = reinterpret_cast<float*>(smem + a.s_z);   // over the Q slice
     float* Ub = reinterpret_cast<float*>(smem + a.s_u);   // over the Q slice
-    u16* Yb = reinterpret_cast<u16*>(smem + a.s_y);       // [C][32] bf16
+    u16* Yb = reinterpret_cast<u16*>(smem + a.s_y);       // [C][CW] bf16
     char* sb = smem + a.s_raw;
     const u16* Xk = reinterpret_cast<const u16*>(sb);
     const u16* Xq = reinterpret_cast<const u16*>(sb + a.s_qoff);
-    const u16* Xv = reinterpret_cast<const u16*>(sb + a.s_voff);   // [C][32]
-    auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
+    const u16* Xv = reinterpret_cast<const u16*>(sb + a.s_voff);   // [C][CW]
+    auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * NCT + c) * 64 + l) * 4); };
+    auto wblk = [&](int jb, int ct) { return WT + ((jb * NCT + ct) * 64 + l) * 16; };
 
-    // ---- memory tiles: d-tile 8 s + w, column tile ct
-    f32x4 Wst[NU][2];
+    // ---- memory tiles: d-tile 8 s + w + NW r, column tile ct
+    f32x4 Wst[NU][NR][NCT];
 #pragma unroll
     for (int s = 0; s < NU; ++s)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            Wst[s][ct] = zero4();
-            if (a.W0) {
-                // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
-                const float* src = a.W0 + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
-                                   orig_col(16 * (8 * s + w) + 4 * g4, kSliceDk);
-                const float2 lo = *reinterpret_cast<const float2*>(src);
-                const float2 hi = *reinterpret_cast<const float2*>(src + kSliceDk);
-                Wst[s][ct] = f32x4{lo.x, hi.x, lo.y, hi.y};
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                Wst[s][r][ct] = zero4();
+                if (a.W0) {
+                    // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+                    const float* src = a.W0 + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
+                                       orig_col(16 * (8 * s + w + NW * r) + 4 * g4, kSliceDk);
+                    const float2 lo = *reinterpret_cast<const float2*>(src);
+                    const float2 hi = *reinterpret_cast<const float2*>(src + kSliceDk);
+                    Wst[s][r][ct] = f32x4{lo.x, hi.x, lo.y, hi.y};
+                }
             }
-        }
 
     // ---- raw inputs of a chunk: k and q rows ([C][64] bf16, RU 16-byte units per thread) and
-    //      the workgroup's 32 v columns ([C][32], one unit per thread).  A unit past the
+    //      the workgroup's CW v columns ([C][CW], 8 NCT bytes per thread).  A unit past the
     //      sequence end reads unit 0 of the chunk (in range) and is zeroed by its mask.
     const int64_t row0 = static_cast<int64_t>(bh) * T;
     const uint4* kB = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.k) + row0 * kSliceDk);
     const uint4* qB = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.q) + row0 * kSliceDk);
     const u16* vB = static_cast<const u16*>(a.v) + row0 * d_v + col0;
-    uint4 rk[RU], rq[RU], rv;
+    constexpr int VPR = CW / (4 * NCT);                      // v units per row (4 NCT columns each)
+    uint4 rk[RU], rq[RU];
+    VU rv;
     uint32_t mk[RU], mv = 0u;
     auto load_raw = [&](int n) {
         const int t0 = n * C, Cn = min(C, T - t0);
 #pragma unroll
         for (int p = 0; p < RU; ++p) {
-            const int e = tid + kSliceThreads * p;
+            const int e = tid + NTH * p;
             const bool ok = (e >> 3) < Cn;
             const int64_t o = static_cast<int64_t>(t0) * 8 + (ok ? e : 0);
             rk[p] = kB[o];
             rq[p] = qB[o];
             mk[p] = ok ? 0xffffffffu : 0u;
         }
-        const bool okv = (tid >> 2) < Cn;
-        rv = *reinterpret_cast<const uint4*>(vB + static_cast<int64_t>(t0 + (okv ? tid >> 2 : 0)) * d_v +
-                                             (okv ? 8 * (tid & 3) : 0));
+        const bool okv = tid / VPR < Cn;
+        rv = *reinterpret_cast<const VU*>(vB + static_cast<int64_t>(t0 + (okv ? tid / VPR : 0)) * d_v +
+                                          (okv ? 4 * NCT * (tid % VPR) : 0));
         mv = okv ? 0xffffffffu : 0u;
     };
     auto store_raw = [&]() {
 #pragma unroll
         for (int p = 0; p < RU; ++p) {
-            const int e = tid + kSliceThreads * p;
+            const int e = tid + NTH * p;
             const uint32_t m = mk[p];
             reinterpret_cast<uint4*>(sb)[e] = make_uint4(rk[p].x & m, rk[p].y & m, rk[p].z & m, rk[p].w & m);
             reinterpret_cast<uint4*>(sb + a.s_qoff)[e] = make_uint4(rq[p].x & m, rq[p].y & m, rq[p].z & m, rq[p].w & m);
         }
-        reinterpret_cast<uint4*>(sb + a.s_voff)[tid] = make_uint4(rv.x & mv, rv.y & mv, rv.z & mv, rv.w & mv);
+        if constexpr (NCT == 1)
+            reinterpret_cast<uint2*>(sb + a.s_voff)[tid] = make_uint2(rv.x & mv, rv.y & mv);
+        else
+            reinterpret_cast<uint4*>(sb + a.s_voff)[tid] = make_uint4(rv.x & mv, rv.y & mv, rv.z & mv, rv.w & mv);
     };
 
     // ---- per-chunk results of the prep kernel: A'' blocks (w, j) hi and lo, P~ blocks (w, j),
@@ -403,16 +420,21 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
 
         // ---- W^T copy (bf16 B blocks): wave w writes its d-tiles
 #pragma unroll
-        for (int s = 0; s < NU; ++s) {
-            const int dt = 8 * s + w;
+        for (int s = 0; s < NU; ++s)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-                *reinterpret_cast<uint2*>(WT + (((dt >> 1) * 2 + ct) * 64 + l) * 16 + 8 * (dt & 1)) =
-                    make_uint2(pack_bf16x2(Wst[s][ct][0], Wst[s][ct][1]), pack_bf16x2(Wst[s][ct][2], Wst[s][ct][3]));
-        }
+            for (int r = 0; r < NR; ++r) {
+                const int dt = 8 * s + w + NW * r;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    *reinterpret_cast<uint2*>(wblk(dt >> 1, ct) + 8 * (dt & 1)) =
+                        make_uint2(pack_bf16x2(Wst[s][r][ct][0], Wst[s][r][ct][1]),
+                                   pack_bf16x2(Wst[s][r][ct][2], Wst[s][r][ct][3]));
+            }
 
         // ---- B: X = K W^T and Q W^T for row tile w, slice by slice
-        f32x4 xacc[2] = {zero4(), zero4()}, qacc[2] = {zero4(), zero4()};
+        f32x4 xacc[NCT], qacc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) xacc[ct] = qacc[ct] = zero4();
         const u16* kr = Ks + (16 * w + l16) * ss + 4 * g4;
         const u16* qr = Qs + (16 * w + l16) * ss + 4 * g4;
         auto opnd = [&](const u16* r, int kk) {
@@ -422,15 +444,15 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
         };
 #pragma unroll
         for (int s = 0; s < NU; ++s) {
-            dpfp_slice_any<C, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, unused_q);
+            dpfp_slice_any<C, NTH, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, unused_q);
             lds_barrier();
 #pragma unroll
             for (int kk = 0; kk < kSliceCols / 32; ++kk) {
                 const int jb = (kSliceCols / 32) * s + kk;
                 const bf16x8 ak = opnd(kr, kk), aq = opnd(qr, kk);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const bf16x8 wb = as_bf16x8(*reinterpret_cast<const uint4*>(WT + ((jb * 2 + ct) * 64 + l) * 16));
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const bf16x8 wb = as_bf16x8(*reinterpret_cast<const uint4*>(wblk(jb, ct)));
                     xacc[ct] = mfma_bf16_k32(ak, wb, xacc[ct]);
                     qacc[ct] = mfma_bf16_k32(aq, wb, qacc[ct]);
                 }
@@ -441,10 +463,10 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
             // Z = V - rho_k o X (rows 16 w + 4 g4 + e, columns 16 ct + l16), over the Q slice
             const f32x4 rkc = rka[w];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    xacc[ct][e] = bf16_bits_to_f32(Xv[(16 * w + 4 * g4 + e) * 32 + 16 * ct + l16]) - rkc[e] * xacc[ct][e];
+                    xacc[ct][e] = bf16_bits_to_f32(Xv[(16 * w + 4 * g4 + e) * CW + 16 * ct + l16]) - rkc[e] * xacc[ct][e];
                 *tile(Zb, w, ct) = xacc[ct];
                 qacc[ct] *= rqv;
             }
@@ -453,7 +475,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
 
         // ---- C: U tiles (w, ct) = A'' Z
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             f32x4 uacc = zero4();
 #pragma unroll
             for (int j = 0; j < NTB; ++j) {
@@ -471,7 +493,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
 
         // ---- D: Y tiles (w, ct), then the memory update slice by slice
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             f32x4 y = qacc[ct];
 #pragma unroll
             for (int j = 0; j < NTB; ++j) {
@@ -480,43 +502,48 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
                 y = mfma_bf16_k32(as_bf16x8(pa[j]), ub, y);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Yb[(16 * w + 4 * g4 + e) * 32 + 16 * ct + l16] = f32_to_bf16_bits(y[e]);
+            for (int e = 0; e < 4; ++e) Yb[(16 * w + 4 * g4 + e) * CW + 16 * ct + l16] = f32_to_bf16_bits(y[e]);
         }
         // B operands rho_k o U of rows 32 j .. 32 j + 31 (tiles 2 j, 2 j + 1)
-        bf16x8 ubk[NTB][2];
+        bf16x8 ubk[NTB][NCT];
 #pragma unroll
         for (int j = 0; j < NTB; ++j)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
                 ubk[j][ct] = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, ct) * rka[2 * j], *tile(Ub, 2 * j + 1, ct) * rka[2 * j + 1]));
 #pragma unroll
         for (int s = 0; s < NU; ++s) {
             // K_s again (the previous K slice is dead: its last reads were in phase B)
-            dpfp_slice_any<C, false>(s + 1, Xk, nullptr, Ks, nullptr, ss, tid, unused_k);
+            dpfp_slice_any<C, NTH, false>(s + 1, Xk, nullptr, Ks, nullptr, ss, tid, unused_k);
             lds_barrier();
-            const u16* kt = Ks + (4 * g4 + (l16 >> 2)) * ss + 16 * w + 4 * (l16 & 3);
 #pragma unroll
-            for (int j = 0; j < NTB; ++j) {
-                const u16* kc = kt + 32 * j * ss;
-                const bf16x4 c0 = lds_read_tr_b16x4(kc);
-                const bf16x4 c1 = lds_read_tr_b16x4(kc + 16 * ss);
-                const bf16x8 kta = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-                Wst[s][0] = mfma_bf16_k32(kta, ubk[j][0], Wst[s][0]);
-                Wst[s][1] = mfma_bf16_k32(kta, ubk[j][1], Wst[s][1]);
+            for (int r = 0; r < NR; ++r) {
+                const u16* kt = Ks + (4 * g4 + (l16 >> 2)) * ss + 16 * (w + NW * r) + 4 * (l16 & 3);
+#pragma unroll
+                for (int j = 0; j < NTB; ++j) {
+                    const u16* kc = kt + 32 * j * ss;
+                    const bf16x4 c0 = lds_read_tr_b16x4(kc);
+                    const bf16x4 c1 = lds_read_tr_b16x4(kc + 16 * ss);
+                    const bf16x8 kta = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) Wst[s][r][ct] = mfma_bf16_k32(kta, ubk[j][ct], Wst[s][r][ct]);
+                }
             }
             if (s + 1 < NU) lds_barrier();                       // compile-time condition
         }
         // the raw slot's last reads were the K builds above, each followed by a barrier
         store_raw();
         lds_barrier();
-        // y rows of the chunk: 16 bytes per thread; rows past the sequence end fall outside the
-        // buffer's range and are dropped
+        // y rows of the chunk: 8 NCT bytes per thread; rows past the sequence end fall outside
+        // the buffer's range and are dropped
         {
-            const int t = tid >> 2, c8 = 8 * (tid & 3);
-            const uint4 v4 = *reinterpret_cast<const uint4*>(Yb + t * 32 + c8);
-            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{v4.x, v4.y, v4.z, v4.w}, yrsrc,
-                                                   ((t0 + t) * d_v + c8) * 2, 0, 0);
+            const int t = tid / VPR, c4 = 4 * NCT * (tid % VPR);
+            const VU v4 = *reinterpret_cast<const VU*>(Yb + t * CW + c4);
+            if constexpr (NCT == 1)
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{v4.x, v4.y}, yrsrc, ((t0 + t) * d_v + c4) * 2, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{v4.x, v4.y, v4.z, v4.w}, yrsrc,
+                                                       ((t0 + t) * d_v + c4) * 2, 0, 0);
         }
     }
 
@@ -524,12 +551,14 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_stream_sliced_kernel(C
 #pragma unroll
         for (int s = 0; s < NU; ++s)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
-                             orig_col(16 * (8 * s + w) + 4 * g4, kSliceDk);
-                *reinterpret_cast<float2*>(dst) = make_float2(Wst[s][ct][0], Wst[s][ct][2]);
-                *reinterpret_cast<float2*>(dst + kSliceDk) = make_float2(Wst[s][ct][1], Wst[s][ct][3]);
-            }
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + col0 + 16 * ct + l16) * D +
+                                 orig_col(16 * (8 * s + w + NW * r) + 4 * g4, kSliceDk);
+                    *reinterpret_cast<float2*>(dst) = make_float2(Wst[s][r][ct][0], Wst[s][r][ct][2]);
+                    *reinterpret_cast<float2*>(dst + kSliceDk) = make_float2(Wst[s][r][ct][1], Wst[s][r][ct][3]);
+                }
     }
 }
 

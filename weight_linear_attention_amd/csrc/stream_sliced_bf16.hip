@@ -32,7 +32,9 @@ int plan_prep_sliced(int C, ChunkArgs* a) {
 
 bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan) {
     const int D = 2 * d_k * nu;
-    if (d_k != kSliceDk || nu < 1 || nu > 4 || d_v % 32 != 0 || C != 128) return false;
+    if (d_k != kSliceDk || nu < 1 || nu > 4 || (C != 64 && C != 128)) return false;
+    const int NCT = C / 64, CW = 16 * NCT;          // column tiles and columns per workgroup
+    if (d_v % CW != 0) return false;
     // the y buffer's byte offsets (up to the last chunk's padded rows) fit 32 bits
     if ((static_cast<int64_t>(T) + C) * d_v * 2 >= (int64_t(1) << 32)) return false;
     ChunkArgs a = {};
@@ -52,18 +54,18 @@ bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPl
     a.s_raw = off;
     a.s_qoff = C * kSliceDk * 2;
     a.s_voff = 2 * C * kSliceDk * 2;
-    off = align16v(a.s_voff + C * 32 * 2);
+    off = align16v(a.s_voff + C * CW * 2);
     a.s_wt = off;
-    off += (D / 32) * 2 * 1024;
+    off += (D / 32) * NCT * 1024;
     a.s_k = off;
     off = align16v(off + C * a.ss * 2);
     a.s_q = off;
     a.s_z = off;
-    a.s_u = off + 16 * 1024;
-    const int qb = C * a.ss * 2;
-    off = align16v(off + (qb > 32 * 1024 ? qb : 32 * 1024));
+    a.s_u = off + C * CW * 4;
+    const int qb = C * a.ss * 2, zu = 2 * C * CW * 4;
+    off = align16v(off + (qb > zu ? qb : zu));
     a.s_y = off;
-    off += C * 32 * 2;
+    off += C * CW * 2;
     if (off > kMaxLdsSliced) return false;
     a.BH = BH;
     a.T = T;
@@ -78,6 +80,7 @@ bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPl
     plan->lds_stream = off;
     plan->ndw = nu;
     plan->sliced_prep = true;
+    plan->sliced_stream = true;
     plan->ws_bytes = a.o_rq + NU * szR;
     return true;
 }
@@ -115,26 +118,34 @@ hipError_t launch_prep_sliced(const StreamPlan& p, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <int NU>
+template <int C, int NU>
 static hipError_t launch_stream_sliced_nu(const StreamPlan& p, hipStream_t stream) {
-    auto kern = delta_stream_sliced_kernel<128, NU>;
+    constexpr int NCT = C / 64;
+    auto kern = delta_stream_sliced_kernel<C, NU, NCT>;
     hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_stream);
     if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / 32)));
-    hipLaunchKernelGGL(kern, grid, dim3(kSliceThreads), p.lds_stream, stream, p.args);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / (16 * NCT))));
+    hipLaunchKernelGGL(kern, grid, dim3(4 * C), p.lds_stream, stream, p.args);
     return hipGetLastError();
 }
 
-hipError_t launch_stream_c128(const StreamPlan& p, hipStream_t stream) {
-    hipError_t e = launch_prep_sliced(p, stream);
-    if (e != hipSuccess) return e;
+template <int C>
+static hipError_t launch_stream_sliced_c(const StreamPlan& p, hipStream_t stream) {
     switch (p.args.nu) {
-        case 1: return launch_stream_sliced_nu<1>(p, stream);
-        case 2: return launch_stream_sliced_nu<2>(p, stream);
-        case 3: return launch_stream_sliced_nu<3>(p, stream);
-        case 4: return launch_stream_sliced_nu<4>(p, stream);
+        case 1: return launch_stream_sliced_nu<C, 1>(p, stream);
+        case 2: return launch_stream_sliced_nu<C, 2>(p, stream);
+        case 3: return launch_stream_sliced_nu<C, 3>(p, stream);
+        case 4: return launch_stream_sliced_nu<C, 4>(p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_stream_sliced(const StreamPlan& p, hipStream_t stream) {
+    hipError_t e = launch_prep_sliced(p, stream);
+    if (e != hipSuccess) return e;
+    if (p.C == 64) return launch_stream_sliced_c<64>(p, stream);
+    if (p.C == 128) return launch_stream_sliced_c<128>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace fwa

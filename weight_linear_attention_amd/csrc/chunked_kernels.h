@@ -51,6 +51,46 @@ __device__ __forceinline__ uint4 pack_bf16x8(const f32x4& lo, const f32x4& hi) {
                       pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
 }
 
+// The residuals x - bf16(x) of eight fp32 values, rounded to bf16: with pack_bf16x8 (the
+// rounded values) a hi + lo pair whose sum carries each value to about 2^-16 relative.
+__device__ __forceinline__ uint4 bf16_lo_part(const f32x4& x0, const f32x4& x1) {
+    f32x4 r0, r1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r0[e] = x0[e] - static_cast<float>(static_cast<__bf16>(x0[e]));
+        r1[e] = x1[e] - static_cast<float>(static_cast<__bf16>(x1[e]));
+    }
+    return pack_bf16x8(r0, r1);
+}
+
+// Split fp32 operand format.  An fp32 operand block pair (k-blocks 2 j', 2 j' + 1 of 16 each,
+// lane l slot e) is stored instead as a bf16 hi block and a lo block, each in the register layout
+// of one 32-deep bf16 MFMA operand: slot (h, e) of the hi block holds bf16(x) for k-block
+// 2 j' + h, slot e, and the lo block bf16(x - bf16(x)).  The sum carries x to about 2^-16
+// relative, and three bf16 MFMAs (hi hi + hi lo + lo hi; the lo lo term is below the split's own
+// error) replace eight fp32 ones: a 32-deep k-step costs 48 cycles instead of 256.  A writer of
+// one fp32 tile (4 values per lane) fills 8 bytes of each block at offset 8 (k-block & 1).
+__device__ __forceinline__ uint2 pack_bf16x4(const f32x4& x) {
+    return make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+}
+__device__ __forceinline__ uint2 bf16_lo_part4(const f32x4& x) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = x[e] - static_cast<float>(static_cast<__bf16>(x[e]));
+    return pack_bf16x4(r);
+}
+// Lane l's 16 bytes of split block pair (hi at `pair_lane`, lo 1 KiB after it) for k-block kb.
+__device__ __forceinline__ void store_split(char* pair_lane, int kb, const f32x4& x) {
+    *reinterpret_cast<uint2*>(pair_lane + 8 * (kb & 1)) = pack_bf16x4(x);
+    *reinterpret_cast<uint2*>(pair_lane + 1024 + 8 * (kb & 1)) = bf16_lo_part4(x);
+}
+__device__ __forceinline__ f32x4 mfma_split(const uint4& ah, const uint4& al, const uint4& bh,
+                                            const uint4& bl, f32x4 acc) {
+    acc = mfma_bf16_k32(as_bf16x8(ah), as_bf16x8(bh), acc);
+    acc = mfma_bf16_k32(as_bf16x8(ah), as_bf16x8(bl), acc);
+    return mfma_bf16_k32(as_bf16x8(al), as_bf16x8(bh), acc);
+}
+
 // Workgroup placement.  Workgroups are dispatched to the 8 XCDs round robin by index; when
 // B*H is a multiple of 8, all workgroups of (b, h) go to XCD (b*H + h) mod 8 in all three
 // kernels, so the chain and output kernels find the prep kernel's results in that XCD's L2.
@@ -194,6 +234,11 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
             } else {
                 val = make_uint4(__float_as_uint(src[0]), __float_as_uint(src[krs]),
                                  __float_as_uint(src[2 * krs]), __float_as_uint(src[3 * krs]));
+                if (a.split) {
+                    // split format: k-block j of d-tile dt into the pair (dt, j & ~1)
+                    store_split(kt + ((static_cast<int64_t>(blk - (j & 1)) * 64) + lam) * 16, j, as_f32x4(val));
+                    continue;
+                }
             }
             *reinterpret_cast<uint4*>(kt + static_cast<int64_t>(e) * 16) = val;
         }
@@ -429,8 +474,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[3], b4[tt].w, acc[tt]);
             }
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-                *reinterpret_cast<f32x4*>(blk_ptr(wy, tt * NDB + dt, l)) = acc[tt];
+            for (int tt = 0; tt < NT; ++tt) {
+                if (a.split) store_split(blk_ptr(wy, tt * NDB + (dt & ~1), l), dt, acc[tt]);
+                else *reinterpret_cast<f32x4*>(blk_ptr(wy, tt * NDB + dt, l)) = acc[tt];
+            }
         }
     }
 }
@@ -765,24 +812,32 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
             if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
             else val = __builtin_bit_cast(uint4, Wst[i]);
             const int jb = dt0 / pair + i;
-            *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+            if constexpr (BF16) *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+            else store_split(lane16(X, jb & ~1), jb, Wst[i]);     // split format for GEMM1
             *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
         }
         lds_barrier();                                               // B1
         if (w < NT) {
             // S = W_y W^T for row tile w, two accumulators over alternating k-blocks
             f32x4 s0 = zero4(), s1 = zero4();
+            if constexpr (BF16) {
 #pragma unroll
-            for (int j = 0; j < NDB; ++j) {
-                const uint4 av = *reinterpret_cast<const uint4*>(lane16(sw, j));
-                const uint4 bv = *reinterpret_cast<const uint4*>(lane16(X, j));
-                f32x4& acc = (j & 1) ? s1 : s0;
-                if constexpr (BF16) {
+                for (int j = 0; j < NDB; ++j) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(lane16(sw, j));
+                    const uint4 bv = *reinterpret_cast<const uint4*>(lane16(X, j));
+                    f32x4& acc = (j & 1) ? s1 : s0;
                     acc = mfma_bf16_k32(as_bf16x8(av), as_bf16x8(bv), acc);
-                } else {
-                    const f32x4 af = as_f32x4(av), bf = as_f32x4(bv);
+                }
+            } else {
+                // fp32 operands in the split format: one 32-deep k-step per block pair
+                static_assert(NDB % 2 == 0, "fp32 k-blocks pair up");
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
+                for (int j = 0; j < NDB; j += 2) {
+                    f32x4& acc = (j & 2) ? s1 : s0;
+                    acc = mfma_split(*reinterpret_cast<const uint4*>(lane16(sw, j)),
+                                     *reinterpret_cast<const uint4*>(lane16(sw, j + 1)),
+                                     *reinterpret_cast<const uint4*>(lane16(X, j)),
+                                     *reinterpret_cast<const uint4*>(lane16(X, j + 1)), acc);
                 }
             }
             const f32x4 uyv = *reinterpret_cast<const f32x4*>(lane16(sw, SL::PW - 1));
@@ -798,7 +853,8 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
             }
             const float* rk = reinterpret_cast<const float*>(smem + slot * SL::SLOT + kChainWaves * SL::PW * 1024);
             const f32x4 rkv = *reinterpret_cast<const f32x4*>(rk + 16 * w + 4 * g4);
-            *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rkv;
+            if constexpr (BF16) *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rkv;
+            else store_split(lane16(Ub, w & ~1), w, U * rkv);      // split format for the update
         }
         lds_barrier();                                               // B2
         // W^T += K^T (rho_k o U) for this wave's d-tiles
@@ -817,14 +873,17 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
                     f32x4& dst = (j & 1) ? odd[i] : Wst[i];
                     dst = mfma_bf16_k32(as_bf16x8(av), as_bf16x8(bu), dst);
                 }
-            } else {
-                const f32x4 uv = *reinterpret_cast<const f32x4*>(lane16(Ub, j));
+            } else if ((j & 1) == 0) {
+                // fp32 operands in the split format: K^T and rho_k o U block pairs (j, j + 1)
+                static_assert(NTB % 2 == 0, "fp32 k-blocks pair up");
+                const uint4 uh = *reinterpret_cast<const uint4*>(lane16(Ub, j));
+                const uint4 ul = *reinterpret_cast<const uint4*>(lane16(Ub, j + 1));
 #pragma unroll
                 for (int i = 0; i < NDP; ++i) {
-                    const f32x4 af = as_f32x4(*reinterpret_cast<const uint4*>(lane16(sw, NDB + i * NTB + j)));
-                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dst = mfma_f32_k4(af[e], uv[e], dst);
+                    f32x4& dst = (j & 2) ? odd[i] : Wst[i];
+                    dst = mfma_split(*reinterpret_cast<const uint4*>(lane16(sw, NDB + i * NTB + j)),
+                                     *reinterpret_cast<const uint4*>(lane16(sw, NDB + i * NTB + j + 1)),
+                                     uh, ul, dst);
                 }
             }
         }
@@ -926,7 +985,8 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
             if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
             else val = __builtin_bit_cast(uint4, Wst[i]);
             const int jb = dt0 / pair + i;
-            *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+            if constexpr (BF16) *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+            else store_split(lane16(X, jb & ~1), jb, Wst[i]);     // split format for GEMM1
             *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
         }
         lds_barrier();                                               // B1: W^T copy complete

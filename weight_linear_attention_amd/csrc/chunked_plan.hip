@@ -110,6 +110,8 @@ bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Chu
             plan->lds_chain = lds;
         }
     }
+    // the staged chain kernel takes fp32 operands in the split bf16 hi + lo format
+    plan->args.split = !bf16 && plan->staged_ndp > 0;
     return true;
 }
 

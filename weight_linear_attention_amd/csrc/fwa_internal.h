@@ -58,6 +58,7 @@ struct ChunkArgs {
     int64_t o_ah, o_al;          // streaming forward: (I + L)^-1 diag(beta) as bf16 hi, lo blocks
     int BH, T, NC, d_k, d_v, nu, D;
     int DP, NDP;
+    int split;                   // fp32: W_y and K^T blocks in the split bf16 hi + lo format
     int krs, lss, pss, aps;
     int ss;                      // row stride (elements) of the shift-sliced K and Q tiles
     int l_kr, l_qr, l_x, l_ls, l_ps, l_li, l_xv, l_small;

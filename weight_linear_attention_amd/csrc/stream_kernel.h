@@ -39,16 +39,6 @@ constexpr int kStreamWaves = 8;
 // disables the access); the hardware drops accesses at or past the range in word 2.
 constexpr int kBufferWord3 = 0x00020000;
 
-__device__ __forceinline__ uint4 bf16_lo_part(const f32x4& x0, const f32x4& x1) {
-    f32x4 r0, r1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r0[e] = x0[e] - static_cast<float>(static_cast<__bf16>(x0[e]));
-        r1[e] = x1[e] - static_cast<float>(static_cast<__bf16>(x1[e]));
-    }
-    return pack_bf16x8(r0, r1);
-}
-
 template <int C, int NDW>
 __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
     static_assert(C == 64, "row tiles map one-to-one onto waves 0-3 and 4-7");

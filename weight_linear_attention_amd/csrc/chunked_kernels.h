@@ -84,6 +84,11 @@ __device__ __forceinline__ void store_split(char* pair_lane, int kb, const f32x4
     *reinterpret_cast<uint2*>(pair_lane + 8 * (kb & 1)) = pack_bf16x4(x);
     *reinterpret_cast<uint2*>(pair_lane + 1024 + 8 * (kb & 1)) = bf16_lo_part4(x);
 }
+// The same for a B-operand pair whose two blocks are not adjacent (hi and lo lane pointers).
+__device__ __forceinline__ void store_split2(char* hi_lane, char* lo_lane, int kb, const f32x4& x) {
+    *reinterpret_cast<uint2*>(hi_lane + 8 * (kb & 1)) = pack_bf16x4(x);
+    *reinterpret_cast<uint2*>(lo_lane + 8 * (kb & 1)) = bf16_lo_part4(x);
+}
 __device__ __forceinline__ f32x4 mfma_split(const uint4& ah, const uint4& al, const uint4& bh,
                                             const uint4& bl, f32x4 acc) {
     acc = mfma_bf16_k32(as_bf16x8(ah), as_bf16x8(bh), acc);
@@ -213,6 +218,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 val = make_uint4(lo.x, lo.y, hi.x, hi.y);
             } else {
                 val = *reinterpret_cast<const uint4*>(src);
+                if (a.split) {
+                    store_split(qa + ((static_cast<int64_t>(blk - (j & 1)) * 64) + lam) * 16, j, as_f32x4(val));
+                    continue;
+                }
             }
             *reinterpret_cast<uint4*>(qa + static_cast<int64_t>(e) * 16) = val;
         }
@@ -261,6 +270,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 }
             } else {
                 if (j <= ta) val = *reinterpret_cast<const uint4*>(src);
+                if (a.split) {
+                    store_split(pa + ((static_cast<int64_t>(blk - (j & 1)) * 64) + lam) * 16, j, as_f32x4(val));
+                    continue;
+                }
             }
             *reinterpret_cast<uint4*>(pa + static_cast<int64_t>(e) * 16) = val;
         }
@@ -812,9 +825,15 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
             if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
             else val = __builtin_bit_cast(uint4, Wst[i]);
             const int jb = dt0 / pair + i;
-            if constexpr (BF16) *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
-            else store_split(lane16(X, jb & ~1), jb, Wst[i]);     // split format for GEMM1
-            *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
+            if constexpr (BF16) {
+                *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+                *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
+            } else {
+                // split format for GEMM1 and for the output kernel's Q W^T
+                store_split(lane16(X, jb & ~1), jb, Wst[i]);
+                store_split2(blk_ptr(wn, static_cast<int64_t>(jb & ~1) * NVT + r, l),
+                             blk_ptr(wn, static_cast<int64_t>(jb | 1) * NVT + r, l), jb, Wst[i]);
+            }
         }
         lds_barrier();                                               // B1
         if (w < NT) {
@@ -849,7 +868,8 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
                 *reinterpret_cast<uint2*>(blk_ptr(un, static_cast<int64_t>(w >> 1) * NVT + r, l) + 8 * (w & 1)) =
                     make_uint2(pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
             } else {
-                *reinterpret_cast<f32x4*>(blk_ptr(un, static_cast<int64_t>(w) * NVT + r, l)) = U;
+                store_split2(blk_ptr(un, static_cast<int64_t>(w & ~1) * NVT + r, l),
+                             blk_ptr(un, static_cast<int64_t>(w | 1) * NVT + r, l), w, U);
             }
             const float* rk = reinterpret_cast<const float*>(smem + slot * SL::SLOT + kChainWaves * SL::PW * 1024);
             const f32x4 rkv = *reinterpret_cast<const f32x4*>(rk + 16 * w + 4 * g4);
@@ -985,9 +1005,15 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
             if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
             else val = __builtin_bit_cast(uint4, Wst[i]);
             const int jb = dt0 / pair + i;
-            if constexpr (BF16) *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
-            else store_split(lane16(X, jb & ~1), jb, Wst[i]);     // split format for GEMM1
-            *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
+            if constexpr (BF16) {
+                *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
+                *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
+            } else {
+                // split format for GEMM1 and for the output kernel's Q W^T
+                store_split(lane16(X, jb & ~1), jb, Wst[i]);
+                store_split2(blk_ptr(wn, static_cast<int64_t>(jb & ~1) * NVT + r, l),
+                             blk_ptr(wn, static_cast<int64_t>(jb | 1) * NVT + r, l), jb, Wst[i]);
+            }
         }
         lds_barrier();                                               // B1: W^T copy complete
         // S = W_y W^T for row tile w, two accumulators over alternating k-blocks
@@ -1101,7 +1127,23 @@ __global__ __launch_bounds__(256) void delta_output_kernel(ChunkArgs a) {
     const char* ws = a.ws;
     const char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
     const char* wn = ws + a.o_wn + u * (static_cast<int64_t>(D) * d_v * sizeof(LT));
+    const char* pa = ws + a.o_pa + u * (static_cast<int64_t>(C) * C * sizeof(LT));
+    const char* un = ws + a.o_un + u * (static_cast<int64_t>(C) * d_v * sizeof(LT));
+    const f32x4 rq = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(ws + a.o_rq) +
+                                                     u * C + 16 * tt + 4 * g4);
     f32x4 acc = zero4();
+    if (!BF16 && a.split) {
+        // fp32 operands in the split bf16 hi + lo format: block pairs (j, j + 1)
+        auto ld = [&](const char* base, int64_t blk) { return *reinterpret_cast<const uint4*>(blk_ptr(base, blk, l)); };
+#pragma unroll 2
+        for (int j = 0; j < NDB; j += 2)
+            acc = mfma_split(ld(qa, tt * NDB + j), ld(qa, tt * NDB + j + 1), ld(wn, j * NVT + vt),
+                             ld(wn, (j + 1) * NVT + vt), acc);
+        acc *= rq;
+        for (int j = 0; j < NT && j <= tt; j += 2)
+            acc = mfma_split(ld(pa, tt * NT + j), ld(pa, tt * NT + j + 1), ld(un, j * NVT + vt),
+                             ld(un, (j + 1) * NVT + vt), acc);
+    } else {
 #pragma unroll 4
     for (int j = 0; j < NDB; ++j) {
         const uint4 av = *reinterpret_cast<const uint4*>(blk_ptr(qa, tt * NDB + j, l));
@@ -1114,11 +1156,7 @@ __global__ __launch_bounds__(256) void delta_output_kernel(ChunkArgs a) {
             for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
         }
     }
-    const f32x4 rq = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(ws + a.o_rq) +
-                                                     u * C + 16 * tt + 4 * g4);
     acc *= rq;
-    const char* pa = ws + a.o_pa + u * (static_cast<int64_t>(C) * C * sizeof(LT));
-    const char* un = ws + a.o_un + u * (static_cast<int64_t>(C) * d_v * sizeof(LT));
     for (int j = 0; j < NTB && pair * j <= tt; ++j) {
         const uint4 av = *reinterpret_cast<const uint4*>(blk_ptr(pa, tt * NTB + j, l));
         const uint4 bv = *reinterpret_cast<const uint4*>(blk_ptr(un, j * NVT + vt, l));
@@ -1129,6 +1167,7 @@ __global__ __launch_bounds__(256) void delta_output_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
         }
+    }
     }
     LT* yB = static_cast<LT*>(a.y) + (static_cast<int64_t>(bh) * T + t0) * d_v;
 #pragma unroll

@@ -57,7 +57,8 @@ def parse():
 # Kernel sources behind each measured unit (their hash keys the committed counter data).
 SOURCES = {
     "chunked": ("chunked_kernels.h", "chunk_tile.h"),
-    "stream": ("stream_kernel.h", "stream_bf16_c64.hip", "chunked_kernels.h", "chunk_tile.h"),
+    "stream": ("stream_kernel.h", "stream_bf16_c64.hip", "stream_sliced.h", "stream_sliced_bf16.hip",
+               "chunked_kernels.h", "chunk_tile.h"),
     "fused": ("forward_kernel.h", "chunk_tile.h"),
     "decode": ("step_kernel.hip",),
     "dpfp": ("dpfp_kernel.hip",),
@@ -70,6 +71,18 @@ def kernel_source_hash(unit):
         with open(os.path.join(HERE, "weight_linear_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def stream_kernels(w):
+    """Kernel names of the streaming path for this shape, by the planner's rule (chunk 128: the
+    shift-sliced prep and serial kernels; chunk 64: the sliced prep for d_k 64 and nu <= 4, then
+    the full-tile serial kernel where it applies, else the sliced one)."""
+    sliced_prep = w.d_k == 64 and w.nu <= 4 and os.environ.get("FWA_STREAM_PREP") != "full"
+    full_ok = w.chunk == 64 and w.d_v % 32 == 0 and w.D % 128 == 0 and w.nu <= 8 and w.D <= 384
+    if w.chunk == 128 or os.environ.get("FWA_STREAM_KERNEL") == "sliced" or not full_ok:
+        return "delta_prep_sliced_kernel + delta_stream_sliced_kernel"
+    return ("delta_prep_sliced_kernel" if sliced_prep else "delta_prep_kernel (compact)") + \
+        " + delta_stream_kernel"
 
 
 def measured_traffic(unit, workload):
@@ -249,11 +262,14 @@ def main():
                     "frac": ach / PEAK_HBM_GBPS}
         kname = {"chunked": "fwa_delta_forward, chunked: delta_prep_kernel + delta_chain_kernel + "
                             "delta_output_kernel",
-                 "stream": "fwa_delta_forward, stream: delta_prep_kernel (compact) + "
-                           "delta_stream_kernel",
+                 "stream": "fwa_delta_forward, stream: " + stream_kernels(w),
                  "fused": "fwa_delta_forward, fused: delta_forward_kernel"}[unit]
         roof.update(kernel=kname, algorithmic_flops=flops, algorithmic_bytes=nbytes,
                     mean_launch_ms=main_ms)
+        if w.dtype == "f32" and unit == "chunked":
+            roof["note"] = ("fp32 inputs and state; the chain and output contractions run on the "
+                            "bf16 MFMA with fp32 operands split into bf16 hi + lo pairs (three "
+                            "products, about 2^-16 relative); the peak quoted is the fp32 MFMA one")
     else:
         if kind == "decode":
             unit = "decode"
@@ -267,7 +283,8 @@ def main():
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBPS, "kernel": kname, "algorithmic_bytes": nbytes,
                 "mean_launch_ms": main_ms}
-    roof["traffic"] = measured_traffic(unit, w.name if kind != "dpfp" else name)
+    roof["traffic"] = measured_traffic(
+        unit, name if kind in ("dpfp", "decode") else f"{w.name}:c{w.chunk}")
 
     out = {
         "metric": "tokens/sec through fast-weight layer (fwd + decode step) & % of MFMA/HBM roofline",

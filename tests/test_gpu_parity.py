@@ -156,6 +156,22 @@ def test_forward_full_size_long_sequence_sampled(path, full_size_case, chunk):
     assert ey <= 2e-2 and ew <= 2e-2
 
 
+@pytest.mark.parametrize("kernel", ["pc", "sliced"])
+def test_stream_kernels_full_size(full_size_case, monkeypatch, kernel):
+    """The 8 x 16 x 16384 workload at chunk 64 on the producer / consumer and the sliced serial
+    kernels, checked like the default one on 6 sampled (b, h) slices."""
+    w, inp, (yr, Wr) = full_size_case
+    monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
+    monkeypatch.setenv("FWA_STREAM_KERNEL", kernel)
+    log(f"forward[stream {kernel}] full {w}")
+    y, Wf = _forward(_dev(inp), w.nu, 64)
+    sel = tuple(torch.tensor(ix) for ix in zip(*_FULL_PICKS))
+    ey = normwise(to_f64(y.cpu()[sel])[None], yr, 2)
+    ew = normwise(to_f64(Wf.cpu()[sel])[None], Wr, 2)
+    log(f"  sampled y err {ey:.3e}  W_final err {ew:.3e}")
+    assert ey <= 2e-2 and ew <= 2e-2
+
+
 def test_forward_T0_and_empty(path):
     w = workload("b4_h8_t4096_d64_nu2_bf16_carried" if path == "stream" else "h8_t1024_d64_nu1_f32",
                  T=0, w0_std=0.1)
@@ -211,7 +227,8 @@ def test_forward_chunk_independence_and_determinism(monkeypatch):
         assert torch.equal(y2, outs[(p, 64)][0]) and torch.equal(W2, outs[(p, 64)][1])
 
 
-@pytest.mark.parametrize("kernel,prep", [("default", "full"), ("default", "sliced"), ("sliced", "sliced")])
+@pytest.mark.parametrize("kernel,prep", [("default", "full"), ("default", "sliced"), ("sliced", "sliced"),
+                                         ("pc", "sliced")])
 def test_stream_prep_variants_and_chunks(monkeypatch, kernel, prep):
     """The streaming path with each serial kernel and prep kernel at chunk 64, and at chunk
     128, against the oracle and against each other; each is deterministic."""

@@ -65,7 +65,8 @@ def test_chunked_every_chain_config(dt, D, C, monkeypatch):
 # wave (1-3), each d_k a different roll window, nu up to 8 the longest roll the extended q rows
 # hold.  The shift-sliced kernel (16-column workgroups) takes d_k = 64 with nu <= 4, so D up to
 # 512, and any d_v here; it is the fallback for d_k = 64 shapes the full-tile kernel does not
-# take, and FWA_STREAM_KERNEL=sliced forces it.  T covers a lone
+# take, and FWA_STREAM_KERNEL=sliced forces it; FWA_STREAM_KERNEL=pc forces the producer /
+# consumer kernel (d_k = 64, nu <= 4, d_v in {32, 64}).  T covers a lone
 # partial chunk, an exact chunk and ragged tails.  Shapes neither kernel takes are refused.
 STREAM_CASES = [
     # (d_k, nu, d_v, B, H, T)
@@ -76,7 +77,7 @@ STREAM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("kernel", ["default", "sliced"])
+@pytest.mark.parametrize("kernel", ["default", "sliced", "pc"])
 @pytest.mark.parametrize("case", STREAM_CASES,
                          ids=[f"dk{c[0]}-nu{c[1]}-dv{c[2]}-T{c[5]}" for c in STREAM_CASES])
 def test_stream_every_split(case, kernel, monkeypatch):
@@ -87,8 +88,10 @@ def test_stream_every_split(case, kernel, monkeypatch):
     monkeypatch.setenv("FWA_STREAM_KERNEL", kernel)
     sliced_ok = d_k == 64 and nu <= 4
     full_ok = nu <= 8 and 2 * d_k * nu <= 384 and d_v % 32 == 0
-    # the default takes the full-tile kernel and falls back to the sliced one; "sliced" forces it
-    if not (sliced_ok if kernel == "sliced" else (full_ok or sliced_ok)):
+    # the default takes the full-tile kernel and falls back to the sliced one; "sliced" forces
+    # it; "pc" forces the producer / consumer kernel (32-column workgroups)
+    ok = {"sliced": sliced_ok, "pc": sliced_ok and d_v % 32 == 0}.get(kernel, full_ok or sliced_ok)
+    if not ok:
         with pytest.raises(fwa.FwaError) as e:
             fwa.delta_forward_info(B, H, T, d_k, d_v, nu, 64, w.torch_dtype)
         assert e.value.status == fwa.FWA_ERR_UNSUPPORTED

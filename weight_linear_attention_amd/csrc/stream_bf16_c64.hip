@@ -18,6 +18,9 @@ constexpr int kMaxLdsStream = 160 * 1024;
 // FWA_STREAM_KERNEL=sliced also forces.  On the 8 x 16 x 16384 (D 384) forward the full-tile
 // kernel takes 1.45 ms and the sliced one 2.5 ms: the sliced one builds the DPFP tiles three
 // times per chunk and column group (K and Q, then K again) and is bound by that VALU work.
+// FWA_STREAM_KERNEL=pc selects the producer / consumer serial kernel (chunk 64, d_k = 64,
+// nu <= 4, d_v in {32, 64}): 2.09 ms on that workload, its single producer wave per SIMD
+// latency-bound on the DPFP work of each step.
 static bool env_is(const char* name, const char* value) {
     const char* s = std::getenv(name);
     return s != nullptr && std::strcmp(s, value) == 0;
@@ -27,6 +30,7 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
 
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan) {
     if (!bf16) return false;
+    if (C == 64 && env_is("FWA_STREAM_KERNEL", "pc")) return plan_stream_pc(BH, T, d_k, d_v, nu, C, plan);
     if (C == 128 || (C == 64 && env_is("FWA_STREAM_KERNEL", "sliced")))
         return plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
     if (!plan_stream_full(BH, T, d_k, d_v, nu, C, plan))
@@ -75,6 +79,7 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
     plan->lds_prep = cp.lds_prep;
     plan->sliced_prep = false;
     plan->sliced_stream = false;
+    plan->pc_stream = false;
     if (d_k == 64 && nu <= 4 && !env_is("FWA_STREAM_PREP", "full")) {
         const int lds = plan_prep_sliced(C, &a);
         if (lds > 0) {
@@ -133,6 +138,7 @@ hipError_t launch_stream(const StreamPlan& plan_in, const void* q, const void* k
     a.y = y;
     a.Wf = Wf;
     a.ws = ws;
+    if (p.pc_stream) return launch_stream_pc(p, stream);
     if (p.sliced_stream) return launch_stream_sliced(p, stream);
     if (p.C != 64) return hipErrorInvalidValue;
     return launch_stream_c64(p, stream);

@@ -58,7 +58,7 @@ def parse():
 SOURCES = {
     "chunked": ("chunked_kernels.h", "chunk_tile.h"),
     "stream": ("stream_kernel.h", "stream_bf16_c64.hip", "stream_sliced.h", "stream_sliced_bf16.hip",
-               "chunked_kernels.h", "chunk_tile.h"),
+               "stream_pc.h", "chunked_kernels.h", "chunk_tile.h"),
     "fused": ("forward_kernel.h", "chunk_tile.h"),
     "decode": ("step_kernel.hip",),
     "dpfp": ("dpfp_kernel.hip",),
@@ -79,6 +79,8 @@ def stream_kernels(w):
     the full-tile serial kernel where it applies, else the sliced one)."""
     sliced_prep = w.d_k == 64 and w.nu <= 4 and os.environ.get("FWA_STREAM_PREP") != "full"
     full_ok = w.chunk == 64 and w.d_v % 32 == 0 and w.D % 128 == 0 and w.nu <= 8 and w.D <= 384
+    if w.chunk == 64 and os.environ.get("FWA_STREAM_KERNEL") == "pc":
+        return "delta_prep_sliced_kernel + delta_stream_pc_kernel"
     if w.chunk == 128 or os.environ.get("FWA_STREAM_KERNEL") == "sliced" or not full_ok:
         return "delta_prep_sliced_kernel + delta_stream_sliced_kernel"
     return ("delta_prep_sliced_kernel" if sliced_prep else "delta_prep_kernel (compact)") + \

@@ -14,6 +14,10 @@ already resident in HBM when timing starts.  Other workloads (--workload):
     copy_calibration                                                a 1 GiB device copy (the
                                                                     reference for HBM counters)
 
+--flush (decode and DPFP workloads) writes a 1 GiB scratch buffer before every timed step,
+outside the timed events, so that no step finds its data in the 256 MB Infinity Cache; the
+rate then comes from per-step event pairs and `roofline.flushed` says so.
+
 Prints ONE JSON line.  `roofline` describes the dominant call: the forward (one launch on the
 fused path, two on the streaming path, three on the chunked path) or, for the decode and DPFP
 workloads, that kernel.
@@ -41,6 +45,7 @@ DEFAULT_WORKLOAD = "h8_t1024_d64_nu1_f32"
 WARMUP_SECONDS = 0.3       # default warm-up length
 EVENT_EVERY = 8            # forward workloads: event-bracketed step every EVENT_EVERY steps
 DECODE_WARM_SLICES = 64    # decode: input slices the warm-up cycles through
+FLUSH_BYTES = 1 << 30      # --flush: scratch written before every timed step
 
 
 def parse():
@@ -51,6 +56,10 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--chunk", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush", action="store_true",
+                   help="decode and DPFP workloads: write a 1 GiB scratch buffer before every timed "
+                        "step (outside the timed events), so no step finds its data in the 256 MB "
+                        "Infinity Cache; the rate is summed from per-step event pairs")
     return p.parse_args()
 
 
@@ -218,18 +227,36 @@ def main():
         for i in range(warmup):
             one_step(warm_idx(i), None)
     torch.cuda.synchronize()
-    marks = {i: [ev(), ev(), ev()] for i in sampled}
-    region = (ev(), ev())
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    region[0].record()
-    for i in range(steps):
-        one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, marks.get(i))
-    region[1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    flush = args.flush and kind in ("decode", "dpfp")
+    if flush:
+        # Every timed step starts with the caches cold: a 1 GiB write (4x the Infinity Cache)
+        # goes before it, outside its event pair; value and duration come from the step events.
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        pairs = [(ev(), ev()) for _ in range(steps)]
+        for i in range(steps):
+            scratch.fill_(float(i))
+            pairs[i][0].record()
+            one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, None)
+            pairs[i][1].record()
+        torch.cuda.synchronize()
+        main_ms = sum(a.elapsed_time(b) for a, b in pairs) / steps
+        elapsed = main_ms * 1e-3 * steps
+        del scratch
+    else:
+        marks = {i: [ev(), ev(), ev()] for i in sampled}
+        region = (ev(), ev())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        region[0].record()
+        for i in range(steps):
+            one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, marks.get(i))
+        region[1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
 
-    if per_call:
+    if flush:
+        pass
+    elif per_call:
         main_ms = sum(marks[i][0].elapsed_time(marks[i][1]) for i in sampled) / len(sampled)
     else:
         main_ms = region[0].elapsed_time(region[1]) / steps
@@ -287,6 +314,8 @@ def main():
                 "mean_launch_ms": main_ms}
     roof["traffic"] = measured_traffic(
         unit, name if kind in ("dpfp", "decode") else f"{w.name}:c{w.chunk}")
+    if flush:
+        roof["flushed"] = "a 1 GiB scratch write before every timed step; per-step events"
 
     out = {
         "metric": "tokens/sec through fast-weight layer (fwd + decode step) & % of MFMA/HBM roofline",

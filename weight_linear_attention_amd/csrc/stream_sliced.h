@@ -92,16 +92,18 @@ __device__ __forceinline__ void dpfp_slice_any(int i, const u16* Xk, const u16* 
 }
 
 // ------------------------------------------------------------------------------------------
-// prep (compact, sliced): one workgroup of 8 waves per chunk (b, h, n).  Writes, per chunk, the
+// prep (compact, sliced): one workgroup of NTH / 64 waves per chunk (b, h, n): 4 at chunk 64,
+// 8 at chunk 128 (one wave per 16-column block of A).  Writes, per chunk, the
 // A-operand blocks of A'' = (I + L)^-1 diag(beta) as a bf16 hi + lo pair (AH, AL; the pair's sum
 // carries the fp32 value to about 2^-17), the A-operand blocks of P~ (PA, zero above the
 // diagonal) and the normalisers rho_k, rho_q (RK, RQ).
 // LDS: phase 1 holds the raw k, q rows and one K and one Q slice; phase 2 (over it) L (fp32),
 // the diagonal-block inverses, and P~ followed by A'' hi / lo over it.
-template <int C, int NU>
-__global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(ChunkArgs a) {
-    constexpr int NT = C / 16, NTB = NT / 2, NW = kSliceThreads / 64;
-    constexpr int NP = 2 * C * (kSliceDk / 8) / kSliceThreads;
+template <int C, int NU, int NTH = kSliceThreads>
+__global__ __launch_bounds__(NTH, 1) void delta_prep_sliced_kernel(ChunkArgs a) {
+    constexpr int NT = C / 16, NTB = NT / 2, NW = NTH / 64;
+    static_assert(NW >= NT, "one wave per block column of A");
+    constexpr int NP = 2 * C * (kSliceDk / 8) / NTH;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     u16* Xk = reinterpret_cast<u16*>(smem + a.l_x);          // [C][64] raw k rows
     u16* Xq = Xk + C * kSliceDk;                              // [C][64] raw q rows
@@ -131,8 +133,8 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
         const uint4* kc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.k) + row0 * kSliceDk);
         const uint4* qc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.q) + row0 * kSliceDk);
 #pragma unroll
-        for (int p = 0; p < C * 8 / kSliceThreads; ++p) {
-            const int e = tid + kSliceThreads * p;               // 16-byte unit, row e / 8
+        for (int p = 0; p < C * 8 / NTH; ++p) {
+            const int e = tid + NTH * p;               // 16-byte unit, row e / 8
             const bool ok = (e >> 3) < Cc;
             const uint32_t m = ok ? 0xffffffffu : 0u;
             const uint4 rk = kc[ok ? e : 0], rq = qc[ok ? e : 0];
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
     // a rolled loop: unrolled, the compiler keeps every slice's task inputs in registers
 #pragma unroll 1
     for (int s = 0; s < NU; ++s) {
-        dpfp_slice_any<C, kSliceThreads, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
+        dpfp_slice_any<C, NTH, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
         lds_barrier();
         gp_accumulate<true, C, false, NW>(gp, Ks, Qs, ss, kSliceCols, w, l16, g4);
         lds_barrier();
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
         s += dpp_f32<0xB1>(s);
         s += dpp_f32<0x4E>(s);
         s += dpp_f32<0x141>(s);
-        const int tau = tid + kSliceThreads * p, rt = tau >> 3;
+        const int tau = tid + NTH * p, rt = tau >> 3;
         if ((tau & 7) == 0) (rt >= C ? rhoq + (rt - C) : rhok + rt)[0] = __builtin_amdgcn_rcpf(s + kDpfpEps);
     }
     lds_barrier();
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
     if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
     {
         char* pa = a.ws + a.o_pa + u * (static_cast<int64_t>(C) * C * 2);
-        for (int e = tid; e < NT * NTB * 64; e += kSliceThreads) {
+        for (int e = tid; e < NT * NTB * 64; e += NTH) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
             const u16* src = Ps + (16 * ta + (lam & 15)) * a.pss + 32 * j + 4 * (lam >> 4);
             uint4 val = make_uint4(0u, 0u, 0u, 0u);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kSliceThreads, 1) void delta_prep_sliced_kernel(Chu
     {
         char* ah = a.ws + a.o_ah + u * (static_cast<int64_t>(C) * C * 2);
         char* al = a.ws + a.o_al + u * (static_cast<int64_t>(C) * C * 2);
-        for (int e = tid; e < NT * NTB * 64; e += kSliceThreads) {
+        for (int e = tid; e < NT * NTB * 64; e += NTH) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
             const int at = (16 * ta + (lam & 15)) * aps + 32 * j + 4 * (lam >> 4);
             const uint2 h0 = *reinterpret_cast<const uint2*>(Bh + at);

@@ -195,8 +195,39 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
     lds_barrier();
 
     {
-        GPTiles<C> gp;
-        gp_compute<BF16, C, false>(gp, Kr, Qr, krs, D, w, l16, g4);
+        // G/P has 2 NQ <= 4 units (one per wave of 0-3); waves 4-7 take the second half of D for
+        // the same units, and the halves are added through LDS (over the staging rows, dead
+        // since DPFP).  Each half must be whole k-steps (32 columns bf16, 16 fp32).
+        using GP = GPTiles<C>;
+        constexpr int NUNITS = 2 * GP::NQ;
+        const bool ksplit = NUNITS <= 4 && D % (BF16 ? 64 : 32) == 0;
+        const int half = ksplit ? (w >> 2) : 0;
+        const int wu = ksplit ? (w & 3) : w;             // the unit this wave computes (if < NUNITS)
+        const int Dw = ksplit ? D / 2 : D;
+        GP gp;
+        gp_compute<BF16, C, false>(gp, Kr + half * Dw, Qr + half * Dw, krs, Dw, wu, l16, g4);
+        if (ksplit) {
+            // the unit's tiles (ra, 0..ra) then (rb, 0..rb): NT + 1 slots of 1 KiB per unit
+            f32x4* part = reinterpret_cast<f32x4*>(smem + a.l_x);
+            const int q = wu < GP::NQ ? wu : wu - GP::NQ;
+            const int ra = q, rb = GP::NT - 1 - q;
+            f32x4* up = part + static_cast<int64_t>(wu) * (GP::NT + 1) * 64 + l;
+            if (w >= 4 && wu < NUNITS) {
+#pragma unroll
+                for (int tb = 0; tb < GP::NT; ++tb) {
+                    if (tb <= ra) up[tb * 64] = gp.a[0][tb];
+                    if (tb <= rb) up[(ra + 1 + tb) * 64] = gp.b[0][tb];
+                }
+            }
+            lds_barrier();
+            if (w < 4 && wu < NUNITS) {
+#pragma unroll
+                for (int tb = 0; tb < GP::NT; ++tb) {
+                    if (tb <= ra) gp.a[0][tb] += up[tb * 64];
+                    if (tb <= rb) gp.b[0][tb] += up[(ra + 1 + tb) * 64];
+                }
+            }
+        }
         lds_barrier();   // the staging rows are dead (L and P~ go over them)
         gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
     }

@@ -256,6 +256,48 @@ __device__ __forceinline__ void gp_unit(f32x4 (&ta)[C / 16], f32x4 (&tb_)[C / 16
                 if (RB != RA) tb_[tb] = mfma_bf16_k32(vb, kv8[tb], tb_[tb]);
             }
         }
+    } else if constexpr (!ROWSUMS) {
+        // fp32 tiles on the bf16 MFMA: each operand split on the fly into bf16 hi + lo
+        // (x = hi + lo to about 2^-16); hi hi + hi lo + lo hi per 32-deep k-step (48 cycles of
+        // MFMA against 256 for the eight fp32 16x16x4 products)
+        auto split8 = [](const float* p, bf16x8& hi, bf16x8& lo) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+            f32x4 r0, r1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = static_cast<__bf16>(x0[e]);
+                hi[4 + e] = static_cast<__bf16>(x1[e]);
+                r0[e] = x0[e] - static_cast<float>(hi[e]);
+                r1[e] = x1[e] - static_cast<float>(hi[4 + e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = static_cast<__bf16>(r0[e]);
+                lo[4 + e] = static_cast<__bf16>(r1[e]);
+            }
+        };
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const int c0 = 32 * kk + 8 * g4;
+            bf16x8 ah, al, bh, bl;
+            split8(Xa + c0, ah, al);
+            split8(Xb + c0, bh, bl);
+#pragma unroll
+            for (int tb = 0; tb <= RB; ++tb) {
+                bf16x8 kh, kl;
+                split8(Kb + 16 * tb * krs + c0, kh, kl);
+                if (tb <= RA) {
+                    ta[tb] = mfma_bf16_k32(ah, kh, ta[tb]);
+                    ta[tb] = mfma_bf16_k32(ah, kl, ta[tb]);
+                    ta[tb] = mfma_bf16_k32(al, kh, ta[tb]);
+                }
+                if (RB != RA) {
+                    tb_[tb] = mfma_bf16_k32(bh, kh, tb_[tb]);
+                    tb_[tb] = mfma_bf16_k32(bh, kl, tb_[tb]);
+                    tb_[tb] = mfma_bf16_k32(bl, kh, tb_[tb]);
+                }
+            }
+        }
     } else {
 #pragma unroll 2
         for (int kk = 0; kk < D / 16; ++kk) {

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
         // since DPFP).  Each half must be whole k-steps (32 columns bf16, 16 fp32).
         using GP = GPTiles<C>;
         constexpr int NUNITS = 2 * GP::NQ;
-        const bool ksplit = NUNITS <= 4 && D % (BF16 ? 64 : 32) == 0;
+        const bool ksplit = NUNITS <= 4 && D % 64 == 0;
         const int half = ksplit ? (w >> 2) : 0;
         const int wu = ksplit ? (w & 3) : w;             // the unit this wave computes (if < NUNITS)
         const int Dw = ksplit ? D / 2 : D;
@@ -233,58 +233,13 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
     }
     lds_barrier();
 
-    // ---- diagonal-block inverses; write-out of the Q, K^T and P~ blocks and the normalisers
-    if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
     char* ws = a.ws;
-    {
-        // QA: blocks (tt, j), j < NDB
-        char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < (LITE ? 0 : NT * NDB * 64); e += kPrepThreads) {
-            const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
-            const LT* src = Qr + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
-            uint4 val;
-            if constexpr (BF16) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(src);
-                const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
-                val = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else {
-                val = *reinterpret_cast<const uint4*>(src);
-                if (a.split) {
-                    store_split(qa + ((static_cast<int64_t>(blk - (j & 1)) * 64) + lam) * 16, j, as_f32x4(val));
-                    continue;
-                }
-            }
-            *reinterpret_cast<uint4*>(qa + static_cast<int64_t>(e) * 16) = val;
-        }
-        // KtA: blocks (dt, j), j < NTB: slot (h, e) = K[16 (pair j + h) + 4 (lam / 16) + e][16 dt + lam % 16]
-        char* kt = ws + a.o_kt + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid; e < (LITE ? 0 : ND * NTB * 64); e += kPrepThreads) {
-            const int blk = e >> 6, lam = e & 63, dt = blk / NTB, j = blk % NTB;
-            const LT* src = Kr + (16 * pair * j + 4 * (lam >> 4)) * krs + 16 * dt + (lam & 15);
-            uint4 val;
-            if constexpr (BF16) {
-                // the wave holds one block (lam = lane): two LDS transpose reads give the 8
-                // slots; lane i of a 16-lane group addresses row 4 (lam / 16) + i / 4, column
-                // 16 dt + 4 (i % 4) of each 16-row half
-                const LT* kp = Kr + (16 * pair * j + 4 * (lam >> 4) + ((lam & 15) >> 2)) * krs +
-                               16 * dt + 4 * (lam & 3);
-                const bf16x4 c0 = lds_read_tr_b16x4(kp);
-                const bf16x4 c1 = lds_read_tr_b16x4(kp + 16 * krs);
-                val = __builtin_bit_cast(uint4, __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7));
-            } else {
-                val = make_uint4(__float_as_uint(src[0]), __float_as_uint(src[krs]),
-                                 __float_as_uint(src[2 * krs]), __float_as_uint(src[3 * krs]));
-                if (a.split) {
-                    // split format: k-block j of d-tile dt into the pair (dt, j & ~1)
-                    store_split(kt + ((static_cast<int64_t>(blk - (j & 1)) * 64) + lam) * 16, j, as_f32x4(val));
-                    continue;
-                }
-            }
-            *reinterpret_cast<uint4*>(kt + static_cast<int64_t>(e) * 16) = val;
-        }
+    // P~ write-out, run by the waves the A phase leaves idle (A does not touch P~); the K^T
+    // blocks are written by the W_y product below, which loads them as its operands anyway
+    auto write_pa = [&](int e0, int estep) {
         // PA: blocks (ta, j), j < NTB; tiles above the diagonal are zero
         char* pa = ws + a.o_pa + u * (static_cast<int64_t>(C) * C * sizeof(LT));
-        for (int e = tid; e < NT * NTB * 64; e += kPrepThreads) {
+        for (int e = e0; e < NT * NTB * 64; e += estep) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
             const LT* src = Ps + (16 * ta + (lam & 15)) * a.pss + 16 * pair * j + 4 * (lam >> 4);
             uint4 val = make_uint4(0u, 0u, 0u, 0u);
@@ -308,6 +263,32 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
             }
             *reinterpret_cast<uint4*>(pa + static_cast<int64_t>(e) * 16) = val;
         }
+    };
+
+    // ---- diagonal-block inverses (the first C threads); write-out of the Q blocks by the other
+    //      waves, and of the normalisers
+    static_assert(C <= 64, "the inverses take wave 0 alone");
+    if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
+    {
+        // QA: blocks (tt, j), j < NDB
+        char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+        for (int e = tid - 64; w > 0 && e < (LITE ? 0 : NT * NDB * 64); e += kPrepThreads - 64) {
+            const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
+            const LT* src = Qr + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
+            uint4 val;
+            if constexpr (BF16) {
+                const uint2 lo = *reinterpret_cast<const uint2*>(src);
+                const uint2 hi = *reinterpret_cast<const uint2*>(src + 16);
+                val = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                val = *reinterpret_cast<const uint4*>(src);
+                if (a.split) {
+                    store_split(qa + ((static_cast<int64_t>(blk - (j & 1)) * 64) + lam) * 16, j, as_f32x4(val));
+                    continue;
+                }
+            }
+            *reinterpret_cast<uint4*>(qa + static_cast<int64_t>(e) * 16) = val;
+        }
         if (tid < C) {
             reinterpret_cast<float*>(ws + a.o_rk)[u * C + tid] = rhok[tid];
             reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
@@ -325,6 +306,8 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
     u16* Bh = Al + C * a.aps;                                        //       A'' hi, lo
     u16* Bl = Bh + C * a.aps;
     const int aps = a.aps;
+    static_assert(NT < kPrepWaves, "waves left over for the write-outs");
+    if (w >= NT) write_pa(tid - 64 * NT, kPrepThreads - 64 * NT);
     if (w < NT) {
         const int tb = w;
         const float bsc = betas[16 * tb + l16];
@@ -427,20 +410,26 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 }
             }
         } else {
-            // k-slot of lane group g in the r-th of four MFMAs is row s = 16 m + 4 g + r
+            // fp32 operands split into bf16 hi + lo, three MFMAs per 32-row k-step; k-slot
+            // (h, e) of lane group g is row s = 32 kb + 16 h + 4 g + e
 #pragma unroll
-            for (int m = 0; m < NT; ++m) {
-                float vb[4];
+            for (int kb = 0; kb < C / 32; ++kb) {
+                f32x4 v0, v1;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) vb[r] = to_f32(Xv[(16 * m + 4 * g4 + r) * d_v + 16 * vt + l16]);
-                f32x4 a4[NT];
+                for (int e = 0; e < 4; ++e) {
+                    v0[e] = to_f32(Xv[(32 * kb + 4 * g4 + e) * d_v + 16 * vt + l16]);
+                    v1[e] = to_f32(Xv[(32 * kb + 16 + 4 * g4 + e) * d_v + 16 * vt + l16]);
+                }
+                const uint4 bh = pack_bf16x8(v0, v1), bl = bf16_lo_part(v0, v1);
 #pragma unroll
-                for (int tt = m; tt < NT; ++tt)
-                    a4[tt] = *reinterpret_cast<const f32x4*>(Bf + (16 * tt + l16) * aps + 16 * m + 4 * g4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(a4[tt][r], vb[r], acc[tt]);
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (32 * kb <= 16 * tt + 15) {
+                        const float* ap = Bf + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ap);
+                        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ap + 16);
+                        acc[tt] = mfma_split(pack_bf16x8(a0, a1), bf16_lo_part(a0, a1), bh, bl, acc[tt]);
+                    }
+                }
             }
         }
 #pragma unroll
@@ -451,6 +440,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
     // ---- W_y^T = K^T A'^T as accumulator tiles (d-tile, t-tile), which are the WyA blocks:
     //      lane l, slot e of tile (dt, tt) holds W_y[16 tt + l % 16][16 dt + 4 (l / 16) + e].
     char* wy = ws + a.o_wy + u * (static_cast<int64_t>(C) * D * sizeof(LT));
+    char* kt = ws + a.o_kt + u * (static_cast<int64_t>(C) * D * sizeof(LT));   // KtA blocks
     if constexpr (BF16) {
         // k-slot (h, e) of lane group g is row s = 32 kb + 16 h + 4 g + e of the chunk; the K^T
         // operand comes from the row-major K tile by two LDS transpose reads.
@@ -469,6 +459,9 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                     const bf16x4 c0 = lds_read_tr_b16x4(kp);
                     const bf16x4 c1 = lds_read_tr_b16x4(kp + 16 * krs);
                     ka[h] = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    // the same operand is the KtA block (d-tile 2 j + h, k-block kb)
+                    *reinterpret_cast<uint4*>(blk_ptr(kt, static_cast<int64_t>(2 * j + h) * NTB + kb, l)) =
+                        __builtin_bit_cast(uint4, ka[h]);
                 }
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
@@ -494,28 +487,40 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 *reinterpret_cast<uint4*>(blk_ptr(wy, tt * NDB + j, l)) = pack_bf16x8(acc[0][tt], acc[1][tt]);
         }
     } else {
-        // k-slot of lane group g in the r-th of four MFMAs is row s = 16 m + 4 g + r.
+        // fp32 operands split into bf16 hi + lo, three MFMAs per 32-row k-step; k-slot (h, e)
+        // of lane group g is row s = 32 kb + 16 h + 4 g + e, so the K^T operand halves are the
+        // KtA blocks (dt, 2 kb + h) as they stand.
         for (int dt = w; dt < ND; dt += kPrepWaves) {
             f32x4 acc[NT];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) acc[tt] = zero4();
 #pragma unroll
-            for (int m = 0; m < NT; ++m) {
-                float ka[4];
+            for (int kb = 0; kb < C / 32; ++kb) {
+                f32x4 k0, k1;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ka[r] = to_f32(Kr[(16 * m + 4 * g4 + r) * krs + 16 * dt + l16]);
-                float4 b4[NT];
+                for (int e = 0; e < 4; ++e) {
+                    k0[e] = to_f32(Kr[(32 * kb + 4 * g4 + e) * krs + 16 * dt + l16]);
+                    k1[e] = to_f32(Kr[(32 * kb + 16 + 4 * g4 + e) * krs + 16 * dt + l16]);
+                }
+                const uint4 kh = pack_bf16x8(k0, k1), kl = bf16_lo_part(k0, k1);
+                if (a.split) {
+                    // the split pair of KtA blocks (dt, 2 kb), (dt, 2 kb + 1)
+                    char* kp = blk_ptr(kt, static_cast<int64_t>(dt) * NTB + 2 * kb, l);
+                    *reinterpret_cast<uint4*>(kp) = kh;
+                    *reinterpret_cast<uint4*>(kp + 1024) = kl;
+                } else {
+                    *reinterpret_cast<f32x4*>(blk_ptr(kt, static_cast<int64_t>(dt) * NTB + 2 * kb, l)) = k0;
+                    *reinterpret_cast<f32x4*>(blk_ptr(kt, static_cast<int64_t>(dt) * NTB + 2 * kb + 1, l)) = k1;
+                }
 #pragma unroll
-                for (int tt = m; tt < NT; ++tt)
-                    b4[tt] = *reinterpret_cast<const float4*>(Af + (16 * tt + l16) * aps + 16 * m + 4 * g4);
-#pragma unroll
-                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[0], b4[tt].x, acc[tt]);
-#pragma unroll
-                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[1], b4[tt].y, acc[tt]);
-#pragma unroll
-                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[2], b4[tt].z, acc[tt]);
-#pragma unroll
-                for (int tt = m; tt < NT; ++tt) acc[tt] = mfma_f32_k4(ka[3], b4[tt].w, acc[tt]);
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (32 * kb <= 16 * tt + 15) {
+                        const float* bp = Af + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp);
+                        const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 16);
+                        acc[tt] = mfma_split(kh, kl, pack_bf16x8(b0, b1), bf16_lo_part(b0, b1), acc[tt]);
+                    }
+                }
             }
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {

@@ -123,9 +123,10 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *              that rebuilds the DPFP features from the raw rows and keeps the memory on chip.
  *              Workspace of B*H*ceil(T/chunk) * (3*chunk*chunk*2 + 2*chunk*4) bytes (24.5 KiB
  *              per chunk of 64, 97 KiB per chunk of 128), kept per (device, stream) as above.
- *              d_v in {32, 64} and D a multiple of 128, with chunk 64 (D in {128, 256, 384};
- *              nu <= 8) or chunk 128 (d_k = 64, nu <= 4: the DPFP features are built one
- *              shift block of 128 columns at a time, so D up to 512 fits on chip).
+ *              Chunk 64: d_v in {32, 64}, D in {128, 256, 384}, nu <= 8; and, for d_k = 64
+ *              with nu <= 4, also d_v = 16 and D = 512.  Chunk 128: d_k = 64, nu <= 4,
+ *              d_v in {32, 64} (the DPFP features are built one shift block of 128 columns
+ *              at a time, so D up to 512 fits on chip).
  *     fused    one launch that keeps the chunk and the memory on chip; allocates nothing.
  *              Needs the chunk's working set (3*chunk*D elements plus chunk-sized scratch)
  *              within the 160 KiB of LDS of one compute unit.

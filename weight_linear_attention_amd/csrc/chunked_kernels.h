@@ -504,10 +504,14 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 }
                 const uint4 kh = pack_bf16x8(k0, k1), kl = bf16_lo_part(k0, k1);
                 if (a.split) {
-                    // the split pair of KtA blocks (dt, 2 kb), (dt, 2 kb + 1)
+                    // the split pair of KtA blocks (dt, 2 kb), (dt, 2 kb + 1), of K~^T =
+                    // K^T diag(rho_k): the staged chain then updates with U itself
+                    const f32x4 r0 = *reinterpret_cast<const f32x4*>(rhok + 32 * kb + 4 * g4);
+                    const f32x4 r1 = *reinterpret_cast<const f32x4*>(rhok + 32 * kb + 16 + 4 * g4);
+                    const f32x4 s0 = k0 * r0, s1 = k1 * r1;
                     char* kp = blk_ptr(kt, static_cast<int64_t>(dt) * NTB + 2 * kb, l);
-                    *reinterpret_cast<uint4*>(kp) = kh;
-                    *reinterpret_cast<uint4*>(kp + 1024) = kl;
+                    *reinterpret_cast<uint4*>(kp) = pack_bf16x8(s0, s1);
+                    *reinterpret_cast<uint4*>(kp + 1024) = bf16_lo_part(s0, s1);
                 } else {
                     *reinterpret_cast<f32x4*>(blk_ptr(kt, static_cast<int64_t>(dt) * NTB + 2 * kb, l)) = k0;
                     *reinterpret_cast<f32x4*>(blk_ptr(kt, static_cast<int64_t>(dt) * NTB + 2 * kb + 1, l)) = k1;
@@ -849,11 +853,41 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
 
     const int64_t szWn = static_cast<int64_t>(D) * a.d_v * sizeof(LT);
     const int64_t szUn = static_cast<int64_t>(C) * a.d_v * sizeof(LT);
+    // fp32 (split format): the outputs of the chunk are formed here, Y = rho_q o (Q W^T) + P~ U
+    // for row tile w, from the Q and P~ blocks (registers, fetched a chunk ahead) and the W^T
+    // copy and U the chain already holds in LDS; no chunk-start memories or U go to the
+    // workspace and no output kernel runs.
+    constexpr bool FUSE_Y = !BF16;
+    constexpr int NQB = FUSE_Y ? NDB : 1, NPB = FUSE_Y ? NT : 1;
+    uint4 qy[NQB], py[NPB];
+    f32x4 rqv = zero4(), qacc = zero4();
+    auto load_q = [&](int64_t uu) {
+        if (!FUSE_Y || w >= NT) return;
+        const char* qa = a.ws + a.o_qa + uu * (static_cast<int64_t>(C) * D * 4);
+#pragma unroll
+        for (int j = 0; j < NQB; ++j) qy[j] = *reinterpret_cast<const uint4*>(blk_ptr(qa, w * NDB + j, l));
+    };
+    auto load_p = [&](int64_t uu) {
+        if (!FUSE_Y || w >= NT) return;
+        const char* pa = a.ws + a.o_pa + uu * (static_cast<int64_t>(C) * C * 4);
+#pragma unroll
+        for (int j = 0; j < NPB; ++j) py[j] = *reinterpret_cast<const uint4*>(blk_ptr(pa, w * NT + j, l));
+        rqv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rq) + uu * C + 16 * w + 4 * g4);
+    };
+    // y of this (b, h), columns 16 r + l16, as a buffer whose range check drops rows past T
+    const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<float*>(a.y) + static_cast<int64_t>(bh) * a.T * a.d_v, static_cast<short>(0),
+        a.T * a.d_v * 4, 0x00020000);
+    if (NC > 0) {
+        load_q(u0);
+        load_p(u0);
+    }
     for (int n = 0; n < NC; ++n) {
         const int64_t uu = u0 + n;
+        const int64_t unext = n + 1 < NC ? uu + 1 : uu;
         const int slot = n & 1;
         char* sw = smem + slot * SL::SLOT + w * SL::PW * 1024;
-        // chunk-start memory: the LDS copy for GEMM1 and the Wn blocks for the output kernel
+        // chunk-start memory: the LDS copy for GEMM1 and (bf16) the Wn blocks for the output kernel
         char* wn = a.ws + a.o_wn + uu * szWn;
 #pragma unroll
         for (int i = 0; i < NDPB; ++i) {
@@ -865,10 +899,7 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
                 *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
                 *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
             } else {
-                // split format for GEMM1 and for the output kernel's Q W^T
-                store_split(lane16(X, jb & ~1), jb, Wst[i]);
-                store_split2(blk_ptr(wn, static_cast<int64_t>(jb & ~1) * NVT + r, l),
-                             blk_ptr(wn, static_cast<int64_t>(jb | 1) * NVT + r, l), jb, Wst[i]);
+                store_split(lane16(X, jb & ~1), jb, Wst[i]);          // split format for GEMM1
             }
         }
         lds_barrier();                                               // B1
@@ -889,30 +920,48 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
 #pragma unroll
                 for (int j = 0; j < NDB; j += 2) {
                     f32x4& acc = (j & 2) ? s1 : s0;
+                    const uint4 xh = *reinterpret_cast<const uint4*>(lane16(X, j));
+                    const uint4 xl = *reinterpret_cast<const uint4*>(lane16(X, j + 1));
                     acc = mfma_split(*reinterpret_cast<const uint4*>(lane16(sw, j)),
-                                     *reinterpret_cast<const uint4*>(lane16(sw, j + 1)),
-                                     *reinterpret_cast<const uint4*>(lane16(X, j)),
-                                     *reinterpret_cast<const uint4*>(lane16(X, j + 1)), acc);
+                                     *reinterpret_cast<const uint4*>(lane16(sw, j + 1)), xh, xl, acc);
+                    qacc = mfma_split(qy[j], qy[j + 1], xh, xl, qacc);   // Q W^T, same W^T blocks
                 }
+                load_q(unext);
             }
             const f32x4 uyv = *reinterpret_cast<const f32x4*>(lane16(sw, SL::PW - 1));
             const f32x4 U = uyv - (s0 + s1);
-            // U for the output kernel: B blocks (j, r); for bf16 tile w is half h = w & 1 of
-            // pair block w / 2 (slots 4 h .. 4 h + 3 of every lane)
-            char* un = a.ws + a.o_un + uu * szUn;
             if constexpr (BF16) {
+                // U for the output kernel: B blocks (j, r); tile w is half h = w & 1 of pair
+                // block w / 2 (slots 4 h .. 4 h + 3 of every lane)
+                char* un = a.ws + a.o_un + uu * szUn;
                 *reinterpret_cast<uint2*>(blk_ptr(un, static_cast<int64_t>(w >> 1) * NVT + r, l) + 8 * (w & 1)) =
                     make_uint2(pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
+                const float* rk = reinterpret_cast<const float*>(smem + slot * SL::SLOT + kChainWaves * SL::PW * 1024);
+                const f32x4 rkv = *reinterpret_cast<const f32x4*>(rk + 16 * w + 4 * g4);
+                *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rkv;
             } else {
-                store_split2(blk_ptr(un, static_cast<int64_t>(w & ~1) * NVT + r, l),
-                             blk_ptr(un, static_cast<int64_t>(w | 1) * NVT + r, l), w, U);
+                // U itself in the split format: the K^T blocks carry rho_k (K~^T)
+                store_split(lane16(Ub, w & ~1), w, U);
             }
-            const float* rk = reinterpret_cast<const float*>(smem + slot * SL::SLOT + kChainWaves * SL::PW * 1024);
-            const f32x4 rkv = *reinterpret_cast<const f32x4*>(rk + 16 * w + 4 * g4);
-            if constexpr (BF16) *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rkv;
-            else store_split(lane16(Ub, w & ~1), w, U * rkv);      // split format for the update
         }
         lds_barrier();                                               // B2
+        if (FUSE_Y && w < NT) {
+            // Y for row tile w = rho_q o (Q W^T) + P~ U (P~ zero above the diagonal)
+            f32x4 yacc = qacc * rqv;
+            qacc = zero4();
+#pragma unroll
+            for (int j = 0; j < NPB; j += 2) {
+                if (j > w) break;
+                yacc = mfma_split(py[j], py[j + 1], *reinterpret_cast<const uint4*>(lane16(Ub, j)),
+                                  *reinterpret_cast<const uint4*>(lane16(Ub, j + 1)), yacc);
+            }
+            load_p(unext);
+            const int t0 = n * C;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yacc[e]), yrsrc,
+                                                      ((t0 + 16 * w + 4 * g4 + e) * a.d_v + vcol) * 4, 0, 0);
+        }
         // W^T += K^T (rho_k o U) for this wave's d-tiles
         f32x4 odd[NDP];
 #pragma unroll
@@ -1293,7 +1342,9 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     else e = a.NDP == 1 ? launch_chain_ndp<BF16, C, 1>(a, stream)
                         : (a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream) : hipErrorInvalidValue);
     if (e != hipSuccess) return e;
-    if (NU > 0) {
+    // the fp32 staged chain forms the outputs itself
+    const bool outputs_done = !BF16 && p.staged_ndp > 0;
+    if (NU > 0 && !outputs_done) {
         const int ntile = (C / 16) * (a.d_v / 16);
         const int64_t grid = NU * ((ntile + 3) / 4);
         hipLaunchKernelGGL((delta_output_kernel<BF16, C>), dim3(static_cast<unsigned>(grid)),

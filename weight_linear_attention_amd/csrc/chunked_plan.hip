@@ -102,7 +102,9 @@ bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Chu
     // waves, ND / 4 d-tiles each.
     plan->staged_ndp = 0;
     plan->lds_chain = 0;
-    if (ND % kChainWaves == 0) {
+    // (fp32: the staged chain stores y through a buffer whose byte offsets must fit 31 bits)
+    const bool y_fits = (static_cast<int64_t>(T) + C) * d_v * 4 < (int64_t(1) << 31);
+    if (ND % kChainWaves == 0 && (bf16 || y_fits)) {
         const int sndp = ND / kChainWaves;
         const int lds = staged_chain_lds(bf16, C, sndp);
         if (lds > 0 && lds <= kMaxLdsPrep) {

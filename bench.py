@@ -14,7 +14,7 @@ already resident in HBM when timing starts.  Other workloads (--workload):
     copy_calibration                                                a 1 GiB device copy (the
                                                                     reference for HBM counters)
 
---flush (decode and DPFP workloads) writes a 1 GiB scratch buffer before every timed step,
+--flush (decode and DPFP workloads) reads a 1 GiB scratch buffer before every timed step,
 outside the timed events, so that no step finds its data in the 256 MB Infinity Cache; the
 rate then comes from per-step event pairs and `roofline.flushed` says so.
 
@@ -45,7 +45,7 @@ DEFAULT_WORKLOAD = "h8_t1024_d64_nu1_f32"
 WARMUP_SECONDS = 0.3       # default warm-up length
 EVENT_EVERY = 8            # forward workloads: event-bracketed step every EVENT_EVERY steps
 DECODE_WARM_SLICES = 64    # decode: input slices the warm-up cycles through
-FLUSH_BYTES = 1 << 30      # --flush: scratch written before every timed step
+FLUSH_BYTES = 1 << 30      # --flush: scratch read before every timed step
 
 
 def parse():
@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--chunk", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
-                   help="decode and DPFP workloads: write a 1 GiB scratch buffer before every timed "
+                   help="decode and DPFP workloads: read a 1 GiB scratch buffer before every timed "
                         "step (outside the timed events), so no step finds its data in the 256 MB "
                         "Infinity Cache; the rate is summed from per-step event pairs")
     return p.parse_args()
@@ -229,12 +229,14 @@ def main():
     torch.cuda.synchronize()
     flush = args.flush and kind in ("decode", "dpfp")
     if flush:
-        # Every timed step starts with the caches cold: a 1 GiB write (4x the Infinity Cache)
+        # Every timed step starts with the caches cold: a 1 GiB read (4x the Infinity Cache)
         # goes before it, outside its event pair; value and duration come from the step events.
-        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        # A read, not a write, so that the step does not also pay for writing back dirty lines.
+        scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         pairs = [(ev(), ev()) for _ in range(steps)]
         for i in range(steps):
-            scratch.fill_(float(i))
+            torch.sum(scratch, dim=0, out=sink)
             pairs[i][0].record()
             one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, None)
             pairs[i][1].record()
@@ -315,7 +317,7 @@ def main():
     roof["traffic"] = measured_traffic(
         unit, name if kind in ("dpfp", "decode") else f"{w.name}:c{w.chunk}")
     if flush:
-        roof["flushed"] = "a 1 GiB scratch write before every timed step; per-step events"
+        roof["flushed"] = "a 1 GiB scratch read before every timed step; per-step events"
 
     out = {
         "metric": "tokens/sec through fast-weight layer (fwd + decode step) & % of MFMA/HBM roofline",

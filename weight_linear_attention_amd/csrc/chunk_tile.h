@@ -73,29 +73,34 @@ __device__ __forceinline__ void store16(float* p, const float (&f)[16]) {
 // shift, written as 16 consecutive internal columns per shift.  The rolled operand of position
 // j for shift i is relu([k,-k]) at (j - i) mod 2 d_k, which is +-k[(j - i) mod d_k], negated
 // when j < i (the index wraps into the [-k] half).  pv = k over the 8 positions before j0
-// (cyclically), so window index 8 + e - i (mod 16) of [pv, a] is k[(j0 + e - i) mod d_k] for
-// every shift D <= 512 allows (d_k = 16: the window is the whole row, so the index is cyclic).
-// With ka = relu(k_j), kb = relu(-k_j) >= 0: ka relu(x) = relu(ka x), kb relu(-x) = relu(-(kb x)).
+// (cyclically), so window index 8 + e - i of [pv, a] is k[(j0 + e - i) mod d_k] for every
+// shift up to 4 (d_k = 16: the window is the whole row, so the index is cyclic).
+// Both factors of a product are non-negative parts of k: the positive and negative parts of the
+// window are taken once per task, and each product is then a single multiply (relu(a) relu(x)
+// equals relu(relu(a) x), so the values are the same as relu of the product).
 template <typename LT, int NU>
 __device__ __forceinline__ float dpfp_task(const float (&a)[8], const float (&pv)[8], int j0,
                                            int d_k, LT* out) {
-    float ka[8], kb[8], sum = 0.0f;
+    static_assert(NU >= 1 && NU <= 4, "window indices 8 - NU .. 15");
+    float P[16], N[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        ka[e] = relu_f(a[e]);
-        kb[e] = relu_f(-a[e]);
+    for (int m = 8 - NU; m < 16; ++m) {
+        const float r = m >= 8 ? a[m - 8] : pv[m];
+        P[m] = relu_f(r);
+        N[m] = P[m] - r;                 // relu(-r), exactly
     }
+    const bool wraps = j0 == 0;          // positions e < i of the first group wrap
+    float sum = 0.0f;
 #pragma unroll
     for (int i = 1; i <= NU; ++i) {
         float f[16];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            constexpr int kW = 16;
-            const int m = (8 + e - i + 4 * kW) % kW;         // compile-time window index
-            const float r = m >= 8 ? a[m - 8] : pv[m];
-            const float x = (j0 + e < i) ? -r : r;
-            f[2 * e] = relu_f(ka[e] * x);
-            f[2 * e + 1] = relu_f(-(kb[e] * x));
+            const int m = 8 + e - i;
+            const float xp = (e < i && wraps) ? N[m] : P[m];
+            const float xn = (e < i && wraps) ? P[m] : N[m];
+            f[2 * e] = P[8 + e] * xp;
+            f[2 * e + 1] = N[8 + e] * xn;
             sum += f[2 * e] + f[2 * e + 1];
         }
         store16(out + 2 * ((i - 1) * d_k + j0), f);

@@ -42,15 +42,23 @@ template <int I>
 __device__ __forceinline__ float dpfp_task_shift(const float (&a)[8], const float (&pv)[8], int j0,
                                                  u16* out) {
     static_assert(I >= 1 && I <= 8, "the window holds rolls of at most 8 positions");
-    float f[16], sum = 0.0f;
+    // positive and negative parts of window indices 8 - I .. 15 of [pv, a]; a product of two
+    // such parts is a single multiply
+    float P[16], N[16], f[16], sum = 0.0f;
+#pragma unroll
+    for (int m = 8 - I; m < 16; ++m) {
+        const float r = m >= 8 ? a[m - 8] : pv[m];
+        P[m] = relu_f(r);
+        N[m] = P[m] - r;                 // relu(-r), exactly
+    }
+    const bool wraps = j0 == 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        constexpr int kOff = 8 - I;
-        const int m = kOff + e;                                  // compile-time window index
-        const float r = m >= 8 ? a[m - 8] : pv[m];
-        const float x = (j0 + e < I) ? -r : r;
-        f[2 * e] = relu_f(relu_f(a[e]) * x);
-        f[2 * e + 1] = relu_f(-(relu_f(-a[e]) * x));
+        const int m = 8 - I + e;                                 // compile-time window index
+        const float xp = (e < I && wraps) ? N[m] : P[m];
+        const float xn = (e < I && wraps) ? P[m] : N[m];
+        f[2 * e] = P[8 + e] * xp;
+        f[2 * e + 1] = N[8 + e] * xn;
         sum += f[2 * e] + f[2 * e + 1];
     }
     store16(out + 2 * j0, f);

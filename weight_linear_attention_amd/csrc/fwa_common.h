@@ -84,6 +84,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr_b16x4(const void* p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// One 8-byte LDS read that the compiler does not pair with another into ds_read2_b64: the
+// element offset passes through an empty asm statement (no instruction), so no two reads share
+// a base register.  On gfx950 a paired read costs about twice the LDS cycles of two single
+// 8-byte reads, and twice that again when the halves of the pair meet on the same banks.
+__device__ __forceinline__ bf16x4 lds_read_b64_single(const u16* base, int off) {
+    __asm__("" : "+v"(off));
+    return *reinterpret_cast<const bf16x4*>(base + off);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its

@@ -175,11 +175,12 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
         f32x4 xacc = zero4(), qacc = zero4();
         {
             constexpr int NDB = 4 * NDW;                           // D / 32 k-steps
-            const u16* kr = Kt + (16 * rt + l16) * krs + 4 * g4;
-            const u16* qr = Qt + (16 * rt + l16) * krs + 4 * g4;
+            const int ro = (16 * rt + l16) * krs + 4 * g4;
+            const u16* kr = Kt;
+            const u16* qr = Qt;
             auto opnd = [&](const u16* r, int jb) {
-                const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(r + 32 * jb);
-                const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(r + 32 * jb + 16);
+                const bf16x4 x0 = lds_read_b64_single(r, ro + 32 * jb);
+                const bf16x4 x1 = lds_read_b64_single(r, ro + 32 * jb + 16);
                 return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
             };
             auto wblk = [&](int jb) {

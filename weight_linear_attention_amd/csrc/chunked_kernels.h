@@ -396,13 +396,12 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     if (32 * kb <= 16 * tt + 15) {
-                        const u16* hp = Bh + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
-                        const u16* lp = Bl + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
-                        const bf16x8 ah = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(hp),
-                                                                  *reinterpret_cast<const bf16x4*>(hp + 16),
+                        const int ho = (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const bf16x8 ah = __builtin_shufflevector(lds_read_b64_single(Bh, ho),
+                                                                  lds_read_b64_single(Bh, ho + 16),
                                                                   0, 1, 2, 3, 4, 5, 6, 7);
-                        const bf16x8 al = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(lp),
-                                                                  *reinterpret_cast<const bf16x4*>(lp + 16),
+                        const bf16x8 al = __builtin_shufflevector(lds_read_b64_single(Bl, ho),
+                                                                  lds_read_b64_single(Bl, ho + 16),
                                                                   0, 1, 2, 3, 4, 5, 6, 7);
                         acc[tt] = mfma_bf16_k32(ah, bv, acc[tt]);
                         acc[tt] = mfma_bf16_k32(al, bv, acc[tt]);
@@ -466,12 +465,11 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     if (32 * kb <= 16 * tt + 15) {
-                        const u16* hp = Ah + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
-                        const u16* lp = Al + (16 * tt + l16) * aps + 32 * kb + 4 * g4;
-                        const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(hp);
-                        const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(hp + 16);
-                        const bf16x4 o0 = *reinterpret_cast<const bf16x4*>(lp);
-                        const bf16x4 o1 = *reinterpret_cast<const bf16x4*>(lp + 16);
+                        const int ho = (16 * tt + l16) * aps + 32 * kb + 4 * g4;
+                        const bf16x4 h0 = lds_read_b64_single(Ah, ho);
+                        const bf16x4 h1 = lds_read_b64_single(Ah, ho + 16);
+                        const bf16x4 o0 = lds_read_b64_single(Al, ho);
+                        const bf16x4 o1 = lds_read_b64_single(Al, ho + 16);
                         const bf16x8 bh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
                         const bf16x8 bl = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll

@@ -445,11 +445,12 @@ __global__ __launch_bounds__(4 * C, 512 / (4 * C)) void delta_stream_sliced_kern
         f32x4 xacc[NCT], qacc[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) xacc[ct] = qacc[ct] = zero4();
-        const u16* kr = Ks + (16 * w + l16) * ss + 4 * g4;
-        const u16* qr = Qs + (16 * w + l16) * ss + 4 * g4;
+        const int ro = (16 * w + l16) * ss + 4 * g4;
+        const u16* kr = Ks;
+        const u16* qr = Qs;
         auto opnd = [&](const u16* r, int kk) {
-            const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(r + 32 * kk);
-            const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(r + 32 * kk + 16);
+            const bf16x4 x0 = lds_read_b64_single(r, ro + 32 * kk);
+            const bf16x4 x1 = lds_read_b64_single(r, ro + 32 * kk + 16);
             return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
         };
 #pragma unroll

@@ -96,6 +96,20 @@ def stream_kernels(w):
         " + delta_stream_kernel"
 
 
+def chunked_kernels(w):
+    """Kernel names of the chunked path for this shape, by the planner's rule for the shapes the
+    benchmark runs (the staged chain where D's 16-row tiles split over 4 compute waves: for bf16
+    at chunk 64 its direct variant, for fp32 with the outputs formed in the chain itself)."""
+    staged = (w.D // 16) % 4 == 0
+    if staged and w.dtype == "f32":
+        return "delta_prep_kernel + delta_chain_staged_kernel (outputs in the chain)"
+    if staged and w.chunk == 64:
+        return "delta_prep_kernel + delta_chain_direct_kernel + delta_output_kernel"
+    if staged:
+        return "delta_prep_kernel + delta_chain_staged_kernel + delta_output_kernel"
+    return "delta_prep_kernel + delta_chain_kernel + delta_output_kernel"
+
+
 def measured_traffic(unit, workload):
     """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken on the
     current kernel sources for this workload; otherwise None."""
@@ -291,14 +305,13 @@ def main():
             ach = nbytes / (main_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": ach / PEAK_HBM_GBPS}
-        kname = {"chunked": "fwa_delta_forward, chunked: delta_prep_kernel + delta_chain_kernel + "
-                            "delta_output_kernel",
+        kname = {"chunked": "fwa_delta_forward, chunked: " + chunked_kernels(w),
                  "stream": "fwa_delta_forward, stream: " + stream_kernels(w),
                  "fused": "fwa_delta_forward, fused: delta_forward_kernel"}[unit]
         roof.update(kernel=kname, algorithmic_flops=flops, algorithmic_bytes=nbytes,
                     mean_launch_ms=main_ms)
         if w.dtype == "f32" and unit == "chunked":
-            roof["note"] = ("fp32 inputs and state; the chain and output contractions run on the "
+            roof["note"] = ("fp32 inputs and state; the prep's and the chain's contractions run on the "
                             "bf16 MFMA with fp32 operands split into bf16 hi + lo pairs (three "
                             "products, about 2^-16 relative); the peak quoted is the fp32 MFMA one")
     else:

@@ -1015,6 +1015,11 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
 // register set, so every register index is static; the loop body has no branches around memory
 // operations (prefetches past the last chunk re-read it), so every wait covers only the loads
 // it needs.
+// The kernel also forms the outputs: wave w accumulates Q W^T for row tile w from the W^T copy
+// GEMM1 reads, and after the second barrier adds P~ U from U (kept in LDS as well) and scales
+// by rho_q; Q, P~ and rho_q travel in the register sets with the other operands, and y goes out
+// through a range-checked buffer store.  No chunk-start memories or U go to the workspace and
+// no output kernel runs.
 template <bool BF16, int C, int NDP>
 __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel(ChunkArgs a) {
     using LT = typename ChunkTypes<BF16>::LT;
@@ -1024,6 +1029,8 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
     static_assert(NDP % pair == 0, "bf16 waves hold whole d-tile pairs");
     __shared__ __attribute__((aligned(1024))) char X[NDB * 1024];   // W^T copy
     __shared__ __attribute__((aligned(1024))) char Ub[NT * 1024];   // rho_k o U, fp32 tiles
+    __shared__ __attribute__((aligned(1024))) char Uo[NT * 1024];   // U, fp32 tiles
+    static_assert(BF16, "the direct chain serves bf16 inputs");
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1037,8 +1044,6 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
     const int64_t ulast = u0 + NC - 1;
     const int64_t szCD = static_cast<int64_t>(C) * D * sizeof(LT);
     const int64_t szUy = static_cast<int64_t>(C) * a.d_v * 4;
-    const int64_t szWn = static_cast<int64_t>(D) * a.d_v * sizeof(LT);
-    const int64_t szUn = static_cast<int64_t>(C) * a.d_v * sizeof(LT);
     auto lane16 = [&](char* base, int blk) { return base + blk * 1024 + l * 16; };
     const char* wyB = a.ws + a.o_wy + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
     const char* ktB = a.ws + a.o_kt + (static_cast<int64_t>(dt0) * NTB * 64 + l) * 16;
@@ -1061,6 +1066,24 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
         uy[set] = *reinterpret_cast<const f32x4*>(uyB + uu * szUy);
         rk[set] = *reinterpret_cast<const f32x4*>(rkB + uu * C);
     };
+    // output operands: Q blocks and P~ blocks of row tile w, rho_q of its rows
+    uint4 qy[2][NDB], py[2][NTB];
+    f32x4 rq[2];
+    const char* qaB = a.ws + a.o_qa + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
+    const char* paB = a.ws + a.o_pa + (static_cast<int64_t>(w) * NTB * 64 + l) * 16;
+    const float* rqB = reinterpret_cast<const float*>(a.ws + a.o_rq) + 16 * w + 4 * g4;
+    const int64_t szCC = static_cast<int64_t>(C) * C * sizeof(LT);
+    auto load_qp = [&](int set, int64_t uu) {
+#pragma unroll
+        for (int j = 0; j < NDB; ++j) qy[set][j] = *reinterpret_cast<const uint4*>(qaB + uu * szCD + j * 1024);
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) py[set][j] = *reinterpret_cast<const uint4*>(paB + uu * szCC + j * 1024);
+        rq[set] = *reinterpret_cast<const f32x4*>(rqB + uu * C);
+    };
+    // y of this (b, h), columns 16 r + l16, as a buffer whose range check drops rows past T
+    const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<LT*>(a.y) + static_cast<int64_t>(bh) * a.T * a.d_v, static_cast<short>(0),
+        a.T * a.d_v * static_cast<int>(sizeof(LT)), 0x00020000);
 
     f32x4 Wst[NDP];
 #pragma unroll
@@ -1080,53 +1103,44 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
     auto chunk = [&](int64_t uu, auto set_tag) {
         constexpr int SET = decltype(set_tag)::value;
         const int64_t ua = clampu(uu + 2);
-        // chunk-start memory: the LDS copy for GEMM1 and the Wn blocks for the output kernel
-        char* wn = a.ws + a.o_wn + uu * szWn;
+        // chunk-start memory: the LDS copy for GEMM1 and Q W^T
 #pragma unroll
-        for (int i = 0; i < NDPB; ++i) {
-            uint4 val;
-            if constexpr (BF16) val = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
-            else val = __builtin_bit_cast(uint4, Wst[i]);
-            const int jb = dt0 / pair + i;
-            if constexpr (BF16) {
-                *reinterpret_cast<uint4*>(lane16(X, jb)) = val;
-                *reinterpret_cast<uint4*>(blk_ptr(wn, static_cast<int64_t>(jb) * NVT + r, l)) = val;
-            } else {
-                // split format for GEMM1 and for the output kernel's Q W^T
-                store_split(lane16(X, jb & ~1), jb, Wst[i]);
-                store_split2(blk_ptr(wn, static_cast<int64_t>(jb & ~1) * NVT + r, l),
-                             blk_ptr(wn, static_cast<int64_t>(jb | 1) * NVT + r, l), jb, Wst[i]);
-            }
-        }
+        for (int i = 0; i < NDPB; ++i)
+            *reinterpret_cast<uint4*>(lane16(X, dt0 / pair + i)) = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
         lds_barrier();                                               // B1: W^T copy complete
-        // S = W_y W^T for row tile w, two accumulators over alternating k-blocks
-        f32x4 s0 = zero4(), s1 = zero4();
+        // S = W_y W^T and Q W^T for row tile w, two accumulators each over alternating k-blocks
+        f32x4 s0 = zero4(), s1 = zero4(), q0 = zero4(), q1 = zero4();
 #pragma unroll
         for (int j = 0; j < NDB; ++j) {
-            const uint4 bv = *reinterpret_cast<const uint4*>(lane16(X, j));
+            const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(lane16(X, j)));
             f32x4& acc = (j & 1) ? s1 : s0;
-            if constexpr (BF16) {
-                acc = mfma_bf16_k32(as_bf16x8(wy[SET][j]), as_bf16x8(bv), acc);
-            } else {
-                const f32x4 af = as_f32x4(wy[SET][j]), bf = as_f32x4(bv);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(af[e], bf[e], acc);
-            }
+            f32x4& qacc = (j & 1) ? q1 : q0;
+            acc = mfma_bf16_k32(as_bf16x8(wy[SET][j]), bv, acc);
+            qacc = mfma_bf16_k32(as_bf16x8(qy[SET][j]), bv, qacc);
         }
         load_wy(SET, ua);
         const f32x4 U = uy[SET] - (s0 + s1);
-        // U for the output kernel: B blocks (j, r); for bf16 tile w is half h = w & 1 of
-        // pair block w / 2 (slots 4 h .. 4 h + 3 of every lane)
-        char* unp = a.ws + a.o_un + uu * szUn;
-        if constexpr (BF16) {
-            *reinterpret_cast<uint2*>(blk_ptr(unp, static_cast<int64_t>(w >> 1) * NVT + r, l) + 8 * (w & 1)) =
-                make_uint2(pack_bf16x2(U[0], U[1]), pack_bf16x2(U[2], U[3]));
-        } else {
-            *reinterpret_cast<f32x4*>(blk_ptr(unp, static_cast<int64_t>(w) * NVT + r, l)) = U;
-        }
         *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rk[SET];
+        *reinterpret_cast<f32x4*>(lane16(Uo, w)) = U;
         load_uy(SET, ua);
-        lds_barrier();                                               // B2: rho_k o U complete
+        lds_barrier();                                               // B2: U and rho_k o U complete
+        {
+            // Y for row tile w = rho_q o (Q W^T) + P~ U (P~ zero above the diagonal)
+            f32x4 y = (q0 + q1) * rq[SET];
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > w) break;
+                const uint4 ub = pack_bf16x8(*reinterpret_cast<const f32x4*>(lane16(Uo, 2 * j)),
+                                             *reinterpret_cast<const f32x4*>(lane16(Uo, 2 * j + 1)));
+                y = mfma_bf16_k32(as_bf16x8(py[SET][j]), as_bf16x8(ub), y);
+            }
+            const int t0 = static_cast<int>(uu - u0) * C;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(y[e]), yrsrc,
+                                                      ((t0 + 16 * w + 4 * g4 + e) * a.d_v + vcol) * 2, 0, 0);
+            load_qp(SET, ua);
+        }
         // W^T += K^T (rho_k o U) for this wave's d-tiles
         f32x4 odd[NDP];
 #pragma unroll
@@ -1162,9 +1176,11 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
         load_wy(0, u0);
         load_uy(0, u0);
         load_kt(0, u0);
+        load_qp(0, u0);
         load_wy(1, clampu(u0 + 1));
         load_uy(1, clampu(u0 + 1));
         load_kt(1, clampu(u0 + 1));
+        load_qp(1, clampu(u0 + 1));
     }
     int n = 0;
     for (; n + 1 < NC; n += 2) {
@@ -1318,8 +1334,10 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     hipError_t e;
     bool direct = false;
     if constexpr (BF16 && C == 64) {
-        // bf16: the direct chain (two chunks of register lookahead) over the staged one
-        if (p.staged_ndp > 0) {
+        // bf16: the direct chain (two chunks of register lookahead, outputs formed in the chain)
+        // over the staged one, where y's byte offsets fit its buffer's 31-bit range
+        const bool y_fits = (static_cast<int64_t>(a.T) + C) * a.d_v * 2 < (int64_t(1) << 31);
+        if (p.staged_ndp > 0 && y_fits) {
             const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.BH) * (a.d_v / 16)));
             if (p.staged_ndp == 2)
                 hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 2>), grid, dim3(64 * kChainWaves), 0, stream, a);
@@ -1340,8 +1358,8 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     else e = a.NDP == 1 ? launch_chain_ndp<BF16, C, 1>(a, stream)
                         : (a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream) : hipErrorInvalidValue);
     if (e != hipSuccess) return e;
-    // the fp32 staged chain forms the outputs itself
-    const bool outputs_done = !BF16 && p.staged_ndp > 0;
+    // the fp32 staged chain and the bf16 direct chain form the outputs themselves
+    const bool outputs_done = (!BF16 && p.staged_ndp > 0) || direct;
     if (NU > 0 && !outputs_done) {
         const int ntile = (C / 16) * (a.d_v / 16);
         const int64_t grid = NU * ((ntile + 3) / 4);

@@ -97,15 +97,14 @@ def stream_kernels(w):
 
 
 def chunked_kernels(w):
-    """Kernel names of the chunked path for this shape, by the planner's rule for the shapes the
-    benchmark runs (the staged chain where D's 16-row tiles split over 4 compute waves: for bf16
-    at chunk 64 its direct variant, for fp32 with the outputs formed in the chain itself)."""
-    staged = (w.D // 16) % 4 == 0
-    if staged and w.dtype == "f32":
+    """Kernel names of the chunked path for this shape, by the planner's rule (the staged chain
+    for fp32 D 64 / 128 and bf16 D 128 / 256, as its direct variant for bf16 at chunk 64; both
+    form the outputs themselves)."""
+    if w.dtype == "f32" and w.D in (64, 128):
         return "delta_prep_kernel + delta_chain_staged_kernel (outputs in the chain)"
-    if staged and w.chunk == 64:
-        return "delta_prep_kernel + delta_chain_direct_kernel + delta_output_kernel"
-    if staged:
+    if w.dtype == "bf16" and w.D in (128, 256) and w.chunk == 64:
+        return "delta_prep_kernel + delta_chain_direct_kernel (outputs in the chain)"
+    if w.dtype == "bf16" and w.D in (128, 256):
         return "delta_prep_kernel + delta_chain_staged_kernel + delta_output_kernel"
     return "delta_prep_kernel + delta_chain_kernel + delta_output_kernel"
 

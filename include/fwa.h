@@ -104,10 +104,14 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *   T == 0 leaves y untouched and writes W_final = W0 (or zeros).  B*H == 0 is a no-op.
  *   T need not be a multiple of chunk.
  *   Three implementations compute the same result (within the tolerances above):
- *     chunked  three launches: every chunk's memory-independent part in parallel, then the
- *              memory carried through the chunks, then the outputs.  It needs a workspace of
- *              B*H*ceil(T/chunk) * (3*chunk*D + chunk*chunk + D*d_v + chunk*d_v) elements of
- *              `dtype` plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values.  The library
+ *     chunked  every chunk's memory-independent part in parallel, then the memory carried
+ *              through the chunks.  The chain forms the outputs itself for fp32 with D in
+ *              {64, 128} and for bf16 at chunk 64 with D in {128, 256} (two launches; y of
+ *              one (b, h) under 2 GiB); otherwise a third launch forms them from the
+ *              chunk-start memories and U that the chain leaves in the workspace.  The
+ *              workspace holds B*H*ceil(T/chunk) * (3*chunk*D + chunk*chunk) elements of
+ *              `dtype`, plus B*H*ceil(T/chunk) * (D*d_v + chunk*d_v) more where the third
+ *              launch runs, plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values.  The library
  *              keeps one workspace per (device, stream) for reuse by later calls on that
  *              stream (they run in stream order, so reuse needs no synchronisation).  A call
  *              that needs more than the stream's workspace holds synchronises `stream`, frees

@@ -137,10 +137,15 @@ def test_step_empty_batch_is_noop():
 # ------------------------------------------------------------------ forward implementation choice
 
 def _workspace_formula(B, H, T, d_k, d_v, nu, chunk, es):
-    """The chunked path's workspace as fwa.h states it."""
+    """The chunked path's workspace as fwa.h states it: the chunk-start memories and U only
+    where the outputs take a launch of their own."""
     D = 2 * d_k * nu
     nc = -(-T // chunk)
-    per_chunk = 3 * chunk * D + chunk * chunk + D * d_v + chunk * d_v
+    if es == 4:
+        chain_outputs = D in (64, 128) and (T + chunk) * d_v * 4 < 2 ** 31
+    else:
+        chain_outputs = chunk == 64 and D in (128, 256) and (T + chunk) * d_v * 2 < 2 ** 31
+    per_chunk = 3 * chunk * D + chunk * chunk + (0 if chain_outputs else D * d_v + chunk * d_v)
     return B * H * nc * per_chunk * es + B * H * nc * chunk * (d_v + 2) * 4
 
 
@@ -184,6 +189,32 @@ def test_forward_info_auto_choice(shape, dtype, path, monkeypatch):
         assert ws == _stream_workspace_formula(B, H, T, chunk)
     else:
         assert ws == 0
+
+
+@pytest.mark.parametrize("shape,dtype,chain_outputs", [
+    ((1, 2, 100, 32, 32, 1, 64), "f32", True),      # D 64: the staged chain forms y
+    ((1, 2, 100, 64, 32, 1, 32), "f32", True),      # D 128 at chunk 32
+    ((1, 2, 100, 16, 16, 1, 32), "f32", False),     # D 32: the output launch runs
+    ((1, 2, 100, 64, 32, 2, 32), "f32", False),     # D 256
+    ((1, 2, 100, 64, 32, 1, 64), "bf16", True),     # bf16 chunk 64, D 128: direct chain
+    ((1, 2, 100, 64, 32, 1, 32), "bf16", False),    # bf16 chunk 32: staged chain + outputs
+    ((1, 2, 100, 64, 32, 3, 64), "bf16", False),    # bf16 D 384
+])
+def test_forward_info_chunked_workspace(shape, dtype, chain_outputs, monkeypatch):
+    """The chunked workspace leaves out the chunk-start memories and U exactly where the chain
+    forms the outputs itself."""
+    import torch
+    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
+    B, H, T, d_k, d_v, nu, chunk = shape
+    es = 2 if dtype == "bf16" else 4
+    path, ws = fwa.delta_forward_info(B, H, T, d_k, d_v, nu, chunk,
+                                      torch.bfloat16 if dtype == "bf16" else torch.float32)
+    D, nc = 2 * d_k * nu, -(-T // chunk)
+    extra = B * H * nc * (D * d_v + chunk * d_v) * es
+    assert path == "chunked"
+    assert ws == _workspace_formula(B, H, T, d_k, d_v, nu, chunk, es)
+    base = B * H * nc * ((3 * chunk * D + chunk * chunk) * es + chunk * (d_v + 2) * 4)
+    assert ws == base + (0 if chain_outputs else extra)
 
 
 def test_forward_info_env_override(monkeypatch):

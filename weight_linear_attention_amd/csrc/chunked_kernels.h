@@ -1335,9 +1335,8 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     bool direct = false;
     if constexpr (BF16 && C == 64) {
         // bf16: the direct chain (two chunks of register lookahead, outputs formed in the chain)
-        // over the staged one, where y's byte offsets fit its buffer's 31-bit range
-        const bool y_fits = (static_cast<int64_t>(a.T) + C) * a.d_v * 2 < (int64_t(1) << 31);
-        if (p.staged_ndp > 0 && y_fits) {
+        // over the staged one
+        if (p.direct) {
             const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.BH) * (a.d_v / 16)));
             if (p.staged_ndp == 2)
                 hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 2>), grid, dim3(64 * kChainWaves), 0, stream, a);
@@ -1359,7 +1358,7 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
                         : (a.NDP == 2 ? launch_chain_ndp<BF16, C, 2>(a, stream) : hipErrorInvalidValue);
     if (e != hipSuccess) return e;
     // the fp32 staged chain and the bf16 direct chain form the outputs themselves
-    const bool outputs_done = (!BF16 && p.staged_ndp > 0) || direct;
+    const bool outputs_done = p.chain_outputs;
     if (NU > 0 && !outputs_done) {
         const int ntile = (C / 16) * (a.d_v / 16);
         const int64_t grid = NU * ((ntile + 3) / 4);

@@ -114,6 +114,13 @@ bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, Chu
     }
     // the staged chain kernel takes fp32 operands in the split bf16 hi + lo format
     plan->args.split = !bf16 && plan->staged_ndp > 0;
+    // bf16 at chunk 64 runs the direct variant (y through a buffer whose byte offsets must fit
+    // 31 bits); it and the fp32 staged kernel form y in the chain, so the workspace ends
+    // before the chunk-start memories and U that the output kernel would read
+    const bool ybf_fits = (static_cast<int64_t>(T) + C) * d_v * 2 < (int64_t(1) << 31);
+    plan->direct = bf16 && C == 64 && plan->staged_ndp > 0 && ybf_fits;
+    plan->chain_outputs = plan->direct || (!bf16 && plan->staged_ndp > 0);
+    if (plan->chain_outputs) plan->ws_bytes = a.o_wn;
     return true;
 }
 

@@ -75,6 +75,8 @@ struct ChunkPlan {
     int64_t ws_bytes;
     int staged_ndp;      // > 0: the staged chain kernel with this many d-tiles per compute wave
     int lds_chain;       // its LDS bytes
+    bool direct;         // bf16, chunk 64: the direct chain variant of the staged decomposition
+    bool chain_outputs;  // the chain forms y itself (no chunk-start memories, no output launch)
 };
 
 // hipFuncSetAttribute(kernel, MaxDynamicSharedMemorySize, bytes) once per (kernel, device,

@@ -98,6 +98,8 @@ FWD_CASES = [
     ("h8_t1024_d64_nu1_f32", {"chunk": 32, "T": 1000}),
     ("h8_t1024_d64_nu1_f32", {"T": 300, "w0_std": 0.05, "nu": 2, "chunk": 32}),
     ("h8_t1024_d64_nu1_f32", {"T": 200, "d_k": 32, "nu": 3, "d_v": 32}),
+    # more chunks (576) than prep workgroups fit at once, ragged tail: the persistent prep
+    ("h8_t1024_d64_nu1_f32", {"B": 3, "T": 1500, "w0_std": 0.05}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"T": 1000, "chunk": 32}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 333, "chunk": 16, "d_v": 16}),

@@ -134,8 +134,47 @@ constexpr int kPrepThreads = 512, kPrepWaves = kPrepThreads / 64;
 
 // LITE (bf16 only, for the streaming forward): stage k, q and beta only; write PA, RK, RQ and
 // A'' = A diag(beta) as hi and lo A-operand blocks (AH, AL); no K^T, Q, W_y or U_y.
-template <bool BF16, int C, bool LITE = false>
-__global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a) {
+// Raw rows of one chunk in registers: 16-byte units e = tid + kPrepThreads i of the k, q and v
+// rows (d_k, d_v <= 128) and the chunk's beta logit of row tid.
+template <bool BF16, int C>
+struct PrepStage {
+    static constexpr int NU16 = (C * 128 * (BF16 ? 2 : 4) / 16 + kPrepThreads - 1) / kPrepThreads;
+    uint4 k[NU16], q[NU16], v[NU16];
+    float bl;
+};
+
+// Issue the loads of chunk `blk`'s raw rows into `st`.  A unit past the sequence end reads the
+// chunk's first unit (always in range); staging zeroes it.
+template <bool BF16, int C, bool LITE>
+__device__ __forceinline__ void prep_stage_load(const ChunkArgs& a, int64_t blk, PrepStage<BF16, C>& st) {
+    using LT = typename ChunkTypes<BF16>::LT;
+    const int tid = threadIdx.x, d_k = a.d_k, d_v = a.d_v, T = a.T;
+    const BhIndex bi = xcd_local(blk, a.BH, a.NC);
+    const int t0 = static_cast<int>(bi.i) * C, Cc = min(C, T - t0);
+    const int64_t row0 = static_cast<int64_t>(bi.bh) * T + t0;
+    const char* kc = reinterpret_cast<const char*>(static_cast<const LT*>(a.k) + row0 * d_k);
+    const char* qc = reinterpret_cast<const char*>(static_cast<const LT*>(a.q) + row0 * d_k);
+    const char* vc = reinterpret_cast<const char*>(static_cast<const LT*>(a.v) + row0 * d_v);
+    const int kb = d_k * static_cast<int>(sizeof(LT)), vb = d_v * static_cast<int>(sizeof(LT));
+#pragma unroll
+    for (int i = 0; i < PrepStage<BF16, C>::NU16; ++i) {
+        const int e = tid + kPrepThreads * i;
+        if (kPrepThreads * i < C * kb / 16) {              // uniform over the workgroup
+            const int ek = e < C * kb / 16 && (e * 16) / kb < Cc ? e * 16 : 0;
+            st.k[i] = *reinterpret_cast<const uint4*>(kc + ek);
+            st.q[i] = *reinterpret_cast<const uint4*>(qc + ek);
+        }
+        if (!LITE && kPrepThreads * i < C * vb / 16) {
+            const int ev = e < C * vb / 16 && (e * 16) / vb < Cc ? e * 16 : 0;
+            st.v[i] = *reinterpret_cast<const uint4*>(vc + ev);
+        }
+    }
+    st.bl = to_f32(static_cast<const LT*>(a.bl)[row0 + (tid < Cc ? tid : 0)]);
+}
+
+template <bool BF16, int C, bool LITE, bool PERSIST>
+__device__ __forceinline__ void prep_chunk(const ChunkArgs& a, int64_t blk, int64_t blk_next,
+                                           PrepStage<BF16, C>& st) {
     using LT = typename ChunkTypes<BF16>::LT;
     constexpr int pair = ChunkTypes<BF16>::pair;
     constexpr int NT = C / 16, NTB = NT / pair;
@@ -152,42 +191,41 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
     float* rhoq = rhok + C;
     float* betas = rhoq + C;
 
-    const int tid = threadIdx.x, l = tid & 63;
+    // In the chunk loop the lane index passes through an empty asm statement in every chunk, so
+    // the per-lane address arithmetic below is recomputed per chunk instead of hoisted out of
+    // the loop (where it would stay live across the whole body).
+    int tid_opaque = static_cast<int>(threadIdx.x);
+    if constexpr (PERSIST) __asm__ volatile("" : "+v"(tid_opaque));
+    const int tid = tid_opaque, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = l & 15, g4 = l >> 4;
     const int d_k = a.d_k, d_v = a.d_v, D = a.D, T = a.T, krs = a.krs;
     const int ND = D / 16, NDB = ND / pair, NVT = d_v / 16;
-    const BhIndex bi = xcd_local(blockIdx.x, a.BH, a.NC);
+    const BhIndex bi = xcd_local(blk, a.BH, a.NC);
     const int bh = bi.bh, n = static_cast<int>(bi.i);
     const int64_t u = static_cast<int64_t>(bh) * a.NC + n;    // unit (b, h, chunk n)
     const int t0 = n * C, Cc = min(C, T - t0);
-    const int64_t row0 = static_cast<int64_t>(bh) * T + t0;
 
-    // ---- stage the chunk's raw k, q, v rows (zeros past the sequence end) and beta
+    // ---- stage the chunk's raw k, q, v rows (zeros past the sequence end) and beta from the
+    //      registers loaded earlier, then issue the next chunk's loads into them
     {
-        const char* kc = reinterpret_cast<const char*>(static_cast<const LT*>(a.k) + row0 * d_k);
-        const char* qc = reinterpret_cast<const char*>(static_cast<const LT*>(a.q) + row0 * d_k);
-        const char* vc = reinterpret_cast<const char*>(static_cast<const LT*>(a.v) + row0 * d_v);
         const int kb = d_k * static_cast<int>(sizeof(LT)), vb = d_v * static_cast<int>(sizeof(LT));
-        // A unit past the sequence end reads the chunk's first unit (always in range) and is
-        // zeroed by the mask.
         auto masked = [](uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); };
-        for (int e = tid; e < C * kb / 16; e += kPrepThreads) {
-            const bool ok = (e * 16) / kb < Cc;
-            const int off = ok ? e * 16 : 0;
-            const uint32_t m = ok ? 0xffffffffu : 0u;
-            reinterpret_cast<uint4*>(Xk)[e] = masked(*reinterpret_cast<const uint4*>(kc + off), m);
-            reinterpret_cast<uint4*>(Xq)[e] = masked(*reinterpret_cast<const uint4*>(qc + off), m);
+#pragma unroll
+        for (int i = 0; i < PrepStage<BF16, C>::NU16; ++i) {
+            const int e = tid + kPrepThreads * i;
+            const uint32_t mk = (e * 16) / kb < Cc ? 0xffffffffu : 0u;
+            if (e < C * kb / 16) {
+                reinterpret_cast<uint4*>(Xk)[e] = masked(st.k[i], mk);
+                reinterpret_cast<uint4*>(Xq)[e] = masked(st.q[i], mk);
+            }
+            if constexpr (!LITE) {
+                const uint32_t mv = (e * 16) / vb < Cc ? 0xffffffffu : 0u;
+                if (e < C * vb / 16) reinterpret_cast<uint4*>(Xv)[e] = masked(st.v[i], mv);
+            }
         }
-        for (int e = tid; e < (LITE ? 0 : C * vb / 16); e += kPrepThreads) {
-            const bool ok = (e * 16) / vb < Cc;
-            const int off = ok ? e * 16 : 0;
-            const uint32_t m = ok ? 0xffffffffu : 0u;
-            reinterpret_cast<uint4*>(Xv)[e] = masked(*reinterpret_cast<const uint4*>(vc + off), m);
-        }
-        if (tid < C)
-            betas[tid] = tid < Cc ? sigmoid_stable(to_f32(static_cast<const LT*>(a.bl)[row0 + tid]))
-                                  : 0.0f;
+        if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(st.bl) : 0.0f;
+        if (blk_next != blk) prep_stage_load<BF16, C, LITE>(a, blk_next, st);
     }
     lds_barrier();
 
@@ -529,6 +567,29 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
                 if (a.split) store_split(blk_ptr(wy, tt * NDB + (dt & ~1), l), dt, acc[tt]);
                 else *reinterpret_cast<f32x4*>(blk_ptr(wy, tt * NDB + dt, l)) = acc[tt];
             }
+        }
+    }
+}
+
+// The prep kernel.  One workgroup per chunk; or, with PERSIST, where there are more chunks than
+// workgroups fit at once, each workgroup takes chunks blockIdx.x, + gridDim.x, ... (the launch
+// sizes the grid to the resident workgroups, a multiple of 8, so every chunk a workgroup takes
+// keeps its XCD) and the next chunk's raw rows load into registers while the current one is
+// processed.
+template <bool BF16, int C, bool LITE = false, bool PERSIST = false>
+__global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a) {
+    PrepStage<BF16, C> st;
+    if constexpr (!PERSIST) {
+        prep_stage_load<BF16, C, LITE>(a, blockIdx.x, st);
+        prep_chunk<BF16, C, LITE, false>(a, blockIdx.x, blockIdx.x, st);
+    } else {
+        const int64_t total = static_cast<int64_t>(a.BH) * a.NC;
+        int64_t blk = blockIdx.x;
+        if (blk < total) prep_stage_load<BF16, C, LITE>(a, blk, st);
+        for (; blk < total; blk += gridDim.x) {
+            const int64_t nxt = blk + gridDim.x < total ? blk + gridDim.x : blk;
+            prep_chunk<BF16, C, LITE, true>(a, blk, nxt, st);
+            lds_barrier();                 // LDS of this chunk is dead before the next staging
         }
     }
 }
@@ -1325,10 +1386,20 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     const ChunkArgs& a = p.args;
     const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
     if (NU > 0) {
-        auto prep = delta_prep_kernel<BF16, C>;
-        hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prep), p.lds_prep);
+        // one workgroup per chunk where all chunks fit at once, else the persistent form
+        auto prep1 = delta_prep_kernel<BF16, C, false, false>;
+        auto prepp = delta_prep_kernel<BF16, C, false, true>;
+        hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prepp), p.lds_prep);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
+        unsigned grid = 0;
+        e = resident_grid(reinterpret_cast<const void*>(prepp), kPrepThreads, p.lds_prep, NU, &grid);
+        if (e != hipSuccess) return e;
+        if (static_cast<int64_t>(grid) < NU) {
+            hipLaunchKernelGGL(prepp, dim3(grid), dim3(kPrepThreads), p.lds_prep, stream, a);
+        } else {
+            if ((e = ensure_lds_attr(reinterpret_cast<const void*>(prep1), p.lds_prep)) != hipSuccess) return e;
+            hipLaunchKernelGGL(prep1, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipError_t e;

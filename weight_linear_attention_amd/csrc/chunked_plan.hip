@@ -25,6 +25,35 @@ hipError_t ensure_lds_attr(const void* kernel, int bytes) {
     return e;
 }
 
+// Workgroups of `kernel` (threads, lds bytes) that fit on the device at once, times its CUs,
+// rounded down to a multiple of 8 (so a workgroup that strides through its chunks by the grid
+// size stays on one XCD); at most `want` and at least 1.  Cached per (kernel, device, lds).
+hipError_t resident_grid(const void* kernel, int threads, int lds, int64_t want, unsigned* grid) {
+    static std::mutex mu;
+    static std::map<std::pair<std::pair<const void*, int>, int>, int64_t> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int64_t cap;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = cache.find({{kernel, dev}, lds});
+        if (it != cache.end()) {
+            cap = it->second;
+        } else {
+            int per_cu = 0, cus = 0;
+            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds)) != hipSuccess) return e;
+            if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+            cap = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+            if (cap >= 8) cap &= ~static_cast<int64_t>(7);
+            cache[{{kernel, dev}, lds}] = cap;
+        }
+    }
+    const int64_t g = want < cap ? want : cap;
+    *grid = static_cast<unsigned>(g > 0 ? g : 1);
+    return hipSuccess;
+}
+
 constexpr int kMaxLdsPrep = 160 * 1024;
 
 bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, ChunkPlan* plan) {

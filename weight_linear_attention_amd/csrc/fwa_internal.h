@@ -83,6 +83,10 @@ struct ChunkPlan {
 // size): the attribute persists, so later launches skip the runtime call.
 hipError_t ensure_lds_attr(const void* kernel, int bytes);
 
+// Workgroups of `kernel` that fit on the current device at once (a multiple of 8 from 8 on),
+// capped at `want`.
+hipError_t resident_grid(const void* kernel, int threads, int lds, int64_t want, unsigned* grid);
+
 bool plan_chunked(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, ChunkPlan* plan);
 hipError_t launch_chunked(const ChunkPlan& plan, const void* q, const void* k, const void* v,
                           const void* bl, const float* W0, void* y, float* Wf, char* ws,

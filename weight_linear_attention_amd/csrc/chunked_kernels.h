@@ -1386,18 +1386,21 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     const ChunkArgs& a = p.args;
     const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
     if (NU > 0) {
-        // one workgroup per chunk where all chunks fit at once, else the persistent form
+        // the persistent form where more chunks than fit at once and it keeps as many
+        // workgroups resident as the one-chunk form, else one workgroup per chunk
         auto prep1 = delta_prep_kernel<BF16, C, false, false>;
         auto prepp = delta_prep_kernel<BF16, C, false, true>;
         hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prepp), p.lds_prep);
         if (e != hipSuccess) return e;
-        unsigned grid = 0;
+        if ((e = ensure_lds_attr(reinterpret_cast<const void*>(prep1), p.lds_prep)) != hipSuccess) return e;
+        unsigned grid = 0, cap1 = 0;
         e = resident_grid(reinterpret_cast<const void*>(prepp), kPrepThreads, p.lds_prep, NU, &grid);
         if (e != hipSuccess) return e;
-        if (static_cast<int64_t>(grid) < NU) {
+        e = resident_grid(reinterpret_cast<const void*>(prep1), kPrepThreads, p.lds_prep, INT64_MAX, &cap1);
+        if (e != hipSuccess) return e;
+        if (static_cast<int64_t>(grid) < NU && grid >= cap1) {
             hipLaunchKernelGGL(prepp, dim3(grid), dim3(kPrepThreads), p.lds_prep, stream, a);
         } else {
-            if ((e = ensure_lds_attr(reinterpret_cast<const void*>(prep1), p.lds_prep)) != hipSuccess) return e;
             hipLaunchKernelGGL(prep1, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -107,8 +107,38 @@ __device__ __forceinline__ void dpfp_slice_any(int i, const u16* Xk, const u16* 
 // diagonal) and the normalisers rho_k, rho_q (RK, RQ).
 // LDS: phase 1 holds the raw k, q rows and one K and one Q slice; phase 2 (over it) L (fp32),
 // the diagonal-block inverses, and P~ followed by A'' hi / lo over it.
-template <int C, int NU, int NTH = kSliceThreads>
-__global__ __launch_bounds__(NTH, 1) void delta_prep_sliced_kernel(ChunkArgs a) {
+// Raw k and q rows of one chunk in registers (16-byte units tid + NTH p) and its beta logit of
+// row tid.
+template <int C, int NTH>
+struct SlicedStage {
+    static constexpr int NPU = C * 8 / NTH;
+    uint4 k[NPU], q[NPU];
+    float bl;
+};
+
+// Issue the loads of chunk `blk`'s raw rows into `st`; a unit past the sequence end reads the
+// chunk's first unit (always in range), and staging zeroes it.
+template <int C, int NTH>
+__device__ __forceinline__ void sliced_stage_load(const ChunkArgs& a, int64_t blk, SlicedStage<C, NTH>& st) {
+    const int tid = threadIdx.x, T = a.T;
+    const BhIndex bi = xcd_local(blk, a.BH, a.NC);
+    const int t0 = static_cast<int>(bi.i) * C, Cc = min(C, T - t0);
+    const int64_t row0 = static_cast<int64_t>(bi.bh) * T + t0;
+    const uint4* kc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.k) + row0 * kSliceDk);
+    const uint4* qc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.q) + row0 * kSliceDk);
+#pragma unroll
+    for (int p = 0; p < SlicedStage<C, NTH>::NPU; ++p) {
+        const int e = tid + NTH * p;                   // 16-byte unit, row e / 8
+        const int ee = (e >> 3) < Cc ? e : 0;
+        st.k[p] = kc[ee];
+        st.q[p] = qc[ee];
+    }
+    st.bl = bf16_bits_to_f32(static_cast<const u16*>(a.bl)[row0 + (tid < Cc ? tid : 0)]);
+}
+
+template <int C, int NU, int NTH, bool PERSIST>
+__device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t blk, int64_t blk_next,
+                                                  SlicedStage<C, NTH>& st) {
     constexpr int NT = C / 16, NTB = NT / 2, NW = NTH / 64;
     static_assert(NW >= NT, "one wave per block column of A");
     constexpr int NP = 2 * C * (kSliceDk / 8) / NTH;
@@ -126,32 +156,31 @@ __global__ __launch_bounds__(NTH, 1) void delta_prep_sliced_kernel(ChunkArgs a) 
     float* rhoq = rhok + C;
     float* betas = rhoq + C;
 
-    const int tid = threadIdx.x, l = tid & 63;
+    // In the chunk loop the lane index passes through an empty asm statement in every chunk, so
+    // the per-lane address arithmetic is recomputed per chunk instead of hoisted out of the loop.
+    int tid_opaque = static_cast<int>(threadIdx.x);
+    if constexpr (PERSIST) __asm__ volatile("" : "+v"(tid_opaque));
+    const int tid = tid_opaque, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = l & 15, g4 = l >> 4;
     const int T = a.T, ss = a.ss, aps = a.aps;
-    const BhIndex bi = xcd_local(blockIdx.x, a.BH, a.NC);
+    const BhIndex bi = xcd_local(blk, a.BH, a.NC);
     const int bh = bi.bh, n = static_cast<int>(bi.i);
     const int64_t u = static_cast<int64_t>(bh) * a.NC + n;
     const int t0 = n * C, Cc = min(C, T - t0);
-    const int64_t row0 = static_cast<int64_t>(bh) * T + t0;
 
-    // ---- stage the chunk's raw k and q rows (zeros past the sequence end) and beta
+    // ---- stage the chunk's raw k and q rows (zeros past the sequence end) and beta from the
+    //      registers loaded earlier, then issue the next chunk's loads into them
     {
-        const uint4* kc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.k) + row0 * kSliceDk);
-        const uint4* qc = reinterpret_cast<const uint4*>(static_cast<const u16*>(a.q) + row0 * kSliceDk);
 #pragma unroll
-        for (int p = 0; p < C * 8 / NTH; ++p) {
+        for (int p = 0; p < SlicedStage<C, NTH>::NPU; ++p) {
             const int e = tid + NTH * p;               // 16-byte unit, row e / 8
-            const bool ok = (e >> 3) < Cc;
-            const uint32_t m = ok ? 0xffffffffu : 0u;
-            const uint4 rk = kc[ok ? e : 0], rq = qc[ok ? e : 0];
-            reinterpret_cast<uint4*>(Xk)[e] = make_uint4(rk.x & m, rk.y & m, rk.z & m, rk.w & m);
-            reinterpret_cast<uint4*>(Xq)[e] = make_uint4(rq.x & m, rq.y & m, rq.z & m, rq.w & m);
+            const uint32_t m = (e >> 3) < Cc ? 0xffffffffu : 0u;
+            reinterpret_cast<uint4*>(Xk)[e] = make_uint4(st.k[p].x & m, st.k[p].y & m, st.k[p].z & m, st.k[p].w & m);
+            reinterpret_cast<uint4*>(Xq)[e] = make_uint4(st.q[p].x & m, st.q[p].y & m, st.q[p].z & m, st.q[p].w & m);
         }
-        if (tid < C)
-            betas[tid] = tid < Cc ? sigmoid_stable(bf16_bits_to_f32(static_cast<const u16*>(a.bl)[row0 + tid]))
-                                  : 0.0f;
+        if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(st.bl) : 0.0f;
+        if (blk_next != blk) sliced_stage_load<C, NTH>(a, blk_next, st);
     }
     lds_barrier();
 
@@ -271,6 +300,27 @@ __global__ __launch_bounds__(NTH, 1) void delta_prep_sliced_kernel(ChunkArgs a) 
             const uint2 l1 = *reinterpret_cast<const uint2*>(Bl + at + 16);
             *reinterpret_cast<uint4*>(ah + static_cast<int64_t>(e) * 16) = make_uint4(h0.x, h0.y, h1.x, h1.y);
             *reinterpret_cast<uint4*>(al + static_cast<int64_t>(e) * 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+        }
+    }
+}
+
+// The sliced prep kernel: one workgroup per chunk, or, with PERSIST (more chunks than fit at
+// once), a grid of the resident workgroups (a multiple of 8) that walks the chunks with the grid
+// as stride, loading the next chunk's raw rows while the current one is processed.
+template <int C, int NU, int NTH = kSliceThreads, bool PERSIST = false>
+__global__ __launch_bounds__(NTH, 1) void delta_prep_sliced_kernel(ChunkArgs a) {
+    SlicedStage<C, NTH> st;
+    if constexpr (!PERSIST) {
+        sliced_stage_load<C, NTH>(a, blockIdx.x, st);
+        prep_sliced_chunk<C, NU, NTH, false>(a, blockIdx.x, blockIdx.x, st);
+    } else {
+        const int64_t total = static_cast<int64_t>(a.BH) * a.NC;
+        int64_t blk = blockIdx.x;
+        if (blk < total) sliced_stage_load<C, NTH>(a, blk, st);
+        for (; blk < total; blk += gridDim.x) {
+            const int64_t nxt = blk + gridDim.x < total ? blk + gridDim.x : blk;
+            prep_sliced_chunk<C, NU, NTH, true>(a, blk, nxt, st);
+            lds_barrier();                 // LDS of this chunk is dead before the next staging
         }
     }
 }

@@ -1,4 +1,4 @@
-// Instantiates the three-launch chunked forward for bf16 inputs and chunks of 64 rows.
+// Instantiates the chunked forward for bf16 inputs and chunks of 64 rows.
 #include "chunked_kernels.h"
 
 namespace fwa {

@@ -1,5 +1,6 @@
-// Chunked forward of the fast-weight delta rule in three launches: chunk-parallel preparation,
-// the serial pass of the memory over the chunks, and chunk-parallel outputs.
+// Chunked forward of the fast-weight delta rule: chunk-parallel preparation and the serial pass
+// of the memory over the chunks, which forms the outputs as it goes for the shapes its staged
+// and direct kernels take; elsewhere a third, chunk-parallel launch forms them.
 //
 // The recurrence ("Fast Weights Transformer" guide, xdnf.cn/news/308600, sections
 // "FastWeightsAttention / update formula" and "... / module structure and source walkthrough"):
@@ -14,8 +15,8 @@
 //  => U = U_y - W_y W^T  with  W_y = (I + L)^-1 diag(beta) K~,  U_y = (I + L)^-1 diag(beta) V
 //     Y = Q~ W^T + P~ U  with  P~ = lower_incl(Q~ K~^T),        W^T <- W^T + K~^T U.
 // W_y, U_y, P~ do not depend on the memory, so every chunk prepares them at once (prep);
-// only U = U_y - W_y W^T and the update K~^T U stay on the serial chain (chain), and Y for all
-// chunks follows from the chunk-start memories (output).
+// only U = U_y - W_y W^T and the update K~^T U stay on the serial chain (chain), and Y follows
+// from the chunk-start memory and U of each chunk (in the chain, or in the output launch).
 //
 // Workspace blocks.  Every operand the chain and output kernels read is stored as 1 KiB blocks
 // in the exact register layout of one MFMA operand (64 lanes x 16 bytes), so each wave loads a
@@ -121,7 +122,7 @@ __device__ __forceinline__ const char* blk_ptr(const char* base, int64_t blk, in
 }
 
 // ------------------------------------------------------------------------------------------
-// prep: one workgroup per chunk (b, h, n).  DPFP, G and P with the normalisers, L and its
+// prep, one chunk (b, h, n) per workgroup pass.  DPFP, G and P with the normalisers, L and its
 // diagonal-block inverses, the block inverse A = (I + L)^-1, U_y by block substitution and
 // W_y^T = K^T (A diag(beta rho_k))^T on the MFMA; writes
 //   WyA (A blocks of W_y, C x D), KtA (A blocks of K^T, D x C, raw products),

@@ -1,4 +1,4 @@
-// Host-side planning of the three-launch chunked forward: the chain kernel's split of D over
+// Host-side planning of the chunked forward: the chain kernel's split of D over
 // waves, the prep kernel's LDS layout and the workspace layout; then dispatch to the
 // (dtype, chunk) instantiation.
 #include "chunked_kernels.h"

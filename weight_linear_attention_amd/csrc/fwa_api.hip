@@ -69,7 +69,7 @@ fwa_status hip_status(hipError_t e, const char* what) {
     return fail(FWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Forward implementation: FWA_FORWARD_PATH = "chunked" (three launches with a D-wide
+// Forward implementation: FWA_FORWARD_PATH = "chunked" (two or three launches with a D-wide
 // workspace), "stream" (bf16: compact prep plus one serial kernel, a 24.5 KB-per-chunk
 // workspace), "fused" (one launch, no workspace), or unset / "auto".  Auto takes the chunked
 // path where it applies and its workspace stays within kAutoWorkspaceLimit: beyond that the

@@ -42,7 +42,7 @@ hipError_t launch_delta_forward(const FwdPlan& plan, const void* q, const void* 
                                 float* Wf, int BH, int H, int T, int d_k, int d_v, int nu, int C,
                                 bool bf16, hipStream_t stream);
 
-// Arguments of the three-launch chunked forward (prep, chain, output kernels): inputs and
+// Arguments of the chunked forward (prep, chain and, where it runs, output kernels): inputs and
 // outputs, the workspace and the byte offsets of its regions, the chain split, and the prep
 // kernel's LDS layout (byte offsets; row strides in elements).
 struct ChunkArgs {

@@ -1,5 +1,5 @@
 // Streaming forward of the fast-weight delta rule for bf16 inputs: the serial pass over the
-// chunks without the D-wide workspace of the three-launch path.
+// chunks without the D-wide workspace of the chunked path.
 //
 // The recurrence ("Fast Weights Transformer" guide, xdnf.cn/news/308600, sections
 // "FastWeightsAttention / update formula" and "... / module structure and source walkthrough")

@@ -32,6 +32,7 @@
 #include "chunk_tile.h"
 #include "fwa_internal.h"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace fwa {
@@ -146,7 +147,7 @@ struct PrepStage {
 
 // Issue the loads of chunk `blk`'s raw rows into `st`.  A unit past the sequence end reads the
 // chunk's first unit (always in range); staging zeroes it.
-template <bool BF16, int C, bool LITE>
+template <bool BF16, int C, bool LITE, int ROLE = 0>
 __device__ __forceinline__ void prep_stage_load(const ChunkArgs& a, int64_t blk, PrepStage<BF16, C>& st) {
     using LT = typename ChunkTypes<BF16>::LT;
     const int tid = threadIdx.x, d_k = a.d_k, d_v = a.d_v, T = a.T;
@@ -163,9 +164,9 @@ __device__ __forceinline__ void prep_stage_load(const ChunkArgs& a, int64_t blk,
         if (kPrepThreads * i < C * kb / 16) {              // uniform over the workgroup
             const int ek = e < C * kb / 16 && (e * 16) / kb < Cc ? e * 16 : 0;
             st.k[i] = *reinterpret_cast<const uint4*>(kc + ek);
-            st.q[i] = *reinterpret_cast<const uint4*>(qc + ek);
+            if constexpr (ROLE != 1) st.q[i] = *reinterpret_cast<const uint4*>(qc + ek);
         }
-        if (!LITE && kPrepThreads * i < C * vb / 16) {
+        if (!LITE && ROLE != 2 && kPrepThreads * i < C * vb / 16) {
             const int ev = e < C * vb / 16 && (e * 16) / vb < Cc ? e * 16 : 0;
             st.v[i] = *reinterpret_cast<const uint4*>(vc + ev);
         }
@@ -173,7 +174,10 @@ __device__ __forceinline__ void prep_stage_load(const ChunkArgs& a, int64_t blk,
     st.bl = to_f32(static_cast<const LT*>(a.bl)[row0 + (tid < Cc ? tid : 0)]);
 }
 
-template <bool BF16, int C, bool LITE, bool PERSIST>
+// ROLE 0 forms everything; with two workgroups per chunk, ROLE 1 (the K side) forms K's DPFP,
+// G, L, A, U_y, W_y, K^T and rho_k, and ROLE 2 (the Q side) forms K's and Q's DPFP, P, P~, Q and
+// rho_q.
+template <bool BF16, int C, bool LITE, bool PERSIST, int ROLE = 0>
 __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, int64_t blk, int64_t blk_next,
                                            PrepStage<BF16, C>& st) {
     using LT = typename ChunkTypes<BF16>::LT;
@@ -218,22 +222,55 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, int64_t blk, int6
             const uint32_t mk = (e * 16) / kb < Cc ? 0xffffffffu : 0u;
             if (e < C * kb / 16) {
                 reinterpret_cast<uint4*>(Xk)[e] = masked(st.k[i], mk);
-                reinterpret_cast<uint4*>(Xq)[e] = masked(st.q[i], mk);
+                if constexpr (ROLE != 1) reinterpret_cast<uint4*>(Xq)[e] = masked(st.q[i], mk);
             }
-            if constexpr (!LITE) {
+            if constexpr (!LITE && ROLE != 2) {
                 const uint32_t mv = (e * 16) / vb < Cc ? 0xffffffffu : 0u;
                 if (e < C * vb / 16) reinterpret_cast<uint4*>(Xv)[e] = masked(st.v[i], mv);
             }
         }
         if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(st.bl) : 0.0f;
-        if (blk_next != blk) prep_stage_load<BF16, C, LITE>(a, blk_next, st);
+        if (blk_next != blk) prep_stage_load<BF16, C, LITE, ROLE>(a, blk_next, st);
     }
     lds_barrier();
 
-    dpfp_chunk<LT, LT, C, kPrepThreads>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l, rhok, rhoq);
+    dpfp_chunk<LT, LT, C, kPrepThreads, ROLE != 1>(Xk, Xq, Kr, Qr, krs, d_k, a.nu, w, l, rhok, rhoq);
     lds_barrier();
 
-    {
+    if constexpr (ROLE != 0) {
+        // one side's two units (G: K rows; P: Q rows), each over four quarters of D on the eight
+        // waves; the quarters are added through LDS (over the staging rows, dead since DPFP)
+        using GP = GPTiles<C>;
+        static_assert(GP::NQ == 2, "two units per side (chunk 64)");
+        const int wu = w & 1, quarter = w >> 1, Dq = D / 4;
+        const int unit = (ROLE == 2 ? GP::NQ : 0) + wu;
+        const int ra = wu, rb = GP::NT - 1 - wu;
+        GP gp;
+        gp_compute<BF16, C, false>(gp, Kr + quarter * Dq, Qr + quarter * Dq, krs, Dq, unit, l16, g4);
+        f32x4* part = reinterpret_cast<f32x4*>(smem + a.l_x);
+        if (quarter > 0) {
+            f32x4* up = part + static_cast<int64_t>(wu * 3 + quarter - 1) * (GP::NT + 1) * 64 + l;
+#pragma unroll
+            for (int tb = 0; tb < GP::NT; ++tb) {
+                if (tb <= ra) up[tb * 64] = gp.a[0][tb];
+                if (tb <= rb) up[(ra + 1 + tb) * 64] = gp.b[0][tb];
+            }
+        }
+        lds_barrier();
+        if (quarter == 0) {
+#pragma unroll
+            for (int qq = 0; qq < 3; ++qq) {
+                const f32x4* up = part + static_cast<int64_t>(wu * 3 + qq) * (GP::NT + 1) * 64 + l;
+#pragma unroll
+                for (int tb = 0; tb < GP::NT; ++tb) {
+                    if (tb <= ra) gp.a[0][tb] += up[tb * 64];
+                    if (tb <= rb) gp.b[0][tb] += up[(ra + 1 + tb) * 64];
+                }
+            }
+        }
+        lds_barrier();   // the staging rows are dead (L and P~ go over them)
+        if (quarter == 0) gp_scale<BF16, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, unit, l16, g4);
+    } else {
         // G/P has 2 NQ <= 4 units (one per wave of 0-3); waves 4-7 take the second half of D for
         // the same units, and the halves are added through LDS (over the staging rows, dead
         // since DPFP).  Each half must be whole k-steps (32 columns bf16, 16 fp32).
@@ -304,14 +341,10 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, int64_t blk, int6
         }
     };
 
-    // ---- diagonal-block inverses (the first C threads); write-out of the Q blocks by the other
-    //      waves, and of the normalisers
-    static_assert(C <= 64, "the inverses take wave 0 alone");
-    if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
-    {
-        // QA: blocks (tt, j), j < NDB
+    // QA: blocks (tt, j), j < NDB
+    auto write_qa = [&](int e0, int estep) {
         char* qa = ws + a.o_qa + u * (static_cast<int64_t>(C) * D * sizeof(LT));
-        for (int e = tid - 64; w > 0 && e < (LITE ? 0 : NT * NDB * 64); e += kPrepThreads - 64) {
+        for (int e = e0; e < NT * NDB * 64; e += estep) {
             const int blk = e >> 6, lam = e & 63, tt = blk / NDB, j = blk % NDB;
             const LT* src = Qr + (16 * tt + (lam & 15)) * krs + 16 * pair * j + 4 * (lam >> 4);
             uint4 val;
@@ -328,10 +361,24 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, int64_t blk, int6
             }
             *reinterpret_cast<uint4*>(qa + static_cast<int64_t>(e) * 16) = val;
         }
-        if (tid < C) {
-            reinterpret_cast<float*>(ws + a.o_rk)[u * C + tid] = rhok[tid];
-            reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
-        }
+    };
+
+    if constexpr (ROLE == 2) {
+        // the Q side ends here: Q, P~ and rho_q go out
+        write_qa(tid, kPrepThreads);
+        write_pa(tid, kPrepThreads);
+        if (tid < C) reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
+        return;
+    }
+
+    // ---- diagonal-block inverses (the first C threads); write-out of the Q blocks by the other
+    //      waves, and of the normalisers
+    static_assert(C <= 64, "the inverses take wave 0 alone");
+    if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
+    if (!LITE && ROLE == 0 && w > 0) write_qa(tid - 64, kPrepThreads - 64);
+    if (tid < C) {
+        reinterpret_cast<float*>(ws + a.o_rk)[u * C + tid] = rhok[tid];
+        if constexpr (ROLE == 0) reinterpret_cast<float*>(ws + a.o_rq)[u * C + tid] = rhoq[tid];
     }
     lds_barrier();   // Li complete; Q is dead (its space holds A')
 
@@ -346,7 +393,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, int64_t blk, int6
     u16* Bl = Bh + C * a.aps;
     const int aps = a.aps;
     static_assert(NT < kPrepWaves, "waves left over for the write-outs");
-    if (w >= NT) write_pa(tid - 64 * NT, kPrepThreads - 64 * NT);
+    if (ROLE == 0 && w >= NT) write_pa(tid - 64 * NT, kPrepThreads - 64 * NT);
     if (w < NT) {
         const int tb = w;
         const float bsc = betas[16 * tb + l16];
@@ -592,6 +639,23 @@ __global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_kernel(ChunkArgs a
             prep_chunk<BF16, C, LITE, true>(a, blk, nxt, st);
             lds_barrier();                 // LDS of this chunk is dead before the next staging
         }
+    }
+}
+
+// The prep as two workgroups per chunk (chunk 64, where twice the chunks fit on the GPU at
+// once): workgroups [0, BH NC) take the K side of chunk blockIdx.x, workgroups [BH NC, 2 BH NC)
+// the Q side of chunk blockIdx.x - BH NC.
+template <bool BF16, int C>
+__global__ __launch_bounds__(kPrepThreads, 1) void delta_prep_split_kernel(ChunkArgs a) {
+    const int64_t total = static_cast<int64_t>(a.BH) * a.NC;
+    PrepStage<BF16, C> st;
+    if (static_cast<int64_t>(blockIdx.x) < total) {
+        prep_stage_load<BF16, C, false, 1>(a, blockIdx.x, st);
+        prep_chunk<BF16, C, false, false, 1>(a, blockIdx.x, blockIdx.x, st);
+    } else {
+        const int64_t blk = blockIdx.x - total;
+        prep_stage_load<BF16, C, false, 2>(a, blk, st);
+        prep_chunk<BF16, C, false, false, 2>(a, blk, blk, st);
     }
 }
 
@@ -1387,11 +1451,33 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     const ChunkArgs& a = p.args;
     const int64_t NU = static_cast<int64_t>(a.BH) * a.NC;
     if (NU > 0) {
+        // two workgroups per chunk (K side, Q side) where twice the chunks fit at once (chunk
+        // 64, D a multiple of 128 so that quarters of D are whole k-steps, and room for the
+        // quarter partials over the staging rows); FWA_PREP_SPLIT=0 turns it off
+        hipError_t e;
+        bool launched = false;
+        if constexpr (C == 64) {
+            auto preps = delta_prep_split_kernel<BF16, C>;
+            const char* env = std::getenv("FWA_PREP_SPLIT");
+            const bool allowed = !(env && env[0] == '0') && a.D % 128 == 0 &&
+                                 a.l_xv - a.l_x >= 6 * (C / 16 + 1) * 1024;
+            if (allowed) {
+                if ((e = ensure_lds_attr(reinterpret_cast<const void*>(preps), p.lds_prep)) != hipSuccess) return e;
+                unsigned caps = 0;
+                e = resident_grid(reinterpret_cast<const void*>(preps), kPrepThreads, p.lds_prep, INT64_MAX, &caps);
+                if (e != hipSuccess) return e;
+                if (2 * NU <= static_cast<int64_t>(caps)) {
+                    hipLaunchKernelGGL(preps, dim3(static_cast<unsigned>(2 * NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
+                    launched = true;
+                }
+            }
+        }
+        if (!launched) {
         // the persistent form where more chunks than fit at once and it keeps as many
         // workgroups resident as the one-chunk form, else one workgroup per chunk
         auto prep1 = delta_prep_kernel<BF16, C, false, false>;
         auto prepp = delta_prep_kernel<BF16, C, false, true>;
-        hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(prepp), p.lds_prep);
+        e = ensure_lds_attr(reinterpret_cast<const void*>(prepp), p.lds_prep);
         if (e != hipSuccess) return e;
         if ((e = ensure_lds_attr(reinterpret_cast<const void*>(prep1), p.lds_prep)) != hipSuccess) return e;
         unsigned grid = 0, cap1 = 0;
@@ -1403,6 +1489,7 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
             hipLaunchKernelGGL(prepp, dim3(grid), dim3(kPrepThreads), p.lds_prep, stream, a);
         } else {
             hipLaunchKernelGGL(prep1, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
+        }
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

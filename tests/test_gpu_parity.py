@@ -229,6 +229,31 @@ def test_forward_chunk_independence_and_determinism(monkeypatch):
         assert torch.equal(y2, outs[(p, 64)][0]) and torch.equal(W2, outs[(p, 64)][1])
 
 
+@pytest.mark.parametrize("name,ov", [("h8_t1024_d64_nu1_f32", {"T": 555, "w0_std": 0.05}),
+                                     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 700})])
+def test_chunked_prep_forms(monkeypatch, name, ov):
+    """The chunked path's prep as two workgroups per chunk (K side and Q side) and as one,
+    against the oracle and against each other; each form is deterministic."""
+    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
+    w = workload(name, **ov)
+    inp = make_inputs(w)
+    d = _dev(inp)
+    yr, Wr = oracle_forward(inp, w.nu)
+    tol = TOL[w.torch_dtype]
+    outs = {}
+    for split in ("1", "0"):
+        monkeypatch.setenv("FWA_PREP_SPLIT", split)
+        y, Wf = _forward(d, w.nu, 64)
+        ey, ew = normwise(to_f64(y), yr, 2), normwise(to_f64(Wf), Wr, 2)
+        log(f"  chunked prep split={split}: y err {ey:.3e}  W_final err {ew:.3e}")
+        assert ey <= tol and ew <= tol
+        y2, W2 = _forward(d, w.nu, 64)
+        assert torch.equal(y, y2) and torch.equal(Wf, W2)
+        outs[split] = (y, Wf)
+    assert normwise(to_f64(outs["1"][0]), to_f64(outs["0"][0]), 2) <= tol
+    assert normwise(to_f64(outs["1"][1]), to_f64(outs["0"][1]), 2) <= tol
+
+
 @pytest.mark.parametrize("kernel,prep", [("default", "full"), ("default", "sliced"), ("sliced", "sliced"),
                                          ("pc", "sliced")])
 def test_stream_prep_variants_and_chunks(monkeypatch, kernel, prep):

@@ -102,6 +102,8 @@ FWD_CASES = [
     ("h8_t1024_d64_nu1_f32", {"B": 3, "T": 1500, "w0_std": 0.05}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"T": 1000, "chunk": 32}),
+    # 6 chunks (a multiple of the direct chain's register sets), ragged tail
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 379}),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 333, "chunk": 16, "d_v": 16}),
     # chunk 128 (shift-sliced streaming path): full size, a ragged tail, d_v 32 with nu 1,
     # nu 4 (D 512) on 3 heads, and a single partial chunk

@@ -97,16 +97,21 @@ def stream_kernels(w):
 
 
 def chunked_kernels(w):
-    """Kernel names of the chunked path for this shape, by the planner's rule (the staged chain
-    for fp32 D 64 / 128 and bf16 D 128 / 256, as its direct variant for bf16 at chunk 64; both
-    form the outputs themselves)."""
+    """Kernel names of the chunked path for this shape, by the planner's rule: the prep as two
+    workgroups per chunk (K side, Q side) at chunk 64 with D a multiple of 128 where twice the
+    chunks fit the GPU at once (one prep workgroup per CU at these sizes); the staged chain for
+    fp32 D 64 / 128 and bf16 D 128 / 256, as its direct variant for bf16 at chunk 64, both
+    forming the outputs themselves."""
+    chunks = w.B * w.H * -(-w.T // w.chunk)
+    split = w.chunk == 64 and w.D % 128 == 0 and 2 * chunks <= 256
+    prep = "delta_prep_split_kernel" if split else "delta_prep_kernel"
     if w.dtype == "f32" and w.D in (64, 128):
-        return "delta_prep_kernel + delta_chain_staged_kernel (outputs in the chain)"
+        return prep + " + delta_chain_staged_kernel (outputs in the chain)"
     if w.dtype == "bf16" and w.D in (128, 256) and w.chunk == 64:
-        return "delta_prep_kernel + delta_chain_direct_kernel (outputs in the chain)"
+        return prep + " + delta_chain_direct_kernel (outputs in the chain)"
     if w.dtype == "bf16" and w.D in (128, 256):
-        return "delta_prep_kernel + delta_chain_staged_kernel + delta_output_kernel"
-    return "delta_prep_kernel + delta_chain_kernel + delta_output_kernel"
+        return prep + " + delta_chain_staged_kernel + delta_output_kernel"
+    return prep + " + delta_chain_kernel + delta_output_kernel"
 
 
 def measured_traffic(unit, workload):

@@ -3,12 +3,15 @@ MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-One step of the default workload is one pass of the whole hot path over one batch: the chunked
+One step of a forward workload is one pass of the whole hot path over one batch: the chunked
 causal forward over B x T tokens (DPFP, beta, intra-chunk work, state work, y and the final
 memory) followed by one decode step per sequence that continues from that memory.  Tokens per
-step = B * (T + 1).  Inputs are seeded synthetic tensors (weight_linear_attention_amd/synthetic.py)
-already resident in HBM when timing starts.  Other workloads (--workload):
-    b4_h8_t4096_d64_nu2_bf16_carried, b8_h16_t16384_d64_nu3_bf16   forward only
+step = B * (T + 1).  The default workload is the largest, b8_h16_t16384_d64_nu3_bf16 (8 x 16
+heads x 16384 tokens, D 384, bf16, chunk 64; --chunk 128 for the sweep's other point).  Inputs
+are seeded synthetic tensors (weight_linear_attention_amd/synthetic.py) already resident in HBM
+when timing starts.  Other workloads (--workload):
+    h8_t1024_d64_nu1_f32, b4_h8_t4096_d64_nu2_bf16_carried, tiny_t64_d16_nu1_f32
+                                                                    forward + decode step
     decode_b256_h8_d64_nu1_f32                                      one fwa_delta_step per step
     dpfp_b8_h16_t16384_d64_nu3_bf16                                 fwa_dpfp on q and k
     copy_calibration                                                a 1 GiB device copy (the
@@ -22,9 +25,8 @@ Prints ONE JSON line.  `roofline` describes the dominant call: the forward (one 
 fused path, two on the streaming path, three on the chunked path) or, for the decode and DPFP
 workloads, that kernel.
 `achieved` is its algorithmic bytes or flops divided by its mean duration, measured with HIP
-events on the launch stream over the timed region (forward workloads: event pairs around the
-calls of every 8th step; decode and DPFP: one pair around the back-to-back calls, divided by
-their number);
+events on the launch stream: one event pair around the back-to-back calls, divided by their
+number (forward workloads: a second region of back-to-back forwards after the timed steps);
 `traffic` is the HBM bytes per call that
 rocprofv3 counted on the same sources (profiles/traffic.json), or null.  `cpu_baseline` times
 the fp64 oracle on the host (rank 0 only).
@@ -41,9 +43,8 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
-DEFAULT_WORKLOAD = "h8_t1024_d64_nu1_f32"
+DEFAULT_WORKLOAD = "b8_h16_t16384_d64_nu3_bf16"
 WARMUP_SECONDS = 0.3       # default warm-up length
-EVENT_EVERY = 8            # forward workloads: event-bracketed step every EVENT_EVERY steps
 DECODE_WARM_SLICES = 64    # decode: input slices the warm-up cycles through
 FLUSH_BYTES = 1 << 30      # --flush: scratch read before every timed step
 
@@ -67,7 +68,7 @@ def parse():
 SOURCES = {
     "chunked": ("chunked_kernels.h", "chunk_tile.h"),
     "stream": ("stream_kernel.h", "stream_bf16_c64.hip", "stream_sliced.h", "stream_sliced_bf16.hip",
-               "stream_pc.h", "chunked_kernels.h", "chunk_tile.h"),
+               "chunked_kernels.h", "chunk_tile.h"),
     "fused": ("forward_kernel.h", "chunk_tile.h"),
     "decode": ("step_kernel.hip",),
     "dpfp": ("dpfp_kernel.hip",),
@@ -86,11 +87,9 @@ def stream_kernels(w):
     """Kernel names of the streaming path for this shape, by the planner's rule (chunk 128: the
     shift-sliced prep and serial kernels; chunk 64: the sliced prep for d_k 64 and nu <= 4, then
     the full-tile serial kernel where it applies, else the sliced one)."""
-    sliced_prep = w.d_k == 64 and w.nu <= 4 and os.environ.get("FWA_STREAM_PREP") != "full"
+    sliced_prep = w.d_k == 64 and w.nu <= 4
     full_ok = w.chunk == 64 and w.d_v % 32 == 0 and w.D % 128 == 0 and w.nu <= 8 and w.D <= 384
-    if w.chunk == 64 and os.environ.get("FWA_STREAM_KERNEL") == "pc":
-        return "delta_prep_sliced_kernel + delta_stream_pc_kernel"
-    if w.chunk == 128 or os.environ.get("FWA_STREAM_KERNEL") == "sliced" or not full_ok:
+    if w.chunk == 128 or not full_ok:
         return "delta_prep_sliced_kernel + delta_stream_sliced_kernel"
     return ("delta_prep_sliced_kernel" if sliced_prep else "delta_prep_kernel (compact)") + \
         " + delta_stream_kernel"
@@ -165,14 +164,13 @@ def main():
         kind, w = "dpfp", workload(name[len("dpfp_"):])
     elif name.startswith("decode_"):
         kind, w = "decode", workload(name)
-    elif name == DEFAULT_WORKLOAD:
-        w = workload(name)
     else:
-        kind, w = "prefill", workload(name)
+        w = workload(name)
     if args.chunk is not None:
         w = workload(w.name, chunk=args.chunk)
     steps = args.steps if args.steps is not None else {
-        "prefill+decode": 2000, "prefill": 50, "decode": 1024, "dpfp": 50}[kind]
+        "prefill+decode": 100 if w.B * w.H * w.T >= (1 << 20) else 1000,
+        "decode": 1024, "dpfp": 50}[kind]
     # Warm-up: --warmup steps, else as many as fill WARMUP_SECONDS (at least 3): the GPU's
     # clocks reach their steady state only after some tens of milliseconds of work.
     warmup = args.warmup
@@ -180,6 +178,7 @@ def main():
     D, BH = w.D, w.B * w.H
 
     # ------------------------------------------------------------------ inputs in HBM
+    nxt = None
     if kind == "decode":
         # DECODE_WARM_SLICES slices for the warm-up (cycled), then one fresh slice per timed step
         inp = make_decode_inputs(w, steps=DECODE_WARM_SLICES + steps)
@@ -193,10 +192,13 @@ def main():
         nxt = {n: torch.randn(w.B, w.H, dd, generator=g).to(w.torch_dtype).to(dev)
                for n, dd in (("q", w.d_k), ("k", w.d_k), ("v", w.d_v))}
         nxt["beta_logit"] = torch.randn(w.B, w.H, generator=g).to(w.torch_dtype).to(dev)
-    y = Wf = phi_q = phi_k = None
-    if kind in ("prefill", "prefill+decode"):
+    y = Wf = phi_q = phi_k = ws = None
+    if kind == "prefill+decode":
         y = torch.empty(w.B, w.H, w.T, w.d_v, dtype=w.torch_dtype, device=dev)
         Wf = torch.empty(w.B, w.H, w.d_v, D, dtype=torch.float32, device=dev)
+        unit, ws_bytes = fwa.delta_forward_info(w.B, w.H, w.T, w.d_k, w.d_v, w.nu, w.chunk,
+                                                w.torch_dtype)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if kind == "dpfp":
         phi_q = torch.empty(w.B, w.H, w.T, D, dtype=w.torch_dtype, device=dev)
         phi_k = torch.empty_like(phi_q)
@@ -204,19 +206,17 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def one_step(i, marks):
-        if kind in ("prefill", "prefill+decode"):
-            if marks:
-                marks[0].record()
-            fwa.delta_forward(d["q"], d["k"], d["v"], d["beta_logit"], d["W0"], chunk=w.chunk,
-                              nu=w.nu, out=y, W_final=Wf)
-            if marks:
-                marks[1].record()
-            if kind == "prefill+decode":
-                fwa.delta_step(nxt["q"], nxt["k"], nxt["v"], nxt["beta_logit"], Wf, nu=w.nu,
-                               out=ystep)
-                if marks:
-                    marks[2].record()
+    def forward():
+        fwa.delta_forward(d["q"], d["k"], d["v"], d["beta_logit"], d["W0"], chunk=w.chunk,
+                          nu=w.nu, out=y, W_final=Wf, workspace=ws)
+
+    def decode_next():
+        fwa.delta_step(nxt["q"], nxt["k"], nxt["v"], nxt["beta_logit"], Wf, nu=w.nu, out=ystep)
+
+    def one_step(i):
+        if kind == "prefill+decode":
+            forward()
+            decode_next()
         elif kind == "decode":
             fwa.delta_step(d["q"][i], d["k"][i], d["v"][i], d["beta_logit"][i], W, nu=w.nu,
                            out=ystep)
@@ -224,28 +224,36 @@ def main():
             fwa.dpfp(d["q"], w.nu, out=phi_q)
             fwa.dpfp(d["k"], w.nu, out=phi_k)
 
+    def region(fn, n):
+        """Milliseconds per call of fn over n back-to-back calls inside one event pair."""
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(n):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
     # Every step runs back to back, as a serving loop would, inside one event pair around the
-    # timed region.  The forward workloads also bracket the calls of every EVENT_EVERY-th step
-    # with events (forward, then decode step), which split forward from decode time: an event
-    # recorded between two launches stalls the queue for a few microseconds, so bracketing
-    # every call would slow the whole loop by about 15% on the default workload.  The decode and
-    # DPFP workloads' mean launch duration is region time / calls, gaps between launches
-    # included.
-    per_call = kind in ("prefill", "prefill+decode")
-    sampled = list(range(0, steps, EVENT_EVERY)) if per_call else []
+    # timed region (an event recorded between two launches stalls the queue for a few
+    # microseconds, so no call inside the region is bracketed).  For the forward workloads a
+    # second region of back-to-back forwards alone (and a third of decode steps alone) then
+    # gives the forward's mean duration for the roofline.
     warm_idx = lambda i: i % DECODE_WARM_SLICES if kind == "decode" else i
     if warmup is None:
         warmup, t_w = 0, time.perf_counter()
         while warmup < 3 or time.perf_counter() - t_w < WARMUP_SECONDS:
-            one_step(warm_idx(warmup), None)
+            one_step(warm_idx(warmup))
             warmup += 1
             if warmup % 64 == 0:
                 torch.cuda.synchronize()
     else:
         for i in range(warmup):
-            one_step(warm_idx(i), None)
+            one_step(warm_idx(i))
     torch.cuda.synchronize()
     flush = args.flush and kind in ("decode", "dpfp")
+    step_ms = None
     if flush:
         # Every timed step starts with the caches cold: a 1 GiB read (4x the Infinity Cache)
         # goes before it, outside its event pair; value and duration come from the step events.
@@ -256,46 +264,34 @@ def main():
         for i in range(steps):
             torch.sum(scratch, dim=0, out=sink)
             pairs[i][0].record()
-            one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, None)
+            one_step(DECODE_WARM_SLICES + i if kind == "decode" else i)
             pairs[i][1].record()
         torch.cuda.synchronize()
         main_ms = sum(a.elapsed_time(b) for a, b in pairs) / steps
         elapsed = main_ms * 1e-3 * steps
         del scratch
     else:
-        marks = {i: [ev(), ev(), ev()] for i in sampled}
-        region = (ev(), ev())
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        region[0].record()
-        for i in range(steps):
-            one_step(DECODE_WARM_SLICES + i if kind == "decode" else i, marks.get(i))
-        region[1].record()
-        torch.cuda.synchronize()
+        step_region_ms = region(lambda i: one_step(DECODE_WARM_SLICES + i if kind == "decode" else i),
+                                steps)
         elapsed = time.perf_counter() - t0
-
-    if flush:
-        pass
-    elif per_call:
-        main_ms = sum(marks[i][0].elapsed_time(marks[i][1]) for i in sampled) / len(sampled)
-    else:
-        main_ms = region[0].elapsed_time(region[1]) / steps
-    step_ms = (sum(marks[i][1].elapsed_time(marks[i][2]) for i in sampled) / len(sampled)
-               if kind == "prefill+decode" else None)
+        if kind == "prefill+decode":
+            main_ms = region(lambda i: forward(), steps)
+            step_ms = region(lambda i: decode_next(), steps)
+        else:
+            main_ms = step_region_ms
 
     # ------------------------------------------------------------------ metric + roofline
     if kind == "prefill+decode":
         tokens = w.B * (w.T + 1)
-    elif kind == "prefill":
-        tokens = w.B * w.T
     elif kind == "decode":
         tokens = w.B
     else:
         tokens = 2 * BH * w.T          # DPFP vectors (q and k) per step
     value = tokens * steps / elapsed
 
-    if kind in ("prefill", "prefill+decode"):
-        unit, _ = fwa.delta_forward_info(w.B, w.H, w.T, w.d_k, w.d_v, w.nu, w.chunk, w.torch_dtype)
+    if kind == "prefill+decode":
         flops = BH * w.T * (6 * D * w.d_v + 6 * D)
         nbytes = (BH * w.T * ((3 * w.d_k + 1) * es + w.d_v * es)
                   + BH * w.d_v * D * 4 * (1 + (d["W0"] is not None)))
@@ -313,11 +309,16 @@ def main():
                  "stream": "fwa_delta_forward, stream: " + stream_kernels(w),
                  "fused": "fwa_delta_forward, fused: delta_forward_kernel"}[unit]
         roof.update(kernel=kname, algorithmic_flops=flops, algorithmic_bytes=nbytes,
-                    mean_launch_ms=main_ms)
+                    mean_launch_ms=main_ms,
+                    timing="one event pair around %d back-to-back forwards" % steps,
+                    algorithmic_mfma_frac=flops / (main_ms * 1e-3) / (PEAK_TFLOPS[w.dtype] * 1e12))
         if w.dtype == "f32" and unit == "chunked":
+            split_peak = PEAK_TFLOPS["bf16"] / 3.0
             roof["note"] = ("fp32 inputs and state; the prep's and the chain's contractions run on the "
                             "bf16 MFMA with fp32 operands split into bf16 hi + lo pairs (three "
                             "products, about 2^-16 relative); the peak quoted is the fp32 MFMA one")
+            roof["split_bf16_ceiling"] = {"peak": split_peak, "unit": "TFLOP/s",
+                                          "frac": flops / (main_ms * 1e-3) / 1e12 / split_peak}
     else:
         if kind == "decode":
             unit = "decode"
@@ -360,8 +361,26 @@ def main():
 
     # ------------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, kind, inp, nxt if kind == "prefill+decode" else None)
+        out["cpu_baseline"] = cpu_baseline(w, kind, inp, nxt)
     print(json.dumps(out), flush=True)
+
+
+def host_cpu():
+    """The host's logical CPU count, the CPUs this process may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_count": os.cpu_count(), "usable_cpus": usable, "model": model}
 
 
 def cpu_baseline(w, kind, inp, nxt):
@@ -372,6 +391,7 @@ def cpu_baseline(w, kind, inp, nxt):
     from weight_linear_attention_amd.synthetic import to_f64
 
     threads = oracle.num_threads()
+    host = host_cpu()
     if kind == "decode":
         # 16 successive steps over all 2048 (b, h) slices (the oracle's step function)
         S = 16
@@ -382,7 +402,8 @@ def cpu_baseline(w, kind, inp, nxt):
                                       to_f64(inp["beta_logit"][s]), Wd, nu=w.nu)
         dt = time.perf_counter() - t0
         return {"value": w.B * S / dt, "unit": "tokens/s", "cores": min(threads, w.B * w.H),
-                "kind": "oracle", "sample": f"{S} decode steps x {w.B}x{w.H} slices (full state)"}
+                "kind": "oracle", "sample": f"{S} decode steps x {w.B}x{w.H} slices (full state)",
+                "threads": threads, "host": host}
     if kind == "dpfp":
         n = 65536
         x = to_f64(inp["q"].reshape(-1, w.d_k)[:n])
@@ -390,8 +411,9 @@ def cpu_baseline(w, kind, inp, nxt):
         oracle.dpfp(x, w.nu)
         dt = time.perf_counter() - t0
         return {"value": n / dt, "unit": "vectors/s", "cores": threads, "kind": "oracle",
-                "sample": f"{n} q vectors"}
-    # forward (+ decode): whole (b, h) slices, as many as needed for a bounded sample
+                "sample": f"{n} q vectors", "threads": threads, "host": host}
+    # forward (+ decode): whole (b, h) slices, as many as needed for a bounded sample (a
+    # multiple of the thread count where the flop cap allows, so every thread has work)
     BH = w.B * w.H
     nsl = min(BH, max(1, threads))
     if w.T * w.D * w.d_v * 6 * nsl > 4e10:      # cap the sample at roughly 1e10..4e10 flops
@@ -415,7 +437,9 @@ def cpu_baseline(w, kind, inp, nxt):
     tok = (w.T + (1 if nxt is not None else 0)) * nsl / w.H * reps
     return {"value": tok / dt, "unit": "tokens/s", "cores": min(threads, nsl), "kind": "oracle",
             "sample": f"{nsl} of {BH} (b,h) slices x T={w.T}"
-                      + (" + 1 decode step" if nxt is not None else "") + f", {reps} rep(s)"}
+                      + (" + 1 decode step" if nxt is not None else "") + f", {reps} rep(s)",
+            "threads": threads, "host": host,
+            "cores_note": "OpenMP threads over independent (b, h) slices: min(threads, slices)"}
 
 
 if __name__ == "__main__":

@@ -20,9 +20,12 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  Every launch goes on
- *     `stream` (0 = the legacy default stream) and FWA_OK means "enqueued".  The only state
- *     the library keeps between calls is the chunked forward's workspace (see
- *     fwa_delta_forward) and which kernels already carry their LDS-size attribute.
+ *     `stream` (0 = the legacy default stream) and FWA_OK means "enqueued".  No entry point
+ *     allocates device memory, frees it or synchronises a stream; scratch memory comes from
+ *     the caller (fwa_delta_forward's workspace).  The only state the library keeps between
+ *     calls is which kernels already carry their LDS-size attribute and how many workgroups
+ *     of a kernel fit on a device (both fixed per device), so a call after a first one on
+ *     the same device can be captured into a HIP graph.
  *   - Layouts are row-major and contiguous (the [B, H, T, d] convention of [TRF], section
  *     "Scaled dot-product attention").  The fast-weight memory W is [B, H, d_v, D] fp32
  *     (d_value x d_key orientation of [FWT], module walkthrough).
@@ -66,10 +69,11 @@ typedef enum {
 
 /* Implementation of fwa_delta_forward (see there). */
 typedef enum {
-    FWA_PATH_NONE = 0,      /* nothing to launch (B*H == 0) */
+    FWA_PATH_AUTO = 0,      /* request only: the planner's choice (what fwa_delta_forward does) */
     FWA_PATH_CHUNKED = 1,
     FWA_PATH_FUSED = 2,
-    FWA_PATH_STREAM = 3
+    FWA_PATH_STREAM = 3,
+    FWA_PATH_NONE = 4       /* report only: nothing to launch (B*H == 0) */
 } fwa_forward_path;
 
 /*
@@ -103,7 +107,15 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *               the stated tolerances.
  *   T == 0 leaves y untouched and writes W_final = W0 (or zeros).  B*H == 0 is a no-op.
  *   T need not be a multiple of chunk.
- *   Three implementations compute the same result (within the tolerances above):
+ *   workspace   device scratch owned by the caller, at least the bytes fwa_delta_forward_info
+ *               reports for the same sizes (NULL / 0 where that is 0), 16-byte aligned, not
+ *               overlapping any other argument.  The call's kernels use it in stream order on
+ *               `stream`; the caller keeps it alive and unused by other work until they have
+ *               run (memory from a stream-ordered allocator on `stream` satisfies this).  Its
+ *               contents on entry do not matter and are undefined on return.  Too small a
+ *               workspace gives FWA_ERR_INVALID_ARG before anything is launched.
+ *   Three implementations compute the same result (within the tolerances above); the planner
+ *   picks one from the sizes alone:
  *     chunked  every chunk's memory-independent part in parallel, then the memory carried
  *              through the chunks.  The chain forms the outputs itself for fp32 with D in
  *              {64, 128} and for bf16 at chunk 64 with D in {128, 256} (two launches; y of
@@ -111,13 +123,7 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *              chunk-start memories and U that the chain leaves in the workspace.  The
  *              workspace holds B*H*ceil(T/chunk) * (3*chunk*D + chunk*chunk) elements of
  *              `dtype`, plus B*H*ceil(T/chunk) * (D*d_v + chunk*d_v) more where the third
- *              launch runs, plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values.  The library
- *              keeps one workspace per (device, stream) for reuse by later calls on that
- *              stream (they run in stream order, so reuse needs no synchronisation).  A call
- *              that needs more than the stream's workspace holds synchronises `stream`, frees
- *              it and allocates a larger one (hipMalloc); workspaces live until the process
- *              ends.  A stream handle must not be destroyed and recreated while work that
- *              used its workspace is still pending.  Chunks of
+ *              launch runs, plus B*H*ceil(T/chunk)*chunk*(d_v + 2) fp32 values.  Chunks of
  *              32 or 64 rows; D in {32, 64, 96, 128, 192, 256}, and for bf16 also 384, 512;
  *              the prep kernel's working set (2*chunk*(D + 8) elements plus chunk-sized
  *              scratch) must fit the 160 KiB of LDS, which leaves out chunk 64 for fp32 D = 256
@@ -126,19 +132,16 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *              normalisers in parallel, then one serial pass per (b, h, 32 columns of d_v)
  *              that rebuilds the DPFP features from the raw rows and keeps the memory on chip.
  *              Workspace of B*H*ceil(T/chunk) * (3*chunk*chunk*2 + 2*chunk*4) bytes (24.5 KiB
- *              per chunk of 64, 97 KiB per chunk of 128), kept per (device, stream) as above.
+ *              per chunk of 64, 97 KiB per chunk of 128).
  *              Chunk 64: d_v in {32, 64}, D in {128, 256, 384}, nu <= 8; and, for d_k = 64
  *              with nu <= 4, also d_v = 16 and D = 512.  Chunk 128: d_k = 64, nu <= 4,
  *              d_v in {32, 64} (the DPFP features are built one shift block of 128 columns
  *              at a time, so D up to 512 fits on chip).
- *     fused    one launch that keeps the chunk and the memory on chip; allocates nothing.
+ *     fused    one launch that keeps the chunk and the memory on chip; no workspace.
  *              Needs the chunk's working set (3*chunk*D elements plus chunk-sized scratch)
  *              within the 160 KiB of LDS of one compute unit.
- *   The environment variable FWA_FORWARD_PATH = chunked | stream | fused | auto (default)
- *   selects one; auto takes the chunked path where it applies and its workspace is at most
- *   2 GiB, else the streaming one where it applies, else the fused one.  A forced path that
- *   does not apply gives FWA_ERR_UNSUPPORTED, an unknown value FWA_ERR_INVALID_ARG, a failed
- *   workspace allocation FWA_ERR_HIP.
+ *   The planner takes the chunked path where it applies and its workspace is at most 2 GiB,
+ *   else the streaming one where it applies, else the fused one.
  *   Implemented shapes: d_k in {16, 32, 64}, d_v in {16, 32, 64}, D = 2*d_k*nu <= 512, and
  *   the conditions of at least one implementation above; other valid shapes give
  *   FWA_ERR_UNSUPPORTED.
@@ -146,19 +149,34 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
 fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
                              const void* beta_logit, const float* W0, void* y, float* W_final,
                              int B, int H, int T, int d_k, int d_v, int nu, int chunk,
-                             fwa_dtype dtype, hipStream_t stream);
+                             fwa_dtype dtype, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
- * fwa_delta_forward_info -- which implementation fwa_delta_forward takes for these sizes
- * (under the current FWA_FORWARD_PATH) and the workspace it would allocate, without
- * launching or allocating anything.
- *   path             out (may be NULL): an fwa_forward_path value
- *   workspace_bytes  out (may be NULL): bytes of the stream-ordered workspace (chunked and
- *                    stream paths), 0 for fused
- *   Size errors are those fwa_delta_forward gives for the same sizes.
+ * fwa_delta_forward_path -- fwa_delta_forward with the implementation named by `request`
+ * (an fwa_forward_path: FWA_PATH_AUTO is exactly fwa_delta_forward).  For callers that must
+ * pin the implementation, such as tests that check each one against the others.  A named
+ * implementation that does not take the sizes gives FWA_ERR_UNSUPPORTED; an unknown request
+ * FWA_ERR_INVALID_ARG.  Same sources, arguments, workspace rule and errors otherwise.
+ */
+fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, const void* v,
+                                  const void* beta_logit, const float* W0, void* y,
+                                  float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
+                                  int chunk, fwa_dtype dtype, void* workspace,
+                                  int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fwa_delta_forward_info -- which implementation a forward call with `request` (an
+ * fwa_forward_path; FWA_PATH_AUTO for fwa_delta_forward) takes for these sizes and the
+ * workspace bytes it needs, without touching the device.
+ *   path             out (may be NULL): FWA_PATH_CHUNKED, _STREAM, _FUSED or _NONE
+ *   workspace_bytes  out (may be NULL): bytes of workspace the call needs (chunked and stream
+ *                    paths), 0 for fused
+ *   Size errors are those the forward gives for the same sizes; outputs are untouched on error.
  */
 fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
-                                  fwa_dtype dtype, int* path, int64_t* workspace_bytes);
+                                  fwa_dtype dtype, int request, int* path,
+                                  int64_t* workspace_bytes);
 
 /*
  * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory

@@ -1,33 +1,53 @@
-"""Independent NumPy transcription of the oracle, used only to cross-check fwa_oracle.c.
+"""A second fp64 implementation of the oracle, in a different algebraic form, used only to
+cross-check fwa_oracle.c.
 
 TEST INFRASTRUCTURE ONLY (tests import it; nothing else does).
 
-Where the C oracle spells DPFP out with explicit modular indices, this twin follows the
-operations the Fast Weights Transformer guide (xdnf.cn/news/308600), section "DPFP / projection
-formula and hyper-parameters", describes: concatenate [k, -k], apply ReLU, build the rolled
-copies (roll by +i along the last axis, i = 1..nu), multiply by the repeated x, then divide by
-(sum + eps) as in section "DPFP / normalisation".  The recurrence is written as matrix-vector
-products and an outer product per step, as in section "FastWeightsAttention / module structure
-and source walkthrough".  fp64 throughout; meant for small shapes only.
+Sources: the Fast Weights Transformer guide (xdnf.cn/news/308600), sections "DPFP / projection
+formula and hyper-parameters", "DPFP / normalisation" and "FastWeightsAttention / update
+formula".  It is written from the definitions, in forms of its own:
+
+  * DPFP as one index gather.  Entry p = (i-1)*2*d_k + j of the raw feature is x[a_p] * x[b_p]
+    with a_p = j and b_p = (j - i) mod 2*d_k, where x[m] = relu(s_m * k[m mod d_k]) and
+    s_m = +1 for m < d_k, -1 otherwise (x is relu([k, -k]) written entry by entry).  The
+    feature is divided by (its sum + 1e-6).
+  * beta = (1 + tanh(l / 2)) / 2, the logistic function in its tanh form.
+  * The recurrence through the row-wise identity: every row r of W moves on its own, with
+    u_r = beta (v_r - W_r . f),  y_r = W_r . g + u_r (f . g),  W_r <- W_r + u_r f,
+    where f = phi(k_t), g = phi(q_t) and W_r is the row before the step.  Expanding
+    (W_r + u_r f) . g shows this is the read after the write that the update formula states;
+    it reads the old row once, as a decode step does.
+
+fp64 throughout; meant for small shapes only.
 """
 import numpy as np
 
 EPS = 1e-6
 
 
+def _gather_tables(d_k, nu):
+    two = 2 * d_k
+    p = np.arange(two * nu)
+    shift = p // two + 1                 # i = 1..nu
+    a = p % two                          # j
+    b = (a - shift) % two                # (j - i) mod 2 d_k
+    return a, b
+
+
 def dpfp(k, nu):
     k = np.asarray(k, dtype=np.float64)
-    x = np.maximum(np.concatenate([k, -k], axis=-1), 0.0)
-    rolled = np.concatenate([np.roll(x, i, axis=-1) for i in range(1, nu + 1)], axis=-1)
-    repeated = np.concatenate([x] * nu, axis=-1)
-    raw = repeated * rolled
-    return raw / (raw.sum(axis=-1, keepdims=True) + EPS)
+    d_k = k.shape[-1]
+    m = np.arange(2 * d_k)
+    sign = np.where(m < d_k, 1.0, -1.0)
+    x = np.maximum(k[..., m % d_k] * sign, 0.0)
+    a, b = _gather_tables(d_k, nu)
+    raw = x[..., a] * x[..., b]
+    total = raw.sum(axis=-1, keepdims=True)
+    return raw / (total + EPS)
 
 
 def sigmoid(l):
-    l = np.asarray(l, dtype=np.float64)
-    return np.where(l >= 0, 1.0 / (1.0 + np.exp(-np.abs(l))),
-                    np.exp(-np.abs(l)) / (1.0 + np.exp(-np.abs(l))))
+    return 0.5 * (1.0 + np.tanh(0.5 * np.asarray(l, dtype=np.float64)))
 
 
 def delta_forward(q, k, v, beta_logit, W0=None, nu=1):
@@ -35,13 +55,17 @@ def delta_forward(q, k, v, beta_logit, W0=None, nu=1):
     B, H, T, d_k = q.shape
     d_v = v.shape[-1]
     D = 2 * d_k * nu
-    phi_q, phi_k = dpfp(q, nu), dpfp(k, nu)
+    F, G = dpfp(k, nu), dpfp(q, nu)
     beta = sigmoid(beta_logit)
-    W = np.zeros((B, H, d_v, D)) if W0 is None else np.array(W0, dtype=np.float64)
+    W_all = np.zeros((B, H, d_v, D)) if W0 is None else np.array(W0, dtype=np.float64)
     y = np.zeros((B, H, T, d_v))
-    for t in range(T):
-        fk, fq = phi_k[:, :, t], phi_q[:, :, t]
-        v_bar = np.einsum("bhvd,bhd->bhv", W, fk)
-        W = W + np.einsum("bhv,bhd->bhvd", beta[:, :, t, None] * (v[:, :, t] - v_bar), fk)
-        y[:, :, t] = np.einsum("bhvd,bhd->bhv", W, fq)
-    return y, W
+    for b in range(B):
+        for h in range(H):
+            W = W_all[b, h]
+            for t in range(T):
+                f, g = F[b, h, t], G[b, h, t]
+                u = beta[b, h, t] * (v[b, h, t] - W.dot(f))
+                y[b, h, t] = W.dot(g) + u * f.dot(g)
+                W = W + u[:, None] * f[None, :]
+            W_all[b, h] = W
+    return y, W_all

@@ -357,7 +357,9 @@ def pin_permutation_equivariance(O):
 
 
 def pin_matches_numpy_twin(O):
-    """Two independent transcriptions (explicit C indices vs. the roll/concat NumPy form)."""
+    """Two implementations in different forms: the C oracle's literal retrieve / write / read
+    loop with explicit modular indices, and the NumPy twin's index-gather DPFP, tanh-form
+    sigmoid and row-wise read-before-write identity."""
     from oracle import twin
     rng = np.random.default_rng(30)
     for (B, H, T, d_k, d_v, nu) in [(1, 1, 64, 16, 16, 1), (1, 2, 40, 64, 64, 1),
@@ -368,6 +370,8 @@ def pin_matches_numpy_twin(O):
         np.testing.assert_allclose(y, y2, rtol=0, atol=1e-13)
         np.testing.assert_allclose(W, W2, rtol=0, atol=1e-13)
         np.testing.assert_allclose(O.dpfp(k, nu), twin.dpfp(k, nu), rtol=0, atol=1e-15)
+    for x in (-30.0, -1.5, 0.0, 0.7, 25.0):
+        assert abs(O.sigmoid(x) - twin.sigmoid(x)) <= 1e-15
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -42,3 +42,19 @@ def oracle_forward(inp, nu, bh_index=None):
         q, k, v, l = (a[sel][None] for a in (q, k, v, l))
         W0 = None if W0 is None else W0[sel][None]
     return oracle.delta_forward(q, k, v, l, W0, nu=nu)
+
+
+def oracle_forward_batched(inp, nu):
+    """Oracle forward on every (b, h) slice, one batch row (H slices) per oracle call so that
+    only one row's fp64 inputs exist at a time.  Returns (y, W_final) as fp64 arrays."""
+    q, k, v, l, W0 = (inp[n] for n in ("q", "k", "v", "beta_logit", "W0"))
+    B, H, T, _ = q.shape
+    d_v = v.shape[-1]
+    D = 2 * q.shape[-1] * nu
+    y = np.empty((B, H, T, d_v), dtype=np.float64)
+    Wf = np.empty((B, H, d_v, D), dtype=np.float64)
+    for b in range(B):
+        row = lambda t: None if t is None else to_f64(t[b:b + 1])
+        y[b:b + 1], Wf[b:b + 1] = oracle.delta_forward(row(q), row(k), row(v), row(l), row(W0),
+                                                        nu=nu)
+    return y, Wf

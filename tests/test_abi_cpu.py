@@ -21,8 +21,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_info", "fwa_delta_step",
-              "fwa_status_string", "fwa_last_error", "fwa_version"):
+    for n in ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_path", "fwa_delta_forward_info",
+              "fwa_delta_step", "fwa_status_string", "fwa_last_error", "fwa_version"):
         assert n in names
     assert set(names) == set(fwa.EXPORTED)
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = fwa.lib()
-    assert L.fwa_version() == 10100
+    assert L.fwa_version() == 10200
     assert L.fwa_status_string(0) == b"FWA_OK"
     assert L.fwa_status_string(1) == b"FWA_ERR_INVALID_ARG"
     assert L.fwa_status_string(2) == b"FWA_ERR_UNSUPPORTED"
@@ -72,13 +72,16 @@ def test_dpfp_zero_vectors_is_noop():
     assert fwa.lib().fwa_dpfp(None, None, 0, 16, 1, 0, None) == 0
 
 
-def _fwd(**kw):
+def _fwd(path=None, **kw):
     a = dict(q=FAKE, k=P(0x20000), v=P(0x30000), bl=P(0x40000), W0=None, y=P(0x50000),
-             Wf=None, B=1, H=1, T=8, d_k=16, d_v=16, nu=1, chunk=64, dtype=0)
+             Wf=None, B=1, H=1, T=8, d_k=16, d_v=16, nu=1, chunk=64, dtype=0,
+             ws=P(0x1000000), ws_bytes=1 << 20)
     a.update(kw)
-    return fwa.lib().fwa_delta_forward(a["q"], a["k"], a["v"], a["bl"], a["W0"], a["y"], a["Wf"],
-                                       a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["nu"],
-                                       a["chunk"], a["dtype"], None)
+    args = (a["q"], a["k"], a["v"], a["bl"], a["W0"], a["y"], a["Wf"], a["B"], a["H"], a["T"],
+            a["d_k"], a["d_v"], a["nu"], a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], None)
+    if path is None:
+        return fwa.lib().fwa_delta_forward(*args)
+    return fwa.lib().fwa_delta_forward_path(path, *args)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -96,9 +99,27 @@ def _fwd(**kw):
     (dict(d_v=48), 2, "d_v"),
     (dict(d_k=64, nu=5), 2, "512"),
     (dict(d_k=64, nu=3, chunk=128, dtype=1), 2, "on-chip"),
+    (dict(ws=None), 1, "workspace of"),                         # the chunked path needs one
+    (dict(ws_bytes=1000), 1, "workspace of"),                   # too small
+    (dict(ws_bytes=-1), 1, "workspace_bytes"),
+    (dict(ws=P(0x1000008)), 1, "aligned"),
+    (dict(ws=P(0x20000)), 1, "workspace overlaps an input"),
+    (dict(ws=P(0x4ff00)), 1, "workspace overlaps an output"),
 ])
 def test_forward_rejects(kw, status, msg):
     assert _fwd(**kw) == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+@pytest.mark.parametrize("path,kw,status,msg", [
+    (7, {}, 1, "unknown forward path"),
+    (-1, {}, 1, "unknown forward path"),
+    (fwa.FWA_PATH_NONE, {}, 1, "unknown forward path"),
+    (fwa.FWA_PATH_CHUNKED, dict(chunk=16), 2, "chunked path does not support"),
+    (fwa.FWA_PATH_STREAM, {}, 2, "takes bf16"),
+])
+def test_forward_path_rejects(path, kw, status, msg):
+    assert _fwd(path=path, **kw) == status
     assert msg in fwa.lib().fwa_last_error().decode()
 
 
@@ -168,9 +189,8 @@ def _stream_workspace_formula(B, H, T, chunk):
     ((2, 2, 300, 64, 64, 6, 64), "f32", "fused"),         # fp32 D 768 > 512: unsupported
     ((0, 8, 1024, 64, 64, 1, 64), "f32", "empty"),
 ])
-def test_forward_info_auto_choice(shape, dtype, path, monkeypatch):
+def test_forward_info_auto_choice(shape, dtype, path):
     import torch
-    monkeypatch.delenv("FWA_FORWARD_PATH", raising=False)
     B, H, T, d_k, d_v, nu, chunk = shape
     td = torch.float32 if dtype == "f32" else torch.bfloat16
     if path == "none" or 2 * d_k * nu > 512:
@@ -200,15 +220,15 @@ def test_forward_info_auto_choice(shape, dtype, path, monkeypatch):
     ((1, 2, 100, 64, 32, 1, 32), "bf16", False),    # bf16 chunk 32: staged chain + outputs
     ((1, 2, 100, 64, 32, 3, 64), "bf16", False),    # bf16 D 384
 ])
-def test_forward_info_chunked_workspace(shape, dtype, chain_outputs, monkeypatch):
+def test_forward_info_chunked_workspace(shape, dtype, chain_outputs):
     """The chunked workspace leaves out the chunk-start memories and U exactly where the chain
     forms the outputs itself."""
     import torch
-    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
     B, H, T, d_k, d_v, nu, chunk = shape
     es = 2 if dtype == "bf16" else 4
     path, ws = fwa.delta_forward_info(B, H, T, d_k, d_v, nu, chunk,
-                                      torch.bfloat16 if dtype == "bf16" else torch.float32)
+                                      torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                      path="chunked")
     D, nc = 2 * d_k * nu, -(-T // chunk)
     extra = B * H * nc * (D * d_v + chunk * d_v) * es
     assert path == "chunked"
@@ -217,32 +237,33 @@ def test_forward_info_chunked_workspace(shape, dtype, chain_outputs, monkeypatch
     assert ws == base + (0 if chain_outputs else extra)
 
 
-def test_forward_info_env_override(monkeypatch):
+def test_forward_info_path_request():
     import torch
     big = (8, 16, 16384, 64, 64, 3, 64, torch.bfloat16)
-    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
-    path, ws = fwa.delta_forward_info(*big)
+    path, ws = fwa.delta_forward_info(*big, path="chunked")
     assert path == "chunked" and ws == _workspace_formula(*big[:7], 2)
-    monkeypatch.setenv("FWA_FORWARD_PATH", "fused")
-    assert fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64) == ("fused", 0)
-    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
+    assert fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64, path="fused") == ("fused", 0)
     with pytest.raises(fwa.FwaError) as e:                # chunk 16 has no chunked plan
-        fwa.delta_forward_info(1, 1, 64, 16, 16, 1, 16)
+        fwa.delta_forward_info(1, 1, 64, 16, 16, 1, 16, path="chunked")
     assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
-    monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
-    assert fwa.delta_forward_info(4, 8, 4096, 64, 64, 2, 64, torch.bfloat16) == (
+    assert fwa.delta_forward_info(4, 8, 4096, 64, 64, 2, 64, torch.bfloat16, path="stream") == (
         "stream", _stream_workspace_formula(4, 8, 4096, 64))
     for args in ((1, 8, 1024, 64, 64, 1, 64),                       # fp32
                  (1, 8, 1024, 64, 64, 1, 32, torch.bfloat16),       # chunk 32
                  (1, 8, 1024, 32, 16, 2, 64, torch.bfloat16),       # d_k 32 with d_v 16
                  (1, 8, 1024, 32, 64, 3, 64, torch.bfloat16)):      # D 192
         with pytest.raises(fwa.FwaError) as e:
-            fwa.delta_forward_info(*args)
+            fwa.delta_forward_info(*args, path="stream")
         assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
-    monkeypatch.setenv("FWA_FORWARD_PATH", "fast")
-    with pytest.raises(fwa.FwaError) as e:
-        fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64)
-    assert e.value.status == fwa.FWA_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        fwa.delta_forward_info(1, 8, 1024, 64, 64, 1, 64, path="fast")
+    L = fwa.lib()
+    got, ws = ctypes.c_int(7), ctypes.c_int64(7)
+    assert L.fwa_delta_forward_info(1, 8, 1024, 64, 64, 1, 64, 0, 9, ctypes.byref(got),
+                                    ctypes.byref(ws)) == fwa.FWA_ERR_INVALID_ARG
+    assert (got.value, ws.value) == (7, 7)
+    assert L.fwa_delta_forward_info(0, 8, 1024, 64, 64, 1, 64, 0, 9, ctypes.byref(got),
+                                    ctypes.byref(ws)) == fwa.FWA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("args", [
@@ -254,5 +275,69 @@ def test_forward_info_env_override(monkeypatch):
 def test_forward_info_invalid(args):
     L = fwa.lib()
     path, ws = ctypes.c_int(7), ctypes.c_int64(7)
-    assert L.fwa_delta_forward_info(*args, ctypes.byref(path), ctypes.byref(ws)) == fwa.FWA_ERR_INVALID_ARG
+    assert L.fwa_delta_forward_info(*args, 0, ctypes.byref(path), ctypes.byref(ws)) == fwa.FWA_ERR_INVALID_ARG
     assert (path.value, ws.value) == (7, 7)      # outputs untouched on error
+
+
+# ------------------------------------------------------------------ binding shape checks
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.float32)
+
+
+@pytest.mark.parametrize("bad", ["k", "v", "beta_logit", "W0", "out", "W_final", "q3"])
+def test_binding_forward_rejects_wrong_shapes(bad):
+    """Every wrong shape raises ValueError in the binding before any device work (CPU tensors:
+    a correct shape would fail later, on the device check)."""
+    B, H, T, dk, dv, nu = 2, 3, 5, 16, 8, 2
+    a = dict(q=_t(B, H, T, dk), k=_t(B, H, T, dk), v=_t(B, H, T, dv), beta_logit=_t(B, H, T),
+             W0=_t(B, H, dv, 2 * dk * nu), out=_t(B, H, T, dv), W_final=_t(B, H, dv, 2 * dk * nu))
+    wrong = {"k": _t(B, H, T, dk + 1), "v": _t(B, H, T + 1, dv), "beta_logit": _t(B, H, T, 1),
+             "W0": _t(B, H, dv, 2 * dk), "out": _t(B, H, T - 1, dv),
+             "W_final": _t(B, H, dv + 1, 2 * dk * nu), "q3": _t(H, T, dk)}
+    if bad == "q3":
+        a["q"] = wrong[bad]
+    else:
+        a[bad] = wrong[bad]
+    with pytest.raises(ValueError, match="shape|must be"):
+        fwa.delta_forward(a["q"], a["k"], a["v"], a["beta_logit"], a["W0"], nu=nu,
+                          out=a["out"], W_final=a["W_final"])
+    # the same tensors with correct shapes get past the shape checks to the device check
+    if bad != "q3":
+        a[bad] = {"k": _t(B, H, T, dk), "v": _t(B, H, T, dv), "beta_logit": _t(B, H, T),
+                  "W0": _t(B, H, dv, 2 * dk * nu), "out": _t(B, H, T, dv),
+                  "W_final": _t(B, H, dv, 2 * dk * nu)}[bad]
+        with pytest.raises(ValueError, match="must be on"):
+            fwa.delta_forward(a["q"], a["k"], a["v"], a["beta_logit"], a["W0"], nu=nu,
+                              out=a["out"], W_final=a["W_final"])
+
+
+@pytest.mark.parametrize("bad", ["k", "v", "beta_logit", "W", "out", "q2"])
+def test_binding_step_rejects_wrong_shapes(bad):
+    B, H, dk, dv, nu = 4, 2, 16, 8, 1
+    a = dict(q=_t(B, H, dk), k=_t(B, H, dk), v=_t(B, H, dv), beta_logit=_t(B, H),
+             W=_t(B, H, dv, 2 * dk * nu), out=_t(B, H, dv))
+    wrong = {"k": _t(B, H, dk // 2), "v": _t(B, H + 1, dv), "beta_logit": _t(B * H),
+             "W": _t(B, H, dv, 2 * dk * nu + 4), "out": _t(B, H, dv, 1), "q2": _t(B, dk)}
+    if bad == "q2":
+        a["q"] = wrong[bad]
+    else:
+        a[bad] = wrong[bad]
+    with pytest.raises(ValueError, match="shape|must be"):
+        fwa.delta_step(a["q"], a["k"], a["v"], a["beta_logit"], a["W"], nu=nu, out=a["out"])
+
+
+def test_binding_dpfp_rejects_wrong_out_shape():
+    x = _t(10, 16)
+    with pytest.raises(ValueError, match="shape"):
+        fwa.dpfp(x, 2, out=_t(10, 32))
+    with pytest.raises(ValueError, match="must be on"):
+        fwa.dpfp(x, 2, out=_t(10, 64))
+
+
+def test_binding_rejects_unknown_path():
+    B, H, T, dk = 1, 1, 4, 16
+    with pytest.raises(ValueError, match="path"):
+        fwa.delta_forward(_t(B, H, T, dk), _t(B, H, T, dk), _t(B, H, T, dk), _t(B, H, T),
+                          path="fastest")

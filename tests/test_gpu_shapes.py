@@ -1,6 +1,7 @@
 """Parity of the forward over every chain-kernel configuration the chunked path's planner can
 pick (each D it accepts, both dtypes, chunks of 32 and 64), over every memory split and roll
-length of the streaming path, and over seeded random shapes (chunks 32, 64, 128) on all implementations.  Same bars as test_gpu_parity: fp32 1e-4, bf16 2e-2 normwise per
+length of the streaming path, and over seeded random shapes (chunks 32, 64, 128) on all
+implementations.  Same bars as test_gpu_parity: fp32 1e-4, bf16 2e-2 normwise per
 (b, h) slice against the fp64 oracle."""
 import random
 
@@ -15,14 +16,14 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def _run(w, path, monkeypatch):
-    monkeypatch.setenv("FWA_FORWARD_PATH", path)
-    got, _ = fwa.delta_forward_info(w.B, w.H, w.T, w.d_k, w.d_v, w.nu, w.chunk, w.torch_dtype)
+def _run(w, path):
+    got, _ = fwa.delta_forward_info(w.B, w.H, w.T, w.d_k, w.d_v, w.nu, w.chunk, w.torch_dtype,
+                                    path=path)
     assert got == path
     inp = make_inputs(w)
     d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
     y, Wf = fwa.delta_forward(d["q"], d["k"], d["v"], d["beta_logit"], d["W0"], chunk=w.chunk,
-                              nu=w.nu)
+                              nu=w.nu, path=path)
     torch.cuda.synchronize()
     yr, Wr = oracle_forward(inp, w.nu)
     ey, ew = normwise(to_f64(y), yr, 2), normwise(to_f64(Wf), Wr, 2)
@@ -46,28 +47,26 @@ for dt, Ds in (("f32", (32, 64, 96, 128, 192, 256)), ("bf16", (32, 64, 96, 128, 
 
 
 @pytest.mark.parametrize("dt,D,C", CASES, ids=[f"{a}-D{b}-C{c}" for a, b, c in CASES])
-def test_chunked_every_chain_config(dt, D, C, monkeypatch):
+def test_chunked_every_chain_config(dt, D, C):
     d_k, nu = D_SHAPES[D]
     w = workload("h8_t1024_d64_nu1_f32", B=1, H=2, T=3 * C + 11, d_k=d_k, nu=nu,
                  d_v=32 if D >= 384 else 64, dtype=dt, chunk=C, w0_std=0.05,
                  seed=7000 + D + C)
-    monkeypatch.setenv("FWA_FORWARD_PATH", "chunked")
     try:
-        fwa.delta_forward_info(w.B, w.H, w.T, d_k, w.d_v, nu, C, w.torch_dtype)
+        fwa.delta_forward_info(w.B, w.H, w.T, d_k, w.d_v, nu, C, w.torch_dtype, path="chunked")
     except fwa.FwaError as e:
         assert e.status == fwa.FWA_ERR_UNSUPPORTED
         pytest.skip(f"the chunked path does not take this shape: {e}")
-    _run(w, "chunked", monkeypatch)
+    _run(w, "chunked")
 
 
-# Streaming path at chunk 64 (bf16), with each serial kernel.  The full-tile kernel takes d_v
-# in {32, 64} and D in {128, 256, 384}: each D gives a different number of memory d-tiles per
-# wave (1-3), each d_k a different roll window, nu up to 8 the longest roll the extended q rows
-# hold.  The shift-sliced kernel (16-column workgroups) takes d_k = 64 with nu <= 4, so D up to
-# 512, and any d_v here; it is the fallback for d_k = 64 shapes the full-tile kernel does not
-# take, and FWA_STREAM_KERNEL=sliced forces it; FWA_STREAM_KERNEL=pc forces the producer /
-# consumer kernel (d_k = 64, nu <= 4, d_v in {32, 64}).  T covers a lone
-# partial chunk, an exact chunk and ragged tails.  Shapes neither kernel takes are refused.
+# Streaming path at chunk 64 (bf16).  The planner takes the full-tile serial kernel for d_v in
+# {32, 64} and D in {128, 256, 384} (each D a different number of memory d-tiles per wave, 1-3;
+# each d_k a different roll window; nu up to 8 the longest roll the extended q rows hold), with
+# the shift-sliced prep for d_k = 64 and the full-tile compact prep for d_k 16 and 32.  It falls
+# back to the shift-sliced serial kernel (16-column workgroups, d_k = 64, nu <= 4) for d_v 16 and
+# D 512.  T covers a lone partial chunk, an exact chunk and ragged tails.  Shapes neither kernel
+# takes are refused.
 STREAM_CASES = [
     # (d_k, nu, d_v, B, H, T)
     (64, 1, 64, 1, 2, 203), (64, 2, 64, 2, 2, 64), (64, 3, 32, 1, 3, 17), (64, 4, 64, 1, 2, 140),
@@ -77,26 +76,20 @@ STREAM_CASES = [
 ]
 
 
-@pytest.mark.parametrize("kernel", ["default", "sliced", "pc"])
 @pytest.mark.parametrize("case", STREAM_CASES,
                          ids=[f"dk{c[0]}-nu{c[1]}-dv{c[2]}-T{c[5]}" for c in STREAM_CASES])
-def test_stream_every_split(case, kernel, monkeypatch):
+def test_stream_every_split(case):
     d_k, nu, d_v, B, H, T = case
     w = workload("b4_h8_t4096_d64_nu2_bf16_carried", B=B, H=H, T=T, d_k=d_k, nu=nu, d_v=d_v,
                  chunk=64, w0_std=0.05, seed=9000 + d_k * 10 + nu)
-    monkeypatch.setenv("FWA_FORWARD_PATH", "stream")
-    monkeypatch.setenv("FWA_STREAM_KERNEL", kernel)
     sliced_ok = d_k == 64 and nu <= 4
     full_ok = nu <= 8 and 2 * d_k * nu <= 384 and d_v % 32 == 0
-    # the default takes the full-tile kernel and falls back to the sliced one; "sliced" forces
-    # it; "pc" forces the producer / consumer kernel (32-column workgroups)
-    ok = {"sliced": sliced_ok, "pc": sliced_ok and d_v % 32 == 0}.get(kernel, full_ok or sliced_ok)
-    if not ok:
+    if not (full_ok or sliced_ok):
         with pytest.raises(fwa.FwaError) as e:
-            fwa.delta_forward_info(B, H, T, d_k, d_v, nu, 64, w.torch_dtype)
+            fwa.delta_forward_info(B, H, T, d_k, d_v, nu, 64, w.torch_dtype, path="stream")
         assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
         return
-    _run(w, "stream", monkeypatch)
+    _run(w, "stream")
 
 
 def _random_cases(n, seed):
@@ -121,20 +114,19 @@ RANDOM = _random_cases(24, 20261202)
 
 
 @pytest.mark.parametrize("case", RANDOM, ids=[f"r{c[0]}" for c in RANDOM])
-def test_random_shapes_every_path(case, monkeypatch):
+def test_random_shapes_every_path(case):
     i, B, H, T, d_k, d_v, nu, dt, C, w0 = case
     w = workload("h8_t1024_d64_nu1_f32", B=B, H=H, T=T, d_k=d_k, d_v=d_v, nu=nu, dtype=dt,
                  chunk=C, w0_std=w0, seed=8000 + i)
     ran = 0
     for path in ("chunked", "stream", "fused"):
-        monkeypatch.setenv("FWA_FORWARD_PATH", path)
         try:
-            fwa.delta_forward_info(B, H, T, d_k, d_v, nu, C, w.torch_dtype)
+            fwa.delta_forward_info(B, H, T, d_k, d_v, nu, C, w.torch_dtype, path=path)
         except fwa.FwaError as e:
             assert e.status == fwa.FWA_ERR_UNSUPPORTED
             log(f"  [{path}] unsupported: {e}")
             continue
-        _run(w, path, monkeypatch)
+        _run(w, path)
         ran += 1
     if ran == 0:
         pytest.skip("neither implementation takes this shape")

@@ -1453,13 +1453,12 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
     if (NU > 0) {
         // two workgroups per chunk (K side, Q side) where twice the chunks fit at once (chunk
         // 64, D a multiple of 128 so that quarters of D are whole k-steps, and room for the
-        // quarter partials over the staging rows); FWA_PREP_SPLIT=0 turns it off
+        // quarter partials over the staging rows)
         hipError_t e;
         bool launched = false;
         if constexpr (C == 64) {
             auto preps = delta_prep_split_kernel<BF16, C>;
-            const char* env = std::getenv("FWA_PREP_SPLIT");
-            const bool allowed = !(env && env[0] == '0') && a.D % 128 == 0 &&
+            const bool allowed = a.D % 128 == 0 &&
                                  a.l_xv - a.l_x >= 6 * (C / 16 + 1) * 1024;
             if (allowed) {
                 if ((e = ensure_lds_attr(reinterpret_cast<const void*>(preps), p.lds_prep)) != hipSuccess) return e;

@@ -7,11 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
-#include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -69,48 +65,11 @@ fwa_status hip_status(hipError_t e, const char* what) {
     return fail(FWA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Forward implementation: FWA_FORWARD_PATH = "chunked" (two or three launches with a D-wide
-// workspace), "stream" (bf16: compact prep plus one serial kernel, a 24.5 KB-per-chunk
-// workspace), "fused" (one launch, no workspace), or unset / "auto".  Auto takes the chunked
-// path where it applies and its workspace stays within kAutoWorkspaceLimit: beyond that the
-// workspace traffic (about 7 D-wide rows per token) outweighs the parallelism it buys.  Larger
-// bf16 problems take the streaming path where it applies, else the fused kernel.
-enum class ForwardPath { kAuto, kChunked, kStream, kFused, kInvalid };
+// The planner takes the chunked implementation where it applies and its workspace stays within
+// kAutoWorkspaceLimit: beyond that the workspace traffic (about 7 D-wide rows per token)
+// outweighs the parallelism it buys.  Larger bf16 problems take the streaming implementation
+// where it applies, else the fused kernel.
 constexpr int64_t kAutoWorkspaceLimit = int64_t(2) << 30;
-ForwardPath forward_path() {
-    const char* s = std::getenv("FWA_FORWARD_PATH");
-    if (!s || !*s || std::strcmp(s, "auto") == 0) return ForwardPath::kAuto;
-    if (std::strcmp(s, "chunked") == 0) return ForwardPath::kChunked;
-    if (std::strcmp(s, "stream") == 0) return ForwardPath::kStream;
-    if (std::strcmp(s, "fused") == 0) return ForwardPath::kFused;
-    return ForwardPath::kInvalid;
-}
-
-// Workspace of the chunked forward: one buffer per (device, stream), reused by every call on
-// that stream (calls on one stream run in order, so reuse needs no synchronisation) and grown
-// when a call needs more: the stream is synchronised, the old buffer freed and a larger one
-// allocated.  Buffers are held until the process ends.
-hipError_t workspace_get(char** ptr, int64_t bytes, hipStream_t stream) {
-    static std::mutex mu;
-    static std::map<std::pair<int, uintptr_t>, std::pair<char*, int64_t>> cache;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(mu);
-    auto& ent = cache[{dev, reinterpret_cast<uintptr_t>(stream)}];
-    if (ent.second < bytes) {
-        if (ent.first) {
-            if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
-            if ((e = hipFree(ent.first)) != hipSuccess) return e;
-            ent = {nullptr, 0};
-        }
-        void* p = nullptr;
-        if ((e = hipMalloc(&p, static_cast<size_t>(bytes))) != hipSuccess) return e;
-        ent = {static_cast<char*>(p), bytes};
-    }
-    *ptr = ent.first;
-    return hipSuccess;
-}
 }  // namespace
 
 extern "C" {
@@ -127,7 +86,7 @@ const char* fwa_status_string(fwa_status s) {
 
 const char* fwa_last_error(void) { return g_last_error.c_str(); }
 
-int fwa_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int fwa_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, fwa_dtype dtype,
                     hipStream_t stream) {
@@ -184,7 +143,7 @@ fwa_status check_forward_shape(const char* fn, int64_t BH, int T, int d_k, int d
     return ok();
 }
 
-// The implementation a forward call takes (FWA_FORWARD_PATH and the shape), with its plan.
+// The implementation a forward call takes (the request and the shape), with its plan.
 struct ForwardChoice {
     int path;                       // FWA_PATH_CHUNKED, FWA_PATH_STREAM or FWA_PATH_FUSED
     fwa::ChunkPlan cplan;
@@ -193,18 +152,17 @@ struct ForwardChoice {
     int64_t ws_bytes;
 };
 
-fwa_status choose_forward(const char* fn, int BH, int T, int d_k, int d_v, int nu, int chunk,
-                          bool bf16, ForwardChoice* c) {
-    const ForwardPath want = forward_path();
-    if (want == ForwardPath::kInvalid)
-        return fail(FWA_ERR_INVALID_ARG,
-                    "%s: FWA_FORWARD_PATH must be auto, chunked, stream or fused", fn);
-    const bool auto_ = want == ForwardPath::kAuto;
-    const bool can_chunk = (auto_ || want == ForwardPath::kChunked) &&
+fwa_status choose_forward(const char* fn, int request, int BH, int T, int d_k, int d_v, int nu,
+                          int chunk, bool bf16, ForwardChoice* c) {
+    if (request != FWA_PATH_AUTO && request != FWA_PATH_CHUNKED && request != FWA_PATH_STREAM &&
+        request != FWA_PATH_FUSED)
+        return fail(FWA_ERR_INVALID_ARG, "%s: unknown forward path %d", fn, request);
+    const bool auto_ = request == FWA_PATH_AUTO;
+    const bool can_chunk = (auto_ || request == FWA_PATH_CHUNKED) &&
                            fwa::plan_chunked(BH, T, d_k, d_v, nu, chunk, bf16, &c->cplan);
-    const bool can_stream = (auto_ || want == ForwardPath::kStream) &&
+    const bool can_stream = (auto_ || request == FWA_PATH_STREAM) &&
                             fwa::plan_stream(BH, T, d_k, d_v, nu, chunk, bf16, &c->splan);
-    const bool can_fuse = (auto_ || want == ForwardPath::kFused) &&
+    const bool can_fuse = (auto_ || request == FWA_PATH_FUSED) &&
                           fwa::plan_forward(BH, d_k, d_v, nu, chunk, bf16, &c->fplan);
     c->ws_bytes = 0;
     if (can_chunk && (!auto_ || c->cplan.ws_bytes <= kAutoWorkspaceLimit || (!can_stream && !can_fuse))) {
@@ -221,54 +179,33 @@ fwa_status choose_forward(const char* fn, int BH, int T, int d_k, int d_v, int n
         c->path = FWA_PATH_FUSED;
         return ok();
     }
-    if (want == ForwardPath::kChunked || want == ForwardPath::kStream)
+    if (request == FWA_PATH_CHUNKED || request == FWA_PATH_STREAM)
         return fail(FWA_ERR_UNSUPPORTED,
                     "%s: the %s path does not support d_k=%d d_v=%d nu=%d chunk=%d%s", fn,
-                    want == ForwardPath::kChunked ? "chunked" : "stream", d_k, d_v, nu, chunk,
-                    want == ForwardPath::kStream && !bf16 ? " (it takes bf16 inputs)" : "");
+                    request == FWA_PATH_CHUNKED ? "chunked" : "stream", d_k, d_v, nu, chunk,
+                    request == FWA_PATH_STREAM && !bf16 ? " (it takes bf16 inputs)" : "");
     return fail(FWA_ERR_UNSUPPORTED,
                 "%s: d_k=%d d_v=%d nu=%d chunk=%d does not fit the on-chip working set", fn, d_k,
                 d_v, nu, chunk);
 }
 
-}  // namespace
-
-extern "C" {
-
-fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
-                                  fwa_dtype dtype, int* path, int64_t* workspace_bytes) {
-    const char* fn = "fwa_delta_forward_info";
+// Checks every argument of a forward call (sizes, pointers, overlaps, the workspace) and picks
+// the implementation; nothing is launched.
+fwa_status check_forward_call(const char* fn, int request, const void* q, const void* k,
+                              const void* v, const void* beta_logit, const float* W0,
+                              const void* y, const float* W_final, int B, int H, int T, int d_k,
+                              int d_v, int nu, int chunk, fwa_dtype dtype, const void* workspace,
+                              int64_t workspace_bytes, ForwardChoice* c) {
     fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
     if (st != FWA_OK) return st;
     const int64_t BH = static_cast<int64_t>(B) * H;
-    int p = FWA_PATH_NONE;
-    int64_t ws = 0;
-    if (BH > 0) {
-        if ((st = check_forward_shape(fn, BH, T, d_k, d_v, nu)) != FWA_OK) return st;
-        ForwardChoice c;
-        if ((st = choose_forward(fn, static_cast<int>(BH), T, d_k, d_v, nu, chunk,
-                                 dtype == FWA_BF16, &c)) != FWA_OK)
-            return st;
-        p = c.path;
-        ws = c.ws_bytes;
-    }
-    if (path) *path = p;
-    if (workspace_bytes) *workspace_bytes = ws;
-    return ok();
-}
-
-fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const void* beta_logit,
-                             const float* W0, void* y, float* W_final, int B, int H, int T,
-                             int d_k, int d_v, int nu, int chunk, fwa_dtype dtype,
-                             hipStream_t stream) {
-    const char* fn = "fwa_delta_forward";
-    fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
-    if (st != FWA_OK) return st;
-    const int64_t BH = static_cast<int64_t>(B) * H;
+    c->path = FWA_PATH_NONE;
+    c->ws_bytes = 0;
     if (BH == 0) return ok();
     if (T > 0 && (!q || !k || !v || !beta_logit || !y))
         return fail(FWA_ERR_INVALID_ARG, "%s: NULL input or output pointer", fn);
-    const void* ptrs[] = {q, k, v, beta_logit, W0, y, W_final};
+    if (workspace_bytes < 0) return fail(FWA_ERR_INVALID_ARG, "%s: workspace_bytes < 0", fn);
+    const void* ptrs[] = {q, k, v, beta_logit, W0, y, W_final, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p))
             return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
@@ -288,30 +225,100 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
         return fail(FWA_ERR_INVALID_ARG, "%s: W0 and W_final partially overlap", fn);
     if (overlap(sy, sw)) return fail(FWA_ERR_INVALID_ARG, "%s: y overlaps W_final", fn);
 
-    const bool bf16 = dtype == FWA_BF16;
-    ForwardChoice c;
-    if ((st = choose_forward(fn, static_cast<int>(BH), T, d_k, d_v, nu, chunk, bf16, &c)) != FWA_OK)
+    if ((st = choose_forward(fn, request, static_cast<int>(BH), T, d_k, d_v, nu, chunk,
+                             dtype == FWA_BF16, c)) != FWA_OK)
         return st;
-    if (c.path != FWA_PATH_FUSED) {
-        char* ws = nullptr;
-        if (c.ws_bytes > 0) {
-            const hipError_t e = workspace_get(&ws, c.ws_bytes, stream);
-            if (e != hipSuccess)
-                return fail(FWA_ERR_HIP, "%s: workspace of %lld bytes: %s", fn,
-                            (long long)c.ws_bytes, hipGetErrorString(e));
-        }
-        if (c.path == FWA_PATH_STREAM)
+    if (c->ws_bytes > 0) {
+        if (!workspace || workspace_bytes < c->ws_bytes)
+            return fail(FWA_ERR_INVALID_ARG,
+                        "%s: the %s path needs a workspace of %lld bytes (got %lld%s)", fn,
+                        c->path == FWA_PATH_CHUNKED ? "chunked" : "stream",
+                        (long long)c->ws_bytes, (long long)workspace_bytes,
+                        workspace ? "" : ", NULL");
+        const Span sws = span(workspace, c->ws_bytes);
+        for (const Span& s : in)
+            if (overlap(s, sws)) return fail(FWA_ERR_INVALID_ARG, "%s: workspace overlaps an input", fn);
+        if (overlap(sws, sy) || overlap(sws, sw))
+            return fail(FWA_ERR_INVALID_ARG, "%s: workspace overlaps an output", fn);
+    }
+    return ok();
+}
+
+// Enqueues the chosen implementation (arguments already checked).
+fwa_status launch_forward(const ForwardChoice& c, const void* q, const void* k, const void* v,
+                          const void* beta_logit, const float* W0, void* y, float* W_final,
+                          int BH, int H, int T, int d_k, int d_v, int nu, int chunk, bool bf16,
+                          void* workspace, hipStream_t stream) {
+    char* ws = static_cast<char*>(workspace);
+    switch (c.path) {
+        case FWA_PATH_NONE:
+            return ok();
+        case FWA_PATH_STREAM:
             return hip_status(fwa::launch_stream(c.splan, q, k, v, beta_logit, W0, y, W_final, ws,
                                                  stream),
                               "fwa_delta_forward launch");
-        return hip_status(fwa::launch_chunked(c.cplan, q, k, v, beta_logit, W0, y, W_final, ws,
-                                              bf16, stream),
-                          "fwa_delta_forward launch");
+        case FWA_PATH_CHUNKED:
+            return hip_status(fwa::launch_chunked(c.cplan, q, k, v, beta_logit, W0, y, W_final,
+                                                  ws, bf16, stream),
+                              "fwa_delta_forward launch");
+        default:
+            return hip_status(fwa::launch_delta_forward(c.fplan, q, k, v, beta_logit, W0, y,
+                                                        W_final, BH, H, T, d_k, d_v, nu, chunk,
+                                                        bf16, stream),
+                              "fwa_delta_forward launch");
     }
-    return hip_status(fwa::launch_delta_forward(c.fplan, q, k, v, beta_logit, W0, y, W_final,
-                                                static_cast<int>(BH), H, T, d_k, d_v, nu, chunk,
-                                                bf16, stream),
-                      "fwa_delta_forward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
+                                  fwa_dtype dtype, int request, int* path,
+                                  int64_t* workspace_bytes) {
+    const char* fn = "fwa_delta_forward_info";
+    fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
+    if (st != FWA_OK) return st;
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    int p = FWA_PATH_NONE;
+    int64_t ws = 0;
+    if (BH > 0) {
+        if ((st = check_forward_shape(fn, BH, T, d_k, d_v, nu)) != FWA_OK) return st;
+        ForwardChoice c;
+        if ((st = choose_forward(fn, request, static_cast<int>(BH), T, d_k, d_v, nu, chunk,
+                                 dtype == FWA_BF16, &c)) != FWA_OK)
+            return st;
+        p = c.path;
+        ws = c.ws_bytes;
+    } else if (request != FWA_PATH_AUTO && request != FWA_PATH_CHUNKED &&
+               request != FWA_PATH_STREAM && request != FWA_PATH_FUSED) {
+        return fail(FWA_ERR_INVALID_ARG, "%s: unknown forward path %d", fn, request);
+    }
+    if (path) *path = p;
+    if (workspace_bytes) *workspace_bytes = ws;
+    return ok();
+}
+
+fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, const void* v,
+                                  const void* beta_logit, const float* W0, void* y,
+                                  float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
+                                  int chunk, fwa_dtype dtype, void* workspace,
+                                  int64_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "fwa_delta_forward";
+    ForwardChoice c;
+    fwa_status st = check_forward_call(fn, request, q, k, v, beta_logit, W0, y, W_final, B, H, T,
+                                       d_k, d_v, nu, chunk, dtype, workspace, workspace_bytes, &c);
+    if (st != FWA_OK) return st;
+    return launch_forward(c, q, k, v, beta_logit, W0, y, W_final, B * H, H, T, d_k, d_v, nu,
+                          chunk, dtype == FWA_BF16, workspace, stream);
+}
+
+fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const void* beta_logit,
+                             const float* W0, void* y, float* W_final, int B, int H, int T,
+                             int d_k, int d_v, int nu, int chunk, fwa_dtype dtype,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return fwa_delta_forward_path(FWA_PATH_AUTO, q, k, v, beta_logit, W0, y, W_final, B, H, T,
+                                  d_k, d_v, nu, chunk, dtype, workspace, workspace_bytes, stream);
 }
 
 fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,

@@ -102,7 +102,6 @@ struct StreamPlan {
     int ndw;             // d-tiles of W^T per wave (of 8)
     bool sliced_prep;    // prep with shift-sliced K and Q tiles (d_k = 64, nu <= 4)
     bool sliced_stream;  // serial kernel with shift-sliced K and Q tiles (chunk 64 or 128)
-    bool pc_stream;      // producer / consumer serial kernel (chunk 64, sliced)
     int64_t ws_bytes;
 };
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan);
@@ -112,8 +111,6 @@ int plan_prep_sliced(int C, ChunkArgs* a);
 bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
 hipError_t launch_prep_sliced(const StreamPlan& plan, hipStream_t stream);
 hipError_t launch_stream_sliced(const StreamPlan& plan, hipStream_t stream);
-bool plan_stream_pc(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
-hipError_t launch_stream_pc(const StreamPlan& plan, hipStream_t stream);
 hipError_t launch_stream(const StreamPlan& plan, const void* q, const void* k, const void* v,
                          const void* bl, const float* W0, void* y, float* Wf, char* ws,
                          hipStream_t stream);

@@ -2,8 +2,6 @@
 // launches (prep kernel in compact mode, then the stream kernel).
 #include "stream_kernel.h"
 
-#include <cstdlib>
-#include <cstring>
 
 namespace fwa {
 
@@ -13,26 +11,16 @@ constexpr int kMaxLdsStream = 160 * 1024;
 
 // Which kernels the streaming path runs.  Chunk 128 takes the shift-sliced kernels (d_k = 64,
 // nu <= 4).  Chunk 64 takes the 32-column full-tile serial kernel, with the sliced prep for
-// d_k = 64 and nu <= 4 (unless FWA_STREAM_PREP=full); shapes that kernel does not take (d_v 16,
-// D 512) fall back to the sliced serial kernel with 16-column workgroups, which
-// FWA_STREAM_KERNEL=sliced also forces.  On the 8 x 16 x 16384 (D 384) forward the full-tile
-// kernel takes 1.45 ms and the sliced one 2.5 ms: the sliced one builds the DPFP tiles three
-// times per chunk and column group (K and Q, then K again) and is bound by that VALU work.
-// FWA_STREAM_KERNEL=pc selects the producer / consumer serial kernel (chunk 64, d_k = 64,
-// nu <= 4, d_v in {32, 64}): 2.09 ms on that workload, its single producer wave per SIMD
-// latency-bound on the DPFP work of each step.
-static bool env_is(const char* name, const char* value) {
-    const char* s = std::getenv(name);
-    return s != nullptr && std::strcmp(s, value) == 0;
-}
-
+// d_k = 64 and nu <= 4 and the full-tile compact prep otherwise; shapes that serial kernel does
+// not take (d_v 16, D 512) fall back to the sliced serial kernel with 16-column workgroups.  On
+// the 8 x 16 x 16384 (D 384) forward the full-tile kernel takes 1.45 ms and the sliced one
+// 2.5 ms: the sliced one builds the DPFP tiles three times per chunk and column group (K and Q,
+// then K again) and is bound by that VALU work, so it is only the fallback.
 static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
 
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan) {
     if (!bf16) return false;
-    if (C == 64 && env_is("FWA_STREAM_KERNEL", "pc")) return plan_stream_pc(BH, T, d_k, d_v, nu, C, plan);
-    if (C == 128 || (C == 64 && env_is("FWA_STREAM_KERNEL", "sliced")))
-        return plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
+    if (C == 128) return plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
     if (!plan_stream_full(BH, T, d_k, d_v, nu, C, plan))
         return C == 64 && plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan);
     return true;
@@ -79,8 +67,7 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
     plan->lds_prep = cp.lds_prep;
     plan->sliced_prep = false;
     plan->sliced_stream = false;
-    plan->pc_stream = false;
-    if (d_k == 64 && nu <= 4 && !env_is("FWA_STREAM_PREP", "full")) {
+    if (d_k == 64 && nu <= 4) {
         const int lds = plan_prep_sliced(C, &a);
         if (lds > 0) {
             plan->lds_prep = lds;
@@ -138,7 +125,6 @@ hipError_t launch_stream(const StreamPlan& plan_in, const void* q, const void* k
     a.y = y;
     a.Wf = Wf;
     a.ws = ws;
-    if (p.pc_stream) return launch_stream_pc(p, stream);
     if (p.sliced_stream) return launch_stream_sliced(p, stream);
     if (p.C != 64) return hipErrorInvalidValue;
     return launch_stream_c64(p, stream);

@@ -1,6 +1,6 @@
 // Shift-sliced streaming forward (bf16, d_k = 64): host planning of the LDS and workspace
 // layouts, and the launches of the sliced prep kernel and the chunk-128 serial kernel.
-#include "stream_pc.h"
+#include "stream_sliced.h"
 
 namespace fwa {
 
@@ -81,61 +81,8 @@ bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPl
     plan->ndw = nu;
     plan->sliced_prep = true;
     plan->sliced_stream = true;
-    plan->pc_stream = false;
     plan->ws_bytes = a.o_rq + NU * szR;
     return true;
-}
-
-// Producer / consumer serial kernel (chunk 64, d_k = 64, nu <= 4, 32 columns per workgroup):
-// the sliced prep's layout and workspace, and the serial kernel's LDS: two raw slots (k, q rows
-// and v columns), two slice slots (K and Q), the W^T copy, Z, U and the y rows.
-bool plan_stream_pc(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan) {
-    if (C != 64) return false;
-    if (!plan_stream_sliced(BH, T, d_k, d_v, nu, C, plan)) return false;
-    if (d_v % 32 != 0) return false;
-    ChunkArgs& a = plan->args;
-    const int D = a.D, CW = 32;
-    int off = 0;
-    a.s_raw = off;
-    off += 2 * (2 * C * kSliceDk * 2 + C * CW * 2);
-    a.s_k = off;
-    off += 4 * C * a.ss * 2;
-    a.s_wt = off;
-    off += (D / 32) * 2 * 1024;
-    a.s_z = off;
-    off += C * CW * 4;
-    a.s_u = off;
-    off += C * CW * 4;
-    a.s_y = off;
-    off += C * CW * 2;
-    a.s_q = a.s_qoff = a.s_voff = 0;
-    if (off > kMaxLdsSliced) return false;
-    plan->lds_stream = off;
-    plan->sliced_stream = false;
-    plan->pc_stream = true;
-    return true;
-}
-
-template <int NU>
-static hipError_t launch_stream_pc_nu(const StreamPlan& p, hipStream_t stream) {
-    auto kern = delta_stream_pc_kernel<NU>;
-    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_stream);
-    if (e != hipSuccess) return e;
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / 32)));
-    hipLaunchKernelGGL(kern, grid, dim3(512), p.lds_stream, stream, p.args);
-    return hipGetLastError();
-}
-
-hipError_t launch_stream_pc(const StreamPlan& p, hipStream_t stream) {
-    hipError_t e = launch_prep_sliced(p, stream);
-    if (e != hipSuccess) return e;
-    switch (p.args.nu) {
-        case 1: return launch_stream_pc_nu<1>(p, stream);
-        case 2: return launch_stream_pc_nu<2>(p, stream);
-        case 3: return launch_stream_pc_nu<3>(p, stream);
-        case 4: return launch_stream_pc_nu<4>(p, stream);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 // Chunk 64 runs the prep as 4-wave workgroups: at 52 KB of LDS three share a CU, and the

@@ -6,12 +6,18 @@ been built (weight_linear_attention_amd/build.py, or __graft_entry__.build()); l
 loudly otherwise -- there is no fallback.
 
 Functions (same names as the C entry points, minus the prefix):
-    dpfp(x, nu)                                   -> phi
-    delta_forward(q, k, v, beta_logit, W0=None, chunk=64, out=None, W_final=None)
-                                                  -> (y, W_final)
-    delta_step(q, k, v, beta_logit, W, out=None)  -> y      (W is updated in place)
-    delta_forward_info(B, H, T, d_k, d_v, nu, chunk, dtype)
-                                                  -> ("chunked" | "fused" | "none", workspace bytes)
+    dpfp(x, nu, out=None)                         -> phi
+    delta_forward(q, k, v, beta_logit, W0=None, chunk=64, nu=1, out=None, W_final=None,
+                  path="auto", workspace=None)    -> (y, W_final)
+    delta_step(q, k, v, beta_logit, W, nu=1, out=None)
+                                                  -> y      (W is updated in place)
+    delta_forward_info(B, H, T, d_k, d_v, nu, chunk, dtype, path="auto")
+                                                  -> ("chunked" | "stream" | "fused" | "none",
+                                                      workspace bytes)
+
+Shapes are checked before anything else, so a wrong shape raises ValueError without touching
+the device.  The forward's workspace is allocated here with torch on the current stream (the
+caching allocator keeps it in stream order) unless the caller passes one.
 """
 import ctypes
 import os
@@ -23,10 +29,14 @@ LIB_PATH = os.path.join(_PKG, "libfwa.so")
 
 FWA_OK, FWA_ERR_INVALID_ARG, FWA_ERR_UNSUPPORTED, FWA_ERR_HIP = 0, 1, 2, 3
 FWA_F32, FWA_BF16 = 0, 1
-FWA_PATH_NONE, FWA_PATH_CHUNKED, FWA_PATH_FUSED, FWA_PATH_STREAM = 0, 1, 2, 3
+FWA_PATH_AUTO, FWA_PATH_CHUNKED, FWA_PATH_FUSED, FWA_PATH_STREAM, FWA_PATH_NONE = 0, 1, 2, 3, 4
+PATHS = {"auto": FWA_PATH_AUTO, "chunked": FWA_PATH_CHUNKED, "fused": FWA_PATH_FUSED,
+         "stream": FWA_PATH_STREAM}
+PATH_NAMES = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED: "fused",
+              FWA_PATH_STREAM: "stream"}
 
-EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_info", "fwa_delta_step",
-            "fwa_status_string", "fwa_last_error", "fwa_version")
+EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_path", "fwa_delta_forward_info",
+            "fwa_delta_step", "fwa_status_string", "fwa_last_error", "fwa_version")
 
 
 class FwaError(RuntimeError):
@@ -50,9 +60,12 @@ def lib():
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     L.fwa_dpfp.argtypes = [P, P, i64, i32, i32, i32, P]
     L.fwa_dpfp.restype = i32
-    L.fwa_delta_forward.argtypes = [P, P, P, P, P, P, P] + [i32] * 7 + [i32, P]
+    fwd = [P, P, P, P, P, P, P] + [i32] * 7 + [i32, P, i64, P]
+    L.fwa_delta_forward.argtypes = fwd
     L.fwa_delta_forward.restype = i32
-    L.fwa_delta_forward_info.argtypes = [i32] * 8 + [ctypes.POINTER(i32), ctypes.POINTER(i64)]
+    L.fwa_delta_forward_path.argtypes = [i32] + fwd
+    L.fwa_delta_forward_path.restype = i32
+    L.fwa_delta_forward_info.argtypes = [i32] * 9 + [ctypes.POINTER(i32), ctypes.POINTER(i64)]
     L.fwa_delta_forward_info.restype = i32
     L.fwa_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5 + [i32, P]
     L.fwa_delta_step.restype = i32
@@ -71,12 +84,18 @@ def _check(status):
                                            L.fwa_last_error().decode()))
 
 
-def _dtype_code(t):
-    if t.dtype == torch.float32:
+def _dtype_code(dtype):
+    if dtype == torch.float32:
         return FWA_F32
-    if t.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         return FWA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+    raise TypeError(f"unsupported dtype {dtype}; expected float32 or bfloat16")
+
+
+def _path_code(path):
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}, got {path!r}")
+    return PATHS[path]
 
 
 def _ptr(t):
@@ -85,6 +104,11 @@ def _ptr(t):
 
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def _need(t, name, device, dtype=None):
@@ -98,33 +122,58 @@ def _need(t, name, device, dtype=None):
 
 def dpfp(x, nu, out=None):
     """DPFP over the last axis: [..., d_k] -> [..., 2*d_k*nu], same dtype and device."""
+    d_k = x.shape[-1]
+    _shape(out, "out", (*x.shape[:-1], 2 * d_k * nu))
     dev = x.device
     _need(x, "x", dev)
-    d_k = x.shape[-1]
     n_vec = x.numel() // d_k if d_k else 0
     if out is None:
         out = torch.empty(*x.shape[:-1], 2 * d_k * nu, dtype=x.dtype, device=dev)
     _need(out, "out", dev, x.dtype)
-    _check(lib().fwa_dpfp(_ptr(x), _ptr(out), n_vec, d_k, nu, _dtype_code(x), _stream(dev)))
+    _check(lib().fwa_dpfp(_ptr(x), _ptr(out), n_vec, d_k, nu, _dtype_code(x.dtype), _stream(dev)))
     return out
 
 
-def delta_forward(q, k, v, beta_logit, W0=None, chunk=64, nu=1, out=None, W_final=None,
-                  return_final=True):
-    """Causal chunked forward. q,k [B,H,T,d_k]; v [B,H,T,d_v]; beta_logit [B,H,T];
-    W0 [B,H,d_v,D] fp32 or None.  Returns (y [B,H,T,d_v], W_final [B,H,d_v,D] fp32 or None)."""
-    dev = q.device
+def check_forward_shapes(q, k, v, beta_logit, W0=None, nu=1, out=None, W_final=None):
+    """Raises ValueError unless the forward's tensors have consistent shapes."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, T, d_k], got {tuple(q.shape)}")
     B, H, T, d_k = q.shape
+    if v.dim() != 4:
+        raise ValueError(f"v must be [B, H, T, d_v], got {tuple(v.shape)}")
     d_v = v.shape[-1]
     D = 2 * d_k * nu
+    _shape(k, "k", q.shape)
+    _shape(v, "v", (B, H, T, d_v))
+    _shape(beta_logit, "beta_logit", (B, H, T))
+    _shape(W0, "W0", (B, H, d_v, D))
+    _shape(out, "out", (B, H, T, d_v))
+    _shape(W_final, "W_final", (B, H, d_v, D))
+    return B, H, T, d_k, d_v, D
+
+
+def delta_forward_info(B, H, T, d_k, d_v, nu=1, chunk=64, dtype=torch.float32, path="auto"):
+    """Implementation ("chunked", "stream", "fused" or "none") a forward with these sizes takes
+    (path="auto": the planner's choice) and the bytes of workspace it needs."""
+    got, ws = ctypes.c_int(0), ctypes.c_int64(0)
+    _check(lib().fwa_delta_forward_info(B, H, T, d_k, d_v, nu, chunk, _dtype_code(dtype),
+                                        _path_code(path), ctypes.byref(got), ctypes.byref(ws)))
+    return PATH_NAMES[got.value], ws.value
+
+
+def delta_forward(q, k, v, beta_logit, W0=None, chunk=64, nu=1, out=None, W_final=None,
+                  return_final=True, path="auto", workspace=None):
+    """Causal chunked forward. q,k [B,H,T,d_k]; v [B,H,T,d_v]; beta_logit [B,H,T];
+    W0 [B,H,d_v,D] fp32 or None.  Returns (y [B,H,T,d_v], W_final [B,H,d_v,D] fp32 or None).
+    `path` pins the implementation ("auto" = the planner's choice); `workspace` is an optional
+    uint8 device tensor of at least delta_forward_info(...)[1] bytes."""
+    B, H, T, d_k, d_v, D = check_forward_shapes(q, k, v, beta_logit, W0, nu, out, W_final)
+    code = _path_code(path)
+    dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta_logit, "beta_logit")):
         _need(t, n, dev, q.dtype)
-    if k.shape != q.shape or v.shape[:3] != (B, H, T) or beta_logit.shape != (B, H, T):
-        raise ValueError("shape mismatch between q, k, v and beta_logit")
     if W0 is not None:
         _need(W0, "W0", dev, torch.float32)
-        if W0.shape != (B, H, d_v, D):
-            raise ValueError(f"W0 must be {(B, H, d_v, D)}")
     if out is None:
         out = torch.empty(B, H, T, d_v, dtype=q.dtype, device=dev)
     _need(out, "out", dev, q.dtype)
@@ -132,39 +181,45 @@ def delta_forward(q, k, v, beta_logit, W0=None, chunk=64, nu=1, out=None, W_fina
         W_final = torch.empty(B, H, d_v, D, dtype=torch.float32, device=dev)
     if W_final is not None:
         _need(W_final, "W_final", dev, torch.float32)
-    _check(lib().fwa_delta_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta_logit), _ptr(W0),
-                                   _ptr(out), _ptr(W_final), B, H, T, d_k, d_v, nu, chunk,
-                                   _dtype_code(q), _stream(dev)))
+    if workspace is None:
+        _, nbytes = delta_forward_info(B, H, T, d_k, d_v, nu, chunk, q.dtype, path)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    else:
+        _need(workspace, "workspace", dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().fwa_delta_forward_path(code, _ptr(q), _ptr(k), _ptr(v), _ptr(beta_logit),
+                                        _ptr(W0), _ptr(out), _ptr(W_final), B, H, T, d_k, d_v,
+                                        nu, chunk, _dtype_code(q.dtype), _ptr(workspace),
+                                        ws_bytes, _stream(dev)))
     return out, W_final
 
 
-def delta_forward_info(B, H, T, d_k, d_v, nu=1, chunk=64, dtype=torch.float32):
-    """Implementation ("chunked", "fused" or "none") that delta_forward takes for these sizes
-    under the current FWA_FORWARD_PATH, and the bytes of workspace it allocates."""
-    code = {torch.float32: FWA_F32, torch.bfloat16: FWA_BF16}.get(dtype)
-    if code is None:
-        raise TypeError(f"unsupported dtype {dtype}; expected float32 or bfloat16")
-    path, ws = ctypes.c_int(0), ctypes.c_int64(0)
-    _check(lib().fwa_delta_forward_info(B, H, T, d_k, d_v, nu, chunk, code, ctypes.byref(path),
-                                        ctypes.byref(ws)))
-    names = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED: "fused",
-             FWA_PATH_STREAM: "stream"}
-    return names[path.value], ws.value
+def check_step_shapes(q, k, v, beta_logit, W, nu=1, out=None):
+    """Raises ValueError unless the decode step's tensors have consistent shapes."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H, d_k], got {tuple(q.shape)}")
+    B, H, d_k = q.shape
+    if v.dim() != 3:
+        raise ValueError(f"v must be [B, H, d_v], got {tuple(v.shape)}")
+    d_v = v.shape[-1]
+    _shape(k, "k", q.shape)
+    _shape(v, "v", (B, H, d_v))
+    _shape(beta_logit, "beta_logit", (B, H))
+    _shape(W, "W", (B, H, d_v, 2 * d_k * nu))
+    _shape(out, "out", (B, H, d_v))
+    return B, H, d_k, d_v
 
 
 def delta_step(q, k, v, beta_logit, W, nu=1, out=None):
     """One decode step; W [B,H,d_v,D] fp32 is updated in place.  Returns y [B,H,d_v]."""
+    B, H, d_k, d_v = check_step_shapes(q, k, v, beta_logit, W, nu, out)
     dev = q.device
-    B, H, d_k = q.shape
-    d_v = v.shape[-1]
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta_logit, "beta_logit")):
         _need(t, n, dev, q.dtype)
     _need(W, "W", dev, torch.float32)
-    if W.shape != (B, H, d_v, 2 * d_k * nu):
-        raise ValueError(f"W must be {(B, H, d_v, 2 * d_k * nu)}")
     if out is None:
         out = torch.empty(B, H, d_v, dtype=q.dtype, device=dev)
     _need(out, "out", dev, q.dtype)
     _check(lib().fwa_delta_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta_logit), _ptr(W), _ptr(out),
-                                B, H, d_k, d_v, nu, _dtype_code(q), _stream(dev)))
+                                B, H, d_k, d_v, nu, _dtype_code(q.dtype), _stream(dev)))
     return out

@@ -77,6 +77,40 @@ def make_inputs(w: Workload, seed: Optional[int] = None):
     return dict(q=cast(q), k=cast(k), v=cast(v), beta_logit=cast(beta_logit), W0=W0)
 
 
+EDGE_CASES = ("beta_saturated", "tiny_keys", "repeated_key", "zero_keys")
+
+
+def make_edge_inputs(w: Workload, case: str, seed: Optional[int] = None):
+    """Forward inputs (as make_inputs) reshaped into one of the method's edge cases:
+      beta_saturated  beta_logit = +-20 (sign drawn at random): beta within 2e-9 of 0 or 1;
+      tiny_keys       k scaled by 1e-3, so DPFP's sum is of the order of its eps;
+      repeated_key    rows [40, 104) of k (across a chunk boundary at 64) all equal row 40;
+      zero_keys       every 7th row of k (from row 3) and rows [64, 80) are zero.
+    The edits are made on the fp32 draw, before any rounding to bf16."""
+    g = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    q = torch.randn(w.B, w.H, w.T, w.d_k, generator=g)
+    k = torch.randn(w.B, w.H, w.T, w.d_k, generator=g)
+    v = torch.randn(w.B, w.H, w.T, w.d_v, generator=g)
+    beta_logit = torch.randn(w.B, w.H, w.T, generator=g)
+    W0 = None
+    if w.w0_std is not None:
+        W0 = torch.randn(w.B, w.H, w.d_v, w.D, generator=g) * w.w0_std
+    if case == "beta_saturated":
+        beta_logit = torch.where(beta_logit >= 0, 20.0, -20.0)
+    elif case == "tiny_keys":
+        k = k * 1e-3
+    elif case == "repeated_key":
+        lo, hi = min(40, w.T), min(104, w.T)
+        k[:, :, lo:hi] = k[:, :, lo:lo + 1]
+    elif case == "zero_keys":
+        k[:, :, 3::7] = 0.0
+        k[:, :, 64:80] = 0.0
+    else:
+        raise ValueError(f"unknown edge case {case!r}")
+    cast = (lambda t: t.to(torch.bfloat16)) if w.dtype == "bf16" else (lambda t: t)
+    return dict(q=cast(q), k=cast(k), v=cast(v), beta_logit=cast(beta_logit), W0=W0)
+
+
 def make_decode_inputs(w: Workload, steps: Optional[int] = None, seed: Optional[int] = None):
     """Decode inputs on the CPU for `steps` successive tokens: q, k [S,B,H,d_k], v [S,B,H,d_v],
     beta_logit [S,B,H], and the initial state W0 (zeros unless w0_std is set)."""

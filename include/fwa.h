@@ -166,6 +166,25 @@ fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, con
                                   int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fwa_delta_forward_noalloc -- fwa_delta_forward for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments as fwa_delta_forward without the workspace, same
+ * results and errors.  Its scratch is a static device array of 64 MiB (FWA_NOALLOC_SCRATCH_BYTES)
+ * that each GPU the library runs on holds until the process ends; the call allocates nothing.
+ * Where the planner's implementation needs more scratch than that, the fused implementation
+ * (which needs none) runs instead; where that does not take the sizes either, the call returns
+ * FWA_ERR_UNSUPPORTED before launching anything.  Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap in time on one GPU (different streams, or host threads
+ * without ordering) race and must not be issued; calls in order on one stream are safe.  The
+ * scratch needs no initial contents.
+ */
+#define FWA_NOALLOC_SCRATCH_BYTES (64ll << 20)
+fwa_status fwa_delta_forward_noalloc(const void* q, const void* k, const void* v,
+                                     const void* beta_logit, const float* W0, void* y,
+                                     float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
+                                     int chunk, fwa_dtype dtype, hipStream_t stream);
+
+/*
  * fwa_delta_forward_info -- which implementation a forward call with `request` (an
  * fwa_forward_path; FWA_PATH_AUTO for fwa_delta_forward) takes for these sizes and the
  * workspace bytes it needs, without touching the device.

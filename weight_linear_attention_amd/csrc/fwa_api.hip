@@ -8,6 +8,7 @@
 
 #include <cstdarg>
 #include <cstring>
+#include <mutex>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -195,7 +196,8 @@ fwa_status check_forward_call(const char* fn, int request, const void* q, const 
                               const void* v, const void* beta_logit, const float* W0,
                               const void* y, const float* W_final, int B, int H, int T, int d_k,
                               int d_v, int nu, int chunk, fwa_dtype dtype, const void* workspace,
-                              int64_t workspace_bytes, ForwardChoice* c) {
+                              int64_t workspace_bytes, ForwardChoice* c,
+                              bool check_workspace = true) {
     fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
     if (st != FWA_OK) return st;
     const int64_t BH = static_cast<int64_t>(B) * H;
@@ -228,7 +230,7 @@ fwa_status check_forward_call(const char* fn, int request, const void* q, const 
     if ((st = choose_forward(fn, request, static_cast<int>(BH), T, d_k, d_v, nu, chunk,
                              dtype == FWA_BF16, c)) != FWA_OK)
         return st;
-    if (c->ws_bytes > 0) {
+    if (c->ws_bytes > 0 && check_workspace) {
         if (!workspace || workspace_bytes < c->ws_bytes)
             return fail(FWA_ERR_INVALID_ARG,
                         "%s: the %s path needs a workspace of %lld bytes (got %lld%s)", fn,
@@ -319,6 +321,74 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const 
                              void* workspace, int64_t workspace_bytes, hipStream_t stream) {
     return fwa_delta_forward_path(FWA_PATH_AUTO, q, k, v, beta_logit, W0, y, W_final, B, H, T,
                                   d_k, d_v, nu, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of fwa_delta_forward_noalloc: a file-scope device array that every GPU the library
+// runs on holds until the process ends.  Host code never uses its name as an address: each
+// device's copy lives at its own address, taken once per device with hipGetSymbolAddress
+// (with that device current) and kept in g_scratch_ptr.
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+hipError_t scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+fwa_status fwa_delta_forward_noalloc(const void* q, const void* k, const void* v,
+                                     const void* beta_logit, const float* W0, void* y,
+                                     float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
+                                     int chunk, fwa_dtype dtype, hipStream_t stream) {
+    const char* fn = "fwa_delta_forward_noalloc";
+    ForwardChoice c;
+    fwa_status st = check_forward_call(fn, FWA_PATH_AUTO, q, k, v, beta_logit, W0, y, W_final, B,
+                                       H, T, d_k, d_v, nu, chunk, dtype, nullptr, 0, &c, false);
+    if (st != FWA_OK) return st;
+    if (c.path == FWA_PATH_NONE) return ok();
+    if (c.ws_bytes > kNoAllocScratchBytes) {
+        // the planner's choice needs more scratch than the static array holds: the fused
+        // implementation needs none, where it takes these sizes
+        const int64_t need = c.ws_bytes;
+        ForwardChoice f;
+        st = check_forward_call(fn, FWA_PATH_FUSED, q, k, v, beta_logit, W0, y, W_final, B, H, T,
+                                d_k, d_v, nu, chunk, dtype, nullptr, 0, &f, false);
+        if (st != FWA_OK)
+            return fail(FWA_ERR_UNSUPPORTED,
+                        "%s: the planned forward needs %lld bytes of scratch, more than the %lld "
+                        "the static scratch holds, and the fused implementation (no scratch) does "
+                        "not take these sizes",
+                        fn, (long long)need, (long long)kNoAllocScratchBytes);
+        c = f;
+    }
+    void* ws = nullptr;
+    const hipError_t e = scratch_for_current_device(&ws);
+    if (e != hipSuccess) return hip_status(e, "fwa_delta_forward_noalloc scratch address");
+    return launch_forward(c, q, k, v, beta_logit, W0, y, W_final, B * H, H, T, d_k, d_v, nu,
+                          chunk, dtype == FWA_BF16, ws, stream);
 }
 
 fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,

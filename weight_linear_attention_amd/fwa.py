@@ -36,7 +36,8 @@ PATH_NAMES = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED
               FWA_PATH_STREAM: "stream"}
 
 EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_path", "fwa_delta_forward_info",
-            "fwa_delta_step", "fwa_status_string", "fwa_last_error", "fwa_version")
+            "fwa_delta_forward_noalloc", "fwa_delta_step", "fwa_status_string", "fwa_last_error",
+            "fwa_version")
 
 
 class FwaError(RuntimeError):
@@ -65,6 +66,8 @@ def lib():
     L.fwa_delta_forward.restype = i32
     L.fwa_delta_forward_path.argtypes = [i32] + fwd
     L.fwa_delta_forward_path.restype = i32
+    L.fwa_delta_forward_noalloc.argtypes = [P, P, P, P, P, P, P] + [i32] * 7 + [i32, P]
+    L.fwa_delta_forward_noalloc.restype = i32
     L.fwa_delta_forward_info.argtypes = [i32] * 9 + [ctypes.POINTER(i32), ctypes.POINTER(i64)]
     L.fwa_delta_forward_info.restype = i32
     L.fwa_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5 + [i32, P]

@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Only tests/, the package's smoke() check and the benc
 CPU-baseline leg may import this package.  It shares no code with the HIP library and never
 imports it.
 
-`dpfp`, `dpfp_mask`, `delta_forward` and `delta_step` wrap the plain-C fp64 implementation in
+`dpfp`, `dpfp_mask`, `delta_forward`, `delta_step` and `delta_backward` (the gradient of
+`delta_forward`) wrap the plain-C fp64 implementation in
 fwa_oracle.c (built by oracle/build.py); `twin` holds an independent NumPy transcription used to
 cross-check it.  All arrays are float64, C-contiguous, in the [B, H, T, d] layout; W is
 [B, H, d_v, D] with D = 2 * d_k * nu.  Inputs given in fp32 or bf16 are taken exactly (bf16 and
@@ -37,6 +38,7 @@ class Oracle:
         L.oracle_dpfp_mask.argtypes = [P, P, i64, i32, i32]
         L.oracle_delta_forward.argtypes = [P, P, P, P, P, P, P] + [i32] * 6
         L.oracle_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5
+        L.oracle_delta_backward.argtypes = [P] * 12 + [i32] * 6
         L.oracle_sigmoid.argtypes = [ctypes.c_double]
         L.oracle_sigmoid.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
@@ -87,6 +89,31 @@ class Oracle:
         self.lib.oracle_delta_forward(_p(q), _p(k), _p(v), _p(beta_logit), _p(W0), _p(y),
                                       _p(Wf), B, H, T, d_k, d_v, nu)
         return y, Wf
+
+    def delta_backward(self, q, k, v, beta_logit, W0, dy, dW_final=None, nu=1):
+        """Gradients of <dy, y> + <dW_final, W_final> through delta_forward (reverse mode
+        through the literal recurrence).  Returns (dq, dk, dv, dbeta_logit, dW0)."""
+        q, k, v, beta_logit, dy = _f64(q), _f64(k), _f64(v), _f64(beta_logit), _f64(dy)
+        B, H, T, d_k = q.shape
+        d_v = v.shape[-1]
+        D = 2 * d_k * nu
+        assert k.shape == q.shape and v.shape == (B, H, T, d_v) and dy.shape == v.shape
+        assert beta_logit.shape == (B, H, T)
+        if W0 is not None:
+            W0 = _f64(W0)
+            assert W0.shape == (B, H, d_v, D)
+        if dW_final is not None:
+            dW_final = _f64(dW_final)
+            assert dW_final.shape == (B, H, d_v, D)
+        dq = np.empty_like(q)
+        dk = np.empty_like(k)
+        dv = np.empty_like(v)
+        dl = np.empty_like(beta_logit)
+        dW0 = np.empty((B, H, d_v, D), dtype=np.float64)
+        self.lib.oracle_delta_backward(_p(q), _p(k), _p(v), _p(beta_logit), _p(W0), _p(dy),
+                                       _p(dW_final), _p(dq), _p(dk), _p(dv), _p(dl), _p(dW0),
+                                       B, H, T, d_k, d_v, nu)
+        return dq, dk, dv, dl, dW0
 
     def delta_step(self, q, k, v, beta_logit, W, nu=1):
         """One decode step. q,k [B,H,d_k], v [B,H,d_v], beta_logit [B,H], W [B,H,d_v,D].
@@ -142,3 +169,7 @@ def delta_forward(q, k, v, beta_logit, W0=None, nu=1):
 
 def delta_step(q, k, v, beta_logit, W, nu=1):
     return default().delta_step(q, k, v, beta_logit, W, nu)
+
+
+def delta_backward(q, k, v, beta_logit, W0, dy, dW_final=None, nu=1):
+    return default().delta_backward(q, k, v, beta_logit, W0, dy, dW_final, nu)

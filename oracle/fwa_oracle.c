@@ -215,3 +215,188 @@ void oracle_delta_step(const double* q, const double* k, const double* v,
         free(pk); free(pq); free(vbar); free(work);
     }
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Gradient of the forward.  The pages train this layer ([FWT] section "Training experiment":
+ * a cross-entropy loss, gradient-norm clipping), which needs the derivatives of the forward
+ * above with respect to every input.  This is that derivative written out: reverse-mode
+ * differentiation of the literal per-step recurrence, one step at a time from t = T-1 down
+ * to 0.  With f = phi(k_t), g = phi(q_t), beta = sigmoid(l_t), P the memory before step t
+ * and N = P + u f^T (u = beta (v - P f)) the memory after it, and G the gradient of the loss
+ * with respect to N (the running gradient, which starts as dW_final):
+ *   y_t = N g          G += dy_t g^T;   dg = N^T dy_t
+ *   N = P + u f^T      du = G f;        df = G^T u
+ *   u = beta (v - vb)  dv_t = beta du;  dbeta = du . (v - vb);  dvb = -beta du
+ *   vb = P f           G <- G + dvb f^T (now the gradient for P);  df += P^T dvb
+ *   beta = sigmoid(l)  dl_t = dbeta * beta * (1 - beta)
+ * and the DPFP derivative takes df, dg back to dk_t, dq_t (dpfp_vjp_one).  dW0 is the final G.
+ * The memories P, N are recomputed from copies kept every ORACLE_CHECKPOINT steps: the
+ * recomputation repeats the forward's operations in the same order, so every value equals the
+ * forward's own.
+ * ------------------------------------------------------------------------------------------ */
+#define ORACLE_CHECKPOINT 64
+
+/* Derivative of DPFP: given k (length d_k) and dphi (length D), adds nothing and writes
+ * dk = (d phi / d k)^T dphi.  phi = raw / (S + eps) with S = sum(raw), so
+ * draw_m = (dphi_m - sum_j dphi_j phi_j) / (S + eps); raw[(i-1)*2d_k + j] = x[j] x[(j-i) mod 2d_k]
+ * sends draw * x[src] to x[j] and draw * x[j] to x[src]; x = relu([k, -k]) passes dx[j] to
+ * k_j where k_j > 0 and -dx[d_k + j] where k_j < 0 (zero where k_j = 0). */
+static void dpfp_vjp_one(const double* k, const double* dphi, double* dk, int d_k, int nu,
+                         double* x, double* raw, double* dx)
+{
+    const int two_dk = 2 * d_k;
+    const int D = two_dk * nu;
+    for (int j = 0; j < d_k; ++j) {
+        x[j] = k[j] > 0.0 ? k[j] : 0.0;
+        x[d_k + j] = k[j] < 0.0 ? -k[j] : 0.0;
+    }
+    double S = 0.0;
+    for (int i = 1; i <= nu; ++i)
+        for (int j = 0; j < two_dk; ++j) {
+            int src = ((j - i) % two_dk + two_dk) % two_dk;
+            raw[(i - 1) * two_dk + j] = x[j] * x[src];
+            S += raw[(i - 1) * two_dk + j];
+        }
+    const double den = S + ORACLE_DPFP_EPS;
+    double dot = 0.0;  /* sum_j dphi_j phi_j */
+    for (int d = 0; d < D; ++d) dot += dphi[d] * (raw[d] / den);
+    for (int m = 0; m < two_dk; ++m) dx[m] = 0.0;
+    for (int i = 1; i <= nu; ++i)
+        for (int j = 0; j < two_dk; ++j) {
+            int src = ((j - i) % two_dk + two_dk) % two_dk;
+            double draw = (dphi[(i - 1) * two_dk + j] - dot) / den;
+            dx[j] += draw * x[src];
+            dx[src] += draw * x[j];
+        }
+    for (int j = 0; j < d_k; ++j) {
+        double g = 0.0;
+        if (k[j] > 0.0) g += dx[j];
+        if (k[j] < 0.0) g -= dx[d_k + j];
+        dk[j] = g;
+    }
+}
+
+/* Gradients of L = <dy, y> + <dW_final, W_final> through oracle_delta_forward.
+ *   q, k, v, beta_logit, W0   the forward's inputs (W0 may be NULL: zeros)
+ *   dy        [B, H, T, d_v]  gradient with respect to y
+ *   dW_final  [B, H, d_v, D]  gradient with respect to W_final, or NULL (zeros)
+ *   dq, dk    [B, H, T, d_k]; dv [B, H, T, d_v]; dbeta_logit [B, H, T]  outputs
+ *   dW0       [B, H, d_v, D]  output (gradient with respect to W0), or NULL to skip it */
+void oracle_delta_backward(const double* q, const double* k, const double* v,
+                           const double* beta_logit, const double* W0, const double* dy,
+                           const double* dW_final, double* dq, double* dk, double* dv,
+                           double* dbeta_logit, double* dW0, int B, int H, int T, int d_k,
+                           int d_v, int nu)
+{
+    const int D = 2 * d_k * nu;
+    const int64_t BH = (int64_t)B * H;
+    const size_t WS = (size_t)d_v * D;
+    const int nck = (T + ORACLE_CHECKPOINT - 1) / ORACLE_CHECKPOINT;
+#pragma omp parallel
+    {
+        double* ck = (double*)malloc(sizeof(double) * WS * (size_t)(nck > 0 ? nck : 1));
+        double* seg = (double*)malloc(sizeof(double) * WS * (ORACLE_CHECKPOINT + 1));
+        double* G = (double*)malloc(sizeof(double) * WS);
+        double* pk = (double*)malloc(sizeof(double) * (size_t)D);
+        double* pq = (double*)malloc(sizeof(double) * (size_t)D);
+        double* df = (double*)malloc(sizeof(double) * (size_t)D);
+        double* dg = (double*)malloc(sizeof(double) * (size_t)D);
+        double* raw = (double*)malloc(sizeof(double) * (size_t)D);
+        double* vbar = (double*)malloc(sizeof(double) * (size_t)d_v);
+        double* u = (double*)malloc(sizeof(double) * (size_t)d_v);
+        double* du = (double*)malloc(sizeof(double) * (size_t)d_v);
+        double* ytmp = (double*)malloc(sizeof(double) * (size_t)d_v);
+        double* work = (double*)malloc(sizeof(double) * 2 * (size_t)d_k);
+        double* dxw = (double*)malloc(sizeof(double) * 2 * (size_t)d_k);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t s = 0; s < BH; ++s) {
+            /* forward once, keeping the memory at the start of every segment */
+            double* W = seg;
+            if (W0) memcpy(W, W0 + s * WS, sizeof(double) * WS);
+            else memset(W, 0, sizeof(double) * WS);
+            for (int t = 0; t < T; ++t) {
+                if (t % ORACLE_CHECKPOINT == 0)
+                    memcpy(ck + (size_t)(t / ORACLE_CHECKPOINT) * WS, W, sizeof(double) * WS);
+                const int64_t row = s * T + t;
+                dpfp_one(&k[row * d_k], pk, d_k, nu, work);
+                dpfp_one(&q[row * d_k], pq, d_k, nu, work);
+                delta_step_one(W, pk, pq, v + row * d_v, oracle_sigmoid(beta_logit[row]), ytmp,
+                               vbar, d_v, D);
+            }
+            if (dW_final) memcpy(G, dW_final + s * WS, sizeof(double) * WS);
+            else memset(G, 0, sizeof(double) * WS);
+            for (int c = nck - 1; c >= 0; --c) {
+                const int t0 = c * ORACLE_CHECKPOINT;
+                const int t1 = t0 + ORACLE_CHECKPOINT < T ? t0 + ORACLE_CHECKPOINT : T;
+                /* seg[i] = memory after step t0 + i - 1 (seg[0] = memory before step t0) */
+                memcpy(seg, ck + (size_t)c * WS, sizeof(double) * WS);
+                for (int t = t0; t < t1; ++t) {
+                    const int64_t row = s * T + t;
+                    double* Wn = seg + (size_t)(t - t0 + 1) * WS;
+                    memcpy(Wn, seg + (size_t)(t - t0) * WS, sizeof(double) * WS);
+                    dpfp_one(&k[row * d_k], pk, d_k, nu, work);
+                    dpfp_one(&q[row * d_k], pq, d_k, nu, work);
+                    delta_step_one(Wn, pk, pq, v + row * d_v, oracle_sigmoid(beta_logit[row]),
+                                   ytmp, vbar, d_v, D);
+                }
+                for (int t = t1 - 1; t >= t0; --t) {
+                    const int64_t row = s * T + t;
+                    const double* P = seg + (size_t)(t - t0) * WS;
+                    const double* N = seg + (size_t)(t - t0 + 1) * WS;
+                    const double* vt = v + row * d_v;
+                    const double* dyt = dy + row * d_v;
+                    dpfp_one(&k[row * d_k], pk, d_k, nu, work);
+                    dpfp_one(&q[row * d_k], pq, d_k, nu, work);
+                    const double beta = oracle_sigmoid(beta_logit[s * T + t]);
+                    for (int r = 0; r < d_v; ++r) {
+                        double sacc = 0.0;
+                        for (int d = 0; d < D; ++d) sacc += P[(size_t)r * D + d] * pk[d];
+                        vbar[r] = sacc;
+                        u[r] = beta * (vt[r] - vbar[r]);
+                    }
+                    /* y_t = N g */
+                    for (int d = 0; d < D; ++d) {
+                        double sacc = 0.0;
+                        for (int r = 0; r < d_v; ++r) sacc += N[(size_t)r * D + d] * dyt[r];
+                        dg[d] = sacc;
+                    }
+                    for (int r = 0; r < d_v; ++r)
+                        for (int d = 0; d < D; ++d) G[(size_t)r * D + d] += dyt[r] * pq[d];
+                    /* N = P + u f^T */
+                    for (int r = 0; r < d_v; ++r) {
+                        double sacc = 0.0;
+                        for (int d = 0; d < D; ++d) sacc += G[(size_t)r * D + d] * pk[d];
+                        du[r] = sacc;
+                    }
+                    for (int d = 0; d < D; ++d) {
+                        double sacc = 0.0;
+                        for (int r = 0; r < d_v; ++r) sacc += G[(size_t)r * D + d] * u[r];
+                        df[d] = sacc;
+                    }
+                    /* u = beta (v - vb) */
+                    double dbeta = 0.0;
+                    for (int r = 0; r < d_v; ++r) {
+                        dv[row * d_v + r] = beta * du[r];
+                        dbeta += du[r] * (vt[r] - vbar[r]);
+                    }
+                    /* vb = P f: G becomes the gradient for P */
+                    for (int r = 0; r < d_v; ++r) {
+                        const double dvb = -beta * du[r];
+                        for (int d = 0; d < D; ++d) G[(size_t)r * D + d] += dvb * pk[d];
+                    }
+                    for (int d = 0; d < D; ++d) {
+                        double sacc = 0.0;
+                        for (int r = 0; r < d_v; ++r) sacc += P[(size_t)r * D + d] * (-beta * du[r]);
+                        df[d] += sacc;
+                    }
+                    dbeta_logit[row] = dbeta * beta * (1.0 - beta);
+                    dpfp_vjp_one(k + row * d_k, df, dk + row * d_k, d_k, nu, work, raw, dxw);
+                    dpfp_vjp_one(q + row * d_k, dg, dq + row * d_k, d_k, nu, work, raw, dxw);
+                }
+            }
+            if (dW0) memcpy(dW0 + s * WS, G, sizeof(double) * WS);
+        }
+        free(ck); free(seg); free(G); free(pk); free(pq); free(df); free(dg); free(raw);
+        free(vbar); free(u); free(du); free(ytmp); free(work); free(dxw);
+    }
+}

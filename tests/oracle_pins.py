@@ -374,4 +374,115 @@ def pin_matches_numpy_twin(O):
         assert abs(O.sigmoid(x) - twin.sigmoid(x)) <= 1e-15
 
 
+# ---------------------------------------------------------------- gradient pins
+# The pages train the layer ([FWT] "Training experiment"), which needs the forward's gradient.
+# These pins tie the oracle's reverse pass to the forward (already pinned above) and to closed
+# forms, never to itself.
+
+def _bwd_case(rng, B, H, T, d_k, d_v, nu, w0=True, dwf=True):
+    """Inputs with |q|, |k| entries in [0.2, 1.5] (no DPFP kink within a finite-difference
+    step), and random cotangents dy, dW_final."""
+    D = 2 * d_k * nu
+    mag = lambda *s: rng.uniform(0.2, 1.5, size=s) * rng.choice([-1.0, 1.0], size=s)
+    q, k = mag(B, H, T, d_k), mag(B, H, T, d_k)
+    v = rng.normal(size=(B, H, T, d_v))
+    l = rng.normal(size=(B, H, T))
+    W0 = rng.normal(size=(B, H, d_v, D)) * 0.3 if w0 else None
+    dy = rng.normal(size=(B, H, T, d_v))
+    dWf = rng.normal(size=(B, H, d_v, D)) if dwf else None
+    return q, k, v, l, W0, dy, dWf
+
+
+def _loss(O, args, nu, dy, dWf):
+    y, W = O.delta_forward(*args, nu=nu)
+    return float((dy * y).sum() + (0.0 if dWf is None else (dWf * W).sum()))
+
+
+def pin_backward_central_differences(O):
+    """Every gradient equals the central difference of the (pinned) forward, on random entries
+    of every input, for nu 1 and 3, with and without W0 and dW_final, and for T = 70 across the
+    reverse pass's 64-step recomputation boundary."""
+    rng = np.random.default_rng(41)
+    h = 1e-6
+    for (B, H, T, d_k, d_v, nu, w0, dwf) in [(1, 2, 9, 4, 3, 1, True, True),
+                                              (1, 1, 70, 4, 3, 3, True, False),
+                                              (2, 1, 6, 8, 5, 2, False, True)]:
+        q, k, v, l, W0, dy, dWf = _bwd_case(rng, B, H, T, d_k, d_v, nu, w0, dwf)
+        grads = O.delta_backward(q, k, v, l, W0, dy, dWf, nu=nu)
+        args = [q, k, v, l, W0]
+        for idx in range(5 if w0 else 4):
+            a0 = args[idx]
+            flat = rng.choice(a0.size, size=min(a0.size, 24), replace=False)
+            num, ana = [], []
+            for f in flat:
+                i = np.unravel_index(f, a0.shape)
+                ap = [x if x is None else x.copy() for x in args]
+                ap[idx][i] += h
+                am = [x if x is None else x.copy() for x in args]
+                am[idx][i] -= h
+                num.append((_loss(O, ap, nu, dy, dWf) - _loss(O, am, nu, dy, dWf)) / (2 * h))
+                ana.append(grads[idx if idx < 4 else 4][i])
+            num, ana = np.array(num), np.array(ana)
+            scale = max(np.abs(num).max(), 1e-12)
+            assert np.abs(num - ana).max() / scale < 1e-6, (idx, np.abs(num - ana).max() / scale)
+
+
+def pin_backward_euler_identity(O):
+    """(y, W_final) is linear in (v, W0) jointly, so L = <dy, y> + <dW_final, W_final> is
+    homogeneous of degree one in them: sum(v * dv) + sum(W0 * dW0) = L exactly (up to
+    rounding), over T = 150 (three recomputation segments)."""
+    rng = np.random.default_rng(42)
+    q, k, v, l, W0, dy, dWf = _bwd_case(rng, 2, 2, 150, 8, 6, 2)
+    L = _loss(O, [q, k, v, l, W0], 2, dy, dWf)
+    _, _, dv, _, dW0 = O.delta_backward(q, k, v, l, W0, dy, dWf, nu=2)
+    lhs = float((v * dv).sum() + (W0 * dW0).sum())
+    assert abs(lhs - L) <= 1e-10 * max(1.0, abs(L)), (lhs, L)
+
+
+def pin_backward_one_step_closed_form(O):
+    """T = 1 from W0 = 0: y = beta v (f.g) and W = beta v f^T, so dv = beta ((f.g) dy +
+    dW_final f), dl = beta (1 - beta) ((f.g) (dy.v) + v^T dW_final f) and
+    dW0 = dW_final + dy g^T - beta (dW_final f + (f.g) dy) f^T."""
+    rng = np.random.default_rng(43)
+    d_k, d_v, nu = 6, 4, 2
+    q, k, v, l, _, dy, dWf = _bwd_case(rng, 1, 1, 1, d_k, d_v, nu, w0=False)
+    W0 = np.zeros((1, 1, d_v, 2 * d_k * nu))
+    _, _, dv, dl, dW0 = O.delta_backward(q, k, v, l, W0, dy, dWf, nu=nu)
+    f, g = O.dpfp(k[0, 0, 0], nu), O.dpfp(q[0, 0, 0], nu)
+    beta = 1.0 / (1.0 + math.exp(-l[0, 0, 0]))
+    fg = float(f @ g)
+    Gf = dWf[0, 0] @ f
+    np.testing.assert_allclose(dv[0, 0, 0], beta * (fg * dy[0, 0, 0] + Gf), rtol=1e-12, atol=1e-14)
+    exp_dl = beta * (1 - beta) * (fg * float(dy[0, 0, 0] @ v[0, 0, 0]) + float(v[0, 0, 0] @ Gf))
+    assert abs(dl[0, 0, 0] - exp_dl) <= 1e-12 * max(1.0, abs(exp_dl))
+    du = Gf + fg * dy[0, 0, 0]
+    exp_dW0 = dWf[0, 0] + np.outer(dy[0, 0, 0], g) - beta * np.outer(du, f)
+    np.testing.assert_allclose(dW0[0, 0], exp_dW0, rtol=1e-12, atol=1e-13)
+
+
+def pin_backward_degenerate(O):
+    """beta = 0 (logit -60): no write happens, so dv = 0, dk = 0, dl = 0 and dW0 = dW_final +
+    sum_t dy_t phi(q_t)^T; zero key rows have zero dk (relu's derivative at 0 taken as 0) and
+    leave dv of their step at beta * (dW f) = 0; d_k = 1 makes phi identically 0."""
+    rng = np.random.default_rng(44)
+    nu = 2
+    q, k, v, l, W0, dy, dWf = _bwd_case(rng, 1, 2, 12, 4, 3, nu)
+    l[:] = -60.0
+    dq, dk, dv, dl, dW0 = O.delta_backward(q, k, v, l, W0, dy, dWf, nu=nu)
+    assert np.abs(dv).max() < 1e-20 and np.abs(dk).max() < 1e-18 and np.abs(dl).max() < 1e-20
+    phq = O.dpfp(q, nu)
+    np.testing.assert_allclose(dW0, dWf + np.einsum("bhtv,bhtd->bhvd", dy, phq), rtol=1e-12,
+                               atol=1e-13)
+    q, k, v, l, W0, dy, dWf = _bwd_case(rng, 1, 1, 10, 4, 3, nu)
+    k[0, 0, 3] = 0.0
+    k[0, 0, 7] = 0.0
+    dq, dk, dv, dl, dW0 = O.delta_backward(q, k, v, l, W0, dy, dWf, nu=nu)
+    assert not dk[0, 0, 3].any() and not dk[0, 0, 7].any()
+    assert dk[0, 0, 2].any() and dk[0, 0, 4].any()
+    q, k, v, l, W0, dy, dWf = _bwd_case(rng, 1, 1, 5, 1, 2, 1)
+    dq, dk, dv, dl, dW0 = O.delta_backward(q, k, v, l, W0, dy, dWf, nu=1)
+    assert not dq.any() and not dk.any() and not dl.any()
+    np.testing.assert_array_equal(dW0, dWf)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -51,6 +51,28 @@ MUTANTS = {
         "int pos_s = src < d_k ? (k[src] > 0.0) : (k[src - d_k] > 0.0);"),
     "step_beta_not_squashed": (
         "double beta = oracle_sigmoid(beta_logit[s]);", "double beta = beta_logit[s];"),
+    # the reverse pass
+    "bwd_retrieval_term_dropped": (
+        "for (int d = 0; d < D; ++d) G[(size_t)r * D + d] += dvb * pk[d];",
+        "for (int d = 0; d < D; ++d) G[(size_t)r * D + d] += 0.0 * pk[d];"),
+    "bwd_key_grad_from_new_memory": (
+        "sacc += P[(size_t)r * D + d] * (-beta * du[r]);",
+        "sacc += N[(size_t)r * D + d] * (-beta * du[r]);"),
+    "bwd_query_grad_from_old_memory": (
+        "sacc += N[(size_t)r * D + d] * dyt[r];", "sacc += P[(size_t)r * D + d] * dyt[r];"),
+    "bwd_dpfp_normaliser_term_dropped": (
+        "double draw = (dphi[(i - 1) * two_dk + j] - dot) / den;",
+        "double draw = dphi[(i - 1) * two_dk + j] / den;"),
+    "bwd_dpfp_negative_half_sign": (
+        "if (k[j] < 0.0) g -= dx[d_k + j];", "if (k[j] < 0.0) g += dx[d_k + j];"),
+    "bwd_dpfp_rolled_factor": ("dx[src] += draw * x[j];", "dx[src] += draw * x[src];"),
+    "bwd_sigmoid_derivative_dropped": (
+        "dbeta_logit[row] = dbeta * beta * (1.0 - beta);", "dbeta_logit[row] = dbeta;"),
+    "bwd_dv_missing_beta": ("dv[row * d_v + r] = beta * du[r];", "dv[row * d_v + r] = du[r];"),
+    "bwd_dbeta_sign": ("dbeta += du[r] * (vt[r] - vbar[r]);", "dbeta += du[r] * (vbar[r] - vt[r]);"),
+    "bwd_checkpoint_stale": (
+        "memcpy(ck + (size_t)(t / ORACLE_CHECKPOINT) * WS, W, sizeof(double) * WS);",
+        "if (t == 0) memcpy(ck + (size_t)(t / ORACLE_CHECKPOINT) * WS, W, sizeof(double) * WS);"),
 }
 
 

@@ -198,6 +198,42 @@ fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu,
                                   int64_t* workspace_bytes);
 
 /*
+ * fwa_delta_backward -- gradient of fwa_delta_forward: given dy = dL/dy and dW_final =
+ * dL/dW_final, returns dL/dq, dL/dk, dL/dv, dL/dbeta_logit and dL/dW0 for the same inputs.
+ *   The pages train this layer with a cross-entropy loss and gradient clipping ([FWT] section
+ *   "Training experiment"), which takes the derivative of the forward of [FWT] sections
+ *   "FastWeightsAttention / update formula" and "DPFP"; this is that derivative (ReLU's
+ *   derivative at 0 taken as 0).
+ *   q, k, v, beta_logit, W0   the forward's inputs, as fwa_delta_forward takes them (W0 NULL
+ *                             for zeros)
+ *   dy          [B, H, T, d_v]  `dtype`
+ *   dW_final    [B, H, d_v, D]  fp32, or NULL when the loss does not depend on W_final
+ *   dq, dk      [B, H, T, d_k]  `dtype`, output
+ *   dv          [B, H, T, d_v]  `dtype`, output
+ *   dbeta_logit [B, H, T]       `dtype`, output
+ *   dW0         [B, H, d_v, D]  fp32 output, or NULL to skip it
+ *   workspace   caller-owned device scratch of at least the bytes fwa_delta_backward_info
+ *               reports, under the same rule as fwa_delta_forward's
+ *   The memory is recomputed (no forward state is taken from the caller).  Outputs must not
+ *   overlap the inputs, each other or the workspace.  T == 0 writes dW0 = dW_final (or zeros).
+ *   Arithmetic is fp32 throughout (fp32 state and gradients), chunks of 32 rows.
+ *   Implemented shapes: d_k in {16, 32, 64}, d_v <= 64, D = 2*d_k*nu <= 384.
+ */
+fwa_status fwa_delta_backward(const void* q, const void* k, const void* v,
+                              const void* beta_logit, const float* W0, const void* dy,
+                              const float* dW_final, void* dq, void* dk, void* dv,
+                              void* dbeta_logit, float* dW0, int B, int H, int T, int d_k,
+                              int d_v, int nu, fwa_dtype dtype, void* workspace,
+                              int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fwa_delta_backward_info -- the workspace bytes fwa_delta_backward needs for these sizes
+ * (0 when B*H == 0), without touching the device.  Size errors are those of the backward.
+ */
+fwa_status fwa_delta_backward_info(int B, int H, int T, int d_k, int d_v, int nu,
+                                   fwa_dtype dtype, int64_t* workspace_bytes);
+
+/*
  * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory
  * carried in and out through W, updated in place.
  *   [FWT] sections "token_wise variant" and "Inference and sampling" (each new token updates

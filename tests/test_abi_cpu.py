@@ -341,3 +341,50 @@ def test_binding_rejects_unknown_path():
     with pytest.raises(ValueError, match="path"):
         fwa.delta_forward(_t(B, H, T, dk), _t(B, H, T, dk), _t(B, H, T, dk), _t(B, H, T),
                           path="fastest")
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=P(0x20000), v=P(0x30000), bl=P(0x40000), W0=None, dy=P(0x60000),
+             dWf=None, dq=P(0x70000), dk=P(0x80000), dv=P(0x90000), dbl=P(0xa0000), dW0=None,
+             B=1, H=1, T=8, d_k=16, d_v=16, nu=1, dtype=0, ws=P(0x1000000), ws_bytes=1 << 24)
+    a.update(kw)
+    return fwa.lib().fwa_delta_backward(
+        a["q"], a["k"], a["v"], a["bl"], a["W0"], a["dy"], a["dWf"], a["dq"], a["dk"], a["dv"],
+        a["dbl"], a["dW0"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["nu"], a["dtype"],
+        a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dy=None), 1, "NULL"),
+    (dict(dq=None), 1, "NULL"),
+    (dict(T=-1), 1, "negative"),
+    (dict(nu=0), 1, "nu"),
+    (dict(dtype=5), 1, "dtype"),
+    (dict(dk=MISALIGNED), 1, "aligned"),
+    (dict(ws=None), 1, "workspace of"),
+    (dict(ws_bytes=64), 1, "workspace of"),
+    (dict(dq=P(0x20000)), 1, "output overlaps an input"),
+    (dict(dv=P(0x80000)), 1, "two outputs overlap"),
+    (dict(d_k=24), 2, "d_k"),
+    (dict(d_v=65), 2, "d_v"),
+    (dict(d_k=64, nu=4), 2, "384"),
+])
+def test_backward_rejects(kw, status, msg):
+    assert _bwd(**kw) == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+def test_backward_info_and_empty_batch():
+    import torch
+    assert _bwd(B=0, q=None, dy=None, dq=None) == 0
+    ws = fwa.delta_backward_info(4, 8, 4096, 64, 64, 2, torch.bfloat16)
+    nc = 4096 // 32
+    D = 256
+    per_chunk = 4 * 32 * D + 3 * 32 * 32 + 32 + 3 * 32 * 64 + 2 * 64 * D
+    assert ws == 4 * 8 * nc * per_chunk * 4        # B * H chunks of nc, fp32
+    assert fwa.delta_backward_info(0, 8, 100, 64, 64, 1) == 0
+    with pytest.raises(fwa.FwaError) as e:
+        fwa.delta_backward_info(1, 1, 10, 64, 128, 1)
+    assert e.value.status == fwa.FWA_ERR_UNSUPPORTED

@@ -1,0 +1,712 @@
+// Gradient of the chunked forward: dq, dk, dv, dbeta_logit and dW0 from dy and dW_final.
+//
+// The layer is trained ("Fast Weights Transformer" guide, xdnf.cn/news/308600, section
+// "Training experiment"), so its forward -- the delta rule of section "FastWeightsAttention /
+// update formula" over the DPFP features of section "DPFP" -- needs its derivatives.  They are
+// taken through the chunk form of the recurrence.  For a chunk of C rows starting from memory
+// W0 (d_v x D) with normalised features K, Q (C x D), beta (C):
+//   G = K K^T,  P = lower_incl(Q K^T),  A = I + diag(beta) strict_lower(G),  T = A^-1 diag(beta)
+//   U = T (V - K W0^T),  Y = Q W0^T + P U,  W1 = W0 + U^T K.
+// With Wy = T K and Uy = T V this is U = Uy - Wy W0^T.  Given dY and dW1 (the gradient of the
+// chunk-end memory), with Ainv = A^-1:
+//   dU = P^T dY + K dW1^T;  lam = Ainv^T dU;  dV = diag(beta) lam
+//   dW0 = dW1 + dY^T Q' - dW1 K^T Wy,  Q' = Q - P Wy           (the reverse chain)
+//   dP = lower_incl(dY U^T);  Z = lam U^T;  dG_ij = -beta_i Z_ij (j < i)
+//   dQ = dY W0 + dP K
+//   dK = U dW1 - diag(beta) lam W0 + dP^T Q + (dG + dG^T) K
+//   dbeta_i = lam_i.V_i - (lam W0)_i.K_i - sum_{j<i} G_ij Z_ij,   dlogit = dbeta beta (1 - beta)
+// and the derivative of DPFP takes dK, dQ to dk, dq.
+//
+// Both chains are row-separable: row r of the memory (and of its gradient) moves with its own
+// column of V (of dY) alone, so the serial passes run one wave per row.  Five launches:
+//   1. bwd_prep         per chunk: K, Q, G, P, Ainv, Wy, Q', Uy, beta           (parallel)
+//   2. bwd_fwd_states   per (b, h, 8 rows): chunk-start memories and U          (serial)
+//   3. bwd_grad_states  per (b, h, 8 rows): chunk-end gradients, K dW1^T, dW0   (serial)
+//   4. bwd_chunk_grads  per chunk: dK, dQ (over 2, 3), dv, dbeta_logit           (parallel)
+//   5. bwd_dpfp         per vector: dk, dq                                      (parallel)
+// Arithmetic is fp32 on the vector ALU; chunk C = 32.
+#include "fwa_common.h"
+#include "fwa_internal.h"
+
+namespace fwa {
+
+constexpr int kBC = 32;              // rows per chunk
+constexpr int kPrepThreads2 = 256;
+constexpr int kRowWaves = 8;         // memory rows per serial workgroup (one wave each)
+
+// Workspace regions (fp32), each indexed by the chunk u = bh * NC + n.
+struct BwdLayout {
+    int64_t kt, qt, wy, qp, ai, pm, gm, be, uy, uu, aa, ws, gs, end;
+};
+
+__host__ __device__ inline BwdLayout bwd_layout(int64_t NU, int D, int d_v) {
+    BwdLayout L;
+    int64_t o = 0;
+    const int64_t CD = int64_t(kBC) * D, CC = int64_t(kBC) * kBC, CV = int64_t(kBC) * d_v;
+    const int64_t VD = int64_t(d_v) * D;
+    L.kt = o; o += NU * CD;
+    L.qt = o; o += NU * CD;
+    L.wy = o; o += NU * CD;      // Wy, then dK (bwd_chunk_grads)
+    L.qp = o; o += NU * CD;      // Q', then dQ
+    L.ai = o; o += NU * CC;
+    L.pm = o; o += NU * CC;
+    L.gm = o; o += NU * CC;
+    L.be = o; o += NU * kBC;
+    L.uy = o; o += NU * CV;      // [c][r]
+    L.uu = o; o += NU * CV;      // [r][c]
+    L.aa = o; o += NU * CV;      // [r][c]
+    L.ws = o; o += NU * VD;      // chunk-start memory [r][d]
+    L.gs = o; o += NU * VD;      // chunk-end memory gradient [r][d]
+    L.end = o;
+    return L;
+}
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* bl;
+    const float* W0;
+    const void* dy;
+    const float* dWf;
+    void* dq;
+    void* dk;
+    void* dv;
+    void* dbl;
+    float* dW0;
+    float* ws;
+    int BH, T, NC, d_k, d_v, nu, D;
+    BwdLayout L;
+};
+
+// ------------------------------------------------------------------------------ 1. prep
+
+// LDS: x rows of k and q (relu([., -.]), C x 2 d_k each), K and Q (C x D), G, P, Ainv
+// (C x (C + 1)), beta, row sums, V (C x d_v).
+template <bool BF16>
+__global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int D = a.D, d_k = a.d_k, d_v = a.d_v, two = 2 * d_k;
+    const int u = blockIdx.x;
+    const int bh = u / a.NC, n = u % a.NC;
+    const int t0 = n * kBC;
+    const int tid = threadIdx.x;
+    constexpr int CS = kBC + 1;
+    float* xk = lds;                         // [C][2 d_k]
+    float* xq = xk + kBC * two;
+    float* Kt = xq + kBC * two;              // [C][D]
+    float* Qt = Kt + kBC * D;
+    float* Gm = Qt + kBC * D;                // [C][CS]
+    float* Pm = Gm + kBC * CS;
+    float* Ai = Pm + kBC * CS;
+    float* be = Ai + kBC * CS;               // [C]
+    float* rs = be + kBC;                    // [2C]: row sum + eps of K, then of Q
+    float* Vs = rs + 2 * kBC;                // [C][d_v]
+
+    // raw rows (zero past the sequence end), beta (zero past the end), v
+    for (int i = tid; i < kBC * d_k; i += kPrepThreads2) {
+        const int c = i / d_k, j = i % d_k;
+        float kv = 0.0f, qv = 0.0f;
+        if (t0 + c < a.T) {
+            const int64_t g = (int64_t(bh) * a.T + t0 + c) * d_k + j;
+            kv = load_elem<BF16>(a.k, g);
+            qv = load_elem<BF16>(a.q, g);
+        }
+        xk[c * two + j] = relu(kv);
+        xk[c * two + d_k + j] = relu(-kv);
+        xq[c * two + j] = relu(qv);
+        xq[c * two + d_k + j] = relu(-qv);
+    }
+    for (int c = tid; c < kBC; c += kPrepThreads2)
+        be[c] = t0 + c < a.T ? sigmoid_stable(load_elem<BF16>(a.bl, int64_t(bh) * a.T + t0 + c)) : 0.0f;
+    for (int i = tid; i < kBC * d_v; i += kPrepThreads2) {
+        const int c = i / d_v, r = i % d_v;
+        Vs[i] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
+    }
+    __syncthreads();
+    // raw DPFP products: block i - 1 holds x[j] x[(j - i) mod 2 d_k]
+    for (int e = tid; e < kBC * D; e += kPrepThreads2) {
+        const int c = e / D, p = e % D;
+        const int i = p / two + 1, j = p % two;
+        int src = j - i;
+        src += (src < 0) ? two : 0;
+        Kt[e] = xk[c * two + j] * xk[c * two + src];
+        Qt[e] = xq[c * two + j] * xq[c * two + src];
+    }
+    __syncthreads();
+    if (tid < 2 * kBC) {
+        const float* row = (tid < kBC ? Kt : Qt) + (tid % kBC) * D;
+        float s = 0.0f;
+        for (int p = 0; p < D; ++p) s += row[p];
+        rs[tid] = s + kDpfpEps;
+    }
+    __syncthreads();
+    const int64_t CD = int64_t(kBC) * D;
+    float* gK = a.ws + a.L.kt + int64_t(u) * CD;
+    float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
+    for (int e = tid; e < kBC * D; e += kPrepThreads2) {
+        const int c = e / D;
+        const float kv = Kt[e] / rs[c], qv = Qt[e] / rs[kBC + c];
+        Kt[e] = kv;
+        Qt[e] = qv;
+        gK[e] = kv;
+        gQ[e] = qv;
+    }
+    __syncthreads();
+    // G = K K^T and P = lower_incl(Q K^T): thread -> (row c, 4 columns j0..j0+3)
+    {
+        const int c = tid / 8, j0 = (tid % 8) * 4;
+        float g[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
+        for (int p = 0; p < D; ++p) {
+            const float kc = Kt[c * D + p], qc = Qt[c * D + p];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kj = Kt[(j0 + e) * D + p];
+                g[e] += kc * kj;
+                pq[e] += qc * kj;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            Gm[c * CS + j0 + e] = g[e];
+            Pm[c * CS + j0 + e] = (j0 + e <= c) ? pq[e] : 0.0f;
+        }
+    }
+    __syncthreads();
+    // Ainv = (I + diag(beta) strict_lower(G))^-1 by forward substitution, one column per thread
+    if (tid < kBC) {
+        const int j = tid;
+        float x[kBC];
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) x[i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) {
+            if (i == j) x[i] = 1.0f;
+            if (i > j) {
+                float s = 0.0f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) s += Gm[i * CS + m] * x[m];
+                x[i] = -be[i] * s;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) Ai[i * CS + j] = x[i];
+    }
+    __syncthreads();
+    // Wy = Ainv diag(beta) K and Q' = Q - P Wy, one column of D per thread at a time
+    float* gWy = a.ws + a.L.wy + int64_t(u) * CD;
+    float* gQp = a.ws + a.L.qp + int64_t(u) * CD;
+    for (int p = tid; p < D; p += kPrepThreads2) {
+        float bk[kBC], wy[kBC];
+#pragma unroll
+        for (int j = 0; j < kBC; ++j) bk[j] = be[j] * Kt[j * D + p];
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j <= i; ++j) s += Ai[i * CS + j] * bk[j];
+            wy[i] = s;
+            gWy[i * D + p] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < kBC; ++i) {
+            float s = Qt[i * D + p];
+#pragma unroll
+            for (int j = 0; j <= i; ++j) s -= Pm[i * CS + j] * wy[j];
+            gQp[i * D + p] = s;
+        }
+    }
+    // Uy = Ainv diag(beta) V ([c][r])
+    float* gUy = a.ws + a.L.uy + int64_t(u) * kBC * d_v;
+    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
+        const int i = e / d_v, r = e % d_v;
+        float s = 0.0f;
+        for (int j = 0; j <= i; ++j) s += Ai[i * CS + j] * be[j] * Vs[j * d_v + r];
+        gUy[e] = s;
+    }
+    // Ainv, P, G, beta
+    float* gAi = a.ws + a.L.ai + int64_t(u) * kBC * kBC;
+    float* gPm = a.ws + a.L.pm + int64_t(u) * kBC * kBC;
+    float* gGm = a.ws + a.L.gm + int64_t(u) * kBC * kBC;
+    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
+        const int i = e / kBC, j = e % kBC;
+        gAi[e] = Ai[i * CS + j];
+        gPm[e] = Pm[i * CS + j];
+        gGm[e] = Gm[i * CS + j];
+    }
+    if (tid < kBC) a.ws[a.L.be + int64_t(u) * kBC + tid] = be[tid];
+}
+
+// ------------------------------------------------------------------------------ row chains
+
+// Reduce-scatter of 32 per-lane partial sums over the wave: on return, lane l holds the sum
+// over all 64 lanes of entry l >> 1.
+__device__ __forceinline__ float wave_reduce_scatter32(float (&v)[kBC]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int half = 16, mask = 32; half >= 1; half >>= 1, mask >>= 1) {
+        const bool up = (lane & mask) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = up ? v[i] : v[i + half];
+            const float keep = up ? v[i + half] : v[i];
+            v[i] = keep + __shfl_xor(send, mask);
+        }
+    }
+    return v[0] + __shfl_xor(v[0], 1);
+}
+
+// Value of `x` held by lane `l` (a wave-uniform index), in every lane.
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Stages `n` floats (a multiple of 4, both pointers 16-byte aligned) from global to LDS with
+// all threads of the workgroup.
+__device__ __forceinline__ void stage(float* dst, const float* src, int n, int tid, int nthr) {
+    for (int i = 4 * tid; i < n; i += 4 * nthr)
+        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
+}
+
+// Chunk-start memories and U: row r of the memory moves as w <- w + K^T u with
+// u = Uy[:, r] - Wy w.  Lane l holds w[l + 64 m], m < NPL.
+template <int NPL>
+__global__ __launch_bounds__(64 * kRowWaves) void bwd_fwd_states_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int D = a.D, d_v = a.d_v;
+    const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
+    const int bh = blockIdx.x / rgroups;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
+    const bool live = r < d_v;
+    float* Wy = lds;                  // [C][D]
+    float* Kt = Wy + kBC * D;         // [C][D]
+    float w[NPL];
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) {
+        const int p = lane + 64 * m;
+        w[m] = (live && a.W0 && p < D) ? a.W0[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
+    }
+    const int64_t CD = int64_t(kBC) * D;
+    for (int n = 0; n < a.NC; ++n) {
+        const int64_t u = int64_t(bh) * a.NC + n;
+        if (live) {
+            float* gw = a.ws + a.L.ws + (u * d_v + r) * D;
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) gw[lane + 64 * m] = w[m];
+        }
+        __syncthreads();
+        stage(Wy, a.ws + a.L.wy + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        stage(Kt, a.ws + a.L.kt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        __syncthreads();
+        float part[kBC];
+#pragma unroll
+        for (int c = 0; c < kBC; ++c) {
+            float s = 0.0f;
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) s += Wy[c * D + lane + 64 * m] * w[m];
+            part[c] = s;
+        }
+        const float x = wave_reduce_scatter32(part);          // (Wy w)[lane >> 1]
+        const int cl = lane >> 1;
+        const float uy = live ? a.ws[a.L.uy + u * kBC * d_v + cl * d_v + r] : 0.0f;
+        const float uc = uy - x;
+        if (live && (lane & 1) == 0) a.ws[a.L.uu + (u * d_v + r) * kBC + cl] = uc;
+#pragma unroll
+        for (int c = 0; c < kBC; ++c) {
+            const float uv = lane_value(uc, 2 * c);
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) w[m] += uv * Kt[c * D + lane + 64 * m];
+        }
+    }
+}
+
+// Chunk-end gradients of the memory, K dW1^T and dW0, chunks in reverse: row r of the
+// gradient moves as g <- g + Q'^T dY[:, r] - Wy^T (K g).
+template <bool BF16, int NPL>
+__global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int D = a.D, d_v = a.d_v;
+    const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
+    const int bh = blockIdx.x / rgroups;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
+    const bool live = r < d_v;
+    float* Kt = lds;                  // [C][D]
+    float* Qp = Kt + kBC * D;
+    float* Wy = Qp + kBC * D;
+    float g[NPL];
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) {
+        const int p = lane + 64 * m;
+        g[m] = (live && a.dWf && p < D) ? a.dWf[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
+    }
+    const int64_t CD = int64_t(kBC) * D;
+    for (int n = a.NC - 1; n >= 0; --n) {
+        const int64_t u = int64_t(bh) * a.NC + n;
+        const int t0 = n * kBC;
+        if (live) {
+            float* gg = a.ws + a.L.gs + (u * d_v + r) * D;
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) gg[lane + 64 * m] = g[m];
+        }
+        // dY[c, r] of this chunk in lane c (zero past the sequence end)
+        float dyc = 0.0f;
+        if (live && lane < kBC && t0 + lane < a.T)
+            dyc = load_elem<BF16>(a.dy, (int64_t(bh) * a.T + t0 + lane) * d_v + r);
+        __syncthreads();
+        stage(Kt, a.ws + a.L.kt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        stage(Qp, a.ws + a.L.qp + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        stage(Wy, a.ws + a.L.wy + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        __syncthreads();
+        float part[kBC];
+#pragma unroll
+        for (int c = 0; c < kBC; ++c) {
+            float s = 0.0f;
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) s += Kt[c * D + lane + 64 * m] * g[m];
+            part[c] = s;
+        }
+        const float ac = wave_reduce_scatter32(part);         // (K g)[lane >> 1]
+        if (live && (lane & 1) == 0) a.ws[a.L.aa + (u * d_v + r) * kBC + (lane >> 1)] = ac;
+#pragma unroll
+        for (int c = 0; c < kBC; ++c) {
+            const float dy = lane_value(dyc, c), av = lane_value(ac, 2 * c);
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D)
+                    g[m] += dy * Qp[c * D + lane + 64 * m] - av * Wy[c * D + lane + 64 * m];
+        }
+    }
+    if (live && a.dW0) {
+#pragma unroll
+        for (int m = 0; m < NPL; ++m)
+            if (lane + 64 * m < D) a.dW0[(int64_t(bh) * d_v + r) * D + lane + 64 * m] = g[m];
+    }
+}
+
+// ------------------------------------------------------------------------------ 4. chunk grads
+
+constexpr int kSlice = 64;   // columns of D per pass in bwd_chunk_grads
+
+template <bool BF16>
+__global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int D = a.D, d_v = a.d_v;
+    const int u = blockIdx.x;
+    const int bh = u / a.NC, n = u % a.NC;
+    const int t0 = n * kBC;
+    const int tid = threadIdx.x;
+    constexpr int CS = kBC + 1;
+    const int CV = kBC * d_v;
+    float* dYs = lds;                 // [C][d_v]
+    float* Us = dYs + CV;             // U
+    float* dUs = Us + CV;             // dU
+    float* Ls = dUs + CV;             // lam
+    float* Vs = Ls + CV;
+    float* Ai = Vs + CV;              // [C][CS]
+    float* Pm = Ai + kBC * CS;
+    float* Gm = Pm + kBC * CS;
+    float* dP = Gm + kBC * CS;
+    float* dG = dP + kBC * CS;        // dG + dG^T
+    float* be = dG + kBC * CS;        // [C]
+    float* bpart = be + kBC;          // [C]: lam_i.V_i - sum_{j<i} G_ij Z_ij
+    float* W0s = bpart + kBC;         // [d_v][kSlice]
+    float* G1s = W0s + d_v * kSlice;
+    float* Ks = G1s + d_v * kSlice;   // [C][kSlice]
+    float* Qs = Ks + kBC * kSlice;
+
+    const int64_t u64 = u;
+    for (int e = tid; e < CV; e += kPrepThreads2) {
+        const int c = e / d_v, r = e % d_v;
+        const bool in = t0 + c < a.T;
+        const int64_t g = (int64_t(bh) * a.T + t0 + c) * d_v + r;
+        dYs[e] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
+        Vs[e] = in ? load_elem<BF16>(a.v, g) : 0.0f;
+        Us[e] = a.ws[a.L.uu + (u64 * d_v + r) * kBC + c];
+        dUs[e] = a.ws[a.L.aa + (u64 * d_v + r) * kBC + c];      // K dW1^T, P^T dY added below
+    }
+    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
+        const int i = e / kBC, j = e % kBC;
+        Ai[i * CS + j] = a.ws[a.L.ai + u64 * kBC * kBC + e];
+        Pm[i * CS + j] = a.ws[a.L.pm + u64 * kBC * kBC + e];
+        Gm[i * CS + j] = a.ws[a.L.gm + u64 * kBC * kBC + e];
+    }
+    if (tid < kBC) be[tid] = a.ws[a.L.be + u64 * kBC + tid];
+    __syncthreads();
+    // dU = P^T dY + K dW1^T
+    for (int e = tid; e < CV; e += kPrepThreads2) {
+        const int i = e / d_v, r = e % d_v;
+        float s = dUs[e];
+        for (int j = i; j < kBC; ++j) s += Pm[j * CS + i] * dYs[j * d_v + r];
+        dUs[e] = s;
+    }
+    __syncthreads();
+    // lam = Ainv^T dU; dv = diag(beta) lam
+    for (int e = tid; e < CV; e += kPrepThreads2) {
+        const int i = e / d_v, r = e % d_v;
+        float s = 0.0f;
+        for (int j = i; j < kBC; ++j) s += Ai[j * CS + i] * dUs[j * d_v + r];
+        Ls[e] = s;
+        if (t0 + i < a.T) store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * s);
+    }
+    __syncthreads();
+    // dP = lower_incl(dY U^T); Z = lam U^T; dG_ij = -beta_i Z_ij (j < i), kept symmetrised
+    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
+        const int i = e / kBC, j = e % kBC;
+        float sp = 0.0f, sz = 0.0f;
+        for (int r = 0; r < d_v; ++r) {
+            sp += dYs[i * d_v + r] * Us[j * d_v + r];
+            sz += Ls[i * d_v + r] * Us[j * d_v + r];
+        }
+        dP[i * CS + j] = j <= i ? sp : 0.0f;
+        dG[i * CS + j] = j < i ? -be[i] * sz : 0.0f;       // strict lower part for now
+        Ai[i * CS + j] = sz;                                // Ai is not needed any more: Z
+    }
+    __syncthreads();
+    if (tid < kBC) {
+        const int i = tid;
+        float s = 0.0f;
+        for (int r = 0; r < d_v; ++r) s += Ls[i * d_v + r] * Vs[i * d_v + r];
+        for (int j = 0; j < i; ++j) s -= Gm[i * CS + j] * Ai[i * CS + j];
+        bpart[i] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {    // upper part = transpose
+        const int i = e / kBC, j = e % kBC;
+        if (j > i) dG[i * CS + j] = dG[j * CS + i];
+    }
+    __syncthreads();
+
+    // per 64-column slice of D: dQ = dY W0 + dP K;  M = lam W0;
+    // dK = U dW1 - diag(beta) M + dP^T Q + (dG + dG^T) K
+    const int i = tid / 8, jq = (tid % 8) * 8;
+    float mk = 0.0f;                                        // sum over D of M_i . K_i
+    const int64_t CD = int64_t(kBC) * D;
+    for (int s0 = 0; s0 < D; s0 += kSlice) {
+        const int sw = D - s0 < kSlice ? D - s0 : kSlice;
+        for (int e = tid; e < d_v * kSlice; e += kPrepThreads2) {
+            const int r = e / kSlice, jj = e % kSlice;
+            const bool in = jj < sw;
+            W0s[e] = in ? a.ws[a.L.ws + (u64 * d_v + r) * D + s0 + jj] : 0.0f;
+            G1s[e] = in ? a.ws[a.L.gs + (u64 * d_v + r) * D + s0 + jj] : 0.0f;
+        }
+        for (int e = tid; e < kBC * kSlice; e += kPrepThreads2) {
+            const int c = e / kSlice, jj = e % kSlice;
+            const bool in = jj < sw;
+            Ks[e] = in ? a.ws[a.L.kt + u64 * CD + c * D + s0 + jj] : 0.0f;
+            Qs[e] = in ? a.ws[a.L.qt + u64 * CD + c * D + s0 + jj] : 0.0f;
+        }
+        __syncthreads();
+        float dq[8], dk[8], mm[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dq[e] = dk[e] = mm[e] = 0.0f;
+        for (int r = 0; r < d_v; ++r) {
+            const float dyv = dYs[i * d_v + r], lv = Ls[i * d_v + r], uv = Us[i * d_v + r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float w0 = W0s[r * kSlice + jq + e];
+                dq[e] += dyv * w0;
+                mm[e] += lv * w0;
+                dk[e] += uv * G1s[r * kSlice + jq + e];
+            }
+        }
+        for (int j = 0; j < kBC; ++j) {
+            const float pij = dP[i * CS + j], pji = dP[j * CS + i], gij = dG[i * CS + j];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kj = Ks[j * kSlice + jq + e];
+                dq[e] += pij * kj;
+                dk[e] += pji * Qs[j * kSlice + jq + e] + gij * kj;
+            }
+        }
+        const float bi = be[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dk[e] -= bi * mm[e];
+            mk += mm[e] * Ks[i * kSlice + jq + e];
+        }
+        float* gdK = a.ws + a.L.wy + u64 * CD + int64_t(i) * D + s0;
+        float* gdQ = a.ws + a.L.qp + u64 * CD + int64_t(i) * D + s0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (jq + e < sw) {
+                gdK[jq + e] = dk[e];
+                gdQ[jq + e] = dq[e];
+            }
+        __syncthreads();
+    }
+    // the 8 threads of row i are adjacent lanes
+    mk += __shfl_xor(mk, 1);
+    mk += __shfl_xor(mk, 2);
+    mk += __shfl_xor(mk, 4);
+    if ((tid & 7) == 0 && t0 + i < a.T) {
+        // beta (1 - beta) as sigmoid(l) sigmoid(-l): 1 - beta cancels where beta rounds to 1
+        const int64_t g = int64_t(bh) * a.T + t0 + i;
+        const float l = load_elem<BF16>(a.bl, g);
+        const float dbeta = bpart[i] - mk;
+        store_elem<BF16>(a.dbl, g, dbeta * sigmoid_stable(l) * sigmoid_stable(-l));
+    }
+}
+
+// ------------------------------------------------------------------------------ 5. DPFP'
+
+// One wave per vector: dx = (d phi / d x)^T dphi for x = k (blockIdx.y == 0, dphi = dK) or
+// x = q (blockIdx.y == 1, dphi = dQ).  phi = raw / (S + eps), so
+// draw_p = (dphi_p - dphi . phi) / (S + eps); with raw(i, j) = x[j] x[(j - i) mod 2 d_k], the
+// relu'd entry m receives sum_i draw(i, m) x[m - i] + draw(i, m + i) x[m + i] (indices mod
+// 2 d_k), and k_j receives that of entry j where k_j > 0 and minus that of entry d_k + j where
+// k_j < 0.
+constexpr int kDpfpWaves = 4;
+
+template <bool BF16>
+__global__ __launch_bounds__(64 * kDpfpWaves) void bwd_dpfp_kernel(BwdArgs a) {
+    __shared__ float xs_all[kDpfpWaves][128];
+    __shared__ float dr_all[kDpfpWaves][512];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t vec = int64_t(blockIdx.x) * kDpfpWaves + wave;      // (bh, t) flat
+    const int64_t nvec = int64_t(a.BH) * a.T;
+    const bool live = vec < nvec;
+    const bool isq = blockIdx.y == 1;
+    const void* x = isq ? a.q : a.k;
+    void* dx_out = isq ? a.dq : a.dk;
+    const int d_k = a.d_k, two = 2 * d_k, D = a.D;
+    float* xs = xs_all[wave];
+    float* dr = dr_all[wave];
+    const int64_t bh = live ? vec / a.T : 0, t = live ? vec % a.T : 0;
+    const float* dphi = a.ws + (isq ? a.L.qp : a.L.wy) +
+                        ((bh * a.NC + t / kBC) * kBC + t % kBC) * int64_t(D);
+    for (int m = lane; m < two; m += 64) {
+        const float kv = live ? load_elem<BF16>(x, vec * d_k + (m % d_k)) : 0.0f;
+        xs[m] = m < d_k ? relu(kv) : relu(-kv);
+    }
+    __syncthreads();
+    float S = 0.0f, dot = 0.0f;
+    for (int p = lane; p < D; p += 64) {
+        const int i = p / two + 1, j = p % two;
+        int src = j - i;
+        src += src < 0 ? two : 0;
+        const float raw = xs[j] * xs[src];
+        S += raw;
+        dot += live ? dphi[p] * raw : 0.0f;
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) {
+        S += __shfl_xor(S, mask);
+        dot += __shfl_xor(dot, mask);
+    }
+    const float den = S + kDpfpEps;
+    const float dphin = dot / den;                          // dphi . phi
+    for (int p = lane; p < D; p += 64) dr[p] = live ? (dphi[p] - dphin) / den : 0.0f;
+    __syncthreads();
+    if (live && lane < d_k) {
+        float dxv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = lane + h * d_k;
+            float s = 0.0f;
+            for (int i = 1; i <= a.nu; ++i) {
+                const int base = (i - 1) * two;
+                int mi = m - i;
+                mi += mi < 0 ? two : 0;
+                int pi = m + i;
+                pi -= pi >= two ? two : 0;
+                s += dr[base + m] * xs[mi] + dr[base + pi] * xs[pi];
+            }
+            dxv[h] = s;
+        }
+        const float kv = load_elem<BF16>(x, vec * d_k + lane);
+        const float gk = (kv > 0.0f ? dxv[0] : 0.0f) - (kv < 0.0f ? dxv[1] : 0.0f);
+        store_elem<BF16>(dx_out, vec * d_k + lane, gk);
+    }
+}
+
+// ------------------------------------------------------------------------------ host
+
+static int bwd_npl(int D) { return (D + 63) / 64; }
+
+bool plan_backward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
+    const int D = 2 * d_k * nu;
+    if (d_k != 16 && d_k != 32 && d_k != 64) return false;
+    if (d_v < 1 || d_v > 64 || D > 384 || nu > 64) return false;
+    const int NC = (T + kBC - 1) / kBC;
+    const BwdLayout L = bwd_layout(int64_t(BH) * NC, D, d_v);
+    *ws_bytes = L.end * 4;
+    return true;
+}
+
+static int lds_prep_bytes(int D, int d_k, int d_v) {
+    return 4 * (2 * kBC * 2 * d_k + 2 * kBC * D + 3 * kBC * (kBC + 1) + 3 * kBC + kBC * d_v);
+}
+static int lds_grads_bytes(int d_v) {
+    return 4 * (5 * kBC * d_v + 5 * kBC * (kBC + 1) + 2 * kBC + 2 * d_v * kSlice + 2 * kBC * kSlice);
+}
+
+template <int NPL, bool BF16>
+static hipError_t launch_rows(const BwdArgs& a, hipStream_t stream) {
+    const int rgroups = (a.d_v + kRowWaves - 1) / kRowWaves;
+    const dim3 grid(static_cast<unsigned>(int64_t(a.BH) * rgroups));
+    auto kf = bwd_fwd_states_kernel<NPL>;
+    auto kg = bwd_grad_states_kernel<BF16, NPL>;
+    const int lf = 4 * 2 * kBC * a.D, lg = 4 * 3 * kBC * a.D;
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kf), lf);
+    if (e != hipSuccess) return e;
+    if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kg), lg)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kf, grid, dim3(64 * kRowWaves), lf, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(kg, grid, dim3(64 * kRowWaves), lg, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_backward_t(BwdArgs a, hipStream_t stream) {
+    const int64_t NU = int64_t(a.BH) * a.NC;
+    hipError_t e;
+    if (NU > 0) {
+        const int lp = lds_prep_bytes(a.D, a.d_k, a.d_v);
+        auto kp = bwd_prep_kernel<BF16>;
+        if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kp), lp)) != hipSuccess) return e;
+        hipLaunchKernelGGL(kp, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads2), lp, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    switch (bwd_npl(a.D)) {
+        case 1: e = launch_rows<1, BF16>(a, stream); break;
+        case 2: e = launch_rows<2, BF16>(a, stream); break;
+        case 3: e = launch_rows<3, BF16>(a, stream); break;
+        case 4: e = launch_rows<4, BF16>(a, stream); break;
+        case 5: e = launch_rows<5, BF16>(a, stream); break;
+        case 6: e = launch_rows<6, BF16>(a, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || NU == 0) return e;
+    const int lg = lds_grads_bytes(a.d_v);
+    auto kc = bwd_chunk_grads_kernel<BF16>;
+    if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kc), lg)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kc, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads2), lg, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nvec = int64_t(a.BH) * a.T;
+    const dim3 grid(static_cast<unsigned>((nvec + kDpfpWaves - 1) / kDpfpWaves), 2);
+    hipLaunchKernelGGL((bwd_dpfp_kernel<BF16>), grid, dim3(64 * kDpfpWaves), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* bl,
+                           const float* W0, const void* dy, const float* dWf, void* dq, void* dk,
+                           void* dv, void* dbl, float* dW0, int BH, int T, int d_k, int d_v,
+                           int nu, bool bf16, void* workspace, hipStream_t stream) {
+    BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.bl = bl; a.W0 = W0; a.dy = dy; a.dWf = dWf;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dbl = dbl; a.dW0 = dW0;
+    a.ws = static_cast<float*>(workspace);
+    a.BH = BH; a.T = T; a.NC = (T + kBC - 1) / kBC; a.d_k = d_k; a.d_v = d_v; a.nu = nu;
+    a.D = 2 * d_k * nu;
+    a.L = bwd_layout(int64_t(BH) * a.NC, a.D, d_v);
+    return bf16 ? launch_backward_t<true>(a, stream) : launch_backward_t<false>(a, stream);
+}
+
+}  // namespace fwa

@@ -115,4 +115,12 @@ hipError_t launch_stream(const StreamPlan& plan, const void* q, const void* k, c
                          const void* bl, const float* W0, void* y, float* Wf, char* ws,
                          hipStream_t stream);
 
+// Gradient of the forward (backward.hip): plan_backward gives the workspace bytes and returns
+// false for shapes it does not implement.
+bool plan_backward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* bl,
+                           const float* W0, const void* dy, const float* dWf, void* dq, void* dk,
+                           void* dv, void* dbl, float* dW0, int BH, int T, int d_k, int d_v,
+                           int nu, bool bf16, void* workspace, hipStream_t stream);
+
 }  // namespace fwa

@@ -14,6 +14,8 @@ Functions (same names as the C entry points, minus the prefix):
     delta_forward_info(B, H, T, d_k, d_v, nu, chunk, dtype, path="auto")
                                                   -> ("chunked" | "stream" | "fused" | "none",
                                                       workspace bytes)
+    delta_backward(q, k, v, beta_logit, dy, W0=None, dW_final=None, nu=1)
+                                                  -> (dq, dk, dv, dbeta_logit, dW0)
 
 Shapes are checked before anything else, so a wrong shape raises ValueError without touching
 the device.  The forward's workspace is allocated here with torch on the current stream (the
@@ -36,8 +38,8 @@ PATH_NAMES = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED
               FWA_PATH_STREAM: "stream"}
 
 EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_path", "fwa_delta_forward_info",
-            "fwa_delta_forward_noalloc", "fwa_delta_step", "fwa_status_string", "fwa_last_error",
-            "fwa_version")
+            "fwa_delta_forward_noalloc", "fwa_delta_backward", "fwa_delta_backward_info",
+            "fwa_delta_step", "fwa_status_string", "fwa_last_error", "fwa_version")
 
 
 class FwaError(RuntimeError):
@@ -70,6 +72,10 @@ def lib():
     L.fwa_delta_forward_noalloc.restype = i32
     L.fwa_delta_forward_info.argtypes = [i32] * 9 + [ctypes.POINTER(i32), ctypes.POINTER(i64)]
     L.fwa_delta_forward_info.restype = i32
+    L.fwa_delta_backward.argtypes = [P] * 12 + [i32] * 6 + [i32, P, i64, P]
+    L.fwa_delta_backward.restype = i32
+    L.fwa_delta_backward_info.argtypes = [i32] * 7 + [ctypes.POINTER(i64)]
+    L.fwa_delta_backward_info.restype = i32
     L.fwa_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5 + [i32, P]
     L.fwa_delta_step.restype = i32
     L.fwa_status_string.argtypes = [i32]
@@ -195,6 +201,45 @@ def delta_forward(q, k, v, beta_logit, W0=None, chunk=64, nu=1, out=None, W_fina
                                         nu, chunk, _dtype_code(q.dtype), _ptr(workspace),
                                         ws_bytes, _stream(dev)))
     return out, W_final
+
+
+def delta_backward_info(B, H, T, d_k, d_v, nu=1, dtype=torch.float32):
+    """Bytes of workspace delta_backward needs for these sizes."""
+    ws = ctypes.c_int64(0)
+    _check(lib().fwa_delta_backward_info(B, H, T, d_k, d_v, nu, _dtype_code(dtype),
+                                         ctypes.byref(ws)))
+    return ws.value
+
+
+def delta_backward(q, k, v, beta_logit, dy, W0=None, dW_final=None, nu=1, need_dW0=True,
+                   workspace=None):
+    """Gradient of delta_forward: returns (dq, dk, dv, dbeta_logit, dW0) for the loss whose
+    gradients with respect to y and W_final are dy and dW_final (None: zero).  dW0 is None when
+    need_dW0 is False."""
+    B, H, T, d_k, d_v, D = check_forward_shapes(q, k, v, beta_logit, W0, nu)
+    _shape(dy, "dy", (B, H, T, d_v))
+    _shape(dW_final, "dW_final", (B, H, d_v, D))
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta_logit, "beta_logit"), (dy, "dy")):
+        _need(t, n, dev, q.dtype)
+    for t, n in ((W0, "W0"), (dW_final, "dW_final")):
+        if t is not None:
+            _need(t, n, dev, torch.float32)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    dv, dl = torch.empty_like(v), torch.empty_like(beta_logit)
+    dW0 = torch.empty(B, H, d_v, D, dtype=torch.float32, device=dev) if need_dW0 else None
+    if workspace is None:
+        nbytes = delta_backward_info(B, H, T, d_k, d_v, nu, q.dtype)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    else:
+        _need(workspace, "workspace", dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().fwa_delta_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta_logit), _ptr(W0),
+                                    _ptr(dy), _ptr(dW_final), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(dl), _ptr(dW0), B, H, T, d_k, d_v, nu,
+                                    _dtype_code(q.dtype), _ptr(workspace), ws_bytes,
+                                    _stream(dev)))
+    return dq, dk, dv, dl, dW0
 
 
 def check_step_shapes(q, k, v, beta_logit, W, nu=1, out=None):

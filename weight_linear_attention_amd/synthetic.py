@@ -111,6 +111,18 @@ def make_edge_inputs(w: Workload, case: str, seed: Optional[int] = None):
     return dict(q=cast(q), k=cast(k), v=cast(v), beta_logit=cast(beta_logit), W0=W0)
 
 
+def make_cotangents(w: Workload, with_dW_final: bool = True, seed: Optional[int] = None):
+    """Gradients of a loss with respect to the forward's outputs, for the backward: dy
+    [B,H,T,d_v] ~ N(0, 1) in the workload's dtype and dW_final [B,H,d_v,D] ~ N(0, 1) fp32
+    (None when with_dW_final is False), drawn from seed + 100 in that order."""
+    g = torch.Generator("cpu").manual_seed((w.seed if seed is None else seed) + 100)
+    dy = torch.randn(w.B, w.H, w.T, w.d_v, generator=g)
+    dWf = torch.randn(w.B, w.H, w.d_v, w.D, generator=g) if with_dW_final else None
+    if w.dtype == "bf16":
+        dy = dy.to(torch.bfloat16)
+    return dict(dy=dy, dW_final=dWf)
+
+
 def make_decode_inputs(w: Workload, steps: Optional[int] = None, seed: Optional[int] = None):
     """Decode inputs on the CPU for `steps` successive tokens: q, k [S,B,H,d_k], v [S,B,H,d_v],
     beta_logit [S,B,H], and the initial state W0 (zeros unless w0_std is set)."""

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Only tests/, the package's smoke() check and the benc
 CPU-baseline leg may import this package.  It shares no code with the HIP library and never
 imports it.
 
-`dpfp`, `dpfp_mask`, `delta_forward`, `delta_step` and `delta_backward` (the gradient of
-`delta_forward`) wrap the plain-C fp64 implementation in
+`dpfp`, `dpfp_mask`, `delta_forward`, `delta_step`, `delta_backward` (the gradient of
+`delta_forward`) and `sum_forward` (sum-update linear attention with the z normaliser) wrap the plain-C fp64 implementation in
 fwa_oracle.c (built by oracle/build.py); `twin` holds an independent NumPy transcription used to
 cross-check it.  All arrays are float64, C-contiguous, in the [B, H, T, d] layout; W is
 [B, H, d_v, D] with D = 2 * d_k * nu.  Inputs given in fp32 or bf16 are taken exactly (bf16 and
@@ -39,6 +39,7 @@ class Oracle:
         L.oracle_delta_forward.argtypes = [P, P, P, P, P, P, P] + [i32] * 6
         L.oracle_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5
         L.oracle_delta_backward.argtypes = [P] * 12 + [i32] * 6
+        L.oracle_sum_forward.argtypes = [P] * 8 + [i32] * 6
         L.oracle_sigmoid.argtypes = [ctypes.c_double]
         L.oracle_sigmoid.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
@@ -115,6 +116,26 @@ class Oracle:
                                        B, H, T, d_k, d_v, nu)
         return dq, dk, dv, dl, dW0
 
+    def sum_forward(self, q, k, v, W0=None, z0=None, nu=1):
+        """Sum-update linear attention with the z normaliser.  Returns (y, W_final, z_final)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, T, d_k = q.shape
+        d_v = v.shape[-1]
+        D = 2 * d_k * nu
+        assert k.shape == q.shape and v.shape == (B, H, T, d_v)
+        if W0 is not None:
+            W0 = _f64(W0)
+            assert W0.shape == (B, H, d_v, D)
+        if z0 is not None:
+            z0 = _f64(z0)
+            assert z0.shape == (B, H, D)
+        y = np.zeros((B, H, T, d_v), dtype=np.float64)
+        Wf = np.empty((B, H, d_v, D), dtype=np.float64)
+        zf = np.empty((B, H, D), dtype=np.float64)
+        self.lib.oracle_sum_forward(_p(q), _p(k), _p(v), _p(W0), _p(z0), _p(y), _p(Wf), _p(zf),
+                                    B, H, T, d_k, d_v, nu)
+        return y, Wf, zf
+
     def delta_step(self, q, k, v, beta_logit, W, nu=1):
         """One decode step. q,k [B,H,d_k], v [B,H,d_v], beta_logit [B,H], W [B,H,d_v,D].
         Returns (y [B,H,d_v], W_new); the W passed in is not modified."""
@@ -169,6 +190,10 @@ def delta_forward(q, k, v, beta_logit, W0=None, nu=1):
 
 def delta_step(q, k, v, beta_logit, W, nu=1):
     return default().delta_step(q, k, v, beta_logit, W, nu)
+
+
+def sum_forward(q, k, v, W0=None, z0=None, nu=1):
+    return default().sum_forward(q, k, v, W0, z0, nu)
 
 
 def delta_backward(q, k, v, beta_logit, W0, dy, dW_final=None, nu=1):

@@ -400,3 +400,57 @@ void oracle_delta_backward(const double* q, const double* k, const double* v,
         free(vbar); free(u); free(du); free(ytmp); free(work); free(dxw);
     }
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Sum-update linear attention with the z normaliser: [FWT] section "Background / fast
+ * computation form of linear self-attention".  Replacing the softmax kernel by
+ * phi(k)^T phi(q) turns causal attention into the recurrence
+ *   W_t = W_{t-1} + v_t phi(k_t)^T,   z_t = z_{t-1} + phi(k_t),   y_t = W_t phi(q_t) / (z_t . phi(q_t))
+ * with phi = DPFP.  Readings: W_0, z_0 are given or zero; where the denominator z_t . phi(q_t)
+ * is exactly 0 (phi(q_t) = 0, or no earlier key shares a feature with q_t) y_t is 0.
+ *   q, k [B, H, T, d_k]; v, y [B, H, T, d_v]; W0, W_final [B, H, d_v, D]; z0, z_final [B, H, D]
+ *   (W0, z0 may be NULL; W_final, z_final may be NULL: not written).
+ * ------------------------------------------------------------------------------------------ */
+void oracle_sum_forward(const double* q, const double* k, const double* v, const double* W0,
+                        const double* z0, double* y, double* W_final, double* z_final, int B,
+                        int H, int T, int d_k, int d_v, int nu)
+{
+    const int D = 2 * d_k * nu;
+    const int64_t BH = (int64_t)B * H;
+#pragma omp parallel
+    {
+        double* W = (double*)malloc(sizeof(double) * (size_t)d_v * D);
+        double* z = (double*)malloc(sizeof(double) * (size_t)D);
+        double* pk = (double*)malloc(sizeof(double) * (size_t)D);
+        double* pq = (double*)malloc(sizeof(double) * (size_t)D);
+        double* work = (double*)malloc(sizeof(double) * 2 * (size_t)d_k);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t s = 0; s < BH; ++s) {
+            if (W0) memcpy(W, W0 + (size_t)s * d_v * D, sizeof(double) * (size_t)d_v * D);
+            else memset(W, 0, sizeof(double) * (size_t)d_v * D);
+            if (z0) memcpy(z, z0 + s * D, sizeof(double) * (size_t)D);
+            else memset(z, 0, sizeof(double) * (size_t)D);
+            for (int t = 0; t < T; ++t) {
+                const int64_t row = s * T + t;
+                dpfp_one(k + (size_t)row * d_k, pk, d_k, nu, work);
+                dpfp_one(q + (size_t)row * d_k, pq, d_k, nu, work);
+                const double* vt = v + row * d_v;
+                /* write */
+                for (int r = 0; r < d_v; ++r)
+                    for (int d = 0; d < D; ++d) W[(size_t)r * D + d] += vt[r] * pk[d];
+                for (int d = 0; d < D; ++d) z[d] += pk[d];
+                /* read, normalised */
+                double den = 0.0;
+                for (int d = 0; d < D; ++d) den += z[d] * pq[d];
+                for (int r = 0; r < d_v; ++r) {
+                    double num = 0.0;
+                    for (int d = 0; d < D; ++d) num += W[(size_t)r * D + d] * pq[d];
+                    y[row * d_v + r] = den != 0.0 ? num / den : 0.0;
+                }
+            }
+            if (W_final) memcpy(W_final + s * d_v * D, W, sizeof(double) * (size_t)d_v * D);
+            if (z_final) memcpy(z_final + s * D, z, sizeof(double) * (size_t)D);
+        }
+        free(W); free(z); free(pk); free(pq); free(work);
+    }
+}

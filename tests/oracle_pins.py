@@ -485,4 +485,55 @@ def pin_backward_degenerate(O):
     np.testing.assert_array_equal(dW0, dWf)
 
 
+# ---------------------------------------------------------------- sum-update pins
+# [FWT] "Background / fast computation form of linear self-attention": with the kernel
+# phi(k)^T phi(q), causal attention sum_s v_s k(s, t) / sum_s k(s, t) becomes the W, z
+# recurrence.  These pins compute the attention form directly (a masked matmul).
+
+def pin_sum_update_is_normalised_masked_matmul(O):
+    """y_t = (W0 phi(q_t) + sum_{s<=t} v_s (phi(k_s).phi(q_t))) / (z0.phi(q_t) + sum_{s<=t}
+    phi(k_s).phi(q_t)); W_final = W0 + V^T Phi_K; z_final = z0 + Phi_K^T 1."""
+    rng = np.random.default_rng(51)
+    for (B, H, T, d_k, d_v, nu, carried) in [(1, 2, 40, 8, 5, 2, False), (2, 1, 33, 16, 4, 1, True)]:
+        q, k, v, _, W0 = _rand_case(rng, B, H, T, d_k, d_v, nu)
+        D = 2 * d_k * nu
+        z0 = rng.uniform(0.0, 0.5, size=(B, H, D)) if carried else None
+        if not carried:
+            W0 = None
+        y, Wf, zf = O.sum_forward(q, k, v, W0, z0, nu=nu)
+        Fq, Fk = O.dpfp(q, nu), O.dpfp(k, nu)
+        for b in range(B):
+            for h in range(H):
+                M = np.tril(Fq[b, h] @ Fk[b, h].T)
+                num = M @ v[b, h]
+                den = M @ np.ones(T)
+                if carried:
+                    num = num + Fq[b, h] @ W0[b, h].T
+                    den = den + Fq[b, h] @ z0[b, h]
+                np.testing.assert_allclose(y[b, h], num / den[:, None], rtol=1e-11, atol=1e-14)
+                W_exp = (0 if W0 is None else W0[b, h]) + v[b, h].T @ Fk[b, h]
+                z_exp = (0 if z0 is None else z0[b, h]) + Fk[b, h].sum(axis=0)
+                np.testing.assert_allclose(Wf[b, h], W_exp, rtol=1e-12, atol=1e-14)
+                np.testing.assert_allclose(zf[b, h], z_exp, rtol=1e-12, atol=1e-14)
+
+
+def pin_sum_update_convex_and_degenerate(O):
+    """From W0 = 0, z0 = 0 every output is a convex combination of the values so far (so a
+    constant value sequence comes back unchanged); a zero query reads 0 (zero denominator)."""
+    rng = np.random.default_rng(52)
+    q, k, v, _, _ = _rand_case(rng, 1, 1, 30, 8, 3, 2)
+    y, _, _ = O.sum_forward(q, k, v, nu=2)
+    lo = np.minimum.accumulate(v[0, 0], axis=0)
+    hi = np.maximum.accumulate(v[0, 0], axis=0)
+    assert np.all(y[0, 0] >= lo - 1e-12) and np.all(y[0, 0] <= hi + 1e-12)
+    c = rng.normal(size=3)
+    yc, _, _ = O.sum_forward(q, k, np.broadcast_to(c, v.shape).copy(), nu=2)
+    np.testing.assert_allclose(yc[0, 0], np.broadcast_to(c, (30, 3)), rtol=1e-12)
+    q2 = q.copy()
+    q2[0, 0, 7] = 0.0
+    y2, _, _ = O.sum_forward(q2, k, v, nu=2)
+    assert not y2[0, 0, 7].any()
+    np.testing.assert_array_equal(np.delete(y2[0, 0], 7, axis=0), np.delete(y[0, 0], 7, axis=0))
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -73,6 +73,20 @@ MUTANTS = {
     "bwd_checkpoint_stale": (
         "memcpy(ck + (size_t)(t / ORACLE_CHECKPOINT) * WS, W, sizeof(double) * WS);",
         "if (t == 0) memcpy(ck + (size_t)(t / ORACLE_CHECKPOINT) * WS, W, sizeof(double) * WS);"),
+    # sum-update linear attention
+    "sum_normaliser_dropped": ("y[row * d_v + r] = den != 0.0 ? num / den : 0.0;",
+                               "y[row * d_v + r] = num;"),
+    "sum_z_not_updated": ("for (int d = 0; d < D; ++d) z[d] += pk[d];",
+                          "for (int d = 0; d < D; ++d) z[d] += 0.0 * pk[d];"),
+    "sum_z_from_query": ("for (int d = 0; d < D; ++d) z[d] += pk[d];",
+                         "for (int d = 0; d < D; ++d) z[d] += pq[d];"),
+    "sum_denominator_with_key": ("for (int d = 0; d < D; ++d) den += z[d] * pq[d];",
+                                 "for (int d = 0; d < D; ++d) den += z[d] * pk[d];"),
+    "sum_value_outer_query": ("for (int d = 0; d < D; ++d) W[(size_t)r * D + d] += vt[r] * pk[d];",
+                              "for (int d = 0; d < D; ++d) W[(size_t)r * D + d] += vt[r] * pq[d];"),
+    "sum_initial_z_ignored": ("if (z0) memcpy(z, z0 + s * D", "if (0) memcpy(z, z0 + s * D"),
+    "sum_initial_state_ignored": ("if (W0) memcpy(W, W0 + (size_t)s * d_v * D",
+                                  "if (0) memcpy(W, W0 + (size_t)s * d_v * D"),
 }
 
 

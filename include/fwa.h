@@ -234,6 +234,32 @@ fwa_status fwa_delta_backward_info(int B, int H, int T, int d_k, int d_v, int nu
                                    fwa_dtype dtype, int64_t* workspace_bytes);
 
 /*
+ * fwa_sum_forward -- causal sum-update linear attention with the z normaliser over DPFP
+ * features, for every (b, h):
+ *     W_t = W_{t-1} + v_t phi(k_t)^T,  z_t = z_{t-1} + phi(k_t),  y_t = W_t phi(q_t) / (z_t . phi(q_t))
+ *   [FWT] section "Background / fast computation form of linear self-attention" (the form the
+ *   delta rule replaces: attention with the kernel phi(k)^T phi(q), computed recurrently).
+ *   Where the denominator z_t . phi(q_t) is exactly 0, y_t is 0.
+ *   q, k        [B, H, T, d_k]  `dtype`
+ *   v, y        [B, H, T, d_v]  `dtype` (y output)
+ *   W0          [B, H, d_v, D]  fp32 or NULL (zeros);  z0 [B, H, D] fp32 or NULL (zeros)
+ *   W_final     [B, H, d_v, D]  fp32 output or NULL;   z_final [B, H, D] fp32 output or NULL;
+ *                               W_final may equal W0 and z_final z0 (in-place carry)
+ *   workspace   caller-owned device scratch of at least the bytes fwa_sum_forward_info reports,
+ *               under fwa_delta_forward's rule
+ *   Arithmetic is fp32 (fp32 state), chunks of 32 rows.  T == 0 copies the initial state.
+ *   Implemented shapes: d_k in {16, 32, 64}, d_v <= 128, D = 2*d_k*nu <= 384.
+ */
+fwa_status fwa_sum_forward(const void* q, const void* k, const void* v, const float* W0,
+                           const float* z0, void* y, float* W_final, float* z_final, int B, int H,
+                           int T, int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                           int64_t workspace_bytes, hipStream_t stream);
+
+/* fwa_sum_forward_info -- workspace bytes fwa_sum_forward needs (0 when B*H == 0). */
+fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, fwa_dtype dtype,
+                                int64_t* workspace_bytes);
+
+/*
  * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory
  * carried in and out through W, updated in place.
  *   [FWT] sections "token_wise variant" and "Inference and sampling" (each new token updates

@@ -388,3 +388,41 @@ def test_backward_info_and_empty_batch():
     with pytest.raises(fwa.FwaError) as e:
         fwa.delta_backward_info(1, 1, 10, 64, 128, 1)
     assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ sum-update forward
+
+def _sum(**kw):
+    a = dict(q=FAKE, k=P(0x20000), v=P(0x30000), W0=None, z0=None, y=P(0x50000), Wf=None,
+             zf=None, B=1, H=1, T=8, d_k=16, d_v=16, nu=1, dtype=0, ws=P(0x1000000),
+             ws_bytes=1 << 24)
+    a.update(kw)
+    return fwa.lib().fwa_sum_forward(a["q"], a["k"], a["v"], a["W0"], a["z0"], a["y"], a["Wf"],
+                                     a["zf"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["nu"],
+                                     a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(v=None), 1, "NULL"),
+    (dict(H=-2), 1, "negative"),
+    (dict(nu=32), 1, "nu"),
+    (dict(y=MISALIGNED), 1, "aligned"),
+    (dict(ws=None), 1, "workspace of"),
+    (dict(y=P(0x30000)), 1, "output overlaps an input"),
+    (dict(W0=P(0x60000), Wf=P(0x60010)), 1, "output overlaps an input"),
+    (dict(zf=P(0x50000)), 1, "two outputs overlap"),
+    (dict(d_k=8), 2, "d_k"),
+    (dict(d_v=129), 2, "d_v"),
+    (dict(d_k=64, nu=4), 2, "384"),
+])
+def test_sum_forward_rejects(kw, status, msg):
+    assert _sum(**kw) == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+def test_sum_forward_info_and_empty_batch():
+    import torch
+    assert _sum(B=0, q=None, y=None) == 0
+    D, d_v, nc = 256, 64, 4096 // 32
+    per_chunk = 2 * 32 * D + 32 * d_v + 32 + D
+    assert fwa.sum_forward_info(4, 8, 4096, 64, d_v, 2, torch.bfloat16) == 4 * 8 * nc * per_chunk * 4

@@ -25,14 +25,12 @@
 //   4. bwd_chunk_grads  per chunk: dK, dQ (over 2, 3), dv, dbeta_logit           (parallel)
 //   5. bwd_dpfp         per vector: dk, dq                                      (parallel)
 // Arithmetic is fp32 on the vector ALU; chunk C = 32.
-#include "fwa_common.h"
+#include "chunk_f32.h"
 #include "fwa_internal.h"
 
 namespace fwa {
 
-constexpr int kBC = 32;              // rows per chunk
 constexpr int kPrepThreads2 = 256;
-constexpr int kRowWaves = 8;         // memory rows per serial workgroup (one wave each)
 
 // Workspace regions (fp32), each indexed by the chunk u = bh * NC + n.
 struct BwdLayout {
@@ -100,23 +98,14 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     float* Pm = Gm + kBC * CS;
     float* Ai = Pm + kBC * CS;
     float* be = Ai + kBC * CS;               // [C]
-    float* rs = be + kBC;                    // [2C]: row sum + eps of K, then of Q
+    float* rs = be + kBC;                    // [2C]: DPFP row sums + eps (K, then Q)
     float* Vs = rs + 2 * kBC;                // [C][d_v]
 
-    // raw rows (zero past the sequence end), beta (zero past the end), v
-    for (int i = tid; i < kBC * d_k; i += kPrepThreads2) {
-        const int c = i / d_k, j = i % d_k;
-        float kv = 0.0f, qv = 0.0f;
-        if (t0 + c < a.T) {
-            const int64_t g = (int64_t(bh) * a.T + t0 + c) * d_k + j;
-            kv = load_elem<BF16>(a.k, g);
-            qv = load_elem<BF16>(a.q, g);
-        }
-        xk[c * two + j] = relu(kv);
-        xk[c * two + d_k + j] = relu(-kv);
-        xq[c * two + j] = relu(qv);
-        xq[c * two + d_k + j] = relu(-qv);
-    }
+    // relu'd raw rows (zero past the sequence end), beta (zero past the end), v
+    load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, a.T - t0 < kBC ? a.T - t0 : kBC, t0, d_k,
+                         tid, kPrepThreads2);
+    load_relu_rows<BF16>(a.q, xq, int64_t(bh) * a.T, a.T - t0 < kBC ? a.T - t0 : kBC, t0, d_k,
+                         tid, kPrepThreads2);
     for (int c = tid; c < kBC; c += kPrepThreads2)
         be[c] = t0 + c < a.T ? sigmoid_stable(load_elem<BF16>(a.bl, int64_t(bh) * a.T + t0 + c)) : 0.0f;
     for (int i = tid; i < kBC * d_v; i += kPrepThreads2) {
@@ -124,35 +113,14 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
         Vs[i] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
     }
     __syncthreads();
-    // raw DPFP products: block i - 1 holds x[j] x[(j - i) mod 2 d_k]
-    for (int e = tid; e < kBC * D; e += kPrepThreads2) {
-        const int c = e / D, p = e % D;
-        const int i = p / two + 1, j = p % two;
-        int src = j - i;
-        src += (src < 0) ? two : 0;
-        Kt[e] = xk[c * two + j] * xk[c * two + src];
-        Qt[e] = xq[c * two + j] * xq[c * two + src];
-    }
-    __syncthreads();
-    if (tid < 2 * kBC) {
-        const float* row = (tid < kBC ? Kt : Qt) + (tid % kBC) * D;
-        float s = 0.0f;
-        for (int p = 0; p < D; ++p) s += row[p];
-        rs[tid] = s + kDpfpEps;
-    }
-    __syncthreads();
+    dpfp_tiles(xk, xq, Kt, Qt, rs, D, d_k, tid, kPrepThreads2);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
     for (int e = tid; e < kBC * D; e += kPrepThreads2) {
-        const int c = e / D;
-        const float kv = Kt[e] / rs[c], qv = Qt[e] / rs[kBC + c];
-        Kt[e] = kv;
-        Qt[e] = qv;
-        gK[e] = kv;
-        gQ[e] = qv;
+        gK[e] = Kt[e];
+        gQ[e] = Qt[e];
     }
-    __syncthreads();
     // G = K K^T and P = lower_incl(Q K^T): thread -> (row c, 4 columns j0..j0+3)
     {
         const int c = tid / 8, j0 = (tid % 8) * 4;
@@ -238,35 +206,6 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------ row chains
-
-// Reduce-scatter of 32 per-lane partial sums over the wave: on return, lane l holds the sum
-// over all 64 lanes of entry l >> 1.
-__device__ __forceinline__ float wave_reduce_scatter32(float (&v)[kBC]) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int half = 16, mask = 32; half >= 1; half >>= 1, mask >>= 1) {
-        const bool up = (lane & mask) != 0;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float send = up ? v[i] : v[i + half];
-            const float keep = up ? v[i + half] : v[i];
-            v[i] = keep + __shfl_xor(send, mask);
-        }
-    }
-    return v[0] + __shfl_xor(v[0], 1);
-}
-
-// Value of `x` held by lane `l` (a wave-uniform index), in every lane.
-__device__ __forceinline__ float lane_value(float x, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
-}
-
-// Stages `n` floats (a multiple of 4, both pointers 16-byte aligned) from global to LDS with
-// all threads of the workgroup.
-__device__ __forceinline__ void stage(float* dst, const float* src, int n, int tid, int nthr) {
-    for (int i = 4 * tid; i < n; i += 4 * nthr)
-        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
-}
 
 // Chunk-start memories and U: row r of the memory moves as w <- w + K^T u with
 // u = Uy[:, r] - Wy w.  Lane l holds w[l + 64 m], m < NPL.

@@ -476,6 +476,90 @@ fwa_status fwa_delta_backward(const void* q, const void* k, const void* v,
                       "fwa_delta_backward launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+fwa_status check_sum_shape(const char* fn, int B, int H, int T, int d_k, int d_v, int nu,
+                           fwa_dtype dtype, int64_t* ws_bytes) {
+    if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (B < 0 || H < 0 || T < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H/T", fn);
+    if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
+    if (nu < 1 || nu > 2 * d_k - 1)
+        return fail(FWA_ERR_INVALID_ARG, "%s: nu=%d outside [1, 2*d_k-1]", fn, nu);
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    *ws_bytes = 0;
+    if (BH == 0) return ok();
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
+    if (d_k != 16 && d_k != 32 && d_k != 64)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: d_k=%d not in {16,32,64}", fn, d_k);
+    if (d_v > 128) return fail(FWA_ERR_UNSUPPORTED, "%s: d_v=%d > 128", fn, d_v);
+    if (D > 384) return fail(FWA_ERR_UNSUPPORTED, "%s: D=2*d_k*nu=%lld > 384", fn, (long long)D);
+    if (!mul_le(kIndexLimit / 64, {BH, static_cast<int64_t>(T) + 64, D}) ||
+        !mul_le(kIndexLimit / 64, {BH, static_cast<int64_t>(T) + 64, d_v}) ||
+        BH > (int64_t(1) << 26) || static_cast<int64_t>(T) * d_v >= (int64_t(1) << 31))
+        return fail(FWA_ERR_UNSUPPORTED, "%s: sizes overflow the index range", fn);
+    if (!fwa::plan_sum_forward(static_cast<int>(BH), T, d_k, d_v, nu, ws_bytes))
+        return fail(FWA_ERR_UNSUPPORTED, "%s: no plan for these sizes", fn);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, fwa_dtype dtype,
+                                int64_t* workspace_bytes) {
+    int64_t ws = 0;
+    const fwa_status st = check_sum_shape("fwa_sum_forward_info", B, H, T, d_k, d_v, nu, dtype, &ws);
+    if (st != FWA_OK) return st;
+    if (workspace_bytes) *workspace_bytes = ws;
+    return ok();
+}
+
+fwa_status fwa_sum_forward(const void* q, const void* k, const void* v, const float* W0,
+                           const float* z0, void* y, float* W_final, float* z_final, int B, int H,
+                           int T, int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                           int64_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "fwa_sum_forward";
+    int64_t need = 0;
+    fwa_status st = check_sum_shape(fn, B, H, T, d_k, d_v, nu, dtype, &need);
+    if (st != FWA_OK) return st;
+    const int64_t BH = static_cast<int64_t>(B) * H;
+    if (BH == 0) return ok();
+    if (T > 0 && (!q || !k || !v || !y))
+        return fail(FWA_ERR_INVALID_ARG, "%s: NULL input or output pointer", fn);
+    if (workspace_bytes < 0) return fail(FWA_ERR_INVALID_ARG, "%s: workspace_bytes < 0", fn);
+    const void* ptrs[] = {q, k, v, W0, z0, y, W_final, z_final, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p))
+            return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(FWA_ERR_INVALID_ARG, "%s: needs a workspace of %lld bytes (got %lld%s)", fn,
+                    (long long)need, (long long)workspace_bytes, workspace ? "" : ", NULL");
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
+    const int es = elem_bytes(dtype);
+    const int64_t nqk = T ? BH * T * d_k * es : 0, nv = T ? BH * T * d_v * es : 0;
+    const int64_t nW = BH * d_v * D * 4, nz = BH * D * 4;
+    const Span in[] = {span(q, nqk), span(k, nqk), span(v, nv), span(W0, W0 ? nW : 0),
+                       span(z0, z0 ? nz : 0)};
+    const Span out[] = {span(y, nv), span(W_final, W_final ? nW : 0),
+                        span(z_final, z_final ? nz : 0), span(workspace, need)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j) {
+            // in-place carry: W_final may be W0 and z_final z0 (exactly)
+            if ((i == 1 && j == 3 && W_final == W0) || (i == 2 && j == 4 && z_final == z0)) continue;
+            if (overlap(out[i], in[j])) return fail(FWA_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out[j])) return fail(FWA_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+    }
+    return hip_status(fwa::launch_sum_forward(q, k, v, W0, z0, y, W_final, z_final,
+                                              static_cast<int>(BH), T, d_k, d_v, nu,
+                                              dtype == FWA_BF16, workspace, stream),
+                      "fwa_sum_forward launch");
+}
+
 fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,
                           float* W, void* y, int B, int H, int d_k, int d_v, int nu,
                           fwa_dtype dtype, hipStream_t stream) {

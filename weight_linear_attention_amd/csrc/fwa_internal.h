@@ -123,4 +123,11 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
                            void* dv, void* dbl, float* dW0, int BH, int T, int d_k, int d_v,
                            int nu, bool bf16, void* workspace, hipStream_t stream);
 
+// Sum-update linear attention with the z normaliser (sum_forward.hip).
+bool plan_sum_forward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes);
+hipError_t launch_sum_forward(const void* q, const void* k, const void* v, const float* W0,
+                              const float* z0, void* y, float* Wf, float* zf, int BH, int T,
+                              int d_k, int d_v, int nu, bool bf16, void* workspace,
+                              hipStream_t stream);
+
 }  // namespace fwa

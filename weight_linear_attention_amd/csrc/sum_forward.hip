@@ -1,0 +1,260 @@
+// Sum-update linear attention with the z normaliser ("Fast Weights Transformer" guide,
+// xdnf.cn/news/308600, section "Background / fast computation form of linear self-attention"):
+//   W_t = W_{t-1} + v_t phi(k_t)^T,  z_t = z_{t-1} + phi(k_t),  y_t = W_t phi(q_t) / (z_t . phi(q_t))
+// with phi = DPFP, and y_t = 0 where the denominator is exactly 0.
+//
+// For a chunk of C rows with normalised features K, Q (C x D) starting from W0, z0, and
+// M = lower_incl(Q K^T):
+//   Y = (Q W0^T + M V) / (Q z0 + M 1)   (row-wise),   W1 = W0 + V^T K,   z1 = z0 + K^T 1.
+// Three launches:
+//   1. sum_prep  per chunk: K, Q, and the chunk-local parts M V and M 1            (parallel)
+//   2. sum_scan  per (b, h, 8 rows of W), chunks in order: row r of W moves on its own
+//      (w <- w + K^T V[:, r]); each wave also carries z (the same for every row), so it forms
+//      y[:, r] itself                                                                (serial)
+//   3. sum_zfinal per (b, h): z_final from z0 and the chunks' key sums (where it is asked for)
+// Arithmetic is fp32 on the vector ALU; chunks of 32 rows.
+#include "chunk_f32.h"
+#include "fwa_internal.h"
+
+namespace fwa {
+
+constexpr int kSumThreads = 256;
+
+struct SumLayout {
+    int64_t kt, qt, nm, dn, ks, end;   // K, Q [C][D]; M V [C][d_v]; M 1 [C]; K^T 1 [D] (per chunk)
+};
+
+static SumLayout sum_layout(int64_t NU, int D, int d_v) {
+    SumLayout L;
+    int64_t o = 0;
+    L.kt = o; o += NU * kBC * D;
+    L.qt = o; o += NU * kBC * D;
+    L.nm = o; o += NU * kBC * d_v;
+    L.dn = o; o += NU * kBC;
+    L.ks = o; o += NU * D;
+    L.end = o;
+    return L;
+}
+
+struct SumArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* W0;
+    const float* z0;
+    void* y;
+    float* Wf;
+    float* zf;
+    float* ws;
+    int BH, T, NC, d_k, d_v, nu, D;
+    SumLayout L;
+};
+
+// LDS: x rows of k and q (C x 2 d_k each), K and Q (C x D), M (C x (C + 1)), row sums, V.
+template <bool BF16>
+__global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
+    extern __shared__ float lds[];
+    const int D = a.D, d_k = a.d_k, d_v = a.d_v, two = 2 * d_k;
+    const int u = blockIdx.x;
+    const int bh = u / a.NC, n = u % a.NC;
+    const int t0 = n * kBC;
+    const int tid = threadIdx.x;
+    const int rows = a.T - t0 < kBC ? a.T - t0 : kBC;
+    constexpr int CS = kBC + 1;
+    float* xk = lds;
+    float* xq = xk + kBC * two;
+    float* Kt = xq + kBC * two;
+    float* Qt = Kt + kBC * D;
+    float* Mm = Qt + kBC * D;
+    float* rs = Mm + kBC * CS;
+    float* Vs = rs + 2 * kBC;
+    load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
+    load_relu_rows<BF16>(a.q, xq, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
+    for (int i = tid; i < kBC * d_v; i += kSumThreads) {
+        const int c = i / d_v, r = i % d_v;
+        Vs[i] = c < rows ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
+    }
+    dpfp_tiles(xk, xq, Kt, Qt, rs, D, d_k, tid, kSumThreads);
+    const int64_t CD = int64_t(kBC) * D;
+    float* gK = a.ws + a.L.kt + int64_t(u) * CD;
+    float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
+    for (int e = tid; e < kBC * D; e += kSumThreads) {
+        gK[e] = Kt[e];
+        gQ[e] = Qt[e];
+    }
+    // M = lower_incl(Q K^T): thread -> (row c, columns j0..j0+3)
+    {
+        const int c = tid / 8, j0 = (tid % 8) * 4;
+        float m[4] = {0, 0, 0, 0};
+        for (int p = 0; p < D; ++p) {
+            const float qc = Qt[c * D + p];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] += qc * Kt[(j0 + e) * D + p];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Mm[c * CS + j0 + e] = (j0 + e <= c) ? m[e] : 0.0f;
+    }
+    __syncthreads();
+    float* gN = a.ws + a.L.nm + int64_t(u) * kBC * d_v;
+    for (int e = tid; e < kBC * d_v; e += kSumThreads) {
+        const int c = e / d_v, r = e % d_v;
+        float s = 0.0f;
+        for (int j = 0; j <= c; ++j) s += Mm[c * CS + j] * Vs[j * d_v + r];
+        gN[e] = s;
+    }
+    if (tid < kBC) {
+        float s = 0.0f;
+        for (int j = 0; j <= tid; ++j) s += Mm[tid * CS + j];
+        a.ws[a.L.dn + int64_t(u) * kBC + tid] = s;
+    }
+    for (int p = tid; p < D; p += kSumThreads) {
+        float s = 0.0f;
+        for (int c = 0; c < kBC; ++c) s += Kt[c * D + p];
+        a.ws[a.L.ks + int64_t(u) * D + p] = s;
+    }
+}
+
+// z_final = z0 + the chunks' column sums of K, one thread per entry (each reads its z0 entry
+// before writing its z_final entry, so z_final may be z0).
+__global__ __launch_bounds__(256) void sum_zfinal_kernel(SumArgs a) {
+    const int bh = blockIdx.x;
+    for (int p = threadIdx.x; p < a.D; p += 256) {
+        float z = a.z0 ? a.z0[int64_t(bh) * a.D + p] : 0.0f;
+        for (int n = 0; n < a.NC; ++n) z += a.ws[a.L.ks + (int64_t(bh) * a.NC + n) * a.D + p];
+        a.zf[int64_t(bh) * a.D + p] = z;
+    }
+}
+
+// Lane l holds w[l + 64 m] (row r of W) and zz[l + 64 m] (z), m < NPL.
+template <bool BF16, int NPL>
+__global__ __launch_bounds__(64 * kRowWaves) void sum_scan_kernel(SumArgs a) {
+    extern __shared__ float lds[];
+    const int D = a.D, d_v = a.d_v;
+    const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
+    const int bh = blockIdx.x / rgroups;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
+    const bool live = r < d_v;
+    float* Kt = lds;
+    float* Qt = Kt + kBC * D;
+    float w[NPL], zz[NPL];
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) {
+        const int p = lane + 64 * m;
+        w[m] = (live && a.W0 && p < D) ? a.W0[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
+        zz[m] = (a.z0 && p < D) ? a.z0[int64_t(bh) * D + p] : 0.0f;
+    }
+    const int64_t CD = int64_t(kBC) * D;
+    for (int n = 0; n < a.NC; ++n) {
+        const int64_t u = int64_t(bh) * a.NC + n;
+        const int t0 = n * kBC;
+        float vc = 0.0f;
+        if (live && lane < kBC && t0 + lane < a.T)
+            vc = load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + lane) * d_v + r);
+        __syncthreads();
+        stage(Kt, a.ws + a.L.kt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        stage(Qt, a.ws + a.L.qt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
+        __syncthreads();
+        float pn[kBC], pd[kBC];
+#pragma unroll
+        for (int c = 0; c < kBC; ++c) {
+            float sn = 0.0f, sd = 0.0f;
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) {
+                    const float qv = Qt[c * D + lane + 64 * m];
+                    sn += qv * w[m];
+                    sd += qv * zz[m];
+                }
+            pn[c] = sn;
+            pd[c] = sd;
+        }
+        const float qw = wave_reduce_scatter32(pn);           // (Q w)[lane >> 1]
+        const float qz = wave_reduce_scatter32(pd);           // (Q z)[lane >> 1]
+        const int c = lane >> 1;
+        if (live && (lane & 1) == 0 && t0 + c < a.T) {
+            const float num = qw + a.ws[a.L.nm + (u * kBC + c) * d_v + r];
+            const float den = qz + a.ws[a.L.dn + u * kBC + c];
+            store_elem<BF16>(a.y, (int64_t(bh) * a.T + t0 + c) * d_v + r, den != 0.0f ? num / den : 0.0f);
+        }
+#pragma unroll
+        for (int cc = 0; cc < kBC; ++cc) {
+            const float vv = lane_value(vc, cc);
+#pragma unroll
+            for (int m = 0; m < NPL; ++m)
+                if (lane + 64 * m < D) {
+                    const float kv = Kt[cc * D + lane + 64 * m];
+                    w[m] += vv * kv;
+                    zz[m] += kv;
+                }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) {
+        const int p = lane + 64 * m;
+        if (p >= D) continue;
+        if (live && a.Wf) a.Wf[(int64_t(bh) * d_v + r) * D + p] = w[m];
+    }
+}
+
+bool plan_sum_forward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
+    const int D = 2 * d_k * nu;
+    if (d_k != 16 && d_k != 32 && d_k != 64) return false;
+    if (d_v < 1 || d_v > 128 || D > 384) return false;
+    const int NC = (T + kBC - 1) / kBC;
+    *ws_bytes = sum_layout(int64_t(BH) * NC, D, d_v).end * 4;
+    return true;
+}
+
+template <int NPL, bool BF16>
+static hipError_t launch_scan(const SumArgs& a, hipStream_t stream) {
+    const int rgroups = (a.d_v + kRowWaves - 1) / kRowWaves;
+    auto kern = sum_scan_kernel<BF16, NPL>;
+    const int lds = 4 * 2 * kBC * a.D;
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(int64_t(a.BH) * rgroups)),
+                       dim3(64 * kRowWaves), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_sum_t(const SumArgs& a, hipStream_t stream) {
+    const int64_t NU = int64_t(a.BH) * a.NC;
+    hipError_t e;
+    if (NU > 0) {
+        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * a.D + kBC * (kBC + 1) + 2 * kBC +
+                            kBC * a.d_v);
+        auto kp = sum_prep_kernel<BF16>;
+        if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kp), lp)) != hipSuccess) return e;
+        hipLaunchKernelGGL(kp, dim3(static_cast<unsigned>(NU)), dim3(kSumThreads), lp, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    switch ((a.D + 63) / 64) {
+        case 1: e = launch_scan<1, BF16>(a, stream); break;
+        case 2: e = launch_scan<2, BF16>(a, stream); break;
+        case 3: e = launch_scan<3, BF16>(a, stream); break;
+        case 4: e = launch_scan<4, BF16>(a, stream); break;
+        case 5: e = launch_scan<5, BF16>(a, stream); break;
+        case 6: e = launch_scan<6, BF16>(a, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || !a.zf) return e;
+    hipLaunchKernelGGL(sum_zfinal_kernel, dim3(static_cast<unsigned>(a.BH)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_forward(const void* q, const void* k, const void* v, const float* W0,
+                              const float* z0, void* y, float* Wf, float* zf, int BH, int T,
+                              int d_k, int d_v, int nu, bool bf16, void* workspace,
+                              hipStream_t stream) {
+    SumArgs a;
+    a.q = q; a.k = k; a.v = v; a.W0 = W0; a.z0 = z0; a.y = y; a.Wf = Wf; a.zf = zf;
+    a.ws = static_cast<float*>(workspace);
+    a.BH = BH; a.T = T; a.NC = (T + kBC - 1) / kBC; a.d_k = d_k; a.d_v = d_v; a.nu = nu;
+    a.D = 2 * d_k * nu;
+    a.L = sum_layout(int64_t(BH) * a.NC, a.D, d_v);
+    return bf16 ? launch_sum_t<true>(a, stream) : launch_sum_t<false>(a, stream);
+}
+
+}  // namespace fwa

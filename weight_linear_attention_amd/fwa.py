@@ -16,6 +16,7 @@ Functions (same names as the C entry points, minus the prefix):
                                                       workspace bytes)
     delta_backward(q, k, v, beta_logit, dy, W0=None, dW_final=None, nu=1)
                                                   -> (dq, dk, dv, dbeta_logit, dW0)
+    sum_forward(q, k, v, W0=None, z0=None, nu=1)  -> (y, W_final, z_final)
 
 Shapes are checked before anything else, so a wrong shape raises ValueError without touching
 the device.  The forward's workspace is allocated here with torch on the current stream (the
@@ -39,7 +40,8 @@ PATH_NAMES = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED
 
 EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_path", "fwa_delta_forward_info",
             "fwa_delta_forward_noalloc", "fwa_delta_backward", "fwa_delta_backward_info",
-            "fwa_delta_step", "fwa_status_string", "fwa_last_error", "fwa_version")
+            "fwa_sum_forward", "fwa_sum_forward_info", "fwa_delta_step", "fwa_status_string",
+            "fwa_last_error", "fwa_version")
 
 
 class FwaError(RuntimeError):
@@ -76,6 +78,10 @@ def lib():
     L.fwa_delta_backward.restype = i32
     L.fwa_delta_backward_info.argtypes = [i32] * 7 + [ctypes.POINTER(i64)]
     L.fwa_delta_backward_info.restype = i32
+    L.fwa_sum_forward.argtypes = [P] * 8 + [i32] * 6 + [i32, P, i64, P]
+    L.fwa_sum_forward.restype = i32
+    L.fwa_sum_forward_info.argtypes = [i32] * 7 + [ctypes.POINTER(i64)]
+    L.fwa_sum_forward_info.restype = i32
     L.fwa_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5 + [i32, P]
     L.fwa_delta_step.restype = i32
     L.fwa_status_string.argtypes = [i32]
@@ -240,6 +246,56 @@ def delta_backward(q, k, v, beta_logit, dy, W0=None, dW_final=None, nu=1, need_d
                                     _dtype_code(q.dtype), _ptr(workspace), ws_bytes,
                                     _stream(dev)))
     return dq, dk, dv, dl, dW0
+
+
+def sum_forward_info(B, H, T, d_k, d_v, nu=1, dtype=torch.float32):
+    """Bytes of workspace sum_forward needs for these sizes."""
+    ws = ctypes.c_int64(0)
+    _check(lib().fwa_sum_forward_info(B, H, T, d_k, d_v, nu, _dtype_code(dtype), ctypes.byref(ws)))
+    return ws.value
+
+
+def sum_forward(q, k, v, W0=None, z0=None, nu=1, out=None, W_final=None, z_final=None,
+                return_final=True, workspace=None):
+    """Sum-update linear attention with the z normaliser.  Returns (y, W_final, z_final)."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, H, T, d_k] and v [B, H, T, d_v]")
+    B, H, T, d_k = q.shape
+    d_v = v.shape[-1]
+    D = 2 * d_k * nu
+    _shape(k, "k", q.shape)
+    _shape(v, "v", (B, H, T, d_v))
+    _shape(W0, "W0", (B, H, d_v, D))
+    _shape(z0, "z0", (B, H, D))
+    _shape(out, "out", (B, H, T, d_v))
+    _shape(W_final, "W_final", (B, H, d_v, D))
+    _shape(z_final, "z_final", (B, H, D))
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dev, q.dtype)
+    for t, n in ((W0, "W0"), (z0, "z0")):
+        if t is not None:
+            _need(t, n, dev, torch.float32)
+    if out is None:
+        out = torch.empty(B, H, T, d_v, dtype=q.dtype, device=dev)
+    _need(out, "out", dev, q.dtype)
+    if return_final and W_final is None:
+        W_final = torch.empty(B, H, d_v, D, dtype=torch.float32, device=dev)
+    if return_final and z_final is None:
+        z_final = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+    for t, n in ((W_final, "W_final"), (z_final, "z_final")):
+        if t is not None:
+            _need(t, n, dev, torch.float32)
+    if workspace is None:
+        nbytes = sum_forward_info(B, H, T, d_k, d_v, nu, q.dtype)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    else:
+        _need(workspace, "workspace", dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().fwa_sum_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(W0), _ptr(z0), _ptr(out),
+                                 _ptr(W_final), _ptr(z_final), B, H, T, d_k, d_v, nu,
+                                 _dtype_code(q.dtype), _ptr(workspace), ws_bytes, _stream(dev)))
+    return out, W_final, z_final
 
 
 def check_step_shapes(q, k, v, beta_logit, W, nu=1, out=None):

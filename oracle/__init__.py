@@ -5,7 +5,8 @@ CPU-baseline leg may import this package.  It shares no code with the HIP librar
 imports it.
 
 `dpfp`, `dpfp_mask`, `delta_forward`, `delta_step`, `delta_backward` (the gradient of
-`delta_forward`) and `sum_forward` (sum-update linear attention with the z normaliser) wrap the plain-C fp64 implementation in
+`delta_forward`), `sum_forward` (sum-update linear attention with the z normaliser),
+`layer_project` and `layer_output` (the linear maps around the layer) wrap the plain-C fp64 implementation in
 fwa_oracle.c (built by oracle/build.py); `twin` holds an independent NumPy transcription used to
 cross-check it.  All arrays are float64, C-contiguous, in the [B, H, T, d] layout; W is
 [B, H, d_v, D] with D = 2 * d_k * nu.  Inputs given in fp32 or bf16 are taken exactly (bf16 and
@@ -40,6 +41,8 @@ class Oracle:
         L.oracle_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5
         L.oracle_delta_backward.argtypes = [P] * 12 + [i32] * 6
         L.oracle_sum_forward.argtypes = [P] * 8 + [i32] * 6
+        L.oracle_layer_project.argtypes = [P] * 6 + [i32] * 6
+        L.oracle_layer_output.argtypes = [P] * 5 + [i32] * 5
         L.oracle_sigmoid.argtypes = [ctypes.c_double]
         L.oracle_sigmoid.restype = ctypes.c_double
         L.oracle_num_threads.restype = ctypes.c_int
@@ -136,6 +139,33 @@ class Oracle:
                                     B, H, T, d_k, d_v, nu)
         return y, Wf, zf
 
+    def layer_project(self, x, Wqkvb, H, d_k, d_v):
+        """x [B, T, d_model] through the stacked bias-free projections Wqkvb
+        [2*H*d_k + H*d_v + H, d_model].  Returns (q, k, v, beta_logit) in [B, H, T, .]."""
+        x, Wqkvb = _f64(x), _f64(Wqkvb)
+        B, T, d_model = x.shape
+        assert Wqkvb.shape == (2 * H * d_k + H * d_v + H, d_model)
+        q = np.empty((B, H, T, d_k))
+        k = np.empty((B, H, T, d_k))
+        v = np.empty((B, H, T, d_v))
+        bl = np.empty((B, H, T))
+        self.lib.oracle_layer_project(_p(x), _p(Wqkvb), _p(q), _p(k), _p(v), _p(bl), B, T,
+                                      d_model, H, d_k, d_v)
+        return q, k, v, bl
+
+    def layer_output(self, y, Wo, bo=None, residual=None):
+        """residual + bo + concat_heads(y) Wo^T for y [B, H, T, d_v], Wo [d_model, H*d_v]."""
+        y, Wo = _f64(y), _f64(Wo)
+        B, H, T, d_v = y.shape
+        d_model = Wo.shape[0]
+        assert Wo.shape == (d_model, H * d_v)
+        bo = None if bo is None else _f64(bo)
+        residual = None if residual is None else _f64(residual)
+        out = np.empty((B, T, d_model))
+        self.lib.oracle_layer_output(_p(y), _p(Wo), _p(bo), _p(residual), _p(out), B, T, H, d_v,
+                                     d_model)
+        return out
+
     def delta_step(self, q, k, v, beta_logit, W, nu=1):
         """One decode step. q,k [B,H,d_k], v [B,H,d_v], beta_logit [B,H], W [B,H,d_v,D].
         Returns (y [B,H,d_v], W_new); the W passed in is not modified."""
@@ -190,6 +220,14 @@ def delta_forward(q, k, v, beta_logit, W0=None, nu=1):
 
 def delta_step(q, k, v, beta_logit, W, nu=1):
     return default().delta_step(q, k, v, beta_logit, W, nu)
+
+
+def layer_project(x, Wqkvb, H, d_k, d_v):
+    return default().layer_project(x, Wqkvb, H, d_k, d_v)
+
+
+def layer_output(y, Wo, bo=None, residual=None):
+    return default().layer_output(y, Wo, bo, residual)
 
 
 def sum_forward(q, k, v, W0=None, z0=None, nu=1):

@@ -454,3 +454,64 @@ void oracle_sum_forward(const double* q, const double* k, const double* v, const
         free(W); free(z); free(pk); free(pq); free(work);
     }
 }
+
+/* ------------------------------------------------------------------------------------------
+ * The projections around the layer: [FWT] section "FastWeightsAttention / module structure
+ * and source walkthrough".  The query, key and value maps are bias-free linear maps from
+ * d_model to heads * d (then split by head), the interpolation weight is a bias-free linear map
+ * to one scalar per head (squashed by the sigmoid inside the layer), and the output is a linear
+ * map (with bias) of the heads' concatenated outputs back to d_model; the Transformer layer
+ * adds it to its input (the attention residual).
+ *   x     [B, T, d_model]
+ *   Wqkvb [3 rows blocks + 1]: rows 0 .. H*d_k - 1 query, H*d_k .. 2*H*d_k - 1 key,
+ *         then H*d_v value rows, then H beta rows; each row has d_model entries (out = x W^T)
+ *   q, k  [B, H, T, d_k]; v [B, H, T, d_v]; beta_logit [B, H, T]
+ * ------------------------------------------------------------------------------------------ */
+void oracle_layer_project(const double* x, const double* Wqkvb, double* q, double* k, double* v,
+                          double* beta_logit, int B, int T, int d_model, int H, int d_k, int d_v)
+{
+    const int nq = H * d_k, nv = H * d_v;
+    const int N = 2 * nq + nv + H;
+#pragma omp parallel for schedule(static)
+    for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+        const int64_t b = bt / T, t = bt % T;
+        const double* xr = x + bt * d_model;
+        for (int n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int c = 0; c < d_model; ++c) s += xr[c] * Wqkvb[(int64_t)n * d_model + c];
+            if (n < nq) {
+                q[((b * H + n / d_k) * T + t) * d_k + n % d_k] = s;
+            } else if (n < 2 * nq) {
+                const int m = n - nq;
+                k[((b * H + m / d_k) * T + t) * d_k + m % d_k] = s;
+            } else if (n < 2 * nq + nv) {
+                const int m = n - 2 * nq;
+                v[((b * H + m / d_v) * T + t) * d_v + m % d_v] = s;
+            } else {
+                const int h = n - 2 * nq - nv;
+                beta_logit[(b * H + h) * T + t] = s;
+            }
+        }
+    }
+}
+
+/* out[b, t, :] = residual[b, t, :] + bo + Wo concat_h(y[b, h, t, :]) with Wo [d_model, H*d_v]
+ * (bo, residual may be NULL: zero). */
+void oracle_layer_output(const double* y, const double* Wo, const double* bo,
+                         const double* residual, double* out, int B, int T, int H, int d_v,
+                         int d_model)
+{
+    const int Kc = H * d_v;
+#pragma omp parallel for schedule(static)
+    for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+        const int64_t b = bt / T, t = bt % T;
+        for (int n = 0; n < d_model; ++n) {
+            double s = 0.0;
+            for (int kk = 0; kk < Kc; ++kk)
+                s += y[((b * H + kk / d_v) * T + t) * d_v + kk % d_v] * Wo[(int64_t)n * Kc + kk];
+            if (bo) s += bo[n];
+            if (residual) s += residual[bt * d_model + n];
+            out[bt * d_model + n] = s;
+        }
+    }
+}

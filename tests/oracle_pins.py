@@ -536,4 +536,34 @@ def pin_sum_update_convex_and_degenerate(O):
     np.testing.assert_array_equal(np.delete(y2[0, 0], 7, axis=0), np.delete(y[0, 0], 7, axis=0))
 
 
+# ---------------------------------------------------------------- projection pins
+# [FWT] "FastWeightsAttention / module structure and source walkthrough": bias-free linear maps
+# to heads * d (split by head) and to one beta logit per head; an output linear map with bias.
+
+def pin_layer_projections_are_matmuls(O):
+    """layer_project equals x W^T (numpy's matmul) split into the q, k, v, beta blocks and by
+    head; layer_output equals residual + bo + concat_heads(y) Wo^T."""
+    rng = np.random.default_rng(61)
+    B, T, d_model, H, d_k, d_v = 2, 5, 24, 3, 4, 6
+    x = rng.normal(size=(B, T, d_model))
+    N = 2 * H * d_k + H * d_v + H
+    Wm = rng.normal(size=(N, d_model))
+    q, k, v, bl = O.layer_project(x, Wm, H, d_k, d_v)
+    full = x @ Wm.T                                   # [B, T, N]
+    split = lambda blk, d: blk.reshape(B, T, H, d).transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(q, split(full[..., :H * d_k], d_k), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(k, split(full[..., H * d_k:2 * H * d_k], d_k), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(v, split(full[..., 2 * H * d_k:2 * H * d_k + H * d_v], d_v),
+                               rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(bl, full[..., -H:].transpose(0, 2, 1), rtol=1e-13, atol=1e-13)
+    y = rng.normal(size=(B, H, T, d_v))
+    Wo = rng.normal(size=(d_model, H * d_v))
+    bo = rng.normal(size=d_model)
+    res = rng.normal(size=(B, T, d_model))
+    cat = y.transpose(0, 2, 1, 3).reshape(B, T, H * d_v)
+    np.testing.assert_allclose(O.layer_output(y, Wo, bo, res), res + bo + cat @ Wo.T, rtol=1e-13,
+                               atol=1e-12)
+    np.testing.assert_allclose(O.layer_output(y, Wo), cat @ Wo.T, rtol=1e-13, atol=1e-12)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

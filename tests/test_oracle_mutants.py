@@ -87,6 +87,15 @@ MUTANTS = {
     "sum_initial_z_ignored": ("if (z0) memcpy(z, z0 + s * D", "if (0) memcpy(z, z0 + s * D"),
     "sum_initial_state_ignored": ("if (W0) memcpy(W, W0 + (size_t)s * d_v * D",
                                   "if (0) memcpy(W, W0 + (size_t)s * d_v * D"),
+    # projections
+    "proj_head_split_transposed": (
+        "q[((b * H + n / d_k) * T + t) * d_k + n % d_k] = s;",
+        "q[((b * H + n % H) * T + t) * d_k + n / H] = s;"),
+    "proj_key_block_offset": ("const int m = n - nq;", "const int m = n - nq + 1 < nq ? n - nq + 1 : n - nq;"),
+    "proj_output_bias_dropped": ("if (bo) s += bo[n];", "if (0) s += bo[n];"),
+    "proj_output_head_order": (
+        "s += y[((b * H + kk / d_v) * T + t) * d_v + kk % d_v] * Wo[(int64_t)n * Kc + kk];",
+        "s += y[((b * H + kk % H) * T + t) * d_v + kk / H] * Wo[(int64_t)n * Kc + kk];"),
 }
 
 

@@ -260,6 +260,56 @@ fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, f
                                 int64_t* workspace_bytes);
 
 /*
+ * fwa_layer_project -- the projections in front of the layer, written straight into its
+ * head-split inputs: for x [B, T, d_model] and the stacked bias-free weights
+ * W_qkvb [2*H*d_k + H*d_v + H, d_model] (rows: H*d_k query, H*d_k key, H*d_v value, then H
+ * interpolation-weight rows; out = x W^T), writes q, k [B, H, T, d_k], v [B, H, T, d_v] and
+ * beta_logit [B, H, T] (the layer applies the sigmoid).
+ *   [FWT] section "FastWeightsAttention / module structure and source walkthrough" (query,
+ *   key and value maps without bias, one interpolation-weight scalar per head).
+ *   All tensors `dtype`; fp32 accumulation.  d_model, d_k and d_v must be multiples of 8.
+ */
+fwa_status fwa_layer_project(const void* x, const void* W_qkvb, void* q, void* k, void* v,
+                             void* beta_logit, int B, int T, int d_model, int H, int d_k, int d_v,
+                             fwa_dtype dtype, hipStream_t stream);
+
+/*
+ * fwa_layer_output -- the output map behind the layer, reading its head-split output:
+ *   out[b, t, :] = residual[b, t, :] + b_o + W_o concat_h(y[b, h, t, :])
+ * with y [B, H, T, d_v], W_o [d_model, H*d_v], b_o [d_model] (or NULL), residual and out
+ * [B, T, d_model] (residual may be NULL, or equal out for the in-place residual add the
+ * Transformer layer does).  [FWT] same section ("output" linear map) and section "Assembling
+ * the Transformer / layer" (the attention residual).  All `dtype`; fp32 accumulation;
+ * d_model and d_v multiples of 8.
+ */
+fwa_status fwa_layer_output(const void* y, const void* W_o, const void* b_o,
+                            const void* residual, void* out, int B, int T, int H, int d_v,
+                            int d_model, fwa_dtype dtype, hipStream_t stream);
+
+/*
+ * fwa_decode_layers -- one new token through L fast-weight attention layers, each with its
+ * own memory: for l = 0 .. L-1,
+ *   (q, k, v, beta_logit) = fwa_layer_project(x, W_qkvb[l]);
+ *   y = fwa_delta_step(q, k, v, beta_logit, W[l]);
+ *   x = fwa_layer_output(y, W_o[l], b_o[l], residual = x)
+ * with x [B, d_model] (`dtype`) updated in place and every W[l] [B, H, d_v, D] (fp32) updated
+ * in place.  [FWT] sections "token_wise variant" (one memory per layer, carried from token to
+ * token) and "Inference and sampling".  W_qkvb, W_o, b_o and W are HOST arrays of L device
+ * pointers (b_o may be NULL, or hold NULL entries); they are read during the call, so the
+ * 3*L launches can be captured into a HIP graph and replayed for later tokens.  workspace: at
+ * least fwa_decode_layers_info's bytes (the per-layer q, k, v, beta_logit and y).
+ * Implemented shapes: those of fwa_layer_project and fwa_delta_step together.
+ */
+fwa_status fwa_decode_layers(void* x, int L, const void* const* W_qkvb, const void* const* W_o,
+                             const void* const* b_o, float* const* W, int B, int d_model, int H,
+                             int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
+
+/* fwa_decode_layers_info -- workspace bytes fwa_decode_layers needs. */
+fwa_status fwa_decode_layers_info(int B, int d_model, int H, int d_k, int d_v, int nu,
+                                  fwa_dtype dtype, int64_t* workspace_bytes);
+
+/*
  * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory
  * carried in and out through W, updated in place.
  *   [FWT] sections "token_wise variant" and "Inference and sampling" (each new token updates

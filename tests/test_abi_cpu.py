@@ -1,5 +1,9 @@
 """The C ABI on the CPU: the library loads, exports every function include/fwa.h declares,
-and rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+and rejects invalid arguments on the host before any HIP call (no GPU needed).
+
+The rejection tests pass pointers that are never dereferenced; should a check ever let one of
+them through, its launch must not reach a real device, so this module runs only where no GPU is
+visible."""
 import ctypes
 import os
 import re
@@ -8,6 +12,10 @@ import subprocess
 import pytest
 
 from weight_linear_attention_amd import fwa
+
+pytestmark = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0,
+    reason="passes never-dereferenced pointers: CPU-only (a GPU is visible here)")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fwa.h")
@@ -426,3 +434,57 @@ def test_sum_forward_info_and_empty_batch():
     D, d_v, nc = 256, 64, 4096 // 32
     per_chunk = 2 * 32 * D + 32 * d_v + 32 + D
     assert fwa.sum_forward_info(4, 8, 4096, 64, d_v, 2, torch.bfloat16) == 4 * 8 * nc * per_chunk * 4
+
+
+# ------------------------------------------------------------------ linear maps and multi-layer decode
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), 1, "NULL"),
+    (dict(d_model=100), 2, "multiples of 8"),
+    (dict(T=-1), 1, "negative"),
+    (dict(q=P(0x10000)), 1, "output overlaps an input"),
+    (dict(bl=P(0x2000010)), 1, "two outputs overlap"),
+    (dict(x=MISALIGNED), 1, "aligned"),
+])
+def test_layer_project_rejects(kw, status, msg):
+    a = dict(x=FAKE, W=P(0x1000000), q=P(0x2000000), k=P(0x3000000), v=P(0x4000000),
+             bl=P(0x5000000), B=1, T=4, d_model=64, H=2, d_k=16, d_v=16, dtype=0)
+    a.update(kw)
+    st = fwa.lib().fwa_layer_project(a["x"], a["W"], a["q"], a["k"], a["v"], a["bl"], a["B"],
+                                     a["T"], a["d_model"], a["H"], a["d_k"], a["d_v"], a["dtype"],
+                                     None)
+    assert st == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(out=None), 1, "NULL"),
+    (dict(d_v=12), 2, "multiples of 8"),
+    (dict(out=FAKE), 1, "out overlaps an input"),
+    (dict(res=P(0x3000010)), 1, "partially overlaps residual"),
+])
+def test_layer_output_rejects(kw, status, msg):
+    a = dict(y=FAKE, Wo=P(0x1000000), bo=None, res=None, out=P(0x3000000), B=1, T=4, H=2,
+             d_v=16, d_model=64, dtype=0)
+    a.update(kw)
+    st = fwa.lib().fwa_layer_output(a["y"], a["Wo"], a["bo"], a["res"], a["out"], a["B"], a["T"],
+                                    a["H"], a["d_v"], a["d_model"], a["dtype"], None)
+    assert st == status
+    assert msg in fwa.lib().fwa_last_error().decode()
+
+
+def test_decode_layers_rejects_before_launch():
+    L = fwa.lib()
+    arr = lambda *p: (ctypes.c_void_p * len(p))(*p)
+    Wp, Wo, W = arr(0x1000000, 0x2000000), arr(0x3000000, 0x4000000), arr(0x5000000, 0x5000000)
+    args = (FAKE, 2, Wp, Wo, None, W, 4, 64, 2, 16, 16, 1, 0)
+    ws = ctypes.c_int64(0)
+    assert L.fwa_decode_layers_info(4, 64, 2, 16, 16, 1, 0, ctypes.byref(ws)) == 0
+    assert ws.value == 2 * 4 * 2 * 16 * 4 + 2 * 4 * 2 * 16 * 4 + 32
+    # the two layers share one memory
+    assert L.fwa_decode_layers(*args, P(0x8000000), ws.value, None) == 1
+    assert "memories of layers" in L.fwa_last_error().decode()
+    assert L.fwa_decode_layers(*args, None, 0, None) == 1
+    assert "workspace" in L.fwa_last_error().decode()
+    assert L.fwa_decode_layers(FAKE, 0, None, None, None, None, 4, 64, 2, 16, 16, 1, 0, None, 0,
+                               None) == 0

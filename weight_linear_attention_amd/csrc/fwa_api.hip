@@ -560,6 +560,165 @@ fwa_status fwa_sum_forward(const void* q, const void* k, const void* v, const fl
                       "fwa_sum_forward launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+fwa_status check_linear_dims(const char* fn, int B, int T, int d_model, int H, int d_k, int d_v,
+                             fwa_dtype dtype) {
+    if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (B < 0 || T < 0 || H < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/T/H", fn);
+    if (d_model < 1 || d_k < 1 || d_v < 1)
+        return fail(FWA_ERR_INVALID_ARG, "%s: d_model, d_k and d_v must be >= 1", fn);
+    if (d_model % 8 || d_k % 8 || d_v % 8)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: d_model, d_k and d_v must be multiples of 8", fn);
+    const int64_t N = 2 * int64_t(H) * d_k + int64_t(H) * d_v + H;
+    if (!mul_le(kIndexLimit, {int64_t(B), int64_t(T), N + d_model}) ||
+        static_cast<int64_t>(B) * T >= (int64_t(1) << 31) || N * d_model >= (int64_t(1) << 31) ||
+        int64_t(H) * d_v * d_model >= (int64_t(1) << 31))
+        return fail(FWA_ERR_UNSUPPORTED, "%s: sizes overflow the index range", fn);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fwa_status fwa_layer_project(const void* x, const void* W_qkvb, void* q, void* k, void* v,
+                             void* beta_logit, int B, int T, int d_model, int H, int d_k, int d_v,
+                             fwa_dtype dtype, hipStream_t stream) {
+    const char* fn = "fwa_layer_project";
+    fwa_status st = check_linear_dims(fn, B, T, d_model, H, d_k, d_v, dtype);
+    if (st != FWA_OK) return st;
+    const int64_t M = int64_t(B) * T;
+    if (M == 0 || H == 0) return ok();
+    if (!x || !W_qkvb || !q || !k || !v || !beta_logit)
+        return fail(FWA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    const void* ptrs[] = {x, W_qkvb, q, k, v, beta_logit};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    const int es = elem_bytes(dtype);
+    const int64_t N = 2 * int64_t(H) * d_k + int64_t(H) * d_v + H;
+    const Span in[] = {span(x, M * d_model * es), span(W_qkvb, N * d_model * es)};
+    const Span out[] = {span(q, M * H * d_k * es), span(k, M * H * d_k * es),
+                        span(v, M * H * d_v * es), span(beta_logit, M * H * es)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span& s : in)
+            if (overlap(out[i], s)) return fail(FWA_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out[j])) return fail(FWA_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+    }
+    return hip_status(fwa::launch_layer_project(x, W_qkvb, q, k, v, beta_logit, B, T, d_model, H,
+                                                d_k, d_v, dtype == FWA_BF16, stream),
+                      "fwa_layer_project launch");
+}
+
+fwa_status fwa_layer_output(const void* y, const void* W_o, const void* b_o,
+                            const void* residual, void* out, int B, int T, int H, int d_v,
+                            int d_model, fwa_dtype dtype, hipStream_t stream) {
+    const char* fn = "fwa_layer_output";
+    fwa_status st = check_linear_dims(fn, B, T, d_model, H, 8, d_v, dtype);
+    if (st != FWA_OK) return st;
+    const int64_t M = int64_t(B) * T;
+    if (M == 0) return ok();
+    if (!out || !W_o || (H > 0 && !y)) return fail(FWA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    const void* ptrs[] = {y, W_o, b_o, residual, out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    const int es = elem_bytes(dtype);
+    const Span so = span(out, M * d_model * es);
+    const Span in[] = {span(y, y ? M * H * d_v * es : 0), span(W_o, int64_t(d_model) * H * d_v * es),
+                       span(b_o, b_o ? d_model * es : 0)};
+    for (const Span& s : in)
+        if (overlap(so, s)) return fail(FWA_ERR_INVALID_ARG, "%s: out overlaps an input", fn);
+    if (residual && residual != out && overlap(so, span(residual, M * d_model * es)))
+        return fail(FWA_ERR_INVALID_ARG, "%s: out partially overlaps residual", fn);
+    return hip_status(fwa::launch_layer_output(y, W_o, b_o, residual, out, B, T, H, d_v, d_model,
+                                               dtype == FWA_BF16, stream),
+                      "fwa_layer_output launch");
+}
+
+fwa_status fwa_decode_layers_info(int B, int d_model, int H, int d_k, int d_v, int nu,
+                                  fwa_dtype dtype, int64_t* workspace_bytes) {
+    const char* fn = "fwa_decode_layers_info";
+    fwa_status st = check_linear_dims(fn, B, 1, d_model, H, d_k, d_v, dtype);
+    if (st != FWA_OK) return st;
+    if (nu < 1 || nu > 2 * d_k - 1)
+        return fail(FWA_ERR_INVALID_ARG, "%s: nu=%d outside [1, 2*d_k-1]", fn, nu);
+    const int64_t BH = int64_t(B) * H;
+    const int es = elem_bytes(dtype);
+    auto up16 = [](int64_t n) { return (n + 15) & ~int64_t(15); };
+    if (workspace_bytes)
+        *workspace_bytes = 2 * up16(BH * d_k * es) + 2 * up16(BH * d_v * es) + up16(BH * es);
+    return ok();
+}
+
+fwa_status fwa_decode_layers(void* x, int L, const void* const* W_qkvb, const void* const* W_o,
+                             const void* const* b_o, float* const* W, int B, int d_model, int H,
+                             int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "fwa_decode_layers";
+    int64_t need = 0;
+    fwa_status st = fwa_decode_layers_info(B, d_model, H, d_k, d_v, nu, dtype, &need);
+    if (st != FWA_OK) return st;
+    if (L < 0) return fail(FWA_ERR_INVALID_ARG, "%s: L < 0", fn);
+    const int64_t BH = int64_t(B) * H;
+    if (L == 0 || BH == 0) return ok();
+    if (!x || !W_qkvb || !W_o || !W) return fail(FWA_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!workspace || workspace_bytes < need)
+        return fail(FWA_ERR_INVALID_ARG, "%s: needs a workspace of %lld bytes (got %lld%s)", fn,
+                    (long long)need, (long long)workspace_bytes, workspace ? "" : ", NULL");
+    if (d_k != 16 && d_k != 32 && d_k != 64 && d_k != 128)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: d_k=%d not in {16,32,64,128}", fn, d_k);
+    const int64_t D = 2 * static_cast<int64_t>(d_k) * nu;
+    int LR = 0;
+    if (D > 1024 || fwa::step_cpl_for(static_cast<int>(D), &LR) == 0)
+        return fail(FWA_ERR_UNSUPPORTED, "%s: D=%lld has no decode-step row layout", fn, (long long)D);
+    const int es = elem_bytes(dtype);
+    const int64_t N = 2 * int64_t(H) * d_k + int64_t(H) * d_v + H;
+    const Span sx = span(x, int64_t(B) * d_model * es), sws = span(workspace, need);
+    if (!aligned16(x) || !aligned16(workspace))
+        return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (overlap(sx, sws)) return fail(FWA_ERR_INVALID_ARG, "%s: x overlaps the workspace", fn);
+    for (int l = 0; l < L; ++l) {
+        if (!W_qkvb[l] || !W_o[l] || !W[l])
+            return fail(FWA_ERR_INVALID_ARG, "%s: NULL pointer for layer %d", fn, l);
+        const void* lp[] = {W_qkvb[l], W_o[l], b_o ? b_o[l] : nullptr, W[l]};
+        for (const void* p : lp)
+            if (p && !aligned16(p))
+                return fail(FWA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned (layer %d)", fn, l);
+        const Span ls[] = {span(W_qkvb[l], N * d_model * es),
+                           span(W_o[l], int64_t(d_model) * H * d_v * es),
+                           span(b_o ? b_o[l] : nullptr, b_o && b_o[l] ? d_model * es : 0),
+                           span(W[l], BH * d_v * D * 4)};
+        for (const Span& s : ls)
+            if (overlap(s, sx) || overlap(s, sws))
+                return fail(FWA_ERR_INVALID_ARG, "%s: layer %d's parameters overlap x or the workspace", fn, l);
+        for (int m = 0; m < l; ++m)
+            if (overlap(ls[3], span(W[m], BH * d_v * D * 4)))
+                return fail(FWA_ERR_INVALID_ARG, "%s: the memories of layers %d and %d overlap", fn, m, l);
+    }
+    auto up16 = [](int64_t n) { return (n + 15) & ~int64_t(15); };
+    char* ws = static_cast<char*>(workspace);
+    void* q = ws;
+    void* k = ws + up16(BH * d_k * es);
+    void* v = ws + 2 * up16(BH * d_k * es);
+    void* y = ws + 2 * up16(BH * d_k * es) + up16(BH * d_v * es);
+    void* bl = ws + 2 * up16(BH * d_k * es) + 2 * up16(BH * d_v * es);
+    const bool bf16 = dtype == FWA_BF16;
+    for (int l = 0; l < L; ++l) {
+        hipError_t e = fwa::launch_layer_project(x, W_qkvb[l], q, k, v, bl, B, 1, d_model, H, d_k,
+                                                 d_v, bf16, stream);
+        if (e == hipSuccess)
+            e = fwa::launch_delta_step(q, k, v, bl, W[l], y, BH, d_k, d_v, nu, bf16, stream);
+        if (e == hipSuccess)
+            e = fwa::launch_layer_output(y, W_o[l], b_o ? b_o[l] : nullptr, x, x, B, 1, H, d_v,
+                                         d_model, bf16, stream);
+        if (e != hipSuccess) return hip_status(e, "fwa_decode_layers launch");
+    }
+    return ok();
+}
+
 fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,
                           float* W, void* y, int B, int H, int d_k, int d_v, int nu,
                           fwa_dtype dtype, hipStream_t stream) {

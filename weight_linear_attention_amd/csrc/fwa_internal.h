@@ -130,4 +130,12 @@ hipError_t launch_sum_forward(const void* q, const void* k, const void* v, const
                               int d_k, int d_v, int nu, bool bf16, void* workspace,
                               hipStream_t stream);
 
+// Linear maps around the layer (projection.hip).
+hipError_t launch_layer_project(const void* x, const void* Wqkvb, void* q, void* k, void* v,
+                                void* bl, int B, int T, int d_model, int H, int d_k, int d_v,
+                                bool bf16, hipStream_t stream);
+hipError_t launch_layer_output(const void* y, const void* Wo, const void* bo, const void* res,
+                               void* out, int B, int T, int H, int d_v, int d_model, bool bf16,
+                               hipStream_t stream);
+
 }  // namespace fwa

@@ -17,6 +17,10 @@ Functions (same names as the C entry points, minus the prefix):
     delta_backward(q, k, v, beta_logit, dy, W0=None, dW_final=None, nu=1)
                                                   -> (dq, dk, dv, dbeta_logit, dW0)
     sum_forward(q, k, v, W0=None, z0=None, nu=1)  -> (y, W_final, z_final)
+    layer_project(x, W_qkvb, H, d_k, d_v)         -> (q, k, v, beta_logit)
+    layer_output(y, W_o, b_o=None, residual=None) -> out
+    decode_layers(x, layers, memories, H, d_k, d_v, nu=1)
+                                                  -> x (one token through all layers, in place)
 
 Shapes are checked before anything else, so a wrong shape raises ValueError without touching
 the device.  The forward's workspace is allocated here with torch on the current stream (the
@@ -40,7 +44,8 @@ PATH_NAMES = {FWA_PATH_NONE: "none", FWA_PATH_CHUNKED: "chunked", FWA_PATH_FUSED
 
 EXPORTED = ("fwa_dpfp", "fwa_delta_forward", "fwa_delta_forward_path", "fwa_delta_forward_info",
             "fwa_delta_forward_noalloc", "fwa_delta_backward", "fwa_delta_backward_info",
-            "fwa_sum_forward", "fwa_sum_forward_info", "fwa_delta_step", "fwa_status_string",
+            "fwa_sum_forward", "fwa_sum_forward_info", "fwa_layer_project", "fwa_layer_output",
+            "fwa_decode_layers", "fwa_decode_layers_info", "fwa_delta_step", "fwa_status_string",
             "fwa_last_error", "fwa_version")
 
 
@@ -82,6 +87,14 @@ def lib():
     L.fwa_sum_forward.restype = i32
     L.fwa_sum_forward_info.argtypes = [i32] * 7 + [ctypes.POINTER(i64)]
     L.fwa_sum_forward_info.restype = i32
+    L.fwa_layer_project.argtypes = [P] * 6 + [i32] * 6 + [i32, P]
+    L.fwa_layer_project.restype = i32
+    L.fwa_layer_output.argtypes = [P] * 5 + [i32] * 5 + [i32, P]
+    L.fwa_layer_output.restype = i32
+    L.fwa_decode_layers.argtypes = [P, i32, P, P, P, P] + [i32] * 6 + [i32, P, i64, P]
+    L.fwa_decode_layers.restype = i32
+    L.fwa_decode_layers_info.argtypes = [i32] * 7 + [ctypes.POINTER(i64)]
+    L.fwa_decode_layers_info.restype = i32
     L.fwa_delta_step.argtypes = [P, P, P, P, P, P] + [i32] * 5 + [i32, P]
     L.fwa_delta_step.restype = i32
     L.fwa_status_string.argtypes = [i32]
@@ -296,6 +309,84 @@ def sum_forward(q, k, v, W0=None, z0=None, nu=1, out=None, W_final=None, z_final
                                  _ptr(W_final), _ptr(z_final), B, H, T, d_k, d_v, nu,
                                  _dtype_code(q.dtype), _ptr(workspace), ws_bytes, _stream(dev)))
     return out, W_final, z_final
+
+
+def layer_project(x, W_qkvb, H, d_k, d_v):
+    """x [B, T, d_model] -> (q, k [B,H,T,d_k], v [B,H,T,d_v], beta_logit [B,H,T])."""
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, T, d_model], got {tuple(x.shape)}")
+    B, T, d_model = x.shape
+    _shape(W_qkvb, "W_qkvb", (2 * H * d_k + H * d_v + H, d_model))
+    dev = x.device
+    _need(x, "x", dev)
+    _need(W_qkvb, "W_qkvb", dev, x.dtype)
+    q = torch.empty(B, H, T, d_k, dtype=x.dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty(B, H, T, d_v, dtype=x.dtype, device=dev)
+    bl = torch.empty(B, H, T, dtype=x.dtype, device=dev)
+    _check(lib().fwa_layer_project(_ptr(x), _ptr(W_qkvb), _ptr(q), _ptr(k), _ptr(v), _ptr(bl),
+                                   B, T, d_model, H, d_k, d_v, _dtype_code(x.dtype), _stream(dev)))
+    return q, k, v, bl
+
+
+def layer_output(y, W_o, b_o=None, residual=None, out=None):
+    """residual + b_o + concat_heads(y) W_o^T for y [B, H, T, d_v]; returns [B, T, d_model]
+    (out may be the residual tensor itself)."""
+    if y.dim() != 4:
+        raise ValueError(f"y must be [B, H, T, d_v], got {tuple(y.shape)}")
+    B, H, T, d_v = y.shape
+    d_model = W_o.shape[0]
+    _shape(W_o, "W_o", (d_model, H * d_v))
+    _shape(b_o, "b_o", (d_model,))
+    _shape(residual, "residual", (B, T, d_model))
+    _shape(out, "out", (B, T, d_model))
+    dev = y.device
+    _need(y, "y", dev)
+    for t, n in ((W_o, "W_o"), (b_o, "b_o"), (residual, "residual")):
+        if t is not None:
+            _need(t, n, dev, y.dtype)
+    if out is None:
+        out = torch.empty(B, T, d_model, dtype=y.dtype, device=dev)
+    _need(out, "out", dev, y.dtype)
+    _check(lib().fwa_layer_output(_ptr(y), _ptr(W_o), _ptr(b_o), _ptr(residual), _ptr(out), B, T,
+                                  H, d_v, d_model, _dtype_code(y.dtype), _stream(dev)))
+    return out
+
+
+def decode_layers(x, layers, memories, H, d_k, d_v, nu=1, workspace=None):
+    """One token through len(layers) layers, in place: x [B, d_model]; layers a list of
+    (W_qkvb, W_o, b_o or None); memories a list of fp32 [B, H, d_v, D] tensors (updated)."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [B, d_model], got {tuple(x.shape)}")
+    B, d_model = x.shape
+    L = len(layers)
+    if len(memories) != L:
+        raise ValueError("one memory per layer")
+    D = 2 * d_k * nu
+    dev = x.device
+    _need(x, "x", dev)
+    for l, ((Wp, Wo, bo), W) in enumerate(zip(layers, memories)):
+        _shape(Wp, f"W_qkvb[{l}]", (2 * H * d_k + H * d_v + H, d_model))
+        _shape(Wo, f"W_o[{l}]", (d_model, H * d_v))
+        _shape(bo, f"b_o[{l}]", (d_model,))
+        _shape(W, f"W[{l}]", (B, H, d_v, D))
+        for t, n in ((Wp, "W_qkvb"), (Wo, "W_o"), (bo, "b_o")):
+            if t is not None:
+                _need(t, n, dev, x.dtype)
+        _need(W, "W", dev, torch.float32)
+    code = _dtype_code(x.dtype)
+    if workspace is None:
+        nbytes = ctypes.c_int64(0)
+        _check(lib().fwa_decode_layers_info(B, d_model, H, d_k, d_v, nu, code, ctypes.byref(nbytes)))
+        workspace = torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", dev)
+    arr = lambda ts: (ctypes.c_void_p * max(L, 1))(*[None if t is None else t.data_ptr() for t in ts])
+    _check(lib().fwa_decode_layers(_ptr(x), L, arr([p[0] for p in layers]), arr([p[1] for p in layers]),
+                                   arr([p[2] for p in layers]), arr(memories), B, d_model, H, d_k,
+                                   d_v, nu, code, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(dev)))
+    return x
 
 
 def check_step_shapes(q, k, v, beta_logit, W, nu=1, out=None):

@@ -13,6 +13,12 @@ when timing starts.  Other workloads (--workload):
     h8_t1024_d64_nu1_f32, b4_h8_t4096_d64_nu2_bf16_carried, tiny_t64_d16_nu1_f32
                                                                     forward + decode step
     decode_b256_h8_d64_nu1_f32                                      one fwa_delta_step per step
+    backward_<forward workload>                                     one fwa_delta_backward
+    sum_<forward workload>                                          one fwa_sum_forward (the
+                                                                    sum-update form with z)
+    layers6_decode_b256_h8_d64_nu1_f32                              one token through 6 layers
+                                                                    (fwa_decode_layers, d_model
+                                                                    512, random-init weights)
     dpfp_b8_h16_t16384_d64_nu3_bf16                                 fwa_dpfp on q and k
     copy_calibration                                                a 1 GiB device copy (the
                                                                     reference for HBM counters)
@@ -43,6 +49,7 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+PEAK_VALU_F32_TFLOPS = 157.3   # 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2 issue x 2.4 GHz
 DEFAULT_WORKLOAD = "b8_h16_t16384_d64_nu3_bf16"
 WARMUP_SECONDS = 0.3       # default warm-up length
 DECODE_WARM_SLICES = 64    # decode: input slices the warm-up cycles through
@@ -72,6 +79,9 @@ SOURCES = {
     "fused": ("forward_kernel.h", "chunk_tile.h"),
     "decode": ("step_kernel.hip",),
     "dpfp": ("dpfp_kernel.hip",),
+    "backward": ("backward.hip", "chunk_f32.h"),
+    "sum": ("sum_forward.hip", "chunk_f32.h"),
+    "layers": ("projection.hip", "step_kernel.hip"),
 }
 
 
@@ -160,17 +170,25 @@ def main():
                           "bytes_written": 4 * n, "seconds": dt}), flush=True)
         return
     kind = "prefill+decode"
+    n_layers = 0
     if name.startswith("dpfp_"):
         kind, w = "dpfp", workload(name[len("dpfp_"):])
     elif name.startswith("decode_"):
         kind, w = "decode", workload(name)
+    elif name.startswith("backward_"):
+        kind, w = "backward", workload(name[len("backward_"):])
+    elif name.startswith("sum_"):
+        kind, w = "sum", workload(name[len("sum_"):])
+    elif name.startswith("layers"):
+        n_layers = int(name[len("layers"):name.index("_")])
+        kind, w = "layers", workload(name[name.index("_") + 1:])
     else:
         w = workload(name)
     if args.chunk is not None:
         w = workload(w.name, chunk=args.chunk)
     steps = args.steps if args.steps is not None else {
         "prefill+decode": 100 if w.B * w.H * w.T >= (1 << 20) else 1000,
-        "decode": 1024, "dpfp": 50}[kind]
+        "decode": 1024, "dpfp": 50, "backward": 20, "sum": 50, "layers": 256}[kind]
     # Warm-up: --warmup steps, else as many as fill WARMUP_SECONDS (at least 3): the GPU's
     # clocks reach their steady state only after some tens of milliseconds of work.
     warmup = args.warmup
@@ -179,7 +197,21 @@ def main():
 
     # ------------------------------------------------------------------ inputs in HBM
     nxt = None
-    if kind == "decode":
+    if kind == "layers":
+        # random-init weights of the projections and output maps (N(0, 1/fan_in)), one token
+        # embedding per step, a zero memory per layer
+        d_model = w.H * w.d_k
+        gl = torch.Generator().manual_seed(w.seed + 11)
+        Nq = 2 * w.H * w.d_k + w.H * w.d_v + w.H
+        layer_w = [(torch.randn(Nq, d_model, generator=gl).div(d_model ** 0.5).to(w.torch_dtype).to(dev),
+                    torch.randn(d_model, w.H * w.d_v, generator=gl).div((w.H * w.d_v) ** 0.5).to(w.torch_dtype).to(dev),
+                    (0.1 * torch.randn(d_model, generator=gl)).to(w.torch_dtype).to(dev))
+                   for _ in range(n_layers)]
+        mems = [torch.zeros(w.B, w.H, w.d_v, w.D, device=dev) for _ in range(n_layers)]
+        toks = torch.randn(64, w.B, d_model, generator=gl).to(w.torch_dtype).to(dev)
+        xl = torch.empty(w.B, d_model, dtype=w.torch_dtype, device=dev)
+        inp = None
+    elif kind == "decode":
         # DECODE_WARM_SLICES slices for the warm-up (cycled), then one fresh slice per timed step
         inp = make_decode_inputs(w, steps=DECODE_WARM_SLICES + steps)
         d = {k: v.to(dev) for k, v in inp.items()}
@@ -187,6 +219,9 @@ def main():
     else:
         inp = make_inputs(w)
         d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    if kind == "backward":
+        from weight_linear_attention_amd.synthetic import make_cotangents
+        cot = {k: (None if v is None else v.to(dev)) for k, v in make_cotangents(w).items()}
     if kind == "prefill+decode":
         g = torch.Generator().manual_seed(w.seed + 7)
         nxt = {n: torch.randn(w.B, w.H, dd, generator=g).to(w.torch_dtype).to(dev)
@@ -220,6 +255,14 @@ def main():
         elif kind == "decode":
             fwa.delta_step(d["q"][i], d["k"][i], d["v"][i], d["beta_logit"][i], W, nu=w.nu,
                            out=ystep)
+        elif kind == "backward":
+            fwa.delta_backward(d["q"], d["k"], d["v"], d["beta_logit"], cot["dy"], W0=d["W0"],
+                               dW_final=cot["dW_final"], nu=w.nu)
+        elif kind == "sum":
+            fwa.sum_forward(d["q"], d["k"], d["v"], d["W0"], nu=w.nu)
+        elif kind == "layers":
+            xl.copy_(toks[i % toks.shape[0]])
+            fwa.decode_layers(xl, layer_w, mems, w.H, w.d_k, w.d_v, w.nu)
         else:
             fwa.dpfp(d["q"], w.nu, out=phi_q)
             fwa.dpfp(d["k"], w.nu, out=phi_k)
@@ -285,7 +328,9 @@ def main():
     # ------------------------------------------------------------------ metric + roofline
     if kind == "prefill+decode":
         tokens = w.B * (w.T + 1)
-    elif kind == "decode":
+    elif kind in ("backward", "sum"):
+        tokens = w.B * w.T
+    elif kind in ("decode", "layers"):
         tokens = w.B
     else:
         tokens = 2 * BH * w.T          # DPFP vectors (q and k) per step
@@ -319,6 +364,48 @@ def main():
                             "products, about 2^-16 relative); the peak quoted is the fp32 MFMA one")
             roof["split_bf16_ceiling"] = {"peak": split_peak, "unit": "TFLOP/s",
                                           "frac": flops / (main_ms * 1e-3) / 1e12 / split_peak}
+    elif kind in ("backward", "sum"):
+        unit = kind
+        if kind == "backward":
+            # the gradient of the literal recurrence: six rank-1 / mat-vec passes over the
+            # memory per token-head (12 D d_v) plus DPFP's derivative; no forward recompute
+            flops = BH * w.T * (12 * D * w.d_v + 12 * D)
+            nbytes = (BH * w.T * ((4 * w.d_k + 2 * w.d_v + 2 + w.d_v) * es)
+                      + BH * w.d_v * D * 4 * (2 + (d["W0"] is not None)))
+            kname = ("fwa_delta_backward: bwd_prep + bwd_fwd_states + bwd_grad_states + "
+                     "bwd_chunk_grads + bwd_dpfp")
+        else:
+            flops = BH * w.T * (4 * D * w.d_v + 9 * D)
+            nbytes = (BH * w.T * (2 * w.d_k + 2 * w.d_v) * es
+                      + BH * (w.d_v * D + D) * 4 * (1 + (d["W0"] is not None)))
+            kname = "fwa_sum_forward: sum_prep + sum_scan + sum_zfinal"
+        t_alu = flops / (PEAK_VALU_F32_TFLOPS * 1e12)
+        t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+        if t_alu >= t_hbm:
+            ach = flops / (main_ms * 1e-3) / 1e12
+            roof = {"bound": "alu", "achieved": ach, "peak": PEAK_VALU_F32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": ach / PEAK_VALU_F32_TFLOPS}
+        else:
+            ach = nbytes / (main_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": ach / PEAK_HBM_GBPS}
+        roof.update(kernel=kname, algorithmic_flops=flops, algorithmic_bytes=nbytes,
+                    mean_launch_ms=main_ms,
+                    timing="one event pair around %d back-to-back calls" % steps)
+    elif kind == "layers":
+        unit = "layers"
+        d_model = w.H * w.d_k
+        Nq = 2 * w.H * w.d_k + w.H * w.d_v + w.H
+        per_layer = (BH * (2 * w.d_v * D * 4 + (2 * w.d_k + 1 + 2 * w.d_v) * es * 2)
+                     + (Nq * d_model + d_model * w.H * w.d_v + d_model) * es + 2 * w.B * d_model * es)
+        nbytes = n_layers * per_layer
+        ach = nbytes / (main_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBPS,
+                "kernel": f"fwa_decode_layers ({n_layers} x linear_kernel<project> + "
+                          "delta_step_kernel + linear_kernel<output>)",
+                "algorithmic_bytes": nbytes, "mean_launch_ms": main_ms,
+                "timing": "one event pair around %d back-to-back tokens" % steps}
     else:
         if kind == "decode":
             unit = "decode"
@@ -333,7 +420,8 @@ def main():
                 "frac": ach / PEAK_HBM_GBPS, "kernel": kname, "algorithmic_bytes": nbytes,
                 "mean_launch_ms": main_ms}
     roof["traffic"] = measured_traffic(
-        unit, name if kind in ("dpfp", "decode") else f"{w.name}:c{w.chunk}")
+        unit, name if kind in ("dpfp", "decode", "backward", "sum", "layers")
+        else f"{w.name}:c{w.chunk}")
     if flush:
         roof["flushed"] = "a 1 GiB scratch read before every timed step; per-step events"
 
@@ -361,7 +449,9 @@ def main():
 
     # ------------------------------------------------------------------ CPU baseline
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, kind, inp, nxt)
+        extra = (cot if kind == "backward" else
+                 (layer_w, n_layers) if kind == "layers" else nxt)
+        out["cpu_baseline"] = cpu_baseline(w, kind, inp, extra)
     print(json.dumps(out), flush=True)
 
 
@@ -392,6 +482,44 @@ def cpu_baseline(w, kind, inp, nxt):
 
     threads = oracle.num_threads()
     host = host_cpu()
+    BH = w.B * w.H
+    sl = lambda t, n: None if t is None else to_f64(t).reshape(1, BH, *t.shape[2:])[:, :n]
+    if kind in ("backward", "sum"):
+        # whole (b, h) slices, a bounded sample (at most ~1e10 flops of oracle work per rep)
+        per_slice = w.T * w.D * w.d_v * (18 if kind == "backward" else 4)
+        nsl = max(1, min(BH, threads, int(1e10 // per_slice)))
+        args = [sl(inp[n], nsl) for n in ("q", "k", "v", "beta_logit", "W0")]
+        reps, dt, t0 = 0, 0.0, time.perf_counter()
+        while dt < 10.0 or reps == 0:
+            if kind == "backward":
+                oracle.delta_backward(*args, sl(nxt["dy"], nsl), sl(nxt["dW_final"], nsl), nu=w.nu)
+            else:
+                oracle.sum_forward(args[0], args[1], args[2], args[4], None, nu=w.nu)
+            reps += 1
+            dt = time.perf_counter() - t0
+        tok = w.T * nsl / w.H * reps
+        return {"value": tok / dt, "unit": "tokens/s", "cores": min(threads, nsl),
+                "kind": "oracle", "sample": f"{nsl} of {BH} (b,h) slices x T={w.T}, {reps} rep(s)",
+                "threads": threads, "host": host}
+    if kind == "layers":
+        layer_w, n_layers = nxt
+        d_model = w.H * w.d_k
+        lw = [tuple(to_f64(t) for t in p) for p in layer_w]
+        Ws = [np.zeros((w.B, w.H, w.d_v, w.D)) for _ in range(n_layers)]
+        rng = np.random.default_rng(0)
+        reps, dt, t0 = 0, 0.0, time.perf_counter()
+        while dt < 10.0 or reps == 0:
+            x = rng.normal(size=(w.B, d_model))
+            for l, (Wp, Wo, bo) in enumerate(lw):
+                q, k, v, bl = oracle.layer_project(x[:, None], Wp, w.H, w.d_k, w.d_v)
+                y, Ws[l] = oracle.delta_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], bl[:, :, 0], Ws[l],
+                                             nu=w.nu)
+                x = oracle.layer_output(y[:, :, None], Wo, bo, x[:, None])[:, 0]
+            reps += 1
+            dt = time.perf_counter() - t0
+        return {"value": w.B * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{reps} token(s) x {w.B} sequences through {n_layers} layers",
+                "threads": threads, "host": host}
     if kind == "decode":
         # 16 successive steps over all 2048 (b, h) slices (the oracle's step function)
         S = 16

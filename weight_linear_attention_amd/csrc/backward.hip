@@ -79,8 +79,8 @@ struct BwdArgs {
 
 // ------------------------------------------------------------------------------ 1. prep
 
-// LDS: x rows of k and q (relu([., -.]), C x 2 d_k each), K and Q (C x D), G, P, Ainv
-// (C x (C + 1)), beta, row sums, V (C x d_v).
+// LDS: x rows of k and q (relu([., -.]), C x 2 d_k each), K and Q (C x SD, SD = D + 8), G, P,
+// Ainv (C x (C + 1)), beta, V (C x d_v).
 template <bool BF16>
 __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     extern __shared__ float lds[];
@@ -90,16 +90,16 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     const int t0 = n * kBC;
     const int tid = threadIdx.x;
     constexpr int CS = kBC + 1;
+    const int SD = tile_stride(D);
     float* xk = lds;                         // [C][2 d_k]
     float* xq = xk + kBC * two;
-    float* Kt = xq + kBC * two;              // [C][D]
-    float* Qt = Kt + kBC * D;
-    float* Gm = Qt + kBC * D;                // [C][CS]
+    float* Kt = xq + kBC * two;              // [C][SD]
+    float* Qt = Kt + kBC * SD;
+    float* Gm = Qt + kBC * SD;               // [C][CS]
     float* Pm = Gm + kBC * CS;
     float* Ai = Pm + kBC * CS;
     float* be = Ai + kBC * CS;               // [C]
-    float* rs = be + kBC;                    // [2C]: DPFP row sums + eps (K, then Q)
-    float* Vs = rs + 2 * kBC;                // [C][d_v]
+    float* Vs = be + kBC;                    // [C][d_v]
 
     // relu'd raw rows (zero past the sequence end), beta (zero past the end), v
     load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, a.T - t0 < kBC ? a.T - t0 : kBC, t0, d_k,
@@ -112,32 +112,32 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
         const int c = i / d_v, r = i % d_v;
         Vs[i] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
     }
-    __syncthreads();
-    dpfp_tiles(xk, xq, Kt, Qt, rs, D, d_k, tid, kPrepThreads2);
+    dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
     for (int e = tid; e < kBC * D; e += kPrepThreads2) {
-        gK[e] = Kt[e];
-        gQ[e] = Qt[e];
+        const int c = e / D, p = e % D;
+        gK[e] = Kt[c * SD + p];
+        gQ[e] = Qt[c * SD + p];
     }
-    // G = K K^T and P = lower_incl(Q K^T): thread -> (row c, 4 columns j0..j0+3)
+    // G = K K^T and P = lower_incl(Q K^T): thread -> (row c, columns j0 + 8 e, e < 4)
     {
-        const int c = tid / 8, j0 = (tid % 8) * 4;
+        const int c = tid / 8, j0 = tid % 8;
         float g[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
         for (int p = 0; p < D; ++p) {
-            const float kc = Kt[c * D + p], qc = Qt[c * D + p];
+            const float kc = Kt[c * SD + p], qc = Qt[c * SD + p];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float kj = Kt[(j0 + e) * D + p];
+                const float kj = Kt[(j0 + 8 * e) * SD + p];
                 g[e] += kc * kj;
                 pq[e] += qc * kj;
             }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            Gm[c * CS + j0 + e] = g[e];
-            Pm[c * CS + j0 + e] = (j0 + e <= c) ? pq[e] : 0.0f;
+            Gm[c * CS + j0 + 8 * e] = g[e];
+            Pm[c * CS + j0 + 8 * e] = (j0 + 8 * e <= c) ? pq[e] : 0.0f;
         }
     }
     __syncthreads();
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     for (int p = tid; p < D; p += kPrepThreads2) {
         float bk[kBC], wy[kBC];
 #pragma unroll
-        for (int j = 0; j < kBC; ++j) bk[j] = be[j] * Kt[j * D + p];
+        for (int j = 0; j < kBC; ++j) bk[j] = be[j] * Kt[j * SD + p];
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
             float s = 0.0f;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
-            float s = Qt[i * D + p];
+            float s = Qt[i * SD + p];
 #pragma unroll
             for (int j = 0; j <= i; ++j) s -= Pm[i * CS + j] * wy[j];
             gQp[i * D + p] = s;
@@ -208,18 +208,24 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------ row chains
 
 // Chunk-start memories and U: row r of the memory moves as w <- w + K^T u with
-// u = Uy[:, r] - Wy w.  Lane l holds w[l + 64 m], m < NPL.
+// u = Uy[:, r] - Wy w.  Lane l holds w[l + 64 m], m < NPL.  The next chunk's Wy and K tiles load
+// into registers while the current chunk computes.
 template <int NPL>
 __global__ __launch_bounds__(64 * kRowWaves) void bwd_fwd_states_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_v = a.d_v;
     const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
     const int bh = blockIdx.x / rgroups;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
     const bool live = r < d_v;
-    float* Wy = lds;                  // [C][D]
-    float* Kt = Wy + kBC * D;         // [C][D]
+    constexpr int SDP = 64 * NPL;     // padded LDS row stride of the staged tiles
+    float* Wy = lds;                  // [C][SDP]
+    float* Kt = Wy + kBC * SDP;       // [C][SDP]
+    int slot[NPL];
+    tile_slots<NPL>(slot, D, tid);
+    zero_tile_pads<NPL>(Wy, D, tid);
+    zero_tile_pads<NPL>(Kt, D, tid);
     float w[NPL];
 #pragma unroll
     for (int m = 0; m < NPL; ++m) {
@@ -227,6 +233,17 @@ __global__ __launch_bounds__(64 * kRowWaves) void bwd_fwd_states_kernel(BwdArgs 
         w[m] = (live && a.W0 && p < D) ? a.W0[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
     }
     const int64_t CD = int64_t(kBC) * D;
+    const int n_tile = kBC * D;
+    f32x4 rwy[NPL], rk[NPL];
+    float uy_next = 0.0f;
+#define FWA_BWD_FWD_FETCH(nn)                                                                   \
+    do {                                                                                       \
+        const int64_t uf = int64_t(bh) * a.NC + (nn);                                          \
+        prefetch_tile<NPL>(rwy, a.ws + a.L.wy + uf * CD, n_tile, tid);                         \
+        prefetch_tile<NPL>(rk, a.ws + a.L.kt + uf * CD, n_tile, tid);                          \
+        uy_next = live ? a.ws[a.L.uy + uf * kBC * d_v + (lane >> 1) * d_v + r] : 0.0f;        \
+    } while (0)
+    if (a.NC > 0) FWA_BWD_FWD_FETCH(0);
     for (int n = 0; n < a.NC; ++n) {
         const int64_t u = int64_t(bh) * a.NC + n;
         if (live) {
@@ -235,48 +252,54 @@ __global__ __launch_bounds__(64 * kRowWaves) void bwd_fwd_states_kernel(BwdArgs 
             for (int m = 0; m < NPL; ++m)
                 if (lane + 64 * m < D) gw[lane + 64 * m] = w[m];
         }
-        __syncthreads();
-        stage(Wy, a.ws + a.L.wy + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        stage(Kt, a.ws + a.L.kt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        __syncthreads();
+        lds_barrier();
+        commit_tile<NPL>(Wy, rwy, slot);
+        commit_tile<NPL>(Kt, rk, slot);
+        const float uy = uy_next;
+        lds_barrier();
+        if (n + 1 < a.NC) FWA_BWD_FWD_FETCH(n + 1);
         float part[kBC];
 #pragma unroll
         for (int c = 0; c < kBC; ++c) {
-            float s = 0.0f;
+            float sacc = 0.0f;
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) s += Wy[c * D + lane + 64 * m] * w[m];
-            part[c] = s;
+            for (int m = 0; m < NPL; ++m) sacc += Wy[c * SDP + lane + 64 * m] * w[m];
+            part[c] = sacc;
         }
         const float x = wave_reduce_scatter32(part);          // (Wy w)[lane >> 1]
-        const int cl = lane >> 1;
-        const float uy = live ? a.ws[a.L.uy + u * kBC * d_v + cl * d_v + r] : 0.0f;
         const float uc = uy - x;
-        if (live && (lane & 1) == 0) a.ws[a.L.uu + (u * d_v + r) * kBC + cl] = uc;
+        if (live && (lane & 1) == 0) a.ws[a.L.uu + (u * d_v + r) * kBC + (lane >> 1)] = uc;
 #pragma unroll
         for (int c = 0; c < kBC; ++c) {
             const float uv = lane_value(uc, 2 * c);
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) w[m] += uv * Kt[c * D + lane + 64 * m];
+            for (int m = 0; m < NPL; ++m) w[m] += uv * Kt[c * SDP + lane + 64 * m];
         }
     }
+#undef FWA_BWD_FWD_FETCH
 }
 
 // Chunk-end gradients of the memory, K dW1^T and dW0, chunks in reverse: row r of the
-// gradient moves as g <- g + Q'^T dY[:, r] - Wy^T (K g).
+// gradient moves as g <- g + Q'^T dY[:, r] - Wy^T (K g).  The previous chunk's tiles load into
+// registers while the current chunk computes.
 template <bool BF16, int NPL>
 __global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_v = a.d_v;
     const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
     const int bh = blockIdx.x / rgroups;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
     const bool live = r < d_v;
-    float* Kt = lds;                  // [C][D]
-    float* Qp = Kt + kBC * D;
-    float* Wy = Qp + kBC * D;
+    constexpr int SDP = 64 * NPL;     // padded LDS row stride of the staged tiles
+    float* Kt = lds;                  // [C][SDP]
+    float* Qp = Kt + kBC * SDP;
+    float* Wy = Qp + kBC * SDP;
+    int slot[NPL];
+    tile_slots<NPL>(slot, D, tid);
+    zero_tile_pads<NPL>(Kt, D, tid);
+    zero_tile_pads<NPL>(Qp, D, tid);
+    zero_tile_pads<NPL>(Wy, D, tid);
     float g[NPL];
 #pragma unroll
     for (int m = 0; m < NPL; ++m) {
@@ -284,42 +307,53 @@ __global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs
         g[m] = (live && a.dWf && p < D) ? a.dWf[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
     }
     const int64_t CD = int64_t(kBC) * D;
+    const int n_tile = kBC * D;
+    f32x4 rk[NPL], rq[NPL], rwy[NPL];
+    float dy_next = 0.0f;
+    // dY[c, r] of the fetched chunk in lane c (zero past the end)
+#define FWA_BWD_GRAD_FETCH(nn)                                                                  \
+    do {                                                                                       \
+        const int64_t uf = int64_t(bh) * a.NC + (nn);                                          \
+        prefetch_tile<NPL>(rk, a.ws + a.L.kt + uf * CD, n_tile, tid);                          \
+        prefetch_tile<NPL>(rq, a.ws + a.L.qp + uf * CD, n_tile, tid);                          \
+        prefetch_tile<NPL>(rwy, a.ws + a.L.wy + uf * CD, n_tile, tid);                         \
+        const int tf = (nn) * kBC + lane;                                                      \
+        dy_next = (live && lane < kBC && tf < a.T)                                            \
+                      ? load_elem<BF16>(a.dy, (int64_t(bh) * a.T + tf) * d_v + r) : 0.0f;     \
+    } while (0)
+    if (a.NC > 0) FWA_BWD_GRAD_FETCH(a.NC - 1);
     for (int n = a.NC - 1; n >= 0; --n) {
         const int64_t u = int64_t(bh) * a.NC + n;
-        const int t0 = n * kBC;
         if (live) {
             float* gg = a.ws + a.L.gs + (u * d_v + r) * D;
 #pragma unroll
             for (int m = 0; m < NPL; ++m)
                 if (lane + 64 * m < D) gg[lane + 64 * m] = g[m];
         }
-        // dY[c, r] of this chunk in lane c (zero past the sequence end)
-        float dyc = 0.0f;
-        if (live && lane < kBC && t0 + lane < a.T)
-            dyc = load_elem<BF16>(a.dy, (int64_t(bh) * a.T + t0 + lane) * d_v + r);
-        __syncthreads();
-        stage(Kt, a.ws + a.L.kt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        stage(Qp, a.ws + a.L.qp + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        stage(Wy, a.ws + a.L.wy + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        __syncthreads();
+        lds_barrier();
+        commit_tile<NPL>(Kt, rk, slot);
+        commit_tile<NPL>(Qp, rq, slot);
+        commit_tile<NPL>(Wy, rwy, slot);
+        const float dyc = dy_next;
+        lds_barrier();
+        if (n > 0) FWA_BWD_GRAD_FETCH(n - 1);
         float part[kBC];
 #pragma unroll
         for (int c = 0; c < kBC; ++c) {
-            float s = 0.0f;
+            float sacc = 0.0f;
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) s += Kt[c * D + lane + 64 * m] * g[m];
-            part[c] = s;
+            for (int m = 0; m < NPL; ++m) sacc += Kt[c * SDP + lane + 64 * m] * g[m];
+            part[c] = sacc;
         }
         const float ac = wave_reduce_scatter32(part);         // (K g)[lane >> 1]
         if (live && (lane & 1) == 0) a.ws[a.L.aa + (u * d_v + r) * kBC + (lane >> 1)] = ac;
-#pragma unroll
+        // partly unrolled: a full unroll hoists all 2 * 32 * NPL tile reads and spills at NPL >= 4
+#pragma unroll 4
         for (int c = 0; c < kBC; ++c) {
             const float dy = lane_value(dyc, c), av = lane_value(ac, 2 * c);
 #pragma unroll
             for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D)
-                    g[m] += dy * Qp[c * D + lane + 64 * m] - av * Wy[c * D + lane + 64 * m];
+                g[m] += dy * Qp[c * SDP + lane + 64 * m] - av * Wy[c * SDP + lane + 64 * m];
         }
     }
     if (live && a.dW0) {
@@ -327,6 +361,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs
         for (int m = 0; m < NPL; ++m)
             if (lane + 64 * m < D) a.dW0[(int64_t(bh) * d_v + r) * D + lane + 64 * m] = g[m];
     }
+#undef FWA_BWD_GRAD_FETCH
 }
 
 // ------------------------------------------------------------------------------ 4. chunk grads
@@ -342,7 +377,8 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     const int t0 = n * kBC;
     const int tid = threadIdx.x;
     constexpr int CS = kBC + 1;
-    const int CV = kBC * d_v;
+    const int SV = d_v + 1;           // padded row stride of the [C][d_v] tiles
+    const int CV = kBC * SV;
     float* dYs = lds;                 // [C][d_v]
     float* Us = dYs + CV;             // U
     float* dUs = Us + CV;             // dU
@@ -361,14 +397,17 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     float* Qs = Ks + kBC * kSlice;
 
     const int64_t u64 = u;
-    for (int e = tid; e < CV; e += kPrepThreads2) {
+    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
         const int c = e / d_v, r = e % d_v;
         const bool in = t0 + c < a.T;
         const int64_t g = (int64_t(bh) * a.T + t0 + c) * d_v + r;
-        dYs[e] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
-        Vs[e] = in ? load_elem<BF16>(a.v, g) : 0.0f;
-        Us[e] = a.ws[a.L.uu + (u64 * d_v + r) * kBC + c];
-        dUs[e] = a.ws[a.L.aa + (u64 * d_v + r) * kBC + c];      // K dW1^T, P^T dY added below
+        dYs[c * SV + r] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
+        Vs[c * SV + r] = in ? load_elem<BF16>(a.v, g) : 0.0f;
+    }
+    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {     // [r][c] in the workspace
+        const int r = e / kBC, c = e % kBC;
+        Us[c * SV + r] = a.ws[a.L.uu + u64 * kBC * d_v + e];
+        dUs[c * SV + r] = a.ws[a.L.aa + u64 * kBC * d_v + e];  // K dW1^T, P^T dY added below
     }
     for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
         const int i = e / kBC, j = e % kBC;
@@ -379,19 +418,19 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     if (tid < kBC) be[tid] = a.ws[a.L.be + u64 * kBC + tid];
     __syncthreads();
     // dU = P^T dY + K dW1^T
-    for (int e = tid; e < CV; e += kPrepThreads2) {
+    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
         const int i = e / d_v, r = e % d_v;
-        float s = dUs[e];
-        for (int j = i; j < kBC; ++j) s += Pm[j * CS + i] * dYs[j * d_v + r];
-        dUs[e] = s;
+        float s = dUs[i * SV + r];
+        for (int j = i; j < kBC; ++j) s += Pm[j * CS + i] * dYs[j * SV + r];
+        dUs[i * SV + r] = s;
     }
     __syncthreads();
     // lam = Ainv^T dU; dv = diag(beta) lam
-    for (int e = tid; e < CV; e += kPrepThreads2) {
+    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
         const int i = e / d_v, r = e % d_v;
         float s = 0.0f;
-        for (int j = i; j < kBC; ++j) s += Ai[j * CS + i] * dUs[j * d_v + r];
-        Ls[e] = s;
+        for (int j = i; j < kBC; ++j) s += Ai[j * CS + i] * dUs[j * SV + r];
+        Ls[i * SV + r] = s;
         if (t0 + i < a.T) store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * s);
     }
     __syncthreads();
@@ -400,8 +439,8 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         const int i = e / kBC, j = e % kBC;
         float sp = 0.0f, sz = 0.0f;
         for (int r = 0; r < d_v; ++r) {
-            sp += dYs[i * d_v + r] * Us[j * d_v + r];
-            sz += Ls[i * d_v + r] * Us[j * d_v + r];
+            sp += dYs[i * SV + r] * Us[j * SV + r];
+            sz += Ls[i * SV + r] * Us[j * SV + r];
         }
         dP[i * CS + j] = j <= i ? sp : 0.0f;
         dG[i * CS + j] = j < i ? -be[i] * sz : 0.0f;       // strict lower part for now
@@ -411,7 +450,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     if (tid < kBC) {
         const int i = tid;
         float s = 0.0f;
-        for (int r = 0; r < d_v; ++r) s += Ls[i * d_v + r] * Vs[i * d_v + r];
+        for (int r = 0; r < d_v; ++r) s += Ls[i * SV + r] * Vs[i * SV + r];
         for (int j = 0; j < i; ++j) s -= Gm[i * CS + j] * Ai[i * CS + j];
         bpart[i] = s;
     }
@@ -446,7 +485,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
 #pragma unroll
         for (int e = 0; e < 8; ++e) dq[e] = dk[e] = mm[e] = 0.0f;
         for (int r = 0; r < d_v; ++r) {
-            const float dyv = dYs[i * d_v + r], lv = Ls[i * d_v + r], uv = Us[i * d_v + r];
+            const float dyv = dYs[i * SV + r], lv = Ls[i * SV + r], uv = Us[i * SV + r];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float w0 = W0s[r * kSlice + jq + e];
@@ -580,10 +619,12 @@ bool plan_backward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
 }
 
 static int lds_prep_bytes(int D, int d_k, int d_v) {
-    return 4 * (2 * kBC * 2 * d_k + 2 * kBC * D + 3 * kBC * (kBC + 1) + 3 * kBC + kBC * d_v);
+    return 4 * (2 * kBC * 2 * d_k + 2 * kBC * tile_stride(D) + 3 * kBC * (kBC + 1) + kBC +
+                kBC * d_v);
 }
 static int lds_grads_bytes(int d_v) {
-    return 4 * (5 * kBC * d_v + 5 * kBC * (kBC + 1) + 2 * kBC + 2 * d_v * kSlice + 2 * kBC * kSlice);
+    return 4 * (5 * kBC * (d_v + 1) + 5 * kBC * (kBC + 1) + 2 * kBC + 2 * d_v * kSlice +
+                2 * kBC * kSlice);
 }
 
 template <int NPL, bool BF16>
@@ -592,7 +633,7 @@ static hipError_t launch_rows(const BwdArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(int64_t(a.BH) * rgroups));
     auto kf = bwd_fwd_states_kernel<NPL>;
     auto kg = bwd_grad_states_kernel<BF16, NPL>;
-    const int lf = 4 * 2 * kBC * a.D, lg = 4 * 3 * kBC * a.D;
+    const int lf = 4 * 2 * kBC * 64 * NPL, lg = 4 * 3 * kBC * 64 * NPL;
     hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kf), lf);
     if (e != hipSuccess) return e;
     if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kg), lg)) != hipSuccess) return e;

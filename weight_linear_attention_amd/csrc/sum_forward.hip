@@ -50,7 +50,7 @@ struct SumArgs {
     SumLayout L;
 };
 
-// LDS: x rows of k and q (C x 2 d_k each), K and Q (C x D), M (C x (C + 1)), row sums, V.
+// LDS: x rows of k and q (C x 2 d_k each), K and Q (C x SD, SD = D + 8), M (C x (C + 1)), V.
 template <bool BF16>
 __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     extern __shared__ float lds[];
@@ -61,38 +61,39 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     const int tid = threadIdx.x;
     const int rows = a.T - t0 < kBC ? a.T - t0 : kBC;
     constexpr int CS = kBC + 1;
+    const int SD = tile_stride(D);
     float* xk = lds;
     float* xq = xk + kBC * two;
     float* Kt = xq + kBC * two;
-    float* Qt = Kt + kBC * D;
-    float* Mm = Qt + kBC * D;
-    float* rs = Mm + kBC * CS;
-    float* Vs = rs + 2 * kBC;
+    float* Qt = Kt + kBC * SD;
+    float* Mm = Qt + kBC * SD;
+    float* Vs = Mm + kBC * CS;
     load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
     load_relu_rows<BF16>(a.q, xq, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
     for (int i = tid; i < kBC * d_v; i += kSumThreads) {
         const int c = i / d_v, r = i % d_v;
         Vs[i] = c < rows ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
     }
-    dpfp_tiles(xk, xq, Kt, Qt, rs, D, d_k, tid, kSumThreads);
+    dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
     for (int e = tid; e < kBC * D; e += kSumThreads) {
-        gK[e] = Kt[e];
-        gQ[e] = Qt[e];
+        const int c = e / D, p = e % D;
+        gK[e] = Kt[c * SD + p];
+        gQ[e] = Qt[c * SD + p];
     }
-    // M = lower_incl(Q K^T): thread -> (row c, columns j0..j0+3)
+    // M = lower_incl(Q K^T): thread -> (row c, columns j0 + 8 e, e < 4)
     {
-        const int c = tid / 8, j0 = (tid % 8) * 4;
+        const int c = tid / 8, j0 = tid % 8;
         float m[4] = {0, 0, 0, 0};
         for (int p = 0; p < D; ++p) {
-            const float qc = Qt[c * D + p];
+            const float qc = Qt[c * SD + p];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) m[e] += qc * Kt[(j0 + e) * D + p];
+            for (int e = 0; e < 4; ++e) m[e] += qc * Kt[(j0 + 8 * e) * SD + p];
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Mm[c * CS + j0 + e] = (j0 + e <= c) ? m[e] : 0.0f;
+        for (int e = 0; e < 4; ++e) Mm[c * CS + j0 + 8 * e] = (j0 + 8 * e <= c) ? m[e] : 0.0f;
     }
     __syncthreads();
     float* gN = a.ws + a.L.nm + int64_t(u) * kBC * d_v;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     }
     for (int p = tid; p < D; p += kSumThreads) {
         float s = 0.0f;
-        for (int c = 0; c < kBC; ++c) s += Kt[c * D + p];
+        for (int c = 0; c < kBC; ++c) s += Kt[c * SD + p];
         a.ws[a.L.ks + int64_t(u) * D + p] = s;
     }
 }
@@ -125,18 +126,24 @@ __global__ __launch_bounds__(256) void sum_zfinal_kernel(SumArgs a) {
     }
 }
 
-// Lane l holds w[l + 64 m] (row r of W) and zz[l + 64 m] (z), m < NPL.
+// Lane l holds w[l + 64 m] (row r of W) and zz[l + 64 m] (z), m < NPL.  The next chunk's K
+// and Q tiles load into registers while the current chunk computes.
 template <bool BF16, int NPL>
 __global__ __launch_bounds__(64 * kRowWaves) void sum_scan_kernel(SumArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_v = a.d_v;
     const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
     const int bh = blockIdx.x / rgroups;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
     const bool live = r < d_v;
-    float* Kt = lds;
-    float* Qt = Kt + kBC * D;
+    constexpr int SDP = 64 * NPL;     // padded LDS row stride of the staged tiles
+    float* Kt = lds;                  // [C][SDP]
+    float* Qt = Kt + kBC * SDP;
+    int slot[NPL];
+    tile_slots<NPL>(slot, D, tid);
+    zero_tile_pads<NPL>(Kt, D, tid);
+    zero_tile_pads<NPL>(Qt, D, tid);
     float w[NPL], zz[NPL];
 #pragma unroll
     for (int m = 0; m < NPL; ++m) {
@@ -145,27 +152,40 @@ __global__ __launch_bounds__(64 * kRowWaves) void sum_scan_kernel(SumArgs a) {
         zz[m] = (a.z0 && p < D) ? a.z0[int64_t(bh) * D + p] : 0.0f;
     }
     const int64_t CD = int64_t(kBC) * D;
+    const int n_tile = kBC * D;
+    f32x4 rk[NPL], rq[NPL];
+    float v_next = 0.0f, nm_next = 0.0f, dn_next = 0.0f;
+    // v[t, r] in lane t - t0; the chunk-local parts of row lane >> 1
+#define FWA_SUM_FETCH(nn)                                                                       \
+    do {                                                                                       \
+        const int64_t uf = int64_t(bh) * a.NC + (nn);                                          \
+        prefetch_tile<NPL>(rk, a.ws + a.L.kt + uf * CD, n_tile, tid);                          \
+        prefetch_tile<NPL>(rq, a.ws + a.L.qt + uf * CD, n_tile, tid);                          \
+        const int tf = (nn) * kBC + lane;                                                      \
+        v_next = (live && lane < kBC && tf < a.T)                                             \
+                     ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + tf) * d_v + r) : 0.0f;       \
+        nm_next = live ? a.ws[a.L.nm + (uf * kBC + (lane >> 1)) * d_v + r] : 0.0f;            \
+        dn_next = a.ws[a.L.dn + uf * kBC + (lane >> 1)];                                       \
+    } while (0)
+    if (a.NC > 0) FWA_SUM_FETCH(0);
     for (int n = 0; n < a.NC; ++n) {
-        const int64_t u = int64_t(bh) * a.NC + n;
         const int t0 = n * kBC;
-        float vc = 0.0f;
-        if (live && lane < kBC && t0 + lane < a.T)
-            vc = load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + lane) * d_v + r);
-        __syncthreads();
-        stage(Kt, a.ws + a.L.kt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        stage(Qt, a.ws + a.L.qt + u * CD, kBC * D, threadIdx.x, 64 * kRowWaves);
-        __syncthreads();
+        lds_barrier();
+        commit_tile<NPL>(Kt, rk, slot);
+        commit_tile<NPL>(Qt, rq, slot);
+        const float vc = v_next, nm = nm_next, dn = dn_next;
+        lds_barrier();
+        if (n + 1 < a.NC) FWA_SUM_FETCH(n + 1);
         float pn[kBC], pd[kBC];
 #pragma unroll
         for (int c = 0; c < kBC; ++c) {
             float sn = 0.0f, sd = 0.0f;
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) {
-                    const float qv = Qt[c * D + lane + 64 * m];
-                    sn += qv * w[m];
-                    sd += qv * zz[m];
-                }
+            for (int m = 0; m < NPL; ++m) {
+                const float qv = Qt[c * SDP + lane + 64 * m];
+                sn += qv * w[m];
+                sd += qv * zz[m];
+            }
             pn[c] = sn;
             pd[c] = sd;
         }
@@ -173,28 +193,26 @@ __global__ __launch_bounds__(64 * kRowWaves) void sum_scan_kernel(SumArgs a) {
         const float qz = wave_reduce_scatter32(pd);           // (Q z)[lane >> 1]
         const int c = lane >> 1;
         if (live && (lane & 1) == 0 && t0 + c < a.T) {
-            const float num = qw + a.ws[a.L.nm + (u * kBC + c) * d_v + r];
-            const float den = qz + a.ws[a.L.dn + u * kBC + c];
+            const float num = qw + nm, den = qz + dn;
             store_elem<BF16>(a.y, (int64_t(bh) * a.T + t0 + c) * d_v + r, den != 0.0f ? num / den : 0.0f);
         }
 #pragma unroll
         for (int cc = 0; cc < kBC; ++cc) {
             const float vv = lane_value(vc, cc);
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) {
-                    const float kv = Kt[cc * D + lane + 64 * m];
-                    w[m] += vv * kv;
-                    zz[m] += kv;
-                }
+            for (int m = 0; m < NPL; ++m) {
+                const float kv = Kt[cc * SDP + lane + 64 * m];
+                w[m] += vv * kv;
+                zz[m] += kv;
+            }
         }
     }
 #pragma unroll
     for (int m = 0; m < NPL; ++m) {
         const int p = lane + 64 * m;
-        if (p >= D) continue;
-        if (live && a.Wf) a.Wf[(int64_t(bh) * d_v + r) * D + p] = w[m];
+        if (p < D && live && a.Wf) a.Wf[(int64_t(bh) * d_v + r) * D + p] = w[m];
     }
+#undef FWA_SUM_FETCH
 }
 
 bool plan_sum_forward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
@@ -210,7 +228,7 @@ template <int NPL, bool BF16>
 static hipError_t launch_scan(const SumArgs& a, hipStream_t stream) {
     const int rgroups = (a.d_v + kRowWaves - 1) / kRowWaves;
     auto kern = sum_scan_kernel<BF16, NPL>;
-    const int lds = 4 * 2 * kBC * a.D;
+    const int lds = 4 * 2 * kBC * 64 * NPL;
     hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(int64_t(a.BH) * rgroups)),
@@ -223,7 +241,7 @@ static hipError_t launch_sum_t(const SumArgs& a, hipStream_t stream) {
     const int64_t NU = int64_t(a.BH) * a.NC;
     hipError_t e;
     if (NU > 0) {
-        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * a.D + kBC * (kBC + 1) + 2 * kBC +
+        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * tile_stride(a.D) + kBC * (kBC + 1) +
                             kBC * a.d_v);
         auto kp = sum_prep_kernel<BF16>;
         if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kp), lp)) != hipSuccess) return e;

@@ -62,6 +62,9 @@ typedef enum {
     FWA_ERR_HIP = 3
 } fwa_status;
 
+/* Element types.  Entry points take the value as a plain int `dtype` (any other value is
+ * rejected with FWA_ERR_INVALID_ARG), so a caller may pass what it likes without undefined
+ * behaviour in the library. */
 typedef enum {
     FWA_F32 = 0,
     FWA_BF16 = 1
@@ -87,7 +90,7 @@ typedef enum {
  *   Implemented shapes: d_k in {16, 32, 64, 128}, any valid nu.
  */
 fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
-                    fwa_dtype dtype, hipStream_t stream);
+                    int dtype, hipStream_t stream);
 
 /*
  * fwa_delta_forward -- causal forward of the delta rule over T steps for every (b, h),
@@ -149,7 +152,7 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
 fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
                              const void* beta_logit, const float* W0, void* y, float* W_final,
                              int B, int H, int T, int d_k, int d_v, int nu, int chunk,
-                             fwa_dtype dtype, void* workspace, int64_t workspace_bytes,
+                             int dtype, void* workspace, int64_t workspace_bytes,
                              hipStream_t stream);
 
 /*
@@ -162,7 +165,7 @@ fwa_status fwa_delta_forward(const void* q, const void* k, const void* v,
 fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, const void* v,
                                   const void* beta_logit, const float* W0, void* y,
                                   float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
-                                  int chunk, fwa_dtype dtype, void* workspace,
+                                  int chunk, int dtype, void* workspace,
                                   int64_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -182,7 +185,7 @@ fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, con
 fwa_status fwa_delta_forward_noalloc(const void* q, const void* k, const void* v,
                                      const void* beta_logit, const float* W0, void* y,
                                      float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
-                                     int chunk, fwa_dtype dtype, hipStream_t stream);
+                                     int chunk, int dtype, hipStream_t stream);
 
 /*
  * fwa_delta_forward_info -- which implementation a forward call with `request` (an
@@ -194,7 +197,7 @@ fwa_status fwa_delta_forward_noalloc(const void* q, const void* k, const void* v
  *   Size errors are those the forward gives for the same sizes; outputs are untouched on error.
  */
 fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
-                                  fwa_dtype dtype, int request, int* path,
+                                  int dtype, int request, int* path,
                                   int64_t* workspace_bytes);
 
 /*
@@ -223,7 +226,7 @@ fwa_status fwa_delta_backward(const void* q, const void* k, const void* v,
                               const void* beta_logit, const float* W0, const void* dy,
                               const float* dW_final, void* dq, void* dk, void* dv,
                               void* dbeta_logit, float* dW0, int B, int H, int T, int d_k,
-                              int d_v, int nu, fwa_dtype dtype, void* workspace,
+                              int d_v, int nu, int dtype, void* workspace,
                               int64_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -231,7 +234,7 @@ fwa_status fwa_delta_backward(const void* q, const void* k, const void* v,
  * (0 when B*H == 0), without touching the device.  Size errors are those of the backward.
  */
 fwa_status fwa_delta_backward_info(int B, int H, int T, int d_k, int d_v, int nu,
-                                   fwa_dtype dtype, int64_t* workspace_bytes);
+                                   int dtype, int64_t* workspace_bytes);
 
 /*
  * fwa_sum_forward -- causal sum-update linear attention with the z normaliser over DPFP
@@ -252,11 +255,11 @@ fwa_status fwa_delta_backward_info(int B, int H, int T, int d_k, int d_v, int nu
  */
 fwa_status fwa_sum_forward(const void* q, const void* k, const void* v, const float* W0,
                            const float* z0, void* y, float* W_final, float* z_final, int B, int H,
-                           int T, int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                           int T, int d_k, int d_v, int nu, int dtype, void* workspace,
                            int64_t workspace_bytes, hipStream_t stream);
 
 /* fwa_sum_forward_info -- workspace bytes fwa_sum_forward needs (0 when B*H == 0). */
-fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, fwa_dtype dtype,
+fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int dtype,
                                 int64_t* workspace_bytes);
 
 /*
@@ -271,7 +274,7 @@ fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, f
  */
 fwa_status fwa_layer_project(const void* x, const void* W_qkvb, void* q, void* k, void* v,
                              void* beta_logit, int B, int T, int d_model, int H, int d_k, int d_v,
-                             fwa_dtype dtype, hipStream_t stream);
+                             int dtype, hipStream_t stream);
 
 /*
  * fwa_layer_output -- the output map behind the layer, reading its head-split output:
@@ -284,7 +287,7 @@ fwa_status fwa_layer_project(const void* x, const void* W_qkvb, void* q, void* k
  */
 fwa_status fwa_layer_output(const void* y, const void* W_o, const void* b_o,
                             const void* residual, void* out, int B, int T, int H, int d_v,
-                            int d_model, fwa_dtype dtype, hipStream_t stream);
+                            int d_model, int dtype, hipStream_t stream);
 
 /*
  * fwa_decode_layers -- one new token through L fast-weight attention layers, each with its
@@ -302,12 +305,12 @@ fwa_status fwa_layer_output(const void* y, const void* W_o, const void* b_o,
  */
 fwa_status fwa_decode_layers(void* x, int L, const void* const* W_qkvb, const void* const* W_o,
                              const void* const* b_o, float* const* W, int B, int d_model, int H,
-                             int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                             int d_k, int d_v, int nu, int dtype, void* workspace,
                              int64_t workspace_bytes, hipStream_t stream);
 
 /* fwa_decode_layers_info -- workspace bytes fwa_decode_layers needs. */
 fwa_status fwa_decode_layers_info(int B, int d_model, int H, int d_k, int d_v, int nu,
-                                  fwa_dtype dtype, int64_t* workspace_bytes);
+                                  int dtype, int64_t* workspace_bytes);
 
 /*
  * fwa_delta_step -- one decode step (a single new token) for every (b, h), with the memory
@@ -325,7 +328,7 @@ fwa_status fwa_decode_layers_info(int B, int d_model, int H, int d_k, int d_v, i
  */
 fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,
                           float* W, void* y, int B, int H, int d_k, int d_v, int nu,
-                          fwa_dtype dtype, hipStream_t stream);
+                          int dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* fwa_status_string(fwa_status s);

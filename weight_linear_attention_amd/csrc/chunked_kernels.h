@@ -888,7 +888,7 @@ template <bool BF16, int C, int NDP>
 __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a) {
     using LT = typename ChunkTypes<BF16>::LT;
     using SL = StagedLayout<BF16, C, NDP>;
-    constexpr int pair = SL::pair, NT = SL::NT, NTB = SL::NTB, ND = SL::ND, NDB = SL::NDB;
+    constexpr int pair = SL::pair, NT = SL::NT, NTB = SL::NTB, NDB = SL::NDB;
     constexpr int NDPB = NDP / pair;
     static_assert(NDP % pair == 0, "bf16 waves hold whole d-tile pairs");
     extern __shared__ __attribute__((aligned(1024))) char smem[];

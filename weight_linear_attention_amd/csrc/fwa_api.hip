@@ -46,8 +46,8 @@ Span span(const void* p, int64_t bytes) {
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
-bool valid_dtype(fwa_dtype d) { return d == FWA_F32 || d == FWA_BF16; }
-int elem_bytes(fwa_dtype d) { return d == FWA_BF16 ? 2 : 4; }
+bool valid_dtype(int d) { return d == FWA_F32 || d == FWA_BF16; }
+int elem_bytes(int d) { return d == FWA_BF16 ? 2 : 4; }
 
 // a * b * c ... <= limit without overflow (all factors >= 0)
 bool mul_le(int64_t limit, std::initializer_list<int64_t> fs) {
@@ -89,7 +89,7 @@ const char* fwa_last_error(void) { return g_last_error.c_str(); }
 
 int fwa_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
-fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, fwa_dtype dtype,
+fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu, int dtype,
                     hipStream_t stream) {
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: unknown dtype %d", dtype);
     if (n_vec < 0) return fail(FWA_ERR_INVALID_ARG, "fwa_dpfp: n_vec < 0");
@@ -118,7 +118,7 @@ namespace {
 
 // Checks of the sizes shared by fwa_delta_forward and fwa_delta_forward_info.
 fwa_status check_forward_sizes(const char* fn, int B, int H, int T, int d_k, int d_v, int nu,
-                               int chunk, fwa_dtype dtype) {
+                               int chunk, int dtype) {
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || H < 0 || T < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H/T", fn);
     if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
@@ -195,7 +195,7 @@ fwa_status choose_forward(const char* fn, int request, int BH, int T, int d_k, i
 fwa_status check_forward_call(const char* fn, int request, const void* q, const void* k,
                               const void* v, const void* beta_logit, const float* W0,
                               const void* y, const float* W_final, int B, int H, int T, int d_k,
-                              int d_v, int nu, int chunk, fwa_dtype dtype, const void* workspace,
+                              int d_v, int nu, int chunk, int dtype, const void* workspace,
                               int64_t workspace_bytes, ForwardChoice* c,
                               bool check_workspace = true) {
     fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
@@ -276,7 +276,7 @@ fwa_status launch_forward(const ForwardChoice& c, const void* q, const void* k, 
 extern "C" {
 
 fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int chunk,
-                                  fwa_dtype dtype, int request, int* path,
+                                  int dtype, int request, int* path,
                                   int64_t* workspace_bytes) {
     const char* fn = "fwa_delta_forward_info";
     fwa_status st = check_forward_sizes(fn, B, H, T, d_k, d_v, nu, chunk, dtype);
@@ -304,7 +304,7 @@ fwa_status fwa_delta_forward_info(int B, int H, int T, int d_k, int d_v, int nu,
 fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, const void* v,
                                   const void* beta_logit, const float* W0, void* y,
                                   float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
-                                  int chunk, fwa_dtype dtype, void* workspace,
+                                  int chunk, int dtype, void* workspace,
                                   int64_t workspace_bytes, hipStream_t stream) {
     const char* fn = "fwa_delta_forward";
     ForwardChoice c;
@@ -317,7 +317,7 @@ fwa_status fwa_delta_forward_path(int request, const void* q, const void* k, con
 
 fwa_status fwa_delta_forward(const void* q, const void* k, const void* v, const void* beta_logit,
                              const float* W0, void* y, float* W_final, int B, int H, int T,
-                             int d_k, int d_v, int nu, int chunk, fwa_dtype dtype,
+                             int d_k, int d_v, int nu, int chunk, int dtype,
                              void* workspace, int64_t workspace_bytes, hipStream_t stream) {
     return fwa_delta_forward_path(FWA_PATH_AUTO, q, k, v, beta_logit, W0, y, W_final, B, H, T,
                                   d_k, d_v, nu, chunk, dtype, workspace, workspace_bytes, stream);
@@ -362,7 +362,7 @@ extern "C" {
 fwa_status fwa_delta_forward_noalloc(const void* q, const void* k, const void* v,
                                      const void* beta_logit, const float* W0, void* y,
                                      float* W_final, int B, int H, int T, int d_k, int d_v, int nu,
-                                     int chunk, fwa_dtype dtype, hipStream_t stream) {
+                                     int chunk, int dtype, hipStream_t stream) {
     const char* fn = "fwa_delta_forward_noalloc";
     ForwardChoice c;
     fwa_status st = check_forward_call(fn, FWA_PATH_AUTO, q, k, v, beta_logit, W0, y, W_final, B,
@@ -396,7 +396,7 @@ fwa_status fwa_delta_forward_noalloc(const void* q, const void* k, const void* v
 namespace {
 
 fwa_status check_backward_shape(const char* fn, int B, int H, int T, int d_k, int d_v, int nu,
-                                fwa_dtype dtype, int64_t* ws_bytes) {
+                                int dtype, int64_t* ws_bytes) {
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || H < 0 || T < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H/T", fn);
     if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
@@ -424,7 +424,7 @@ fwa_status check_backward_shape(const char* fn, int B, int H, int T, int d_k, in
 extern "C" {
 
 fwa_status fwa_delta_backward_info(int B, int H, int T, int d_k, int d_v, int nu,
-                                   fwa_dtype dtype, int64_t* workspace_bytes) {
+                                   int dtype, int64_t* workspace_bytes) {
     int64_t ws = 0;
     const fwa_status st = check_backward_shape("fwa_delta_backward_info", B, H, T, d_k, d_v, nu,
                                                dtype, &ws);
@@ -437,7 +437,7 @@ fwa_status fwa_delta_backward(const void* q, const void* k, const void* v,
                               const void* beta_logit, const float* W0, const void* dy,
                               const float* dW_final, void* dq, void* dk, void* dv,
                               void* dbeta_logit, float* dW0, int B, int H, int T, int d_k,
-                              int d_v, int nu, fwa_dtype dtype, void* workspace,
+                              int d_v, int nu, int dtype, void* workspace,
                               int64_t workspace_bytes, hipStream_t stream) {
     const char* fn = "fwa_delta_backward";
     int64_t need = 0;
@@ -481,7 +481,7 @@ fwa_status fwa_delta_backward(const void* q, const void* k, const void* v,
 namespace {
 
 fwa_status check_sum_shape(const char* fn, int B, int H, int T, int d_k, int d_v, int nu,
-                           fwa_dtype dtype, int64_t* ws_bytes) {
+                           int dtype, int64_t* ws_bytes) {
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || H < 0 || T < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H/T", fn);
     if (d_k < 1 || d_v < 1) return fail(FWA_ERR_INVALID_ARG, "%s: d_k and d_v must be >= 1", fn);
@@ -508,7 +508,7 @@ fwa_status check_sum_shape(const char* fn, int B, int H, int T, int d_k, int d_v
 
 extern "C" {
 
-fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, fwa_dtype dtype,
+fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, int dtype,
                                 int64_t* workspace_bytes) {
     int64_t ws = 0;
     const fwa_status st = check_sum_shape("fwa_sum_forward_info", B, H, T, d_k, d_v, nu, dtype, &ws);
@@ -519,7 +519,7 @@ fwa_status fwa_sum_forward_info(int B, int H, int T, int d_k, int d_v, int nu, f
 
 fwa_status fwa_sum_forward(const void* q, const void* k, const void* v, const float* W0,
                            const float* z0, void* y, float* W_final, float* z_final, int B, int H,
-                           int T, int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                           int T, int d_k, int d_v, int nu, int dtype, void* workspace,
                            int64_t workspace_bytes, hipStream_t stream) {
     const char* fn = "fwa_sum_forward";
     int64_t need = 0;
@@ -565,7 +565,7 @@ fwa_status fwa_sum_forward(const void* q, const void* k, const void* v, const fl
 namespace {
 
 fwa_status check_linear_dims(const char* fn, int B, int T, int d_model, int H, int d_k, int d_v,
-                             fwa_dtype dtype) {
+                             int dtype) {
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || T < 0 || H < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/T/H", fn);
     if (d_model < 1 || d_k < 1 || d_v < 1)
@@ -586,7 +586,7 @@ extern "C" {
 
 fwa_status fwa_layer_project(const void* x, const void* W_qkvb, void* q, void* k, void* v,
                              void* beta_logit, int B, int T, int d_model, int H, int d_k, int d_v,
-                             fwa_dtype dtype, hipStream_t stream) {
+                             int dtype, hipStream_t stream) {
     const char* fn = "fwa_layer_project";
     fwa_status st = check_linear_dims(fn, B, T, d_model, H, d_k, d_v, dtype);
     if (st != FWA_OK) return st;
@@ -615,7 +615,7 @@ fwa_status fwa_layer_project(const void* x, const void* W_qkvb, void* q, void* k
 
 fwa_status fwa_layer_output(const void* y, const void* W_o, const void* b_o,
                             const void* residual, void* out, int B, int T, int H, int d_v,
-                            int d_model, fwa_dtype dtype, hipStream_t stream) {
+                            int d_model, int dtype, hipStream_t stream) {
     const char* fn = "fwa_layer_output";
     fwa_status st = check_linear_dims(fn, B, T, d_model, H, 8, d_v, dtype);
     if (st != FWA_OK) return st;
@@ -639,7 +639,7 @@ fwa_status fwa_layer_output(const void* y, const void* W_o, const void* b_o,
 }
 
 fwa_status fwa_decode_layers_info(int B, int d_model, int H, int d_k, int d_v, int nu,
-                                  fwa_dtype dtype, int64_t* workspace_bytes) {
+                                  int dtype, int64_t* workspace_bytes) {
     const char* fn = "fwa_decode_layers_info";
     fwa_status st = check_linear_dims(fn, B, 1, d_model, H, d_k, d_v, dtype);
     if (st != FWA_OK) return st;
@@ -655,7 +655,7 @@ fwa_status fwa_decode_layers_info(int B, int d_model, int H, int d_k, int d_v, i
 
 fwa_status fwa_decode_layers(void* x, int L, const void* const* W_qkvb, const void* const* W_o,
                              const void* const* b_o, float* const* W, int B, int d_model, int H,
-                             int d_k, int d_v, int nu, fwa_dtype dtype, void* workspace,
+                             int d_k, int d_v, int nu, int dtype, void* workspace,
                              int64_t workspace_bytes, hipStream_t stream) {
     const char* fn = "fwa_decode_layers";
     int64_t need = 0;
@@ -721,7 +721,7 @@ fwa_status fwa_decode_layers(void* x, int L, const void* const* W_qkvb, const vo
 
 fwa_status fwa_delta_step(const void* q, const void* k, const void* v, const void* beta_logit,
                           float* W, void* y, int B, int H, int d_k, int d_v, int nu,
-                          fwa_dtype dtype, hipStream_t stream) {
+                          int dtype, hipStream_t stream) {
     const char* fn = "fwa_delta_step";
     if (!valid_dtype(dtype)) return fail(FWA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || H < 0) return fail(FWA_ERR_INVALID_ARG, "%s: negative B/H", fn);

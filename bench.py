@@ -96,13 +96,15 @@ def kernel_source_hash(unit):
 def stream_kernels(w):
     """Kernel names of the streaming path for this shape, by the planner's rule (chunk 128: the
     shift-sliced prep and serial kernels; chunk 64: the sliced prep for d_k 64 and nu <= 4, then
-    the full-tile serial kernel where it applies, else the sliced one)."""
+    the pipelined serial kernel for d_k 64 and nu <= 3, the full-tile one where it applies, else
+    the sliced one)."""
     sliced_prep = w.d_k == 64 and w.nu <= 4
     full_ok = w.chunk == 64 and w.d_v % 32 == 0 and w.D % 128 == 0 and w.nu <= 8 and w.D <= 384
     if w.chunk == 128 or not full_ok:
         return "delta_prep_sliced_kernel + delta_stream_sliced_kernel"
+    serial = "delta_stream_pipe_kernel" if w.d_k == 64 and w.nu <= 3 else "delta_stream_kernel"
     return ("delta_prep_sliced_kernel" if sliced_prep else "delta_prep_kernel (compact)") + \
-        " + delta_stream_kernel"
+        " + " + serial
 
 
 def chunked_kernels(w):

@@ -102,6 +102,7 @@ struct StreamPlan {
     int ndw;             // d-tiles of W^T per wave (of 8)
     bool sliced_prep;    // prep with shift-sliced K and Q tiles (d_k = 64, nu <= 4)
     bool sliced_stream;  // serial kernel with shift-sliced K and Q tiles (chunk 64 or 128)
+    bool pipe;           // pipelined serial kernel (d_k = 64, nu <= 3, chunk 64)
     int64_t ws_bytes;
 };
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan);

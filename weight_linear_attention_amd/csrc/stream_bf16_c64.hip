@@ -10,12 +10,11 @@ static int align16s(int x) { return (x + 15) & ~15; }
 constexpr int kMaxLdsStream = 160 * 1024;
 
 // Which kernels the streaming path runs.  Chunk 128 takes the shift-sliced kernels (d_k = 64,
-// nu <= 4).  Chunk 64 takes the 32-column full-tile serial kernel, with the sliced prep for
-// d_k = 64 and nu <= 4 and the full-tile compact prep otherwise; shapes that serial kernel does
-// not take (d_v 16, D 512) fall back to the sliced serial kernel with 16-column workgroups.  On
-// the 8 x 16 x 16384 (D 384) forward the full-tile kernel takes 1.45 ms and the sliced one
-// 2.5 ms: the sliced one builds the DPFP tiles three times per chunk and column group (K and Q,
-// then K again) and is bound by that VALU work, so it is only the fallback.
+// nu <= 4).  Chunk 64 takes a 32-column serial kernel: the pipelined one for d_k = 64 and
+// nu <= 3, the full-tile one for d_k 16 and 32, with the sliced prep for d_k = 64 and nu <= 4
+// and the full-tile compact prep otherwise; shapes neither serial kernel takes (d_v 16, D 512)
+// fall back to the sliced serial kernel with 16-column workgroups, which builds the DPFP tiles
+// three times per chunk and column group and is bound by that VALU work.
 static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, StreamPlan* plan);
 
 bool plan_stream(int BH, int T, int d_k, int d_v, int nu, int C, bool bf16, StreamPlan* plan) {
@@ -63,6 +62,30 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
     a.s_u = off;
     off += 8 * 1024;
     if (off > kMaxLdsStream) return false;
+    plan->pipe = false;
+    if (d_k == 64 && nu <= 3) {
+        // pipelined kernel: two K tiles, W^T copy, Z, U and Q W^T exchange tiles, y and v rows
+        int o = 0;
+        a.s_k = o;
+        o = align16s(o + C * a.krs * 2);
+        a.s_q = o;
+        o = align16s(o + C * a.krs * 2);
+        a.s_wt = o;
+        o += (D / 32) * 2 * 1024;
+        a.s_z = o;
+        o += 8 * 1024;
+        a.s_u = o;
+        o += 8 * 1024;
+        a.s_raw = o;
+        o += 8 * 1024;
+        a.s_y = o;
+        o += C * 32 * 2;
+        a.s_voff = o;
+        o += C * 32 * 2;
+        if (o > kMaxLdsStream) return false;
+        off = o;
+        plan->pipe = true;
+    }
     plan->C = C;
     plan->lds_prep = cp.lds_prep;
     plan->sliced_prep = false;
@@ -79,6 +102,16 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
     plan->ndw = D / 128;
     plan->ws_bytes = a.o_rq + NU * szR;
     return true;
+}
+
+template <int NU>
+static hipError_t launch_stream_pipe(const StreamPlan& p, hipStream_t stream) {
+    auto kern = delta_stream_pipe_kernel<NU>;
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_stream);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.args.BH) * (p.args.d_v / 32)));
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kStreamWaves), p.lds_stream, stream, p.args);
+    return hipGetLastError();
 }
 
 template <int NDW>
@@ -103,6 +136,14 @@ hipError_t launch_stream_c64(const StreamPlan& p, hipStream_t stream) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads), p.lds_prep, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (p.pipe) {
+        switch (a.nu) {
+            case 1: return launch_stream_pipe<1>(p, stream);
+            case 2: return launch_stream_pipe<2>(p, stream);
+            case 3: return launch_stream_pipe<3>(p, stream);
+            default: return hipErrorInvalidValue;
+        }
     }
     switch (p.ndw) {
         case 1: return launch_stream_ndw<1>(p, stream);

@@ -282,6 +282,313 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
     }
 }
 
+// Pipelined serial pass for d_k = 64, nu <= 3 (D = 128 nu): the same chunk algebra as
+// delta_stream_kernel, with the DPFP work taken off the serial critical path.
+//   * Q is never stored: each wave builds its A operands of Q in registers from the raw q rows
+//     (lane l16 of a row tile, positions j0 .. j0+3 of one shift block per 32-deep k-step) and
+//     forms a partial Q W^T over half of the k-steps, for both column tiles; the two waves of a
+//     row tile swap the halves they do not own through LDS.
+//   * K is double-buffered: the K tile of chunk n + 1 is built in phase C of chunk n, where the
+//     SIMDs otherwise wait on the short U products and the barrier, instead of in a phase of
+//     its own.  (Built in phase B, between the X and Q W^T products, it measured slower: the
+//     compiler does not interleave it, and split by shift it costs registers.)  The prep results of chunk n + 1 are loaded as soon as chunk n's are dead (after
+//     the memory update), a whole chunk ahead of their use.
+//   * The W^T copy is written in the canonical B-operand layout (lane L, slot s = k-row
+//     8 (L / 16) + s of the block, column L % 16), so the K operand of X = K W^T is one 16-byte
+//     LDS read per k-step, and the register-built Q operand uses the same k order.
+// Wave w owns row tile rt = w % 4 and column tile / Q half h = w / 4.  Per chunk:
+//   B  X = K W^T for tile (rt, h) over all of D; partial Q W^T over k-steps 4 p + 2 h + e
+//      (both column tiles); Z = V - rho_k o X to LDS, the partner's partial to LDS.
+//   C  U tile (rt, h) = A'' Z; Q W^T tile (rt, h) = own + partner partial, times rho_q; the
+//      next chunk's K tile (one DPFP task per thread) and v columns.
+//   D  Y tile (rt, h) = rho_q o Q W^T + P~ U; the memory tiles += K^T (rho_k o U); the W^T
+//      copy.
+// Three LDS-only barriers per chunk.  Global loads are issued by every lane in every chunk with
+// clamped addresses (masked after arrival), so the compiler's in-order wait counts stay exact.
+template <int NU>
+__global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) {
+    constexpr int C = 64, DK = 64, NDW = NU, NTB = 2;
+    static_assert(NU >= 1 && NU <= 3, "window index 4 + f - i stays in 0 .. 7");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = l & 15, g4 = l >> 4;
+    const int d_v = a.d_v, D = a.D, T = a.T, NC = a.NC, krs = a.krs;
+    const int NP = d_v / 32;
+    const BhIndex bi = xcd_local(blockIdx.x, a.BH, NP);
+    const int bh = bi.bh, col0 = 32 * static_cast<int>(bi.i);
+    const int rt = w & 3, h = w >> 2;
+
+    u16* const Kb0 = reinterpret_cast<u16*>(smem + a.s_k);
+    u16* const Kb1 = reinterpret_cast<u16*>(smem + a.s_q);
+    char* const WT = smem + a.s_wt;
+    float* const Zb = reinterpret_cast<float*>(smem + a.s_z);
+    float* const Ub = reinterpret_cast<float*>(smem + a.s_u);
+    float* const Xq = reinterpret_cast<float*>(smem + a.s_raw);    // Q W^T partials exchanged
+    u16* const Yb = reinterpret_cast<u16*>(smem + a.s_y);          // [C][32] bf16
+    u16* const Vr = reinterpret_cast<u16*>(smem + a.s_voff);       // [C][32] bf16
+    auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
+
+    // ---- memory tiles: d-tile w + 8 s, column tile c (rows d = 16 dt + 4 g4 + e, column l16)
+    f32x4 Wst[NDW][2];
+#pragma unroll
+    for (int s = 0; s < NDW; ++s)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            Wst[s][c] = zero4();
+            if (a.W0) {
+                const float* src = a.W0 + (static_cast<int64_t>(bh) * d_v + col0 + 16 * c + l16) * D +
+                                   orig_col(16 * (w + 8 * s) + 4 * g4, DK);
+                const float2 lo = *reinterpret_cast<const float2*>(src);
+                const float2 hi = *reinterpret_cast<const float2*>(src + DK);
+                Wst[s][c] = f32x4{lo.x, hi.x, lo.y, hi.y};
+            }
+        }
+    // the memory tiles as bf16 B blocks of W^T: block jb = dt / 2, lane 16 (2 (dt & 1) + g4 / 2)
+    // + l16, slots 4 (g4 & 1) .. + 3
+    auto write_wt = [&]() {
+#pragma unroll
+        for (int s = 0; s < NDW; ++s) {
+            const int dt = w + 8 * s;
+            const int lp = 16 * (2 * (dt & 1) + (g4 >> 1)) + l16;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                *reinterpret_cast<uint2*>(WT + (((dt >> 1) * 2 + c) * 64 + lp) * 16 + 8 * (g4 & 1)) =
+                    make_uint2(pack_bf16x2(Wst[s][c][0], Wst[s][c][1]), pack_bf16x2(Wst[s][c][2], Wst[s][c][3]));
+        }
+    };
+    auto wblk = [&](int jb, int c) {
+        return as_bf16x8(*reinterpret_cast<const uint4*>(WT + ((jb * 2 + c) * 64 + l) * 16));
+    };
+
+    // ---- raw inputs.  K task of this thread: row tid / 8, positions 8 (tid % 8) .. + 7 and the
+    //      8 positions before them (cyclically); the v columns as before; the Q windows of the
+    //      wave's row tile: q[j0 - 4 .. j0 + 3] for j0 = 16 (2 h + e) + 4 g4, e = 0, 1
+    const int64_t row0 = static_cast<int64_t>(bh) * T;
+    const u16* kB = static_cast<const u16*>(a.k) + row0 * DK;
+    const u16* qB = static_cast<const u16*>(a.q) + row0 * DK;
+    const u16* vB = static_cast<const u16*>(a.v) + row0 * d_v + col0;
+    const int ktr = tid >> 3, kjg = tid & 7;
+    uint4 ka, kp, rv;
+    uint32_t mk = 0u, mv = 0u;
+    auto load_k = [&](int n) {
+        const int t0 = n * C, Cn = min(C, T - t0);
+        const bool ok = ktr < Cn;
+        const u16* r = kB + static_cast<int64_t>(t0 + (ok ? ktr : 0)) * DK;
+        ka = *reinterpret_cast<const uint4*>(r + 8 * kjg);
+        kp = *reinterpret_cast<const uint4*>(r + 8 * ((kjg + 7) & 7));
+        mk = ok ? 0xffffffffu : 0u;
+        const bool okv = tid < 4 * C && (tid >> 2) < Cn;
+        rv = *reinterpret_cast<const uint4*>(vB + static_cast<int64_t>(t0 + (okv ? tid >> 2 : 0)) * d_v +
+                                             (okv ? 8 * (tid & 3) : 0));
+        mv = okv ? 0xffffffffu : 0u;
+    };
+    uint2 qlo[2], qhi[2];
+    auto load_q = [&](int n) {
+        const int t0 = n * C, Cn = min(C, T - t0);
+        const int rr = 16 * rt + l16;
+        const u16* r = qB + static_cast<int64_t>(t0 + (rr < Cn ? rr : 0)) * DK;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int j0 = 16 * (2 * h + e) + 4 * g4;
+            qlo[e] = *reinterpret_cast<const uint2*>(r + ((j0 + DK - 4) & (DK - 1)));
+            qhi[e] = *reinterpret_cast<const uint2*>(r + j0);
+        }
+    };
+    // the next chunk's K tile: one DPFP task per thread (rows past the end zero)
+    auto build_k = [&](u16* Kn) {
+        const uint32_t ak[4] = {ka.x & mk, ka.y & mk, ka.z & mk, ka.w & mk};
+        const uint32_t pk[4] = {kp.x & mk, kp.y & mk, kp.z & mk, kp.w & mk};
+        float a8[8], p8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a8[2 * e] = __uint_as_float(ak[e] << 16);
+            a8[2 * e + 1] = __uint_as_float(ak[e] & 0xffff0000u);
+            p8[2 * e] = __uint_as_float(pk[e] << 16);
+            p8[2 * e + 1] = __uint_as_float(pk[e] & 0xffff0000u);
+        }
+        dpfp_task<u16, NU>(a8, p8, 8 * kjg, DK, Kn + ktr * krs);
+    };
+    auto store_v = [&]() {
+        if (tid < 4 * C)
+            reinterpret_cast<uint4*>(Vr)[tid] = make_uint4(rv.x & mv, rv.y & mv, rv.z & mv, rv.w & mv);
+    };
+
+    // ---- per-chunk results of the prep kernel (as in delta_stream_kernel)
+    uint4 ah[NTB], al[NTB], pa[NTB];
+    f32x4 rka[4], rkc, rqv;
+    auto load_ws = [&](int n) {
+        const int64_t u = static_cast<int64_t>(bh) * NC + n;
+        const char* ahp = a.ws + a.o_ah + u * (C * C * 2);
+        const char* alp = a.ws + a.o_al + u * (C * C * 2);
+        const char* pap = a.ws + a.o_pa + u * (C * C * 2);
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, rt * NTB + j, l));
+            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, rt * NTB + j, l));
+            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, rt * NTB + j, l));
+        }
+        const float* rk = reinterpret_cast<const float*>(a.ws + a.o_rk) + u * C;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) rka[tt] = *reinterpret_cast<const f32x4*>(rk + 16 * tt + 4 * g4);
+        rkc = *reinterpret_cast<const f32x4*>(rk + 16 * rt + 4 * g4);
+        rqv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rq) + u * C + 16 * rt + 4 * g4);
+    };
+
+    if (NC > 0) {
+        load_k(0);
+        load_q(0);
+        load_ws(0);
+        write_wt();
+        build_k(Kb0);
+        store_v();
+        load_k(NC > 1 ? 1 : 0);
+    }
+    lds_barrier();
+
+    const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0), (T * d_v - col0) * 2,
+        kBufferWord3);
+    for (int n = 0; n < NC; ++n) {
+        const int t0 = n * C;
+        const int nn = n + 1 < NC ? n + 1 : n;
+        const int n2 = n + 2 < NC ? n + 2 : NC - 1;
+        const u16* Kc = (n & 1) ? Kb1 : Kb0;
+        u16* Kn = (n & 1) ? Kb0 : Kb1;
+
+        // ---- B: X tile (rt, h), partial Q W^T (rt, both), Z
+        f32x4 xa = zero4(), xb = zero4(), qo = zero4(), qx = zero4();
+        {
+            // window values as fp32 positive / negative parts; for the lane whose window starts
+            // at position 0 the four values before it wrap into the [-k] half, so their roles as
+            // the rolled factor swap
+            float Pw[2][8], Nw[2][8];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t wd[4] = {qlo[e].x, qlo[e].y, qhi[e].x, qhi[e].y};
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const float r = (m & 1) ? __uint_as_float(wd[m >> 1] & 0xffff0000u)
+                                            : __uint_as_float(wd[m >> 1] << 16);
+                    Pw[e][m] = relu_f(r);
+                    Nw[e][m] = Pw[e][m] - r;
+                }
+            }
+            const bool wrap = h == 0 && g4 == 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float p0 = Pw[0][m], n0 = Nw[0][m];
+                Pw[0][m] = wrap ? n0 : p0;
+                Nw[0][m] = wrap ? p0 : n0;
+            }
+            const u16* kr = Kc + (16 * rt + l16) * krs + 8 * g4;
+#pragma unroll
+            for (int p = 0; p < NU; ++p)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int jo = 4 * p + 2 * h + e, jx = 4 * p + 2 - 2 * h + e;
+                    const bf16x8 k_o = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 32 * jo));
+                    const bf16x8 k_x = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 32 * jx));
+                    const bf16x8 w_oh = wblk(jo, h), w_xh = wblk(jx, h), w_oo = wblk(jo, 1 - h);
+                    // A operand of Q for k-step jo: slot 2 f + s = position j0 + f of shift p + 1,
+                    // half s (s = 0: relu(q_j) times the rolled factor, s = 1: relu(-q_j) times it)
+                    bf16x8 qa;
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        const int m = 4 + f - (p + 1);
+                        qa[2 * f] = static_cast<__bf16>(Pw[e][4 + f] * Pw[e][m]);
+                        qa[2 * f + 1] = static_cast<__bf16>(Nw[e][4 + f] * Nw[e][m]);
+                    }
+                    xa = mfma_bf16_k32(k_o, w_oh, xa);
+                    xb = mfma_bf16_k32(k_x, w_xh, xb);
+                    qo = mfma_bf16_k32(qa, w_oh, qo);
+                    qx = mfma_bf16_k32(qa, w_oo, qx);
+                }
+        }
+        load_q(nn);
+        xa += xb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            xa[e] = bf16_bits_to_f32(Vr[(16 * rt + 4 * g4 + e) * 32 + 16 * h + l16]) - rkc[e] * xa[e];
+        *tile(Zb, rt, h) = xa;
+        *tile(Xq, rt, 1 - h) = qx;
+        lds_barrier();                                           // B2
+
+        // ---- C: U tile (rt, h) = A'' Z; the full Q W^T tile
+        {
+            f32x4 u = zero4();
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > rt) break;                            // A'' is zero above the diagonal
+                const f32x4 z0 = *tile(Zb, 2 * j, h), z1 = *tile(Zb, 2 * j + 1, h);
+                const bf16x8 zh = as_bf16x8(pack_bf16x8(z0, z1));
+                const bf16x8 zl = as_bf16x8(bf16_lo_part(z0, z1));
+                u = mfma_bf16_k32(as_bf16x8(ah[j]), zh, u);
+                u = mfma_bf16_k32(as_bf16x8(ah[j]), zl, u);
+                u = mfma_bf16_k32(as_bf16x8(al[j]), zh, u);
+            }
+            *tile(Ub, rt, h) = u;
+        }
+        const f32x4 qacc = (qo + *tile(Xq, rt, h)) * rqv;
+        // the next chunk's K tile and v columns (buffers last read in the previous chunk and in
+        // phase B), then the loads of the chunk after it
+        build_k(Kn);
+        store_v();
+        load_k(n2);
+        lds_barrier();                                           // B3
+
+        // ---- D: Y tile (rt, h), memory update, W^T copy
+        {
+            f32x4 y = qacc;
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                if (2 * j > rt) break;
+                const bf16x8 ub = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, h), *tile(Ub, 2 * j + 1, h)));
+                y = mfma_bf16_k32(as_bf16x8(pa[j]), ub, y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Yb[(16 * rt + 4 * g4 + e) * 32 + 16 * h + l16] = f32_to_bf16_bits(y[e]);
+        }
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            const bf16x8 ub0 = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, 0) * rka[2 * j], *tile(Ub, 2 * j + 1, 0) * rka[2 * j + 1]));
+            const bf16x8 ub1 = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, 1) * rka[2 * j], *tile(Ub, 2 * j + 1, 1) * rka[2 * j + 1]));
+            const u16* kt = Kc + (32 * j + 4 * g4 + (l16 >> 2)) * krs + 4 * (l16 & 3);
+#pragma unroll
+            for (int s = 0; s < NDW; ++s) {
+                const u16* kc = kt + 16 * (w + 8 * s);
+                const bf16x4 c0 = lds_read_tr_b16x4(kc);
+                const bf16x4 c1 = lds_read_tr_b16x4(kc + 16 * krs);
+                const bf16x8 kta = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                Wst[s][0] = mfma_bf16_k32(kta, ub0, Wst[s][0]);
+                Wst[s][1] = mfma_bf16_k32(kta, ub1, Wst[s][1]);
+            }
+        }
+        load_ws(nn);            // this chunk's prep results are dead from here on
+        write_wt();
+        lds_barrier();                                           // B4
+        {
+            const int t = tid >> 3, c4 = 4 * (tid & 7);
+            const uint2 v2 = *reinterpret_cast<const uint2*>(Yb + t * 32 + c4);
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{v2.x, v2.y}, yrsrc,
+                                                  ((t0 + t) * d_v + c4) * 2, 0, 0);
+        }
+    }
+
+    if (a.Wf) {
+#pragma unroll
+        for (int s = 0; s < NDW; ++s)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float* dst = a.Wf + (static_cast<int64_t>(bh) * d_v + col0 + 16 * c + l16) * D +
+                             orig_col(16 * (w + 8 * s) + 4 * g4, DK);
+                *reinterpret_cast<float2*>(dst) = make_float2(Wst[s][c][0], Wst[s][c][2]);
+                *reinterpret_cast<float2*>(dst + DK) = make_float2(Wst[s][c][1], Wst[s][c][3]);
+            }
+    }
+}
+
 hipError_t launch_stream_c64(const StreamPlan& p, hipStream_t s);
 
 }  // namespace fwa

@@ -81,6 +81,7 @@ bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPl
     plan->ndw = nu;
     plan->sliced_prep = true;
     plan->sliced_stream = true;
+    plan->pipe = false;
     plan->ws_bytes = a.o_rq + NU * szR;
     return true;
 }

@@ -143,8 +143,9 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *     fused    one launch that keeps the chunk and the memory on chip; no workspace.
  *              Needs the chunk's working set (3*chunk*D elements plus chunk-sized scratch)
  *              within the 160 KiB of LDS of one compute unit.
- *   The planner takes the chunked path where it applies and its workspace is at most 2 GiB,
- *   else the streaming one where it applies, else the fused one.
+ *   The planner takes the chunked path where it applies, its workspace is at most 2 GiB and
+ *   the streaming path does not fill the GPU (B*H*(d_v/32) serial workgroups of at least 128,
+ *   or 64 at D >= 384); else the streaming one where it applies, else the fused one.
  *   Implemented shapes: d_k in {16, 32, 64}, d_v in {16, 32, 64}, D = 2*d_k*nu <= 512, and
  *   the conditions of at least one implementation above; other valid shapes give
  *   FWA_ERR_UNSUPPORTED.

@@ -187,6 +187,9 @@ def _stream_workspace_formula(B, H, T, chunk):
 @pytest.mark.parametrize("shape,dtype,path", [
     ((1, 8, 1024, 64, 64, 1, 64), "f32", "chunked"),      # 8 heads x 1024, D 128
     ((4, 8, 4096, 64, 64, 2, 64), "bf16", "chunked"),     # 32 heads x 4096, D 256
+    ((4, 8, 4096, 64, 64, 3, 64), "bf16", "stream"),      # D 384: 64 serial workgroups suffice
+    ((8, 16, 4096, 64, 64, 2, 64), "bf16", "stream"),     # 256 serial workgroups
+    ((2, 8, 16384, 64, 64, 2, 64), "bf16", "chunked"),    # 32 serial workgroups: too few
     ((8, 16, 16384, 64, 64, 3, 64), "bf16", "stream"),    # 128 heads x 16384: 7.6 GB chunked workspace
     ((8, 16, 16384, 64, 16, 3, 64), "bf16", "stream"),    # d_v 16: 16-column sliced serial kernel
     ((8, 16, 16384, 32, 16, 4, 64), "bf16", "fused"),     # d_k 32, d_v 16: no streaming plan

@@ -69,8 +69,14 @@ fwa_status hip_status(hipError_t e, const char* what) {
 // The planner takes the chunked implementation where it applies and its workspace stays within
 // kAutoWorkspaceLimit: beyond that the workspace traffic (about 7 D-wide rows per token)
 // outweighs the parallelism it buys.  Larger bf16 problems take the streaming implementation
-// where it applies, else the fused kernel.
+// where it applies, else the fused kernel.  Where both apply, the streaming one is taken once
+// its serial workgroups (one per head and 32 columns of d_v) number kStreamFill, or half that
+// at D >= 384, where the chunked workspace traffic is largest: on MI355X the streaming forward
+// of 128 heads x 4096 at D 256 takes 387 us against 672, of 32 heads x 4096 at D 384 256 us
+// against 379, while 32 heads x 4096 at D 256 (227 against 264 us) and 16 heads x 16384 stay
+// chunked.
 constexpr int64_t kAutoWorkspaceLimit = int64_t(2) << 30;
+constexpr int64_t kStreamFill = 128;
 }  // namespace
 
 extern "C" {
@@ -166,7 +172,11 @@ fwa_status choose_forward(const char* fn, int request, int BH, int T, int d_k, i
     const bool can_fuse = (auto_ || request == FWA_PATH_FUSED) &&
                           fwa::plan_forward(BH, d_k, d_v, nu, chunk, bf16, &c->fplan);
     c->ws_bytes = 0;
-    if (can_chunk && (!auto_ || c->cplan.ws_bytes <= kAutoWorkspaceLimit || (!can_stream && !can_fuse))) {
+    const int64_t serial_wgs = static_cast<int64_t>(BH) * (d_v / 32);
+    const bool stream_fills = can_stream && (serial_wgs >= kStreamFill ||
+                                             (2 * d_k * nu >= 384 && 2 * serial_wgs >= kStreamFill));
+    if (can_chunk && (!auto_ || (c->cplan.ws_bytes <= kAutoWorkspaceLimit && !stream_fills) ||
+                      (!can_stream && !can_fuse))) {
         c->path = FWA_PATH_CHUNKED;
         c->ws_bytes = c->cplan.ws_bytes;
         return ok();

@@ -4,14 +4,15 @@
 // head-split [B, H, T, d] layout the layer reads, and the output map (with bias) of the heads'
 // concatenated outputs, read straight from [B, H, T, d_v] and added to a residual.
 //
-// Both are C[M x N] = A[M x K] B^T with B an [N x K] weight (out = x W^T).  Each wave computes
-// one 16 x 16 tile of C; a workgroup of 4 waves covers 32 x 32, so a token-wise decode (M = the
-// number of sequences, a few hundred) still spreads over hundreds of workgroups.  bf16 operands
-// use v_mfma_f32_16x16x32_bf16; fp32 operands v_mfma_f32_16x16x4f32 (four per 16-deep k block).
-// In both, lane l supplies row l % 16 of A and of B^T over a run of consecutive k (8 bf16 or 4
-// fp32: one 16-byte load each, contiguous in x, y and the weights).  The k loop runs in stages of
-// four such loads per operand, the next stage's loads issued before the current stage's products,
-// so one memory round trip is in flight behind the MFMAs instead of one per k-step.
+// Both are C[M x N] = A[M x K] B^T with B an [N x K] weight (out = x W^T).  A workgroup of 4
+// waves computes one 16 x 16 tile of C with the k range split over its waves (stages of four
+// 16-byte loads per operand and lane, stage s to wave s % 4), so a token-wise decode (M = the
+// number of sequences, a few hundred) spreads over a thousand or more workgroups and each wave
+// waits for about one memory round trip: its stages' loads go out two at a time, ahead of their
+// products.  The four partial tiles are summed through LDS.  bf16 operands use
+// v_mfma_f32_16x16x32_bf16; fp32 operands v_mfma_f32_16x16x4f32 (four per 16-deep k block).  In
+// both, lane l supplies row l % 16 of A and of B^T over a run of consecutive k (8 bf16 or 4
+// fp32: one 16-byte load each, contiguous in x, y and the weights).
 #include "fwa_common.h"
 #include "fwa_internal.h"
 
@@ -28,32 +29,38 @@ struct LinArgs {
     void* v;
     void* bl;
     int M, N, K, T, H, d_k, d_v;
+    int mblk0;           // first 16-row block of this launch (grids are at most 65535 tall)
 };
 
 enum { kLinProject = 0, kLinOutput = 1 };
 
 // Element offset of A[m][kk] (the first of a run of consecutive kk within one head).
 template <int MODE>
-__device__ __forceinline__ int64_t a_offset(const LinArgs& a, int64_t m, int kk) {
+// `mb`, `mt` are m / T and m % T (row m = token t of sequence b); 32-bit divisions, as
+// M = B T fits an int.
+__device__ __forceinline__ int64_t a_offset(const LinArgs& a, int64_t m, int mb, int mt, int kk) {
     if constexpr (MODE == kLinProject) return m * a.K + kk;
-    const int64_t b = m / a.T, t = m % a.T;
-    return ((b * a.H + kk / a.d_v) * a.T + t) * a.d_v + kk % a.d_v;
+    const int hh = static_cast<int>(static_cast<unsigned>(kk) / static_cast<unsigned>(a.d_v));
+    return ((int64_t(mb) * a.H + hh) * a.T + mt) * a.d_v + (kk - hh * a.d_v);
 }
 
 template <bool BF16, int MODE>
 __global__ __launch_bounds__(256) void linear_kernel(LinArgs a) {
     constexpr int KL = BF16 ? 32 : 16;          // k covered by one 16-byte load per lane
     constexpr int U = 4;                         // loads per operand per stage
+    constexpr int ES = BF16 ? 2 : 4;
+    __shared__ f32x4 part[4][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t m0 = int64_t(blockIdx.y) * 32 + (wave >> 1) * 16;
-    const int n0 = blockIdx.x * 32 + (wave & 1) * 16;
+    const int64_t m0 = (int64_t(a.mblk0) + blockIdx.y) * 16;
+    const int n0 = blockIdx.x * 16;
     const int li = lane & 15, lg = lane >> 4;
     const int64_t m = m0 + li;
     const int n = n0 + li;
     const bool mok = m < a.M, nok = n < a.N;
+    const unsigned mu = mok ? static_cast<unsigned>(m) : 0u;
+    const int mb = static_cast<int>(mu / static_cast<unsigned>(a.T)), mt = static_cast<int>(mu) - mb * a.T;
     const char* Ab = static_cast<const char*>(a.A);
-    const char* Bb = static_cast<const char*>(a.Bw) + (nok ? int64_t(n) * a.K * (BF16 ? 2 : 4) : 0);
-    constexpr int ES = BF16 ? 2 : 4;
+    const char* Bb = static_cast<const char*>(a.Bw) + (nok ? int64_t(n) * a.K * ES : 0);
     uint4 ra0[U], rb0[U], ra1[U], rb1[U];
     // stage st: k runs kk = st U KL + u KL + (KL / 4) lg; a run past K (or a row past M / N)
     // loads nothing and reads as zero
@@ -64,7 +71,7 @@ __global__ __launch_bounds__(256) void linear_kernel(LinArgs a) {
             const bool kok = kk < a.K;
             xa[u] = make_uint4(0u, 0u, 0u, 0u);
             xb[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (mok && kok) xa[u] = *reinterpret_cast<const uint4*>(Ab + a_offset<MODE>(a, m, kk) * ES);
+            if (mok && kok) xa[u] = *reinterpret_cast<const uint4*>(Ab + a_offset<MODE>(a, m, mb, mt, kk) * ES);
             if (nok && kok) xb[u] = *reinterpret_cast<const uint4*>(Bb + int64_t(kk) * ES);
         }
     };
@@ -85,41 +92,65 @@ __global__ __launch_bounds__(256) void linear_kernel(LinArgs a) {
             }
         }
     };
-    // two register sets, alternating: the next stage's loads go out before this stage's MFMAs
+    // this wave's stages wave, wave + 4, ...: two register sets, the next pair's loads issued
+    // before the current pair's products
     const int stages = (a.K + U * KL - 1) / (U * KL);
-    load(0, ra0, rb0);
-    for (int st = 0; st < stages; st += 2) {
-        if (st + 1 < stages) load(st + 1, ra1, rb1);
+    int st = wave;
+    if (st < stages) load(st, ra0, rb0);
+    if (st + 4 < stages) load(st + 4, ra1, rb1);
+    for (; st < stages; st += 8) {
         products(ra0, rb0);
-        if (st + 1 >= stages) break;
-        if (st + 2 < stages) load(st + 2, ra0, rb0);
+        if (st + 8 < stages) load(st + 8, ra0, rb0);
+        if (st + 4 >= stages) break;
         products(ra1, rb1);
+        if (st + 12 < stages) load(st + 12, ra1, rb1);
     }
+    part[wave][lane] = acc + acc2;
+    __syncthreads();
+    if (wave != 0) return;
+    acc = part[0][lane] + part[1][lane];
+    acc2 = part[2][lane] + part[3][lane];
     acc += acc2;
     // result slot r: row m0 + 4 lg + r, column n0 + li
     if (!nok) return;
-    const int nq = a.H * a.d_k, nv = a.H * a.d_v;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t mr = m0 + 4 * lg + r;
-        if (mr >= a.M) continue;
-        const float val = acc[r];
-        if constexpr (MODE == kLinProject) {
-            const int64_t b = mr / a.T, t = mr % a.T;
-            if (n < nq) {
-                store_elem<BF16>(a.q, ((b * a.H + n / a.d_k) * a.T + t) * a.d_k + n % a.d_k, val);
-            } else if (n < 2 * nq) {
-                const int c = n - nq;
-                store_elem<BF16>(a.k, ((b * a.H + c / a.d_k) * a.T + t) * a.d_k + c % a.d_k, val);
-            } else if (n < 2 * nq + nv) {
-                const int c = n - 2 * nq;
-                store_elem<BF16>(a.v, ((b * a.H + c / a.d_v) * a.T + t) * a.d_v + c % a.d_v, val);
-            } else {
-                store_elem<BF16>(a.bl, (b * a.H + (n - 2 * nq - nv)) * a.T + t, val);
-            }
+    if constexpr (MODE == kLinProject) {
+        // the column's destination: q, k, v (head hh, column c) or the beta logit of head hh
+        const int nq = a.H * a.d_k, nv = a.H * a.d_v;
+        void* dst;
+        int hh, c, dw;
+        if (n < 2 * nq) {
+            const int cn = n < nq ? n : n - nq;
+            dst = n < nq ? a.q : a.k;
+            hh = static_cast<int>(static_cast<unsigned>(cn) / static_cast<unsigned>(a.d_k));
+            c = cn - hh * a.d_k;
+            dw = a.d_k;
+        } else if (n < 2 * nq + nv) {
+            const int cn = n - 2 * nq;
+            dst = a.v;
+            hh = static_cast<int>(static_cast<unsigned>(cn) / static_cast<unsigned>(a.d_v));
+            c = cn - hh * a.d_v;
+            dw = a.d_v;
         } else {
-            float o = val;
-            if (a.bias) o += load_elem<BF16>(a.bias, n);
+            dst = a.bl;
+            hh = n - 2 * nq - nv;
+            c = 0;
+            dw = 1;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t mr = m0 + 4 * lg + r;
+            if (mr >= a.M) continue;
+            const int b = static_cast<int>(static_cast<unsigned>(mr) / static_cast<unsigned>(a.T));
+            const int tt = static_cast<int>(mr) - b * a.T;
+            store_elem<BF16>(dst, ((int64_t(b) * a.H + hh) * a.T + tt) * dw + c, acc[r]);
+        }
+    } else {
+        const float bias = a.bias ? load_elem<BF16>(a.bias, n) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t mr = m0 + 4 * lg + r;
+            if (mr >= a.M) continue;
+            float o = acc[r] + bias;
             if (a.res) o += load_elem<BF16>(a.res, mr * a.N + n);
             store_elem<BF16>(a.out, mr * a.N + n, o);
         }
@@ -127,12 +158,20 @@ __global__ __launch_bounds__(256) void linear_kernel(LinArgs a) {
 }
 
 template <int MODE>
-static hipError_t launch_linear(const LinArgs& a, bool bf16, hipStream_t stream) {
-    if (a.M == 0 || a.N == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((a.N + 31) / 32), static_cast<unsigned>((int64_t(a.M) + 31) / 32));
-    if (bf16) hipLaunchKernelGGL((linear_kernel<true, MODE>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((linear_kernel<false, MODE>), grid, dim3(256), 0, stream, a);
-    return hipGetLastError();
+static hipError_t launch_linear(const LinArgs& a0, bool bf16, hipStream_t stream) {
+    if (a0.M == 0 || a0.N == 0) return hipSuccess;
+    const int mblocks = static_cast<int>((int64_t(a0.M) + 15) / 16);
+    for (int b0 = 0; b0 < mblocks; b0 += 65535) {
+        LinArgs a = a0;
+        a.mblk0 = b0;
+        const int nb = mblocks - b0 < 65535 ? mblocks - b0 : 65535;
+        const dim3 grid(static_cast<unsigned>((a.N + 15) / 16), static_cast<unsigned>(nb));
+        if (bf16) hipLaunchKernelGGL((linear_kernel<true, MODE>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((linear_kernel<false, MODE>), grid, dim3(256), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_layer_project(const void* x, const void* Wqkvb, void* q, void* k, void* v,

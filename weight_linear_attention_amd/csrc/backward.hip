@@ -367,7 +367,21 @@ __global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs
 // ------------------------------------------------------------------------------ 4. chunk grads
 
 constexpr int kSlice = 64;   // columns of D per pass in bwd_chunk_grads
+constexpr int kCS = kBC + 4; // row stride of the C x C tiles (16-byte rows, few bank clashes)
 
+// Padded d_v: the d_v contraction runs in 16-deep blocks; the row stride adds 4 floats.
+__host__ __device__ inline int grads_dv16(int d_v) { return (d_v + 15) & ~15; }
+__host__ __device__ inline int grads_dvp(int d_v) { return grads_dv16(d_v) + 4; }
+
+// One chunk per workgroup of 4 waves.  The C x C and C x d_v work (dU, lam, dv, dP, Z, dG, the
+// beta partials) runs on the vector ALU; the D-wide products, per 64-column slice of D,
+//   dQ = dY W0 + dP K,   M = lam W0,   dK = U dW1 + dP^T Q + (dG + dG^T) K - diag(beta) M,
+// run on the fp32 MFMA: wave w owns column tile w of the slice, both row tiles.  A 16-deep k
+// block feeds four 16x16x4 products, lane group g supplying k = 4 g + s to sub-step s for both
+// operands, so each lane reads its A and B values as one 16-byte LDS read each: the A operands
+// (dY, lam, U, dP, dP^T, dG) row-major, the B operands (W0, dW1, K, Q slices) transposed
+// ([column][k]) when staged.  The next slice's operands load into registers while the current
+// slice computes.
 template <bool BF16>
 __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs a) {
     extern __shared__ float lds[];
@@ -376,10 +390,10 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     const int bh = u / a.NC, n = u % a.NC;
     const int t0 = n * kBC;
     const int tid = threadIdx.x;
-    constexpr int CS = kBC + 1;
-    const int SV = d_v + 1;           // padded row stride of the [C][d_v] tiles
+    constexpr int CS = kCS;
+    const int DV16 = grads_dv16(d_v), SV = grads_dvp(d_v);   // padded [C][d_v] rows
     const int CV = kBC * SV;
-    float* dYs = lds;                 // [C][d_v]
+    float* dYs = lds;                 // [C][SV], zero past d_v
     float* Us = dYs + CV;             // U
     float* dUs = Us + CV;             // dU
     float* Ls = dUs + CV;             // lam
@@ -388,22 +402,28 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     float* Pm = Ai + kBC * CS;
     float* Gm = Pm + kBC * CS;
     float* dP = Gm + kBC * CS;
-    float* dG = dP + kBC * CS;        // dG + dG^T
+    float* dPT = dP + kBC * CS;       // dP^T
+    float* dG = dPT + kBC * CS;       // dG + dG^T
     float* be = dG + kBC * CS;        // [C]
     float* bpart = be + kBC;          // [C]: lam_i.V_i - sum_{j<i} G_ij Z_ij
-    float* W0s = bpart + kBC;         // [d_v][kSlice]
-    float* G1s = W0s + d_v * kSlice;
-    float* Ks = G1s + d_v * kSlice;   // [C][kSlice]
-    float* Qs = Ks + kBC * kSlice;
+    float* mkb = bpart + kBC;         // [4][C]: per-wave partial sums of M_i . K_i
+    float* W0T = mkb + 4 * kBC;       // [kSlice][SV]: W0 slice transposed
+    float* G1T = W0T + kSlice * SV;   // dW1 slice transposed
+    float* KT = G1T + kSlice * SV;    // [kSlice][CS]: K slice transposed
+    float* QT = KT + kSlice * CS;
 
     const int64_t u64 = u;
-    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
-        const int c = e / d_v, r = e % d_v;
-        const bool in = t0 + c < a.T;
+    for (int e = tid; e < kBC * SV; e += kPrepThreads2) {
+        const int c = e / SV, r = e % SV;
+        const bool in = t0 + c < a.T && r < d_v;
         const int64_t g = (int64_t(bh) * a.T + t0 + c) * d_v + r;
-        dYs[c * SV + r] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
-        Vs[c * SV + r] = in ? load_elem<BF16>(a.v, g) : 0.0f;
+        dYs[e] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
+        Vs[e] = in ? load_elem<BF16>(a.v, g) : 0.0f;
+        Us[e] = 0.0f;
+        dUs[e] = 0.0f;
+        Ls[e] = 0.0f;
     }
+    __syncthreads();
     for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {     // [r][c] in the workspace
         const int r = e / kBC, c = e % kBC;
         Us[c * SV + r] = a.ws[a.L.uu + u64 * kBC * d_v + e];
@@ -434,7 +454,8 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         if (t0 + i < a.T) store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * s);
     }
     __syncthreads();
-    // dP = lower_incl(dY U^T); Z = lam U^T; dG_ij = -beta_i Z_ij (j < i), kept symmetrised
+    // dP = lower_incl(dY U^T) (and its transpose); Z = lam U^T; dG_ij = -beta_i Z_ij (j < i),
+    // kept symmetrised
     for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
         const int i = e / kBC, j = e % kBC;
         float sp = 0.0f, sz = 0.0f;
@@ -443,6 +464,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
             sz += Ls[i * SV + r] * Us[j * SV + r];
         }
         dP[i * CS + j] = j <= i ? sp : 0.0f;
+        dPT[j * CS + i] = j <= i ? sp : 0.0f;
         dG[i * CS + j] = j < i ? -be[i] * sz : 0.0f;       // strict lower part for now
         Ai[i * CS + j] = sz;                                // Ai is not needed any more: Z
     }
@@ -459,72 +481,135 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         const int i = e / kBC, j = e % kBC;
         if (j > i) dG[i * CS + j] = dG[j * CS + i];
     }
-    __syncthreads();
 
-    // per 64-column slice of D: dQ = dY W0 + dP K;  M = lam W0;
-    // dK = U dW1 - diag(beta) M + dP^T Q + (dG + dG^T) K
-    const int i = tid / 8, jq = (tid % 8) * 8;
-    float mk = 0.0f;                                        // sum over D of M_i . K_i
+    // ---- D-wide products per 64-column slice
+    const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int64_t CD = int64_t(kBC) * D;
+    // staging: thread -> (column n, d_v entries r = 4 tid / 64 ... ) of W0 and dW1; (column n,
+    // rows) of K and Q.  Element e < d_v * kSlice: r = e / kSlice, n = e % kSlice (coalesced
+    // along D); e < kBC * kSlice for K and Q.
+    constexpr int NW = 64 * kSlice / kPrepThreads2;      // W0 / dW1 elements per thread (d_v <= 64)
+    constexpr int NK = kBC * kSlice / kPrepThreads2;     // K / Q elements per thread
+    float pw[NW], pg[NW], pk[NK], pq[NK];
+    auto fetch = [&](int s0) {
+#pragma unroll
+        for (int p = 0; p < NW; ++p) {
+            const int e = tid + kPrepThreads2 * p, r = e / kSlice, nn = e % kSlice;
+            const bool in = r < d_v && s0 + nn < D;
+            const int64_t o = (u64 * d_v + (in ? r : 0)) * D + (in ? s0 + nn : 0);
+            pw[p] = in ? a.ws[a.L.ws + o] : 0.0f;
+            pg[p] = in ? a.ws[a.L.gs + o] : 0.0f;
+        }
+#pragma unroll
+        for (int p = 0; p < NK; ++p) {
+            const int e = tid + kPrepThreads2 * p, c = e / kSlice, nn = e % kSlice;
+            const bool in = s0 + nn < D;
+            const int64_t o = u64 * CD + c * D + (in ? s0 + nn : 0);
+            pk[p] = in ? a.ws[a.L.kt + o] : 0.0f;
+            pq[p] = in ? a.ws[a.L.qt + o] : 0.0f;
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int p = 0; p < NW; ++p) {
+            const int e = tid + kPrepThreads2 * p, r = e / kSlice, nn = e % kSlice;
+            if (r < DV16) {
+                W0T[nn * SV + r] = pw[p];
+                G1T[nn * SV + r] = pg[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NK; ++p) {
+            const int e = tid + kPrepThreads2 * p, c = e / kSlice, nn = e % kSlice;
+            KT[nn * CS + c] = pk[p];
+            QT[nn * CS + c] = pq[p];
+        }
+    };
+    float mkp[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mkp[rt][e] = 0.0f;
+    const int ncol = 16 * wv + l16;                         // the lane's column in the slice
+    fetch(0);
     for (int s0 = 0; s0 < D; s0 += kSlice) {
-        const int sw = D - s0 < kSlice ? D - s0 : kSlice;
-        for (int e = tid; e < d_v * kSlice; e += kPrepThreads2) {
-            const int r = e / kSlice, jj = e % kSlice;
-            const bool in = jj < sw;
-            W0s[e] = in ? a.ws[a.L.ws + (u64 * d_v + r) * D + s0 + jj] : 0.0f;
-            G1s[e] = in ? a.ws[a.L.gs + (u64 * d_v + r) * D + s0 + jj] : 0.0f;
-        }
-        for (int e = tid; e < kBC * kSlice; e += kPrepThreads2) {
-            const int c = e / kSlice, jj = e % kSlice;
-            const bool in = jj < sw;
-            Ks[e] = in ? a.ws[a.L.kt + u64 * CD + c * D + s0 + jj] : 0.0f;
-            Qs[e] = in ? a.ws[a.L.qt + u64 * CD + c * D + s0 + jj] : 0.0f;
-        }
+        __syncthreads();                                    // the previous slice's reads are done
+        commit();
+        if (s0 + kSlice < D) fetch(s0 + kSlice);
         __syncthreads();
-        float dq[8], dk[8], mm[8];
+        f32x4 dq[2], mm[2], dk[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dq[e] = dk[e] = mm[e] = 0.0f;
-        for (int r = 0; r < d_v; ++r) {
-            const float dyv = dYs[i * SV + r], lv = Ls[i * SV + r], uv = Us[i * SV + r];
+        for (int rt = 0; rt < 2; ++rt) dq[rt] = mm[rt] = dk[rt] = zero4();
+        // k over d_v
+        for (int kb = 0; kb < DV16; kb += 16) {
+            const f32x4 bw = *reinterpret_cast<const f32x4*>(W0T + ncol * SV + kb + 4 * g4);
+            const f32x4 bg = *reinterpret_cast<const f32x4*>(G1T + ncol * SV + kb + 4 * g4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float w0 = W0s[r * kSlice + jq + e];
-                dq[e] += dyv * w0;
-                mm[e] += lv * w0;
-                dk[e] += uv * G1s[r * kSlice + jq + e];
+            for (int rt = 0; rt < 2; ++rt) {
+                const int ro = (16 * rt + l16) * SV + kb + 4 * g4;
+                const f32x4 ady = *reinterpret_cast<const f32x4*>(dYs + ro);
+                const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + ro);
+                const f32x4 au = *reinterpret_cast<const f32x4*>(Us + ro);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    dq[rt] = mfma_f32_k4(ady[s], bw[s], dq[rt]);
+                    mm[rt] = mfma_f32_k4(al[s], bw[s], mm[rt]);
+                    dk[rt] = mfma_f32_k4(au[s], bg[s], dk[rt]);
+                }
             }
         }
-        for (int j = 0; j < kBC; ++j) {
-            const float pij = dP[i * CS + j], pji = dP[j * CS + i], gij = dG[i * CS + j];
+        // k over the chunk rows
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float kj = Ks[j * kSlice + jq + e];
-                dq[e] += pij * kj;
-                dk[e] += pji * Qs[j * kSlice + jq + e] + gij * kj;
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 bk = *reinterpret_cast<const f32x4*>(KT + ncol * CS + kb + 4 * g4);
+            const f32x4 bq = *reinterpret_cast<const f32x4*>(QT + ncol * CS + kb + 4 * g4);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int ro = (16 * rt + l16) * CS + kb + 4 * g4;
+                const f32x4 ap = *reinterpret_cast<const f32x4*>(dP + ro);
+                const f32x4 apt = *reinterpret_cast<const f32x4*>(dPT + ro);
+                const f32x4 ag = *reinterpret_cast<const f32x4*>(dG + ro);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    dq[rt] = mfma_f32_k4(ap[s], bk[s], dq[rt]);
+                    dk[rt] = mfma_f32_k4(apt[s], bq[s], dk[rt]);
+                    dk[rt] = mfma_f32_k4(ag[s], bk[s], dk[rt]);
+                }
             }
         }
-        const float bi = be[i];
+        // result slot e of row tile rt: row i = 16 rt + 4 g4 + e, column s0 + ncol
+        const int col = s0 + ncol;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dk[e] -= bi * mm[e];
-            mk += mm[e] * Ks[i * kSlice + jq + e];
-        }
-        float* gdK = a.ws + a.L.wy + u64 * CD + int64_t(i) * D + s0;
-        float* gdQ = a.ws + a.L.qp + u64 * CD + int64_t(i) * D + s0;
+        for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (jq + e < sw) {
-                gdK[jq + e] = dk[e];
-                gdQ[jq + e] = dq[e];
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * rt + 4 * g4 + e;
+                const float m = mm[rt][e];
+                mkp[rt][e] += m * KT[ncol * CS + i];
+                if (col < D) {
+                    a.ws[a.L.wy + u64 * CD + int64_t(i) * D + col] = dk[rt][e] - be[i] * m;
+                    a.ws[a.L.qp + u64 * CD + int64_t(i) * D + col] = dq[rt][e];
+                }
             }
-        __syncthreads();
+        }
     }
-    // the 8 threads of row i are adjacent lanes
-    mk += __shfl_xor(mk, 1);
-    mk += __shfl_xor(mk, 2);
-    mk += __shfl_xor(mk, 4);
-    if ((tid & 7) == 0 && t0 + i < a.T) {
+    // M_i . K_i: the 16 lanes of a row group hold its columns; then the four waves
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float s = mkp[rt][e];
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            s += __shfl_xor(s, 4);
+            s += __shfl_xor(s, 8);
+            if (l16 == 0) mkb[wv * kBC + 16 * rt + 4 * g4 + e] = s;
+        }
+    __syncthreads();
+    if (tid < kBC && t0 + tid < a.T) {
         // beta (1 - beta) as sigmoid(l) sigmoid(-l): 1 - beta cancels where beta rounds to 1
+        const int i = tid;
+        const float mk = (mkb[i] + mkb[kBC + i]) + (mkb[2 * kBC + i] + mkb[3 * kBC + i]);
         const int64_t g = int64_t(bh) * a.T + t0 + i;
         const float l = load_elem<BF16>(a.bl, g);
         const float dbeta = bpart[i] - mk;
@@ -623,8 +708,9 @@ static int lds_prep_bytes(int D, int d_k, int d_v) {
                 kBC * d_v);
 }
 static int lds_grads_bytes(int d_v) {
-    return 4 * (5 * kBC * (d_v + 1) + 5 * kBC * (kBC + 1) + 2 * kBC + 2 * d_v * kSlice +
-                2 * kBC * kSlice);
+    const int SV = grads_dvp(d_v);
+    return 4 * (5 * kBC * SV + 6 * kBC * kCS + 2 * kBC + 4 * kBC + 2 * kSlice * SV +
+                2 * kSlice * kCS);
 }
 
 template <int NPL, bool BF16>

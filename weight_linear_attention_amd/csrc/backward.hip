@@ -373,15 +373,16 @@ constexpr int kCS = kBC + 4; // row stride of the C x C tiles (16-byte rows, few
 __host__ __device__ inline int grads_dv16(int d_v) { return (d_v + 15) & ~15; }
 __host__ __device__ inline int grads_dvp(int d_v) { return grads_dv16(d_v) + 4; }
 
-// One chunk per workgroup of 4 waves.  The C x C and C x d_v work (dU, lam, dv, dP, Z, dG, the
-// beta partials) runs on the vector ALU; the D-wide products, per 64-column slice of D,
-//   dQ = dY W0 + dP K,   M = lam W0,   dK = U dW1 + dP^T Q + (dG + dG^T) K - diag(beta) M,
-// run on the fp32 MFMA: wave w owns column tile w of the slice, both row tiles.  A 16-deep k
-// block feeds four 16x16x4 products, lane group g supplying k = 4 g + s to sub-step s for both
-// operands, so each lane reads its A and B values as one 16-byte LDS read each: the A operands
-// (dY, lam, U, dP, dP^T, dG) row-major, the B operands (W0, dW1, K, Q slices) transposed
-// ([column][k]) when staged.  The next slice's operands load into registers while the current
-// slice computes.
+// One chunk per workgroup of 4 waves, every contraction on the fp32 MFMA (16x16x4; a 16-deep k
+// block feeds four products, lane group g supplying k = 4 g + s to sub-step s for both operands,
+// so each lane reads its A and B values as one 16-byte LDS read each: A operands row-major
+// [row][k], B operands transposed [column][k]):
+//   dU = P^T dY + (K dW1^T, from the row pass)      lam = Ainv^T dU      dv = diag(beta) lam
+//   dP = lower_incl(dY U^T)      Z = lam U^T      dG_ij = -beta_i Z_ij (j < i), symmetrised
+// then, per 64-column slice of D (wave w: column tile w, both row tiles),
+//   dQ = dY W0 + dP K,   M = lam W0,   dK = U dW1 + dP^T Q + (dG + dG^T) K - diag(beta) M.
+// The chunk's operands are loaded into registers in one batch before any LDS store; the next
+// slice's W0, dW1, K and Q load into registers while the current slice computes.
 template <bool BF16>
 __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs a) {
     extern __shared__ float lds[];
@@ -390,18 +391,22 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     const int bh = u / a.NC, n = u % a.NC;
     const int t0 = n * kBC;
     const int tid = threadIdx.x;
+    const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     constexpr int CS = kCS;
     const int DV16 = grads_dv16(d_v), SV = grads_dvp(d_v);   // padded [C][d_v] rows
+    const int NR = DV16 / 16;                                  // 16-column tiles of d_v
     const int CV = kBC * SV;
-    float* dYs = lds;                 // [C][SV], zero past d_v
+    float* dYs = lds;                 // [C][SV] row-major, zero past d_v
     float* Us = dYs + CV;             // U
-    float* dUs = Us + CV;             // dU
-    float* Ls = dUs + CV;             // lam
+    float* Ls = Us + CV;              // lam
     float* Vs = Ls + CV;
-    float* Ai = Vs + CV;              // [C][CS]
-    float* Pm = Ai + kBC * CS;
-    float* Gm = Pm + kBC * CS;
-    float* dP = Gm + kBC * CS;
+    float* dYT = Vs + CV;             // [DV16][CS]: dY^T
+    float* dUT = dYT + DV16 * CS;     // dU^T
+    float* PmT = dUT + DV16 * CS;     // [C][CS]: P^T
+    float* AiT = PmT + kBC * CS;      // Ainv^T
+    float* Gm = AiT + kBC * CS;       // G
+    float* Zs = Gm + kBC * CS;        // Z
+    float* dP = Zs + kBC * CS;
     float* dPT = dP + kBC * CS;       // dP^T
     float* dG = dPT + kBC * CS;       // dG + dG^T
     float* be = dG + kBC * CS;        // [C]
@@ -413,116 +418,205 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     float* QT = KT + kSlice * CS;
 
     const int64_t u64 = u;
-    for (int e = tid; e < kBC * SV; e += kPrepThreads2) {
-        const int c = e / SV, r = e % SV;
-        const bool in = t0 + c < a.T && r < d_v;
-        const int64_t g = (int64_t(bh) * a.T + t0 + c) * d_v + r;
-        dYs[e] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
-        Vs[e] = in ? load_elem<BF16>(a.v, g) : 0.0f;
-        Us[e] = 0.0f;
-        dUs[e] = 0.0f;
-        Ls[e] = 0.0f;
-    }
-    __syncthreads();
-    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {     // [r][c] in the workspace
-        const int r = e / kBC, c = e % kBC;
-        Us[c * SV + r] = a.ws[a.L.uu + u64 * kBC * d_v + e];
-        dUs[c * SV + r] = a.ws[a.L.aa + u64 * kBC * d_v + e];  // K dW1^T, P^T dY added below
-    }
-    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
-        const int i = e / kBC, j = e % kBC;
-        Ai[i * CS + j] = a.ws[a.L.ai + u64 * kBC * kBC + e];
-        Pm[i * CS + j] = a.ws[a.L.pm + u64 * kBC * kBC + e];
-        Gm[i * CS + j] = a.ws[a.L.gm + u64 * kBC * kBC + e];
-    }
-    if (tid < kBC) be[tid] = a.ws[a.L.be + u64 * kBC + tid];
-    __syncthreads();
-    // dU = P^T dY + K dW1^T
-    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
-        const int i = e / d_v, r = e % d_v;
-        float s = dUs[i * SV + r];
-        for (int j = i; j < kBC; ++j) s += Pm[j * CS + i] * dYs[j * SV + r];
-        dUs[i * SV + r] = s;
-    }
-    __syncthreads();
-    // lam = Ainv^T dU; dv = diag(beta) lam
-    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
-        const int i = e / d_v, r = e % d_v;
-        float s = 0.0f;
-        for (int j = i; j < kBC; ++j) s += Ai[j * CS + i] * dUs[j * SV + r];
-        Ls[i * SV + r] = s;
-        if (t0 + i < a.T) store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * s);
-    }
-    __syncthreads();
-    // dP = lower_incl(dY U^T) (and its transpose); Z = lam U^T; dG_ij = -beta_i Z_ij (j < i),
-    // kept symmetrised
-    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
-        const int i = e / kBC, j = e % kBC;
-        float sp = 0.0f, sz = 0.0f;
-        for (int r = 0; r < d_v; ++r) {
-            sp += dYs[i * SV + r] * Us[j * SV + r];
-            sz += Ls[i * SV + r] * Us[j * SV + r];
+    // ---- the chunk's operands, all loads first.  dy, v: (row c = tid / 64 + 4 m, entry r =
+    //      tid % 64); U, K dW1^T: workspace [r][c] units tid + 256 m; Ainv, P, G: [i][j] units
+    //      tid + 256 m
+    {
+        constexpr int MR = kBC / (kPrepThreads2 / 64);           // 8 rows per thread
+        constexpr int MU = kBC * 64 / kPrepThreads2;              // 8 units (d_v <= 64)
+        constexpr int MC = kBC * kBC / kPrepThreads2;             // 4 units
+        const int r = tid & 63;
+        float fy[MR], fv[MR], fu[MU], fa[MU], fi[MC], fp[MC], fg[MC];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const int c = (tid >> 6) + 4 * m;
+            const bool in = t0 + c < a.T && r < d_v;
+            const int64_t g = (int64_t(bh) * a.T + t0 + (in ? c : 0)) * d_v + (in ? r : 0);
+            fy[m] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
+            fv[m] = in ? load_elem<BF16>(a.v, g) : 0.0f;
         }
-        dP[i * CS + j] = j <= i ? sp : 0.0f;
-        dPT[j * CS + i] = j <= i ? sp : 0.0f;
-        dG[i * CS + j] = j < i ? -be[i] * sz : 0.0f;       // strict lower part for now
-        Ai[i * CS + j] = sz;                                // Ai is not needed any more: Z
+#pragma unroll
+        for (int m = 0; m < MU; ++m) {
+            const int e = tid + kPrepThreads2 * m;
+            const bool in = e < kBC * d_v;
+            fu[m] = in ? a.ws[a.L.uu + u64 * kBC * d_v + e] : 0.0f;
+            fa[m] = in ? a.ws[a.L.aa + u64 * kBC * d_v + e] : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            const int e = tid + kPrepThreads2 * m;
+            fi[m] = a.ws[a.L.ai + u64 * kBC * kBC + e];
+            fp[m] = a.ws[a.L.pm + u64 * kBC * kBC + e];
+            fg[m] = a.ws[a.L.gm + u64 * kBC * kBC + e];
+        }
+        const float fb = tid < kBC ? a.ws[a.L.be + u64 * kBC + tid] : 0.0f;
+        // zero padding: rows past d_v of the transposed tiles, entries past d_v of the row tiles
+        for (int e = tid; e < (DV16 - d_v) * CS; e += kPrepThreads2) {
+            dYT[d_v * CS + e] = 0.0f;
+            dUT[d_v * CS + e] = 0.0f;
+        }
+        for (int e = tid; e < kBC * (SV - d_v); e += kPrepThreads2) {
+            const int c = e / (SV - d_v), rr = d_v + e % (SV - d_v);
+            dYs[c * SV + rr] = 0.0f;
+            Us[c * SV + rr] = 0.0f;
+            Ls[c * SV + rr] = 0.0f;
+            Vs[c * SV + rr] = 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const int c = (tid >> 6) + 4 * m;
+            if (r < d_v) {
+                dYs[c * SV + r] = fy[m];
+                dYT[r * CS + c] = fy[m];
+                Vs[c * SV + r] = fv[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MU; ++m) {
+            const int e = tid + kPrepThreads2 * m, rr = e >> 5, c = e & (kBC - 1);
+            if (e < kBC * d_v) {
+                Us[c * SV + rr] = fu[m];
+                dUT[rr * CS + c] = fa[m];                  // K dW1^T, P^T dY added below
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            const int e = tid + kPrepThreads2 * m, i = e >> 5, j = e & (kBC - 1);
+            AiT[j * CS + i] = fi[m];
+            PmT[j * CS + i] = fp[m];
+            Gm[i * CS + j] = fg[m];
+        }
+        if (tid < kBC) be[tid] = fb;
     }
     __syncthreads();
-    if (tid < kBC) {
-        const int i = tid;
-        float s = 0.0f;
-        for (int r = 0; r < d_v; ++r) s += Ls[i * SV + r] * Vs[i * SV + r];
-        for (int j = 0; j < i; ++j) s -= Gm[i * CS + j] * Ai[i * CS + j];
-        bpart[i] = s;
+    // ---- dU = P^T dY + K dW1^T (tiles (it, rt) of dU, stored transposed)
+    for (int tau = wv; tau < 2 * NR; tau += 4) {
+        const int it = tau & 1, rt = tau >> 1;
+        float* out = dUT + (16 * rt + l16) * CS + 16 * it + 4 * g4;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(out);
+#pragma unroll
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(PmT + (16 * it + l16) * CS + kb + 4 * g4);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(dYT + (16 * rt + l16) * CS + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+        }
+        *reinterpret_cast<f32x4*>(out) = acc;
     }
     __syncthreads();
-    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {    // upper part = transpose
-        const int i = e / kBC, j = e % kBC;
+    // ---- lam = Ainv^T dU; dv = diag(beta) lam
+    for (int tau = wv; tau < 2 * NR; tau += 4) {
+        const int it = tau & 1, rt = tau >> 1;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(AiT + (16 * it + l16) * CS + kb + 4 * g4);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(dUT + (16 * rt + l16) * CS + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+        }
+        const int r = 16 * rt + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * it + 4 * g4 + e;
+            Ls[i * SV + r] = acc[e];
+            if (r < d_v && t0 + i < a.T)
+                store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * acc[e]);
+        }
+    }
+    __syncthreads();
+    // ---- dP = lower_incl(dY U^T) (and its transpose), Z = lam U^T, dG: wave w -> tile
+    //      (w % 2, w / 2) of both
+    {
+        const int it = wv & 1, jt = wv >> 1;
+        f32x4 sp = zero4(), sz = zero4();
+        for (int kb = 0; kb < DV16; kb += 16) {
+            const f32x4 bu = *reinterpret_cast<const f32x4*>(Us + (16 * jt + l16) * SV + kb + 4 * g4);
+            const f32x4 ay = *reinterpret_cast<const f32x4*>(dYs + (16 * it + l16) * SV + kb + 4 * g4);
+            const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + (16 * it + l16) * SV + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                sp = mfma_f32_k4(ay[s], bu[s], sp);
+                sz = mfma_f32_k4(al[s], bu[s], sz);
+            }
+        }
+        const int j = 16 * jt + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * it + 4 * g4 + e;
+            const float p = j <= i ? sp[e] : 0.0f;
+            dP[i * CS + j] = p;
+            dPT[j * CS + i] = p;
+            dG[i * CS + j] = j < i ? -be[i] * sz[e] : 0.0f;     // strict lower part for now
+            Zs[i * CS + j] = sz[e];
+        }
+    }
+    __syncthreads();
+    // ---- dG's upper part = its transpose; beta partials lam_i.V_i - sum_{j<i} G_ij Z_ij over
+    //      the 8 adjacent lanes of row i
+    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
+        const int i = e >> 5, j = e & (kBC - 1);
         if (j > i) dG[i * CS + j] = dG[j * CS + i];
+    }
+    {
+        const int i = tid >> 3, p8 = tid & 7;
+        float s = 0.0f;
+        for (int r = p8; r < d_v; r += 8) s += Ls[i * SV + r] * Vs[i * SV + r];
+        for (int j = p8; j < i; j += 8) s -= Gm[i * CS + j] * Zs[i * CS + j];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        if (p8 == 0) bpart[i] = s;
     }
 
     // ---- D-wide products per 64-column slice
-    const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int64_t CD = int64_t(kBC) * D;
-    // staging: thread -> (column n, d_v entries r = 4 tid / 64 ... ) of W0 and dW1; (column n,
-    // rows) of K and Q.  Element e < d_v * kSlice: r = e / kSlice, n = e % kSlice (coalesced
-    // along D); e < kBC * kSlice for K and Q.
-    constexpr int NW = 64 * kSlice / kPrepThreads2;      // W0 / dW1 elements per thread (d_v <= 64)
-    constexpr int NK = kBC * kSlice / kPrepThreads2;     // K / Q elements per thread
-    float pw[NW], pg[NW], pk[NK], pq[NK];
+    // staging: thread -> (column nn, 4 consecutive k) units u = tid + 256 p: nn = u % 64, k0 =
+    // 4 (u / 64); four global loads down the k rows (coalesced along D over the lanes) become one
+    // 16-byte LDS store of the transposed row.  W0 and dW1: k = the d_v index; K and Q: k = the
+    // chunk row.
+    constexpr int NW = 16 * kSlice / kPrepThreads2;      // W0 / dW1 units per thread (d_v <= 64)
+    constexpr int NK = (kBC / 4) * kSlice / kPrepThreads2;   // K / Q units per thread
+    f32x4 pw[NW], pg[NW], pk[NK], pq[NK];
     auto fetch = [&](int s0) {
 #pragma unroll
         for (int p = 0; p < NW; ++p) {
-            const int e = tid + kPrepThreads2 * p, r = e / kSlice, nn = e % kSlice;
-            const bool in = r < d_v && s0 + nn < D;
-            const int64_t o = (u64 * d_v + (in ? r : 0)) * D + (in ? s0 + nn : 0);
-            pw[p] = in ? a.ws[a.L.ws + o] : 0.0f;
-            pg[p] = in ? a.ws[a.L.gs + o] : 0.0f;
+            const int e = tid + kPrepThreads2 * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
+            const bool cin = s0 + nn < D;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool in = cin && k0 + q < d_v;
+                const int64_t o = (u64 * d_v + (in ? k0 + q : 0)) * D + (in ? s0 + nn : 0);
+                pw[p][q] = in ? a.ws[a.L.ws + o] : 0.0f;
+                pg[p][q] = in ? a.ws[a.L.gs + o] : 0.0f;
+            }
         }
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
-            const int e = tid + kPrepThreads2 * p, c = e / kSlice, nn = e % kSlice;
+            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e / kSlice), nn = e % kSlice;
             const bool in = s0 + nn < D;
-            const int64_t o = u64 * CD + c * D + (in ? s0 + nn : 0);
-            pk[p] = in ? a.ws[a.L.kt + o] : 0.0f;
-            pq[p] = in ? a.ws[a.L.qt + o] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t o = u64 * CD + (c0 + q) * D + (in ? s0 + nn : 0);
+                pk[p][q] = in ? a.ws[a.L.kt + o] : 0.0f;
+                pq[p][q] = in ? a.ws[a.L.qt + o] : 0.0f;
+            }
         }
     };
     auto commit = [&]() {
 #pragma unroll
         for (int p = 0; p < NW; ++p) {
-            const int e = tid + kPrepThreads2 * p, r = e / kSlice, nn = e % kSlice;
-            if (r < DV16) {
-                W0T[nn * SV + r] = pw[p];
-                G1T[nn * SV + r] = pg[p];
+            const int e = tid + kPrepThreads2 * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
+            if (k0 < DV16) {
+                *reinterpret_cast<f32x4*>(W0T + nn * SV + k0) = pw[p];
+                *reinterpret_cast<f32x4*>(G1T + nn * SV + k0) = pg[p];
             }
         }
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
-            const int e = tid + kPrepThreads2 * p, c = e / kSlice, nn = e % kSlice;
-            KT[nn * CS + c] = pk[p];
-            QT[nn * CS + c] = pq[p];
+            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e / kSlice), nn = e % kSlice;
+            *reinterpret_cast<f32x4*>(KT + nn * CS + c0) = pk[p];
+            *reinterpret_cast<f32x4*>(QT + nn * CS + c0) = pq[p];
         }
     };
     float mkp[2][4];
@@ -708,9 +802,9 @@ static int lds_prep_bytes(int D, int d_k, int d_v) {
                 kBC * d_v);
 }
 static int lds_grads_bytes(int d_v) {
-    const int SV = grads_dvp(d_v);
-    return 4 * (5 * kBC * SV + 6 * kBC * kCS + 2 * kBC + 4 * kBC + 2 * kSlice * SV +
-                2 * kSlice * kCS);
+    const int SV = grads_dvp(d_v), DV16 = grads_dv16(d_v);
+    return 4 * (4 * kBC * SV + 2 * DV16 * kCS + 7 * kBC * kCS + 2 * kBC + 4 * kBC +
+                2 * kSlice * SV + 2 * kSlice * kCS);
 }
 
 template <int NPL, bool BF16>

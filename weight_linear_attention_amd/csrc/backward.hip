@@ -31,6 +31,7 @@
 namespace fwa {
 
 constexpr int kPrepThreads2 = 256;
+constexpr int kCS = kBC + 4; // row stride of the C x C tiles (16-byte rows, few bank clashes)
 
 // Workspace regions (fp32), each indexed by the chunk u = bh * NC + n.
 struct BwdLayout {
@@ -79,8 +80,11 @@ struct BwdArgs {
 
 // ------------------------------------------------------------------------------ 1. prep
 
-// LDS: x rows of k and q (relu([., -.]), C x 2 d_k each), K and Q (C x SD, SD = D + 8), G, P,
-// Ainv (C x (C + 1)), beta, V (C x d_v).
+// LDS: x rows of k and q (relu([., -.]), C x 2 d_k each; T = Ainv diag(beta) over them once
+// they are dead), K and Q (C x SD, SD = D + 8; W_y over K once it is dead), G, P, Ainv
+// (C x kCS), beta, V (C x d_v).  The products G = K K^T, P = Q K^T, W_y = T K, P W_y and
+// U_y = T V run on the fp32 MFMA (16x16x4; lane group g supplies k = 4 g + s to sub-step s
+// for both operands: A as one 16-byte read of a row, B as four reads down a column).
 template <bool BF16>
 __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     extern __shared__ float lds[];
@@ -89,11 +93,13 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     const int bh = u / a.NC, n = u % a.NC;
     const int t0 = n * kBC;
     const int tid = threadIdx.x;
-    constexpr int CS = kBC + 1;
+    const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    constexpr int CS = kCS;
     const int SD = tile_stride(D);
     float* xk = lds;                         // [C][2 d_k]
     float* xq = xk + kBC * two;
-    float* Kt = xq + kBC * two;              // [C][SD]
+    float* Ts = xk;                          // [C][CS] T = Ainv diag(beta), after DPFP
+    float* Kt = xq + kBC * two;              // [C][SD]; W_y once K is dead
     float* Qt = Kt + kBC * SD;
     float* Gm = Qt + kBC * SD;               // [C][CS]
     float* Pm = Gm + kBC * CS;
@@ -108,38 +114,42 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
                          tid, kPrepThreads2);
     for (int c = tid; c < kBC; c += kPrepThreads2)
         be[c] = t0 + c < a.T ? sigmoid_stable(load_elem<BF16>(a.bl, int64_t(bh) * a.T + t0 + c)) : 0.0f;
-    for (int i = tid; i < kBC * d_v; i += kPrepThreads2) {
-        const int c = i / d_v, r = i % d_v;
-        Vs[i] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
-    }
+    for (int c = wv; c < kBC; c += kPrepThreads2 / 64)
+        for (int r = lane; r < d_v; r += 64)
+            Vs[c * d_v + r] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
     dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
-    for (int e = tid; e < kBC * D; e += kPrepThreads2) {
-        const int c = e / D, p = e % D;
-        gK[e] = Kt[c * SD + p];
-        gQ[e] = Qt[c * SD + p];
-    }
-    // G = K K^T and P = lower_incl(Q K^T): thread -> (row c, columns j0 + 8 e, e < 4)
-    {
-        const int c = tid / 8, j0 = tid % 8;
-        float g[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
-        for (int p = 0; p < D; ++p) {
-            const float kc = Kt[c * SD + p], qc = Qt[c * SD + p];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float kj = Kt[(j0 + 8 * e) * SD + p];
-                g[e] += kc * kj;
-                pq[e] += qc * kj;
-            }
+    for (int c = wv; c < kBC; c += kPrepThreads2 / 64)
+        for (int p = lane; p < D; p += 64) {
+            gK[c * D + p] = Kt[c * SD + p];
+            gQ[c * D + p] = Qt[c * SD + p];
         }
+    // G = K K^T (all four tiles) and P = lower_incl(Q K^T) (tiles (0,0), (1,0), (1,1));
+    // wave w takes tiles w and w + 4 of that list
+    for (int tau = wv; tau < 7; tau += 4) {
+        const bool isP = tau >= 4;
+        const int it = isP ? (tau == 4 ? 0 : 1) : tau >> 1;
+        const int jt = isP ? (tau == 6 ? 1 : 0) : tau & 1;
+        const float* X = isP ? Qt : Kt;
+        f32x4 acc = zero4();
+        for (int kb = 0; kb < D; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(X + (16 * it + l16) * SD + kb + 4 * g4);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(Kt + (16 * jt + l16) * SD + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+        }
+        const int col = 16 * jt + l16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            Gm[c * CS + j0 + 8 * e] = g[e];
-            Pm[c * CS + j0 + 8 * e] = (j0 + 8 * e <= c) ? pq[e] : 0.0f;
+            const int row = 16 * it + 4 * g4 + e;
+            if (isP) Pm[row * CS + col] = col <= row ? acc[e] : 0.0f;
+            else Gm[row * CS + col] = acc[e];
         }
     }
+    for (int e = tid; e < 16 * 16; e += kPrepThreads2)         // P tile (0, 1): above the diagonal
+        Pm[(e >> 4) * CS + 16 + (e & 15)] = 0.0f;
     __syncthreads();
     // Ainv = (I + diag(beta) strict_lower(G))^-1 by forward substitution, one column per thread
     if (tid < kBC) {
@@ -161,43 +171,84 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
         for (int i = 0; i < kBC; ++i) Ai[i * CS + j] = x[i];
     }
     __syncthreads();
-    // Wy = Ainv diag(beta) K and Q' = Q - P Wy, one column of D per thread at a time
+    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {       // T = Ainv diag(beta)
+        const int i = e >> 5, j = e & (kBC - 1);
+        Ts[i * CS + j] = Ai[i * CS + j] * be[j];
+    }
+    __syncthreads();
+    // W_y = T K: tiles (it, pt) w + 4 q, accumulators kept until every wave has read K
+    const int NPT = D / 16;
+    constexpr int kMaxWy = 384 / 16 * 2 / 4;                     // tiles per wave at D <= 384
+    f32x4 wy[kMaxWy];
     float* gWy = a.ws + a.L.wy + int64_t(u) * CD;
-    float* gQp = a.ws + a.L.qp + int64_t(u) * CD;
-    for (int p = tid; p < D; p += kPrepThreads2) {
-        float bk[kBC], wy[kBC];
 #pragma unroll
-        for (int j = 0; j < kBC; ++j) bk[j] = be[j] * Kt[j * SD + p];
+    for (int q = 0; q < kMaxWy; ++q) {
+        const int tau = wv + 4 * q;
+        wy[q] = zero4();
+        if (tau >= 2 * NPT) continue;
+        const int it = tau & 1, pt = tau >> 1;
 #pragma unroll
-        for (int i = 0; i < kBC; ++i) {
-            float s = 0.0f;
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + (16 * it + l16) * CS + kb + 4 * g4);
 #pragma unroll
-            for (int j = 0; j <= i; ++j) s += Ai[i * CS + j] * bk[j];
-            wy[i] = s;
-            gWy[i * D + p] = s;
+            for (int s = 0; s < 4; ++s)
+                wy[q] = mfma_f32_k4(av[s], Kt[(kb + 4 * g4 + s) * SD + 16 * pt + l16], wy[q]);
         }
 #pragma unroll
-        for (int i = 0; i < kBC; ++i) {
-            float s = Qt[i * SD + p];
+        for (int e = 0; e < 4; ++e) gWy[int64_t(16 * it + 4 * g4 + e) * D + 16 * pt + l16] = wy[q][e];
+    }
+    __syncthreads();                                             // K is dead: W_y over it
 #pragma unroll
-            for (int j = 0; j <= i; ++j) s -= Pm[i * CS + j] * wy[j];
-            gQp[i * D + p] = s;
+    for (int q = 0; q < kMaxWy; ++q) {
+        const int tau = wv + 4 * q;
+        if (tau >= 2 * NPT) continue;
+        const int it = tau & 1, pt = tau >> 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Kt[(16 * it + 4 * g4 + e) * SD + 16 * pt + l16] = wy[q][e];
+    }
+    __syncthreads();
+    // Q' = Q - P W_y
+    float* gQp = a.ws + a.L.qp + int64_t(u) * CD;
+    for (int tau = wv; tau < 2 * NPT; tau += 4) {
+        const int it = tau & 1, pt = tau >> 1;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Pm + (16 * it + l16) * CS + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = mfma_f32_k4(av[s], Kt[(kb + 4 * g4 + s) * SD + 16 * pt + l16], acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * it + 4 * g4 + e, col = 16 * pt + l16;
+            gQp[int64_t(row) * D + col] = Qt[row * SD + col] - acc[e];
         }
     }
-    // Uy = Ainv diag(beta) V ([c][r])
+    // Uy = T V ([c][r])
     float* gUy = a.ws + a.L.uy + int64_t(u) * kBC * d_v;
-    for (int e = tid; e < kBC * d_v; e += kPrepThreads2) {
-        const int i = e / d_v, r = e % d_v;
-        float s = 0.0f;
-        for (int j = 0; j <= i; ++j) s += Ai[i * CS + j] * be[j] * Vs[j * d_v + r];
-        gUy[e] = s;
+    for (int tau = wv; tau < 2 * ((d_v + 15) / 16); tau += 4) {
+        const int it = tau & 1, rt = tau >> 1;
+        const int r = 16 * rt + l16;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + (16 * it + l16) * CS + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = mfma_f32_k4(av[s], r < d_v ? Vs[(kb + 4 * g4 + s) * d_v + r] : 0.0f, acc);
+        }
+        if (r < d_v) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gUy[(16 * it + 4 * g4 + e) * d_v + r] = acc[e];
+        }
     }
     // Ainv, P, G, beta
     float* gAi = a.ws + a.L.ai + int64_t(u) * kBC * kBC;
     float* gPm = a.ws + a.L.pm + int64_t(u) * kBC * kBC;
     float* gGm = a.ws + a.L.gm + int64_t(u) * kBC * kBC;
     for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
-        const int i = e / kBC, j = e % kBC;
+        const int i = e >> 5, j = e & (kBC - 1);
         gAi[e] = Ai[i * CS + j];
         gPm[e] = Pm[i * CS + j];
         gGm[e] = Gm[i * CS + j];
@@ -367,7 +418,6 @@ __global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs
 // ------------------------------------------------------------------------------ 4. chunk grads
 
 constexpr int kSlice = 64;   // columns of D per pass in bwd_chunk_grads
-constexpr int kCS = kBC + 4; // row stride of the C x C tiles (16-byte rows, few bank clashes)
 
 // Padded d_v: the d_v contraction runs in 16-deep blocks; the row stride adds 4 floats.
 __host__ __device__ inline int grads_dv16(int d_v) { return (d_v + 15) & ~15; }
@@ -798,7 +848,7 @@ bool plan_backward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
 }
 
 static int lds_prep_bytes(int D, int d_k, int d_v) {
-    return 4 * (2 * kBC * 2 * d_k + 2 * kBC * tile_stride(D) + 3 * kBC * (kBC + 1) + kBC +
+    return 4 * (2 * kBC * 2 * d_k + 2 * kBC * tile_stride(D) + 3 * kBC * kCS + kBC +
                 kBC * d_v);
 }
 static int lds_grads_bytes(int d_v) {

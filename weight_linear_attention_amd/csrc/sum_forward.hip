@@ -60,7 +60,8 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     const int t0 = n * kBC;
     const int tid = threadIdx.x;
     const int rows = a.T - t0 < kBC ? a.T - t0 : kBC;
-    constexpr int CS = kBC + 1;
+    const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    constexpr int CS = kBC + 4;       // 16-byte rows for the MFMA operand reads
     const int SD = tile_stride(D);
     float* xk = lds;
     float* xq = xk + kBC * two;
@@ -70,38 +71,56 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     float* Vs = Mm + kBC * CS;
     load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
     load_relu_rows<BF16>(a.q, xq, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
-    for (int i = tid; i < kBC * d_v; i += kSumThreads) {
-        const int c = i / d_v, r = i % d_v;
-        Vs[i] = c < rows ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
-    }
+    for (int c = wv; c < kBC; c += kSumThreads / 64)
+        for (int r = lane; r < d_v; r += 64)
+            Vs[c * d_v + r] = c < rows ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
     dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
-    for (int e = tid; e < kBC * D; e += kSumThreads) {
-        const int c = e / D, p = e % D;
-        gK[e] = Kt[c * SD + p];
-        gQ[e] = Qt[c * SD + p];
-    }
-    // M = lower_incl(Q K^T): thread -> (row c, columns j0 + 8 e, e < 4)
-    {
-        const int c = tid / 8, j0 = tid % 8;
-        float m[4] = {0, 0, 0, 0};
-        for (int p = 0; p < D; ++p) {
-            const float qc = Qt[c * SD + p];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m[e] += qc * Kt[(j0 + 8 * e) * SD + p];
+    for (int c = wv; c < kBC; c += kSumThreads / 64)
+        for (int p = lane; p < D; p += 64) {
+            gK[c * D + p] = Kt[c * SD + p];
+            gQ[c * D + p] = Qt[c * SD + p];
         }
+    // M = lower_incl(Q K^T) on the fp32 MFMA: wave w < 3 takes tile (0,0), (1,0), (1,1); wave 3
+    // zeroes tile (0, 1).  Lane group g supplies k = 4 g + s to sub-step s of a 16-deep block.
+    if (wv < 3) {
+        const int it = wv == 0 ? 0 : 1, jt = wv == 2 ? 1 : 0;
+        f32x4 acc = zero4();
+        for (int kb = 0; kb < D; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Qt + (16 * it + l16) * SD + kb + 4 * g4);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(Kt + (16 * jt + l16) * SD + kb + 4 * g4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Mm[c * CS + j0 + 8 * e] = (j0 + 8 * e <= c) ? m[e] : 0.0f;
+            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+        }
+        const int col = 16 * jt + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * it + 4 * g4 + e;
+            Mm[row * CS + col] = col <= row ? acc[e] : 0.0f;
+        }
+    } else {
+        for (int e = lane; e < 256; e += 64) Mm[(e >> 4) * CS + 16 + (e & 15)] = 0.0f;
     }
     __syncthreads();
+    // M V ([c][r]) on the fp32 MFMA: tiles (it, rt), wave w takes w + 4 q
     float* gN = a.ws + a.L.nm + int64_t(u) * kBC * d_v;
-    for (int e = tid; e < kBC * d_v; e += kSumThreads) {
-        const int c = e / d_v, r = e % d_v;
-        float s = 0.0f;
-        for (int j = 0; j <= c; ++j) s += Mm[c * CS + j] * Vs[j * d_v + r];
-        gN[e] = s;
+    for (int tau = wv; tau < 2 * ((d_v + 15) / 16); tau += 4) {
+        const int it = tau & 1, rt = tau >> 1;
+        const int r = 16 * rt + l16;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < kBC; kb += 16) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Mm + (16 * it + l16) * CS + kb + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = mfma_f32_k4(av[s], r < d_v ? Vs[(kb + 4 * g4 + s) * d_v + r] : 0.0f, acc);
+        }
+        if (r < d_v) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gN[(16 * it + 4 * g4 + e) * d_v + r] = acc[e];
+        }
     }
     if (tid < kBC) {
         float s = 0.0f;
@@ -241,7 +260,7 @@ static hipError_t launch_sum_t(const SumArgs& a, hipStream_t stream) {
     const int64_t NU = int64_t(a.BH) * a.NC;
     hipError_t e;
     if (NU > 0) {
-        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * tile_stride(a.D) + kBC * (kBC + 1) +
+        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * tile_stride(a.D) + kBC * (kBC + 4) +
                             kBC * a.d_v);
         auto kp = sum_prep_kernel<BF16>;
         if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kp), lp)) != hipSuccess) return e;

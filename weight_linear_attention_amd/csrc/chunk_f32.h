@@ -16,12 +16,23 @@ constexpr int kRowWaves = 8;         // memory rows per serial workgroup (one wa
 template <bool BF16>
 __device__ __forceinline__ void load_relu_rows(const void* src, float* xs, int64_t base, int rows,
                                                int t0, int d_k, int tid, int nthr) {
-    const int two = 2 * d_k;
-    for (int i = tid; i < kBC * d_k; i += nthr) {
-        const int c = i / d_k, j = i % d_k;
-        const float x = c < rows ? load_elem<BF16>(src, (base + t0 + c) * d_k + j) : 0.0f;
-        xs[c * two + j] = relu(x);
-        xs[c * two + d_k + j] = relu(-x);
+    // d_k is a power of two up to 64 and nthr >= 256: at most 8 elements per thread, all loads
+    // issued before the first store
+    const int two = 2 * d_k, lg = __builtin_ctz(d_k);
+    constexpr int kMax = kBC * 64 / 256;
+    float xv[kMax];
+#pragma unroll
+    for (int m = 0; m < kMax; ++m) {
+        const int i = tid + nthr * m, c = i >> lg, j = i & (d_k - 1);
+        xv[m] = (i < kBC * d_k && c < rows) ? load_elem<BF16>(src, (base + t0 + c) * d_k + j) : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < kMax; ++m) {
+        const int i = tid + nthr * m, c = i >> lg, j = i & (d_k - 1);
+        if (i < kBC * d_k) {
+            xs[c * two + j] = relu(xv[m]);
+            xs[c * two + d_k + j] = relu(-xv[m]);
+        }
     }
 }
 
@@ -44,8 +55,9 @@ __device__ __forceinline__ void dpfp_tiles(const float* xa, const float* xb, flo
     const float* xra = xa + c * two;
     const float* xrb = xb + c * two;
     float sa = 0.0f, sb = 0.0f;
+    // position j and shift i of column p = (i - 1) 2 d_k + j, advanced without divisions
+    int i = 1, j = s0;
     for (int p = s0; p < D; p += 8) {
-        const int i = p / two + 1, j = p % two;
         int src = j - i;
         src += (src < 0) ? two : 0;
         const float ra = xra[j] * xra[src], rb = xrb[j] * xrb[src];
@@ -53,6 +65,11 @@ __device__ __forceinline__ void dpfp_tiles(const float* xa, const float* xb, flo
         Fb[c * SD + p] = rb;
         sa += ra;
         sb += rb;
+        j += 8;
+        if (j >= two) {
+            j -= two;
+            ++i;
+        }
     }
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) {

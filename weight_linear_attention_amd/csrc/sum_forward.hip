@@ -8,11 +8,10 @@
 //   Y = (Q W0^T + M V) / (Q z0 + M 1)   (row-wise),   W1 = W0 + V^T K,   z1 = z0 + K^T 1.
 // Three launches:
 //   1. sum_prep  per chunk: K, Q, and the chunk-local parts M V and M 1            (parallel)
-//   2. sum_scan  per (b, h, 8 rows of W), chunks in order: row r of W moves on its own
-//      (w <- w + K^T V[:, r]); each wave also carries z (the same for every row), so it forms
-//      y[:, r] itself                                                                (serial)
+//   2. sum_scan  per (b, h, 16 rows of W), chunks in order: W^T in fp32 MFMA accumulators
+//      split over the 4 waves by d-tiles; Q W^T, Q z, y, then W^T += K^T V, z += K^T 1 (serial)
 //   3. sum_zfinal per (b, h): z_final from z0 and the chunks' key sums (where it is asked for)
-// Arithmetic is fp32 on the vector ALU; chunks of 32 rows.
+// Arithmetic is fp32 (the vector ALU and the fp32 MFMA); chunks of 32 rows.
 #include "chunk_f32.h"
 #include "fwa_internal.h"
 
@@ -145,93 +144,189 @@ __global__ __launch_bounds__(256) void sum_zfinal_kernel(SumArgs a) {
     }
 }
 
-// Lane l holds w[l + 64 m] (row r of W) and zz[l + 64 m] (z), m < NPL.  The next chunk's K
-// and Q tiles load into registers while the current chunk computes.
-template <bool BF16, int NPL>
-__global__ __launch_bounds__(64 * kRowWaves) void sum_scan_kernel(SumArgs a) {
+// One workgroup of 4 waves per (b, h, 16 columns of W = 16 rows of the memory), chunks in
+// order.  The memory W^T (D x 16) lives in fp32 MFMA accumulators, wave w holding d-tiles
+// w + 4 q (rows d = 16 dt + 4 (l / 16) + e, column l % 16 of lane l, slot e), which is exactly
+// the B operand of a 16x16x4 product over those d (lane group g supplies k = 4 g + s to
+// sub-step s).  Per chunk:
+//   1. each wave forms its part of Q W^T over its d-tiles (two 16-row tiles) and of Q z (z, the
+//      same for every column, sits in LDS), into LDS;
+//   2. waves 0 and 1 sum the four parts of row tile 0 and 1 and write y = (Q W^T + M V) /
+//      (Q z + M 1) (0 where the denominator is exactly 0);
+//   3. each wave adds K^T V to its d-tiles and K^T 1 to its entries of z (K and V staged
+//      transposed, so every operand read is one 16-byte read per lane).
+// The next chunk's K and Q tiles, V columns and chunk-local parts load into registers while
+// the current chunk computes.
+template <bool BF16, int NDW>
+__global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
     extern __shared__ float lds[];
-    const int D = a.D, d_v = a.d_v;
-    const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
-    const int bh = blockIdx.x / rgroups;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
-    const bool live = r < d_v;
-    constexpr int SDP = 64 * NPL;     // padded LDS row stride of the staged tiles
-    float* Kt = lds;                  // [C][SDP]
-    float* Qt = Kt + kBC * SDP;
-    int slot[NPL];
-    tile_slots<NPL>(slot, D, tid);
-    zero_tile_pads<NPL>(Kt, D, tid);
-    zero_tile_pads<NPL>(Qt, D, tid);
-    float w[NPL], zz[NPL];
+    const int D = a.D, d_v = a.d_v, NDT = a.D / 16;
+    const int cgroups = (d_v + 15) / 16;
+    const int bh = blockIdx.x / cgroups, col0 = (blockIdx.x % cgroups) * 16;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int col = col0 + l16;
+    const bool cok = col < d_v;
+    const int SDQ = D + 4;                    // row stride of the staged tiles
+    constexpr int VS = kBC + 4;               // row stride of V^T
+    float* Qt = lds;                          // [C][SDQ]
+    float* KT = Qt + kBC * SDQ;               // [D][VS]: K^T
+    float* Vt = KT + D * VS;                  // [16][VS]: V^T of the chunk's 16 columns
+    float* zs = Vt + 16 * VS;                 // [D]
+    f32x4* red = reinterpret_cast<f32x4*>(zs + D);   // [4 waves][2 row tiles][64 lanes]
+    float* qzr = reinterpret_cast<float*>(red + 4 * 2 * 64);   // [4][C]
+
+    // memory tiles and z
+    f32x4 W[NDW];
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-        const int p = lane + 64 * m;
-        w[m] = (live && a.W0 && p < D) ? a.W0[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
-        zz[m] = (a.z0 && p < D) ? a.z0[int64_t(bh) * D + p] : 0.0f;
+    for (int q = 0; q < NDW; ++q) {
+        const int dt = wv + 4 * q;
+        W[q] = zero4();
+        if (a.W0 && cok && dt < NDT)
+            W[q] = *reinterpret_cast<const f32x4*>(a.W0 + (int64_t(bh) * d_v + col) * D + 16 * dt + 4 * g4);
+    }
+    for (int d = tid; d < D; d += 256) zs[d] = a.z0 ? a.z0[int64_t(bh) * D + d] : 0.0f;
+
+    // staging units: Q as 16-byte units u = tid + 256 m of the [C][D] tile (row u / (D / 4));
+    // K^T as units (column d = u % D, rows 4 (u / D) .. + 3), four loads down a column of K
+    // (coalesced along D over the lanes) and one 16-byte store.  The LDS offsets are fixed, so
+    // they are computed once.
+    const int units = kBC * D / 4;
+    constexpr int NUM = 2 * NDW;              // D / 32 <= 2 NDW units per thread and tile
+    int loff[NUM], koff[NUM], kgo[NUM];
+#pragma unroll
+    for (int m = 0; m < NUM; ++m) {
+        const int uu = tid + 256 * m;
+        const int c = uu / (D / 4), c4 = uu - c * (D / 4);
+        loff[m] = uu < units ? c * SDQ + 4 * c4 : -1;
+        const int kc = uu / D, kd = uu - kc * D;
+        koff[m] = kd * VS + 4 * kc;
+        kgo[m] = 4 * kc * D + kd;
     }
     const int64_t CD = int64_t(kBC) * D;
-    const int n_tile = kBC * D;
-    f32x4 rk[NPL], rq[NPL];
-    float v_next = 0.0f, nm_next = 0.0f, dn_next = 0.0f;
-    // v[t, r] in lane t - t0; the chunk-local parts of row lane >> 1
-#define FWA_SUM_FETCH(nn)                                                                       \
-    do {                                                                                       \
-        const int64_t uf = int64_t(bh) * a.NC + (nn);                                          \
-        prefetch_tile<NPL>(rk, a.ws + a.L.kt + uf * CD, n_tile, tid);                          \
-        prefetch_tile<NPL>(rq, a.ws + a.L.qt + uf * CD, n_tile, tid);                          \
-        const int tf = (nn) * kBC + lane;                                                      \
-        v_next = (live && lane < kBC && tf < a.T)                                             \
-                     ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + tf) * d_v + r) : 0.0f;       \
-        nm_next = live ? a.ws[a.L.nm + (uf * kBC + (lane >> 1)) * d_v + r] : 0.0f;            \
-        dn_next = a.ws[a.L.dn + uf * kBC + (lane >> 1)];                                       \
-    } while (0)
-    if (a.NC > 0) FWA_SUM_FETCH(0);
+    f32x4 pq[NUM], pk[NUM];
+    float pv[2], pnm[4], pdn[4];
+    auto fetch = [&](int n) {
+        const int64_t uf = int64_t(bh) * a.NC + n;
+        const f32x4* gq = reinterpret_cast<const f32x4*>(a.ws + a.L.qt + uf * CD);
+        const float* gk = a.ws + a.L.kt + uf * CD;
+#pragma unroll
+        for (int m = 0; m < NUM; ++m) {
+            const int uu = tid + 256 * m;
+            pq[m] = uu < units ? gq[uu] : zero4();
+            pk[m] = zero4();
+            if (uu < units) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pk[m][q] = gk[kgo[m] + q * D];
+            }
+        }
+        // V^T: element e = tid + 256 m2 -> (c = e / 16, column e % 16)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int e = tid + 256 * m2, c = e >> 4, cc = col0 + (e & 15);
+            const int t = n * kBC + c;
+            pv[m2] = (t < a.T && cc < d_v) ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t) * d_v + cc) : 0.0f;
+        }
+        // chunk-local parts of the rows this lane writes (row tile wv, waves 0 and 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 16 * (wv & 1) + 4 * g4 + e;
+            pnm[e] = cok ? a.ws[a.L.nm + (uf * kBC + c) * d_v + col] : 0.0f;
+            pdn[e] = a.ws[a.L.dn + uf * kBC + c];
+        }
+    };
+    if (a.NC > 0) fetch(0);
     for (int n = 0; n < a.NC; ++n) {
         const int t0 = n * kBC;
-        lds_barrier();
-        commit_tile<NPL>(Kt, rk, slot);
-        commit_tile<NPL>(Qt, rq, slot);
-        const float vc = v_next, nm = nm_next, dn = dn_next;
-        lds_barrier();
-        if (n + 1 < a.NC) FWA_SUM_FETCH(n + 1);
-        float pn[kBC], pd[kBC];
+        __syncthreads();                      // the previous chunk's tile reads are done
 #pragma unroll
-        for (int c = 0; c < kBC; ++c) {
-            float sn = 0.0f, sd = 0.0f;
-#pragma unroll
-            for (int m = 0; m < NPL; ++m) {
-                const float qv = Qt[c * SDP + lane + 64 * m];
-                sn += qv * w[m];
-                sd += qv * zz[m];
+        for (int m = 0; m < NUM; ++m)
+            if (loff[m] >= 0) {
+                *reinterpret_cast<f32x4*>(Qt + loff[m]) = pq[m];
+                *reinterpret_cast<f32x4*>(KT + koff[m]) = pk[m];
             }
-            pn[c] = sn;
-            pd[c] = sd;
-        }
-        const float qw = wave_reduce_scatter32(pn);           // (Q w)[lane >> 1]
-        const float qz = wave_reduce_scatter32(pd);           // (Q z)[lane >> 1]
-        const int c = lane >> 1;
-        if (live && (lane & 1) == 0 && t0 + c < a.T) {
-            const float num = qw + nm, den = qz + dn;
-            store_elem<BF16>(a.y, (int64_t(bh) * a.T + t0 + c) * d_v + r, den != 0.0f ? num / den : 0.0f);
-        }
 #pragma unroll
-        for (int cc = 0; cc < kBC; ++cc) {
-            const float vv = lane_value(vc, cc);
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int e = tid + 256 * m2;
+            Vt[(e & 15) * VS + (e >> 4)] = pv[m2];
+        }
+        float nm[4], dn[4];
 #pragma unroll
-            for (int m = 0; m < NPL; ++m) {
-                const float kv = Kt[cc * SDP + lane + 64 * m];
-                w[m] += vv * kv;
-                zz[m] += kv;
+        for (int e = 0; e < 4; ++e) {
+            nm[e] = pnm[e];
+            dn[e] = pdn[e];
+        }
+        __syncthreads();
+        if (n + 1 < a.NC) fetch(n + 1);
+        // ---- 1. parts of Q W^T (MFMA) and Q z (lane -> row c = lane % 32, half of each d-tile)
+        f32x4 P0 = zero4(), P1 = zero4();
+        float qz = 0.0f;
+        const int cz = lane & 31, hz = lane >> 5;
+#pragma unroll
+        for (int q = 0; q < NDW; ++q) {
+            const int dt = wv + 4 * q;
+            if (dt >= NDT) continue;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(Qt + l16 * SDQ + 16 * dt + 4 * g4);
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(Qt + (16 + l16) * SDQ + 16 * dt + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                P0 = mfma_f32_k4(a0[s], W[q][s], P0);
+                P1 = mfma_f32_k4(a1[s], W[q][s], P1);
             }
+#pragma unroll
+            for (int dd = 0; dd < 8; ++dd) {
+                const int d = 16 * dt + 8 * hz + dd;
+                qz += Qt[cz * SDQ + d] * zs[d];
+            }
+        }
+        qz += __shfl_xor(qz, 32);
+        red[(wv * 2 + 0) * 64 + lane] = P0;
+        red[(wv * 2 + 1) * 64 + lane] = P1;
+        if (lane < kBC) qzr[wv * kBC + lane] = qz;
+        __syncthreads();
+        // ---- 2. y rows of row tile wv (waves 0, 1)
+        if (wv < 2) {
+            const int rt = wv;
+            const f32x4 num = (red[(0 * 2 + rt) * 64 + lane] + red[(1 * 2 + rt) * 64 + lane]) +
+                              (red[(2 * 2 + rt) * 64 + lane] + red[(3 * 2 + rt) * 64 + lane]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * rt + 4 * g4 + e;
+                const float den = (qzr[c] + qzr[kBC + c]) + (qzr[2 * kBC + c] + qzr[3 * kBC + c]) + dn[e];
+                const float nv = num[e] + nm[e];
+                if (cok && t0 + c < a.T)
+                    store_elem<BF16>(a.y, (int64_t(bh) * a.T + t0 + c) * d_v + col,
+                                     den != 0.0f ? nv / den : 0.0f);
+            }
+        }
+        // ---- 3. W^T += K^T V and z += K^T 1 on this wave's d-tiles
+#pragma unroll
+        for (int q = 0; q < NDW; ++q) {
+            const int dt = wv + 4 * q;
+            if (dt >= NDT) continue;
+            const float* kr = KT + (16 * dt + l16) * VS;
+#pragma unroll
+            for (int kb = 0; kb < kBC; kb += 16) {
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(Vt + l16 * VS + kb + 4 * g4);
+                const f32x4 av = *reinterpret_cast<const f32x4*>(kr + kb + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) W[q] = mfma_f32_k4(av[s], bv[s], W[q]);
+            }
+            const f32x4 z0v = *reinterpret_cast<const f32x4*>(kr + 8 * g4);
+            const f32x4 z1v = *reinterpret_cast<const f32x4*>(kr + 8 * g4 + 4);
+            float zp = (z0v[0] + z0v[1]) + (z0v[2] + z0v[3]) + (z1v[0] + z1v[1]) + (z1v[2] + z1v[3]);
+            zp += __shfl_xor(zp, 16);
+            zp += __shfl_xor(zp, 32);
+            if (g4 == 0) zs[16 * dt + l16] += zp;
         }
     }
+    if (a.Wf && cok) {
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-        const int p = lane + 64 * m;
-        if (p < D && live && a.Wf) a.Wf[(int64_t(bh) * d_v + r) * D + p] = w[m];
+        for (int q = 0; q < NDW; ++q) {
+            const int dt = wv + 4 * q;
+            if (dt < NDT)
+                *reinterpret_cast<f32x4*>(a.Wf + (int64_t(bh) * d_v + col) * D + 16 * dt + 4 * g4) = W[q];
+        }
     }
-#undef FWA_SUM_FETCH
 }
 
 bool plan_sum_forward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
@@ -243,15 +338,16 @@ bool plan_sum_forward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes
     return true;
 }
 
-template <int NPL, bool BF16>
+template <int NDW, bool BF16>
 static hipError_t launch_scan(const SumArgs& a, hipStream_t stream) {
-    const int rgroups = (a.d_v + kRowWaves - 1) / kRowWaves;
-    auto kern = sum_scan_kernel<BF16, NPL>;
-    const int lds = 4 * 2 * kBC * 64 * NPL;
+    const int cgroups = (a.d_v + 15) / 16;
+    auto kern = sum_scan_kernel<BF16, NDW>;
+    const int lds = 4 * (kBC * (a.D + 4) + a.D * (kBC + 4) + 16 * (kBC + 4) + a.D + 4 * 2 * 64 * 4 +
+                         4 * kBC);
     hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(int64_t(a.BH) * rgroups)),
-                       dim3(64 * kRowWaves), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(int64_t(a.BH) * cgroups)), dim3(256), lds,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -267,7 +363,7 @@ static hipError_t launch_sum_t(const SumArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(kp, dim3(static_cast<unsigned>(NU)), dim3(kSumThreads), lp, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    switch ((a.D + 63) / 64) {
+    switch ((a.D / 16 + 3) / 4) {
         case 1: e = launch_scan<1, BF16>(a, stream); break;
         case 2: e = launch_scan<2, BF16>(a, stream); break;
         case 3: e = launch_scan<3, BF16>(a, stream); break;

@@ -441,7 +441,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": name if kind != "prefill+decode" else
-                   f"{w.name}: chunked forward over B*T tokens + 1 decode step per sequence",
+                   f"{w.name}: forward over B*T tokens (chunk {w.chunk}) + 1 decode step per sequence",
                    "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "nu": w.nu,
                    "D": D, "chunk": w.chunk, "tokens_per_step": tokens,
                    "initial_memory": "zeros" if w.w0_std is None else f"N(0,{w.w0_std}^2)"},

@@ -374,8 +374,7 @@ def main():
             flops = BH * w.T * (12 * D * w.d_v + 12 * D)
             nbytes = (BH * w.T * ((4 * w.d_k + 2 * w.d_v + 2 + w.d_v) * es)
                       + BH * w.d_v * D * 4 * (2 + (d["W0"] is not None)))
-            kname = ("fwa_delta_backward: bwd_prep + bwd_fwd_states + bwd_grad_states + "
-                     "bwd_chunk_grads + bwd_dpfp")
+            kname = "fwa_delta_backward: bwd_prep + bwd_states + bwd_chunk_grads + bwd_dpfp"
         else:
             flops = BH * w.T * (4 * D * w.d_v + 9 * D)
             nbytes = (BH * w.T * (2 * w.d_k + 2 * w.d_v) * es

@@ -43,10 +43,10 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t NU, int D, int d_v) {
     int64_t o = 0;
     const int64_t CD = int64_t(kBC) * D, CC = int64_t(kBC) * kBC, CV = int64_t(kBC) * d_v;
     const int64_t VD = int64_t(d_v) * D;
-    L.kt = o; o += NU * CD;
-    L.qt = o; o += NU * CD;
-    L.wy = o; o += NU * CD;      // Wy, then dK (bwd_chunk_grads)
-    L.qp = o; o += NU * CD;      // Q', then dQ
+    L.kt = o; o += NU * CD;      // K^T [d][c]
+    L.qt = o; o += NU * CD;      // Q^T [d][c]
+    L.wy = o; o += NU * CD;      // Wy^T [d][c], then dK [c][d] (bwd_chunk_grads)
+    L.qp = o; o += NU * CD;      // Q'^T [d][c], then dQ [c][d]
     L.ai = o; o += NU * CC;
     L.pm = o; o += NU * CC;
     L.gm = o; o += NU * CC;
@@ -119,13 +119,20 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
             Vs[c * d_v + r] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
     dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
+    // K and Q leave transposed ([D][C]): unit e = 4 consecutive rows c of column d = e / 8
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
-    for (int c = wv; c < kBC; c += kPrepThreads2 / 64)
-        for (int p = lane; p < D; p += 64) {
-            gK[c * D + p] = Kt[c * SD + p];
-            gQ[c * D + p] = Qt[c * SD + p];
+    for (int e = tid; e < 8 * D; e += kPrepThreads2) {
+        const int d = e >> 3, c0 = 4 * (e & 7);
+        f32x4 kv, qv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kv[j] = Kt[(c0 + j) * SD + d];
+            qv[j] = Qt[(c0 + j) * SD + d];
         }
+        *reinterpret_cast<f32x4*>(gK + 4 * e) = kv;
+        *reinterpret_cast<f32x4*>(gQ + 4 * e) = qv;
+    }
     // G = K K^T (all four tiles) and P = lower_incl(Q K^T) (tiles (0,0), (1,0), (1,1));
     // wave w takes tiles w and w + 4 of that list
     for (int tau = wv; tau < 7; tau += 4) {
@@ -194,8 +201,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
             for (int s = 0; s < 4; ++s)
                 wy[q] = mfma_f32_k4(av[s], Kt[(kb + 4 * g4 + s) * SD + 16 * pt + l16], wy[q]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gWy[int64_t(16 * it + 4 * g4 + e) * D + 16 * pt + l16] = wy[q][e];
+        *reinterpret_cast<f32x4*>(gWy + (16 * pt + l16) * kBC + 16 * it + 4 * g4) = wy[q];   // [D][C]
     }
     __syncthreads();                                             // K is dead: W_y over it
 #pragma unroll
@@ -219,11 +225,11 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
             for (int s = 0; s < 4; ++s)
                 acc = mfma_f32_k4(av[s], Kt[(kb + 4 * g4 + s) * SD + 16 * pt + l16], acc);
         }
+        const int col = 16 * pt + l16;
+        f32x4 qp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * it + 4 * g4 + e, col = 16 * pt + l16;
-            gQp[int64_t(row) * D + col] = Qt[row * SD + col] - acc[e];
-        }
+        for (int e = 0; e < 4; ++e) qp[e] = Qt[(16 * it + 4 * g4 + e) * SD + col] - acc[e];
+        *reinterpret_cast<f32x4*>(gQp + col * kBC + 16 * it + 4 * g4) = qp;      // [D][C]
     }
     // Uy = T V ([c][r])
     float* gUy = a.ws + a.L.uy + int64_t(u) * kBC * d_v;
@@ -256,163 +262,282 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     if (tid < kBC) a.ws[a.L.be + int64_t(u) * kBC + tid] = be[tid];
 }
 
-// ------------------------------------------------------------------------------ row chains
+// ------------------------------------------------------------------------------ state chains
 
-// Chunk-start memories and U: row r of the memory moves as w <- w + K^T u with
-// u = Uy[:, r] - Wy w.  Lane l holds w[l + 64 m], m < NPL.  The next chunk's Wy and K tiles load
-// into registers while the current chunk computes.
-template <int NPL>
-__global__ __launch_bounds__(64 * kRowWaves) void bwd_fwd_states_kernel(BwdArgs a) {
-    extern __shared__ float lds[];
-    const int D = a.D, d_v = a.d_v;
-    const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
-    const int bh = blockIdx.x / rgroups;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
-    const bool live = r < d_v;
-    constexpr int SDP = 64 * NPL;     // padded LDS row stride of the staged tiles
-    float* Wy = lds;                  // [C][SDP]
-    float* Kt = Wy + kBC * SDP;       // [C][SDP]
-    int slot[NPL];
-    tile_slots<NPL>(slot, D, tid);
-    zero_tile_pads<NPL>(Wy, D, tid);
-    zero_tile_pads<NPL>(Kt, D, tid);
-    float w[NPL];
-#pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-        const int p = lane + 64 * m;
-        w[m] = (live && a.W0 && p < D) ? a.W0[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
-    }
-    const int64_t CD = int64_t(kBC) * D;
-    const int n_tile = kBC * D;
-    f32x4 rwy[NPL], rk[NPL];
-    float uy_next = 0.0f;
-#define FWA_BWD_FWD_FETCH(nn)                                                                   \
-    do {                                                                                       \
-        const int64_t uf = int64_t(bh) * a.NC + (nn);                                          \
-        prefetch_tile<NPL>(rwy, a.ws + a.L.wy + uf * CD, n_tile, tid);                         \
-        prefetch_tile<NPL>(rk, a.ws + a.L.kt + uf * CD, n_tile, tid);                          \
-        uy_next = live ? a.ws[a.L.uy + uf * kBC * d_v + (lane >> 1) * d_v + r] : 0.0f;        \
-    } while (0)
-    if (a.NC > 0) FWA_BWD_FWD_FETCH(0);
-    for (int n = 0; n < a.NC; ++n) {
-        const int64_t u = int64_t(bh) * a.NC + n;
-        if (live) {
-            float* gw = a.ws + a.L.ws + (u * d_v + r) * D;
-#pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) gw[lane + 64 * m] = w[m];
-        }
-        lds_barrier();
-        commit_tile<NPL>(Wy, rwy, slot);
-        commit_tile<NPL>(Kt, rk, slot);
-        const float uy = uy_next;
-        lds_barrier();
-        if (n + 1 < a.NC) FWA_BWD_FWD_FETCH(n + 1);
-        float part[kBC];
-#pragma unroll
-        for (int c = 0; c < kBC; ++c) {
-            float sacc = 0.0f;
-#pragma unroll
-            for (int m = 0; m < NPL; ++m) sacc += Wy[c * SDP + lane + 64 * m] * w[m];
-            part[c] = sacc;
-        }
-        const float x = wave_reduce_scatter32(part);          // (Wy w)[lane >> 1]
-        const float uc = uy - x;
-        if (live && (lane & 1) == 0) a.ws[a.L.uu + (u * d_v + r) * kBC + (lane >> 1)] = uc;
-#pragma unroll
-        for (int c = 0; c < kBC; ++c) {
-            const float uv = lane_value(uc, 2 * c);
-#pragma unroll
-            for (int m = 0; m < NPL; ++m) w[m] += uv * Kt[c * SDP + lane + 64 * m];
-        }
-    }
-#undef FWA_BWD_FWD_FETCH
+// The two chains over the chunks, one launch: workgroups [0, G) run the forward chain of the
+// chunk-start memories, workgroups [G, 2 G) the reverse chain of the chunk-end memory
+// gradients (G = B H ceil(d_v / 16)); neither reads what the other writes.  A workgroup of 8
+// waves owns 16 rows r of one memory, held transposed (D x 16) in fp32 MFMA accumulators: wave
+// w holds d-tiles dt = w + 8 q (rows d = 16 dt + 4 (l / 16) + e, column l % 16 of lane l, slot
+// e), which is the B operand of a 16x16x4 product over those d as it stands (lane group g
+// supplies k = 4 g + s to sub-step s).  Per chunk each wave forms its part of a 32 x 16 product
+// over its d-tiles, waves 0 and 1 sum the eight parts of one 16-row tile each into LDS (in the
+// layout of the update's B operand), and each wave updates its d-tiles.  The per-chunk [D][C]
+// tiles are stored transposed in the workspace and staged as they are into LDS rows of kTS
+// floats; the next chunk's tiles load into registers while the current chunk computes.
+constexpr int kStWaves = 8;
+constexpr int kStThreads = 64 * kStWaves;
+constexpr int kTS = kBC + 4;     // LDS row stride of the transposed tiles and the [16][C] operands
+
+// LDS floats of the state chains: two [D][kTS] tiles, two [16][kTS] operands, the per-wave
+// partial products (8 waves x 2 row tiles x 64 lanes x 4)
+__host__ __device__ inline int states_lds_floats(int D) {
+    return 2 * D * kTS + 2 * 16 * kTS + kStWaves * 2 * 64 * 4;
 }
 
-// Chunk-end gradients of the memory, K dW1^T and dW0, chunks in reverse: row r of the
-// gradient moves as g <- g + Q'^T dY[:, r] - Wy^T (K g).  The previous chunk's tiles load into
-// registers while the current chunk computes.
-template <bool BF16, int NPL>
-__global__ __launch_bounds__(64 * kRowWaves) void bwd_grad_states_kernel(BwdArgs a) {
-    extern __shared__ float lds[];
-    const int D = a.D, d_v = a.d_v;
-    const int rgroups = (d_v + kRowWaves - 1) / kRowWaves;
-    const int bh = blockIdx.x / rgroups;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = (blockIdx.x % rgroups) * kRowWaves + wave;
-    const bool live = r < d_v;
-    constexpr int SDP = 64 * NPL;     // padded LDS row stride of the staged tiles
-    float* Kt = lds;                  // [C][SDP]
-    float* Qp = Kt + kBC * SDP;
-    float* Wy = Qp + kBC * SDP;
-    int slot[NPL];
-    tile_slots<NPL>(slot, D, tid);
-    zero_tile_pads<NPL>(Kt, D, tid);
-    zero_tile_pads<NPL>(Qp, D, tid);
-    zero_tile_pads<NPL>(Wy, D, tid);
-    float g[NPL];
+// Every lane issues the same loads (a unit past the tile loads the last one again and is not
+// committed), so the in-order load counter lets each commit wait for its own tile only.
+template <int NUM>
+__device__ __forceinline__ void fetch_tile_t(f32x4 (&r)[NUM], const float* g, int units, int tid) {
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) {
-        const int p = lane + 64 * m;
-        g[m] = (live && a.dWf && p < D) ? a.dWf[(int64_t(bh) * d_v + r) * D + p] : 0.0f;
+    for (int m = 0; m < NUM; ++m) r[m] = g4[min(tid + kStThreads * m, units - 1)];
+}
+
+// unit uu = 4 consecutive c of row d = uu / 8
+template <int NUM>
+__device__ __forceinline__ void commit_tile_t(float* s, const f32x4 (&r)[NUM], int units, int tid) {
+#pragma unroll
+    for (int m = 0; m < NUM; ++m) {
+        const int uu = tid + kStThreads * m;
+        if (uu < units) *reinterpret_cast<f32x4*>(s + (uu >> 3) * kTS + 4 * (uu & 7)) = r[m];
+    }
+}
+
+// This wave's part of X^T = A S^T over its d-tiles, A ([C][D]) read from its transposed LDS copy
+// AT ([D][kTS]) and S^T in the accumulators, into red: rows c = 16 rt + 4 (l / 16) + e of X^T
+// in red[wave][rt][lane].
+template <int NDW>
+__device__ __forceinline__ void states_partial(const float* AT, const f32x4 (&S)[NDW], int NDT,
+                                               int wv, int lane, f32x4* red) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+    f32x4 P0 = zero4(), P1 = zero4();
+#pragma unroll
+    for (int q = 0; q < NDW; ++q) {
+        const int dt = wv + kStWaves * q;
+        if (dt >= NDT) continue;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float* row = AT + (16 * dt + 4 * g4 + s) * kTS;
+            P0 = mfma_f32_k4(row[l16], S[q][s], P0);
+            P1 = mfma_f32_k4(row[16 + l16], S[q][s], P1);
+        }
+    }
+    red[(wv * 2 + 0) * 64 + lane] = P0;
+    red[(wv * 2 + 1) * 64 + lane] = P1;
+}
+
+// The sum of the eight waves' parts of row tile rt, in this lane's accumulator slots.
+__device__ __forceinline__ f32x4 states_sum(const f32x4* red, int rt, int lane) {
+    f32x4 x = red[rt * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kStWaves; ++w) x += red[(w * 2 + rt) * 64 + lane];
+    return x;
+}
+
+// Row r of the memory moves as w <- w + K^T u with u = Uy[:, r] - Wy w (the chunk's own
+// correction of the values, "Linear Transformers Are Secretly Fast Weight Programmers",
+// delta rule in chunked form); writes each chunk-start memory and u.
+template <int NDW>
+__device__ __forceinline__ void fwd_states_chain(const BwdArgs& a, float* lds, int bh, int r0) {
+    const int D = a.D, d_v = a.d_v, NDT = D / 16;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int r = r0 + l16;
+    const bool rok = r < d_v;
+    float* WyT = lds;                             // [D][kTS]
+    float* KT = WyT + D * kTS;                    // [D][kTS]
+    float* UyT = KT + D * kTS;                    // [16][kTS]: Uy^T, then u^T
+    f32x4* red = reinterpret_cast<f32x4*>(UyT + 2 * 16 * kTS);  // [8 waves][2][64 lanes]
+    f32x4 W[NDW];
+#pragma unroll
+    for (int q = 0; q < NDW; ++q) {
+        const int dt = wv + kStWaves * q;
+        W[q] = zero4();
+        if (a.W0 && rok && dt < NDT)
+            W[q] = *reinterpret_cast<const f32x4*>(a.W0 + (int64_t(bh) * d_v + r) * D + 16 * dt + 4 * g4);
     }
     const int64_t CD = int64_t(kBC) * D;
-    const int n_tile = kBC * D;
-    f32x4 rk[NPL], rq[NPL], rwy[NPL];
-    float dy_next = 0.0f;
-    // dY[c, r] of the fetched chunk in lane c (zero past the end)
-#define FWA_BWD_GRAD_FETCH(nn)                                                                  \
-    do {                                                                                       \
-        const int64_t uf = int64_t(bh) * a.NC + (nn);                                          \
-        prefetch_tile<NPL>(rk, a.ws + a.L.kt + uf * CD, n_tile, tid);                          \
-        prefetch_tile<NPL>(rq, a.ws + a.L.qp + uf * CD, n_tile, tid);                          \
-        prefetch_tile<NPL>(rwy, a.ws + a.L.wy + uf * CD, n_tile, tid);                         \
-        const int tf = (nn) * kBC + lane;                                                      \
-        dy_next = (live && lane < kBC && tf < a.T)                                            \
-                      ? load_elem<BF16>(a.dy, (int64_t(bh) * a.T + tf) * d_v + r) : 0.0f;     \
-    } while (0)
-    if (a.NC > 0) FWA_BWD_GRAD_FETCH(a.NC - 1);
+    const int units = 8 * D;
+    constexpr int NUM = 2 * NDW;
+    f32x4 rwy[NUM], rk[NUM];
+    // Uy^T element of this thread: row yr = tid % 16 of the 16, chunk row yc = tid / 16 (rows
+    // past d_v load row d_v - 1 and commit 0)
+    const int yc = tid >> 4, yr = tid & 15;
+    const bool yok = r0 + yr < d_v;
+    const int yrc = min(r0 + yr, d_v - 1);
+    float uy_next;
+    auto fetch = [&](int nn) {
+        const int64_t uf = int64_t(bh) * a.NC + nn;
+        fetch_tile_t(rwy, a.ws + a.L.wy + uf * CD, units, tid);
+        fetch_tile_t(rk, a.ws + a.L.kt + uf * CD, units, tid);
+        uy_next = a.ws[a.L.uy + (uf * kBC + yc) * d_v + yrc];
+    };
+    if (a.NC > 0) fetch(0);
+    for (int n = 0; n < a.NC; ++n) {
+        const int64_t u = int64_t(bh) * a.NC + n;
+        if (rok) {
+            float* gw = a.ws + a.L.ws + (u * d_v + r) * D;
+#pragma unroll
+            for (int q = 0; q < NDW; ++q) {
+                const int dt = wv + kStWaves * q;
+                if (dt < NDT) *reinterpret_cast<f32x4*>(gw + 16 * dt + 4 * g4) = W[q];
+            }
+        }
+        lds_barrier();                            // the previous chunk's reads are done
+        commit_tile_t(WyT, rwy, units, tid);
+        commit_tile_t(KT, rk, units, tid);
+        UyT[yr * kTS + yc] = yok ? uy_next : 0.0f;
+        lds_barrier();
+        fetch(n + 1 < a.NC ? n + 1 : n);          // unconditional: the load counts stay fixed
+        states_partial(WyT, W, NDT, wv, lane, red);
+        lds_barrier();
+        // u^T = Uy^T - (Wy W^T)^T: waves 0 and 1 sum row tile wv, each lane rewriting its own
+        // 16 bytes of UyT
+        if (wv < 2) {
+            f32x4* up = reinterpret_cast<f32x4*>(UyT + l16 * kTS + 16 * wv + 4 * g4);
+            const f32x4 uc = *up - states_sum(red, wv, lane);
+            *up = uc;
+            if (rok)
+                *reinterpret_cast<f32x4*>(a.ws + a.L.uu + (u * d_v + r) * kBC + 16 * wv + 4 * g4) = uc;
+        }
+        lds_barrier();
+        // W^T += K^T u on this wave's d-tiles
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(UyT + l16 * kTS + 16 * rt + 4 * g4);
+#pragma unroll
+            for (int q = 0; q < NDW; ++q) {
+                const int dt = wv + kStWaves * q;
+                if (dt >= NDT) continue;
+                const f32x4 av = *reinterpret_cast<const f32x4*>(KT + (16 * dt + l16) * kTS + 16 * rt + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) W[q] = mfma_f32_k4(av[s], bv[s], W[q]);
+            }
+        }
+    }
+}
+
+// Row r of the memory gradient moves backwards as g <- g + Q'^T dY[:, r] - Wy^T (K g); writes
+// each chunk-end gradient, K g, and the gradient of the initial memory.  The K tile's LDS rows
+// take the Wy tile once the products with K are done.
+template <bool BF16, int NDW>
+__device__ __forceinline__ void grad_states_chain(const BwdArgs& a, float* lds, int bh, int r0) {
+    const int D = a.D, d_v = a.d_v, NDT = D / 16;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int r = r0 + l16;
+    const bool rok = r < d_v;
+    float* KT = lds;                              // [D][kTS]: K^T, then Wy^T
+    float* WyT = KT;
+    float* QpT = KT + D * kTS;                    // [D][kTS]
+    float* dYT = QpT + D * kTS;                   // [16][kTS]: dY^T of the 16 rows
+    float* AT = dYT + 16 * kTS;                   // [16][kTS]: -(K g)^T
+    f32x4* red = reinterpret_cast<f32x4*>(AT + 16 * kTS);
+    f32x4 G[NDW];
+#pragma unroll
+    for (int q = 0; q < NDW; ++q) {
+        const int dt = wv + kStWaves * q;
+        G[q] = zero4();
+        if (a.dWf && rok && dt < NDT)
+            G[q] = *reinterpret_cast<const f32x4*>(a.dWf + (int64_t(bh) * d_v + r) * D + 16 * dt + 4 * g4);
+    }
+    const int64_t CD = int64_t(kBC) * D;
+    const int units = 8 * D;
+    constexpr int NUM = 2 * NDW;
+    f32x4 rk[NUM], rq[NUM], rwy[NUM];
+    // dY^T element of this thread: row yr = tid % 16 of the 16, chunk row yc = tid / 16, loaded
+    // as stored (clamped into the sequence) and converted when committed
+    using YT = std::conditional_t<BF16, u16, float>;
+    const int yc = tid >> 4, yr = tid & 15;
+    const bool yok = r0 + yr < d_v;
+    const int yrc = min(r0 + yr, d_v - 1);
+    YT dy_next{};
+    auto fetch_kq = [&](int nn) {
+        const int64_t uf = int64_t(bh) * a.NC + nn;
+        fetch_tile_t(rk, a.ws + a.L.kt + uf * CD, units, tid);
+        fetch_tile_t(rq, a.ws + a.L.qp + uf * CD, units, tid);
+        const int tf = min(nn * kBC + yc, a.T - 1);
+        dy_next = static_cast<const YT*>(a.dy)[(int64_t(bh) * a.T + tf) * d_v + yrc];
+    };
+    auto fetch_wy = [&](int nn) {
+        fetch_tile_t(rwy, a.ws + a.L.wy + (int64_t(bh) * a.NC + nn) * CD, units, tid);
+    };
+    if (a.NC > 0) {
+        fetch_kq(a.NC - 1);
+        fetch_wy(a.NC - 1);
+    }
     for (int n = a.NC - 1; n >= 0; --n) {
         const int64_t u = int64_t(bh) * a.NC + n;
-        if (live) {
+        const int nn = n > 0 ? n - 1 : 0;         // unconditional prefetch: load counts stay fixed
+        if (rok) {
             float* gg = a.ws + a.L.gs + (u * d_v + r) * D;
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                if (lane + 64 * m < D) gg[lane + 64 * m] = g[m];
+            for (int q = 0; q < NDW; ++q) {
+                const int dt = wv + kStWaves * q;
+                if (dt < NDT) *reinterpret_cast<f32x4*>(gg + 16 * dt + 4 * g4) = G[q];
+            }
         }
+        lds_barrier();                            // the previous chunk's reads are done
+        commit_tile_t(KT, rk, units, tid);
+        commit_tile_t(QpT, rq, units, tid);
+        dYT[yr * kTS + yc] = (yok && n * kBC + yc < a.T) ? to_f32(dy_next) : 0.0f;
         lds_barrier();
-        commit_tile<NPL>(Kt, rk, slot);
-        commit_tile<NPL>(Qp, rq, slot);
-        commit_tile<NPL>(Wy, rwy, slot);
-        const float dyc = dy_next;
+        fetch_kq(nn);
+        states_partial(KT, G, NDT, wv, lane, red);
         lds_barrier();
-        if (n > 0) FWA_BWD_GRAD_FETCH(n - 1);
-        float part[kBC];
-#pragma unroll
-        for (int c = 0; c < kBC; ++c) {
-            float sacc = 0.0f;
-#pragma unroll
-            for (int m = 0; m < NPL; ++m) sacc += Kt[c * SDP + lane + 64 * m] * g[m];
-            part[c] = sacc;
+        // -(K g)^T: waves 0 and 1 sum row tile wv
+        if (wv < 2) {
+            const f32x4 ac = states_sum(red, wv, lane);
+            *reinterpret_cast<f32x4*>(AT + l16 * kTS + 16 * wv + 4 * g4) = -ac;
+            if (rok)
+                *reinterpret_cast<f32x4*>(a.ws + a.L.aa + (u * d_v + r) * kBC + 16 * wv + 4 * g4) = ac;
         }
-        const float ac = wave_reduce_scatter32(part);         // (K g)[lane >> 1]
-        if (live && (lane & 1) == 0) a.ws[a.L.aa + (u * d_v + r) * kBC + (lane >> 1)] = ac;
-        // partly unrolled: a full unroll hoists all 2 * 32 * NPL tile reads and spills at NPL >= 4
-#pragma unroll 4
-        for (int c = 0; c < kBC; ++c) {
-            const float dy = lane_value(dyc, c), av = lane_value(ac, 2 * c);
+        commit_tile_t(WyT, rwy, units, tid);      // K^T is dead
+        fetch_wy(nn);
+        lds_barrier();
+        // G^T += Q'^T dY - Wy^T (K g) on this wave's d-tiles
 #pragma unroll
-            for (int m = 0; m < NPL; ++m)
-                g[m] += dy * Qp[c * SDP + lane + 64 * m] - av * Wy[c * SDP + lane + 64 * m];
+        for (int rt = 0; rt < 2; ++rt) {
+            const f32x4 by = *reinterpret_cast<const f32x4*>(dYT + l16 * kTS + 16 * rt + 4 * g4);
+            const f32x4 ba = *reinterpret_cast<const f32x4*>(AT + l16 * kTS + 16 * rt + 4 * g4);
+#pragma unroll
+            for (int q = 0; q < NDW; ++q) {
+                const int dt = wv + kStWaves * q;
+                if (dt >= NDT) continue;
+                const int ro = (16 * dt + l16) * kTS + 16 * rt + 4 * g4;
+                const f32x4 aq = *reinterpret_cast<const f32x4*>(QpT + ro);
+                const f32x4 aw = *reinterpret_cast<const f32x4*>(WyT + ro);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    G[q] = mfma_f32_k4(aq[s], by[s], G[q]);
+                    G[q] = mfma_f32_k4(aw[s], ba[s], G[q]);
+                }
+            }
         }
     }
-    if (live && a.dW0) {
+    if (a.dW0 && rok) {
 #pragma unroll
-        for (int m = 0; m < NPL; ++m)
-            if (lane + 64 * m < D) a.dW0[(int64_t(bh) * d_v + r) * D + lane + 64 * m] = g[m];
+        for (int q = 0; q < NDW; ++q) {
+            const int dt = wv + kStWaves * q;
+            if (dt < NDT)
+                *reinterpret_cast<f32x4*>(a.dW0 + (int64_t(bh) * d_v + r) * D + 16 * dt + 4 * g4) = G[q];
+        }
     }
-#undef FWA_BWD_GRAD_FETCH
+}
+
+// Workgroups are dispatched to the 8 XCDs round robin by index: logical index L counts the
+// workgroups of XCD 0 first, then XCD 1, ..., so the row groups of one (b, h) and role, which
+// stage the same tiles in step, share an L2.
+template <bool BF16, int NDW>
+__global__ __launch_bounds__(kStThreads) void bwd_states_kernel(BwdArgs a) {
+    extern __shared__ float lds[];
+    const int rgroups = (a.d_v + 15) / 16;
+    const int G = a.BH * rgroups, N = 2 * G;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int L = x * (N >> 3) + min(x, N & 7) + j;
+    const int b = L < G ? L : L - G;
+    const int bh = b / rgroups, r0 = (b % rgroups) * 16;
+    if (L < G) fwd_states_chain<NDW>(a, lds, bh, r0);
+    else grad_states_chain<BF16, NDW>(a, lds, bh, r0);
 }
 
 // ------------------------------------------------------------------------------ 4. chunk grads
@@ -621,10 +746,11 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
 
     // ---- D-wide products per 64-column slice
     const int64_t CD = int64_t(kBC) * D;
-    // staging: thread -> (column nn, 4 consecutive k) units u = tid + 256 p: nn = u % 64, k0 =
-    // 4 (u / 64); four global loads down the k rows (coalesced along D over the lanes) become one
-    // 16-byte LDS store of the transposed row.  W0 and dW1: k = the d_v index; K and Q: k = the
-    // chunk row.
+    // staging: W0 and dW1 ([d_v][D] rows) as units u = tid + 256 p of (column nn = u % 64, four
+    // consecutive d_v indices from 4 (u / 64)): four global loads down the rows (coalesced along
+    // D over the lanes) become one 16-byte LDS store of the transposed row.  K and Q are stored
+    // transposed ([D][C]): unit u = (column nn = u / 8, chunk rows 4 (u % 8) .. + 3), one 16-byte
+    // load and one 16-byte store.
     constexpr int NW = 16 * kSlice / kPrepThreads2;      // W0 / dW1 units per thread (d_v <= 64)
     constexpr int NK = (kBC / 4) * kSlice / kPrepThreads2;   // K / Q units per thread
     f32x4 pw[NW], pg[NW], pk[NK], pq[NK];
@@ -643,14 +769,11 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
-            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e / kSlice), nn = e % kSlice;
+            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e & 7), nn = e >> 3;
             const bool in = s0 + nn < D;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t o = u64 * CD + (c0 + q) * D + (in ? s0 + nn : 0);
-                pk[p][q] = in ? a.ws[a.L.kt + o] : 0.0f;
-                pq[p][q] = in ? a.ws[a.L.qt + o] : 0.0f;
-            }
+            const int64_t o = u64 * CD + int64_t(in ? s0 + nn : 0) * kBC + c0;   // [D][C] tiles
+            pk[p] = in ? *reinterpret_cast<const f32x4*>(a.ws + a.L.kt + o) : zero4();
+            pq[p] = in ? *reinterpret_cast<const f32x4*>(a.ws + a.L.qt + o) : zero4();
         }
     };
     auto commit = [&]() {
@@ -664,7 +787,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
-            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e / kSlice), nn = e % kSlice;
+            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e & 7), nn = e >> 3;
             *reinterpret_cast<f32x4*>(KT + nn * CS + c0) = pk[p];
             *reinterpret_cast<f32x4*>(QT + nn * CS + c0) = pq[p];
         }
@@ -835,7 +958,6 @@ __global__ __launch_bounds__(64 * kDpfpWaves) void bwd_dpfp_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------ host
 
-static int bwd_npl(int D) { return (D + 63) / 64; }
 
 bool plan_backward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
     const int D = 2 * d_k * nu;
@@ -857,19 +979,14 @@ static int lds_grads_bytes(int d_v) {
                 2 * kSlice * SV + 2 * kSlice * kCS);
 }
 
-template <int NPL, bool BF16>
-static hipError_t launch_rows(const BwdArgs& a, hipStream_t stream) {
-    const int rgroups = (a.d_v + kRowWaves - 1) / kRowWaves;
-    const dim3 grid(static_cast<unsigned>(int64_t(a.BH) * rgroups));
-    auto kf = bwd_fwd_states_kernel<NPL>;
-    auto kg = bwd_grad_states_kernel<BF16, NPL>;
-    const int lf = 4 * 2 * kBC * 64 * NPL, lg = 4 * 3 * kBC * 64 * NPL;
-    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kf), lf);
+template <int NDW, bool BF16>
+static hipError_t launch_states(const BwdArgs& a, hipStream_t stream) {
+    const int64_t G = int64_t(a.BH) * ((a.d_v + 15) / 16);
+    auto k = bwd_states_kernel<BF16, NDW>;
+    const int l = 4 * states_lds_floats(a.D);
+    hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(k), l);
     if (e != hipSuccess) return e;
-    if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kg), lg)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kf, grid, dim3(64 * kRowWaves), lf, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(kg, grid, dim3(64 * kRowWaves), lg, stream, a);
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(2 * G)), dim3(kStThreads), l, stream, a);
     return hipGetLastError();
 }
 
@@ -884,13 +1001,10 @@ static hipError_t launch_backward_t(BwdArgs a, hipStream_t stream) {
         hipLaunchKernelGGL(kp, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads2), lp, stream, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    switch (bwd_npl(a.D)) {
-        case 1: e = launch_rows<1, BF16>(a, stream); break;
-        case 2: e = launch_rows<2, BF16>(a, stream); break;
-        case 3: e = launch_rows<3, BF16>(a, stream); break;
-        case 4: e = launch_rows<4, BF16>(a, stream); break;
-        case 5: e = launch_rows<5, BF16>(a, stream); break;
-        case 6: e = launch_rows<6, BF16>(a, stream); break;
+    switch ((a.D + 127) / 128) {                 // d-tiles per wave
+        case 1: e = launch_states<1, BF16>(a, stream); break;
+        case 2: e = launch_states<2, BF16>(a, stream); break;
+        case 3: e = launch_states<3, BF16>(a, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || NU == 0) return e;

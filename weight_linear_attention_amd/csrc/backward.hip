@@ -108,15 +108,11 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     float* Vs = be + kBC;                    // [C][d_v]
 
     // relu'd raw rows (zero past the sequence end), beta (zero past the end), v
-    load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, a.T - t0 < kBC ? a.T - t0 : kBC, t0, d_k,
-                         tid, kPrepThreads2);
-    load_relu_rows<BF16>(a.q, xq, int64_t(bh) * a.T, a.T - t0 < kBC ? a.T - t0 : kBC, t0, d_k,
-                         tid, kPrepThreads2);
-    for (int c = tid; c < kBC; c += kPrepThreads2)
-        be[c] = t0 + c < a.T ? sigmoid_stable(load_elem<BF16>(a.bl, int64_t(bh) * a.T + t0 + c)) : 0.0f;
-    for (int c = wv; c < kBC; c += kPrepThreads2 / 64)
-        for (int r = lane; r < d_v; r += 64)
-            Vs[c * d_v + r] = t0 + c < a.T ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
+    const int rows = a.T - t0 < kBC ? a.T - t0 : kBC;
+    const float blv = load_elem<BF16>(a.bl, int64_t(bh) * a.T + t0 + min(tid & (kBC - 1), rows - 1));
+    load_chunk_inputs<BF16, kPrepThreads2, 64>(a.k, a.q, a.v, xk, xq, Vs, int64_t(bh) * a.T, rows,
+                                               t0, d_k, d_v, tid);
+    if (tid < kBC) be[tid] = tid < rows ? sigmoid_stable(blv) : 0.0f;
     dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
     // K and Q leave transposed ([D][C]): unit e = 4 consecutive rows c of column d = e / 8
@@ -158,24 +154,26 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     for (int e = tid; e < 16 * 16; e += kPrepThreads2)         // P tile (0, 1): above the diagonal
         Pm[(e >> 4) * CS + 16 + (e & 15)] = 0.0f;
     __syncthreads();
-    // Ainv = (I + diag(beta) strict_lower(G))^-1 by forward substitution, one column per thread
-    if (tid < kBC) {
-        const int j = tid;
-        float x[kBC];
+    // Ainv = (I + diag(beta) strict_lower(G))^-1 by forward substitution: column j = tid / 8 by
+    // the 8 adjacent threads s = tid % 8, thread s holding x[m] for m = s mod 8; each row's sum
+    // adds the 8 threads' parts over the lanes
+    {
+        const int j = tid >> 3, s = tid & 7;
+        float xs[kBC / 8];
 #pragma unroll
-        for (int i = 0; i < kBC; ++i) x[i] = 0.0f;
+        for (int k = 0; k < kBC / 8; ++k) xs[k] = 0.0f;
 #pragma unroll
         for (int i = 0; i < kBC; ++i) {
-            if (i == j) x[i] = 1.0f;
-            if (i > j) {
-                float s = 0.0f;
+            float p = 0.0f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) s += Gm[i * CS + m] * x[m];
-                x[i] = -be[i] * s;
-            }
+            for (int k = 0; k < kBC / 8; ++k)
+                if (8 * k < i && s + 8 * k < i) p += Gm[i * CS + s + 8 * k] * xs[k];
+            p = sum8_dpp(p);
+            const float xi = i == j ? 1.0f : (i > j ? -be[i] * p : 0.0f);
+            if (s == (i & 7)) xs[i >> 3] = xi;
         }
 #pragma unroll
-        for (int i = 0; i < kBC; ++i) Ai[i * CS + j] = x[i];
+        for (int k = 0; k < kBC / 8; ++k) Ai[(s + 8 * k) * CS + j] = xs[k];
     }
     __syncthreads();
     for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {       // T = Ainv diag(beta)

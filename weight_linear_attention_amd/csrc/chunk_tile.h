@@ -32,12 +32,6 @@ __device__ __forceinline__ int orig_col(int c, int d_k) {
 
 __device__ __forceinline__ float relu_f(float x) { return fmaxf(x, 0.0f); }
 
-// x from another lane of the same 16-lane row, selected by a DPP control (compile-time).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
 // Eight consecutive staged inputs (bf16 or fp32) as fp32.  `p` is 16-byte aligned.
 __device__ __forceinline__ void load8_f32(const u16* p, float (&v)[8]) {
     const uint4 r = *reinterpret_cast<const uint4*>(p);

@@ -95,6 +95,20 @@ __device__ __forceinline__ bf16x4 lds_read_b64_single(const u16* base, int off) 
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
+// x from another lane of the same 16-lane row, selected by a DPP control (compile-time).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes, in every lane of the group, by DPP (no LDS traffic):
+// lane ^ 1, lane ^ 2 (quad permutes), then the mirrored lane of the other quad.
+__device__ __forceinline__ float sum8_dpp(float x) {
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    return x + dpp_f32<0x141>(x);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
 // global loads and stores in flight.  The kernels here share data inside a workgroup through
 // LDS alone, so a barrier never has to drain prefetched loads or the stores of results that

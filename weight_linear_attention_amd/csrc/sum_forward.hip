@@ -68,11 +68,8 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     float* Qt = Kt + kBC * SD;
     float* Mm = Qt + kBC * SD;
     float* Vs = Mm + kBC * CS;
-    load_relu_rows<BF16>(a.k, xk, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
-    load_relu_rows<BF16>(a.q, xq, int64_t(bh) * a.T, rows, t0, d_k, tid, kSumThreads);
-    for (int c = wv; c < kBC; c += kSumThreads / 64)
-        for (int r = lane; r < d_v; r += 64)
-            Vs[c * d_v + r] = c < rows ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t0 + c) * d_v + r) : 0.0f;
+    load_chunk_inputs<BF16, kSumThreads, 128>(a.k, a.q, a.v, xk, xq, Vs, int64_t(bh) * a.T, rows,
+                                              t0, d_k, d_v, tid);
     dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;

@@ -1132,7 +1132,7 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
 }
 
 // ------------------------------------------------------------------------------------------
-// chain, direct: the staged kernel's decomposition (compute wave w owns row tile w of
+// chain, direct: the staged kernel's decomposition (chain wave w owns row tile w of
 // S = W_y W^T over all of D and d-tiles w NDP .. +NDP of the memory) with no loader waves: each
 // wave loads its own operand blocks (W_y row tile, K^T d-tiles, U_y tile, rho_k) into registers
 // two chunks ahead, into one of two register sets, right after their last use.  LDS carries only
@@ -1141,17 +1141,17 @@ __global__ __launch_bounds__(512, 1) void delta_chain_staged_kernel(ChunkArgs a)
 // register set, so every register index is static; the loop body has no branches around memory
 // operations (prefetches past the last chunk re-read it), so every wait covers only the loads
 // it needs.
-// The kernel also forms the outputs: wave w accumulates Q W^T for row tile w from the W^T copy
-// GEMM1 reads, and after the second barrier adds P~ U from U (kept in LDS as well) and scales
-// by rho_q; Q, P~ and rho_q travel in the register sets with the other operands, and y goes out
-// through a range-checked buffer store.  No chunk-start memories or U go to the workspace and
-// no output kernel runs.
+// The outputs are formed by a second group of NT waves next to the chain, off its dependency
+// chain: output wave NT + t accumulates Q W^T for row tile t from the W^T copy while the chain
+// waves form S, and after the second barrier adds P~ U from U (kept in LDS as well) and scales by
+// rho_q; Q, P~ and rho_q travel in its own register sets, and y goes out through a range-checked
+// buffer store.  No chunk-start memories or U go to the workspace and no output kernel runs.
 template <bool BF16, int C, int NDP>
-__global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(128 * kChainWaves, 1) void delta_chain_direct_kernel(ChunkArgs a) {
     using LT = typename ChunkTypes<BF16>::LT;
     constexpr int pair = BF16 ? 2 : 1, NT = C / 16, NTB = NT / pair;
     constexpr int ND = kChainWaves * NDP, NDB = ND / pair, NDPB = NDP / pair;
-    static_assert(NT == kChainWaves, "one row tile of S per wave");
+    static_assert(NT == kChainWaves, "one row tile of S per chain wave");
     static_assert(NDP % pair == 0, "bf16 waves hold whole d-tile pairs");
     __shared__ __attribute__((aligned(1024))) char X[NDB * 1024];   // W^T copy
     __shared__ __attribute__((aligned(1024))) char Ub[NT * 1024];   // rho_k o U, fp32 tiles
@@ -1159,7 +1159,9 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
     static_assert(BF16, "the direct chain serves bf16 inputs");
 
     const int tid = threadIdx.x, l = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool outw = wave >= NT;                 // output waves NT .. 2 NT - 1
+    const int w = outw ? wave - NT : wave;        // the wave's row tile
     const int l16 = l & 15, g4 = l >> 4;
     const int d_k = a.d_k, D = a.D, NC = a.NC, NVT = a.d_v / 16;
     const BhIndex bi = xcd_local(blockIdx.x, a.BH, NVT);
@@ -1171,28 +1173,110 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
     const int64_t szCD = static_cast<int64_t>(C) * D * sizeof(LT);
     const int64_t szUy = static_cast<int64_t>(C) * a.d_v * 4;
     auto lane16 = [&](char* base, int blk) { return base + blk * 1024 + l * 16; };
-    const char* wyB = a.ws + a.o_wy + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
-    const char* ktB = a.ws + a.o_kt + (static_cast<int64_t>(dt0) * NTB * 64 + l) * 16;
-    const char* uyB = a.ws + a.o_uy + ((static_cast<int64_t>(w) * NVT + r) * 64 + l) * 16;
-    const float* rkB = reinterpret_cast<const float*>(a.ws + a.o_rk) + 16 * w + 4 * g4;
-
-    uint4 wy[2][NDB];          // W_y blocks of row tile w, per register set
-    uint4 kt[2][NDP * NTB];    // K^T blocks of d-tiles dt0 ..
-    f32x4 uy[2], rk[2];        // U_y tile (w, r) and rho_k of its rows
     auto clampu = [&](int64_t uu) { return uu <= ulast ? uu : ulast; };
-    auto load_wy = [&](int set, int64_t uu) {
+
+    if (!outw) {
+        const char* wyB = a.ws + a.o_wy + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
+        const char* ktB = a.ws + a.o_kt + (static_cast<int64_t>(dt0) * NTB * 64 + l) * 16;
+        const char* uyB = a.ws + a.o_uy + ((static_cast<int64_t>(w) * NVT + r) * 64 + l) * 16;
+        const float* rkB = reinterpret_cast<const float*>(a.ws + a.o_rk) + 16 * w + 4 * g4;
+        uint4 wy[2][NDB];          // W_y blocks of row tile w, per register set
+        uint4 kt[2][NDP * NTB];    // K^T blocks of d-tiles dt0 ..
+        f32x4 uy[2], rk[2];        // U_y tile (w, r) and rho_k of its rows
+        auto load_wy = [&](int set, int64_t uu) {
 #pragma unroll
-        for (int j = 0; j < NDB; ++j) wy[set][j] = *reinterpret_cast<const uint4*>(wyB + uu * szCD + j * 1024);
-    };
-    auto load_kt = [&](int set, int64_t uu) {
+            for (int j = 0; j < NDB; ++j) wy[set][j] = *reinterpret_cast<const uint4*>(wyB + uu * szCD + j * 1024);
+        };
+        auto load_kt = [&](int set, int64_t uu) {
 #pragma unroll
-        for (int b = 0; b < NDP * NTB; ++b) kt[set][b] = *reinterpret_cast<const uint4*>(ktB + uu * szCD + b * 1024);
-    };
-    auto load_uy = [&](int set, int64_t uu) {
-        uy[set] = *reinterpret_cast<const f32x4*>(uyB + uu * szUy);
-        rk[set] = *reinterpret_cast<const f32x4*>(rkB + uu * C);
-    };
-    // output operands: Q blocks and P~ blocks of row tile w, rho_q of its rows
+            for (int b = 0; b < NDP * NTB; ++b) kt[set][b] = *reinterpret_cast<const uint4*>(ktB + uu * szCD + b * 1024);
+        };
+        auto load_uy = [&](int set, int64_t uu) {
+            uy[set] = *reinterpret_cast<const f32x4*>(uyB + uu * szUy);
+            rk[set] = *reinterpret_cast<const f32x4*>(rkB + uu * C);
+        };
+        f32x4 Wst[NDP];
+#pragma unroll
+        for (int i = 0; i < NDP; ++i) {
+            Wst[i] = zero4();
+            if (a.W0) {
+                // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
+                const float* src = a.W0 + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                                   orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+                const float2 lo = *reinterpret_cast<const float2*>(src);
+                const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
+                Wst[i] = f32x4{lo.x, hi.x, lo.y, hi.y};
+            }
+        }
+        // One chunk with register set SET; its operands are replaced by those of chunk uu + 2.
+        auto chunk = [&](int64_t uu, auto set_tag) {
+            constexpr int SET = decltype(set_tag)::value;
+            const int64_t ua = clampu(uu + 2);
+            // chunk-start memory: the LDS copy for GEMM1 and Q W^T
+#pragma unroll
+            for (int i = 0; i < NDPB; ++i)
+                *reinterpret_cast<uint4*>(lane16(X, dt0 / pair + i)) = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
+            lds_barrier();                                           // B1: W^T copy complete
+            // S = W_y W^T for row tile w, two accumulators over alternating k-blocks
+            f32x4 s0 = zero4(), s1 = zero4();
+#pragma unroll
+            for (int j = 0; j < NDB; ++j) {
+                const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(lane16(X, j)));
+                f32x4& acc = (j & 1) ? s1 : s0;
+                acc = mfma_bf16_k32(as_bf16x8(wy[SET][j]), bv, acc);
+            }
+            load_wy(SET, ua);
+            const f32x4 U = uy[SET] - (s0 + s1);
+            *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rk[SET];
+            *reinterpret_cast<f32x4*>(lane16(Uo, w)) = U;
+            load_uy(SET, ua);
+            lds_barrier();                                           // B2: U and rho_k o U complete
+            // W^T += K^T (rho_k o U) for this wave's d-tiles
+            f32x4 odd[NDP];
+#pragma unroll
+            for (int i = 0; i < NDP; ++i) odd[i] = zero4();
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+                const f32x4 u0v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j));
+                const f32x4 u1v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j + 1));
+                const uint4 bu = pack_bf16x8(u0v, u1v);
+#pragma unroll
+                for (int i = 0; i < NDP; ++i) {
+                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
+                    dst = mfma_bf16_k32(as_bf16x8(kt[SET][i * NTB + j]), as_bf16x8(bu), dst);
+                }
+            }
+            load_kt(SET, ua);
+#pragma unroll
+            for (int i = 0; i < NDP; ++i) Wst[i] += odd[i];
+        };
+        if (NC > 0) {
+            load_wy(0, u0);
+            load_uy(0, u0);
+            load_kt(0, u0);
+            load_wy(1, clampu(u0 + 1));
+            load_uy(1, clampu(u0 + 1));
+            load_kt(1, clampu(u0 + 1));
+        }
+        int n = 0;
+        for (; n + 1 < NC; n += 2) {
+            chunk(u0 + n, std::integral_constant<int, 0>());
+            chunk(u0 + n + 1, std::integral_constant<int, 1>());
+        }
+        if (n < NC) chunk(u0 + n, std::integral_constant<int, 0>());
+        if (a.Wf) {
+#pragma unroll
+            for (int i = 0; i < NDP; ++i) {
+                float* dst = a.Wf + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
+                             orig_col(16 * (dt0 + i) + 4 * g4, d_k);
+                *reinterpret_cast<float2*>(dst) = make_float2(Wst[i][0], Wst[i][2]);
+                *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[i][1], Wst[i][3]);
+            }
+        }
+        return;
+    }
+
+    // ---- output waves: Q blocks and P~ blocks of row tile w, rho_q of its rows
     uint4 qy[2][NDB], py[2][NTB];
     f32x4 rq[2];
     const char* qaB = a.ws + a.o_qa + (static_cast<int64_t>(w) * NDB * 64 + l) * 16;
@@ -1210,102 +1294,36 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
     const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<LT*>(a.y) + static_cast<int64_t>(bh) * a.T * a.d_v, static_cast<short>(0),
         a.T * a.d_v * static_cast<int>(sizeof(LT)), 0x00020000);
-
-    f32x4 Wst[NDP];
-#pragma unroll
-    for (int i = 0; i < NDP; ++i) {
-        Wst[i] = zero4();
-        if (a.W0) {
-            // internal columns c0 .. c0+3 = positions (o, o + d_k, o + 1, o + d_k + 1)
-            const float* src = a.W0 + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
-                               orig_col(16 * (dt0 + i) + 4 * g4, d_k);
-            const float2 lo = *reinterpret_cast<const float2*>(src);
-            const float2 hi = *reinterpret_cast<const float2*>(src + d_k);
-            Wst[i] = f32x4{lo.x, hi.x, lo.y, hi.y};
-        }
-    }
-
-    // One chunk with register set SET; its operands are replaced by those of chunk uu + 2.
     auto chunk = [&](int64_t uu, auto set_tag) {
         constexpr int SET = decltype(set_tag)::value;
         const int64_t ua = clampu(uu + 2);
-        // chunk-start memory: the LDS copy for GEMM1 and Q W^T
-#pragma unroll
-        for (int i = 0; i < NDPB; ++i)
-            *reinterpret_cast<uint4*>(lane16(X, dt0 / pair + i)) = pack_bf16x8(Wst[2 * i], Wst[2 * i + 1]);
         lds_barrier();                                               // B1: W^T copy complete
-        // S = W_y W^T and Q W^T for row tile w, two accumulators each over alternating k-blocks
-        f32x4 s0 = zero4(), s1 = zero4(), q0 = zero4(), q1 = zero4();
+        f32x4 q0 = zero4(), q1 = zero4();
 #pragma unroll
         for (int j = 0; j < NDB; ++j) {
             const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(lane16(X, j)));
-            f32x4& acc = (j & 1) ? s1 : s0;
             f32x4& qacc = (j & 1) ? q1 : q0;
-            acc = mfma_bf16_k32(as_bf16x8(wy[SET][j]), bv, acc);
             qacc = mfma_bf16_k32(as_bf16x8(qy[SET][j]), bv, qacc);
         }
-        load_wy(SET, ua);
-        const f32x4 U = uy[SET] - (s0 + s1);
-        *reinterpret_cast<f32x4*>(lane16(Ub, w)) = U * rk[SET];
-        *reinterpret_cast<f32x4*>(lane16(Uo, w)) = U;
-        load_uy(SET, ua);
-        lds_barrier();                                               // B2: U and rho_k o U complete
-        {
-            // Y for row tile w = rho_q o (Q W^T) + P~ U (P~ zero above the diagonal)
-            f32x4 y = (q0 + q1) * rq[SET];
-#pragma unroll
-            for (int j = 0; j < NTB; ++j) {
-                if (2 * j > w) break;
-                const uint4 ub = pack_bf16x8(*reinterpret_cast<const f32x4*>(lane16(Uo, 2 * j)),
-                                             *reinterpret_cast<const f32x4*>(lane16(Uo, 2 * j + 1)));
-                y = mfma_bf16_k32(as_bf16x8(py[SET][j]), as_bf16x8(ub), y);
-            }
-            const int t0 = static_cast<int>(uu - u0) * C;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(y[e]), yrsrc,
-                                                      ((t0 + 16 * w + 4 * g4 + e) * a.d_v + vcol) * 2, 0, 0);
-            load_qp(SET, ua);
-        }
-        // W^T += K^T (rho_k o U) for this wave's d-tiles
-        f32x4 odd[NDP];
-#pragma unroll
-        for (int i = 0; i < NDP; ++i) odd[i] = zero4();
+        lds_barrier();                                               // B2: U complete
+        // Y for row tile w = rho_q o (Q W^T) + P~ U (P~ zero above the diagonal)
+        f32x4 y = (q0 + q1) * rq[SET];
 #pragma unroll
         for (int j = 0; j < NTB; ++j) {
-            if constexpr (BF16) {
-                const f32x4 u0v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j));
-                const f32x4 u1v = *reinterpret_cast<const f32x4*>(lane16(Ub, 2 * j + 1));
-                const uint4 bu = pack_bf16x8(u0v, u1v);
-#pragma unroll
-                for (int i = 0; i < NDP; ++i) {
-                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
-                    dst = mfma_bf16_k32(as_bf16x8(kt[SET][i * NTB + j]), as_bf16x8(bu), dst);
-                }
-            } else {
-                const f32x4 uv = *reinterpret_cast<const f32x4*>(lane16(Ub, j));
-#pragma unroll
-                for (int i = 0; i < NDP; ++i) {
-                    const f32x4 af = as_f32x4(kt[SET][i * NTB + j]);
-                    f32x4& dst = (j & 1) ? odd[i] : Wst[i];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dst = mfma_f32_k4(af[e], uv[e], dst);
-                }
-            }
+            if (2 * j > w) break;
+            const uint4 ub = pack_bf16x8(*reinterpret_cast<const f32x4*>(lane16(Uo, 2 * j)),
+                                         *reinterpret_cast<const f32x4*>(lane16(Uo, 2 * j + 1)));
+            y = mfma_bf16_k32(as_bf16x8(py[SET][j]), as_bf16x8(ub), y);
         }
-        load_kt(SET, ua);
+        const int t0 = static_cast<int>(uu - u0) * C;
 #pragma unroll
-        for (int i = 0; i < NDP; ++i) Wst[i] += odd[i];
+        for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(y[e]), yrsrc,
+                                                  ((t0 + 16 * w + 4 * g4 + e) * a.d_v + vcol) * 2, 0, 0);
+        load_qp(SET, ua);
     };
-
     if (NC > 0) {
-        load_wy(0, u0);
-        load_uy(0, u0);
-        load_kt(0, u0);
         load_qp(0, u0);
-        load_wy(1, clampu(u0 + 1));
-        load_uy(1, clampu(u0 + 1));
-        load_kt(1, clampu(u0 + 1));
         load_qp(1, clampu(u0 + 1));
     }
     int n = 0;
@@ -1314,16 +1332,6 @@ __global__ __launch_bounds__(64 * kChainWaves, 1) void delta_chain_direct_kernel
         chunk(u0 + n + 1, std::integral_constant<int, 1>());
     }
     if (n < NC) chunk(u0 + n, std::integral_constant<int, 0>());
-
-    if (a.Wf) {
-#pragma unroll
-        for (int i = 0; i < NDP; ++i) {
-            float* dst = a.Wf + (static_cast<int64_t>(bh) * a.d_v + vcol) * D +
-                         orig_col(16 * (dt0 + i) + 4 * g4, d_k);
-            *reinterpret_cast<float2*>(dst) = make_float2(Wst[i][0], Wst[i][2]);
-            *reinterpret_cast<float2*>(dst + d_k) = make_float2(Wst[i][1], Wst[i][3]);
-        }
-    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1500,9 +1508,9 @@ hipError_t launch_chunked_t(const ChunkPlan& p, hipStream_t stream) {
         if (p.direct) {
             const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.BH) * (a.d_v / 16)));
             if (p.staged_ndp == 2)
-                hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 2>), grid, dim3(64 * kChainWaves), 0, stream, a);
+                hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 2>), grid, dim3(128 * kChainWaves), 0, stream, a);
             else
-                hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 4>), grid, dim3(64 * kChainWaves), 0, stream, a);
+                hipLaunchKernelGGL((delta_chain_direct_kernel<BF16, C, 4>), grid, dim3(128 * kChainWaves), 0, stream, a);
             direct = true;
         }
     }

@@ -100,6 +100,125 @@ __device__ __forceinline__ void dpfp_slice_any(int i, const u16* Xk, const u16* 
 }
 
 // ------------------------------------------------------------------------------------------
+// G = K K^T and P = Q K^T at chunk 64 with the DPFP operands built in registers.  The MFMA A
+// operand of row r and the B operand of column r (16x16x32 bf16) hold the same eight values per
+// lane: slot 2 f + h of lane (l16, g4) in k-step kk of shift block i is internal column
+// (i - 1) 2 d_k + 2 (16 kk + 4 g4 + f) + h of row r.  Each lane builds them from a window of
+// its staged raw row, positions p0 - 4 .. p0 + 3 (p0 = 16 kk + 4 g4), so no feature tile goes
+// through LDS: the window is read once per k-step and serves every shift.  The staged rows are
+// kRawRow bf16 apart (136 bytes: the 16 rows a wave reads at once fall in distinct banks).
+constexpr int kRawRow = kSliceDk + 4;
+
+// The window's k values as fp32 positive and negative parts.  For the window starting at
+// position 0, the four entries before it wrap into the [-k] half, so their parts swap.
+struct DpfpWin {
+    float P[8], N[8];
+};
+__device__ __forceinline__ DpfpWin dpfp_window(const u16* row, int p0) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + ((p0 + kSliceDk - 4) & (kSliceDk - 1)));
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + p0);
+    const uint32_t wd[4] = {lo.x, lo.y, hi.x, hi.y};
+    DpfpWin wn;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float r = (e & 1) ? __uint_as_float(wd[e >> 1] & 0xffff0000u) : __uint_as_float(wd[e >> 1] << 16);
+        wn.P[e] = relu_f(r);
+        wn.N[e] = wn.P[e] - r;                 // relu(-r), exactly
+    }
+    const bool wrap = p0 == 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float p = wn.P[e], n = wn.N[e];
+        wn.P[e] = wrap ? n : p;
+        wn.N[e] = wrap ? p : n;
+    }
+    return wn;
+}
+
+// The operand of shift I: slot 2 f + h = position p0 + f, half h (h = 0: relu(k_j) times the
+// rolled factor, h = 1: relu(-k_j) times it); with SUM, the fp32 products are added to *sum.
+template <int I, bool SUM>
+__device__ __forceinline__ bf16x8 dpfp_operand(const DpfpWin& wn, float& sum) {
+    bf16x8 o;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int m = 4 + f - I;
+        const float a = wn.P[4 + f] * wn.P[m], b = wn.N[4 + f] * wn.N[m];
+        o[2 * f] = static_cast<__bf16>(a);
+        o[2 * f + 1] = static_cast<__bf16>(b);
+        if constexpr (SUM) sum += a + b;
+    }
+    return o;
+}
+
+// One k-step of shift I for unit (Q, ISP): rows RA = Q and RB = 3 - Q of X (K, or Q for ISP)
+// against the K rows 0 .. RB.
+template <int Q, bool ISP, int I>
+__device__ __forceinline__ void gp_raw_step(f32x4 (&ta)[4], f32x4 (&tb_)[4], float& sa, float& sb,
+                                            const DpfpWin& wa, const DpfpWin& wb,
+                                            const DpfpWin (&wk)[4 - Q]) {
+    constexpr int RA = Q, RB = 3 - Q;
+    const bf16x8 va = dpfp_operand<I, true>(wa, sa);
+    const bf16x8 vb = dpfp_operand<I, true>(wb, sb);
+    float dummy = 0.0f;
+#pragma unroll
+    for (int tb = 0; tb <= RB; ++tb) {
+        const bf16x8 kv = (!ISP && tb == RA) ? va : (!ISP && tb == RB) ? vb : dpfp_operand<I, false>(wk[tb], dummy);
+        if (tb <= RA) ta[tb] = mfma_bf16_k32(va, kv, ta[tb]);
+        tb_[tb] = mfma_bf16_k32(vb, kv, tb_[tb]);
+    }
+}
+
+// Unit (Q, ISP) over all of D: the tiles of rows RA, RB and the fp32 row sums of this lane's
+// share of those rows (positions 4 g4 .. + 3 of every 16).
+template <int Q, bool ISP, int NU>
+__device__ __forceinline__ void gp_raw_unit(f32x4 (&ta)[4], f32x4 (&tb_)[4], float& sa, float& sb,
+                                            const u16* Xk, const u16* Xq, int l16, int g4) {
+    static_assert(NU >= 1 && NU <= 4, "window entries 4 + f - i stay in 0 .. 7");
+    constexpr int RA = Q, RB = 3 - Q;
+    const u16* X = ISP ? Xq : Xk;
+#pragma unroll 1
+    for (int kk = 0; kk < kSliceCols / 32; ++kk) {
+        const int p0 = 16 * kk + 4 * g4;
+        const DpfpWin wa = dpfp_window(X + (16 * RA + l16) * kRawRow, p0);
+        const DpfpWin wb = dpfp_window(X + (16 * RB + l16) * kRawRow, p0);
+        DpfpWin wk[RB + 1];
+#pragma unroll
+        for (int tb = 0; tb <= RB; ++tb)
+            if (ISP || (tb != RA && tb != RB)) wk[tb] = dpfp_window(Xk + (16 * tb + l16) * kRawRow, p0);
+        gp_raw_step<Q, ISP, 1>(ta, tb_, sa, sb, wa, wb, wk);
+        if constexpr (NU >= 2) gp_raw_step<Q, ISP, 2>(ta, tb_, sa, sb, wa, wb, wk);
+        if constexpr (NU >= 3) gp_raw_step<Q, ISP, 3>(ta, tb_, sa, sb, wa, wb, wk);
+        if constexpr (NU >= 4) gp_raw_step<Q, ISP, 4>(ta, tb_, sa, sb, wa, wb, wk);
+    }
+}
+
+// Chunk 64, four waves: wave w runs unit (q = w % 2, P if w >= 2) and writes the normalisers
+// 1 / (row sum + eps) of its rows RA, RB (K rows for G units, Q rows for P units).
+template <int NU>
+__device__ __forceinline__ void gp_raw_c64(GPTiles<64, 4>& gp, const u16* Xk, const u16* Xq,
+                                           float* rhok, float* rhoq, int w, int l16, int g4) {
+    float sa = 0.0f, sb = 0.0f;
+    switch (w) {
+        case 0: gp_raw_unit<0, false, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
+        case 1: gp_raw_unit<1, false, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
+        case 2: gp_raw_unit<0, true, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
+        default: gp_raw_unit<1, true, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
+    }
+    // the four lanes l16 + 16 g4 of a row hold its four shares
+    sa += __shfl_xor(sa, 16);
+    sa += __shfl_xor(sa, 32);
+    sb += __shfl_xor(sb, 16);
+    sb += __shfl_xor(sb, 32);
+    const int q = w & 1;
+    float* rho = w >= 2 ? rhoq : rhok;
+    if (g4 == 0) {
+        rho[16 * q + l16] = __builtin_amdgcn_rcpf(sa + kDpfpEps);
+        rho[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(sb + kDpfpEps);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // prep (compact, sliced): one workgroup of NTH / 64 waves per chunk (b, h, n): 4 at chunk 64,
 // 8 at chunk 128 (one wave per 16-column block of A).  Writes, per chunk, the
 // A-operand blocks of A'' = (I + L)^-1 diag(beta) as a bf16 hi + lo pair (AH, AL; the pair's sum
@@ -143,8 +262,12 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     static_assert(NW >= NT, "one wave per block column of A");
     constexpr int NP = 2 * C * (kSliceDk / 8) / NTH;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    u16* Xk = reinterpret_cast<u16*>(smem + a.l_x);          // [C][64] raw k rows
-    u16* Xq = Xk + C * kSliceDk;                              // [C][64] raw q rows
+    // raw k and q rows: [C][XS]; at chunk 64 the rows are padded for the register-built
+    // operands' window reads
+    constexpr bool RAWGP = C == 64 && NW == 4;
+    constexpr int XS = RAWGP ? kRawRow : kSliceDk;
+    u16* Xk = reinterpret_cast<u16*>(smem + a.l_x);
+    u16* Xq = Xk + C * XS;
     u16* Ks = reinterpret_cast<u16*>(smem + a.l_kr);          // [C][ss] K slice
     u16* Qs = reinterpret_cast<u16*>(smem + a.l_qr);          // [C][ss] Q slice
     float* Ls = reinterpret_cast<float*>(smem + a.l_ls);      // [C][lss] L      (phase 2)
@@ -176,38 +299,55 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
         for (int p = 0; p < SlicedStage<C, NTH>::NPU; ++p) {
             const int e = tid + NTH * p;               // 16-byte unit, row e / 8
             const uint32_t m = (e >> 3) < Cc ? 0xffffffffu : 0u;
-            reinterpret_cast<uint4*>(Xk)[e] = make_uint4(st.k[p].x & m, st.k[p].y & m, st.k[p].z & m, st.k[p].w & m);
-            reinterpret_cast<uint4*>(Xq)[e] = make_uint4(st.q[p].x & m, st.q[p].y & m, st.q[p].z & m, st.q[p].w & m);
+            const uint4 kv = make_uint4(st.k[p].x & m, st.k[p].y & m, st.k[p].z & m, st.k[p].w & m);
+            const uint4 qv = make_uint4(st.q[p].x & m, st.q[p].y & m, st.q[p].z & m, st.q[p].w & m);
+            if constexpr (XS == kSliceDk) {
+                reinterpret_cast<uint4*>(Xk)[e] = kv;
+                reinterpret_cast<uint4*>(Xq)[e] = qv;
+            } else {
+                // 8-byte aligned rows: two 8-byte stores per unit
+                const int o = (e >> 3) * XS + 8 * (e & 7);
+                *reinterpret_cast<uint2*>(Xk + o) = make_uint2(kv.x, kv.y);
+                *reinterpret_cast<uint2*>(Xk + o + 4) = make_uint2(kv.z, kv.w);
+                *reinterpret_cast<uint2*>(Xq + o) = make_uint2(qv.x, qv.y);
+                *reinterpret_cast<uint2*>(Xq + o + 4) = make_uint2(qv.z, qv.w);
+            }
         }
         if (tid < C) betas[tid] = tid < Cc ? sigmoid_stable(st.bl) : 0.0f;
         if (blk_next != blk) sliced_stage_load<C, NTH>(a, blk_next, st);
     }
     lds_barrier();
 
-    // ---- G = K K^T and P = Q K^T over the shift slices; row sums from the DPFP tasks
+    // ---- G = K K^T and P = Q K^T over D, and the normalisers
     GPTiles<C, NW> gp;
     gp_zero(gp);
-    float sums[NP];
+    if constexpr (RAWGP) {
+        // operands built in registers from the raw rows
+        gp_raw_c64<NU>(gp, Xk, Xq, rhok, rhoq, w, l16, g4);
+    } else {
+        // shift slices through LDS; row sums from the DPFP tasks
+        float sums[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) sums[p] = 0.0f;
-    // a rolled loop: unrolled, the compiler keeps every slice's task inputs in registers
+        for (int p = 0; p < NP; ++p) sums[p] = 0.0f;
+        // a rolled loop: unrolled, the compiler keeps every slice's task inputs in registers
 #pragma unroll 1
-    for (int s = 0; s < NU; ++s) {
-        dpfp_slice_any<C, NTH, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
-        lds_barrier();
-        gp_accumulate<true, C, false, NW>(gp, Ks, Qs, ss, kSliceCols, w, l16, g4);
-        lds_barrier();
-    }
-    // row sums over the row's eight adjacent lanes (lane ^ 1, lane ^ 2, then the mirror inside
-    // 8 lanes); the row's first lane writes rho = 1 / (sum + eps)
+        for (int s = 0; s < NU; ++s) {
+            dpfp_slice_any<C, NTH, true>(s + 1, Xk, Xq, Ks, Qs, ss, tid, sums);
+            lds_barrier();
+            gp_accumulate<true, C, false, NW>(gp, Ks, Qs, ss, kSliceCols, w, l16, g4);
+            lds_barrier();
+        }
+        // row sums over the row's eight adjacent lanes (lane ^ 1, lane ^ 2, then the mirror
+        // inside 8 lanes); the row's first lane writes rho = 1 / (sum + eps)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        float s = sums[p];
-        s += dpp_f32<0xB1>(s);
-        s += dpp_f32<0x4E>(s);
-        s += dpp_f32<0x141>(s);
-        const int tau = tid + NTH * p, rt = tau >> 3;
-        if ((tau & 7) == 0) (rt >= C ? rhoq + (rt - C) : rhok + rt)[0] = __builtin_amdgcn_rcpf(s + kDpfpEps);
+        for (int p = 0; p < NP; ++p) {
+            float s = sums[p];
+            s += dpp_f32<0xB1>(s);
+            s += dpp_f32<0x4E>(s);
+            s += dpp_f32<0x141>(s);
+            const int tau = tid + NTH * p, rt = tau >> 3;
+            if ((tau & 7) == 0) (rt >= C ? rhoq + (rt - C) : rhok + rt)[0] = __builtin_amdgcn_rcpf(s + kDpfpEps);
+        }
     }
     lds_barrier();
 
@@ -308,7 +448,7 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
 // once), a grid of the resident workgroups (a multiple of 8) that walks the chunks with the grid
 // as stride, loading the next chunk's raw rows while the current one is processed.
 template <int C, int NU, int NTH = kSliceThreads, bool PERSIST = false>
-__global__ __launch_bounds__(NTH, 1) void delta_prep_sliced_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(NTH, (C == 64 && !PERSIST) ? 3 : 1) void delta_prep_sliced_kernel(ChunkArgs a) {
     SlicedStage<C, NTH> st;
     if constexpr (!PERSIST) {
         sliced_stage_load<C, NTH>(a, blockIdx.x, st);

@@ -16,7 +16,7 @@ int plan_prep_sliced(int C, ChunkArgs* a) {
     a->aps = C + 8;
     // phase 1: raw k, q rows, then one K and one Q slice
     a->l_x = 0;
-    a->l_kr = align16v(2 * C * kSliceDk * 2);
+    a->l_kr = align16v(2 * C * (C == 64 ? kRawRow : kSliceDk) * 2);   // raw rows (padded at 64)
     a->l_qr = align16v(a->l_kr + C * a->ss * 2);
     const int p1 = align16v(a->l_qr + C * a->ss * 2);
     // phase 2 (over phase 1): L, the diagonal-block inverses, P~ and then A'' hi / lo

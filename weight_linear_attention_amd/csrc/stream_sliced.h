@@ -151,70 +151,109 @@ __device__ __forceinline__ bf16x8 dpfp_operand(const DpfpWin& wn, float& sum) {
     return o;
 }
 
-// One k-step of shift I for unit (Q, ISP): rows RA = Q and RB = 3 - Q of X (K, or Q for ISP)
-// against the K rows 0 .. RB.
-template <int Q, bool ISP, int I>
-__device__ __forceinline__ void gp_raw_step(f32x4 (&ta)[4], f32x4 (&tb_)[4], float& sa, float& sb,
-                                            const DpfpWin& wa, const DpfpWin& wb,
-                                            const DpfpWin (&wk)[4 - Q]) {
+// The tiles of tile-row pair Q (rows RA = Q, RB = 3 - Q) of both G = K K^T and P = Q K^T,
+// with the row sums of K rows and Q rows RA, RB: ga / gb tiles (RA, tb) / (RB, tb) of G,
+// pa / pb those of P, sums kA, kB, qA, qB.
+struct GPPair {
+    f32x4 ga[4], gb[4], pa[4], pb[4];
+    float kA, kB, qA, qB;
+};
+
+// One k-step of shift I: the A operands of K and Q rows RA, RB, then the K rows 0 .. RB as B
+// operands one at a time (rows RA and RB are the A operands already built).
+template <int Q, int I>
+__device__ __forceinline__ void gp_pair_step(GPPair& g, const DpfpWin& ka, const DpfpWin& kb,
+                                             const DpfpWin& qa, const DpfpWin& qb,
+                                             const u16* Xk, int p0, int l16) {
     constexpr int RA = Q, RB = 3 - Q;
-    const bf16x8 va = dpfp_operand<I, true>(wa, sa);
-    const bf16x8 vb = dpfp_operand<I, true>(wb, sb);
+    const bf16x8 vka = dpfp_operand<I, true>(ka, g.kA);
+    const bf16x8 vkb = dpfp_operand<I, true>(kb, g.kB);
+    const bf16x8 vqa = dpfp_operand<I, true>(qa, g.qA);
+    const bf16x8 vqb = dpfp_operand<I, true>(qb, g.qB);
     float dummy = 0.0f;
 #pragma unroll
     for (int tb = 0; tb <= RB; ++tb) {
-        const bf16x8 kv = (!ISP && tb == RA) ? va : (!ISP && tb == RB) ? vb : dpfp_operand<I, false>(wk[tb], dummy);
-        if (tb <= RA) ta[tb] = mfma_bf16_k32(va, kv, ta[tb]);
-        tb_[tb] = mfma_bf16_k32(vb, kv, tb_[tb]);
+        bf16x8 kv;
+        if (tb == RA) kv = vka;
+        else if (tb == RB) kv = vkb;
+        else kv = dpfp_operand<I, false>(dpfp_window(Xk + (16 * tb + l16) * kRawRow, p0), dummy);
+        if (tb <= RA) {
+            g.ga[tb] = mfma_bf16_k32(vka, kv, g.ga[tb]);
+            g.pa[tb] = mfma_bf16_k32(vqa, kv, g.pa[tb]);
+        }
+        g.gb[tb] = mfma_bf16_k32(vkb, kv, g.gb[tb]);
+        g.pb[tb] = mfma_bf16_k32(vqb, kv, g.pb[tb]);
     }
 }
 
-// Unit (Q, ISP) over all of D: the tiles of rows RA, RB and the fp32 row sums of this lane's
-// share of those rows (positions 4 g4 .. + 3 of every 16).
-template <int Q, bool ISP, int NU>
-__device__ __forceinline__ void gp_raw_unit(f32x4 (&ta)[4], f32x4 (&tb_)[4], float& sa, float& sb,
-                                            const u16* Xk, const u16* Xq, int l16, int g4) {
+// Pair Q over the k-steps kk0, kk0 + 1 of every shift block (half of D); the sums cover this
+// lane's positions 4 g4 .. + 3 of every 16 in those k-steps.
+template <int Q, int NU>
+__device__ __forceinline__ void gp_pair_half(GPPair& g, const u16* Xk, const u16* Xq, int kk0,
+                                             int l16, int g4) {
     static_assert(NU >= 1 && NU <= 4, "window entries 4 + f - i stay in 0 .. 7");
     constexpr int RA = Q, RB = 3 - Q;
-    const u16* X = ISP ? Xq : Xk;
 #pragma unroll 1
-    for (int kk = 0; kk < kSliceCols / 32; ++kk) {
+    for (int kk = kk0; kk < kk0 + 2; ++kk) {
         const int p0 = 16 * kk + 4 * g4;
-        const DpfpWin wa = dpfp_window(X + (16 * RA + l16) * kRawRow, p0);
-        const DpfpWin wb = dpfp_window(X + (16 * RB + l16) * kRawRow, p0);
-        DpfpWin wk[RB + 1];
-#pragma unroll
-        for (int tb = 0; tb <= RB; ++tb)
-            if (ISP || (tb != RA && tb != RB)) wk[tb] = dpfp_window(Xk + (16 * tb + l16) * kRawRow, p0);
-        gp_raw_step<Q, ISP, 1>(ta, tb_, sa, sb, wa, wb, wk);
-        if constexpr (NU >= 2) gp_raw_step<Q, ISP, 2>(ta, tb_, sa, sb, wa, wb, wk);
-        if constexpr (NU >= 3) gp_raw_step<Q, ISP, 3>(ta, tb_, sa, sb, wa, wb, wk);
-        if constexpr (NU >= 4) gp_raw_step<Q, ISP, 4>(ta, tb_, sa, sb, wa, wb, wk);
+        const DpfpWin ka = dpfp_window(Xk + (16 * RA + l16) * kRawRow, p0);
+        const DpfpWin kb = dpfp_window(Xk + (16 * RB + l16) * kRawRow, p0);
+        const DpfpWin qa = dpfp_window(Xq + (16 * RA + l16) * kRawRow, p0);
+        const DpfpWin qb = dpfp_window(Xq + (16 * RB + l16) * kRawRow, p0);
+        gp_pair_step<Q, 1>(g, ka, kb, qa, qb, Xk, p0, l16);
+        if constexpr (NU >= 2) gp_pair_step<Q, 2>(g, ka, kb, qa, qb, Xk, p0, l16);
+        if constexpr (NU >= 3) gp_pair_step<Q, 3>(g, ka, kb, qa, qb, Xk, p0, l16);
+        if constexpr (NU >= 4) gp_pair_step<Q, 4>(g, ka, kb, qa, qb, Xk, p0, l16);
     }
 }
 
-// Chunk 64, four waves: wave w runs unit (q = w % 2, P if w >= 2) and writes the normalisers
-// 1 / (row sum + eps) of its rows RA, RB (K rows for G units, Q rows for P units).
+// Chunk 64, four waves: wave w takes pair q = w % 2 over half h = w / 2 of the k-steps.  The
+// h = 1 waves leave their partial tiles and sums in LDS at `part` (dead space of the phase);
+// after the barrier the h = 0 waves add them and write the normalisers 1 / (row sum + eps)
+// of K rows and Q rows RA, RB.  The caller then scales the h = 0 waves' tiles.
 template <int NU>
-__device__ __forceinline__ void gp_raw_c64(GPTiles<64, 4>& gp, const u16* Xk, const u16* Xq,
-                                           float* rhok, float* rhoq, int w, int l16, int g4) {
-    float sa = 0.0f, sb = 0.0f;
-    switch (w) {
-        case 0: gp_raw_unit<0, false, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
-        case 1: gp_raw_unit<1, false, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
-        case 2: gp_raw_unit<0, true, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
-        default: gp_raw_unit<1, true, NU>(gp.a[0], gp.b[0], sa, sb, Xk, Xq, l16, g4); break;
+__device__ __forceinline__ void gp_raw_c64(GPPair& g, const u16* Xk, const u16* Xq, f32x4* part,
+                                           float* rhok, float* rhoq, int w, int l, int l16, int g4) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) g.ga[t] = g.gb[t] = g.pa[t] = g.pb[t] = zero4();
+    g.kA = g.kB = g.qA = g.qB = 0.0f;
+    const int q = w & 1, h = w >> 1;
+    if (q == 0) gp_pair_half<0, NU>(g, Xk, Xq, 2 * h, l16, g4);
+    else gp_pair_half<1, NU>(g, Xk, Xq, 2 * h, l16, g4);
+    // the four lanes l16 + 16 g4 of a row hold its shares
+    float s[4] = {g.kA, g.kB, g.qA, g.qB};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s[i] += __shfl_xor(s[i], 16);
+        s[i] += __shfl_xor(s[i], 32);
     }
-    // the four lanes l16 + 16 g4 of a row hold its four shares
-    sa += __shfl_xor(sa, 16);
-    sa += __shfl_xor(sa, 32);
-    sb += __shfl_xor(sb, 16);
-    sb += __shfl_xor(sb, 32);
-    const int q = w & 1;
-    float* rho = w >= 2 ? rhoq : rhok;
-    if (g4 == 0) {
-        rho[16 * q + l16] = __builtin_amdgcn_rcpf(sa + kDpfpEps);
-        rho[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(sb + kDpfpEps);
+    f32x4* mine = part + q * 17 * 64 + l;              // 16 tiles + the sums, per pair
+    if (h == 1) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            mine[(4 * 0 + t) * 64] = g.ga[t];
+            mine[(4 * 1 + t) * 64] = g.gb[t];
+            mine[(4 * 2 + t) * 64] = g.pa[t];
+            mine[(4 * 3 + t) * 64] = g.pb[t];
+        }
+        mine[16 * 64] = f32x4{s[0], s[1], s[2], s[3]};
+    }
+    lds_barrier();
+    if (h == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            g.ga[t] += mine[(4 * 0 + t) * 64];
+            g.gb[t] += mine[(4 * 1 + t) * 64];
+            g.pa[t] += mine[(4 * 2 + t) * 64];
+            g.pb[t] += mine[(4 * 3 + t) * 64];
+        }
+        const f32x4 o = mine[16 * 64];
+        if (g4 == 0) {
+            rhok[16 * q + l16] = __builtin_amdgcn_rcpf(s[0] + o[0] + kDpfpEps);
+            rhok[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(s[1] + o[1] + kDpfpEps);
+            rhoq[16 * q + l16] = __builtin_amdgcn_rcpf(s[2] + o[2] + kDpfpEps);
+            rhoq[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(s[3] + o[3] + kDpfpEps);
+        }
     }
 }
 
@@ -320,11 +359,13 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
 
     // ---- G = K K^T and P = Q K^T over D, and the normalisers
     GPTiles<C, NW> gp;
-    gp_zero(gp);
+    GPPair gpp;
     if constexpr (RAWGP) {
-        // operands built in registers from the raw rows
-        gp_raw_c64<NU>(gp, Xk, Xq, rhok, rhoq, w, l16, g4);
+        // operands built in registers from the raw rows; partial tiles over the K slice's
+        // space (dead at chunk 64)
+        gp_raw_c64<NU>(gpp, Xk, Xq, reinterpret_cast<f32x4*>(Ks), rhok, rhoq, w, l, l16, g4);
     } else {
+        gp_zero(gp);
         // shift slices through LDS; row sums from the DPFP tasks
         float sums[NP];
 #pragma unroll
@@ -351,7 +392,17 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     }
     lds_barrier();
 
-    gp_scale<true, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
+    if constexpr (RAWGP) {
+        if (w == 0) {
+            gp_scale_unit<true, C, 0>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
+            gp_scale_unit<true, C, 0>(gpp.pa, gpp.pb, true, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
+        } else if (w == 1) {
+            gp_scale_unit<true, C, 1>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
+            gp_scale_unit<true, C, 1>(gpp.pa, gpp.pb, true, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
+        }
+    } else {
+        gp_scale<true, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);
+    }
     lds_barrier();
 
     // ---- diagonal-block inverses; write-out of the P~ blocks and the normalisers

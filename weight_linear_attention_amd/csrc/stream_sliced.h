@@ -208,9 +208,10 @@ __device__ __forceinline__ void gp_pair_half(GPPair& g, const u16* Xk, const u16
 }
 
 // Chunk 64, four waves: wave w takes pair q = w % 2 over half h = w / 2 of the k-steps.  The
-// h = 1 waves leave their partial tiles and sums in LDS at `part` (dead space of the phase);
-// after the barrier the h = 0 waves add them and write the normalisers 1 / (row sum + eps)
-// of K rows and Q rows RA, RB.  The caller then scales the h = 0 waves' tiles.
+// two waves of a pair then swap halves through LDS at `part` (dead space of the phase): the
+// h = 0 wave completes the pair's G tiles and K normalisers, the h = 1 wave its P tiles and Q
+// normalisers (1 / (row sum + eps)).  The caller scales the completed tiles (G in ga / gb of
+// the h = 0 waves, P in pa / pb of the h = 1 waves).
 template <int NU>
 __device__ __forceinline__ void gp_raw_c64(GPPair& g, const u16* Xk, const u16* Xq, f32x4* part,
                                            float* rhok, float* rhoq, int w, int l, int l16, int g4) {
@@ -227,32 +228,38 @@ __device__ __forceinline__ void gp_raw_c64(GPPair& g, const u16* Xk, const u16* 
         s[i] += __shfl_xor(s[i], 16);
         s[i] += __shfl_xor(s[i], 32);
     }
-    f32x4* mine = part + q * 17 * 64 + l;              // 16 tiles + the sums, per pair
-    if (h == 1) {
+    // slot (q, h): the half that wave (q, 1 - h) completes, 8 tiles (32 KB for the four slots)
+    // and its 2 row sums (2 KB after the tiles)
+    f32x4* mine = part + (q * 2 + h) * 8 * 64 + l;
+    f32x4* other = part + (q * 2 + 1 - h) * 8 * 64 + l;
+    float2* sums = reinterpret_cast<float2*>(part + 4 * 8 * 64);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            mine[(4 * 0 + t) * 64] = g.ga[t];
-            mine[(4 * 1 + t) * 64] = g.gb[t];
-            mine[(4 * 2 + t) * 64] = g.pa[t];
-            mine[(4 * 3 + t) * 64] = g.pb[t];
-        }
-        mine[16 * 64] = f32x4{s[0], s[1], s[2], s[3]};
+    for (int t = 0; t < 4; ++t) {
+        mine[t * 64] = h == 0 ? g.pa[t] : g.ga[t];
+        mine[(4 + t) * 64] = h == 0 ? g.pb[t] : g.gb[t];
     }
+    sums[(q * 2 + h) * 64 + l] = h == 0 ? make_float2(s[2], s[3]) : make_float2(s[0], s[1]);
     lds_barrier();
+    const float2 o = sums[(q * 2 + 1 - h) * 64 + l];
     if (h == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            g.ga[t] += mine[(4 * 0 + t) * 64];
-            g.gb[t] += mine[(4 * 1 + t) * 64];
-            g.pa[t] += mine[(4 * 2 + t) * 64];
-            g.pb[t] += mine[(4 * 3 + t) * 64];
+            g.ga[t] += other[t * 64];
+            g.gb[t] += other[(4 + t) * 64];
         }
-        const f32x4 o = mine[16 * 64];
         if (g4 == 0) {
-            rhok[16 * q + l16] = __builtin_amdgcn_rcpf(s[0] + o[0] + kDpfpEps);
-            rhok[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(s[1] + o[1] + kDpfpEps);
-            rhoq[16 * q + l16] = __builtin_amdgcn_rcpf(s[2] + o[2] + kDpfpEps);
-            rhoq[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(s[3] + o[3] + kDpfpEps);
+            rhok[16 * q + l16] = __builtin_amdgcn_rcpf(s[0] + o.x + kDpfpEps);
+            rhok[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(s[1] + o.y + kDpfpEps);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            g.pa[t] += other[t * 64];
+            g.pb[t] += other[(4 + t) * 64];
+        }
+        if (g4 == 0) {
+            rhoq[16 * q + l16] = __builtin_amdgcn_rcpf(s[2] + o.x + kDpfpEps);
+            rhoq[16 * (3 - q) + l16] = __builtin_amdgcn_rcpf(s[3] + o.y + kDpfpEps);
         }
     }
 }
@@ -361,8 +368,8 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     GPTiles<C, NW> gp;
     GPPair gpp;
     if constexpr (RAWGP) {
-        // operands built in registers from the raw rows; partial tiles over the K slice's
-        // space (dead at chunk 64)
+        // operands built in registers from the raw rows; partial tiles over the K and Q
+        // slices' space (34 KB, dead at chunk 64)
         gp_raw_c64<NU>(gpp, Xk, Xq, reinterpret_cast<f32x4*>(Ks), rhok, rhoq, w, l, l16, g4);
     } else {
         gp_zero(gp);
@@ -393,12 +400,11 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     lds_barrier();
 
     if constexpr (RAWGP) {
-        if (w == 0) {
-            gp_scale_unit<true, C, 0>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
-            gp_scale_unit<true, C, 0>(gpp.pa, gpp.pb, true, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
-        } else if (w == 1) {
-            gp_scale_unit<true, C, 1>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
-            gp_scale_unit<true, C, 1>(gpp.pa, gpp.pb, true, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4);
+        switch (w) {
+            case 0: gp_scale_unit<true, C, 0>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4); break;
+            case 1: gp_scale_unit<true, C, 1>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4); break;
+            case 2: gp_scale_unit<true, C, 0>(gpp.pa, gpp.pb, true, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4); break;
+            default: gp_scale_unit<true, C, 1>(gpp.pa, gpp.pb, true, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4); break;
         }
     } else {
         gp_scale<true, C>(gp, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, w, l16, g4);

@@ -32,6 +32,9 @@ def _weights(seed, d_model, H, d_k, d_v, dtype, L=1):
     (4, 256, 512, 8, 64, 64, torch.bfloat16),
     (2, 77, 136, 3, 16, 24, torch.float32),
     (3, 45, 72, 5, 32, 8, torch.bfloat16),
+    # ragged rows, columns and k runs with 32-row tiles (the projection here; both maps below)
+    (3, 333, 264, 5, 40, 48, torch.float32),
+    (2, 700, 520, 4, 32, 40, torch.bfloat16),
 ])
 def test_layer_project_and_output(B, T, d_model, H, d_k, d_v, dtype):
     log(f"layer maps B{B} T{T} d_model{d_model} H{H} d_k{d_k} d_v{d_v} {dtype}")

@@ -324,7 +324,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     char* const WT = smem + a.s_wt;
     float* const Zb = reinterpret_cast<float*>(smem + a.s_z);
     float* const Ub = reinterpret_cast<float*>(smem + a.s_u);
-    float* const Xq = reinterpret_cast<float*>(smem + a.s_raw);    // Q W^T partials exchanged
+    float* const Xq = reinterpret_cast<float*>(smem + a.s_raw);    // Q W^T partials exchanged,
+                                                                   // then rho_k o U
     u16* const Yb = reinterpret_cast<u16*>(smem + a.s_y);          // [C][32] bf16
     u16* const Vr = reinterpret_cast<u16*>(smem + a.s_voff);       // [C][32] bf16
     auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
 
     // ---- per-chunk results of the prep kernel (as in delta_stream_kernel)
     uint4 ah[NTB], al[NTB], pa[NTB];
-    f32x4 rka[4], rkc, rqv;
+    f32x4 rkc, rqv;
     auto load_ws = [&](int n) {
         const int64_t u = static_cast<int64_t>(bh) * NC + n;
         const char* ahp = a.ws + a.o_ah + u * (C * C * 2);
@@ -429,8 +430,6 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
             pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, rt * NTB + j, l));
         }
         const float* rk = reinterpret_cast<const float*>(a.ws + a.o_rk) + u * C;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) rka[tt] = *reinterpret_cast<const f32x4*>(rk + 16 * tt + 4 * g4);
         rkc = *reinterpret_cast<const f32x4*>(rk + 16 * rt + 4 * g4);
         rqv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rq) + u * C + 16 * rt + 4 * g4);
     };
@@ -515,6 +514,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
         lds_barrier();                                           // B2
 
         // ---- C: U tile (rt, h) = A'' Z; the full Q W^T tile
+        f32x4 qacc;
         {
             f32x4 u = zero4();
 #pragma unroll
@@ -528,8 +528,11 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
                 u = mfma_bf16_k32(as_bf16x8(al[j]), zh, u);
             }
             *tile(Ub, rt, h) = u;
+            // this wave's Q W^T partner tile is read once, here; its slot then takes rho_k o U,
+            // the memory update's operand, so no wave needs the other row tiles' rho_k
+            qacc = (qo + *tile(Xq, rt, h)) * rqv;
+            *tile(Xq, rt, h) = u * rkc;
         }
-        const f32x4 qacc = (qo + *tile(Xq, rt, h)) * rqv;
         // the next chunk's K tile and v columns (buffers last read in the previous chunk and in
         // phase B), then the loads of the chunk after it
         build_k(Kn);
@@ -551,8 +554,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
         }
 #pragma unroll
         for (int j = 0; j < NTB; ++j) {
-            const bf16x8 ub0 = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, 0) * rka[2 * j], *tile(Ub, 2 * j + 1, 0) * rka[2 * j + 1]));
-            const bf16x8 ub1 = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, 1) * rka[2 * j], *tile(Ub, 2 * j + 1, 1) * rka[2 * j + 1]));
+            const bf16x8 ub0 = as_bf16x8(pack_bf16x8(*tile(Xq, 2 * j, 0), *tile(Xq, 2 * j + 1, 0)));
+            const bf16x8 ub1 = as_bf16x8(pack_bf16x8(*tile(Xq, 2 * j, 1), *tile(Xq, 2 * j + 1, 1)));
             const u16* kt = Kc + (32 * j + 4 * g4 + (l16 >> 2)) * krs + 4 * (l16 & 3);
 #pragma unroll
             for (int s = 0; s < NDW; ++s) {

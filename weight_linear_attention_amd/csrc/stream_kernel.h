@@ -363,21 +363,21 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     };
 
     // ---- raw inputs.  K task of this thread: row tid / 8, positions 8 (tid % 8) .. + 7 and the
-    //      8 positions before them (cyclically); the v columns as before; the Q windows of the
+    //      8 positions before them (cyclically: the previous lane's 8 of the same row, taken
+    //      by DPP when the tile is built); the v columns as before; the Q windows of the
     //      wave's row tile: q[j0 - 4 .. j0 + 3] for j0 = 16 (2 h + e) + 4 g4, e = 0, 1
     const int64_t row0 = static_cast<int64_t>(bh) * T;
     const u16* kB = static_cast<const u16*>(a.k) + row0 * DK;
     const u16* qB = static_cast<const u16*>(a.q) + row0 * DK;
     const u16* vB = static_cast<const u16*>(a.v) + row0 * d_v + col0;
     const int ktr = tid >> 3, kjg = tid & 7;
-    uint4 ka, kp, rv;
+    uint4 ka, rv;
     uint32_t mk = 0u, mv = 0u;
     auto load_k = [&](int n) {
         const int t0 = n * C, Cn = min(C, T - t0);
         const bool ok = ktr < Cn;
         const u16* r = kB + static_cast<int64_t>(t0 + (ok ? ktr : 0)) * DK;
         ka = *reinterpret_cast<const uint4*>(r + 8 * kjg);
-        kp = *reinterpret_cast<const uint4*>(r + 8 * ((kjg + 7) & 7));
         mk = ok ? 0xffffffffu : 0u;
         const bool okv = tid < 4 * C && (tid >> 2) < Cn;
         rv = *reinterpret_cast<const uint4*>(vB + static_cast<int64_t>(t0 + (okv ? tid >> 2 : 0)) * d_v +
@@ -399,7 +399,16 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     // the next chunk's K tile: one DPFP task per thread (rows past the end zero)
     auto build_k = [&](u16* Kn) {
         const uint32_t ak[4] = {ka.x & mk, ka.y & mk, ka.z & mk, ka.w & mk};
-        const uint32_t pk[4] = {kp.x & mk, kp.y & mk, kp.z & mk, kp.w & mk};
+        // a row's eight tasks sit in eight aligned lanes: lane kjg - 1 (kjg >= 1, DPP row_shr:1)
+        // or kjg + 7 (kjg == 0, row_shl:7) holds the positions before this task's
+        const uint32_t a4[4] = {ka.x, ka.y, ka.z, ka.w};
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t prev = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a4[e]), 0x111, 0xF, 0xF, false));
+            const uint32_t wrap = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a4[e]), 0x107, 0xF, 0xF, false));
+            pk[e] = (kjg == 0 ? wrap : prev) & mk;
+        }
         float a8[8], p8[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -62,9 +62,24 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
     a.s_u = off;
     off += 8 * 1024;
     if (off > kMaxLdsStream) return false;
+    plan->C = C;
+    plan->lds_prep = cp.lds_prep;
+    plan->sliced_prep = false;
+    plan->sliced_stream = false;
+    if (d_k == 64 && nu <= 4) {
+        const int lds = plan_prep_sliced(C, &a);
+        if (lds > 0) {
+            plan->lds_prep = lds;
+            plan->sliced_prep = true;
+        }
+    }
     plan->pipe = false;
-    if (d_k == 64 && nu <= 3) {
-        // pipelined kernel: two K tiles, W^T copy, Z, U and Q W^T exchange tiles, y and v rows
+    if (d_k == 64 && nu <= 3 && plan->sliced_prep) {
+        // pipelined kernel: two K tiles, W^T copy, Z tiles, the bf16 U and rho_k o U blocks, Q W^T
+        // exchange tiles, y and v rows.  Its K rows are 800 bytes at D = 384 (row stride = 32
+        // mod 256 bytes), where both the 16-byte operand reads of 16 rows x 4 lanes and the
+        // transposed reads hit distinct banks; the sliced prep does not use this stride.
+        a.krs = D + 16;
         int o = 0;
         a.s_k = o;
         o = align16s(o + C * a.krs * 2);
@@ -85,17 +100,6 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
         if (o > kMaxLdsStream) return false;
         off = o;
         plan->pipe = true;
-    }
-    plan->C = C;
-    plan->lds_prep = cp.lds_prep;
-    plan->sliced_prep = false;
-    plan->sliced_stream = false;
-    if (d_k == 64 && nu <= 4) {
-        const int lds = plan_prep_sliced(C, &a);
-        if (lds > 0) {
-            plan->lds_prep = lds;
-            plan->sliced_prep = true;
-        }
     }
     plan->args = a;
     plan->lds_stream = off;

@@ -323,12 +323,20 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     u16* const Kb1 = reinterpret_cast<u16*>(smem + a.s_q);
     char* const WT = smem + a.s_wt;
     float* const Zb = reinterpret_cast<float*>(smem + a.s_z);
-    float* const Ub = reinterpret_cast<float*>(smem + a.s_u);
-    float* const Xq = reinterpret_cast<float*>(smem + a.s_raw);    // Q W^T partials exchanged,
-                                                                   // then rho_k o U
+    char* const Ub = smem + a.s_u;                                 // U, then rho_k o U at + 4 KiB:
+                                                                   // bf16 B blocks of 32 rows
+    float* const Xq = reinterpret_cast<float*>(smem + a.s_raw);    // Q W^T partials exchanged
     u16* const Yb = reinterpret_cast<u16*>(smem + a.s_y);          // [C][32] bf16
     u16* const Vr = reinterpret_cast<u16*>(smem + a.s_voff);       // [C][32] bf16
     auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
+    // B block (row pair j, column tile c) of a bf16 U-type operand: lane l's 16 bytes hold its
+    // four values of row tile 2 j, then its four of row tile 2 j + 1
+    auto ublk = [&](int off, int j, int c) {
+        return as_bf16x8(*reinterpret_cast<const uint4*>(Ub + off + ((j * 2 + c) * 64 + l) * 16));
+    };
+    auto put_ublk = [&](int off, const f32x4& x) {
+        *reinterpret_cast<uint2*>(Ub + off + (((rt >> 1) * 2 + h) * 64 + l) * 16 + 8 * (rt & 1)) = pack_bf16x4(x);
+    };
 
     // ---- memory tiles: d-tile w + 8 s, column tile c (rows d = 16 dt + 4 g4 + e, column l16)
     f32x4 Wst[NDW][2];
@@ -536,11 +544,11 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
                 u = mfma_bf16_k32(as_bf16x8(ah[j]), zl, u);
                 u = mfma_bf16_k32(as_bf16x8(al[j]), zh, u);
             }
-            *tile(Ub, rt, h) = u;
-            // this wave's Q W^T partner tile is read once, here; its slot then takes rho_k o U,
-            // the memory update's operand, so no wave needs the other row tiles' rho_k
+            // U for Y and rho_k o U for the memory update, stored once as the bf16 operands
+            // both take (so no wave needs the other row tiles' rho_k)
+            put_ublk(0, u);
+            put_ublk(4096, u * rkc);
             qacc = (qo + *tile(Xq, rt, h)) * rqv;
-            *tile(Xq, rt, h) = u * rkc;
         }
         // the next chunk's K tile and v columns (buffers last read in the previous chunk and in
         // phase B), then the loads of the chunk after it
@@ -555,16 +563,14 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
 #pragma unroll
             for (int j = 0; j < NTB; ++j) {
                 if (2 * j > rt) break;
-                const bf16x8 ub = as_bf16x8(pack_bf16x8(*tile(Ub, 2 * j, h), *tile(Ub, 2 * j + 1, h)));
-                y = mfma_bf16_k32(as_bf16x8(pa[j]), ub, y);
+                y = mfma_bf16_k32(as_bf16x8(pa[j]), ublk(0, j, h), y);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) Yb[(16 * rt + 4 * g4 + e) * 32 + 16 * h + l16] = f32_to_bf16_bits(y[e]);
         }
 #pragma unroll
         for (int j = 0; j < NTB; ++j) {
-            const bf16x8 ub0 = as_bf16x8(pack_bf16x8(*tile(Xq, 2 * j, 0), *tile(Xq, 2 * j + 1, 0)));
-            const bf16x8 ub1 = as_bf16x8(pack_bf16x8(*tile(Xq, 2 * j, 1), *tile(Xq, 2 * j + 1, 1)));
+            const bf16x8 ub0 = ublk(4096, j, 0), ub1 = ublk(4096, j, 1);
             const u16* kt = Kc + (32 * j + 4 * g4 + (l16 >> 2)) * krs + 4 * (l16 & 3);
 #pragma unroll
             for (int s = 0; s < NDW; ++s) {

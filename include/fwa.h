@@ -134,8 +134,11 @@ fwa_status fwa_dpfp(const void* x, void* phi, int64_t n_vec, int d_k, int nu,
  *     stream   bf16 only, two launches: every chunk's (I + L)^-1 diag(beta), P~ and DPFP
  *              normalisers in parallel, then one serial pass per (b, h, 32 columns of d_v)
  *              that rebuilds the DPFP features from the raw rows and keeps the memory on chip.
- *              Workspace of B*H*ceil(T/chunk) * (3*chunk*chunk*2 + 2*chunk*4) bytes (24.5 KiB
- *              per chunk of 64, 97 KiB per chunk of 128).
+ *              Workspace of B*H*ceil(T/chunk) * (3*S + 2*chunk*4) bytes, S the bytes of one
+ *              chunk's block-lower-triangular operand matrix: for d_k = 64 only its 16 x 32
+ *              blocks on and below the diagonal, S = 1024*(chunk/32)*(chunk/32 + 1) (18.5 KiB
+ *              per chunk of 64, 61 KiB per chunk of 128); for d_k = 16 and 32 the full
+ *              S = chunk*chunk*2 (24.5 KiB per chunk of 64).
  *              Chunk 64: d_v in {32, 64}, D in {128, 256, 384}, nu <= 8; and, for d_k = 64
  *              with nu <= 4, also d_v = 16 and D = 512.  Chunk 128: d_k = 64, nu <= 4,
  *              d_v in {32, 64} (the DPFP features are built one shift block of 128 columns

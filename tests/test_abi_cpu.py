@@ -178,10 +178,12 @@ def _workspace_formula(B, H, T, d_k, d_v, nu, chunk, es):
     return B * H * nc * per_chunk * es + B * H * nc * chunk * (d_v + 2) * 4
 
 
-def _stream_workspace_formula(B, H, T, chunk):
-    """The streaming path's workspace as fwa.h states it."""
+def _stream_workspace_formula(B, H, T, d_k, chunk):
+    """The streaming path's workspace as fwa.h states it: at d_k = 64 only the operand blocks
+    on and below the diagonal are stored."""
     nc = -(-T // chunk)
-    return B * H * nc * (3 * chunk * chunk * 2 + 2 * chunk * 4)
+    s = 1024 * (chunk // 32) * (chunk // 32 + 1) if d_k == 64 else chunk * chunk * 2
+    return B * H * nc * (3 * s + 2 * chunk * 4)
 
 
 @pytest.mark.parametrize("shape,dtype,path", [
@@ -217,7 +219,7 @@ def test_forward_info_auto_choice(shape, dtype, path):
     if path == "chunked":
         assert ws == _workspace_formula(B, H, T, d_k, d_v, nu, chunk, 2 if dtype == "bf16" else 4)
     elif path == "stream":
-        assert ws == _stream_workspace_formula(B, H, T, chunk)
+        assert ws == _stream_workspace_formula(B, H, T, d_k, chunk)
     else:
         assert ws == 0
 
@@ -258,7 +260,10 @@ def test_forward_info_path_request():
         fwa.delta_forward_info(1, 1, 64, 16, 16, 1, 16, path="chunked")
     assert e.value.status == fwa.FWA_ERR_UNSUPPORTED
     assert fwa.delta_forward_info(4, 8, 4096, 64, 64, 2, 64, torch.bfloat16, path="stream") == (
-        "stream", _stream_workspace_formula(4, 8, 4096, 64))
+        "stream", _stream_workspace_formula(4, 8, 4096, 64, 64))
+    # d_k = 32 takes the compact prep, which stores every operand block
+    assert fwa.delta_forward_info(4, 8, 4096, 32, 64, 2, 64, torch.bfloat16, path="stream") == (
+        "stream", _stream_workspace_formula(4, 8, 4096, 32, 64))
     for args in ((1, 8, 1024, 64, 64, 1, 64),                       # fp32
                  (1, 8, 1024, 64, 64, 1, 32, torch.bfloat16),       # chunk 32
                  (1, 8, 1024, 32, 16, 2, 64, torch.bfloat16),       # d_k 32 with d_v 16

@@ -122,6 +122,18 @@ __device__ __forceinline__ const char* blk_ptr(const char* base, int64_t blk, in
     return base + (blk * 64 + l) * 16;
 }
 
+// Block-lower-triangular operand matrices of a chunk (A'' hi, lo and P~ as 16-row x 32-column
+// A-operand blocks (ta, j)) in the order that leaves out the blocks above the diagonal: block
+// (ta, j) exists for 2 j <= ta, row tile by row tile, so row tile ta starts after
+// sum_{r < ta} (r / 2 + 1) blocks.  C = 64 keeps 6 of 8 blocks, C = 128 20 of 32.
+__host__ __device__ constexpr int tri_nblocks(int C) {
+    return (C / 32) * (C / 32 + 1);
+}
+__device__ __forceinline__ int tri_blk(int ta, int j) {
+    const int hf = ta >> 1;
+    return hf * (hf + 1) + (ta & 1) * (hf + 1) + j;
+}
+
 // ------------------------------------------------------------------------------------------
 // prep, one chunk (b, h, n) per workgroup pass.  DPFP, G and P with the normalisers, L and its
 // diagonal-block inverses, the block inverse A = (I + L)^-1, U_y by block substitution and

@@ -35,13 +35,7 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
     if (!plan_chunked(BH, T, d_k, d_v, nu, C, true, &cp)) return false;   // prep LDS layout
     ChunkArgs a = cp.args;
     const int64_t NU = static_cast<int64_t>(BH) * a.NC;
-    const int64_t szCC = static_cast<int64_t>(C) * C * 2, szR = C * 4;
     a.o_wy = a.o_kt = a.o_qa = a.o_uy = a.o_wn = a.o_un = 0;
-    a.o_pa = 0;
-    a.o_ah = a.o_pa + NU * szCC;
-    a.o_al = a.o_ah + NU * szCC;
-    a.o_rk = a.o_al + NU * szCC;
-    a.o_rq = a.o_rk + NU * szR;
     // the y buffer's byte offsets (up to the last chunk's padded rows) fit 32 bits
     if ((static_cast<int64_t>(T) + C) * d_v * 2 >= (int64_t(1) << 32)) return false;
     // stream kernel LDS: K and Q tiles, the raw slot, W^T copy, Z (then y) and U tiles
@@ -100,7 +94,21 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
         if (o > kMaxLdsStream) return false;
         off = o;
         plan->pipe = true;
+    } else if (plan->sliced_prep) {
+        // the 32-column full-tile serial kernel reads every block: it takes the compact prep
+        plan->sliced_prep = false;
+        plan->lds_prep = cp.lds_prep;
     }
+    // workspace: A'' hi, lo and P~ blocks (the sliced prep stores those on and below the
+    // diagonal only, the compact prep all of them), then rho_k and rho_q
+    const int64_t szCC = plan->sliced_prep ? static_cast<int64_t>(tri_nblocks(C)) * 1024
+                                           : static_cast<int64_t>(C) * C * 2;
+    const int64_t szR = C * 4;
+    a.o_pa = 0;
+    a.o_ah = a.o_pa + NU * szCC;
+    a.o_al = a.o_ah + NU * szCC;
+    a.o_rk = a.o_al + NU * szCC;
+    a.o_rq = a.o_rk + NU * szR;
     plan->args = a;
     plan->lds_stream = off;
     plan->ndw = D / 128;

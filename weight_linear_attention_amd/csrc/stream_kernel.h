@@ -435,16 +435,19 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     // ---- per-chunk results of the prep kernel (as in delta_stream_kernel)
     uint4 ah[NTB], al[NTB], pa[NTB];
     f32x4 rkc, rqv;
+    // (the A'' and P~ blocks are stored on and below the diagonal only, in tri_blk order; the
+    // loads of a block above it re-read the row tile's last block and go unused)
     auto load_ws = [&](int n) {
         const int64_t u = static_cast<int64_t>(bh) * NC + n;
-        const char* ahp = a.ws + a.o_ah + u * (C * C * 2);
-        const char* alp = a.ws + a.o_al + u * (C * C * 2);
-        const char* pap = a.ws + a.o_pa + u * (C * C * 2);
+        const char* ahp = a.ws + a.o_ah + u * (tri_nblocks(C) * 1024);
+        const char* alp = a.ws + a.o_al + u * (tri_nblocks(C) * 1024);
+        const char* pap = a.ws + a.o_pa + u * (tri_nblocks(C) * 1024);
 #pragma unroll
         for (int j = 0; j < NTB; ++j) {
-            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, rt * NTB + j, l));
-            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, rt * NTB + j, l));
-            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, rt * NTB + j, l));
+            const int tb = tri_blk(rt, min(j, rt >> 1));
+            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, tb, l));
+            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, tb, l));
+            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, tb, l));
         }
         const float* rk = reinterpret_cast<const float*>(a.ws + a.o_rk) + u * C;
         rkc = *reinterpret_cast<const f32x4*>(rk + 16 * rt + 4 * g4);

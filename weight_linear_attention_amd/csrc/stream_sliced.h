@@ -411,12 +411,14 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     }
     lds_barrier();
 
-    // ---- diagonal-block inverses; write-out of the P~ blocks and the normalisers
+    // ---- diagonal-block inverses; write-out of the P~ blocks (those on or below the diagonal,
+    //      in tri_blk order) and the normalisers
     if (tid < C) diag_inverse(Ls, a.lss, Li, tid);
     {
-        char* pa = a.ws + a.o_pa + u * (static_cast<int64_t>(C) * C * 2);
+        char* pa = a.ws + a.o_pa + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
         for (int e = tid; e < NT * NTB * 64; e += NTH) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
+            if (2 * j > ta) continue;                    // uniform over the wave
             const u16* src = Ps + (16 * ta + (lam & 15)) * a.pss + 32 * j + 4 * (lam >> 4);
             uint4 val = make_uint4(0u, 0u, 0u, 0u);
             if (2 * j <= ta) {
@@ -429,7 +431,7 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
                 val.z = hi.x;
                 val.w = hi.y;
             }
-            *reinterpret_cast<uint4*>(pa + static_cast<int64_t>(e) * 16) = val;
+            *reinterpret_cast<uint4*>(blk_ptr(pa, tri_blk(ta, j), lam)) = val;
         }
         if (tid < C) {
             reinterpret_cast<float*>(a.ws + a.o_rk)[u * C + tid] = rhok[tid];
@@ -484,19 +486,22 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     lds_barrier();
 
     // ---- AH, AL: A-operand blocks (ta, j) of A'' hi and lo (slot (h, e) of lane l =
-    //      A''[16 ta + l % 16][16 (2 j + h) + 4 (l / 16) + e]); blocks above the diagonal are zero
+    //      A''[16 ta + l % 16][16 (2 j + h) + 4 (l / 16) + e]), those on or below the diagonal
+    //      in tri_blk order
     {
-        char* ah = a.ws + a.o_ah + u * (static_cast<int64_t>(C) * C * 2);
-        char* al = a.ws + a.o_al + u * (static_cast<int64_t>(C) * C * 2);
+        char* ah = a.ws + a.o_ah + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
+        char* al = a.ws + a.o_al + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
         for (int e = tid; e < NT * NTB * 64; e += NTH) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
+            if (2 * j > ta) continue;                    // uniform over the wave
             const int at = (16 * ta + (lam & 15)) * aps + 32 * j + 4 * (lam >> 4);
             const uint2 h0 = *reinterpret_cast<const uint2*>(Bh + at);
             const uint2 h1 = *reinterpret_cast<const uint2*>(Bh + at + 16);
             const uint2 l0 = *reinterpret_cast<const uint2*>(Bl + at);
             const uint2 l1 = *reinterpret_cast<const uint2*>(Bl + at + 16);
-            *reinterpret_cast<uint4*>(ah + static_cast<int64_t>(e) * 16) = make_uint4(h0.x, h0.y, h1.x, h1.y);
-            *reinterpret_cast<uint4*>(al + static_cast<int64_t>(e) * 16) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+            const int tb = tri_blk(ta, j);
+            *reinterpret_cast<uint4*>(blk_ptr(ah, tb, lam)) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            *reinterpret_cast<uint4*>(blk_ptr(al, tb, lam)) = make_uint4(l0.x, l0.y, l1.x, l1.y);
         }
     }
 }
@@ -636,19 +641,22 @@ __global__ __launch_bounds__(4 * C, 512 / (4 * C)) void delta_stream_sliced_kern
     };
 
     // ---- per-chunk results of the prep kernel: A'' blocks (w, j) hi and lo, P~ blocks (w, j),
-    //      rho_k of every row tile and rho_q of row tile w (accumulator row order)
+    //      rho_k of every row tile and rho_q of row tile w (accumulator row order).  Blocks
+    //      above the diagonal are not stored: their loads re-read the row tile's last block and
+    //      go unused (every wave issues the same loads in every chunk)
     uint4 ah[NTB], al[NTB], pa[NTB];
     f32x4 rka[NT], rqv;
     auto load_ws = [&](int n) {
         const int64_t u = static_cast<int64_t>(bh) * NC + n;
-        const char* ahp = a.ws + a.o_ah + u * (C * C * 2);
-        const char* alp = a.ws + a.o_al + u * (C * C * 2);
-        const char* pap = a.ws + a.o_pa + u * (C * C * 2);
+        const char* ahp = a.ws + a.o_ah + u * (tri_nblocks(C) * 1024);
+        const char* alp = a.ws + a.o_al + u * (tri_nblocks(C) * 1024);
+        const char* pap = a.ws + a.o_pa + u * (tri_nblocks(C) * 1024);
 #pragma unroll
         for (int j = 0; j < NTB; ++j) {
-            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, w * NTB + j, l));
-            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, w * NTB + j, l));
-            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, w * NTB + j, l));
+            const int tb = tri_blk(w, min(j, w >> 1));
+            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, tb, l));
+            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, tb, l));
+            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, tb, l));
         }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)

@@ -42,7 +42,8 @@ bool plan_stream_sliced(int BH, int T, int d_k, int d_v, int nu, int C, StreamPl
     if (lds_prep == 0) return false;
     const int NC = (T + C - 1) / C;
     const int64_t NU = static_cast<int64_t>(BH) * NC;
-    const int64_t szCC = static_cast<int64_t>(C) * C * 2, szR = C * 4;
+    // A'' hi, lo and P~: the blocks on and below the diagonal (the sliced prep's order)
+    const int64_t szCC = static_cast<int64_t>(tri_nblocks(C)) * 1024, szR = C * 4;
     a.o_pa = 0;
     a.o_ah = a.o_pa + NU * szCC;
     a.o_al = a.o_ah + NU * szCC;

@@ -110,27 +110,22 @@ __device__ __forceinline__ void dpfp_slice_any(int i, const u16* Xk, const u16* 
 constexpr int kRawRow = kSliceDk + 4;
 
 // The window's k values as fp32 positive and negative parts.  For the window starting at
-// position 0, the four entries before it wrap into the [-k] half, so their parts swap.
+// position 0, the four entries before it wrap into the [-k] half: their signs are flipped in
+// the packed words before unpacking, which swaps their parts.
 struct DpfpWin {
     float P[8], N[8];
 };
 __device__ __forceinline__ DpfpWin dpfp_window(const u16* row, int p0) {
     const uint2 lo = *reinterpret_cast<const uint2*>(row + ((p0 + kSliceDk - 4) & (kSliceDk - 1)));
     const uint2 hi = *reinterpret_cast<const uint2*>(row + p0);
-    const uint32_t wd[4] = {lo.x, lo.y, hi.x, hi.y};
+    const uint32_t sg = p0 == 0 ? 0x80008000u : 0u;
+    const uint32_t wd[4] = {lo.x ^ sg, lo.y ^ sg, hi.x, hi.y};
     DpfpWin wn;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float r = (e & 1) ? __uint_as_float(wd[e >> 1] & 0xffff0000u) : __uint_as_float(wd[e >> 1] << 16);
         wn.P[e] = relu_f(r);
         wn.N[e] = wn.P[e] - r;                 // relu(-r), exactly
-    }
-    const bool wrap = p0 == 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float p = wn.P[e], n = wn.N[e];
-        wn.P[e] = wrap ? n : p;
-        wn.N[e] = wrap ? p : n;
     }
     return wn;
 }

@@ -259,6 +259,18 @@ __device__ __forceinline__ void gp_raw_c64(GPPair& g, const u16* Xk, const u16* 
     }
 }
 
+// A 16x16 fp32 tile in accumulator layout (lane (l16, g4), slot e: row 4 g4 + e, column l16)
+// transposed into row layout (lane (l16, g4), slot e: row l16, column 4 g4 + e) on the MFMA:
+// the tile fed as the A operand of the four k-steps of a 16x16x4 product reads as its transpose,
+// and the B operand is the identity (id[s] = 1 where 4 g4 + s == l16), so each output is one
+// exact product with 1.
+__device__ __forceinline__ f32x4 tile_to_rows(const f32x4& x, const float (&id)[4]) {
+    f32x4 t = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) t = mfma_f32_k4(x[s], id[s], t);
+    return t;
+}
+
 // ------------------------------------------------------------------------------------------
 // prep (compact, sliced): one workgroup of NTH / 64 waves per chunk (b, h, n): 4 at chunk 64,
 // 8 at chunk 128 (one wave per 16-column block of A).  Writes, per chunk, the
@@ -395,6 +407,7 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     lds_barrier();
 
     if constexpr (RAWGP) {
+        // waves 0, 1 hold G of pairs 0, 1; waves 2, 3 P of pairs 0, 1
         switch (w) {
             case 0: gp_scale_unit<true, C, 0>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4); break;
             case 1: gp_scale_unit<true, C, 1>(gpp.ga, gpp.gb, false, rhok, rhoq, betas, Ls, a.lss, Ps, a.pss, l16, g4); break;
@@ -436,10 +449,19 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
     lds_barrier();   // Li complete; P~ is dead (its space holds A'')
 
     // ---- A = (I + L)^-1 by block columns (column block tb = w), stored as A'' = A diag(beta)
-    //      in bf16 hi + lo:  A[ta][tb] = -Li[ta] sum_{tb <= tc < ta} L[ta][tc] A[tc][tb]
+    //      in bf16 hi + lo:  A[ta][tb] = -Li[ta] sum_{tb <= tc < ta} L[ta][tc] A[tc][tb].  At
+    //      chunk 64 each block goes to row layout on the MFMA and straight into its A-operand
+    //      blocks in the workspace (half tb & 1 of block (ta, tb / 2); a block on the diagonal
+    //      with even ta also writes its zero half); otherwise through LDS (Bh, Bl).
+    char* ahg = a.ws + a.o_ah + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
+    char* alg = a.ws + a.o_al + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
+    float id[4];                                       // identity B operands of tile_to_rows
+#pragma unroll
+    for (int s = 0; s < 4; ++s) id[s] = 4 * g4 + s == l16 ? 1.0f : 0.0f;
     if (w < NT) {
         const int tb = w;
         const float bsc = betas[16 * tb + l16];
+        const f32x4 bsr = *reinterpret_cast<const f32x4*>(betas + 16 * tb + 4 * g4);
         f32x4 Ab[NT];
 #pragma unroll
         for (int ta = 0; ta < NT; ++ta) {
@@ -468,24 +490,40 @@ __device__ __forceinline__ void prep_sliced_chunk(const ChunkArgs& a, int64_t bl
                 val = -val;
             }
             Ab[ta] = val;
+            if constexpr (RAWGP) {
+                if (ta >= tb) {
+                    const f32x4 y = tile_to_rows(val, id) * bsr;
+                    const uint2 hi = pack_bf16x4(y), lo = bf16_lo_part4(y);
+                    const int64_t off = (static_cast<int64_t>(tri_blk(ta, tb >> 1)) * 64 + l) * 16;
+                    if (ta == tb && (tb & 1) == 0) {
+                        *reinterpret_cast<uint4*>(ahg + off) = make_uint4(hi.x, hi.y, 0u, 0u);
+                        *reinterpret_cast<uint4*>(alg + off) = make_uint4(lo.x, lo.y, 0u, 0u);
+                    } else {
+                        *reinterpret_cast<uint2*>(ahg + off + 8 * (tb & 1)) = hi;
+                        *reinterpret_cast<uint2*>(alg + off + 8 * (tb & 1)) = lo;
+                    }
+                }
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int at = (16 * ta + 4 * g4 + e) * aps + 16 * tb + l16;
-                const float y = val[e] * bsc;
-                const u16 yh = f32_to_bf16_bits(y);
-                Bh[at] = yh;
-                Bl[at] = f32_to_bf16_bits(y - bf16_bits_to_f32(yh));
+                for (int e = 0; e < 4; ++e) {
+                    const int at = (16 * ta + 4 * g4 + e) * aps + 16 * tb + l16;
+                    const float y = val[e] * bsc;
+                    const u16 yh = f32_to_bf16_bits(y);
+                    Bh[at] = yh;
+                    Bl[at] = f32_to_bf16_bits(y - bf16_bits_to_f32(yh));
+                }
             }
         }
     }
+    if constexpr (RAWGP) return;
     lds_barrier();
 
     // ---- AH, AL: A-operand blocks (ta, j) of A'' hi and lo (slot (h, e) of lane l =
     //      A''[16 ta + l % 16][16 (2 j + h) + 4 (l / 16) + e]), those on or below the diagonal
     //      in tri_blk order
     {
-        char* ah = a.ws + a.o_ah + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
-        char* al = a.ws + a.o_al + u * (static_cast<int64_t>(tri_nblocks(C)) * 1024);
+        char* ah = ahg;
+        char* al = alg;
         for (int e = tid; e < NT * NTB * 64; e += NTH) {
             const int blk = e >> 6, lam = e & 63, ta = blk / NTB, j = blk % NTB;
             if (2 * j > ta) continue;                    // uniform over the wave

@@ -119,4 +119,31 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup placement.  Workgroups are dispatched to the 8 XCDs round robin by index; when
+// B*H is a multiple of 8, all workgroups of (b, h) go to XCD (b*H + h) mod 8 in all three
+// kernels, so the chain and output kernels find the prep kernel's results in that XCD's L2.
+// Maps a workgroup index to (bh, i), i = index among the workgroups of bh (per_bh of them).
+struct BhIndex {
+    int bh;
+    int64_t i;
+};
+__device__ __forceinline__ BhIndex xcd_local(int64_t b, int BH, int64_t per_bh) {
+    if (((b | per_bh) >> 32) == 0) {
+        // workgroup indices fit 32 bits (a uniform branch): 32-bit division is a few
+        // instructions, the 64-bit one about a hundred
+        const uint32_t bb = static_cast<uint32_t>(b), pb = static_cast<uint32_t>(per_bh);
+        if ((BH & 7) == 0) {
+            const uint32_t x = bb & 7, j = bb >> 3, q = j / pb;
+            return BhIndex{static_cast<int>(q * 8 + x), static_cast<int64_t>(j - q * pb)};
+        }
+        const uint32_t q = bb / pb;
+        return BhIndex{static_cast<int>(q), static_cast<int64_t>(bb - q * pb)};
+    }
+    if ((BH & 7) == 0) {
+        const int64_t x = b & 7, j = b >> 3;      // XCD and index inside it
+        return BhIndex{static_cast<int>((j / per_bh) * 8 + x), j % per_bh};
+    }
+    return BhIndex{static_cast<int>(b / per_bh), b % per_bh};
+}
+
 }  // namespace fwa

@@ -6,11 +6,16 @@
 // For a chunk of C rows with normalised features K, Q (C x D) starting from W0, z0, and
 // M = lower_incl(Q K^T):
 //   Y = (Q W0^T + M V) / (Q z0 + M 1)   (row-wise),   W1 = W0 + V^T K,   z1 = z0 + K^T 1.
-// Three launches:
+// Launches:
 //   1. sum_prep  per chunk: K, Q, and the chunk-local parts M V and M 1            (parallel)
 //   2. sum_scan  per (b, h, 16 rows of W), chunks in order: W^T in fp32 MFMA accumulators
 //      split over the 4 waves by d-tiles; Q W^T, Q z, y, then W^T += K^T V, z += K^T 1 (serial)
 //   3. sum_zfinal per (b, h): z_final from z0 and the chunks' key sums (where it is asked for)
+// The memory's recurrence is a plain sum, so where fewer than 256 serial workgroups would cover
+// the sequences, each sequence is cut into NB blocks of LC chunks: a launch before the scan
+// forms the sums of K^T V and of the key sums over SP parts of every block but the last in
+// parallel (sum_blocksum), and block b's scan starts from W0 + the parts of blocks 0 .. b - 1
+// (W0 itself copied into the workspace by that launch, since W_final may be W0).
 // Arithmetic is fp32 (the vector ALU and the fp32 MFMA); chunks of 32 rows.
 #include "chunk_f32.h"
 #include "fwa_internal.h"
@@ -20,10 +25,30 @@ namespace fwa {
 constexpr int kSumThreads = 256;
 
 struct SumLayout {
-    int64_t kt, qt, nm, dn, ks, end;   // K, Q [C][D]; M V [C][d_v]; M 1 [C]; K^T 1 [D] (per chunk)
+    int64_t kt, qt, nm, dn, ks;   // K, Q [C][D]; M V [C][d_v]; M 1 [C]; K^T 1 [D] (per chunk)
+    int64_t wc, bs, zb;           // with NB > 1: W0 copy [BH][d_v][D]; sums of K^T V over the
+    int64_t end;                  // block parts [NB-1][SP][BH][d_v][D] and of K^T 1 [..][BH][D]
 };
 
-static SumLayout sum_layout(int64_t NU, int D, int d_v) {
+// Blocks per sequence: enough (b, h, 16-column) scan workgroups to cover the 256 CUs, at most
+// one per chunk.  *LC = chunks per block; the count returned is the number of non-empty blocks.
+static int sum_blocks(int BH, int NC, int d_v, int* LC) {
+    const int64_t wgs = int64_t(BH) * ((d_v + 15) / 16);
+    int nb = 1;
+    if (NC > 1 && wgs < 256) nb = static_cast<int>(256 / wgs < NC ? 256 / wgs : NC);
+    *LC = NC > 0 ? (NC + nb - 1) / nb : 1;
+    return NC > 0 ? (NC + *LC - 1) / *LC : 1;
+}
+// Parts per block for the block sums: about 512 sum workgroups, each over at least one chunk.
+static int sum_parts(int BH, int NB, int LC, int d_v) {
+    if (NB <= 1) return 1;
+    const int64_t wgs = int64_t(BH) * (NB - 1) * ((d_v + 15) / 16);
+    const int64_t sp = 512 / wgs;
+    return static_cast<int>(sp < 1 ? 1 : (sp > LC ? LC : sp));
+}
+
+static SumLayout sum_layout(int64_t BH, int NC, int D, int d_v, int NB, int SP) {
+    const int64_t NU = BH * NC;
     SumLayout L;
     int64_t o = 0;
     L.kt = o; o += NU * kBC * D;
@@ -31,6 +56,9 @@ static SumLayout sum_layout(int64_t NU, int D, int d_v) {
     L.nm = o; o += NU * kBC * d_v;
     L.dn = o; o += NU * kBC;
     L.ks = o; o += NU * D;
+    L.wc = o; o += NB > 1 ? BH * d_v * D : 0;
+    L.bs = o; o += NB > 1 ? int64_t(NB - 1) * SP * BH * d_v * D : 0;
+    L.zb = o; o += NB > 1 ? int64_t(NB - 1) * SP * BH * D : 0;
     L.end = o;
     return L;
 }
@@ -46,6 +74,8 @@ struct SumArgs {
     float* zf;
     float* ws;
     int BH, T, NC, d_k, d_v, nu, D;
+    int NB, LC, SP;               // blocks per sequence, chunks per block (NB = 1: one scan),
+                                  // parts per block for the block sums
     SumLayout L;
 };
 
@@ -132,12 +162,107 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
 
 // z_final = z0 + the chunks' column sums of K, one thread per entry (each reads its z0 entry
 // before writing its z_final entry, so z_final may be z0).
+// Eight independent partial sums keep eight loads in flight per thread.
 __global__ __launch_bounds__(256) void sum_zfinal_kernel(SumArgs a) {
     const int bh = blockIdx.x;
     for (int p = threadIdx.x; p < a.D; p += 256) {
-        float z = a.z0 ? a.z0[int64_t(bh) * a.D + p] : 0.0f;
-        for (int n = 0; n < a.NC; ++n) z += a.ws[a.L.ks + (int64_t(bh) * a.NC + n) * a.D + p];
-        a.zf[int64_t(bh) * a.D + p] = z;
+        const float* ks = a.ws + a.L.ks + int64_t(bh) * a.NC * a.D + p;
+        float zp[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        int n = 0;
+        for (; n + 8 <= a.NC; n += 8)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) zp[i] += ks[int64_t(n + i) * a.D];
+        for (; n < a.NC; ++n) zp[0] += ks[int64_t(n) * a.D];
+        const float z = a.z0 ? a.z0[int64_t(bh) * a.D + p] : 0.0f;
+        a.zf[int64_t(bh) * a.D + p] = z + (((zp[0] + zp[1]) + (zp[2] + zp[3])) + ((zp[4] + zp[5]) + (zp[6] + zp[7])));
+    }
+}
+
+// Blocked scan, first launch: per (b, h, block blk < NB - 1, part sp, 16 columns) the sum of
+// K^T V over the part's chunks (fp32 MFMA; the same accumulator layout as the scan's memory
+// tiles: wave w holds d-tiles w + 4 q, lane group g supplies rows 4 g + s of each 16-row step
+// to sub-step s), and, in its first column group, the part's sum of the key sums.  A chunk's
+// operands (NDW x 8 values of K and 8 of V per lane) load a chunk ahead of its products.  The
+// workgroups of block NB - 1 (part 0) copy W0 (zeros where there is none) into the workspace.
+template <bool BF16, int NDW>
+__global__ __launch_bounds__(256) void sum_blocksum_kernel(SumArgs a) {
+    const int D = a.D, d_v = a.d_v, NDT = D / 16;
+    const int cgroups = (d_v + 15) / 16;
+    // the column groups of one (b, h, block, part) share an XCD (and its L2 copy of K)
+    const BhIndex xi = xcd_local(blockIdx.x, a.BH * a.NB * a.SP, cgroups);
+    const int cg = static_cast<int>(xi.i);
+    int rest = xi.bh;
+    const int sp = rest % a.SP;
+    rest /= a.SP;
+    const int blk = rest % a.NB, bh = rest / a.NB;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int col = 16 * cg + l16;
+    const bool cok = col < d_v;
+    if (blk == a.NB - 1) {
+        if (sp != 0) return;
+#pragma unroll
+        for (int q = 0; q < NDW; ++q) {
+            const int dt = wv + 4 * q;
+            if (!cok || dt >= NDT) continue;
+            const int64_t o = (int64_t(bh) * d_v + col) * D + 16 * dt + 4 * g4;
+            *reinterpret_cast<f32x4*>(a.ws + a.L.wc + o) =
+                a.W0 ? *reinterpret_cast<const f32x4*>(a.W0 + o) : zero4();
+        }
+        return;
+    }
+    // this part's chunks
+    const int b0 = blk * a.LC, b1 = min(a.NC, b0 + a.LC);
+    const int per = (b1 - b0 + a.SP - 1) / a.SP;
+    const int c0 = min(b1, b0 + sp * per), c1 = min(b1, c0 + per);
+    const int64_t part = (int64_t(blk) * a.SP + sp) * a.BH + bh;
+    if (cg == 0) {
+        for (int p = tid; p < D; p += 256) {
+            float zp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            int c = c0;
+            for (; c + 4 <= c1; c += 4)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zp[i] += a.ws[a.L.ks + (int64_t(bh) * a.NC + c + i) * D + p];
+            for (; c < c1; ++c) zp[0] += a.ws[a.L.ks + (int64_t(bh) * a.NC + c) * D + p];
+            a.ws[a.L.zb + part * D + p] = (zp[0] + zp[1]) + (zp[2] + zp[3]);
+        }
+    }
+    f32x4 acc[NDW];
+#pragma unroll
+    for (int q = 0; q < NDW; ++q) acc[q] = zero4();
+    float kv[NDW][8], vv[8];
+    auto fetch = [&](int c) {
+        const float* Kc = a.ws + a.L.kt + (int64_t(bh) * a.NC + c) * (kBC * D);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 16 * (i >> 2) + 4 * g4 + (i & 3), t = c * kBC + r;
+            vv[i] = (cok && t < a.T) ? load_elem<BF16>(a.v, (int64_t(bh) * a.T + t) * d_v + col) : 0.0f;
+#pragma unroll
+            for (int q = 0; q < NDW; ++q) {
+                const int dt = wv + 4 * q < NDT ? wv + 4 * q : 0;
+                kv[q][i] = Kc[r * D + 16 * dt + l16];
+            }
+        }
+    };
+    if (c0 < c1) fetch(c0);
+    for (int c = c0; c < c1; ++c) {
+        float kc[NDW][8], vc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            vc[i] = vv[i];
+#pragma unroll
+            for (int q = 0; q < NDW; ++q) kc[q][i] = kv[q][i];
+        }
+        if (c + 1 < c1) fetch(c + 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int q = 0; q < NDW; ++q) acc[q] = mfma_f32_k4(kc[q][i], vc[i], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NDW; ++q) {
+        const int dt = wv + 4 * q;
+        if (cok && dt < NDT)
+            *reinterpret_cast<f32x4*>(a.ws + a.L.bs + (part * d_v + col) * D + 16 * dt + 4 * g4) = acc[q];
     }
 }
 
@@ -159,7 +284,11 @@ __global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_v = a.d_v, NDT = a.D / 16;
     const int cgroups = (d_v + 15) / 16;
-    const int bh = blockIdx.x / cgroups, col0 = (blockIdx.x % cgroups) * 16;
+    // the column groups of one (b, h, block) share an XCD (and its L2 copy of the chunk's tiles)
+    const BhIndex xi = xcd_local(blockIdx.x, a.BH * a.NB, cgroups);
+    const int rest = xi.bh, col0 = static_cast<int>(xi.i) * 16;
+    const int blk = rest % a.NB, bh = rest / a.NB;
+    const int c0 = blk * a.LC, c1 = min(a.NC, c0 + a.LC);   // this workgroup's chunks
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int col = col0 + l16;
     const bool cok = col < d_v;
@@ -172,16 +301,28 @@ __global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
     f32x4* red = reinterpret_cast<f32x4*>(zs + D);   // [4 waves][2 row tiles][64 lanes]
     float* qzr = reinterpret_cast<float*>(red + 4 * 2 * 64);   // [4][C]
 
-    // memory tiles and z
+    // memory tiles and z at the block's start: W0 and z0 (one block), else the workspace's W0
+    // copy plus the sums of the blocks before this one
     f32x4 W[NDW];
 #pragma unroll
     for (int q = 0; q < NDW; ++q) {
         const int dt = wv + 4 * q;
         W[q] = zero4();
-        if (a.W0 && cok && dt < NDT)
-            W[q] = *reinterpret_cast<const f32x4*>(a.W0 + (int64_t(bh) * d_v + col) * D + 16 * dt + 4 * g4);
+        if (!cok || dt >= NDT) continue;
+        const int64_t o = (int64_t(bh) * d_v + col) * D + 16 * dt + 4 * g4;
+        if (a.NB == 1) {
+            if (a.W0) W[q] = *reinterpret_cast<const f32x4*>(a.W0 + o);
+        } else {
+            W[q] = *reinterpret_cast<const f32x4*>(a.ws + a.L.wc + o);
+            for (int b = 0; b < blk * a.SP; ++b)
+                W[q] += *reinterpret_cast<const f32x4*>(a.ws + a.L.bs + int64_t(b) * a.BH * d_v * D + o);
+        }
     }
-    for (int d = tid; d < D; d += 256) zs[d] = a.z0 ? a.z0[int64_t(bh) * D + d] : 0.0f;
+    for (int d = tid; d < D; d += 256) {
+        float z = a.z0 ? a.z0[int64_t(bh) * D + d] : 0.0f;
+        for (int b = 0; b < blk * a.SP; ++b) z += a.ws[a.L.zb + (int64_t(b) * a.BH + bh) * D + d];
+        zs[d] = z;
+    }
 
     // staging units: Q as 16-byte units u = tid + 256 m of the [C][D] tile (row u / (D / 4));
     // K^T as units (column d = u % D, rows 4 (u / D) .. + 3), four loads down a column of K
@@ -231,8 +372,8 @@ __global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
             pdn[e] = a.ws[a.L.dn + uf * kBC + c];
         }
     };
-    if (a.NC > 0) fetch(0);
-    for (int n = 0; n < a.NC; ++n) {
+    if (c0 < c1) fetch(c0);
+    for (int n = c0; n < c1; ++n) {
         const int t0 = n * kBC;
         __syncthreads();                      // the previous chunk's tile reads are done
 #pragma unroll
@@ -253,7 +394,7 @@ __global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
             dn[e] = pdn[e];
         }
         __syncthreads();
-        if (n + 1 < a.NC) fetch(n + 1);
+        if (n + 1 < c1) fetch(n + 1);
         // ---- 1. parts of Q W^T (MFMA) and Q z (lane -> row c = lane % 32, half of each d-tile)
         f32x4 P0 = zero4(), P1 = zero4();
         float qz = 0.0f;
@@ -316,7 +457,7 @@ __global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
             if (g4 == 0) zs[16 * dt + l16] += zp;
         }
     }
-    if (a.Wf && cok) {
+    if (a.Wf && cok && blk == a.NB - 1) {
 #pragma unroll
         for (int q = 0; q < NDW; ++q) {
             const int dt = wv + 4 * q;
@@ -331,7 +472,9 @@ bool plan_sum_forward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes
     if (d_k != 16 && d_k != 32 && d_k != 64) return false;
     if (d_v < 1 || d_v > 128 || D > 384) return false;
     const int NC = (T + kBC - 1) / kBC;
-    *ws_bytes = sum_layout(int64_t(BH) * NC, D, d_v).end * 4;
+    int LC;
+    const int NB = sum_blocks(BH, NC, d_v, &LC);
+    *ws_bytes = sum_layout(BH, NC, D, d_v, NB, sum_parts(BH, NB, LC, d_v)).end * 4;
     return true;
 }
 
@@ -343,8 +486,14 @@ static hipError_t launch_scan(const SumArgs& a, hipStream_t stream) {
                          4 * kBC);
     hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(int64_t(a.BH) * cgroups)), dim3(256), lds,
-                       stream, a);
+    if (a.NB > 1) {
+        auto bk = sum_blocksum_kernel<BF16, NDW>;
+        hipLaunchKernelGGL(bk, dim3(static_cast<unsigned>(int64_t(a.BH) * a.NB * a.SP * cgroups)),
+                           dim3(256), 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(int64_t(a.BH) * a.NB * cgroups)), dim3(256),
+                       lds, stream, a);
     return hipGetLastError();
 }
 
@@ -383,7 +532,9 @@ hipError_t launch_sum_forward(const void* q, const void* k, const void* v, const
     a.ws = static_cast<float*>(workspace);
     a.BH = BH; a.T = T; a.NC = (T + kBC - 1) / kBC; a.d_k = d_k; a.d_v = d_v; a.nu = nu;
     a.D = 2 * d_k * nu;
-    a.L = sum_layout(int64_t(BH) * a.NC, a.D, d_v);
+    a.NB = sum_blocks(BH, a.NC, d_v, &a.LC);
+    a.SP = sum_parts(BH, a.NB, a.LC, d_v);
+    a.L = sum_layout(BH, a.NC, a.D, d_v, a.NB, a.SP);
     return bf16 ? launch_sum_t<true>(a, stream) : launch_sum_t<false>(a, stream);
 }
 

@@ -442,9 +442,9 @@ def test_sum_forward_info_and_empty_batch():
     D, d_v, nc = 256, 64, 4096 // 32
     per_chunk = 2 * 32 * D + 32 * d_v + 32 + D
     # 32 heads x 4 column groups = 128 scan workgroups: two blocks per sequence, the first
-    # summed in 512 / 128 = 4 parts, so the workspace adds the W0 copy and four parts' K^T V
-    # sums and key sums
-    blocked = 32 * d_v * D + 4 * 32 * d_v * D + 4 * 32 * D
+    # summed in 2048 / 128 = 16 parts, so the workspace adds the W0 copy and sixteen parts'
+    # K^T V sums and key sums
+    blocked = 32 * d_v * D + 16 * 32 * d_v * D + 16 * 32 * D
     assert fwa.sum_forward_info(4, 8, 4096, 64, d_v, 2, torch.bfloat16) == (4 * 8 * nc * per_chunk + blocked) * 4
     # 64 heads x 4 column groups fill the GPU: one block, no extra regions
     assert fwa.sum_forward_info(8, 8, 4096, 64, d_v, 2, torch.bfloat16) == 8 * 8 * nc * per_chunk * 4

@@ -39,12 +39,15 @@ static int sum_blocks(int BH, int NC, int d_v, int* LC) {
     *LC = NC > 0 ? (NC + nb - 1) / nb : 1;
     return NC > 0 ? (NC + *LC - 1) / *LC : 1;
 }
-// Parts per block for the block sums: about 512 sum workgroups, each over at least one chunk.
+// Parts per block for the block sums: about 2048 sum workgroups (eight per CU, so that their
+// load latency hides behind each other's products), each over at least four chunks (a scan
+// workgroup adds up the parts of every block before its own).
 static int sum_parts(int BH, int NB, int LC, int d_v) {
     if (NB <= 1) return 1;
     const int64_t wgs = int64_t(BH) * (NB - 1) * ((d_v + 15) / 16);
-    const int64_t sp = 512 / wgs;
-    return static_cast<int>(sp < 1 ? 1 : (sp > LC ? LC : sp));
+    int64_t sp = 2048 / wgs;
+    if (sp > LC / 4) sp = LC / 4;
+    return static_cast<int>(sp < 1 ? 1 : sp);
 }
 
 static SumLayout sum_layout(int64_t BH, int NC, int D, int d_v, int NB, int SP) {
@@ -313,9 +316,16 @@ __global__ __launch_bounds__(256) void sum_scan_kernel(SumArgs a) {
         if (a.NB == 1) {
             if (a.W0) W[q] = *reinterpret_cast<const f32x4*>(a.W0 + o);
         } else {
-            W[q] = *reinterpret_cast<const f32x4*>(a.ws + a.L.wc + o);
-            for (int b = 0; b < blk * a.SP; ++b)
-                W[q] += *reinterpret_cast<const f32x4*>(a.ws + a.L.bs + int64_t(b) * a.BH * d_v * D + o);
+            // four independent sums keep four loads in flight
+            const float* src = a.ws + a.L.bs + o;
+            const int64_t stride = int64_t(a.BH) * d_v * D;
+            f32x4 s4[4] = {zero4(), zero4(), zero4(), zero4()};
+            int b = 0;
+            for (; b + 4 <= blk * a.SP; b += 4)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s4[i] += *reinterpret_cast<const f32x4*>(src + (b + i) * stride);
+            for (; b < blk * a.SP; ++b) s4[0] += *reinterpret_cast<const f32x4*>(src + b * stride);
+            W[q] = *reinterpret_cast<const f32x4*>(a.ws + a.L.wc + o) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
         }
     }
     for (int d = tid; d < D; d += 256) {

@@ -892,10 +892,15 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
 // k_j < 0.
 constexpr int kDpfpWaves = 4;
 
+// Each wave owns its slices of xs and dr, so their LDS traffic stays inside the wave, whose
+// LDS operations complete in order: a wave barrier (which only keeps the compiler from moving
+// the reads above the writes) replaces the workgroup barrier.  Every global load of the vector
+// (its D entries of dphi, then x) is issued first.
 template <bool BF16>
 __global__ __launch_bounds__(64 * kDpfpWaves) void bwd_dpfp_kernel(BwdArgs a) {
+    constexpr int KP = 6;                                    // D / 64 <= 6 (D <= 384)
     __shared__ float xs_all[kDpfpWaves][128];
-    __shared__ float dr_all[kDpfpWaves][512];
+    __shared__ float dr_all[kDpfpWaves][64 * KP];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t vec = int64_t(blockIdx.x) * kDpfpWaves + wave;      // (bh, t) flat
     const int64_t nvec = int64_t(a.BH) * a.T;
@@ -909,19 +914,29 @@ __global__ __launch_bounds__(64 * kDpfpWaves) void bwd_dpfp_kernel(BwdArgs a) {
     const int64_t bh = live ? vec / a.T : 0, t = live ? vec % a.T : 0;
     const float* dphi = a.ws + (isq ? a.L.qp : a.L.wy) +
                         ((bh * a.NC + t / kBC) * kBC + t % kBC) * int64_t(D);
-    for (int m = lane; m < two; m += 64) {
-        const float kv = live ? load_elem<BF16>(x, vec * d_k + (m % d_k)) : 0.0f;
-        xs[m] = m < d_k ? relu(kv) : relu(-kv);
+    float dph[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int p = lane + 64 * k;
+        dph[k] = (live && p < D) ? dphi[p] : 0.0f;
     }
-    __syncthreads();
+    // lane < 2 d_k holds relu'd entry m = lane (d_k = 16, 32) or entries lane and lane + 64
+    // (d_k = 64); kv0 = x[lane % d_k]
+    const float kv0 = (live && lane < two) ? load_elem<BF16>(x, vec * d_k + (lane % d_k)) : 0.0f;
+    if (lane < two) xs[lane] = lane < d_k ? relu(kv0) : relu(-kv0);
+    if (two > 64) xs[lane + 64] = relu(-kv0);
+    __builtin_amdgcn_wave_barrier();
     float S = 0.0f, dot = 0.0f;
-    for (int p = lane; p < D; p += 64) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int p = lane + 64 * k;
+        if (p >= D) break;
         const int i = p / two + 1, j = p % two;
         int src = j - i;
         src += src < 0 ? two : 0;
         const float raw = xs[j] * xs[src];
         S += raw;
-        dot += live ? dphi[p] * raw : 0.0f;
+        dot += dph[k] * raw;
     }
 #pragma unroll
     for (int mask = 32; mask >= 1; mask >>= 1) {
@@ -930,8 +945,12 @@ __global__ __launch_bounds__(64 * kDpfpWaves) void bwd_dpfp_kernel(BwdArgs a) {
     }
     const float den = S + kDpfpEps;
     const float dphin = dot / den;                          // dphi . phi
-    for (int p = lane; p < D; p += 64) dr[p] = live ? (dphi[p] - dphin) / den : 0.0f;
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int p = lane + 64 * k;
+        if (p < D) dr[p] = (dph[k] - dphin) / den;
+    }
+    __builtin_amdgcn_wave_barrier();
     if (live && lane < d_k) {
         float dxv[2];
 #pragma unroll
@@ -948,8 +967,7 @@ __global__ __launch_bounds__(64 * kDpfpWaves) void bwd_dpfp_kernel(BwdArgs a) {
             }
             dxv[h] = s;
         }
-        const float kv = load_elem<BF16>(x, vec * d_k + lane);
-        const float gk = (kv > 0.0f ? dxv[0] : 0.0f) - (kv < 0.0f ? dxv[1] : 0.0f);
+        const float gk = (kv0 > 0.0f ? dxv[0] : 0.0f) - (kv0 < 0.0f ? dxv[1] : 0.0f);
         store_elem<BF16>(dx_out, vec * d_k + lane, gk);
     }
 }

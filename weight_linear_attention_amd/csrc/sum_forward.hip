@@ -82,9 +82,14 @@ struct SumArgs {
     SumLayout L;
 };
 
-// LDS: x rows of k and q (C x 2 d_k each), K and Q (C x SD, SD = D + 8), M (C x (C + 1)), V.
+// LDS: x rows of k and q (C x 2 d_k each), one shift slice of K and of Q (C x (2 d_k + 4)),
+// M (C x (C + 4)), V: 78 KB at d_k = 64 and d_v = 64, so two workgroups share a CU.
+// The row sums of the raw features come first (a pass of products without stores); then, one
+// shift i at a time, the slice's normalised features (columns (i - 1) 2 d_k .. + 2 d_k - 1)
+// go to LDS, to the workspace (16-byte stores) and into M = lower_incl(Q K^T) (fp32 MFMA
+// accumulators of waves 0-2) and the key sums (wave 3).
 template <bool BF16>
-__global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
+__global__ __launch_bounds__(kSumThreads, 2) void sum_prep_kernel(SumArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_k = a.d_k, d_v = a.d_v, two = 2 * d_k;
     const int u = blockIdx.x;
@@ -94,40 +99,77 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     const int rows = a.T - t0 < kBC ? a.T - t0 : kBC;
     const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     constexpr int CS = kBC + 4;       // 16-byte rows for the MFMA operand reads
-    const int SD = tile_stride(D);
+    const int SS = two + 4;           // slice row stride
     float* xk = lds;
     float* xq = xk + kBC * two;
-    float* Kt = xq + kBC * two;
-    float* Qt = Kt + kBC * SD;
-    float* Mm = Qt + kBC * SD;
+    float* Ks = xq + kBC * two;
+    float* Qs = Ks + kBC * SS;
+    float* Mm = Qs + kBC * SS;
     float* Vs = Mm + kBC * CS;
     load_chunk_inputs<BF16, kSumThreads, 128>(a.k, a.q, a.v, xk, xq, Vs, int64_t(bh) * a.T, rows,
                                               t0, d_k, d_v, tid);
-    dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
+    __syncthreads();
+    // row sums: row c = tid / 8, entries p = tid % 8 + 8 m of every shift (the eight threads of
+    // a row are adjacent lanes)
+    const int c = tid >> 3, s0 = tid & 7;
+    const float* xrk = xk + c * two;
+    const float* xrq = xq + c * two;
+    float sk = 0.0f, sq = 0.0f;
+    for (int i = 1; i <= a.nu; ++i)
+        for (int jj = s0; jj < two; jj += 8) {
+            int src = jj - i;
+            src += (src < 0) ? two : 0;
+            sk += xrk[jj] * xrk[src];
+            sq += xrq[jj] * xrq[src];
+        }
+    sk = sum8_dpp(sk);
+    sq = sum8_dpp(sq);
+    const float ik = 1.0f / (sk + kDpfpEps), iq = 1.0f / (sq + kDpfpEps);
     const int64_t CD = int64_t(kBC) * D;
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
-    for (int c = wv; c < kBC; c += kSumThreads / 64)
-        for (int p = lane; p < D; p += 64) {
-            gK[c * D + p] = Kt[c * SD + p];
-            gQ[c * D + p] = Qt[c * SD + p];
+    float* gks = a.ws + a.L.ks + int64_t(u) * D;
+    // waves 0-2: tiles (0,0), (1,0), (1,1) of M
+    const int it = wv == 0 ? 0 : 1, jt = wv == 2 ? 1 : 0;
+    f32x4 acc = zero4();
+    for (int i = 1; i <= a.nu; ++i) {
+        for (int jj = s0; jj < two; jj += 8) {
+            int src = jj - i;
+            src += (src < 0) ? two : 0;
+            Ks[c * SS + jj] = xrk[jj] * xrk[src] * ik;
+            Qs[c * SS + jj] = xrq[jj] * xrq[src] * iq;
         }
-    // M = lower_incl(Q K^T) on the fp32 MFMA: wave w < 3 takes tile (0,0), (1,0), (1,1); wave 3
-    // zeroes tile (0, 1).  Lane group g supplies k = 4 g + s to sub-step s of a 16-deep block.
-    if (wv < 3) {
-        const int it = wv == 0 ? 0 : 1, jt = wv == 2 ? 1 : 0;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < D; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(Qt + (16 * it + l16) * SD + kb + 4 * g4);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(Kt + (16 * jt + l16) * SD + kb + 4 * g4);
+        __syncthreads();
+        // the slice to the workspace: 16-byte units e = (row, 4 columns)
+        const int col0 = (i - 1) * two, q4 = two / 4;
+        for (int e = tid; e < kBC * q4; e += kSumThreads) {
+            const int r = e / q4, cc = 4 * (e - r * q4);
+            *reinterpret_cast<f32x4*>(gK + r * D + col0 + cc) = *reinterpret_cast<const f32x4*>(Ks + r * SS + cc);
+            *reinterpret_cast<f32x4*>(gQ + r * D + col0 + cc) = *reinterpret_cast<const f32x4*>(Qs + r * SS + cc);
+        }
+        if (wv < 3) {
+            for (int kb = 0; kb < two; kb += 16) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(Qs + (16 * it + l16) * SS + kb + 4 * g4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(Ks + (16 * jt + l16) * SS + kb + 4 * g4);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+                for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+            }
+        } else {
+            for (int f = lane; f < two; f += 64) {
+                float ssum = 0.0f;
+#pragma unroll 8
+                for (int r = 0; r < kBC; ++r) ssum += Ks[r * SS + f];
+                gks[col0 + f] = ssum;
+            }
         }
-        const int col = 16 * jt + l16;
+        __syncthreads();                                 // the slice is dead
+    }
+    if (wv < 3) {
+        const int colm = 16 * jt + l16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * it + 4 * g4 + e;
-            Mm[row * CS + col] = col <= row ? acc[e] : 0.0f;
+            Mm[row * CS + colm] = colm <= row ? acc[e] : 0.0f;
         }
     } else {
         for (int e = lane; e < 256; e += 64) Mm[(e >> 4) * CS + 16 + (e & 15)] = 0.0f;
@@ -136,30 +178,25 @@ __global__ __launch_bounds__(kSumThreads) void sum_prep_kernel(SumArgs a) {
     // M V ([c][r]) on the fp32 MFMA: tiles (it, rt), wave w takes w + 4 q
     float* gN = a.ws + a.L.nm + int64_t(u) * kBC * d_v;
     for (int tau = wv; tau < 2 * ((d_v + 15) / 16); tau += 4) {
-        const int it = tau & 1, rt = tau >> 1;
+        const int it2 = tau & 1, rt = tau >> 1;
         const int r = 16 * rt + l16;
-        f32x4 acc = zero4();
+        f32x4 acc2 = zero4();
 #pragma unroll
         for (int kb = 0; kb < kBC; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(Mm + (16 * it + l16) * CS + kb + 4 * g4);
+            const f32x4 av = *reinterpret_cast<const f32x4*>(Mm + (16 * it2 + l16) * CS + kb + 4 * g4);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                acc = mfma_f32_k4(av[s], r < d_v ? Vs[(kb + 4 * g4 + s) * d_v + r] : 0.0f, acc);
+                acc2 = mfma_f32_k4(av[s], r < d_v ? Vs[(kb + 4 * g4 + s) * d_v + r] : 0.0f, acc2);
         }
         if (r < d_v) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gN[(16 * it + 4 * g4 + e) * d_v + r] = acc[e];
+            for (int e = 0; e < 4; ++e) gN[(16 * it2 + 4 * g4 + e) * d_v + r] = acc2[e];
         }
     }
     if (tid < kBC) {
-        float s = 0.0f;
-        for (int j = 0; j <= tid; ++j) s += Mm[tid * CS + j];
-        a.ws[a.L.dn + int64_t(u) * kBC + tid] = s;
-    }
-    for (int p = tid; p < D; p += kSumThreads) {
-        float s = 0.0f;
-        for (int c = 0; c < kBC; ++c) s += Kt[c * SD + p];
-        a.ws[a.L.ks + int64_t(u) * D + p] = s;
+        float sm = 0.0f;
+        for (int j2 = 0; j2 <= tid; ++j2) sm += Mm[tid * CS + j2];
+        a.ws[a.L.dn + int64_t(u) * kBC + tid] = sm;
     }
 }
 
@@ -512,7 +549,7 @@ static hipError_t launch_sum_t(const SumArgs& a, hipStream_t stream) {
     const int64_t NU = int64_t(a.BH) * a.NC;
     hipError_t e;
     if (NU > 0) {
-        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * tile_stride(a.D) + kBC * (kBC + 4) +
+        const int lp = 4 * (2 * kBC * 2 * a.d_k + 2 * kBC * (2 * a.d_k + 4) + kBC * (kBC + 4) +
                             kBC * a.d_v);
         auto kp = sum_prep_kernel<BF16>;
         if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kp), lp)) != hipSuccess) return e;

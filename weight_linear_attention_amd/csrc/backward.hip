@@ -80,13 +80,31 @@ struct BwdArgs {
 
 // ------------------------------------------------------------------------------ 1. prep
 
-// LDS: x rows of k and q (relu([., -.]), C x 2 d_k each; T = Ainv diag(beta) over them once
-// they are dead), K and Q (C x SD, SD = D + 8; W_y over K once it is dead), G, P, Ainv
-// (C x kCS), beta, V (C x d_v).  The products G = K K^T, P = Q K^T, W_y = T K, P W_y and
-// U_y = T V run on the fp32 MFMA (16x16x4; lane group g supplies k = 4 g + s to sub-step s
-// for both operands: A as one 16-byte read of a row, B as four reads down a column).
+// Floats of the prep's two LDS regions (see below).
+__host__ __device__ inline int bwd_prep_region_a(int d_k) {
+    const int x = 2 * kBC * 2 * d_k, t = 2 * (2 * d_k) * kCS;
+    return x > t ? x : t;
+}
+__host__ __device__ inline int bwd_prep_region_b(int d_k) {
+    const int sl = 2 * kBC * (2 * d_k + 4), m = 4 * kBC * kCS;
+    return sl > m ? sl : m;
+}
+
+// LDS (77 KB at d_k = 64, d_v = 64: two workgroups per CU):
+//   region A: the relu'd raw rows of k and q (C x 2 d_k each) in the first pass; in the second
+//             one shift slice of K^T and of Q^T read back ([2 d_k][kCS] each), W_y^T of the
+//             slice over K^T once it is read;
+//   region B: one shift slice of K and of Q (C x (2 d_k + 4)) in the first pass; then G, P,
+//             Ainv and T = Ainv diag(beta) (C x kCS each);
+//   beta (C), V (C x d_v).
+// The row sums of the raw features come first (the order dpfp_tiles uses).  First pass, one
+// shift i at a time: the slice's normalised features (columns (i - 1) 2 d_k .. + 2 d_k - 1) go
+// to the workspace transposed and into the G = K K^T and P = lower_incl(Q K^T) accumulators.
+// Then Ainv and T.  Second pass, per slice: K^T and Q^T back from the workspace (written by this
+// workgroup, visible after the workgroup barrier), W_y = T K and Q' = Q - P W_y.  Every product
+// runs on the fp32 MFMA (16x16x4; lane group g supplies k = 4 g + s to sub-step s).
 template <bool BF16>
-__global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kPrepThreads2, 2) void bwd_prep_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_k = a.d_k, d_v = a.d_v, two = 2 * d_k;
     const int u = blockIdx.x;
@@ -95,16 +113,19 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     constexpr int CS = kCS;
-    const int SD = tile_stride(D);
+    const int SS = two + 4;
+    const int regA = bwd_prep_region_a(d_k), regB = bwd_prep_region_b(d_k);
     float* xk = lds;                         // [C][2 d_k]
     float* xq = xk + kBC * two;
-    float* Ts = xk;                          // [C][CS] T = Ainv diag(beta), after DPFP
-    float* Kt = xq + kBC * two;              // [C][SD]; W_y once K is dead
-    float* Qt = Kt + kBC * SD;
-    float* Gm = Qt + kBC * SD;               // [C][CS]
+    float* KT = lds;                         // [2 d_k][CS] (second pass)
+    float* QT = KT + two * CS;
+    float* Ks = lds + regA;                  // [C][SS] (first pass)
+    float* Qs = Ks + kBC * SS;
+    float* Gm = lds + regA;                  // [C][CS] each
     float* Pm = Gm + kBC * CS;
     float* Ai = Pm + kBC * CS;
-    float* be = Ai + kBC * CS;               // [C]
+    float* Ts = Ai + kBC * CS;
+    float* be = lds + regA + regB;           // [C]
     float* Vs = be + kBC;                    // [C][d_v]
 
     // relu'd raw rows (zero past the sequence end), beta (zero past the end), v
@@ -113,42 +134,78 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
     load_chunk_inputs<BF16, kPrepThreads2, 64>(a.k, a.q, a.v, xk, xq, Vs, int64_t(bh) * a.T, rows,
                                                t0, d_k, d_v, tid);
     if (tid < kBC) be[tid] = tid < rows ? sigmoid_stable(blv) : 0.0f;
-    dpfp_tiles(xk, xq, Kt, Qt, D, d_k, tid);
+    __syncthreads();
+    // row sums: row c = tid / 8 by its eight adjacent threads, entries p = tid % 8 + 8 m
+    const int c = tid >> 3, s0 = tid & 7;
+    const float* xrk = xk + c * two;
+    const float* xrq = xq + c * two;
+    float sk = 0.0f, sq = 0.0f;
+    for (int i = 1; i <= a.nu; ++i)
+        for (int jj = s0; jj < two; jj += 8) {
+            int src = jj - i;
+            src += (src < 0) ? two : 0;
+            sk += xrk[jj] * xrk[src];
+            sq += xrq[jj] * xrq[src];
+        }
+    sk = sum8_dpp(sk);
+    sq = sum8_dpp(sq);
+    const float ik = 1.0f / (sk + kDpfpEps), iq = 1.0f / (sq + kDpfpEps);
     const int64_t CD = int64_t(kBC) * D;
-    // K and Q leave transposed ([D][C]): unit e = 4 consecutive rows c of column d = e / 8
     float* gK = a.ws + a.L.kt + int64_t(u) * CD;
     float* gQ = a.ws + a.L.qt + int64_t(u) * CD;
-    for (int e = tid; e < 8 * D; e += kPrepThreads2) {
-        const int d = e >> 3, c0 = 4 * (e & 7);
-        f32x4 kv, qv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kv[j] = Kt[(c0 + j) * SD + d];
-            qv[j] = Qt[(c0 + j) * SD + d];
+    // G (all four tiles) and P (tiles (0,0), (1,0), (1,1)): wave w takes tiles w and w + 4
+    f32x4 gacc[2] = {zero4(), zero4()};
+    for (int i = 1; i <= a.nu; ++i) {
+        const int col0 = (i - 1) * two;
+        for (int jj = s0; jj < two; jj += 8) {
+            int src = jj - i;
+            src += (src < 0) ? two : 0;
+            Ks[c * SS + jj] = xrk[jj] * xrk[src] * ik;
+            Qs[c * SS + jj] = xrq[jj] * xrq[src] * iq;
         }
-        *reinterpret_cast<f32x4*>(gK + 4 * e) = kv;
-        *reinterpret_cast<f32x4*>(gQ + 4 * e) = qv;
+        __syncthreads();
+        // K and Q leave transposed ([D][C]): unit e = 4 consecutive rows of column col0 + e / 8
+        for (int e = tid; e < 8 * two; e += kPrepThreads2) {
+            const int f = e >> 3, c0 = 4 * (e & 7);
+            f32x4 kv, qv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kv[j] = Ks[(c0 + j) * SS + f];
+                qv[j] = Qs[(c0 + j) * SS + f];
+            }
+            *reinterpret_cast<f32x4*>(gK + (col0 + f) * kBC + c0) = kv;
+            *reinterpret_cast<f32x4*>(gQ + (col0 + f) * kBC + c0) = qv;
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int tau = wv + 4 * q;
+            if (tau >= 7) continue;
+            const bool isP = tau >= 4;
+            const int it = isP ? (tau == 4 ? 0 : 1) : tau >> 1;
+            const int jt = isP ? (tau == 6 ? 1 : 0) : tau & 1;
+            const float* X = isP ? Qs : Ks;
+            for (int kb = 0; kb < two; kb += 16) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(X + (16 * it + l16) * SS + kb + 4 * g4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(Ks + (16 * jt + l16) * SS + kb + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) gacc[q] = mfma_f32_k4(av[s], bv[s], gacc[q]);
+            }
+        }
+        __syncthreads();                                         // the slice is dead
     }
-    // G = K K^T (all four tiles) and P = lower_incl(Q K^T) (tiles (0,0), (1,0), (1,1));
-    // wave w takes tiles w and w + 4 of that list
-    for (int tau = wv; tau < 7; tau += 4) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int tau = wv + 4 * q;
+        if (tau >= 7) continue;
         const bool isP = tau >= 4;
         const int it = isP ? (tau == 4 ? 0 : 1) : tau >> 1;
         const int jt = isP ? (tau == 6 ? 1 : 0) : tau & 1;
-        const float* X = isP ? Qt : Kt;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < D; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(X + (16 * it + l16) * SD + kb + 4 * g4);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(Kt + (16 * jt + l16) * SD + kb + 4 * g4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
-        }
         const int col = 16 * jt + l16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * it + 4 * g4 + e;
-            if (isP) Pm[row * CS + col] = col <= row ? acc[e] : 0.0f;
-            else Gm[row * CS + col] = acc[e];
+            if (isP) Pm[row * CS + col] = col <= row ? gacc[q][e] : 0.0f;
+            else Gm[row * CS + col] = gacc[q][e];
         }
     }
     for (int e = tid; e < 16 * 16; e += kPrepThreads2)         // P tile (0, 1): above the diagonal
@@ -180,54 +237,58 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_prep_kernel(BwdArgs a) {
         const int i = e >> 5, j = e & (kBC - 1);
         Ts[i * CS + j] = Ai[i * CS + j] * be[j];
     }
-    __syncthreads();
-    // W_y = T K: tiles (it, pt) w + 4 q, accumulators kept until every wave has read K
-    const int NPT = D / 16;
-    constexpr int kMaxWy = 384 / 16 * 2 / 4;                     // tiles per wave at D <= 384
-    f32x4 wy[kMaxWy];
+    // second pass: W_y = T K and Q' = Q - P W_y per slice; tiles (it, pt) w + 4 q of the slice
     float* gWy = a.ws + a.L.wy + int64_t(u) * CD;
-#pragma unroll
-    for (int q = 0; q < kMaxWy; ++q) {
-        const int tau = wv + 4 * q;
-        wy[q] = zero4();
-        if (tau >= 2 * NPT) continue;
-        const int it = tau & 1, pt = tau >> 1;
-#pragma unroll
-        for (int kb = 0; kb < kBC; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + (16 * it + l16) * CS + kb + 4 * g4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                wy[q] = mfma_f32_k4(av[s], Kt[(kb + 4 * g4 + s) * SD + 16 * pt + l16], wy[q]);
-        }
-        *reinterpret_cast<f32x4*>(gWy + (16 * pt + l16) * kBC + 16 * it + 4 * g4) = wy[q];   // [D][C]
-    }
-    __syncthreads();                                             // K is dead: W_y over it
-#pragma unroll
-    for (int q = 0; q < kMaxWy; ++q) {
-        const int tau = wv + 4 * q;
-        if (tau >= 2 * NPT) continue;
-        const int it = tau & 1, pt = tau >> 1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Kt[(16 * it + 4 * g4 + e) * SD + 16 * pt + l16] = wy[q][e];
-    }
-    __syncthreads();
-    // Q' = Q - P W_y
     float* gQp = a.ws + a.L.qp + int64_t(u) * CD;
-    for (int tau = wv; tau < 2 * NPT; tau += 4) {
-        const int it = tau & 1, pt = tau >> 1;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < kBC; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(Pm + (16 * it + l16) * CS + kb + 4 * g4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                acc = mfma_f32_k4(av[s], Kt[(kb + 4 * g4 + s) * SD + 16 * pt + l16], acc);
+    const int NPT = two / 16;
+    constexpr int kMaxWy = 128 / 16 * 2 / 4;                     // tiles per wave, 2 d_k <= 128
+    for (int i = 1; i <= a.nu; ++i) {
+        const int col0 = (i - 1) * two;
+        __syncthreads();                                         // T written; last slice dead
+        for (int e = tid; e < 8 * two; e += kPrepThreads2) {
+            const int f = e >> 3, c0 = 4 * (e & 7);
+            *reinterpret_cast<f32x4*>(KT + f * CS + c0) = *reinterpret_cast<const f32x4*>(gK + (col0 + f) * kBC + c0);
+            *reinterpret_cast<f32x4*>(QT + f * CS + c0) = *reinterpret_cast<const f32x4*>(gQ + (col0 + f) * kBC + c0);
         }
-        const int col = 16 * pt + l16;
-        f32x4 qp;
+        __syncthreads();
+        f32x4 wy[kMaxWy];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qp[e] = Qt[(16 * it + 4 * g4 + e) * SD + col] - acc[e];
-        *reinterpret_cast<f32x4*>(gQp + col * kBC + 16 * it + 4 * g4) = qp;      // [D][C]
+        for (int q = 0; q < kMaxWy; ++q) {
+            const int tau = wv + 4 * q;
+            wy[q] = zero4();
+            if (tau >= 2 * NPT) continue;
+            const int it = tau & 1, pt = tau >> 1;
+#pragma unroll
+            for (int kb = 0; kb < kBC; kb += 16) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(Ts + (16 * it + l16) * CS + kb + 4 * g4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(KT + (16 * pt + l16) * CS + kb + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) wy[q] = mfma_f32_k4(av[s], bv[s], wy[q]);
+            }
+            *reinterpret_cast<f32x4*>(gWy + (col0 + 16 * pt + l16) * kBC + 16 * it + 4 * g4) = wy[q];   // [D][C]
+        }
+        __syncthreads();                                         // K^T is dead: W_y^T over it
+#pragma unroll
+        for (int q = 0; q < kMaxWy; ++q) {
+            const int tau = wv + 4 * q;
+            if (tau >= 2 * NPT) continue;
+            const int it = tau & 1, pt = tau >> 1;
+            *reinterpret_cast<f32x4*>(KT + (16 * pt + l16) * CS + 16 * it + 4 * g4) = wy[q];
+        }
+        __syncthreads();
+        for (int tau = wv; tau < 2 * NPT; tau += 4) {
+            const int it = tau & 1, pt = tau >> 1;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < kBC; kb += 16) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(Pm + (16 * it + l16) * CS + kb + 4 * g4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(KT + (16 * pt + l16) * CS + kb + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+            }
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(QT + (16 * pt + l16) * CS + 16 * it + 4 * g4);
+            *reinterpret_cast<f32x4*>(gQp + (col0 + 16 * pt + l16) * kBC + 16 * it + 4 * g4) = qv - acc;   // [D][C]
+        }
     }
     // Uy = T V ([c][r])
     float* gUy = a.ws + a.L.uy + int64_t(u) * kBC * d_v;
@@ -986,8 +1047,8 @@ bool plan_backward(int BH, int T, int d_k, int d_v, int nu, int64_t* ws_bytes) {
 }
 
 static int lds_prep_bytes(int D, int d_k, int d_v) {
-    return 4 * (2 * kBC * 2 * d_k + 2 * kBC * tile_stride(D) + 3 * kBC * kCS + kBC +
-                kBC * d_v);
+    (void)D;
+    return 4 * (bwd_prep_region_a(d_k) + bwd_prep_region_b(d_k) + kBC + kBC * d_v);
 }
 static int lds_grads_bytes(int d_v) {
     const int SV = grads_dvp(d_v), DV16 = grads_dv16(d_v);

@@ -290,17 +290,21 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
 //     row tile swap the halves they do not own through LDS.
 //   * K is double-buffered: the K tile of chunk n + 1 is built in phase C of chunk n, where the
 //     SIMDs otherwise wait on the short U products and the barrier, instead of in a phase of
-//     its own.  (Built in phase B, between the X and Q W^T products, it measured slower: the
-//     compiler does not interleave it, and split by shift it costs registers.)  The prep results of chunk n + 1 are loaded as soon as chunk n's are dead (after
-//     the memory update), a whole chunk ahead of their use.
+//     its own.  (Built in phase B, between the X and Q W^T products, or in phase D beside the
+//     memory update, it measured slower.)  Its 8 preceding positions per task come from the
+//     neighbouring lane by DPP.  The prep results of chunk n + 1 are loaded as soon as chunk
+//     n's are dead (after the memory update), a whole chunk ahead of their use.
 //   * The W^T copy is written in the canonical B-operand layout (lane L, slot s = k-row
 //     8 (L / 16) + s of the block, column L % 16), so the K operand of X = K W^T is one 16-byte
 //     LDS read per k-step, and the register-built Q operand uses the same k order.
+//   * U and rho_k o U are stored once, by the wave that forms the U tile, as the packed bf16 B
+//     blocks that Y and the memory update read (one 16-byte read per block and k-step).
 // Wave w owns row tile rt = w % 4 and column tile / Q half h = w / 4.  Per chunk:
 //   B  X = K W^T for tile (rt, h) over all of D; partial Q W^T over k-steps 4 p + 2 h + e
 //      (both column tiles); Z = V - rho_k o X to LDS, the partner's partial to LDS.
-//   C  U tile (rt, h) = A'' Z; Q W^T tile (rt, h) = own + partner partial, times rho_q; the
-//      next chunk's K tile (one DPFP task per thread) and v columns.
+//   C  U tile (rt, h) = A'' Z, stored as U and rho_k o U blocks; Q W^T tile (rt, h) = own +
+//      partner partial, times rho_q; the next chunk's K tile (one DPFP task per thread) and
+//      v columns.
 //   D  Y tile (rt, h) = rho_q o Q W^T + P~ U; the memory tiles += K^T (rho_k o U); the W^T
 //      copy.
 // Three LDS-only barriers per chunk.  Global loads are issued by every lane in every chunk with

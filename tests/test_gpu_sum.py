@@ -39,6 +39,9 @@ SUM_CASES = [
     ("b4_h8_t4096_d64_nu2_bf16_carried", {}, True),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 999, "nu": 3, "w0_std": None}, False),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 2, "H": 3, "T": 45, "d_k": 32, "nu": 5, "d_v": 8}, True),
+    # 16 heads x 4 column groups: 4 blocks of 24 chunks, the first three summed in 6 parts of 4,
+    # the last block 22 chunks
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 2, "T": 3000}, True),
 ]
 
 

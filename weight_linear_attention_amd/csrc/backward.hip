@@ -602,23 +602,26 @@ __global__ __launch_bounds__(kStThreads) void bwd_states_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------ 4. chunk grads
 
 constexpr int kSlice = 64;   // columns of D per pass in bwd_chunk_grads
+constexpr int kGradThreads = 512;                 // bwd_chunk_grads: 8 waves
+constexpr int kGradWaves = kGradThreads / 64;
 
 // Padded d_v: the d_v contraction runs in 16-deep blocks; the row stride adds 4 floats.
 __host__ __device__ inline int grads_dv16(int d_v) { return (d_v + 15) & ~15; }
 __host__ __device__ inline int grads_dvp(int d_v) { return grads_dv16(d_v) + 4; }
 
-// One chunk per workgroup of 4 waves, every contraction on the fp32 MFMA (16x16x4; a 16-deep k
+// One chunk per workgroup of 8 waves (two per SIMD, so one wave's MFMA chain overlaps the other's
+// LDS reads), every contraction on the fp32 MFMA (16x16x4; a 16-deep k
 // block feeds four products, lane group g supplying k = 4 g + s to sub-step s for both operands,
 // so each lane reads its A and B values as one 16-byte LDS read each: A operands row-major
 // [row][k], B operands transposed [column][k]):
 //   dU = P^T dY + (K dW1^T, from the row pass)      lam = Ainv^T dU      dv = diag(beta) lam
 //   dP = lower_incl(dY U^T)      Z = lam U^T      dG_ij = -beta_i Z_ij (j < i), symmetrised
-// then, per 64-column slice of D (wave w: column tile w, both row tiles),
+// then, per 64-column slice of D (wave w: column tile w % 4, row tile w / 4),
 //   dQ = dY W0 + dP K,   M = lam W0,   dK = U dW1 + dP^T Q + (dG + dG^T) K - diag(beta) M.
 // The chunk's operands are loaded into registers in one batch before any LDS store; the next
 // slice's W0, dW1, K and Q load into registers while the current slice computes.
 template <bool BF16>
-__global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kGradThreads) void bwd_chunk_grads_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_v = a.d_v;
     const int u = blockIdx.x;
@@ -645,25 +648,25 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     float* dG = dPT + kBC * CS;       // dG + dG^T
     float* be = dG + kBC * CS;        // [C]
     float* bpart = be + kBC;          // [C]: lam_i.V_i - sum_{j<i} G_ij Z_ij
-    float* mkb = bpart + kBC;         // [4][C]: per-wave partial sums of M_i . K_i
+    float* mkb = bpart + kBC;         // [4][C]: partial sums of M_i . K_i per column tile
     float* W0T = mkb + 4 * kBC;       // [kSlice][SV]: W0 slice transposed
     float* G1T = W0T + kSlice * SV;   // dW1 slice transposed
     float* KT = G1T + kSlice * SV;    // [kSlice][CS]: K slice transposed
     float* QT = KT + kSlice * CS;
 
     const int64_t u64 = u;
-    // ---- the chunk's operands, all loads first.  dy, v: (row c = tid / 64 + 4 m, entry r =
-    //      tid % 64); U, K dW1^T: workspace [r][c] units tid + 256 m; Ainv, P, G: [i][j] units
-    //      tid + 256 m
+    // ---- the chunk's operands, all loads first.  dy, v: (row c = tid / 64 + 8 m, entry r =
+    //      tid % 64); U, K dW1^T: workspace [r][c] units tid + 512 m; Ainv, P, G: [i][j] units
+    //      tid + 512 m
     {
-        constexpr int MR = kBC / (kPrepThreads2 / 64);           // 8 rows per thread
-        constexpr int MU = kBC * 64 / kPrepThreads2;              // 8 units (d_v <= 64)
-        constexpr int MC = kBC * kBC / kPrepThreads2;             // 4 units
+        constexpr int MR = kBC / (kGradThreads / 64);           // 4 rows per thread
+        constexpr int MU = kBC * 64 / kGradThreads;              // 4 units (d_v <= 64)
+        constexpr int MC = kBC * kBC / kGradThreads;             // 2 units
         const int r = tid & 63;
         float fy[MR], fv[MR], fu[MU], fa[MU], fi[MC], fp[MC], fg[MC];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-            const int c = (tid >> 6) + 4 * m;
+            const int c = (tid >> 6) + kGradWaves * m;
             const bool in = t0 + c < a.T && r < d_v;
             const int64_t g = (int64_t(bh) * a.T + t0 + (in ? c : 0)) * d_v + (in ? r : 0);
             fy[m] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
@@ -671,25 +674,25 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int m = 0; m < MU; ++m) {
-            const int e = tid + kPrepThreads2 * m;
+            const int e = tid + kGradThreads * m;
             const bool in = e < kBC * d_v;
             fu[m] = in ? a.ws[a.L.uu + u64 * kBC * d_v + e] : 0.0f;
             fa[m] = in ? a.ws[a.L.aa + u64 * kBC * d_v + e] : 0.0f;
         }
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
-            const int e = tid + kPrepThreads2 * m;
+            const int e = tid + kGradThreads * m;
             fi[m] = a.ws[a.L.ai + u64 * kBC * kBC + e];
             fp[m] = a.ws[a.L.pm + u64 * kBC * kBC + e];
             fg[m] = a.ws[a.L.gm + u64 * kBC * kBC + e];
         }
         const float fb = tid < kBC ? a.ws[a.L.be + u64 * kBC + tid] : 0.0f;
         // zero padding: rows past d_v of the transposed tiles, entries past d_v of the row tiles
-        for (int e = tid; e < (DV16 - d_v) * CS; e += kPrepThreads2) {
+        for (int e = tid; e < (DV16 - d_v) * CS; e += kGradThreads) {
             dYT[d_v * CS + e] = 0.0f;
             dUT[d_v * CS + e] = 0.0f;
         }
-        for (int e = tid; e < kBC * (SV - d_v); e += kPrepThreads2) {
+        for (int e = tid; e < kBC * (SV - d_v); e += kGradThreads) {
             const int c = e / (SV - d_v), rr = d_v + e % (SV - d_v);
             dYs[c * SV + rr] = 0.0f;
             Us[c * SV + rr] = 0.0f;
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-            const int c = (tid >> 6) + 4 * m;
+            const int c = (tid >> 6) + kGradWaves * m;
             if (r < d_v) {
                 dYs[c * SV + r] = fy[m];
                 dYT[r * CS + c] = fy[m];
@@ -707,7 +710,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int m = 0; m < MU; ++m) {
-            const int e = tid + kPrepThreads2 * m, rr = e >> 5, c = e & (kBC - 1);
+            const int e = tid + kGradThreads * m, rr = e >> 5, c = e & (kBC - 1);
             if (e < kBC * d_v) {
                 Us[c * SV + rr] = fu[m];
                 dUT[rr * CS + c] = fa[m];                  // K dW1^T, P^T dY added below
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
-            const int e = tid + kPrepThreads2 * m, i = e >> 5, j = e & (kBC - 1);
+            const int e = tid + kGradThreads * m, i = e >> 5, j = e & (kBC - 1);
             AiT[j * CS + i] = fi[m];
             PmT[j * CS + i] = fp[m];
             Gm[i * CS + j] = fg[m];
@@ -724,7 +727,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     }
     __syncthreads();
     // ---- dU = P^T dY + K dW1^T (tiles (it, rt) of dU, stored transposed)
-    for (int tau = wv; tau < 2 * NR; tau += 4) {
+    for (int tau = wv; tau < 2 * NR; tau += kGradWaves) {
         const int it = tau & 1, rt = tau >> 1;
         float* out = dUT + (16 * rt + l16) * CS + 16 * it + 4 * g4;
         f32x4 acc = *reinterpret_cast<const f32x4*>(out);
@@ -739,7 +742,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     }
     __syncthreads();
     // ---- lam = Ainv^T dU; dv = diag(beta) lam
-    for (int tau = wv; tau < 2 * NR; tau += 4) {
+    for (int tau = wv; tau < 2 * NR; tau += kGradWaves) {
         const int it = tau & 1, rt = tau >> 1;
         f32x4 acc = zero4();
 #pragma unroll
@@ -759,48 +762,51 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
     }
     __syncthreads();
-    // ---- dP = lower_incl(dY U^T) (and its transpose), Z = lam U^T, dG: wave w -> tile
-    //      (w % 2, w / 2) of both
+    // ---- dP = lower_incl(dY U^T) (and its transpose) on waves 0 .. 3, Z = lam U^T and dG on
+    //      waves 4 .. 7: wave w -> tile (w % 2, (w / 2) % 2)
     {
-        const int it = wv & 1, jt = wv >> 1;
-        f32x4 sp = zero4(), sz = zero4();
+        const bool zw = wv >= 4;
+        const int it = wv & 1, jt = (wv >> 1) & 1;
+        const float* A = zw ? Ls : dYs;
+        f32x4 acc = zero4();
         for (int kb = 0; kb < DV16; kb += 16) {
             const f32x4 bu = *reinterpret_cast<const f32x4*>(Us + (16 * jt + l16) * SV + kb + 4 * g4);
-            const f32x4 ay = *reinterpret_cast<const f32x4*>(dYs + (16 * it + l16) * SV + kb + 4 * g4);
-            const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + (16 * it + l16) * SV + kb + 4 * g4);
+            const f32x4 av = *reinterpret_cast<const f32x4*>(A + (16 * it + l16) * SV + kb + 4 * g4);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                sp = mfma_f32_k4(ay[s], bu[s], sp);
-                sz = mfma_f32_k4(al[s], bu[s], sz);
-            }
+            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bu[s], acc);
         }
         const int j = 16 * jt + l16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * it + 4 * g4 + e;
-            const float p = j <= i ? sp[e] : 0.0f;
-            dP[i * CS + j] = p;
-            dPT[j * CS + i] = p;
-            dG[i * CS + j] = j < i ? -be[i] * sz[e] : 0.0f;     // strict lower part for now
-            Zs[i * CS + j] = sz[e];
+            if (zw) {
+                dG[i * CS + j] = j < i ? -be[i] * acc[e] : 0.0f;    // strict lower part for now
+                Zs[i * CS + j] = acc[e];
+            } else {
+                const float p = j <= i ? acc[e] : 0.0f;
+                dP[i * CS + j] = p;
+                dPT[j * CS + i] = p;
+            }
         }
     }
     __syncthreads();
     // ---- dG's upper part = its transpose; beta partials lam_i.V_i - sum_{j<i} G_ij Z_ij over
-    //      the 8 adjacent lanes of row i
-    for (int e = tid; e < kBC * kBC; e += kPrepThreads2) {
+    //      the 16 adjacent lanes of row i
+    for (int e = tid; e < kBC * kBC; e += kGradThreads) {
         const int i = e >> 5, j = e & (kBC - 1);
         if (j > i) dG[i * CS + j] = dG[j * CS + i];
     }
     {
-        const int i = tid >> 3, p8 = tid & 7;
+        static_assert(kGradThreads == 16 * kBC, "16 lanes per chunk row");
+        const int i = tid >> 4, p16 = tid & 15;
         float s = 0.0f;
-        for (int r = p8; r < d_v; r += 8) s += Ls[i * SV + r] * Vs[i * SV + r];
-        for (int j = p8; j < i; j += 8) s -= Gm[i * CS + j] * Zs[i * CS + j];
+        for (int r = p16; r < d_v; r += 16) s += Ls[i * SV + r] * Vs[i * SV + r];
+        for (int j = p16; j < i; j += 16) s -= Gm[i * CS + j] * Zs[i * CS + j];
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 4);
-        if (p8 == 0) bpart[i] = s;
+        s += __shfl_xor(s, 8);
+        if (p16 == 0) bpart[i] = s;
     }
 
     // ---- D-wide products per 64-column slice
@@ -810,13 +816,13 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     // D over the lanes) become one 16-byte LDS store of the transposed row.  K and Q are stored
     // transposed ([D][C]): unit u = (column nn = u / 8, chunk rows 4 (u % 8) .. + 3), one 16-byte
     // load and one 16-byte store.
-    constexpr int NW = 16 * kSlice / kPrepThreads2;      // W0 / dW1 units per thread (d_v <= 64)
-    constexpr int NK = (kBC / 4) * kSlice / kPrepThreads2;   // K / Q units per thread
+    constexpr int NW = 16 * kSlice / kGradThreads;      // W0 / dW1 units per thread (d_v <= 64)
+    constexpr int NK = (kBC / 4) * kSlice / kGradThreads;   // K / Q units per thread
     f32x4 pw[NW], pg[NW], pk[NK], pq[NK];
     auto fetch = [&](int s0) {
 #pragma unroll
         for (int p = 0; p < NW; ++p) {
-            const int e = tid + kPrepThreads2 * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
+            const int e = tid + kGradThreads * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
             const bool cin = s0 + nn < D;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -828,7 +834,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
-            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e & 7), nn = e >> 3;
+            const int e = tid + kGradThreads * p, c0 = 4 * (e & 7), nn = e >> 3;
             const bool in = s0 + nn < D;
             const int64_t o = u64 * CD + int64_t(in ? s0 + nn : 0) * kBC + c0;   // [D][C] tiles
             pk[p] = in ? *reinterpret_cast<const f32x4*>(a.ws + a.L.kt + o) : zero4();
@@ -838,7 +844,7 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
     auto commit = [&]() {
 #pragma unroll
         for (int p = 0; p < NW; ++p) {
-            const int e = tid + kPrepThreads2 * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
+            const int e = tid + kGradThreads * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
             if (k0 < DV16) {
                 *reinterpret_cast<f32x4*>(W0T + nn * SV + k0) = pw[p];
                 *reinterpret_cast<f32x4*>(G1T + nn * SV + k0) = pg[p];
@@ -846,42 +852,35 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         }
 #pragma unroll
         for (int p = 0; p < NK; ++p) {
-            const int e = tid + kPrepThreads2 * p, c0 = 4 * (e & 7), nn = e >> 3;
+            const int e = tid + kGradThreads * p, c0 = 4 * (e & 7), nn = e >> 3;
             *reinterpret_cast<f32x4*>(KT + nn * CS + c0) = pk[p];
             *reinterpret_cast<f32x4*>(QT + nn * CS + c0) = pq[p];
         }
     };
-    float mkp[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mkp[rt][e] = 0.0f;
-    const int ncol = 16 * wv + l16;                         // the lane's column in the slice
+    // wave w: column tile w % 4 of the slice, row tile w / 4 of the chunk
+    const int rt = wv >> 2;
+    float mkp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int ncol = 16 * (wv & 3) + l16;                   // the lane's column in the slice
     fetch(0);
     for (int s0 = 0; s0 < D; s0 += kSlice) {
         __syncthreads();                                    // the previous slice's reads are done
         commit();
         if (s0 + kSlice < D) fetch(s0 + kSlice);
         __syncthreads();
-        f32x4 dq[2], mm[2], dk[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) dq[rt] = mm[rt] = dk[rt] = zero4();
+        f32x4 dq = zero4(), mm = zero4(), dk = zero4();
         // k over d_v
         for (int kb = 0; kb < DV16; kb += 16) {
             const f32x4 bw = *reinterpret_cast<const f32x4*>(W0T + ncol * SV + kb + 4 * g4);
             const f32x4 bg = *reinterpret_cast<const f32x4*>(G1T + ncol * SV + kb + 4 * g4);
+            const int ro = (16 * rt + l16) * SV + kb + 4 * g4;
+            const f32x4 ady = *reinterpret_cast<const f32x4*>(dYs + ro);
+            const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + ro);
+            const f32x4 au = *reinterpret_cast<const f32x4*>(Us + ro);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int ro = (16 * rt + l16) * SV + kb + 4 * g4;
-                const f32x4 ady = *reinterpret_cast<const f32x4*>(dYs + ro);
-                const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + ro);
-                const f32x4 au = *reinterpret_cast<const f32x4*>(Us + ro);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    dq[rt] = mfma_f32_k4(ady[s], bw[s], dq[rt]);
-                    mm[rt] = mfma_f32_k4(al[s], bw[s], mm[rt]);
-                    dk[rt] = mfma_f32_k4(au[s], bg[s], dk[rt]);
-                }
+            for (int s = 0; s < 4; ++s) {
+                dq = mfma_f32_k4(ady[s], bw[s], dq);
+                mm = mfma_f32_k4(al[s], bw[s], mm);
+                dk = mfma_f32_k4(au[s], bg[s], dk);
             }
         }
         // k over the chunk rows
@@ -889,48 +888,40 @@ __global__ __launch_bounds__(kPrepThreads2) void bwd_chunk_grads_kernel(BwdArgs 
         for (int kb = 0; kb < kBC; kb += 16) {
             const f32x4 bk = *reinterpret_cast<const f32x4*>(KT + ncol * CS + kb + 4 * g4);
             const f32x4 bq = *reinterpret_cast<const f32x4*>(QT + ncol * CS + kb + 4 * g4);
+            const int ro = (16 * rt + l16) * CS + kb + 4 * g4;
+            const f32x4 ap = *reinterpret_cast<const f32x4*>(dP + ro);
+            const f32x4 apt = *reinterpret_cast<const f32x4*>(dPT + ro);
+            const f32x4 ag = *reinterpret_cast<const f32x4*>(dG + ro);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int ro = (16 * rt + l16) * CS + kb + 4 * g4;
-                const f32x4 ap = *reinterpret_cast<const f32x4*>(dP + ro);
-                const f32x4 apt = *reinterpret_cast<const f32x4*>(dPT + ro);
-                const f32x4 ag = *reinterpret_cast<const f32x4*>(dG + ro);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    dq[rt] = mfma_f32_k4(ap[s], bk[s], dq[rt]);
-                    dk[rt] = mfma_f32_k4(apt[s], bq[s], dk[rt]);
-                    dk[rt] = mfma_f32_k4(ag[s], bk[s], dk[rt]);
-                }
+            for (int s = 0; s < 4; ++s) {
+                dq = mfma_f32_k4(ap[s], bk[s], dq);
+                dk = mfma_f32_k4(apt[s], bq[s], dk);
+                dk = mfma_f32_k4(ag[s], bk[s], dk);
             }
         }
-        // result slot e of row tile rt: row i = 16 rt + 4 g4 + e, column s0 + ncol
+        // result slot e: row i = 16 rt + 4 g4 + e, column s0 + ncol
         const int col = s0 + ncol;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * rt + 4 * g4 + e;
-                const float m = mm[rt][e];
-                mkp[rt][e] += m * KT[ncol * CS + i];
-                if (col < D) {
-                    a.ws[a.L.wy + u64 * CD + int64_t(i) * D + col] = dk[rt][e] - be[i] * m;
-                    a.ws[a.L.qp + u64 * CD + int64_t(i) * D + col] = dq[rt][e];
-                }
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * rt + 4 * g4 + e;
+            const float m = mm[e];
+            mkp[e] += m * KT[ncol * CS + i];
+            if (col < D) {
+                a.ws[a.L.wy + u64 * CD + int64_t(i) * D + col] = dk[e] - be[i] * m;
+                a.ws[a.L.qp + u64 * CD + int64_t(i) * D + col] = dq[e];
             }
         }
     }
-    // M_i . K_i: the 16 lanes of a row group hold its columns; then the four waves
+    // M_i . K_i: the 16 lanes of a row group hold its columns; then the four column tiles
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float s = mkp[rt][e];
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            s += __shfl_xor(s, 4);
-            s += __shfl_xor(s, 8);
-            if (l16 == 0) mkb[wv * kBC + 16 * rt + 4 * g4 + e] = s;
-        }
+    for (int e = 0; e < 4; ++e) {
+        float s = mkp[e];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        if (l16 == 0) mkb[(wv & 3) * kBC + 16 * rt + 4 * g4 + e] = s;
+    }
     __syncthreads();
     if (tid < kBC && t0 + tid < a.T) {
         // beta (1 - beta) as sigmoid(l) sigmoid(-l): 1 - beta cancels where beta rounds to 1
@@ -1088,7 +1079,7 @@ static hipError_t launch_backward_t(BwdArgs a, hipStream_t stream) {
     const int lg = lds_grads_bytes(a.d_v);
     auto kc = bwd_chunk_grads_kernel<BF16>;
     if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kc), lg)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kc, dim3(static_cast<unsigned>(NU)), dim3(kPrepThreads2), lg, stream, a);
+    hipLaunchKernelGGL(kc, dim3(static_cast<unsigned>(NU)), dim3(kGradThreads), lg, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nvec = int64_t(a.BH) * a.T;
     const dim3 grid(static_cast<unsigned>((nvec + kDpfpWaves - 1) / kDpfpWaves), 2);

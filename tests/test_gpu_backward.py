@@ -54,6 +54,8 @@ BWD_CASES = [
     ("b4_h8_t4096_d64_nu2_bf16_carried", {}, True),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "T": 1000, "nu": 3}, True),
     ("b4_h8_t4096_d64_nu2_bf16_carried", {"B": 1, "H": 2, "T": 45, "d_k": 16, "nu": 5, "d_v": 24}, False),
+    # more chunks than resident workgroups, not a multiple of them, and a ragged last chunk
+    ("b4_h8_t4096_d64_nu2_bf16_carried", {"T": 2100}, False),
 ]
 
 

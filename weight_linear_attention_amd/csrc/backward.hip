@@ -618,15 +618,15 @@ __host__ __device__ inline int grads_dvp(int d_v) { return grads_dv16(d_v) + 4; 
 //   dP = lower_incl(dY U^T)      Z = lam U^T      dG_ij = -beta_i Z_ij (j < i), symmetrised
 // then, per 64-column slice of D (wave w: column tile w % 4, row tile w / 4),
 //   dQ = dY W0 + dP K,   M = lam W0,   dK = U dW1 + dP^T Q + (dG + dG^T) K - diag(beta) M.
-// The chunk's operands are loaded into registers in one batch before any LDS store; the next
-// slice's W0, dW1, K and Q load into registers while the current slice computes.
-template <bool BF16>
+// One chunk per workgroup, or, with PERSIST (more chunks than workgroups fit at once), the
+// resident workgroups walk the chunks with the grid as stride and each chunk's operands load into
+// registers during the previous chunk; the next slice's W0, dW1, K and Q load into registers
+// while the current slice computes.
+template <bool BF16, bool PERSIST>
 __global__ __launch_bounds__(kGradThreads) void bwd_chunk_grads_kernel(BwdArgs a) {
     extern __shared__ float lds[];
     const int D = a.D, d_v = a.d_v;
-    const int u = blockIdx.x;
-    const int bh = u / a.NC, n = u % a.NC;
-    const int t0 = n * kBC;
+    const int64_t NU = int64_t(a.BH) * a.NC;
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     constexpr int CS = kCS;
@@ -654,283 +654,308 @@ __global__ __launch_bounds__(kGradThreads) void bwd_chunk_grads_kernel(BwdArgs a
     float* KT = G1T + kSlice * SV;    // [kSlice][CS]: K slice transposed
     float* QT = KT + kSlice * CS;
 
-    const int64_t u64 = u;
-    // ---- the chunk's operands, all loads first.  dy, v: (row c = tid / 64 + 8 m, entry r =
+    // ---- a chunk's operands in registers.  dy, v: (row c = tid / 64 + 8 m, entry r =
     //      tid % 64); U, K dW1^T: workspace [r][c] units tid + 512 m; Ainv, P, G: [i][j] units
-    //      tid + 512 m
-    {
-        constexpr int MR = kBC / (kGradThreads / 64);           // 4 rows per thread
-        constexpr int MU = kBC * 64 / kGradThreads;              // 4 units (d_v <= 64)
-        constexpr int MC = kBC * kBC / kGradThreads;             // 2 units
-        const int r = tid & 63;
-        float fy[MR], fv[MR], fu[MU], fa[MU], fi[MC], fp[MC], fg[MC];
+    //      tid + 512 m.  Every lane issues every load (an entry outside the chunk reads the
+    //      chunk's first one and is zeroed), so the in-order load counter lets each wait cover
+    //      only the loads it needs.
+    constexpr int MR = kBC / (kGradThreads / 64);           // 4 rows per thread
+    constexpr int MU = kBC * 64 / kGradThreads;              // 4 units (d_v <= 64)
+    constexpr int MC = kBC * kBC / kGradThreads;             // 2 units
+    const int r = tid & 63;
+    float fy[MR], fv[MR], fu[MU], fa[MU], fi[MC], fp[MC], fg[MC], fb;
+    auto load_chunk = [&](int64_t uu) {
+        const int bhl = static_cast<int>(uu / a.NC), tl = static_cast<int>(uu % a.NC) * kBC;
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             const int c = (tid >> 6) + kGradWaves * m;
-            const bool in = t0 + c < a.T && r < d_v;
-            const int64_t g = (int64_t(bh) * a.T + t0 + (in ? c : 0)) * d_v + (in ? r : 0);
-            fy[m] = in ? load_elem<BF16>(a.dy, g) : 0.0f;
-            fv[m] = in ? load_elem<BF16>(a.v, g) : 0.0f;
+            const bool in = tl + c < a.T && r < d_v;
+            const int64_t g = (int64_t(bhl) * a.T + tl + (in ? c : 0)) * d_v + (in ? r : 0);
+            const float y = load_elem<BF16>(a.dy, g), v = load_elem<BF16>(a.v, g);
+            fy[m] = in ? y : 0.0f;
+            fv[m] = in ? v : 0.0f;
         }
 #pragma unroll
         for (int m = 0; m < MU; ++m) {
             const int e = tid + kGradThreads * m;
             const bool in = e < kBC * d_v;
-            fu[m] = in ? a.ws[a.L.uu + u64 * kBC * d_v + e] : 0.0f;
-            fa[m] = in ? a.ws[a.L.aa + u64 * kBC * d_v + e] : 0.0f;
+            const float x = a.ws[a.L.uu + uu * kBC * d_v + (in ? e : 0)];
+            const float y = a.ws[a.L.aa + uu * kBC * d_v + (in ? e : 0)];
+            fu[m] = in ? x : 0.0f;
+            fa[m] = in ? y : 0.0f;
         }
 #pragma unroll
         for (int m = 0; m < MC; ++m) {
             const int e = tid + kGradThreads * m;
-            fi[m] = a.ws[a.L.ai + u64 * kBC * kBC + e];
-            fp[m] = a.ws[a.L.pm + u64 * kBC * kBC + e];
-            fg[m] = a.ws[a.L.gm + u64 * kBC * kBC + e];
+            fi[m] = a.ws[a.L.ai + uu * kBC * kBC + e];
+            fp[m] = a.ws[a.L.pm + uu * kBC * kBC + e];
+            fg[m] = a.ws[a.L.gm + uu * kBC * kBC + e];
         }
-        const float fb = tid < kBC ? a.ws[a.L.be + u64 * kBC + tid] : 0.0f;
-        // zero padding: rows past d_v of the transposed tiles, entries past d_v of the row tiles
-        for (int e = tid; e < (DV16 - d_v) * CS; e += kGradThreads) {
-            dYT[d_v * CS + e] = 0.0f;
-            dUT[d_v * CS + e] = 0.0f;
-        }
-        for (int e = tid; e < kBC * (SV - d_v); e += kGradThreads) {
-            const int c = e / (SV - d_v), rr = d_v + e % (SV - d_v);
-            dYs[c * SV + rr] = 0.0f;
-            Us[c * SV + rr] = 0.0f;
-            Ls[c * SV + rr] = 0.0f;
-            Vs[c * SV + rr] = 0.0f;
-        }
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            const int c = (tid >> 6) + kGradWaves * m;
-            if (r < d_v) {
-                dYs[c * SV + r] = fy[m];
-                dYT[r * CS + c] = fy[m];
-                Vs[c * SV + r] = fv[m];
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MU; ++m) {
-            const int e = tid + kGradThreads * m, rr = e >> 5, c = e & (kBC - 1);
-            if (e < kBC * d_v) {
-                Us[c * SV + rr] = fu[m];
-                dUT[rr * CS + c] = fa[m];                  // K dW1^T, P^T dY added below
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MC; ++m) {
-            const int e = tid + kGradThreads * m, i = e >> 5, j = e & (kBC - 1);
-            AiT[j * CS + i] = fi[m];
-            PmT[j * CS + i] = fp[m];
-            Gm[i * CS + j] = fg[m];
-        }
-        if (tid < kBC) be[tid] = fb;
-    }
-    __syncthreads();
-    // ---- dU = P^T dY + K dW1^T (tiles (it, rt) of dU, stored transposed)
-    for (int tau = wv; tau < 2 * NR; tau += kGradWaves) {
-        const int it = tau & 1, rt = tau >> 1;
-        float* out = dUT + (16 * rt + l16) * CS + 16 * it + 4 * g4;
-        f32x4 acc = *reinterpret_cast<const f32x4*>(out);
-#pragma unroll
-        for (int kb = 0; kb < kBC; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(PmT + (16 * it + l16) * CS + kb + 4 * g4);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(dYT + (16 * rt + l16) * CS + kb + 4 * g4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
-        }
-        *reinterpret_cast<f32x4*>(out) = acc;
-    }
-    __syncthreads();
-    // ---- lam = Ainv^T dU; dv = diag(beta) lam
-    for (int tau = wv; tau < 2 * NR; tau += kGradWaves) {
-        const int it = tau & 1, rt = tau >> 1;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < kBC; kb += 16) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(AiT + (16 * it + l16) * CS + kb + 4 * g4);
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(dUT + (16 * rt + l16) * CS + kb + 4 * g4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
-        }
-        const int r = 16 * rt + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * it + 4 * g4 + e;
-            Ls[i * SV + r] = acc[e];
-            if (r < d_v && t0 + i < a.T)
-                store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * acc[e]);
-        }
-    }
-    __syncthreads();
-    // ---- dP = lower_incl(dY U^T) (and its transpose) on waves 0 .. 3, Z = lam U^T and dG on
-    //      waves 4 .. 7: wave w -> tile (w % 2, (w / 2) % 2)
-    {
-        const bool zw = wv >= 4;
-        const int it = wv & 1, jt = (wv >> 1) & 1;
-        const float* A = zw ? Ls : dYs;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < DV16; kb += 16) {
-            const f32x4 bu = *reinterpret_cast<const f32x4*>(Us + (16 * jt + l16) * SV + kb + 4 * g4);
-            const f32x4 av = *reinterpret_cast<const f32x4*>(A + (16 * it + l16) * SV + kb + 4 * g4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bu[s], acc);
-        }
-        const int j = 16 * jt + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * it + 4 * g4 + e;
-            if (zw) {
-                dG[i * CS + j] = j < i ? -be[i] * acc[e] : 0.0f;    // strict lower part for now
-                Zs[i * CS + j] = acc[e];
-            } else {
-                const float p = j <= i ? acc[e] : 0.0f;
-                dP[i * CS + j] = p;
-                dPT[j * CS + i] = p;
-            }
-        }
-    }
-    __syncthreads();
-    // ---- dG's upper part = its transpose; beta partials lam_i.V_i - sum_{j<i} G_ij Z_ij over
-    //      the 16 adjacent lanes of row i
-    for (int e = tid; e < kBC * kBC; e += kGradThreads) {
-        const int i = e >> 5, j = e & (kBC - 1);
-        if (j > i) dG[i * CS + j] = dG[j * CS + i];
-    }
-    {
-        static_assert(kGradThreads == 16 * kBC, "16 lanes per chunk row");
-        const int i = tid >> 4, p16 = tid & 15;
-        float s = 0.0f;
-        for (int r = p16; r < d_v; r += 16) s += Ls[i * SV + r] * Vs[i * SV + r];
-        for (int j = p16; j < i; j += 16) s -= Gm[i * CS + j] * Zs[i * CS + j];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (p16 == 0) bpart[i] = s;
-    }
+        fb = a.ws[a.L.be + uu * kBC + (tid & (kBC - 1))];
+    };
 
-    // ---- D-wide products per 64-column slice
-    const int64_t CD = int64_t(kBC) * D;
-    // staging: W0 and dW1 ([d_v][D] rows) as units u = tid + 256 p of (column nn = u % 64, four
-    // consecutive d_v indices from 4 (u / 64)): four global loads down the rows (coalesced along
-    // D over the lanes) become one 16-byte LDS store of the transposed row.  K and Q are stored
-    // transposed ([D][C]): unit u = (column nn = u / 8, chunk rows 4 (u % 8) .. + 3), one 16-byte
-    // load and one 16-byte store.
-    constexpr int NW = 16 * kSlice / kGradThreads;      // W0 / dW1 units per thread (d_v <= 64)
-    constexpr int NK = (kBC / 4) * kSlice / kGradThreads;   // K / Q units per thread
-    f32x4 pw[NW], pg[NW], pk[NK], pq[NK];
-    auto fetch = [&](int s0) {
-#pragma unroll
-        for (int p = 0; p < NW; ++p) {
-            const int e = tid + kGradThreads * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
-            const bool cin = s0 + nn < D;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bool in = cin && k0 + q < d_v;
-                const int64_t o = (u64 * d_v + (in ? k0 + q : 0)) * D + (in ? s0 + nn : 0);
-                pw[p][q] = in ? a.ws[a.L.ws + o] : 0.0f;
-                pg[p][q] = in ? a.ws[a.L.gs + o] : 0.0f;
+    // Chunks u = blockIdx.x + k gridDim.x (the grid holds the workgroups resident at once); the
+    // next chunk's operands load while the current one computes.
+    int64_t u = blockIdx.x;
+    load_chunk(u);
+    for (; u < NU; u += gridDim.x) {
+        const int64_t u64 = u;
+        const int bh = static_cast<int>(u / a.NC), n = static_cast<int>(u % a.NC);
+        const int t0 = n * kBC;
+        __syncthreads();                                        // the previous chunk's reads are done
+        {
+            // zero padding: rows past d_v of the transposed tiles, entries past d_v of the row tiles
+            for (int e = tid; e < (DV16 - d_v) * CS; e += kGradThreads) {
+                dYT[d_v * CS + e] = 0.0f;
+                dUT[d_v * CS + e] = 0.0f;
             }
-        }
-#pragma unroll
-        for (int p = 0; p < NK; ++p) {
-            const int e = tid + kGradThreads * p, c0 = 4 * (e & 7), nn = e >> 3;
-            const bool in = s0 + nn < D;
-            const int64_t o = u64 * CD + int64_t(in ? s0 + nn : 0) * kBC + c0;   // [D][C] tiles
-            pk[p] = in ? *reinterpret_cast<const f32x4*>(a.ws + a.L.kt + o) : zero4();
-            pq[p] = in ? *reinterpret_cast<const f32x4*>(a.ws + a.L.qt + o) : zero4();
-        }
-    };
-    auto commit = [&]() {
-#pragma unroll
-        for (int p = 0; p < NW; ++p) {
-            const int e = tid + kGradThreads * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
-            if (k0 < DV16) {
-                *reinterpret_cast<f32x4*>(W0T + nn * SV + k0) = pw[p];
-                *reinterpret_cast<f32x4*>(G1T + nn * SV + k0) = pg[p];
+            for (int e = tid; e < kBC * (SV - d_v); e += kGradThreads) {
+                const int c = e / (SV - d_v), rr = d_v + e % (SV - d_v);
+                dYs[c * SV + rr] = 0.0f;
+                Us[c * SV + rr] = 0.0f;
+                Ls[c * SV + rr] = 0.0f;
+                Vs[c * SV + rr] = 0.0f;
             }
-        }
 #pragma unroll
-        for (int p = 0; p < NK; ++p) {
-            const int e = tid + kGradThreads * p, c0 = 4 * (e & 7), nn = e >> 3;
-            *reinterpret_cast<f32x4*>(KT + nn * CS + c0) = pk[p];
-            *reinterpret_cast<f32x4*>(QT + nn * CS + c0) = pq[p];
+            for (int m = 0; m < MR; ++m) {
+                const int c = (tid >> 6) + kGradWaves * m;
+                if (r < d_v) {
+                    dYs[c * SV + r] = fy[m];
+                    dYT[r * CS + c] = fy[m];
+                    Vs[c * SV + r] = fv[m];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MU; ++m) {
+                const int e = tid + kGradThreads * m, rr = e >> 5, c = e & (kBC - 1);
+                if (e < kBC * d_v) {
+                    Us[c * SV + rr] = fu[m];
+                    dUT[rr * CS + c] = fa[m];                  // K dW1^T, P^T dY added below
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const int e = tid + kGradThreads * m, i = e >> 5, j = e & (kBC - 1);
+                AiT[j * CS + i] = fi[m];
+                PmT[j * CS + i] = fp[m];
+                Gm[i * CS + j] = fg[m];
+            }
+            if (tid < kBC) be[tid] = fb;
         }
-    };
-    // wave w: column tile w % 4 of the slice, row tile w / 4 of the chunk
-    const int rt = wv >> 2;
-    float mkp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int ncol = 16 * (wv & 3) + l16;                   // the lane's column in the slice
-    fetch(0);
-    for (int s0 = 0; s0 < D; s0 += kSlice) {
-        __syncthreads();                                    // the previous slice's reads are done
-        commit();
-        if (s0 + kSlice < D) fetch(s0 + kSlice);
+        // ---- operands of the D-wide products, per 64-column slice
+        const int64_t CD = int64_t(kBC) * D;
+        // staging: W0 and dW1 ([d_v][D] rows) as units e = tid + 512 p of (column nn = e % 64, four
+        // consecutive d_v indices from 4 (e / 64)): four global loads down the rows (coalesced along
+        // D over the lanes) become one 16-byte LDS store of the transposed row.  K and Q are stored
+        // transposed ([D][C]): unit e = (column nn = e / 8, chunk rows 4 (e % 8) .. + 3), one 16-byte
+        // load and one 16-byte store.
+        constexpr int NW = 16 * kSlice / kGradThreads;      // W0 / dW1 units per thread (d_v <= 64)
+        constexpr int NK = (kBC / 4) * kSlice / kGradThreads;   // K / Q units per thread
+        f32x4 pw[NW], pg[NW], pk[NK], pq[NK];
+        auto fetch = [&](int s0) {
+#pragma unroll
+            for (int p = 0; p < NW; ++p) {
+                const int e = tid + kGradThreads * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
+                const bool cin = s0 + nn < D;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bool in = cin && k0 + q < d_v;
+                    const int64_t o = (u64 * d_v + (in ? k0 + q : 0)) * D + (in ? s0 + nn : 0);
+                    const float x = a.ws[a.L.ws + o], y = a.ws[a.L.gs + o];
+                    pw[p][q] = in ? x : 0.0f;
+                    pg[p][q] = in ? y : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = tid + kGradThreads * p, c0 = 4 * (e & 7), nn = e >> 3;
+                const bool in = s0 + nn < D;
+                const int64_t o = u64 * CD + int64_t(in ? s0 + nn : 0) * kBC + c0;   // [D][C] tiles
+                const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws + a.L.kt + o);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(a.ws + a.L.qt + o);
+                pk[p] = in ? x : zero4();
+                pq[p] = in ? y : zero4();
+            }
+        };
+        auto commit = [&]() {
+#pragma unroll
+            for (int p = 0; p < NW; ++p) {
+                const int e = tid + kGradThreads * p, k0 = 4 * (e / kSlice), nn = e % kSlice;
+                if (k0 < DV16) {
+                    *reinterpret_cast<f32x4*>(W0T + nn * SV + k0) = pw[p];
+                    *reinterpret_cast<f32x4*>(G1T + nn * SV + k0) = pg[p];
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < NK; ++p) {
+                const int e = tid + kGradThreads * p, c0 = 4 * (e & 7), nn = e >> 3;
+                *reinterpret_cast<f32x4*>(KT + nn * CS + c0) = pk[p];
+                *reinterpret_cast<f32x4*>(QT + nn * CS + c0) = pq[p];
+            }
+        };
+        fetch(0);
+        if constexpr (PERSIST)   // the next chunk (this one again past the end: the load counts stay fixed)
+            load_chunk(u + gridDim.x < NU ? u + gridDim.x : u);
         __syncthreads();
-        f32x4 dq = zero4(), mm = zero4(), dk = zero4();
-        // k over d_v
-        for (int kb = 0; kb < DV16; kb += 16) {
-            const f32x4 bw = *reinterpret_cast<const f32x4*>(W0T + ncol * SV + kb + 4 * g4);
-            const f32x4 bg = *reinterpret_cast<const f32x4*>(G1T + ncol * SV + kb + 4 * g4);
-            const int ro = (16 * rt + l16) * SV + kb + 4 * g4;
-            const f32x4 ady = *reinterpret_cast<const f32x4*>(dYs + ro);
-            const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + ro);
-            const f32x4 au = *reinterpret_cast<const f32x4*>(Us + ro);
+        // ---- dU = P^T dY + K dW1^T (tiles (it, rt) of dU, stored transposed)
+        for (int tau = wv; tau < 2 * NR; tau += kGradWaves) {
+            const int it = tau & 1, rt = tau >> 1;
+            float* out = dUT + (16 * rt + l16) * CS + 16 * it + 4 * g4;
+            f32x4 acc = *reinterpret_cast<const f32x4*>(out);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                dq = mfma_f32_k4(ady[s], bw[s], dq);
-                mm = mfma_f32_k4(al[s], bw[s], mm);
-                dk = mfma_f32_k4(au[s], bg[s], dk);
+            for (int kb = 0; kb < kBC; kb += 16) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(PmT + (16 * it + l16) * CS + kb + 4 * g4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(dYT + (16 * rt + l16) * CS + kb + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+            }
+            *reinterpret_cast<f32x4*>(out) = acc;
+        }
+        __syncthreads();
+        // ---- lam = Ainv^T dU; dv = diag(beta) lam
+        for (int tau = wv; tau < 2 * NR; tau += kGradWaves) {
+            const int it = tau & 1, rt = tau >> 1;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < kBC; kb += 16) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(AiT + (16 * it + l16) * CS + kb + 4 * g4);
+                const f32x4 bv = *reinterpret_cast<const f32x4*>(dUT + (16 * rt + l16) * CS + kb + 4 * g4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bv[s], acc);
+            }
+            const int r = 16 * rt + l16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * g4 + e;
+                Ls[i * SV + r] = acc[e];
+                if (r < d_v && t0 + i < a.T)
+                    store_elem<BF16>(a.dv, (int64_t(bh) * a.T + t0 + i) * d_v + r, be[i] * acc[e]);
             }
         }
-        // k over the chunk rows
+        __syncthreads();
+        // ---- dP = lower_incl(dY U^T) (and its transpose) on waves 0 .. 3, Z = lam U^T and dG on
+        //      waves 4 .. 7: wave w -> tile (w % 2, (w / 2) % 2)
+        {
+            const bool zw = wv >= 4;
+            const int it = wv & 1, jt = (wv >> 1) & 1;
+            const float* A = zw ? Ls : dYs;
+            f32x4 acc = zero4();
+            for (int kb = 0; kb < DV16; kb += 16) {
+                const f32x4 bu = *reinterpret_cast<const f32x4*>(Us + (16 * jt + l16) * SV + kb + 4 * g4);
+                const f32x4 av = *reinterpret_cast<const f32x4*>(A + (16 * it + l16) * SV + kb + 4 * g4);
 #pragma unroll
-        for (int kb = 0; kb < kBC; kb += 16) {
-            const f32x4 bk = *reinterpret_cast<const f32x4*>(KT + ncol * CS + kb + 4 * g4);
-            const f32x4 bq = *reinterpret_cast<const f32x4*>(QT + ncol * CS + kb + 4 * g4);
-            const int ro = (16 * rt + l16) * CS + kb + 4 * g4;
-            const f32x4 ap = *reinterpret_cast<const f32x4*>(dP + ro);
-            const f32x4 apt = *reinterpret_cast<const f32x4*>(dPT + ro);
-            const f32x4 ag = *reinterpret_cast<const f32x4*>(dG + ro);
+                for (int s = 0; s < 4; ++s) acc = mfma_f32_k4(av[s], bu[s], acc);
+            }
+            const int j = 16 * jt + l16;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                dq = mfma_f32_k4(ap[s], bk[s], dq);
-                dk = mfma_f32_k4(apt[s], bq[s], dk);
-                dk = mfma_f32_k4(ag[s], bk[s], dk);
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * g4 + e;
+                if (zw) {
+                    dG[i * CS + j] = j < i ? -be[i] * acc[e] : 0.0f;    // strict lower part for now
+                    Zs[i * CS + j] = acc[e];
+                } else {
+                    const float p = j <= i ? acc[e] : 0.0f;
+                    dP[i * CS + j] = p;
+                    dPT[j * CS + i] = p;
+                }
             }
         }
-        // result slot e: row i = 16 rt + 4 g4 + e, column s0 + ncol
-        const int col = s0 + ncol;
+        __syncthreads();
+        // ---- dG's upper part = its transpose; beta partials lam_i.V_i - sum_{j<i} G_ij Z_ij over
+        //      the 16 adjacent lanes of row i
+        for (int e = tid; e < kBC * kBC; e += kGradThreads) {
+            const int i = e >> 5, j = e & (kBC - 1);
+            if (j > i) dG[i * CS + j] = dG[j * CS + i];
+        }
+        {
+            static_assert(kGradThreads == 16 * kBC, "16 lanes per chunk row");
+            const int i = tid >> 4, p16 = tid & 15;
+            float s = 0.0f;
+            for (int r = p16; r < d_v; r += 16) s += Ls[i * SV + r] * Vs[i * SV + r];
+            for (int j = p16; j < i; j += 16) s -= Gm[i * CS + j] * Zs[i * CS + j];
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            s += __shfl_xor(s, 4);
+            s += __shfl_xor(s, 8);
+            if (p16 == 0) bpart[i] = s;
+        }
+
+        // wave w: column tile w % 4 of the slice, row tile w / 4 of the chunk
+        const int rt = wv >> 2;
+        float mkp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int ncol = 16 * (wv & 3) + l16;                   // the lane's column in the slice
+        // ---- D-wide products per 64-column slice
+        for (int s0 = 0; s0 < D; s0 += kSlice) {
+            __syncthreads();                                    // the previous slice's reads are done
+            commit();
+            fetch(s0 + kSlice < D ? s0 + kSlice : s0);          // unconditional: the load counts stay fixed
+            __syncthreads();
+            f32x4 dq = zero4(), mm = zero4(), dk = zero4();
+            // k over d_v
+            for (int kb = 0; kb < DV16; kb += 16) {
+                const f32x4 bw = *reinterpret_cast<const f32x4*>(W0T + ncol * SV + kb + 4 * g4);
+                const f32x4 bg = *reinterpret_cast<const f32x4*>(G1T + ncol * SV + kb + 4 * g4);
+                const int ro = (16 * rt + l16) * SV + kb + 4 * g4;
+                const f32x4 ady = *reinterpret_cast<const f32x4*>(dYs + ro);
+                const f32x4 al = *reinterpret_cast<const f32x4*>(Ls + ro);
+                const f32x4 au = *reinterpret_cast<const f32x4*>(Us + ro);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    dq = mfma_f32_k4(ady[s], bw[s], dq);
+                    mm = mfma_f32_k4(al[s], bw[s], mm);
+                    dk = mfma_f32_k4(au[s], bg[s], dk);
+                }
+            }
+            // k over the chunk rows
+#pragma unroll
+            for (int kb = 0; kb < kBC; kb += 16) {
+                const f32x4 bk = *reinterpret_cast<const f32x4*>(KT + ncol * CS + kb + 4 * g4);
+                const f32x4 bq = *reinterpret_cast<const f32x4*>(QT + ncol * CS + kb + 4 * g4);
+                const int ro = (16 * rt + l16) * CS + kb + 4 * g4;
+                const f32x4 ap = *reinterpret_cast<const f32x4*>(dP + ro);
+                const f32x4 apt = *reinterpret_cast<const f32x4*>(dPT + ro);
+                const f32x4 ag = *reinterpret_cast<const f32x4*>(dG + ro);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    dq = mfma_f32_k4(ap[s], bk[s], dq);
+                    dk = mfma_f32_k4(apt[s], bq[s], dk);
+                    dk = mfma_f32_k4(ag[s], bk[s], dk);
+                }
+            }
+            // result slot e: row i = 16 rt + 4 g4 + e, column s0 + ncol
+            const int col = s0 + ncol;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * rt + 4 * g4 + e;
+                const float m = mm[e];
+                mkp[e] += m * KT[ncol * CS + i];
+                if (col < D) {
+                    a.ws[a.L.wy + u64 * CD + int64_t(i) * D + col] = dk[e] - be[i] * m;
+                    a.ws[a.L.qp + u64 * CD + int64_t(i) * D + col] = dq[e];
+                }
+            }
+        }
+        // M_i . K_i: the 16 lanes of a row group hold its columns; then the four column tiles
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * rt + 4 * g4 + e;
-            const float m = mm[e];
-            mkp[e] += m * KT[ncol * CS + i];
-            if (col < D) {
-                a.ws[a.L.wy + u64 * CD + int64_t(i) * D + col] = dk[e] - be[i] * m;
-                a.ws[a.L.qp + u64 * CD + int64_t(i) * D + col] = dq[e];
-            }
+            float s = mkp[e];
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            s += __shfl_xor(s, 4);
+            s += __shfl_xor(s, 8);
+            if (l16 == 0) mkb[(wv & 3) * kBC + 16 * rt + 4 * g4 + e] = s;
         }
-    }
-    // M_i . K_i: the 16 lanes of a row group hold its columns; then the four column tiles
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float s = mkp[e];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (l16 == 0) mkb[(wv & 3) * kBC + 16 * rt + 4 * g4 + e] = s;
-    }
-    __syncthreads();
-    if (tid < kBC && t0 + tid < a.T) {
-        // beta (1 - beta) as sigmoid(l) sigmoid(-l): 1 - beta cancels where beta rounds to 1
-        const int i = tid;
-        const float mk = (mkb[i] + mkb[kBC + i]) + (mkb[2 * kBC + i] + mkb[3 * kBC + i]);
-        const int64_t g = int64_t(bh) * a.T + t0 + i;
-        const float l = load_elem<BF16>(a.bl, g);
-        const float dbeta = bpart[i] - mk;
-        store_elem<BF16>(a.dbl, g, dbeta * sigmoid_stable(l) * sigmoid_stable(-l));
+        __syncthreads();
+        if (tid < kBC && t0 + tid < a.T) {
+            // beta (1 - beta) as sigmoid(l) sigmoid(-l): 1 - beta cancels where beta rounds to 1
+            const int i = tid;
+            const float mk = (mkb[i] + mkb[kBC + i]) + (mkb[2 * kBC + i] + mkb[3 * kBC + i]);
+            const int64_t g = int64_t(bh) * a.T + t0 + i;
+            const float l = load_elem<BF16>(a.bl, g);
+            const float dbeta = bpart[i] - mk;
+            store_elem<BF16>(a.dbl, g, dbeta * sigmoid_stable(l) * sigmoid_stable(-l));
+        }
+        if constexpr (!PERSIST) break;
     }
 }
 
@@ -1076,10 +1101,20 @@ static hipError_t launch_backward_t(BwdArgs a, hipStream_t stream) {
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || NU == 0) return e;
+    // chunk gradients: one chunk per workgroup where all fit at once, else the resident
+    // workgroups walk the chunks, each loading its next chunk's operands during the current one
     const int lg = lds_grads_bytes(a.d_v);
-    auto kc = bwd_chunk_grads_kernel<BF16>;
-    if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kc), lg)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kc, dim3(static_cast<unsigned>(NU)), dim3(kGradThreads), lg, stream, a);
+    auto kc1 = bwd_chunk_grads_kernel<BF16, false>;
+    auto kcp = bwd_chunk_grads_kernel<BF16, true>;
+    if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kc1), lg)) != hipSuccess) return e;
+    if ((e = ensure_lds_attr(reinterpret_cast<const void*>(kcp), lg)) != hipSuccess) return e;
+    unsigned cap = 0;
+    if ((e = resident_grid(reinterpret_cast<const void*>(kcp), kGradThreads, lg, INT64_MAX, &cap)) != hipSuccess)
+        return e;
+    if (NU <= int64_t(cap))
+        hipLaunchKernelGGL(kc1, dim3(static_cast<unsigned>(NU)), dim3(kGradThreads), lg, stream, a);
+    else
+        hipLaunchKernelGGL(kcp, dim3(cap), dim3(kGradThreads), lg, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nvec = int64_t(a.BH) * a.T;
     const dim3 grid(static_cast<unsigned>((nvec + kDpfpWaves - 1) / kDpfpWaves), 2);

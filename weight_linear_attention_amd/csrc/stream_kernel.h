@@ -301,7 +301,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
 //     blocks that Y and the memory update read (one 16-byte read per block and k-step).
 // Wave w owns row tile rt = w % 4 and column tile / Q half h = w / 4.  Per chunk:
 //   B  X = K W^T for tile (rt, h) over all of D; partial Q W^T over k-steps 4 p + 2 h + e
-//      (both column tiles); Z = V - rho_k o X to LDS, the partner's partial to LDS.
+//      (both column tiles); Z = V - rho_k o X to LDS (split into the bf16 hi and lo blocks
+//      that the U product reads), the partner's partial to LDS.
 //   C  U tile (rt, h) = A'' Z, stored as U and rho_k o U blocks; Q W^T tile (rt, h) = own +
 //      partner partial, times rho_q; the next chunk's K tile (one DPFP task per thread) and
 //      v columns.
@@ -326,7 +327,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     u16* const Kb0 = reinterpret_cast<u16*>(smem + a.s_k);
     u16* const Kb1 = reinterpret_cast<u16*>(smem + a.s_q);
     char* const WT = smem + a.s_wt;
-    float* const Zb = reinterpret_cast<float*>(smem + a.s_z);
+    char* const Zc = smem + a.s_z;                                 // Z as bf16 hi, then lo at
+                                                                   // + 4 KiB: B blocks as U's
     char* const Ub = smem + a.s_u;                                 // U, then rho_k o U at + 4 KiB:
                                                                    // bf16 B blocks of 32 rows
     float* const Xq = reinterpret_cast<float*>(smem + a.s_raw);    // Q W^T partials exchanged
@@ -340,6 +342,15 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     };
     auto put_ublk = [&](int off, const f32x4& x) {
         *reinterpret_cast<uint2*>(Ub + off + (((rt >> 1) * 2 + h) * 64 + l) * 16 + 8 * (rt & 1)) = pack_bf16x4(x);
+    };
+    // Z tile (rt, h), split once by the wave that forms it into the hi and lo blocks U = A'' Z reads
+    auto put_zblk = [&](const f32x4& x) {
+        char* const d = Zc + (((rt >> 1) * 2 + h) * 64 + l) * 16 + 8 * (rt & 1);
+        *reinterpret_cast<uint2*>(d) = pack_bf16x4(x);
+        *reinterpret_cast<uint2*>(d + 4096) = bf16_lo_part4(x);
+    };
+    auto zblk = [&](int off, int j) {
+        return as_bf16x8(*reinterpret_cast<const uint4*>(Zc + off + ((j * 2 + h) * 64 + l) * 16));
     };
 
     // ---- memory tiles: d-tile w + 8 s, column tile c (rows d = 16 dt + 4 g4 + e, column l16)
@@ -533,7 +544,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             xa[e] = bf16_bits_to_f32(Vr[(16 * rt + 4 * g4 + e) * 32 + 16 * h + l16]) - rkc[e] * xa[e];
-        *tile(Zb, rt, h) = xa;
+        put_zblk(xa);
         *tile(Xq, rt, 1 - h) = qx;
         lds_barrier();                                           // B2
 
@@ -544,9 +555,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
 #pragma unroll
             for (int j = 0; j < NTB; ++j) {
                 if (2 * j > rt) break;                            // A'' is zero above the diagonal
-                const f32x4 z0 = *tile(Zb, 2 * j, h), z1 = *tile(Zb, 2 * j + 1, h);
-                const bf16x8 zh = as_bf16x8(pack_bf16x8(z0, z1));
-                const bf16x8 zl = as_bf16x8(bf16_lo_part(z0, z1));
+                const bf16x8 zh = zblk(0, j), zl = zblk(4096, j);
                 u = mfma_bf16_k32(as_bf16x8(ah[j]), zh, u);
                 u = mfma_bf16_k32(as_bf16x8(ah[j]), zl, u);
                 u = mfma_bf16_k32(as_bf16x8(al[j]), zh, u);

@@ -72,9 +72,11 @@ __device__ __forceinline__ void store16(float* p, const float (&f)[16]) {
 // Both factors of a product are non-negative parts of k: the positive and negative parts of the
 // window are taken once per task, and each product is then a single multiply (relu(a) relu(x)
 // equals relu(relu(a) x), so the values are the same as relu of the product).
+// With `wraps` false the caller has already negated pv for the group at position 0 (so the
+// wrapped operands need no swap here).
 template <typename LT, int NU>
-__device__ __forceinline__ float dpfp_task(const float (&a)[8], const float (&pv)[8], int j0,
-                                           int d_k, LT* out) {
+__device__ __forceinline__ float dpfp_task_w(const float (&a)[8], const float (&pv)[8], int j0,
+                                             int d_k, LT* out, bool wraps) {
     static_assert(NU >= 1 && NU <= 4, "window indices 8 - NU .. 15");
     float P[16], N[16];
 #pragma unroll
@@ -83,7 +85,6 @@ __device__ __forceinline__ float dpfp_task(const float (&a)[8], const float (&pv
         P[m] = relu_f(r);
         N[m] = P[m] - r;                 // relu(-r), exactly
     }
-    const bool wraps = j0 == 0;          // positions e < i of the first group wrap
     float sum = 0.0f;
 #pragma unroll
     for (int i = 1; i <= NU; ++i) {
@@ -100,6 +101,11 @@ __device__ __forceinline__ float dpfp_task(const float (&a)[8], const float (&pv
         store16(out + 2 * ((i - 1) * d_k + j0), f);
     }
     return sum;
+}
+template <typename LT, int NU>
+__device__ __forceinline__ float dpfp_task(const float (&a)[8], const float (&pv)[8], int j0,
+                                           int d_k, LT* out) {
+    return dpfp_task_w<LT, NU>(a, pv, j0, d_k, out, j0 == 0);   // positions e < i of group 0 wrap
 }
 
 // Any nu (runtime shift count): the rolled operands are read from the staged row per shift.

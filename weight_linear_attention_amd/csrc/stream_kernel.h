@@ -430,7 +430,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
         for (int e = 0; e < 4; ++e) {
             const uint32_t prev = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a4[e]), 0x111, 0xF, 0xF, false));
             const uint32_t wrap = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a4[e]), 0x107, 0xF, 0xF, false));
-            pk[e] = (kjg == 0 ? wrap : prev) & mk;
+            // the positions before 0 wrap into the [-k] half: their signs flip here
+            pk[e] = (kjg == 0 ? wrap ^ 0x80008000u : prev) & mk;
         }
         float a8[8], p8[8];
 #pragma unroll
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
             p8[2 * e] = __uint_as_float(pk[e] << 16);
             p8[2 * e + 1] = __uint_as_float(pk[e] & 0xffff0000u);
         }
-        dpfp_task<u16, NU>(a8, p8, 8 * kjg, DK, Kn + ktr * krs);
+        dpfp_task_w<u16, NU>(a8, p8, 8 * kjg, DK, Kn + ktr * krs, false);
     };
     auto store_v = [&]() {
         if (tid < 4 * C)
@@ -494,12 +495,14 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
         f32x4 xa = zero4(), xb = zero4(), qo = zero4(), qx = zero4();
         {
             // window values as fp32 positive / negative parts; for the lane whose window starts
-            // at position 0 the four values before it wrap into the [-k] half, so their roles as
-            // the rolled factor swap
+            // at position 0 the four values before it wrap into the [-k] half: their signs are
+            // flipped before unpacking, which swaps their parts
             float Pw[2][8], Nw[2][8];
+            const uint32_t sg = (h == 0 && g4 == 0) ? 0x80008000u : 0u;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const uint32_t wd[4] = {qlo[e].x, qlo[e].y, qhi[e].x, qhi[e].y};
+                const uint32_t se = e == 0 ? sg : 0u;
+                const uint32_t wd[4] = {qlo[e].x ^ se, qlo[e].y ^ se, qhi[e].x, qhi[e].y};
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const float r = (m & 1) ? __uint_as_float(wd[m >> 1] & 0xffff0000u)
@@ -507,13 +510,6 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
                     Pw[e][m] = relu_f(r);
                     Nw[e][m] = Pw[e][m] - r;
                 }
-            }
-            const bool wrap = h == 0 && g4 == 0;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float p0 = Pw[0][m], n0 = Nw[0][m];
-                Pw[0][m] = wrap ? n0 : p0;
-                Nw[0][m] = wrap ? p0 : n0;
             }
             const u16* kr = Kc + (16 * rt + l16) * krs + 8 * g4;
 #pragma unroll

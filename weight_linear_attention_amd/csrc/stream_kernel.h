@@ -16,7 +16,8 @@
 //      read).
 //   Wave w owns tile (row tile w % 4, column tile w / 4) of X, Q W^T, U and Y:
 //   B  X = K W^T and Q W^T over all of D (one W^T block per k-step feeds both products); Z =
-//      V - rho_k o X to LDS (fp32 tiles), rho_q o Q W^T kept in registers.
+//      V - rho_k o X to LDS (split once into bf16 hi and lo B blocks), rho_q o Q W^T kept in
+//      registers.
 //   C  U = A'' Z (A'' and Z as bf16 hi + lo pairs, 3 MFMAs per k-step).
 //   D  Y = rho_q o (Q W^T) + P~ U, as bf16 rows in LDS (over Z); the wave's memory tiles +=
 //      K^T (rho_k o U), K^T read from the K tile by LDS
@@ -58,7 +59,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
     u16* Kt = reinterpret_cast<u16*>(smem + a.s_k);
     u16* Qt = reinterpret_cast<u16*>(smem + a.s_q);
     char* WT = smem + a.s_wt;                  // B blocks (jb, ct) of W^T, bf16
-    float* Zb = reinterpret_cast<float*>(smem + a.s_z);
+    char* Zc = smem + a.s_z;                   // Z as bf16 hi, then lo at + 4 KiB: B blocks of
+                                               // 32 rows (row pair j, column tile c)
     float* Ub = reinterpret_cast<float*>(smem + a.s_u);
     char* sb = smem + a.s_raw;                 // raw k rows, q rows, v columns of one chunk
     auto tile = [&](float* base, int r, int c) { return reinterpret_cast<f32x4*>(base + ((r * 2 + c) * 64 + l) * 4); };
@@ -206,7 +208,10 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 xacc[e] = bf16_bits_to_f32(vs[(16 * rt + 4 * g4 + e) * 32 + 16 * ct + l16]) - rkc[e] * xacc[e];
-            *tile(Zb, rt, ct) = xacc;
+            // split once, by the wave that forms the tile, into the hi and lo blocks U = A'' Z reads
+            char* const zd = Zc + (((rt >> 1) * 2 + ct) * 64 + l) * 16 + 8 * (rt & 1);
+            *reinterpret_cast<uint2*>(zd) = pack_bf16x4(xacc);
+            *reinterpret_cast<uint2*>(zd + 4096) = bf16_lo_part4(xacc);
             qacc *= rqv;
         }
         lds_barrier();                                           // B2
@@ -217,9 +222,9 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
 #pragma unroll
             for (int j = 0; j < NTB; ++j) {
                 if (2 * j > rt) break;                            // A'' is zero above the diagonal
-                const f32x4 z0 = *tile(Zb, 2 * j, ct), z1 = *tile(Zb, 2 * j + 1, ct);
-                const bf16x8 zh = as_bf16x8(pack_bf16x8(z0, z1));
-                const bf16x8 zl = as_bf16x8(bf16_lo_part(z0, z1));
+                const char* zs = Zc + ((j * 2 + ct) * 64 + l) * 16;
+                const bf16x8 zh = as_bf16x8(*reinterpret_cast<const uint4*>(zs));
+                const bf16x8 zl = as_bf16x8(*reinterpret_cast<const uint4*>(zs + 4096));
                 u = mfma_bf16_k32(as_bf16x8(ah[j]), zh, u);
                 u = mfma_bf16_k32(as_bf16x8(ah[j]), zl, u);
                 u = mfma_bf16_k32(as_bf16x8(al[j]), zh, u);

@@ -149,8 +149,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_kernel(ChunkArgs a) {
     // where row T would begin, so rows past the sequence end are dropped by the hardware
     u16* Yb = reinterpret_cast<u16*>(smem + a.s_z);          // [C][32] bf16, over Z
     const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0), (T * d_v - col0) * 2,
-        kBufferWord3);
+        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0),
+        static_cast<int>((static_cast<uint32_t>(T) * d_v - col0) * 2u), kBufferWord3);
     for (int n = 0; n < NC; ++n) {
         const int t0 = n * C;
         const int nn = n + 1 < NC ? n + 1 : n;          // the last chunk re-reads itself
@@ -399,18 +399,25 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     const u16* qB = static_cast<const u16*>(a.q) + row0 * DK;
     const u16* vB = static_cast<const u16*>(a.v) + row0 * d_v + col0;
     const int ktr = tid >> 3, kjg = tid & 7;
+    // k rows and v columns of this (b, h) as buffers whose range check returns zeros past the
+    // sequence end (the planner keeps their byte sizes below 2^32)
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(kB), static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(T) * DK * 2u),
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(vB), static_cast<short>(0),
+        static_cast<int>((static_cast<uint32_t>(T) * d_v - col0) * 2u), kBufferWord3);
     uint4 ka, rv;
-    uint32_t mk = 0u, mv = 0u;
     auto load_k = [&](int n) {
-        const int t0 = n * C, Cn = min(C, T - t0);
-        const bool ok = ktr < Cn;
-        const u16* r = kB + static_cast<int64_t>(t0 + (ok ? ktr : 0)) * DK;
-        ka = *reinterpret_cast<const uint4*>(r + 8 * kjg);
-        mk = ok ? 0xffffffffu : 0u;
-        const bool okv = tid < 4 * C && (tid >> 2) < Cn;
-        rv = *reinterpret_cast<const uint4*>(vB + static_cast<int64_t>(t0 + (okv ? tid >> 2 : 0)) * d_v +
-                                             (okv ? 8 * (tid & 3) : 0));
-        mv = okv ? 0xffffffffu : 0u;
+        const uint32_t t0 = static_cast<uint32_t>(n) * C;
+        const u32x4 k4 = __builtin_amdgcn_raw_buffer_load_b128(
+            krsrc, static_cast<int>(((t0 + ktr) * DK + 8 * kjg) * 2u), 0, 0);
+        ka = make_uint4(k4.x, k4.y, k4.z, k4.w);
+        // threads past the chunk's v units read past the buffer (zeros, no memory traffic)
+        const uint32_t vo = tid < 4 * C ? ((t0 + (tid >> 2)) * d_v + 8 * (tid & 3)) * 2u : 0xfffffff0u;
+        const u32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, static_cast<int>(vo), 0, 0);
+        rv = make_uint4(v4.x, v4.y, v4.z, v4.w);
     };
     uint2 qlo[2], qhi[2];
     auto load_q = [&](int n) {
@@ -424,9 +431,10 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
             qhi[e] = *reinterpret_cast<const uint2*>(r + j0);
         }
     };
-    // the next chunk's K tile: one DPFP task per thread (rows past the end zero)
+    // the next chunk's K tile: one DPFP task per thread (rows past the end zero: their k loads
+    // return zeros)
     auto build_k = [&](u16* Kn) {
-        const uint32_t ak[4] = {ka.x & mk, ka.y & mk, ka.z & mk, ka.w & mk};
+        const uint32_t ak[4] = {ka.x, ka.y, ka.z, ka.w};
         // a row's eight tasks sit in eight aligned lanes: lane kjg - 1 (kjg >= 1, DPP row_shr:1)
         // or kjg + 7 (kjg == 0, row_shl:7) holds the positions before this task's
         const uint32_t a4[4] = {ka.x, ka.y, ka.z, ka.w};
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
             const uint32_t prev = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a4[e]), 0x111, 0xF, 0xF, false));
             const uint32_t wrap = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a4[e]), 0x107, 0xF, 0xF, false));
             // the positions before 0 wrap into the [-k] half: their signs flip here
-            pk[e] = (kjg == 0 ? wrap ^ 0x80008000u : prev) & mk;
+            pk[e] = kjg == 0 ? wrap ^ 0x80008000u : prev;
         }
         float a8[8], p8[8];
 #pragma unroll
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     };
     auto store_v = [&]() {
         if (tid < 4 * C)
-            reinterpret_cast<uint4*>(Vr)[tid] = make_uint4(rv.x & mv, rv.y & mv, rv.z & mv, rv.w & mv);
+            reinterpret_cast<uint4*>(Vr)[tid] = rv;
     };
 
     // ---- per-chunk results of the prep kernel (as in delta_stream_kernel)
@@ -487,8 +495,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     lds_barrier();
 
     const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0), (T * d_v - col0) * 2,
-        kBufferWord3);
+        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0),
+        static_cast<int>((static_cast<uint32_t>(T) * d_v - col0) * 2u), kBufferWord3);
     for (int n = 0; n < NC; ++n) {
         const int t0 = n * C;
         const int nn = n + 1 < NC ? n + 1 : n;

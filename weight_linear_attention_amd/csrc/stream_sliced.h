@@ -706,8 +706,8 @@ __global__ __launch_bounds__(4 * C, 512 / (4 * C)) void delta_stream_sliced_kern
     // y of this workgroup's columns as a buffer: offsets from (b, h, t = 0, col0); the range ends
     // where row T would begin, so rows past the sequence end are dropped by the hardware
     const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0), (T * d_v - col0) * 2,
-        kBufferWord3);
+        static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0),
+        static_cast<int>((static_cast<uint32_t>(T) * d_v - col0) * 2u), kBufferWord3);
     float unused_q[NPQ], unused_k[NPK];   // the serial pass takes rho from the prep; the task
                                           // sums written here are dead and compiled away
     for (int n = 0; n < NC; ++n) {

@@ -419,16 +419,22 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
         const u32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(vrsrc, static_cast<int>(vo), 0, 0);
         rv = make_uint4(v4.x, v4.y, v4.z, v4.w);
     };
+    // q rows likewise (rows past the end read zeros; their y rows are dropped at the store)
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(qB), static_cast<short>(0), static_cast<int>(static_cast<uint32_t>(T) * DK * 2u),
+        kBufferWord3);
     uint2 qlo[2], qhi[2];
     auto load_q = [&](int n) {
-        const int t0 = n * C, Cn = min(C, T - t0);
-        const int rr = 16 * rt + l16;
-        const u16* r = qB + static_cast<int64_t>(t0 + (rr < Cn ? rr : 0)) * DK;
+        const uint32_t r0 = (static_cast<uint32_t>(n) * C + 16 * rt + l16) * DK;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int j0 = 16 * (2 * h + e) + 4 * g4;
-            qlo[e] = *reinterpret_cast<const uint2*>(r + ((j0 + DK - 4) & (DK - 1)));
-            qhi[e] = *reinterpret_cast<const uint2*>(r + j0);
+            const uint32_t j0 = 16 * (2 * h + e) + 4 * g4;
+            const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(
+                qrsrc, static_cast<int>((r0 + ((j0 + DK - 4) & (DK - 1))) * 2u), 0, 0);
+            const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(qrsrc, static_cast<int>((r0 + j0) * 2u), 0, 0);
+            qlo[e] = make_uint2(lo.x, lo.y);
+            qhi[e] = make_uint2(hi.x, hi.y);
         }
     };
     // the next chunk's K tile: one DPFP task per thread (rows past the end zero: their k loads
@@ -466,21 +472,34 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     f32x4 rkc, rqv;
     // (the A'' and P~ blocks are stored on and below the diagonal only, in tri_blk order; the
     // loads of a block above it re-read the row tile's last block and go unused)
+    // the prep results of this (b, h) as buffers: each lane's offsets are fixed, the chunk's
+    // offset is uniform (no range check: every chunk index is below NC)
+    const int64_t ub0 = static_cast<int64_t>(bh) * NC;
+    constexpr uint32_t szT = tri_nblocks(C) * 1024;
+    auto ws_rsrc = [&](int64_t off) {
+        return __builtin_amdgcn_make_buffer_rsrc(a.ws + off, static_cast<short>(0), -1, kBufferWord3);
+    };
+    const __amdgpu_buffer_rsrc_t ahr = ws_rsrc(a.o_ah + ub0 * szT), alr = ws_rsrc(a.o_al + ub0 * szT),
+                                 par = ws_rsrc(a.o_pa + ub0 * szT);
+    const __amdgpu_buffer_rsrc_t rkr = ws_rsrc(a.o_rk + ub0 * C * 4), rqr = ws_rsrc(a.o_rq + ub0 * C * 4);
+    int blo[NTB];
+#pragma unroll
+    for (int j = 0; j < NTB; ++j) blo[j] = (tri_blk(rt, min(j, rt >> 1)) * 64 + l) * 16;
+    const int rlo = (16 * rt + 4 * g4) * 4;
     auto load_ws = [&](int n) {
-        const int64_t u = static_cast<int64_t>(bh) * NC + n;
-        const char* ahp = a.ws + a.o_ah + u * (tri_nblocks(C) * 1024);
-        const char* alp = a.ws + a.o_al + u * (tri_nblocks(C) * 1024);
-        const char* pap = a.ws + a.o_pa + u * (tri_nblocks(C) * 1024);
+        const int so = static_cast<int>(static_cast<uint32_t>(n) * szT);
+        const int sr = static_cast<int>(static_cast<uint32_t>(n) * C * 4u);
 #pragma unroll
         for (int j = 0; j < NTB; ++j) {
-            const int tb = tri_blk(rt, min(j, rt >> 1));
-            ah[j] = *reinterpret_cast<const uint4*>(blk_ptr(ahp, tb, l));
-            al[j] = *reinterpret_cast<const uint4*>(blk_ptr(alp, tb, l));
-            pa[j] = *reinterpret_cast<const uint4*>(blk_ptr(pap, tb, l));
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(ahr, blo[j], so, 0);
+            const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(alr, blo[j], so, 0);
+            const u32x4 z = __builtin_amdgcn_raw_buffer_load_b128(par, blo[j], so, 0);
+            ah[j] = make_uint4(x.x, x.y, x.z, x.w);
+            al[j] = make_uint4(y.x, y.y, y.z, y.w);
+            pa[j] = make_uint4(z.x, z.y, z.z, z.w);
         }
-        const float* rk = reinterpret_cast<const float*>(a.ws + a.o_rk) + u * C;
-        rkc = *reinterpret_cast<const f32x4*>(rk + 16 * rt + 4 * g4);
-        rqv = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.ws + a.o_rq) + u * C + 16 * rt + 4 * g4);
+        rkc = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rkr, rlo, sr, 0));
+        rqv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rqr, rlo, sr, 0));
     };
 
     if (NC > 0) {

@@ -73,6 +73,7 @@ STREAM_CASES = [
     (64, 3, 16, 2, 1, 150), (64, 1, 16, 1, 1, 64),
     (32, 2, 64, 1, 2, 129), (32, 4, 32, 2, 1, 200), (32, 6, 64, 1, 1, 75), (16, 4, 64, 1, 2, 100),
     (16, 8, 32, 1, 2, 190), (16, 12, 64, 1, 1, 70),
+    (64, 3, 64, 1, 2, 300),           # an odd chunk count above one (the chunk loop's tail)
 ]
 
 

@@ -118,6 +118,7 @@ static bool plan_stream_full(int BH, int T, int d_k, int d_v, int nu, int C, Str
 
 template <int NU>
 static hipError_t launch_stream_pipe(const StreamPlan& p, hipStream_t stream) {
+    if (p.args.krs != 2 * 64 * NU + 16) return hipErrorInvalidValue;   // the kernel's fixed K stride
     auto kern = delta_stream_pipe_kernel<NU>;
     hipError_t e = ensure_lds_attr(reinterpret_cast<const void*>(kern), p.lds_stream);
     if (e != hipSuccess) return e;

@@ -323,7 +323,8 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = l & 15, g4 = l >> 4;
-    const int d_v = a.d_v, D = a.D, T = a.T, NC = a.NC, krs = a.krs;
+    const int d_v = a.d_v, D = a.D, T = a.T, NC = a.NC;
+    constexpr int krs = 2 * DK * NU + 16;       // K row stride (bf16), as the planner sets it
     const int NP = d_v / 32;
     const BhIndex bi = xcd_local(blockIdx.x, a.BH, NP);
     const int bh = bi.bh, col0 = 32 * static_cast<int>(bi.i);
@@ -516,12 +517,15 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
     const __amdgpu_buffer_rsrc_t yrsrc = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<u16*>(a.y) + row0 * d_v + col0, static_cast<short>(0),
         static_cast<int>((static_cast<uint32_t>(T) * d_v - col0) * 2u), kBufferWord3);
-    for (int n = 0; n < NC; ++n) {
+    // One chunk; ODD (chunk parity) picks the K buffers, so that the loop below, two chunks per
+    // iteration, addresses them with fixed offsets.
+    auto chunk = [&](int n, auto odd_tag) {
+        constexpr bool ODD = decltype(odd_tag)::value;
         const int t0 = n * C;
         const int nn = n + 1 < NC ? n + 1 : n;
         const int n2 = n + 2 < NC ? n + 2 : NC - 1;
-        const u16* Kc = (n & 1) ? Kb1 : Kb0;
-        u16* Kn = (n & 1) ? Kb0 : Kb1;
+        const u16* Kc = ODD ? Kb1 : Kb0;
+        u16* Kn = ODD ? Kb0 : Kb1;
 
         // ---- B: X tile (rt, h), partial Q W^T (rt, both), Z
         f32x4 xa = zero4(), xb = zero4(), qo = zero4(), qx = zero4();
@@ -633,10 +637,16 @@ __global__ __launch_bounds__(512, 1) void delta_stream_pipe_kernel(ChunkArgs a) 
             const int t = tid >> 3, c4 = 4 * (tid & 7);
             const uint2 v2 = *reinterpret_cast<const uint2*>(Yb + t * 32 + c4);
             typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{v2.x, v2.y}, yrsrc,
-                                                  ((t0 + t) * d_v + c4) * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{v2.x, v2.y}, yrsrc, static_cast<int>((static_cast<uint32_t>(t0 + t) * d_v + c4) * 2u), 0, 0);
         }
+    };
+    int n = 0;
+    for (; n + 1 < NC; n += 2) {
+        chunk(n, std::false_type());
+        chunk(n + 1, std::true_type());
     }
+    if (n < NC) chunk(n, std::false_type());
 
     if (a.Wf) {
 #pragma unroll
